@@ -1,0 +1,205 @@
+"""CPU oracle for the DSA layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  The GPU library never does, and it
+shares no code with the C source here (``oracle.c``).
+
+The functions follow the formulas of the Kwai Keye-VL-2.0 report (xllm-io
+review page, section "核心公式"; report section 2.3): the lightning indexer
+score, the Top-k index set and GQA sparse aggregation.  Every result is
+float64.  See ``oracle.c`` for the arithmetic and the readings of points the
+pages leave open.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with the host C compiler (no -ffast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True, cwd=_HERE)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build())
+            P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+            lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+            lib.oracle_e4m3_to_double.restype = D
+            lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+            lib.oracle_bf16_to_double.restype = D
+            lib.oracle_index_scores.argtypes = [P, P, P, P, P, I, I, I, I, I, I64, P, I, P]
+            lib.oracle_index_scores.restype = None
+            lib.oracle_topk.argtypes = [P, I64, I, P, I, P, P]
+            lib.oracle_topk.restype = None
+            lib.oracle_sparse_gqa_attn.argtypes = [P, P, P, I, P, I, I, P, P, I, P, I, I, I, I, D, P]
+            lib.oracle_sparse_gqa_attn.restype = None
+            lib.oracle_decode.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I,
+                                          I, D, P, I, P, P, P]
+            lib.oracle_decode.restype = None
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = I
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def _np(a, dtype=None):
+    """Accept numpy arrays or CPU torch tensors; return a C-contiguous numpy array."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        import torch
+        t = a.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            t = t.view(torch.uint16)
+        elif t.dtype == torch.float8_e4m3fn:
+            t = t.view(torch.uint8)
+        a = t.numpy()
+    a = np.ascontiguousarray(a)
+    if dtype is not None and a.dtype != dtype:
+        a = a.astype(dtype)
+    return a
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def e4m3_to_double(code: int) -> float:
+    return _load().oracle_e4m3_to_double(code)
+
+
+def bf16_to_double(bits: int) -> float:
+    return _load().oracle_bf16_to_double(bits)
+
+
+def index_scores(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, q_pos0=0, rows=None):
+    """I[t, s] for the query rows ``rows`` (default: all), s in [0, Tk).
+
+    q_idx [Tq, HI, dI] (uint8 E4M3 codes or float32), q_scale [Tq] or None,
+    w [Tq, HI] float32, k_idx [Tk, dI], k_scale [Tk] or None.  Entries with
+    s > q_pos0 + t are -inf.  Returns float64 [len(rows), Tk].
+    """
+    lib = _load()
+    code_dtype = np.uint8 if idx_dtype == FP8_E4M3 else np.float32
+    q_idx = _np(q_idx, code_dtype)
+    k_idx = _np(k_idx, code_dtype)
+    w = _np(w, np.float32)
+    q_scale = _np(q_scale, np.float32)
+    k_scale = _np(k_scale, np.float32)
+    Tq, HI, dI = q_idx.shape
+    Tk = k_idx.shape[0]
+    assert k_idx.shape == (Tk, dI) and w.shape == (Tq, HI)
+    if idx_dtype == FP8_E4M3:
+        assert q_scale.shape == (Tq,) and k_scale.shape == (Tk,)
+    rows = np.arange(Tq, dtype=np.int32) if rows is None else _np(rows, np.int32)
+    out = np.empty((len(rows), Tk), dtype=np.float64)
+    lib.oracle_index_scores(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+                            idx_dtype, Tq, Tk, HI, dI, int(q_pos0), _ptr(rows), len(rows),
+                            _ptr(out))
+    return out
+
+
+def topk(scores, pos, k):
+    """Top-k of each row of ``scores`` over candidates 0..pos[r].
+
+    Returns (idx int32 [rows, k] ascending with -1 padding, kth float64 [rows]):
+    kth is the score of the last member in selection order (the k-th largest,
+    or the smallest when fewer than k candidates exist).
+    """
+    lib = _load()
+    scores = _np(scores, np.float64)
+    if scores.ndim == 1:
+        scores = scores[None, :]
+    pos = _np(np.broadcast_to(np.asarray(pos, dtype=np.int64), (scores.shape[0],)), np.int64)
+    assert np.all(pos < scores.shape[1])
+    idx = np.empty((scores.shape[0], k), dtype=np.int32)
+    kth = np.empty(scores.shape[0], dtype=np.float64)
+    lib.oracle_topk(_ptr(scores), scores.shape[1], scores.shape[0], _ptr(pos), k, _ptr(idx),
+                    _ptr(kth))
+    return idx, kth
+
+
+def sparse_gqa_attn(q, k, v, dtype, idx, Hq, G, sm_scale, rows=None, block_table=None,
+                    block_size=0, row_seq=None):
+    """Attention of each query row over its index set (same set for every group).
+
+    q [T, Hq, d]; k, v [Tk, G, d] (or paged [NB, block_size, G, d] with
+    block_table [B, max_blocks] and row_seq [T]); idx [T, kk] (-1 skipped).
+    dtype: F32 or BF16 (bf16 passed as uint16 bits).  Returns float64
+    [len(rows), Hq, d].
+    """
+    lib = _load()
+    el = np.float32 if dtype == F32 else np.uint16
+    q, k, v = _np(q, el), _np(k, el), _np(v, el)
+    idx = _np(idx, np.int32)
+    T, Hq_, d = q.shape
+    assert Hq_ == Hq and Hq % G == 0
+    kk = idx.shape[1]
+    rows = np.arange(T, dtype=np.int32) if rows is None else _np(rows, np.int32)
+    bt = _np(block_table, np.int32)
+    rs = _np(row_seq, np.int32)
+    max_blocks = 0 if bt is None else bt.shape[1]
+    out = np.empty((len(rows), Hq, d), dtype=np.float64)
+    lib.oracle_sparse_gqa_attn(_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(bt), max_blocks,
+                               int(block_size), _ptr(rs), _ptr(idx), kk, _ptr(rows), len(rows),
+                               Hq, G, d, float(sm_scale), _ptr(out))
+    return out
+
+
+def decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, dtype,
+           block_table, seq_lens, block_size, k, sm_scale, seqs=None):
+    """One paged decode step for the sequences ``seqs`` (default: all).
+
+    Returns (idx int32 [n, k], kth float64 [n], out float64 [n, Hq, d]).
+    """
+    lib = _load()
+    el = np.float32 if dtype == F32 else np.uint16
+    q = _np(q, el)
+    q_idx = _np(q_idx, np.uint8)
+    q_scale, w = _np(q_scale, np.float32), _np(w, np.float32)
+    kidx_cache, kidx_scale = _np(kidx_cache, np.uint8), _np(kidx_scale, np.float32)
+    k_cache, v_cache = _np(k_cache, el), _np(v_cache, el)
+    block_table, seq_lens = _np(block_table, np.int32), _np(seq_lens, np.int32)
+    B, Hq, d = q.shape
+    _, HI, dI = q_idx.shape
+    G = k_cache.shape[2]
+    seqs = np.arange(B, dtype=np.int32) if seqs is None else _np(seqs, np.int32)
+    n = len(seqs)
+    idx = np.empty((n, k), dtype=np.int32)
+    kth = np.empty(n, dtype=np.float64)
+    out = np.empty((n, Hq, d), dtype=np.float64)
+    lib.oracle_decode(_ptr(q), _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(kidx_cache),
+                      _ptr(kidx_scale), _ptr(k_cache), _ptr(v_cache), dtype, _ptr(block_table),
+                      _ptr(seq_lens), block_table.shape[1], int(block_size), HI, dI, Hq, G, d,
+                      int(k), float(sm_scale), _ptr(seqs), n, _ptr(idx), _ptr(kth), _ptr(out))
+    return idx, kth, out

@@ -1,0 +1,403 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Nothing here compares the oracle with itself: each test checks it against a
+hand-computed value, a library routine, a closed form, an invariant, or a
+brute-force characterisation on a tiny input.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from golden_io import indexer_hand, topk_ties
+from workloads import quantize_e4m3_per_token
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+# ------------------------------------------------------------------ decoding
+
+def test_e4m3_decode_matches_torch_all_codes():
+    """Every one of the 256 OCP E4M3 codes decodes as torch's float8_e4m3fn does."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2                      # S.1111.111 only
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_e4m3_decode_special_values():
+    """Values the OCP E4M3 definition fixes: max 448, subnormals, -0."""
+    assert oracle.e4m3_to_double(0x7E) == 448.0
+    assert oracle.e4m3_to_double(0xFE) == -448.0
+    assert oracle.e4m3_to_double(0x01) == 2.0 ** -9       # smallest subnormal
+    assert oracle.e4m3_to_double(0x07) == 7 * 2.0 ** -9   # largest subnormal
+    assert oracle.e4m3_to_double(0x08) == 2.0 ** -6       # smallest normal
+    assert oracle.e4m3_to_double(0x38) == 1.0
+    assert math.copysign(1.0, oracle.e4m3_to_double(0x80)) == -1.0
+    assert math.isnan(oracle.e4m3_to_double(0x7F))
+
+
+def test_bf16_decode_matches_torch():
+    bits = torch.tensor([0x0000, 0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F, 0x8000, 0x3C00],
+                        dtype=torch.int32).to(torch.uint16)
+    ref = bits.view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits.to(torch.int32)])
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------- indexer
+
+def _hand_case():
+    d = indexer_hand()
+    HI, dI = d["HI"], d["dI"]
+    T = len(d["k"])
+    q = np.zeros((T, HI, dI), np.uint8)
+    qs = np.zeros(T, np.float32)
+    for (t, j), (codes, sc) in d["q"].items():
+        q[t, j] = codes
+        qs[t] = sc
+    k = np.array([d["k"][s][0] for s in range(T)], np.uint8)
+    ks = np.array([d["k"][s][1] for s in range(T)], np.float32)
+    w = np.array([d["w"][t] for t in range(T)], np.float32)
+    return d, q, qs, w, k, ks
+
+
+def test_indexer_hand_computed_golden():
+    """tests/golden/indexer_hand.txt: scores worked out by hand from the formula."""
+    d, q, qs, w, k, ks = _hand_case()
+    I = oracle.index_scores(q, qs, w, k, ks, oracle.FP8_E4M3)
+    T = I.shape[0]
+    for t in range(T):
+        for s in range(T):
+            if s > t:
+                assert I[t, s] == -np.inf
+            else:
+                assert I[t, s] == d["I"][(t, s)], (t, s)
+
+
+def test_hand_codes_are_the_values_the_fixture_claims():
+    """The fixture's hex codes decode (by torch) to the small exact values used in the working."""
+    d, q, qs, w, k, ks = _hand_case()
+    vals = torch.from_numpy(k).view(torch.float8_e4m3fn).float().numpy()
+    assert vals.tolist() == [[1, 0, 2, -1], [0.5, 1, -1, 0], [-2, 1, 0, 1.5]]
+
+
+def test_topk_of_hand_scores_golden():
+    d, q, qs, w, k, ks = _hand_case()
+    I = oracle.index_scores(q, qs, w, k, ks, oracle.FP8_E4M3)
+    for kk, t, expect in d["topk"]:
+        idx, _ = oracle.topk(I[t:t + 1], [t], kk)
+        got = [x for x in idx[0].tolist() if x >= 0]
+        assert got == expect, (kk, t, got)
+
+
+def _rand_fp8_case(rng, T, HI, dI, signed_w=False):
+    qf = torch.from_numpy(rng.standard_normal((T, HI, dI)).astype(np.float32))
+    kf = torch.from_numpy(rng.standard_normal((T, dI)).astype(np.float32))
+    q, qs = quantize_e4m3_per_token(qf)
+    k, ks = quantize_e4m3_per_token(kf)
+    w = rng.uniform(-1 if signed_w else 0, 1, (T, HI)).astype(np.float32)
+    return q.numpy(), qs.numpy(), w, k.numpy(), ks.numpy()
+
+
+def test_indexer_single_head_unit_weight_is_relu_of_dot():
+    """Special case H^I = 1, w = 1: I[t,s] = ReLU(q^I[t] . k^I[s]) (a plain matmul)."""
+    rng = np.random.default_rng(0)
+    q, qs, w, k, ks = _rand_fp8_case(rng, 12, 1, 32)
+    w[:] = 1.0
+    I = oracle.index_scores(q, qs, w, k, ks, oracle.FP8_E4M3)
+    qv = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()[:, 0, :] * qs[:, None]
+    kv = torch.from_numpy(k).view(torch.float8_e4m3fn).double().numpy() * ks[:, None]
+    ref = np.maximum(qv @ kv.T, 0.0)
+    tri = np.tril(np.ones_like(ref, dtype=bool))
+    assert np.allclose(I[tri], ref[tri], rtol=1e-13, atol=1e-13)
+    assert np.all(I[~tri] == -np.inf)
+
+
+def test_indexer_all_negative_dots_score_zero():
+    """Every head's dot product negative => I = 0 whatever w is."""
+    one, neg = 0x38, 0xB8
+    q = np.full((2, 3, 4), one, np.uint8)
+    k = np.array([[one] * 4, [neg] * 4], np.uint8)         # k1 = -q direction
+    qs = np.ones(2, np.float32)
+    ks = np.ones(2, np.float32)
+    w = np.array([[0.3, 0.7, 5.0], [1.0, 2.0, 3.0]], np.float32)
+    I = oracle.index_scores(q, qs, w, k, ks, oracle.FP8_E4M3)
+    assert I[1, 1] == 0.0
+    assert I[1, 0] == pytest.approx(4.0 * (1 + 2 + 3))
+
+
+def test_indexer_linear_in_w_and_positive_for_positive_w():
+    rng = np.random.default_rng(1)
+    q, qs, w1, k, ks = _rand_fp8_case(rng, 20, 4, 16, signed_w=True)
+    w2 = rng.uniform(-1, 1, w1.shape).astype(np.float32)
+    I1 = oracle.index_scores(q, qs, w1, k, ks, oracle.FP8_E4M3)
+    I2 = oracle.index_scores(q, qs, w2, k, ks, oracle.FP8_E4M3)
+    I12 = oracle.index_scores(q, qs, (w1.astype(np.float64) + w2).astype(np.float32), k, ks,
+                              oracle.FP8_E4M3)
+    tri = np.isfinite(I1)
+    # w1 + w2 rounds to fp32; compare against the exactly representable sums only
+    exact = (w1.astype(np.float64) + w2 == (w1 + w2).astype(np.float64)).all()
+    if exact:
+        assert np.allclose(I12[tri], I1[tri] + I2[tri], rtol=1e-12, atol=1e-12)
+    wpos = np.abs(w1)
+    Ip = oracle.index_scores(q, qs, wpos, k, ks, oracle.FP8_E4M3)
+    assert np.all(Ip[tri] >= 0)
+
+
+def test_indexer_key_scale_law():
+    """Doubling k_scale[s] doubles column s exactly (scales are positive, ReLU is homogeneous)."""
+    rng = np.random.default_rng(2)
+    q, qs, w, k, ks = _rand_fp8_case(rng, 16, 4, 16, signed_w=True)
+    I = oracle.index_scores(q, qs, w, k, ks, oracle.FP8_E4M3)
+    ks2 = ks.copy()
+    ks2[5] *= 2
+    I2 = oracle.index_scores(q, qs, w, k, ks2, oracle.FP8_E4M3)
+    assert np.array_equal(I2[:, 5][5:], 2 * I[:, 5][5:])
+    other = [s for s in range(16) if s != 5]
+    assert np.array_equal(I2[:, other], I[:, other])
+
+
+def test_indexer_head_permutation_invariance_and_key_locality():
+    rng = np.random.default_rng(3)
+    q, qs, w, k, ks = _rand_fp8_case(rng, 16, 6, 16, signed_w=True)
+    I = oracle.index_scores(q, qs, w, k, ks, oracle.FP8_E4M3)
+    perm = rng.permutation(6)
+    Ip = oracle.index_scores(np.ascontiguousarray(q[:, perm]), qs, np.ascontiguousarray(w[:, perm]),
+                             k, ks, oracle.FP8_E4M3)
+    fin = np.isfinite(I)
+    assert np.allclose(Ip[fin], I[fin], rtol=1e-13, atol=1e-13)
+    # changing key 3 only changes column 3
+    k2 = k.copy()
+    k2[3] = rng.integers(0, 0x77, 16)
+    I3 = oracle.index_scores(q, qs, w, k2, ks, oracle.FP8_E4M3)
+    cols = [s for s in range(16) if s != 3]
+    assert np.array_equal(I3[:, cols], I[:, cols])
+
+
+def test_indexer_rows_subset_and_query_offset():
+    """Sampled rows equal the full computation; q_pos0 shifts the causal boundary."""
+    rng = np.random.default_rng(4)
+    q, qs, w, k, ks = _rand_fp8_case(rng, 24, 4, 16)
+    I = oracle.index_scores(q, qs, w, k, ks, oracle.FP8_E4M3)
+    rows = np.array([0, 7, 23], np.int32)
+    Ir = oracle.index_scores(q, qs, w, k, ks, oracle.FP8_E4M3, rows=rows)
+    assert np.array_equal(Ir, I[rows])
+    # the last 8 queries alone, at positions 16..23
+    Io = oracle.index_scores(q[16:], qs[16:], w[16:], k, ks, oracle.FP8_E4M3, q_pos0=16)
+    assert np.array_equal(Io, I[16:])
+
+
+def test_indexer_f32_matches_float64_matmul_definition_on_tiny():
+    """fp32 indexer: brute force over heads with numpy float64 matmuls."""
+    rng = np.random.default_rng(5)
+    T, HI, dI = 10, 3, 8
+    q = rng.standard_normal((T, HI, dI)).astype(np.float32)
+    k = rng.standard_normal((T, dI)).astype(np.float32)
+    w = rng.uniform(-1, 1, (T, HI)).astype(np.float32)
+    I = oracle.index_scores(q, None, w, k, None, oracle.F32)
+    for t in range(T):
+        for s in range(T):
+            if s > t:
+                assert I[t, s] == -np.inf
+                continue
+            dots = q[t].astype(np.float64) @ k[s].astype(np.float64)
+            assert I[t, s] == pytest.approx(float(np.sum(w[t] * np.maximum(dots, 0))), rel=1e-12, abs=1e-12)
+
+
+# --------------------------------------------------------------------- top-k
+
+def test_topk_golden_ties():
+    scores, cases = topk_ties()
+    for kk, expect in cases:
+        idx, kth = oracle.topk(np.array([scores]), [len(scores) - 1], kk)
+        got = idx[0].tolist()
+        assert got[:len(expect)] == expect, (kk, got)
+        assert all(x == -1 for x in got[len(expect):])
+
+
+def _check_topk_definition(row, pos, kk, sel):
+    """The unique answer: n = min(k, pos+1) distinct positions in [0, pos], ascending, and every
+    selected position beats every unselected one (higher score, or equal score and lower index)."""
+    n = min(kk, pos + 1)
+    chosen = [x for x in sel if x >= 0]
+    assert len(chosen) == n and all(x == -1 for x in sel[n:])
+    assert chosen == sorted(set(chosen))
+    assert all(0 <= x <= pos for x in chosen)
+    rest = [s for s in range(pos + 1) if s not in set(chosen)]
+    for a in chosen:
+        for b in rest:
+            assert row[a] > row[b] or (row[a] == row[b] and a < b), (a, b)
+
+
+def test_topk_brute_force_tiny_with_heavy_ties():
+    rng = np.random.default_rng(6)
+    for trial in range(200):
+        L = int(rng.integers(1, 14))
+        row = rng.integers(-3, 4, L).astype(np.float64) * 0.5
+        row[rng.random(L) < 0.2] *= -1  # introduce -0.0 where row is 0
+        pos = int(rng.integers(0, L))
+        kk = int(rng.integers(1, L + 3))
+        idx, kth = oracle.topk(row[None, :], [pos], kk)
+        sel = idx[0].tolist()
+        _check_topk_definition(row, pos, kk, sel)
+        # exhaustive: among all n-subsets of [0,pos], the selected one maximises the sorted scores
+        n = min(kk, pos + 1)
+        if pos < 9:
+            best = max(itertools.combinations(range(pos + 1), n),
+                       key=lambda c: (sorted((row[i] for i in c), reverse=True), [-i for i in c]))
+            assert sorted(best) == [x for x in sel if x >= 0]
+
+
+def test_topk_dense_when_k_covers_prefix():
+    rng = np.random.default_rng(7)
+    row = rng.standard_normal(50)
+    for pos in (0, 1, 10, 49):
+        idx, _ = oracle.topk(row[None, :], [pos], 64)
+        assert idx[0, :pos + 1].tolist() == list(range(pos + 1))
+        assert np.all(idx[0, pos + 1:] == -1)
+
+
+def test_topk_kth_is_the_kth_largest():
+    rng = np.random.default_rng(8)
+    row = rng.standard_normal(100)
+    idx, kth = oracle.topk(row[None, :], [99], 10)
+    assert kth[0] == np.sort(row)[::-1][9]
+
+
+# ----------------------------------------------------------------- attention
+
+def _attn_inputs(rng, T, Hq, G, d, dtype):
+    q = rng.standard_normal((T, Hq, d)).astype(np.float32) / math.sqrt(d)
+    k = rng.standard_normal((T, G, d)).astype(np.float32) / math.sqrt(d)
+    v = rng.standard_normal((T, G, d)).astype(np.float32)
+    if dtype == oracle.BF16:
+        conv = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+        return conv(q), conv(k), conv(v)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", [oracle.F32, oracle.BF16])
+def test_attention_equals_dense_causal_sdpa_when_k_covers_prefix(dtype):
+    """k >= t+1 makes DSA dense: compare with torch's causal SDPA in float64, KV heads repeated."""
+    rng = np.random.default_rng(9)
+    T, Hq, G, d = 40, 8, 2, 32
+    q, k, v = _attn_inputs(rng, T, Hq, G, d, dtype)
+    idx = np.array([[s if s <= t else -1 for s in range(T)] for t in range(T)], np.int32)
+    out = oracle.sparse_gqa_attn(q, k, v, dtype, idx, Hq, G, 1 / math.sqrt(d))
+    tq = torch.as_tensor(q).double().permute(1, 0, 2)
+    tk = torch.as_tensor(k).double().repeat_interleave(Hq // G, dim=1).permute(1, 0, 2)
+    tv = torch.as_tensor(v).double().repeat_interleave(Hq // G, dim=1).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True,
+                                                           scale=1 / math.sqrt(d))
+    assert np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(10)
+    T, Hq, G, d = 16, 4, 2, 8
+    q, k, v = _attn_inputs(rng, T, Hq, G, d, oracle.F32)
+    sm = 0.3
+    # t = 0 attends only to itself: output = V[0, g]
+    idx0 = np.full((T, 4), -1, np.int32)
+    idx0[0, 0] = 0
+    out = oracle.sparse_gqa_attn(q, k, v, oracle.F32, idx0, Hq, G, sm, rows=[0])
+    for h in range(Hq):
+        assert np.allclose(out[0, h], v[0, h // 2], atol=1e-15, rtol=0)
+    # identical keys => uniform weights => mean of the selected V rows
+    k_same = np.repeat(k[:1], T, axis=0)
+    sel = np.array([[1, 4, 9, 12]] * T, np.int32)
+    out = oracle.sparse_gqa_attn(q, k_same, v, oracle.F32, sel, Hq, G, sm, rows=[13])
+    for h in range(Hq):
+        assert np.allclose(out[0, h], v[[1, 4, 9, 12], h // 2].astype(np.float64).mean(0), atol=1e-14)
+    # identical V rows => that row, whatever the weights
+    v_same = np.repeat(v[3:4], T, axis=0)
+    out = oracle.sparse_gqa_attn(q, k, v_same, oracle.F32, sel, Hq, G, sm, rows=[13])
+    for h in range(Hq):
+        assert np.allclose(out[0, h], v_same[0, h // 2], atol=1e-14)
+    # an empty set gives zeros
+    out = oracle.sparse_gqa_attn(q, k, v, oracle.F32, np.full((T, 4), -1, np.int32), Hq, G, sm, rows=[5])
+    assert np.all(out == 0)
+
+
+def test_attention_two_keys_closed_form():
+    """Two selected keys: weights are the logistic of the logit difference."""
+    rng = np.random.default_rng(11)
+    T, Hq, G, d = 8, 2, 1, 4
+    q, k, v = _attn_inputs(rng, T, Hq, G, d, oracle.F32)
+    sm = 0.7
+    sel = np.full((T, 3), -1, np.int32)
+    sel[6, :2] = [2, 5]
+    out = oracle.sparse_gqa_attn(q, k, v, oracle.F32, sel, Hq, G, sm, rows=[6])
+    for h in range(Hq):
+        l2 = sm * float(np.dot(q[6, h].astype(np.float64), k[2, 0]))
+        l5 = sm * float(np.dot(q[6, h].astype(np.float64), k[5, 0]))
+        p2 = 1.0 / (1.0 + math.exp(l5 - l2))
+        expect = p2 * v[2, 0].astype(np.float64) + (1 - p2) * v[5, 0]
+        assert np.allclose(out[0, h], expect, atol=1e-14)
+
+
+def test_attention_invariances():
+    rng = np.random.default_rng(12)
+    T, Hq, G, d = 24, 8, 4, 16
+    q, k, v = _attn_inputs(rng, T, Hq, G, d, oracle.F32)
+    sel = np.stack([rng.permutation(T)[:6] for _ in range(T)]).astype(np.int32)
+    out = oracle.sparse_gqa_attn(q, k, v, oracle.F32, sel, Hq, G, 0.25)
+    perm = np.ascontiguousarray(sel[:, ::-1])
+    outp = oracle.sparse_gqa_attn(q, k, v, oracle.F32, perm, Hq, G, 0.25)
+    assert np.allclose(out, outp, atol=1e-14)
+    # group 0's output depends only on group 0's K/V
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 1:] = rng.standard_normal(k2[:, 1:].shape)
+    v2[:, 1:] = rng.standard_normal(v2[:, 1:].shape)
+    out2 = oracle.sparse_gqa_attn(q, k2, v2, oracle.F32, sel, Hq, G, 0.25)
+    assert np.array_equal(out2[:, :2], out[:, :2])
+    assert not np.allclose(out2[:, 2:], out[:, 2:])
+    # the same index set serves every group: head h in group h // (Hq/G)
+    assert np.array_equal(out[:, 0], oracle.sparse_gqa_attn(q, k, v, oracle.F32, sel, Hq, G, 0.25)[:, 0])
+
+
+# ---------------------------------------------------------------- paged decode
+
+def _paged_from_contiguous(rng, arrays, L, bs, extra_blocks=3):
+    """Scatter contiguous per-token arrays into a shuffled paged layout."""
+    nb = (L + bs - 1) // bs
+    NB = nb + extra_blocks
+    perm = rng.permutation(NB)[:nb].astype(np.int32)
+    out = []
+    for a in arrays:
+        paged = np.zeros((NB, bs) + a.shape[1:], a.dtype)
+        for i in range(nb):
+            n = min(bs, L - i * bs)
+            paged[perm[i], :n] = a[i * bs:i * bs + n]
+        out.append(paged)
+    return perm, out
+
+
+def test_decode_equals_prefill_row_through_block_table():
+    """Decode of a sequence of length t+1 equals prefill row t (paged vs contiguous addressing)."""
+    rng = np.random.default_rng(13)
+    L, HI, dI, Hq, G, d, kk, bs = 45, 4, 16, 4, 2, 8, 7, 8
+    q_idx, qs, w, k_idx, ks = _rand_fp8_case(rng, L, HI, dI)
+    q = rng.standard_normal((L, Hq, d)).astype(np.float32)
+    k = rng.standard_normal((L, G, d)).astype(np.float32)
+    v = rng.standard_normal((L, G, d)).astype(np.float32)
+    I = oracle.index_scores(q_idx, qs, w, k_idx, ks, oracle.FP8_E4M3)
+    idx, kth = oracle.topk(I, np.arange(L), kk)
+    out = oracle.sparse_gqa_attn(q, k, v, oracle.F32, idx, Hq, G, 0.4)
+    for t in (0, 6, 7, 30, 44):
+        n = t + 1
+        perm, (kc, vc, kic, ksc) = _paged_from_contiguous(rng, [k[:n], v[:n], k_idx[:n], ks[:n]], n, bs)
+        bt = perm[None, :]
+        i2, kth2, o2 = oracle.decode(q[t:t + 1], q_idx[t:t + 1], qs[t:t + 1], w[t:t + 1], kic, ksc,
+                                     kc, vc, oracle.F32, bt, np.array([n], np.int32), bs, kk, 0.4)
+        assert np.array_equal(i2[0], idx[t])
+        assert kth2[0] == kth[t]
+        assert np.allclose(o2[0], out[t], atol=1e-13)
