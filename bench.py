@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA layer on one MI355X.
+
+One step = one full causal prefill of a 128K-token sequence through the DSA
+layer (FP8 lightning indexer -> top-k (k = 2048) -> GQA sparse attention),
+processed in 8K-query chunks, on seeded synthetic inputs already resident in
+HBM.  ``value`` is prefill tokens per second.  The paged decode step (64
+sequences at 256K, and at lengths drawn from 32K..256K) is timed in a second
+region and reported under ``decode``.
+
+Per-kernel durations come from HIP events recorded on the stream the kernels
+are launched on, around every launch of the timed steps.  Each kernel's
+achieved rate is its algorithmic work (FP8 FLOPs for the indexer, bytes for
+top-k and the attention gather) divided by its average duration; the
+dominant kernel is reported as ``roofline``.  The CPU oracle, timed on a
+stratified sample of query rows, is reported as ``cpu_baseline``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"fp8": 5.0e15, "bf16": 2.5e15, "hbm": 8.0e12}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="prefill_128k_clustered")
+    p.add_argument("--decode-workloads", default="decode_paged_64x256k,decode_paged_64x32k-256k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=48)
+    p.add_argument("--no-decode", action="store_true")
+    return p.parse_args()
+
+
+def prefill_work(cfg):
+    """Algorithmic work of each kernel for one chunked prefill (per chunk lists)."""
+    L, k, C = cfg.L, cfg.k, cfg.chunk or cfg.L
+    chunks = []
+    for r0 in range(0, L, C):
+        r1 = min(L, r0 + C)
+        pairs = (r1 * (r1 + 1) - r0 * (r0 + 1)) // 2          # sum_{t=r0}^{r1-1} (t+1)
+        n_sel = sum(min(k, t + 1) for t in range(r0, r1))
+        long_rows = sum(1 for t in range(r0, r1) if t + 1 > k)
+        pairs_long = sum(t + 1 for t in range(r0, r1) if t + 1 > k)
+        chunks.append({
+            "index_flop": 2 * cfg.HI * cfg.dI * pairs,
+            # top-k reads each causal score of a row that needs selection once, writes k indices
+            "topk_bytes": 4 * pairs_long + 4 * k * (r1 - r0),
+            # gather of K and V rows of every selected position for all groups + q in + out
+            "attn_bytes": n_sel * cfg.G * cfg.d * 2 * 2 + (r1 - r0) * cfg.Hq * cfg.d * 2 * 2,
+            "attn_flop": 4 * n_sel * cfg.Hq * cfg.d,
+            "rows": r1 - r0, "long_rows": long_rows,
+        })
+    return chunks
+
+
+def run_prefill_bench(args, dsa, W, torch):
+    cfg = W.ALL[args.workload]
+    dev = "cuda"
+    log("generating", cfg.name)
+    x = W.prefill_inputs(cfg, dev)
+    torch.cuda.synchronize()
+    L, k, C = cfg.L, cfg.k, cfg.chunk or cfg.L
+    ld = (L + 3) // 4 * 4
+    scores = torch.empty(C, ld, dtype=torch.float32, device=dev)
+    idx = torch.empty(L, k, dtype=torch.int32, device=dev)
+    out = torch.empty_like(x["q"])
+    stream = torch.cuda.current_stream()
+    s_ptr = stream.cuda_stream
+    n_chunks = (L + C - 1) // C
+
+    def step(events=None):
+        for c, r0 in enumerate(range(0, L, C)):
+            rows = min(C, L - r0)
+            tk = r0 + rows
+            sl = slice(r0, r0 + rows)
+            ev = events[c] if events else None
+            if ev: ev[0].record(stream)
+            dsa.dsa_index_scores(x["q_idx"][sl], x["q_scale"][sl], x["w"][sl], x["k_idx"], x["k_scale"],
+                                 dsa.DSA_FP8_E4M3, rows, tk, cfg.HI, cfg.dI, r0, scores, ld, stream)
+            if ev: ev[1].record(stream)
+            dsa.dsa_topk(scores, ld, rows, tk, r0, k, idx[sl], None, 0, stream)
+            if ev: ev[2].record(stream)
+            dsa.dsa_sparse_gqa_attn(x["q"][sl], x["k"], x["v"], dsa.DSA_BF16, tk, None, 0, 0, None,
+                                    None, idx[sl], rows, k, cfg.Hq, cfg.G, cfg.d, cfg.sm_scale,
+                                    out[sl], None, 0, stream)
+            if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_chunks)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    # per-kernel average durations (per launch) over the timed steps
+    dur = {"index": [], "topk": [], "attn": []}
+    for s in range(args.steps):
+        for c in range(n_chunks):
+            e = events[s][c]
+            dur["index"].append(e[0].elapsed_time(e[1]) * 1e-3)
+            dur["topk"].append(e[1].elapsed_time(e[2]) * 1e-3)
+            dur["attn"].append(e[2].elapsed_time(e[3]) * 1e-3)
+    work = prefill_work(cfg)
+    kern = {}
+    tot = lambda key: sum(w[key] for w in work)
+    for name, key, unit, peak, bound in (("index", "index_flop", "TFLOP/s", PEAK["fp8"], "mfma"),
+                                         ("topk", "topk_bytes", "GB/s", PEAK["hbm"], "hbm"),
+                                         ("attn", "attn_bytes", "GB/s", PEAK["hbm"], "hbm")):
+        per_launch_work = tot(key) / n_chunks
+        avg = sum(dur[name]) / len(dur[name])
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        achieved = per_launch_work / avg / scale
+        kern[name] = {"bound": bound, "achieved": round(achieved, 2), "peak": peak / scale,
+                      "unit": unit, "frac": round(achieved * scale / peak, 4),
+                      "avg_launch_ms": round(avg * 1e3, 4), "launches": len(dur[name]),
+                      "ms_per_step": round(sum(dur[name]) / args.steps * 1e3, 3),
+                      "work_per_launch": per_launch_work}
+    # the fused entry point on the same inputs (same kernels, one call per step)
+    ws = dsa.workspace(dsa.dsa_prefill_workspace_size(L, 0, C, k))
+    out2 = torch.empty_like(out)
+    for _ in range(max(1, args.warmup)):
+        dsa.dsa_prefill(x["q"], x["k"], x["v"], dsa.DSA_BF16, x["q_idx"], x["q_scale"], x["w"],
+                        x["k_idx"], x["k_scale"], dsa.DSA_FP8_E4M3, L, 0, cfg.Hq, cfg.G, cfg.d,
+                        cfg.HI, cfg.dI, k, cfg.sm_scale, C, out2, None, ws, ws.numel(), stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        dsa.dsa_prefill(x["q"], x["k"], x["v"], dsa.DSA_BF16, x["q_idx"], x["q_scale"], x["w"],
+                        x["k_idx"], x["k_scale"], dsa.DSA_FP8_E4M3, L, 0, cfg.Hq, cfg.G, cfg.d,
+                        cfg.HI, cfg.dI, k, cfg.sm_scale, C, out2, None, ws, ws.numel(), stream)
+    torch.cuda.synchronize()
+    fused_ms = (time.perf_counter() - t1) / args.steps * 1e3
+    same = bool(torch.equal(out, out2))
+    del ws, scores
+    return cfg, x, idx, out, ms_step, kern, fused_ms, same
+
+
+def run_decode_bench(args, dsa, W, torch, name):
+    cfg = W.ALL[name]
+    log("generating", cfg.name)
+    x = W.decode_inputs(cfg, "cuda")
+    out = torch.empty_like(x["q"])
+    n = dsa.dsa_decode_workspace_size(cfg.B, x["max_blocks"], cfg.block, cfg.k, cfg.Hq, cfg.d)
+    ws = dsa.workspace(n)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dsa.dsa_decode(x["q"], x["q_idx"], x["q_scale"], x["w"], x["kidx_cache"], x["kidx_scale"],
+                       x["k_cache"], x["v_cache"], dsa.DSA_BF16, x["block_table"], x["seq_lens"],
+                       cfg.B, x["NB"], x["max_blocks"], cfg.block, cfg.Hq, cfg.G, cfg.d, cfg.HI,
+                       cfg.dI, cfg.k, cfg.sm_scale, out, None, ws, ws.numel(), stream)
+    for _ in range(max(2, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(10, args.steps * 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) / steps * 1e3
+    lens = x["seq_lens"].long().cpu()
+    # algorithmic bytes: indexer keys (codes + scale) + score write/read + gather + q/out
+    key_bytes = int(lens.sum()) * (cfg.dI + 4)
+    score_bytes = int(lens.sum()) * 8
+    gather = int(torch.clamp(lens, max=cfg.k).sum()) * cfg.G * cfg.d * 2 * 2
+    qo = cfg.B * (cfg.Hq * cfg.d * 2 * 2 + cfg.HI * cfg.dI + cfg.HI * 4)
+    total = key_bytes + score_bytes + gather + qo
+    res = {"workload": cfg.name, "us_per_step": round(us_step, 2),
+           "us_per_token": round(us_step / cfg.B, 3),
+           "mean_len": float(lens.float().mean()), "algorithmic_bytes": total,
+           "achieved_GBps": round(total / (us_step * 1e-6) / 1e9, 1),
+           "hbm_frac": round(total / (us_step * 1e-6) / PEAK["hbm"], 4)}
+    del x, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args, cfg, x, torch):
+    """The oracle on a stratified sample of query rows of the same workload."""
+    import numpy as np
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import to_np
+    L = cfg.L
+    n = args.cpu_rows
+    rows = np.array([int((i + 0.5) * L / n) for i in range(n)], np.int32)
+    rt = torch.from_numpy(rows).long().to(x["q"].device)
+    qi, qs, w = to_np(x["q_idx"][rt]), to_np(x["q_scale"][rt]), to_np(x["w"][rt])
+    ki, ks = to_np(x["k_idx"]), to_np(x["k_scale"])
+    q, kk, vv = to_np(x["q"][rt]), to_np(x["k"]), to_np(x["v"])
+    threads = oracle.num_threads()
+    idx = np.empty((n, cfg.k), np.int32)
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(j):
+        # one call per row keeps each row at its own causal length; rows run in parallel
+        r = int(rows[j])
+        s = oracle.index_scores(qi[j:j + 1], qs[j:j + 1], w[j:j + 1], ki[:r + 1], ks[:r + 1],
+                                oracle.FP8_E4M3, q_pos0=r)
+        sel, _ = oracle.topk(s, [r], cfg.k)
+        return sel[0]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for j, sel in enumerate(ex.map(one, range(n))):
+            idx[j] = sel
+    oracle.sparse_gqa_attn(q, kk, vv, oracle.BF16, idx, cfg.Hq, cfg.G, cfg.sm_scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d query rows at positions (i+0.5)*L/%d of the %s workload (full indexer "
+                      "over each row's prefix, top-k, attention), %.1f s wall" % (n, n, cfg.name, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the DSA layer here is a single-GPU build "
+              "(no collectives); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_sparse_02_amd as dsa
+    import workloads as W
+    dsa.load_library()
+    cfg, x, idx, out, ms_step, kern, fused_ms, same = run_prefill_bench(args, dsa, W, torch)
+    dom = max(kern, key=lambda n: kern[n]["ms_per_step"])
+    r = kern[dom]
+    roofline = {"bound": r["bound"], "achieved": r["achieved"], "peak": r["peak"], "unit": r["unit"],
+                "frac": r["frac"], "traffic": None, "kernel": dom}
+    result = {
+        "metric": "DSA layer tokens/s at 128K prefill + decode us/token at 256K, % of MI355X roofline",
+        "value": round(cfg.L / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8+bf16",
+        "data": "synthetic (seeded; clustered FP8 indexer keys, bf16 q/k/v)",
+        "config": {"workload": cfg.name, "seq_len": cfg.L, "chunk_rows": cfg.chunk, "topk": cfg.k,
+                   "Hq": cfg.Hq, "G": cfg.G, "d": cfg.d, "HI": cfg.HI, "dI": cfg.dI,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": kern,
+        "fused_prefill_ms": round(fused_ms, 3), "fused_equals_staged": same,
+    }
+    del x, idx, out
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        result["decode"] = [run_decode_bench(args, dsa, W, torch, n)
+                            for n in args.decode_workloads.split(",") if n]
+    if not args.no_cpu_baseline:
+        x = W.prefill_inputs(cfg, "cuda")
+        result["cpu_baseline"] = cpu_baseline(args, cfg, x, torch)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

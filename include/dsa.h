@@ -1,0 +1,183 @@
+/*
+ * dsa.h -- C interface of libdsa, the DeepSeek Sparse Attention (DSA) layer in
+ * the GQA form of the Kwai Keye-VL-2.0 report, for AMD MI355X (gfx950).
+ *
+ * The layer (report section 2.3; xllm-io review page, section "核心公式"):
+ *   1. lightning indexer   I[t,s] = sum_j w[t,j] * ReLU(q^I[t,j] . k^I[s])  for s <= t,
+ *      one FP8 key vector per token shared by all H^I indexer heads (MQA style);
+ *   2. top-k               Omega_t = the min(k, t+1) positions with the largest I[t,:];
+ *   3. GQA sparse attention u[t,g] = softmax attention of token t's query heads in
+ *      group g over { (K[s,g], V[s,g]) : s in Omega_t }, the same Omega_t for
+ *      every group; outputs concatenated over groups.
+ *
+ * Conventions common to every call
+ *  - Every pointer argument is DEVICE memory owned by the caller, unless noted.
+ *    The library keeps no pointer after a call returns, allocates nothing and
+ *    never synchronises: work is queued on `stream` and its results are ready
+ *    when the stream reaches that point.
+ *  - Arrays are dense row-major with the shapes given in brackets.  Arrays of
+ *    vectors (q, k, v, out, indexer codes, w, scores, workspace) must be
+ *    16-byte aligned; per-token scales, index lists, block tables and
+ *    sequence lengths need only 4-byte alignment.
+ *  - Positions are absolute and 0-based; the causal rule is s <= position, so
+ *    the token itself is a candidate.
+ *  - Query head h belongs to KV group h / (Hq / G).
+ *  - FP8 means OCP E4M3 (bias 7, max 448, S.1111.111 = NaN) with a per-token
+ *    fp32 scale: value = scale * e4m3(code).
+ *  - bf16 inputs give bf16 outputs and fp32 inputs give fp32 outputs; all
+ *    internal accumulation is fp32.
+ *  - Errors: all arguments are checked on the host before anything is queued,
+ *    so a call that fails with DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED or
+ *    DSA_ERR_WORKSPACE has queued nothing.  A failed kernel launch returns
+ *    DSA_ERR_HIP.  dsa_last_error() then describes the failure (per thread).
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Index values read from device memory (Omega entries, block-table
+ *    entries, sequence lengths) are bounds-checked by the kernels: an entry
+ *    outside its valid range is skipped, never dereferenced.
+ *  - Calls are reentrant; concurrent calls on different streams are safe.
+ */
+#ifndef LIBDSA_DSA_H
+#define LIBDSA_DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or shape */
+    DSA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head size, dtype mix) */
+    DSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the size query says */
+    DSA_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} dsa_status_t;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype_t;
+
+/* Static text for a status code. */
+const char* dsa_status_string(dsa_status_t s);
+/* Detail of the last failed call on this host thread ("" if none). */
+const char* dsa_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dsa_version(void);
+
+/*
+ * Lightning indexer (report section 2.3.1; review page "核心公式", first formula).
+ *
+ *   scores[i, s] = sum_j w[i, j] * ReLU(q^I[i, j] . k^I[s])   for s <= q_pos0 + i
+ *   scores[i, s] = -INFINITY                                  for s >  q_pos0 + i
+ * for 0 <= i < Tq, 0 <= s < Tk.  Row i is the query at position q_pos0 + i.
+ *
+ * idx_dtype = DSA_FP8_E4M3: q_idx uint8 [Tq, HI, dI], q_scale [Tq], k_idx uint8
+ *   [Tk, dI], k_scale [Tk]; dI must be 128, 1 <= HI <= 128, HI % 4 == 0.  Products
+ *   run on FP8 matrix cores with fp32 accumulation, then ReLU, the w-weighted
+ *   head sum and the scales in fp32.
+ * idx_dtype = DSA_F32: q_idx float [Tq, HI, dI], k_idx float [Tk, dI], scales
+ *   ignored (may be NULL); dI % 4 == 0, dI <= 128, HI * dI <= 1024.
+ * w: float [Tq, HI], any sign.  scores: float, row stride ld_scores >= Tk,
+ *   ld_scores % 4 == 0.  Requires Tk >= q_pos0 + Tq (every query sees its prefix).
+ */
+dsa_status_t dsa_index_scores(const void* q_idx, const float* q_scale, const float* w,
+                              const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype,
+                              int Tq, int Tk, int HI, int dI, int64_t q_pos0,
+                              float* scores, int64_t ld_scores, hipStream_t stream);
+
+/*
+ * Top-k index set (review page "核心公式", second formula; k = 2048 in the
+ * report; deterministic selection, report section 5.2.1).
+ *
+ * Row i (position p = q_pos0 + i) selects n = min(k, p + 1) of the candidates
+ * s = 0..p of scores[i, :]: the n largest, equal scores going to the lower s,
+ * -0.0 equal to +0.0.  idx [Tq, k] int32 receives them in ascending order,
+ * followed by -1.  Rows with p + 1 <= k need no selection and read nothing.
+ * Scores are expected finite; NaN orders above +inf (positive NaN) or below
+ * -inf (negative NaN).  1 <= k <= 8192; ld_scores >= Tk >= q_pos0 + Tq.
+ * Workspace: dsa_topk_workspace_size() bytes (may be 0; ws may then be NULL).
+ */
+size_t dsa_topk_workspace_size(int Tq, int Tk, int k);
+dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int Tq, int Tk, int64_t q_pos0,
+                      int k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * GQA sparse aggregation (report section 2.3.2; review page "核心公式", third
+ * formula): for every query row t and head h in group g = h / (Hq / G),
+ *   out[t, h, :] = softmax_s(sm_scale * q[t, h, :] . K[s, g, :]) V[s, g, :]
+ * over the positions s listed in idx[t, 0..k) (entries < 0 are skipped), the
+ * same list for every group.  A row with no valid entry gives zeros.
+ *
+ * dtype DSA_BF16 (bf16 matrix cores, fp32 softmax) or DSA_F32 (fp32 vector
+ * ALU); d must be 128; Hq % G == 0 and Hq / G <= 16.
+ * q [Tq, Hq, d]; out [Tq, Hq, d] (same dtype).
+ * Contiguous K/V (block_table == NULL): k, v [n_kv, G, d]; entries outside
+ *   [0, n_kv) are skipped.
+ * Paged K/V (block_table != NULL): k, v [n_kv, block_size, G, d] with n_kv
+ *   physical blocks; position s of sequence b lives in block
+ *   block_table[b, s / block_size] at slot s % block_size; block_table is
+ *   [n_seq, max_blocks].  row_seq [Tq] gives the sequence of each row (NULL:
+ *   row t is sequence t).  seq_lens [n_seq] (NULL: no length limit beyond
+ *   max_blocks * block_size) bounds the valid positions of each sequence.
+ * ws (nullable): with at least dsa_sparse_gqa_attn_workspace_size() bytes the
+ *   library may split long rows across workgroups and combine the partial
+ *   softmax results; with NULL every row is done by one workgroup.
+ */
+size_t dsa_sparse_gqa_attn_workspace_size(int Tq, int k, int Hq, int d);
+dsa_status_t dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, dsa_dtype_t dtype,
+                                 int n_kv, const int32_t* block_table, int max_blocks,
+                                 int block_size, const int32_t* row_seq, const int32_t* seq_lens,
+                                 const int32_t* idx, int Tq, int topk, int Hq, int G, int d,
+                                 float sm_scale, void* out, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
+ * Fused prefill of one sequence: indexer -> top-k -> sparse attention for the
+ * Tq queries at positions q_pos0 .. q_pos0 + Tq - 1 over the Tk = q_pos0 + Tq
+ * keys (report sections 2.3.1-2.3.2).  Queries are processed in chunks of
+ * chunk_rows rows (the chunked indexer of report section 5.2.1, split along
+ * the query axis); every row still sees its whole prefix, so chunking changes
+ * no result.  chunk_rows <= 0 means one chunk.
+ *
+ * q [Tq, Hq, d], k / v [Tk, G, d] (dtype), q_idx / q_scale / w [Tq, ...] and
+ * k_idx / k_scale [Tk, ...] as in dsa_index_scores, out [Tq, Hq, d].
+ * idx_out (nullable) [Tq, topk] receives every row's Omega as dsa_topk writes it.
+ * Workspace: dsa_prefill_workspace_size() bytes; it holds one chunk's fp32
+ * score matrix (chunk_rows x Tk) and, when idx_out is NULL, its index sets.
+ */
+size_t dsa_prefill_workspace_size(int Tq, int64_t q_pos0, int chunk_rows, int topk);
+dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_t dtype,
+                         const void* q_idx, const float* q_scale, const float* w,
+                         const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype,
+                         int Tq, int64_t q_pos0, int Hq, int G, int d, int HI, int dI, int topk,
+                         float sm_scale, int chunk_rows, void* out, int32_t* idx_out,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Paged decode step (report section 5.3): one new query per sequence b, at
+ * position seq_lens[b] - 1, whose own K/V/k^I entries are already in the
+ * caches.  Runs the FP8 indexer over the sequence's paged indexer keys, the
+ * top-k, and sparse attention over the paged K/V.
+ *
+ * q [B, Hq, d] (dtype), q_idx uint8 [B, HI, dI], q_scale [B], w [B, HI];
+ * kidx_cache uint8 [num_blocks, block_size, dI], kidx_scale [num_blocks, block_size];
+ * k_cache / v_cache [num_blocks, block_size, G, d] (dtype);
+ * block_table int32 [B, max_blocks]; seq_lens int32 [B] (device).
+ * A sequence length outside [1, max_blocks * block_size] yields a zero output
+ * row and an index row of -1.  dI must be 128; dtype DSA_BF16 or DSA_F32.
+ * out [B, Hq, d]; idx_out (nullable) [B, topk].
+ * Workspace: dsa_decode_workspace_size() bytes.
+ */
+size_t dsa_decode_workspace_size(int B, int max_blocks, int block_size, int topk, int Hq, int d);
+dsa_status_t dsa_decode(const void* q, const void* q_idx, const float* q_scale, const float* w,
+                        const void* kidx_cache, const float* kidx_scale, const void* k_cache,
+                        const void* v_cache, dsa_dtype_t dtype, const int32_t* block_table,
+                        const int32_t* seq_lens, int B, int num_blocks, int max_blocks,
+                        int block_size, int Hq, int G, int d, int HI, int dI, int topk,
+                        float sm_scale, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBDSA_DSA_H */

@@ -1,0 +1,247 @@
+"""libdsa: DeepSeek Sparse Attention (GQA form) for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/dsa.h``.  Every step of the
+layer -- lightning indexer, top-k, GQA sparse attention, the fused prefill and
+paged decode -- runs in the HIP kernels of ``libdsa.so``; this module only
+marshals torch tensors (device pointers) and the current HIP stream.  It has
+no fallback: if the library is missing or the tensors are not on the GPU the
+calls raise.
+
+Functions named ``dsa_*`` mirror the C entry points one to one.  ``prefill``
+and ``decode`` are conveniences that allocate outputs and workspace with torch
+and call ``dsa_prefill`` / ``dsa_decode``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libdsa.so")
+
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
+          4: "DSA_ERR_HIP"}
+
+# every symbol the header declares, in declaration order
+EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version", "dsa_index_scores",
+           "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_gqa_attn_workspace_size",
+           "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill",
+           "dsa_decode_workspace_size", "dsa_decode"]
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), detail))
+        self.status = status
+        self.detail = detail
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdsa.so (built in-tree by ``build.build()``); raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise OSError("libdsa.so not found at %s; build it with "
+                          "`python -m long_context_sparse_02_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        P, I, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+        sig = {
+            "dsa_status_string": ([I], ctypes.c_char_p),
+            "dsa_last_error": ([], ctypes.c_char_p),
+            "dsa_version": ([], I),
+            "dsa_index_scores": ([P, P, P, P, P, I, I, I, I, I, I64, P, I64, P], I),
+            "dsa_topk_workspace_size": ([I, I, I], SZ),
+            "dsa_topk": ([P, I64, I, I, I64, I, P, P, SZ, P], I),
+            "dsa_sparse_gqa_attn_workspace_size": ([I, I, I, I], SZ),
+            "dsa_sparse_gqa_attn": ([P, P, P, I, I, P, I, I, P, P, P, I, I, I, I, I, F, P, P, SZ, P], I),
+            "dsa_prefill_workspace_size": ([I, I64, I, I], SZ),
+            "dsa_prefill": ([P, P, P, I, P, P, P, P, P, I, I, I64, I, I, I, I, I, I, F, I, P, P, P,
+                             SZ, P], I),
+            "dsa_decode_workspace_size": ([I, I, I, I, I, I], SZ),
+            "dsa_decode": ([P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, I, F, P, P,
+                            P, SZ, P], I),
+        }
+        for name in EXPORTS:
+            fn = getattr(lib, name)
+            fn.argtypes, fn.restype = sig[name]
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise DSAError(status, load_library().dsa_last_error().decode())
+
+
+def _ptr(t):
+    """Device pointer of a CUDA tensor (None -> NULL).  Host tensors are rejected."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libdsa takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libdsa takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dtype_code(t) -> int:
+    import torch
+    return {torch.float32: DSA_F32, torch.bfloat16: DSA_BF16, torch.uint8: DSA_FP8_E4M3,
+            torch.float8_e4m3fn: DSA_FP8_E4M3}[t.dtype]
+
+
+# ------------------------------------------------------------ raw entry points
+
+def dsa_version() -> int:
+    return load_library().dsa_version()
+
+
+def dsa_index_scores(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, q_pos0, scores,
+                     ld_scores, stream=None):
+    _check(load_library().dsa_index_scores(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx),
+                                           _ptr(k_scale), idx_dtype, Tq, Tk, HI, dI, q_pos0,
+                                           _ptr(scores), ld_scores, _stream(stream)))
+
+
+def dsa_topk_workspace_size(Tq, Tk, k) -> int:
+    return load_library().dsa_topk_workspace_size(Tq, Tk, k)
+
+
+def dsa_topk(scores, ld_scores, Tq, Tk, q_pos0, k, idx, ws=None, ws_bytes=0, stream=None):
+    _check(load_library().dsa_topk(_ptr(scores), ld_scores, Tq, Tk, q_pos0, k, _ptr(idx), _ptr(ws),
+                                   ws_bytes, _stream(stream)))
+
+
+def dsa_sparse_gqa_attn_workspace_size(Tq, k, Hq, d) -> int:
+    return load_library().dsa_sparse_gqa_attn_workspace_size(Tq, k, Hq, d)
+
+
+def dsa_sparse_gqa_attn(q, k, v, dtype, n_kv, block_table, max_blocks, block_size, row_seq,
+                        seq_lens, idx, Tq, topk, Hq, G, d, sm_scale, out, ws=None, ws_bytes=0,
+                        stream=None):
+    _check(load_library().dsa_sparse_gqa_attn(
+        _ptr(q), _ptr(k), _ptr(v), dtype, n_kv, _ptr(block_table), max_blocks, block_size,
+        _ptr(row_seq), _ptr(seq_lens), _ptr(idx), Tq, topk, Hq, G, d, float(sm_scale), _ptr(out),
+        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dsa_prefill_workspace_size(Tq, q_pos0, chunk_rows, topk) -> int:
+    return load_library().dsa_prefill_workspace_size(Tq, q_pos0, chunk_rows, topk)
+
+
+def dsa_prefill(q, k, v, dtype, q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, q_pos0, Hq, G,
+                d, HI, dI, topk, sm_scale, chunk_rows, out, idx_out, ws, ws_bytes, stream=None):
+    _check(load_library().dsa_prefill(
+        _ptr(q), _ptr(k), _ptr(v), dtype, _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx),
+        _ptr(k_scale), idx_dtype, Tq, q_pos0, Hq, G, d, HI, dI, topk, float(sm_scale), chunk_rows,
+        _ptr(out), _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dsa_decode_workspace_size(B, max_blocks, block_size, topk, Hq, d) -> int:
+    return load_library().dsa_decode_workspace_size(B, max_blocks, block_size, topk, Hq, d)
+
+
+def dsa_decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, dtype, block_table,
+               seq_lens, B, num_blocks, max_blocks, block_size, Hq, G, d, HI, dI, topk, sm_scale,
+               out, idx_out, ws, ws_bytes, stream=None):
+    _check(load_library().dsa_decode(
+        _ptr(q), _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(kidx_cache), _ptr(kidx_scale),
+        _ptr(k_cache), _ptr(v_cache), dtype, _ptr(block_table), _ptr(seq_lens), B, num_blocks,
+        max_blocks, block_size, Hq, G, d, HI, dI, topk, float(sm_scale), _ptr(out), _ptr(idx_out),
+        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+# ------------------------------------------------------------ conveniences
+
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def index_scores(q_idx, q_scale, w, k_idx, k_scale, q_pos0=0, stream=None):
+    """Scores [Tq, ld] (fp32) of the lightning indexer; columns >= Tk are padding."""
+    import torch
+    Tq, HI, dI = q_idx.shape
+    Tk = k_idx.shape[0]
+    ld = (Tk + 3) // 4 * 4
+    scores = torch.empty(Tq, ld, dtype=torch.float32, device=q_idx.device)
+    dsa_index_scores(q_idx, q_scale, w, k_idx, k_scale, dtype_code(q_idx), Tq, Tk, HI, dI, q_pos0,
+                     scores, ld, stream)
+    return scores
+
+
+def topk(scores, Tk, k, q_pos0=0, stream=None):
+    import torch
+    Tq, ld = scores.shape
+    idx = torch.empty(Tq, k, dtype=torch.int32, device=scores.device)
+    n = dsa_topk_workspace_size(Tq, Tk, k)
+    ws = workspace(n, scores.device) if n else None
+    dsa_topk(scores, ld, Tq, Tk, q_pos0, k, idx, ws, n, stream)
+    return idx
+
+
+def sparse_gqa_attn(q, k, v, idx, G, sm_scale, block_table=None, block_size=0, row_seq=None,
+                    seq_lens=None, split=True, stream=None):
+    import torch
+    Tq, Hq, d = q.shape
+    topk_ = idx.shape[1]
+    out = torch.empty_like(q)
+    n_kv = k.shape[0]
+    max_blocks = block_table.shape[1] if block_table is not None else 0
+    n = dsa_sparse_gqa_attn_workspace_size(Tq, topk_, Hq, d) if split else 0
+    ws = workspace(n, q.device) if n else None
+    dsa_sparse_gqa_attn(q, k, v, dtype_code(q), n_kv, block_table, max_blocks, block_size, row_seq,
+                        seq_lens, idx, Tq, topk_, Hq, G, d, sm_scale, out, ws, n, stream)
+    return out
+
+
+def prefill(q, k, v, q_idx, q_scale, w, k_idx, k_scale, topk, sm_scale, chunk_rows=0, q_pos0=0,
+            return_idx=False, ws=None, stream=None):
+    """Fused DSA prefill; returns out (and idx if return_idx)."""
+    import torch
+    Tq, Hq, d = q.shape
+    G = k.shape[1]
+    _, HI, dI = q_idx.shape
+    out = torch.empty_like(q)
+    idx = torch.empty(Tq, topk, dtype=torch.int32, device=q.device) if return_idx else None
+    n = dsa_prefill_workspace_size(Tq, q_pos0, chunk_rows, topk)
+    if ws is None or ws.numel() < n:
+        ws = workspace(n, q.device)
+    dsa_prefill(q, k, v, dtype_code(q), q_idx, q_scale, w, k_idx, k_scale, dtype_code(q_idx), Tq,
+                q_pos0, Hq, G, d, HI, dI, topk, sm_scale, chunk_rows, out, idx, ws, ws.numel(),
+                stream)
+    return (out, idx) if return_idx else out
+
+
+def decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, block_table, seq_lens,
+           topk, sm_scale, return_idx=False, ws=None, stream=None):
+    """One paged DSA decode step; returns out (and idx if return_idx)."""
+    import torch
+    B, Hq, d = q.shape
+    _, HI, dI = q_idx.shape
+    NB, bs, G, _ = k_cache.shape
+    max_blocks = block_table.shape[1]
+    out = torch.empty_like(q)
+    idx = torch.empty(B, topk, dtype=torch.int32, device=q.device) if return_idx else None
+    n = dsa_decode_workspace_size(B, max_blocks, bs, topk, Hq, d)
+    if ws is None or ws.numel() < n:
+        ws = workspace(n, q.device)
+    dsa_decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, dtype_code(q),
+               block_table, seq_lens, B, NB, max_blocks, bs, Hq, G, d, HI, dI, topk, sm_scale, out,
+               idx, ws, ws.numel(), stream)
+    return (out, idx) if return_idx else out

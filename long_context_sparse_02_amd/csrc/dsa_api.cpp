@@ -1,0 +1,362 @@
+// dsa_api.cpp -- C entry points of libdsa: argument checks, workspace
+// planning and the chunked prefill / paged decode drivers.  Every check runs
+// on the host before anything is queued; all work goes onto the caller's
+// stream with no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "internal.h"
+
+#define DSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512];
+
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+dsa_status_t hip_fail(hipError_t e, const char* what) {
+    return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+#define REQUIRE(cond, st, ...) \
+    do { if (!(cond)) return fail(st, __VA_ARGS__); } while (0)
+#define REQUIRE_PTR(p) \
+    do { \
+        if (!(p)) return fail(DSA_ERR_INVALID_ARG, "%s is NULL", #p); \
+        if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+    } while (0)
+// scalar-accessed arrays (scales, index lists, block tables) need only 4-byte alignment
+#define REQUIRE_PTR4(p) \
+    do { \
+        if (!(p)) return fail(DSA_ERR_INVALID_ARG, "%s is NULL", #p); \
+        if (!aligned4(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 4-byte aligned", #p); \
+    } while (0)
+#define REQUIRE_OPT_PTR4(p) \
+    do { if ((p) && !aligned4(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 4-byte aligned", #p); } while (0)
+#define REQUIRE_OPT_PTR(p) \
+    do { if ((p) && !aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); } while (0)
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ld_for(int64_t Tk) { return (Tk + 3) / 4 * 4; }
+
+dsa_status_t check_indexer(const void* q_idx, const float* q_scale, const float* w,
+                           const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype,
+                           int Tq, int Tk, int HI, int dI, int64_t q_pos0) {
+    REQUIRE(Tq >= 0 && Tk >= 0, DSA_ERR_INVALID_ARG, "negative size (Tq=%d, Tk=%d)", Tq, Tk);
+    REQUIRE(q_pos0 >= 0, DSA_ERR_INVALID_ARG, "q_pos0 must be >= 0 (got %lld)", (long long)q_pos0);
+    REQUIRE((int64_t)Tk >= q_pos0 + Tq, DSA_ERR_INVALID_ARG,
+            "Tk (%d) must cover every query's prefix (q_pos0 + Tq = %lld)", Tk,
+            (long long)(q_pos0 + Tq));
+    REQUIRE(HI >= 1, DSA_ERR_INVALID_ARG, "HI must be >= 1 (got %d)", HI);
+    REQUIRE_PTR(q_idx);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(k_idx);
+    if (idx_dtype == DSA_FP8_E4M3) {
+        REQUIRE(dI == 128, DSA_ERR_UNSUPPORTED, "FP8 indexer needs dI == 128 (got %d)", dI);
+        REQUIRE(HI <= 128 && HI % 4 == 0, DSA_ERR_UNSUPPORTED,
+                "FP8 indexer needs HI %% 4 == 0 and HI <= 128 (got %d)", HI);
+        REQUIRE_PTR4(q_scale);
+        REQUIRE_PTR4(k_scale);
+    } else if (idx_dtype == DSA_F32) {
+        REQUIRE(dI >= 4 && dI <= 128 && dI % 4 == 0, DSA_ERR_UNSUPPORTED,
+                "fp32 indexer needs dI %% 4 == 0 and 4 <= dI <= 128 (got %d)", dI);
+        REQUIRE((int64_t)HI * dI <= 1024, DSA_ERR_UNSUPPORTED,
+                "fp32 indexer needs HI * dI <= 1024 (got %d * %d)", HI, dI);
+    } else {
+        return fail(DSA_ERR_UNSUPPORTED, "indexer dtype %d is not FP8_E4M3 or F32", (int)idx_dtype);
+    }
+    return DSA_OK;
+}
+
+dsa_status_t run_indexer(const void* q_idx, const float* q_scale, const float* w,
+                         const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype, int Tq,
+                         int Tk, int HI, int dI, int64_t q_pos0, float* scores, int64_t ld,
+                         hipStream_t stream) {
+    hipError_t e;
+    if (idx_dtype == DSA_FP8_E4M3)
+        e = dsa::launch_index_fp8(static_cast<const uint8_t*>(q_idx), q_scale, w,
+                                  static_cast<const uint8_t*>(k_idx), k_scale, Tq, Tk, HI, q_pos0,
+                                  scores, ld, stream);
+    else
+        e = dsa::launch_index_f32(static_cast<const float*>(q_idx), w,
+                                  static_cast<const float*>(k_idx), Tq, Tk, HI, dI, q_pos0, scores,
+                                  ld, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer launch");
+}
+
+dsa_status_t check_attn_shape(dsa_dtype_t dtype, int Hq, int G, int d, int topk) {
+    REQUIRE(dtype == DSA_BF16 || dtype == DSA_F32, DSA_ERR_UNSUPPORTED,
+            "attention dtype %d is not BF16 or F32", (int)dtype);
+    REQUIRE(d == 128, DSA_ERR_UNSUPPORTED, "head size d must be 128 (got %d)", d);
+    REQUIRE(G >= 1 && Hq >= 1 && Hq % G == 0, DSA_ERR_INVALID_ARG,
+            "Hq (%d) must be a positive multiple of G (%d)", Hq, G);
+    REQUIRE(Hq / G <= 16, DSA_ERR_UNSUPPORTED, "at most 16 query heads per group (got %d)", Hq / G);
+    REQUIRE(topk >= 1 && topk <= 8192, DSA_ERR_INVALID_ARG, "topk must be in [1, 8192] (got %d)", topk);
+    return DSA_OK;
+}
+
+}  // namespace
+
+DSA_EXPORT const char* dsa_status_string(dsa_status_t s) {
+    switch (s) {
+        case DSA_OK: return "DSA_OK";
+        case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+        case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+        case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+        case DSA_ERR_HIP: return "DSA_ERR_HIP";
+    }
+    return "DSA_ERR_UNKNOWN";
+}
+
+DSA_EXPORT const char* dsa_last_error(void) { return g_err; }
+
+DSA_EXPORT int dsa_version(void) { return 10000; }
+
+DSA_EXPORT dsa_status_t dsa_index_scores(const void* q_idx, const float* q_scale, const float* w,
+                                         const void* k_idx, const float* k_scale,
+                                         dsa_dtype_t idx_dtype, int Tq, int Tk, int HI, int dI,
+                                         int64_t q_pos0, float* scores, int64_t ld_scores,
+                                         hipStream_t stream) {
+    g_err[0] = 0;
+    dsa_status_t st = check_indexer(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, q_pos0);
+    if (st != DSA_OK) return st;
+    REQUIRE_PTR(scores);
+    REQUIRE(ld_scores >= Tk && ld_scores % 4 == 0, DSA_ERR_INVALID_ARG,
+            "ld_scores (%lld) must be >= Tk (%d) and a multiple of 4", (long long)ld_scores, Tk);
+    return run_indexer(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, q_pos0, scores,
+                       ld_scores, stream);
+}
+
+DSA_EXPORT size_t dsa_topk_workspace_size(int Tq, int Tk, int k) {
+    (void)Tq; (void)Tk; (void)k;
+    return 0;
+}
+
+DSA_EXPORT dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int Tq, int Tk,
+                                 int64_t q_pos0, int k, int32_t* idx, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    g_err[0] = 0;
+    (void)ws; (void)ws_bytes;
+    REQUIRE(Tq >= 0 && Tk >= 0 && q_pos0 >= 0, DSA_ERR_INVALID_ARG, "negative size or position");
+    REQUIRE((int64_t)Tk >= q_pos0 + Tq, DSA_ERR_INVALID_ARG,
+            "Tk (%d) must cover every query's prefix (q_pos0 + Tq = %lld)", Tk, (long long)(q_pos0 + Tq));
+    REQUIRE(k >= 1 && k <= 8192, DSA_ERR_INVALID_ARG, "k must be in [1, 8192] (got %d)", k);
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR4(idx);
+    REQUIRE(ld_scores >= Tk && ld_scores % 4 == 0, DSA_ERR_INVALID_ARG,
+            "ld_scores (%lld) must be >= Tk (%d) and a multiple of 4", (long long)ld_scores, Tk);
+    hipError_t e = dsa::launch_topk(scores, ld_scores, Tq, Tk, q_pos0, nullptr, k, idx, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "top-k launch");
+}
+
+DSA_EXPORT size_t dsa_sparse_gqa_attn_workspace_size(int Tq, int k, int Hq, int d) {
+    if (Tq <= 0 || k <= 0 || Hq <= 0 || d <= 0) return 0;
+    return round_up(dsa::attn_partials_bytes(Tq, dsa::attn_num_splits(Tq, k), Hq, d));
+}
+
+namespace {
+
+dsa_status_t run_attn(const void* q, const void* k, const void* v, dsa_dtype_t dtype, int n_kv,
+                      const int32_t* block_table, int max_blocks, int block_size,
+                      const int32_t* row_seq, const int32_t* seq_lens, const int32_t* idx, int Tq,
+                      int topk, int Hq, int G, int d, float sm_scale, void* out, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+    dsa::AttnArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.idx = idx; a.Tq = Tq; a.topk = topk; a.Hq = Hq;
+    a.G = G; a.d = d; a.sm_scale = sm_scale; a.n_kv = n_kv; a.block_table = block_table;
+    a.max_blocks = max_blocks; a.block_size = block_size; a.row_seq = row_seq;
+    a.seq_lens = seq_lens; a.bf16 = dtype == DSA_BF16;
+    int nsplit = dsa::attn_num_splits(Tq, topk);
+    if (!ws || ws_bytes < dsa::attn_partials_bytes(Tq, nsplit, Hq, d)) nsplit = 1;
+    hipError_t e = dsa::launch_sparse_attn(a, nsplit, static_cast<float*>(ws), stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "attention launch");
+}
+
+}  // namespace
+
+DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn(const void* q, const void* k, const void* v,
+                                            dsa_dtype_t dtype, int n_kv, const int32_t* block_table,
+                                            int max_blocks, int block_size, const int32_t* row_seq,
+                                            const int32_t* seq_lens, const int32_t* idx, int Tq,
+                                            int topk, int Hq, int G, int d, float sm_scale,
+                                            void* out, void* ws, size_t ws_bytes,
+                                            hipStream_t stream) {
+    g_err[0] = 0;
+    dsa_status_t st = check_attn_shape(dtype, Hq, G, d, topk);
+    if (st != DSA_OK) return st;
+    REQUIRE(Tq >= 0 && n_kv >= 0, DSA_ERR_INVALID_ARG, "negative size (Tq=%d, n_kv=%d)", Tq, n_kv);
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR4(idx); REQUIRE_PTR(out);
+    REQUIRE_OPT_PTR(ws);
+    if (block_table) {
+        REQUIRE_PTR4(block_table);
+        REQUIRE_OPT_PTR4(row_seq);
+        REQUIRE_OPT_PTR4(seq_lens);
+        REQUIRE(max_blocks >= 1 && block_size >= 1, DSA_ERR_INVALID_ARG,
+                "paged K/V needs max_blocks >= 1 and block_size >= 1 (got %d, %d)", max_blocks, block_size);
+        REQUIRE((int64_t)n_kv * block_size < INT32_MAX, DSA_ERR_UNSUPPORTED,
+                "paged cache holds too many tokens (%lld)", (long long)n_kv * block_size);
+    }
+    return run_attn(q, k, v, dtype, n_kv, block_table, max_blocks, block_size, row_seq, seq_lens,
+                    idx, Tq, topk, Hq, G, d, sm_scale, out, ws, ws_bytes, stream);
+}
+
+namespace {
+
+struct PrefillPlan {
+    int chunk;
+    int64_t Tk;
+    int64_t ld;
+    size_t scores_bytes, idx_bytes, total;
+};
+
+PrefillPlan plan_prefill(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
+    PrefillPlan p;
+    p.chunk = (chunk_rows <= 0 || chunk_rows > Tq) ? Tq : chunk_rows;
+    p.Tk = q_pos0 + Tq;
+    p.ld = ld_for(p.Tk);
+    p.scores_bytes = round_up((size_t)p.chunk * p.ld * sizeof(float));
+    p.idx_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
+    p.total = p.scores_bytes + p.idx_bytes;
+    return p;
+}
+
+}  // namespace
+
+DSA_EXPORT size_t dsa_prefill_workspace_size(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
+    if (Tq <= 0 || q_pos0 < 0 || topk <= 0) return 0;
+    return plan_prefill(Tq, q_pos0, chunk_rows, topk).total;
+}
+
+DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_t dtype,
+                                    const void* q_idx, const float* q_scale, const float* w,
+                                    const void* k_idx, const float* k_scale,
+                                    dsa_dtype_t idx_dtype, int Tq, int64_t q_pos0, int Hq, int G,
+                                    int d, int HI, int dI, int topk, float sm_scale,
+                                    int chunk_rows, void* out, int32_t* idx_out, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    REQUIRE(Tq >= 0 && q_pos0 >= 0, DSA_ERR_INVALID_ARG, "negative size or position");
+    REQUIRE(q_pos0 + Tq <= INT32_MAX - 4, DSA_ERR_UNSUPPORTED, "sequence too long");
+    const int Tk = (int)(q_pos0 + Tq);
+    dsa_status_t st = check_indexer(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, q_pos0);
+    if (st != DSA_OK) return st;
+    st = check_attn_shape(dtype, Hq, G, d, topk);
+    if (st != DSA_OK) return st;
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(out);
+    REQUIRE_OPT_PTR4(idx_out);
+    if (Tq == 0) return DSA_OK;
+    const PrefillPlan plan = plan_prefill(Tq, q_pos0, chunk_rows, topk);
+    REQUIRE(ws && aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
+            "prefill needs %zu workspace bytes (got %zu%s)", plan.total, ws_bytes,
+            ws ? "" : ", ws is NULL");
+    float* scores = static_cast<float*>(ws);
+    int32_t* idx_ws = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.scores_bytes);
+    const size_t qrow = (size_t)Hq * d * (dtype == DSA_BF16 ? 2 : 4);
+    const size_t qirow = (size_t)HI * dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
+    for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
+        const int rows = (Tq - r0 < plan.chunk) ? Tq - r0 : plan.chunk;
+        const int64_t pos0 = q_pos0 + r0;
+        const int tk = (int)(pos0 + rows);                     // keys this chunk can see
+        st = run_indexer(static_cast<const char*>(q_idx) + r0 * qirow,
+                         q_scale ? q_scale + r0 : nullptr, w + (int64_t)r0 * HI, k_idx, k_scale,
+                         idx_dtype, rows, tk, HI, dI, pos0, scores, plan.ld, stream);
+        if (st != DSA_OK) return st;
+        int32_t* idx_c = idx_out ? idx_out + (int64_t)r0 * topk : idx_ws;
+        hipError_t e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c, stream);
+        if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        st = run_attn(static_cast<const char*>(q) + r0 * qrow, k, v, dtype, tk, nullptr, 0, 0,
+                      nullptr, nullptr, idx_c, rows, topk, Hq, G, d, sm_scale,
+                      static_cast<char*>(out) + r0 * qrow, nullptr, 0, stream);
+        if (st != DSA_OK) return st;
+    }
+    return DSA_OK;
+}
+
+namespace {
+
+struct DecodePlan {
+    int64_t ld;
+    int nsplit;
+    size_t scores_bytes, idx_bytes, part_bytes, total;
+};
+
+DecodePlan plan_decode(int B, int max_blocks, int block_size, int topk, int Hq, int d) {
+    DecodePlan p;
+    p.ld = ld_for((int64_t)max_blocks * block_size);
+    p.scores_bytes = round_up((size_t)B * p.ld * sizeof(float));
+    p.idx_bytes = round_up((size_t)B * topk * sizeof(int32_t));
+    p.nsplit = dsa::attn_num_splits(B, topk);
+    p.part_bytes = round_up(dsa::attn_partials_bytes(B, p.nsplit, Hq, d));
+    p.total = p.scores_bytes + p.idx_bytes + p.part_bytes;
+    return p;
+}
+
+}  // namespace
+
+DSA_EXPORT size_t dsa_decode_workspace_size(int B, int max_blocks, int block_size, int topk,
+                                            int Hq, int d) {
+    if (B <= 0 || max_blocks <= 0 || block_size <= 0 || topk <= 0 || Hq <= 0 || d <= 0) return 0;
+    return plan_decode(B, max_blocks, block_size, topk, Hq, d).total;
+}
+
+DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float* q_scale,
+                                   const float* w, const void* kidx_cache, const float* kidx_scale,
+                                   const void* k_cache, const void* v_cache, dsa_dtype_t dtype,
+                                   const int32_t* block_table, const int32_t* seq_lens, int B,
+                                   int num_blocks, int max_blocks, int block_size, int Hq, int G,
+                                   int d, int HI, int dI, int topk, float sm_scale, void* out,
+                                   int32_t* idx_out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    g_err[0] = 0;
+    REQUIRE(B >= 0 && num_blocks >= 0, DSA_ERR_INVALID_ARG, "negative size (B=%d, num_blocks=%d)", B, num_blocks);
+    REQUIRE(max_blocks >= 1 && block_size >= 1, DSA_ERR_INVALID_ARG,
+            "max_blocks and block_size must be >= 1 (got %d, %d)", max_blocks, block_size);
+    REQUIRE((int64_t)max_blocks * block_size <= INT32_MAX - 4, DSA_ERR_UNSUPPORTED,
+            "max_blocks * block_size too large");
+    REQUIRE((int64_t)num_blocks * block_size < INT32_MAX, DSA_ERR_UNSUPPORTED,
+            "paged cache holds too many tokens");
+    REQUIRE(dI == 128, DSA_ERR_UNSUPPORTED, "decode indexer needs dI == 128 (got %d)", dI);
+    REQUIRE(HI >= 1 && HI <= 128 && HI % 4 == 0, DSA_ERR_UNSUPPORTED,
+            "decode indexer needs HI %% 4 == 0 and HI <= 128 (got %d)", HI);
+    dsa_status_t st = check_attn_shape(dtype, Hq, G, d, topk);
+    if (st != DSA_OK) return st;
+    REQUIRE_PTR(q); REQUIRE_PTR(q_idx); REQUIRE_PTR4(q_scale); REQUIRE_PTR(w);
+    REQUIRE_PTR(kidx_cache); REQUIRE_PTR4(kidx_scale); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
+    REQUIRE_PTR4(block_table); REQUIRE_PTR4(seq_lens); REQUIRE_PTR(out);
+    REQUIRE_OPT_PTR4(idx_out);
+    if (B == 0) return DSA_OK;
+    const DecodePlan plan = plan_decode(B, max_blocks, block_size, topk, Hq, d);
+    REQUIRE(ws && aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
+            "decode needs %zu workspace bytes (got %zu%s)", plan.total, ws_bytes, ws ? "" : ", ws is NULL");
+    char* base = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(base);
+    int32_t* idx_c = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + plan.scores_bytes);
+    float* partials = reinterpret_cast<float*>(base + plan.scores_bytes + plan.idx_bytes);
+    const int cap = max_blocks * block_size;
+
+    hipError_t e = dsa::launch_index_fp8_paged(
+        static_cast<const uint8_t*>(q_idx), q_scale, w, static_cast<const uint8_t*>(kidx_cache),
+        kidx_scale, block_table, seq_lens, B, num_blocks, max_blocks, block_size, HI, scores,
+        plan.ld, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
+    e = dsa::launch_topk(scores, plan.ld, B, cap, 0, seq_lens, topk, idx_c, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode top-k launch");
+    return run_attn(q, k_cache, v_cache, dtype, num_blocks, block_table, max_blocks, block_size,
+                    nullptr, seq_lens, idx_c, B, topk, Hq, G, d, sm_scale, out, partials,
+                    plan.part_bytes, stream);
+}

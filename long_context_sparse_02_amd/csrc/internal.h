@@ -1,0 +1,43 @@
+// internal.h -- launchers shared between the libdsa translation units.
+// Each launcher queues one kernel on `stream` and returns the launch status;
+// arguments have already been validated by the C entry points.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Lightning indexer, contiguous keys (prefill).  Row i is position q_pos0 + i.
+hipError_t launch_index_fp8(const uint8_t* q_idx, const float* q_scale, const float* w,
+                            const uint8_t* k_idx, const float* k_scale, int Tq, int Tk, int HI,
+                            int64_t q_pos0, float* scores, int64_t ld, hipStream_t stream);
+hipError_t launch_index_f32(const float* q_idx, const float* w, const float* k_idx, int Tq,
+                            int Tk, int HI, int dI, int64_t q_pos0, float* scores, int64_t ld,
+                            hipStream_t stream);
+// Lightning indexer over a paged key cache, one query per sequence (decode).
+// scores [B, ld]; entries s >= seq_len are left unwritten.
+hipError_t launch_index_fp8_paged(const uint8_t* q_idx, const float* q_scale, const float* w,
+                                  const uint8_t* kidx_cache, const float* kidx_scale,
+                                  const int32_t* block_table, const int32_t* seq_lens, int B,
+                                  int num_blocks, int max_blocks, int block_size, int HI,
+                                  float* scores, int64_t ld, hipStream_t stream);
+
+// Top-k per row.  Candidates of row i: 0 .. n_i-1 with n_i = q_pos0 + i + 1, or
+// n_i = clamp(row_len[i], 0, Tk) when row_len is given.
+hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t q_pos0,
+                       const int32_t* row_len, int k, int32_t* idx, hipStream_t stream);
+
+struct AttnArgs {
+    const void* q; const void* k; const void* v; void* out;
+    const int32_t* idx; int Tq; int topk; int Hq; int G; int d; float sm_scale;
+    int n_kv;                                  // contiguous rows, or physical blocks
+    const int32_t* block_table; int max_blocks; int block_size;
+    const int32_t* row_seq; const int32_t* seq_lens;
+    int bf16;                                  // 1: bf16 I/O, 0: fp32 I/O
+};
+// Splits used for a given shape when a workspace is available (1 = no split).
+int attn_num_splits(int Tq, int topk);
+size_t attn_partials_bytes(int Tq, int nsplit, int Hq, int d);
+hipError_t launch_sparse_attn(const AttnArgs& a, int nsplit, float* partials, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,139 @@
+"""The C-ABI boundary on the host: exports, workspace sizing and argument checks.
+
+No kernel runs here: every call below fails validation, which happens on the
+host before anything is queued (fake, never-dereferenced device addresses).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_02_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+A = 0x10000          # a 16-byte aligned fake device address
+MIS = 0x10004        # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dsa.LIB_PATH):
+        from long_context_sparse_02_amd import build
+        build.build()
+    return dsa.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(dsa.EXPORTS)
+
+
+def test_status_strings_and_version(lib):
+    for code, name in dsa.STATUS.items():
+        assert lib.dsa_status_string(code).decode() == name
+    assert lib.dsa_version() >= 10000
+
+
+def _st(lib, fn, *args):
+    return getattr(lib, fn)(*args)
+
+
+def test_index_scores_argument_checks(lib):
+    f = lib.dsa_index_scores
+    ok = [A, A, A, A, A, dsa.DSA_FP8_E4M3, 16, 16, 64, 128, 0, A, 16, None]
+    assert f(*ok[:0], None, *ok[1:]) == 1                      # NULL q_idx
+    assert b"q_idx" in lib.dsa_last_error()
+    bad = list(ok); bad[0] = MIS
+    assert f(*bad) == 1 and b"aligned" in lib.dsa_last_error()
+    bad = list(ok); bad[9] = 64
+    assert f(*bad) == 2                                         # FP8 needs dI = 128
+    bad = list(ok); bad[8] = 6
+    assert f(*bad) == 2                                         # HI % 4
+    bad = list(ok); bad[7] = 15
+    assert f(*bad) == 1                                         # Tk < q_pos0 + Tq
+    bad = list(ok); bad[10] = 3
+    assert f(*bad) == 1
+    bad = list(ok); bad[12] = 14
+    assert f(*bad) == 1                                         # ld < Tk
+    bad = list(ok); bad[12] = 18
+    assert f(*bad) == 1                                         # ld % 4
+    bad = list(ok); bad[5] = dsa.DSA_BF16
+    assert f(*bad) == 2                                         # bf16 indexer unsupported
+    bad = list(ok); bad[1] = None
+    assert f(*bad) == 1                                         # FP8 needs scales
+    bad = list(ok); bad[5] = dsa.DSA_F32; bad[9] = 64; bad[8] = 32
+    assert f(*bad) == 2                                         # fp32: HI * dI > 1024
+
+
+def test_topk_argument_checks(lib):
+    f = lib.dsa_topk
+    ok = [A, 16, 8, 16, 8, 4, A, None, 0, None]
+    bad = list(ok); bad[5] = 0
+    assert f(*bad) == 1
+    bad = list(ok); bad[5] = 8193
+    assert f(*bad) == 1
+    bad = list(ok); bad[3] = 15
+    assert f(*bad) == 1
+    bad = list(ok); bad[6] = None
+    assert f(*bad) == 1
+    bad = list(ok); bad[1] = 17
+    assert f(*bad) == 1
+    assert lib.dsa_topk_workspace_size(8, 16, 4) == 0
+
+
+def test_attention_argument_checks(lib):
+    f = lib.dsa_sparse_gqa_attn
+    ok = [A, A, A, dsa.DSA_BF16, 100, None, 0, 0, None, None, A, 4, 16, 32, 4, 128, 0.1, A, None, 0, None]
+    bad = list(ok); bad[15] = 64
+    assert f(*bad) == 2                                         # d != 128
+    bad = list(ok); bad[13] = 30
+    assert f(*bad) == 1                                         # Hq % G
+    bad = list(ok); bad[13] = 68
+    assert f(*bad) == 2                                         # > 16 heads per group
+    bad = list(ok); bad[3] = dsa.DSA_FP8_E4M3
+    assert f(*bad) == 2
+    bad = list(ok); bad[12] = 0
+    assert f(*bad) == 1
+    bad = list(ok); bad[5] = A; bad[6] = 0
+    assert f(*bad) == 1                                         # paged without max_blocks
+    bad = list(ok); bad[17] = MIS
+    assert f(*bad) == 1
+
+
+def test_prefill_and_decode_workspace_checks(lib):
+    n = lib.dsa_prefill_workspace_size(1000, 0, 256, 64)
+    assert n >= 256 * 1000 * 4 + 256 * 64 * 4
+    assert lib.dsa_prefill_workspace_size(1000, 0, 0, 64) >= 1000 * 1000 * 4
+    f = lib.dsa_prefill
+    args = [A, A, A, dsa.DSA_BF16, A, A, A, A, A, dsa.DSA_FP8_E4M3, 1000, 0, 32, 4, 128, 64, 128,
+            64, 0.1, 256, A, None, A, n - 1, None]
+    assert f(*args) == 3 and b"workspace" in lib.dsa_last_error()
+    args[22] = None
+    assert f(*args) == 3
+    nd = lib.dsa_decode_workspace_size(64, 4096, 64, 2048, 32, 128)
+    assert nd >= 64 * 4096 * 64 * 4
+    fd = lib.dsa_decode
+    dargs = [A, A, A, A, A, A, A, A, dsa.DSA_BF16, A, A, 64, 1000, 4096, 64, 32, 4, 128, 64, 128,
+             2048, 0.1, A, None, A, nd - 16, None]
+    assert fd(*dargs) == 3
+    dargs[19] = 64
+    assert fd(*dargs) == 2                                      # decode dI must be 128
+    dargs[19] = 128; dargs[10] = None
+    assert fd(*dargs) == 1                                      # seq_lens NULL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        dsa._ptr(x)
