@@ -83,6 +83,8 @@ def run_prefill_bench(args, dsa, W, torch):
     stream = torch.cuda.current_stream()
     s_ptr = stream.cuda_stream
     n_chunks = (L + C - 1) // C
+    iws_n = dsa.dsa_index_scores_workspace_size(C, cfg.HI, cfg.dI, dsa.DSA_FP8_E4M3)
+    iws = dsa.workspace(iws_n)
 
     def step(events=None):
         for c, r0 in enumerate(range(0, L, C)):
@@ -92,7 +94,8 @@ def run_prefill_bench(args, dsa, W, torch):
             ev = events[c] if events else None
             if ev: ev[0].record(stream)
             dsa.dsa_index_scores(x["q_idx"][sl], x["q_scale"][sl], x["w"][sl], x["k_idx"], x["k_scale"],
-                                 dsa.DSA_FP8_E4M3, rows, tk, cfg.HI, cfg.dI, r0, scores, ld, stream)
+                                 dsa.DSA_FP8_E4M3, rows, tk, cfg.HI, cfg.dI, r0, scores, ld, iws,
+                                 iws_n, stream)
             if ev: ev[1].record(stream)
             dsa.dsa_topk(scores, ld, rows, tk, r0, k, idx[sl], None, 0, stream)
             if ev: ev[2].record(stream)

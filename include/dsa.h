@@ -79,11 +79,17 @@ int dsa_version(void);
  *   ignored (may be NULL); dI % 4 == 0, dI <= 128, HI * dI <= 1024.
  * w: float [Tq, HI], any sign.  scores: float, row stride ld_scores >= Tk,
  *   ld_scores % 4 == 0.  Requires Tk >= q_pos0 + Tq (every query sees its prefix).
+ * Workspace: dsa_index_scores_workspace_size() bytes of device memory (the FP8
+ *   path keeps a per-token mix of the w-weighted indexer queries there: 512 bytes
+ *   per query row; the fp32 path needs none and ws may be NULL).  The scores
+ *   are computed as sum_j w ReLU(x_j) = 1/2 (sum_j w_j x_j + sum_j w_j |x_j|).
  */
+size_t dsa_index_scores_workspace_size(int Tq, int HI, int dI, dsa_dtype_t idx_dtype);
 dsa_status_t dsa_index_scores(const void* q_idx, const float* q_scale, const float* w,
                               const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype,
                               int Tq, int Tk, int HI, int dI, int64_t q_pos0,
-                              float* scores, int64_t ld_scores, hipStream_t stream);
+                              float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /*
  * Top-k index set (review page "核心公式", second formula; k = 2048 in the

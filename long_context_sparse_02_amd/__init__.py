@@ -25,7 +25,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "D
           4: "DSA_ERR_HIP"}
 
 # every symbol the header declares, in declaration order
-EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version", "dsa_index_scores",
+EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
+           "dsa_index_scores_workspace_size", "dsa_index_scores",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_gqa_attn_workspace_size",
            "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill",
            "dsa_decode_workspace_size", "dsa_decode"]
@@ -58,7 +59,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_status_string": ([I], ctypes.c_char_p),
             "dsa_last_error": ([], ctypes.c_char_p),
             "dsa_version": ([], I),
-            "dsa_index_scores": ([P, P, P, P, P, I, I, I, I, I, I64, P, I64, P], I),
+            "dsa_index_scores_workspace_size": ([I, I, I, I], SZ),
+            "dsa_index_scores": ([P, P, P, P, P, I, I, I, I, I, I64, P, I64, P, SZ, P], I),
             "dsa_topk_workspace_size": ([I, I, I], SZ),
             "dsa_topk": ([P, I64, I, I, I64, I, P, P, SZ, P], I),
             "dsa_sparse_gqa_attn_workspace_size": ([I, I, I, I], SZ),
@@ -111,11 +113,16 @@ def dsa_version() -> int:
     return load_library().dsa_version()
 
 
+def dsa_index_scores_workspace_size(Tq, HI, dI, idx_dtype) -> int:
+    return load_library().dsa_index_scores_workspace_size(Tq, HI, dI, idx_dtype)
+
+
 def dsa_index_scores(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, q_pos0, scores,
-                     ld_scores, stream=None):
+                     ld_scores, ws=None, ws_bytes=0, stream=None):
     _check(load_library().dsa_index_scores(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx),
                                            _ptr(k_scale), idx_dtype, Tq, Tk, HI, dI, q_pos0,
-                                           _ptr(scores), ld_scores, _stream(stream)))
+                                           _ptr(scores), ld_scores, _ptr(ws), ws_bytes,
+                                           _stream(stream)))
 
 
 def dsa_topk_workspace_size(Tq, Tk, k) -> int:
@@ -180,8 +187,10 @@ def index_scores(q_idx, q_scale, w, k_idx, k_scale, q_pos0=0, stream=None):
     Tk = k_idx.shape[0]
     ld = (Tk + 3) // 4 * 4
     scores = torch.empty(Tq, ld, dtype=torch.float32, device=q_idx.device)
+    n = dsa_index_scores_workspace_size(Tq, HI, dI, dtype_code(q_idx))
+    ws = workspace(n, q_idx.device) if n else None
     dsa_index_scores(q_idx, q_scale, w, k_idx, k_scale, dtype_code(q_idx), Tq, Tk, HI, dI, q_pos0,
-                     scores, ld, stream)
+                     scores, ld, ws, n, stream)
     return scores
 
 

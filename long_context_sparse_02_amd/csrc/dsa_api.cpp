@@ -83,15 +83,19 @@ dsa_status_t check_indexer(const void* q_idx, const float* q_scale, const float*
     return DSA_OK;
 }
 
+size_t indexer_ws_bytes(int Tq, dsa_dtype_t idx_dtype) {
+    return idx_dtype == DSA_FP8_E4M3 ? round_up(dsa::index_fp8_workspace_bytes(Tq)) : 0;
+}
+
 dsa_status_t run_indexer(const void* q_idx, const float* q_scale, const float* w,
                          const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype, int Tq,
                          int Tk, int HI, int dI, int64_t q_pos0, float* scores, int64_t ld,
-                         hipStream_t stream) {
+                         void* ws, hipStream_t stream) {
     hipError_t e;
     if (idx_dtype == DSA_FP8_E4M3)
         e = dsa::launch_index_fp8(static_cast<const uint8_t*>(q_idx), q_scale, w,
                                   static_cast<const uint8_t*>(k_idx), k_scale, Tq, Tk, HI, q_pos0,
-                                  scores, ld, stream);
+                                  scores, ld, ws, stream);
     else
         e = dsa::launch_index_f32(static_cast<const float*>(q_idx), w,
                                   static_cast<const float*>(k_idx), Tq, Tk, HI, dI, q_pos0, scores,
@@ -127,19 +131,30 @@ DSA_EXPORT const char* dsa_last_error(void) { return g_err; }
 
 DSA_EXPORT int dsa_version(void) { return 10000; }
 
+DSA_EXPORT size_t dsa_index_scores_workspace_size(int Tq, int HI, int dI, dsa_dtype_t idx_dtype) {
+    (void)HI; (void)dI;
+    if (Tq <= 0) return 0;
+    return indexer_ws_bytes(Tq, idx_dtype);
+}
+
 DSA_EXPORT dsa_status_t dsa_index_scores(const void* q_idx, const float* q_scale, const float* w,
                                          const void* k_idx, const float* k_scale,
                                          dsa_dtype_t idx_dtype, int Tq, int Tk, int HI, int dI,
                                          int64_t q_pos0, float* scores, int64_t ld_scores,
-                                         hipStream_t stream) {
+                                         void* ws, size_t ws_bytes, hipStream_t stream) {
     g_err[0] = 0;
     dsa_status_t st = check_indexer(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, q_pos0);
     if (st != DSA_OK) return st;
     REQUIRE_PTR(scores);
     REQUIRE(ld_scores >= Tk && ld_scores % 4 == 0, DSA_ERR_INVALID_ARG,
             "ld_scores (%lld) must be >= Tk (%d) and a multiple of 4", (long long)ld_scores, Tk);
+    const size_t need = indexer_ws_bytes(Tq, idx_dtype);
+    if (need) {
+        REQUIRE(ws && aligned16(ws) && ws_bytes >= need, DSA_ERR_WORKSPACE,
+                "indexer needs %zu workspace bytes (got %zu%s)", need, ws_bytes, ws ? "" : ", ws is NULL");
+    }
     return run_indexer(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, q_pos0, scores,
-                       ld_scores, stream);
+                       ld_scores, ws, stream);
 }
 
 DSA_EXPORT size_t dsa_topk_workspace_size(int Tq, int Tk, int k) {
@@ -221,9 +236,11 @@ struct PrefillPlan {
     int chunk;
     int64_t Tk;
     int64_t ld;
-    size_t scores_bytes, idx_bytes, total;
+    size_t scores_bytes, idx_bytes, index_bytes, total;
 };
 
+// The workspace holds one chunk's scores, its index sets, and the indexer's scratch
+// (sized for FP8, the larger of the two indexer paths).
 PrefillPlan plan_prefill(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
     PrefillPlan p;
     p.chunk = (chunk_rows <= 0 || chunk_rows > Tq) ? Tq : chunk_rows;
@@ -231,7 +248,8 @@ PrefillPlan plan_prefill(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
     p.ld = ld_for(p.Tk);
     p.scores_bytes = round_up((size_t)p.chunk * p.ld * sizeof(float));
     p.idx_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
-    p.total = p.scores_bytes + p.idx_bytes;
+    p.index_bytes = indexer_ws_bytes(p.chunk, DSA_FP8_E4M3);
+    p.total = p.scores_bytes + p.idx_bytes + p.index_bytes;
     return p;
 }
 
@@ -266,6 +284,7 @@ DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v,
             ws ? "" : ", ws is NULL");
     float* scores = static_cast<float*>(ws);
     int32_t* idx_ws = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.scores_bytes);
+    void* index_ws = static_cast<char*>(ws) + plan.scores_bytes + plan.idx_bytes;
     const size_t qrow = (size_t)Hq * d * (dtype == DSA_BF16 ? 2 : 4);
     const size_t qirow = (size_t)HI * dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
     for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
@@ -274,7 +293,7 @@ DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v,
         const int tk = (int)(pos0 + rows);                     // keys this chunk can see
         st = run_indexer(static_cast<const char*>(q_idx) + r0 * qirow,
                          q_scale ? q_scale + r0 : nullptr, w + (int64_t)r0 * HI, k_idx, k_scale,
-                         idx_dtype, rows, tk, HI, dI, pos0, scores, plan.ld, stream);
+                         idx_dtype, rows, tk, HI, dI, pos0, scores, plan.ld, index_ws, stream);
         if (st != DSA_OK) return st;
         int32_t* idx_c = idx_out ? idx_out + (int64_t)r0 * topk : idx_ws;
         hipError_t e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c, stream);

@@ -7,16 +7,31 @@
 // FP8 prefill kernel: the dot products run on the 16x16x128 FP8 matrix core
 // with d_I = 128 as the whole contraction.  A (rows) = 16 keys, B (columns) =
 // 16 query tokens for one indexer head j, so each lane's four results are four
-// keys of ONE token and the head loop (ReLU, w-weighted sum) stays inside the
-// lane: no cross-lane reduction.  The per-token scales factor out of the ReLU
-// (they are positive) and are applied once in the epilogue.
+// keys of ONE token and the head loop stays inside the lane: no cross-lane
+// reduction.  The per-token scales factor out of the ReLU (they are positive)
+// and are applied once in the epilogue.
+//
+// The head sum is evaluated through ReLU(x) = (x + |x|) / 2:
+//   sum_j w_j ReLU(x_j) = 1/2 (qmix . k) + 1/2 sum_j w_j |x_j|,
+//   qmix = sum_j w_j q_j  (the w-weighted mix of the token's indexer queries).
+// The first term is one dot product per (token, key) pair for all heads; a
+// pre-pass builds qmix per token as a bf16 hi + lo pair (about 16 significant
+// bits) and the main kernel seeds its accumulators with it on the bf16 matrix
+// core (keys are exact in bf16).  The second term then costs ONE vector
+// instruction per product, an fma with an |x| source modifier, instead of a
+// max and an fma.  On gfx950 a wave's vector ALU work does not overlap its own
+// matrix-core work, so halving it is worth about 1.3x on this kernel.
 //
 // A wave keeps its NK key tiles (16*NK keys, 8 VGPRs each) in registers for the
-// whole head loop and streams one 32-byte slice of q^I per lane per head, which
-// the four waves of a workgroup (same 16 tokens, different keys) share through
-// L1/L2.  Work items are ordered token-tile-major and mapped so that
-// consecutive items run on one XCD: the key blocks of a token tile are
-// processed together and the tile's 128 KB of q^I stays in that XCD's L2.
+// whole head loop.  The four waves of a workgroup share the same 16 tokens, so
+// q^I is staged cooperatively in LDS, 8 heads (16 KB) at a time and
+// double-buffered: the next batch's global loads are in flight while the
+// current batch runs on the matrix cores.  Within a batch the loop is software
+// pipelined by one head: the MFMAs of head j are issued before the epilogue of
+// head j-1, whose results are then long complete.  Work items are ordered token-tile-major and
+// mapped so that consecutive items run on one XCD: the key blocks of a token
+// tile are processed together and the tile's 128 KB of q^I stays in that
+// XCD's L2.
 #include "device_common.h"
 #include "internal.h"
 
@@ -31,44 +46,103 @@ __device__ __forceinline__ v8i load32B(const uint8_t* p) {
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
+// Exact OCP E4M3 decode (bias 7, 3 mantissa bits; finite codes).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                        : (float)m * 0.001953125f;           // m * 2^-9
+    return (c & 0x80u) ? -mag : mag;
+}
+
+// qmix[t] = sum_j w[t,j] * fp8(q^I[t,j,:]) as bf16 hi [t][0][:] and lo [t][1][:]
+// (hi = RNE(qmix), lo = RNE(qmix - hi)).  One wave per token, two dims per lane.
+__global__ __launch_bounds__(256) void qmix_kernel(const uint8_t* __restrict__ q_idx,
+                                                   const float* __restrict__ w, int Tq, int HI,
+                                                   uint16_t* __restrict__ qmix)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= Tq) return;
+    const uint8_t* q = q_idx + (int64_t)t * HI * 128 + 2 * lane;
+    const float* wr = w + (int64_t)t * HI;
+    float s0 = 0.f, s1 = 0.f;
+    for (int j = 0; j < HI; ++j) {
+        const uint32_t two = *reinterpret_cast<const uint16_t*>(q + (int64_t)j * 128);
+        const float wj = wr[j];
+        s0 = fmaf(wj, e4m3_to_f32(two & 0xffu), s0);
+        s1 = fmaf(wj, e4m3_to_f32(two >> 8), s1);
+    }
+    const uint16_t h0 = f32_to_bf16_bits(s0), h1 = f32_to_bf16_bits(s1);
+    const uint16_t l0 = f32_to_bf16_bits(s0 - bf16_bits_to_f32(h0));
+    const uint16_t l1 = f32_to_bf16_bits(s1 - bf16_bits_to_f32(h1));
+    uint32_t* out = reinterpret_cast<uint32_t*>(qmix + (int64_t)t * 256);
+    out[lane] = h0 | ((uint32_t)h1 << 16);
+    out[64 + lane] = l0 | ((uint32_t)l1 << 16);
+}
+
+// Eight FP8 codes (bytes 8m .. 8m+7 of a key slice) as eight bf16 values (exact).
+__device__ __forceinline__ v8bf fp8x8_to_bf16(const v8i& a, int m) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const uint32_t d0 = (uint32_t)a[2 * m], d1 = (uint32_t)a[2 * m + 1];
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+constexpr int kHeadBatch = 8;            // indexer heads staged in LDS at a time
+constexpr int kQPitch = 144;             // LDS row pitch (bytes) of one token's 128 codes
+
 template <int NK>
-__global__ __launch_bounds__(256) void index_fp8_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void index_fp8_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
-    const float* __restrict__ k_scale, int Tq, int Tk, int HI, int64_t q_pos0,
-    float* __restrict__ scores, int64_t ld, int n_kb)
+    const float* __restrict__ k_scale, const uint16_t* __restrict__ qmix, int Tq, int Tk,
+    int HI, int64_t q_pos0, float* __restrict__ scores, int64_t ld, int n_kb)
 {
     constexpr int kKeysPerWave = 16 * NK;
     constexpr int kKeysPerWG = kIdxWaves * kKeysPerWave;
+    // q^I of the workgroup's 16 tokens for one batch of heads, double-buffered
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[2][kHeadBatch][16][kQPitch];
+    __shared__ float w_lds[2][kHeadBatch][16];
+
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     const int tt = work / n_kb;
     const int kb = work - tt * n_kb;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
 
-    const int t = tt * 16 + col;                      // this lane's query row
+    const int t0 = tt * 16;
+    const int t = t0 + col;                           // this lane's query row
     const bool t_ok = t < Tq;
     const int tc = t_ok ? t : Tq - 1;
     const int64_t pos = q_pos0 + t;
-    const int64_t pos_hi = q_pos0 + min(tt * 16 + 15, Tq - 1);
-    const int s_base = kb * kKeysPerWG + wave * kKeysPerWave;
+    const int64_t pos_hi = q_pos0 + min(t0 + 15, Tq - 1);
+    const int wg_base = kb * kKeysPerWG;
+    const int s_base = wg_base + wave * kKeysPerWave;
     float* __restrict__ out_row = scores + (int64_t)tc * ld;
-    if (s_base >= Tk) return;
+    // a wave tile entirely above the diagonal (or past Tk) only writes -inf
+    const bool active = s_base < Tk && (int64_t)s_base <= pos_hi;
 
-    if ((int64_t)s_base > pos_hi) {                   // tile entirely above the diagonal
-        if (t_ok) {
+    auto fill_masked = [&]() {
+        if (!t_ok || s_base >= Tk) return;
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                const int s0 = s_base + 16 * i + 4 * grp;
-                if (s0 + 3 < Tk) {
-                    *reinterpret_cast<float4*>(out_row + s0) =
-                        make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                } else {
-                    for (int e = 0; e < 4; ++e)
-                        if (s0 + e < Tk) out_row[s0 + e] = -INFINITY;
-                }
+        for (int i = 0; i < NK; ++i) {
+            const int s0 = s_base + 16 * i + 4 * grp;
+            if (s0 + 3 < Tk) {
+                *reinterpret_cast<float4*>(out_row + s0) =
+                    make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            } else {
+                for (int e = 0; e < 4; ++e)
+                    if (s0 + e < Tk) out_row[s0 + e] = -INFINITY;
             }
         }
+    };
+    if ((int64_t)wg_base > pos_hi) {                  // uniform over the workgroup
+        fill_masked();
         return;
     }
 
@@ -77,38 +151,113 @@ __global__ __launch_bounds__(256) void index_fp8_kernel(
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
         const int s = s_base + 16 * i + col;
-        a[i] = (s < Tk) ? load32B(k_idx + (int64_t)s * 128 + grp * 32) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        a[i] = (active && s < Tk) ? load32B(k_idx + (int64_t)s * 128 + grp * 32)
+                                  : v8i{0, 0, 0, 0, 0, 0, 0, 0};
     }
 
-    float acc[NK][4];
+    // cooperative staging of one head batch: 1024 16-byte chunks, 4 per thread
+    const int n_batch = (HI + kHeadBatch - 1) / kHeadBatch;
+    v4i stage[4];
+    float wstage = 0.f;
+    auto load_batch = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i)
-        for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int id = tid + 256 * i;
+            const int c = id & 7, tok = (id >> 3) & 15, hh = id >> 7;
+            const int h = b * kHeadBatch + hh;
+            const int tr = min(t0 + tok, Tq - 1);
+            stage[i] = (h < HI) ? *reinterpret_cast<const v4i*>(q_idx + ((int64_t)tr * HI + h) * 128 + c * 16)
+                                : v4i{0, 0, 0, 0};
+        }
+        if (tid < 16 * kHeadBatch) {
+            const int tok = tid & 15, hh = tid >> 4;
+            const int h = b * kHeadBatch + hh;
+            wstage = (h < HI) ? w[(int64_t)min(t0 + tok, Tq - 1) * HI + h] : 0.f;
+        }
+    };
+    auto store_batch = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int id = tid + 256 * i;
+            const int c = id & 7, tok = (id >> 3) & 15, hh = id >> 7;
+            *reinterpret_cast<v4i*>(&q_lds[buf][hh][tok][c * 16]) = stage[i];
+        }
+        if (tid < 16 * kHeadBatch) w_lds[buf][tid >> 4][tid & 15] = wstage;
+    };
 
-    const uint8_t* __restrict__ qp = q_idx + (int64_t)tc * HI * 128 + grp * 32;
-    const float* __restrict__ wp = w + (int64_t)tc * HI;
+    // accumulators start at the linear term qmix . k (bf16 matrix core)
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-
-    v8i b_next = load32B(qp);
-    for (int j0 = 0; j0 < HI; j0 += 4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wp + j0);
-        const float wj[4] = {w4.x, w4.y, w4.z, w4.w};
+    float acc[NK][4];
+    {
+        const uint16_t* qm = qmix + (int64_t)tc * 256 + grp * 32;
+        v8bf bh[4], bl[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const v8i b = b_next;
-            const int jn = j0 + jj + 1;
-            if (jn < HI) b_next = load32B(qp + (int64_t)jn * 128);
+        for (int m = 0; m < 4; ++m) {
+            bh[m] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 8 * m));
+            bl[m] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 128 + 8 * m));
+        }
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                const v4f d = mfma_fp8_16x16x128(a[i], b, zero);
+        for (int i = 0; i < NK; ++i) {
+            v4f lin = zero;
+            if (active) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][e] += wj[jj] * fmaxf(d[e], 0.f);
+                for (int m = 0; m < 4; ++m) {
+                    const v8bf ka = fp8x8_to_bf16(a[i], m);
+                    lin = mfma_bf16_16x16x32(ka, bh[m], lin);
+                    lin = mfma_bf16_16x16x32(ka, bl[m], lin);
+                }
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = lin[e];
         }
     }
+    // the epilogue of "head -1" adds 0 * max(0, 0): no special first iteration
+    v4f dprev[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) dprev[i] = zero;
+    float wprev = 0.f;
+
+    load_batch(0);
+    store_batch(0);
+    __syncthreads();
+    for (int b = 0; b < n_batch; ++b) {
+        const int buf = b & 1;
+        if (b + 1 < n_batch) load_batch(b + 1);       // in flight during this batch's math
+        if (active) {
+#pragma unroll
+            for (int hh = 0; hh < kHeadBatch; ++hh) {
+                const uint8_t* qrow = &q_lds[buf][hh][col][grp * 32];
+                const v4i lo = *reinterpret_cast<const v4i*>(qrow);
+                const v4i hi = *reinterpret_cast<const v4i*>(qrow + 16);
+                const v8i bq = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                const float wj = w_lds[buf][hh][col];
+                v4f dcur[NK];
+#pragma unroll
+                for (int i = 0; i < NK; ++i) dcur[i] = mfma_fp8_16x16x128(a[i], bq, zero);
+                // w-weighted |x| of the previous head while these run (one fma each)
+#pragma unroll
+                for (int i = 0; i < NK; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
+#pragma unroll
+                for (int i = 0; i < NK; ++i) dprev[i] = dcur[i];
+                wprev = wj;
+            }
+        }
+        if (b + 1 < n_batch) store_batch(buf ^ 1);
+        __syncthreads();
+    }
+    if (!active) {
+        fill_masked();
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
 
     if (!t_ok) return;
-    const float qs = q_scale[tc];
+    const float qs = 0.5f * q_scale[tc];                // (linear + |x| terms) / 2
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
         const int s0 = s_base + 16 * i + 4 * grp;
@@ -124,6 +273,204 @@ __global__ __launch_bounds__(256) void index_fp8_kernel(
         } else {
             for (int e = 0; e < 4; ++e)
                 if (s0 + e < Tk) out_row[s0 + e] = r[e];
+        }
+    }
+}
+
+// Resident-q variant for HI <= 64: a workgroup of 16 waves loads the whole q^I
+// tile of its 16 tokens (all heads, 144 KB with padding) into LDS once, then
+// walks a group of key blocks (1024 keys each, 64 per wave) with no further
+// barrier.  Each wave's keys live in registers for its head loop; with four
+// waves per SIMD drifting out of phase, one wave's matrix-core work overlaps
+// another's vector ALU work and memory waits (a wave's own VALU and MFMA
+// instructions do not overlap on gfx950).
+#ifndef DSA_IDX_RES_NK
+#define DSA_IDX_RES_NK 4
+#endif
+#ifndef DSA_IDX_RES_WAVES
+#define DSA_IDX_RES_WAVES 16
+#endif
+constexpr int kResHeads = 64;
+constexpr int kResWaves = DSA_IDX_RES_WAVES;
+constexpr int kResNK = DSA_IDX_RES_NK;
+
+template <int NK>
+__global__ __launch_bounds__(kResWaves * 64) __attribute__((amdgpu_waves_per_eu(kResWaves / 4, kResWaves / 4)))
+void index_fp8_resident_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ k_scale, const uint16_t* __restrict__ qmix, int Tq, int Tk,
+    int HI, int64_t q_pos0, float* __restrict__ scores, int64_t ld, int n_kb, int n_kg, int kg)
+{
+    constexpr int kKeysPerWave = 16 * NK;
+    constexpr int kKeysPerBlock = kResWaves * kKeysPerWave;
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[kResHeads][16][kQPitch];
+    __shared__ float w_lds[kResHeads][16];
+    __shared__ __attribute__((aligned(16))) uint16_t qm_lds[16][264];   // padded rows: no bank conflicts
+
+    // key-group-major order: the workgroups resident on one XCD share a key group (hot in
+    // that XCD's L2) and differ in their token tiles
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int n_tt = (Tq + 15) / 16;
+    const int g = work / n_tt;
+    const int tt = work - g * n_tt;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int t0 = tt * 16;
+    const int t = t0 + col;
+    const bool t_ok = t < Tq;
+    const int tc = t_ok ? t : Tq - 1;
+    const int64_t pos = q_pos0 + t;
+    const int64_t pos_hi = q_pos0 + min(t0 + 15, Tq - 1);
+    const int kb_begin = g * kg, kb_end = min(n_kb, kb_begin + kg);
+    float* __restrict__ out_row = scores + (int64_t)tc * ld;
+
+    // whole group above the diagonal: only -inf to write
+    if ((int64_t)kb_begin * kKeysPerBlock > pos_hi) {
+        if (t_ok) {
+            for (int kb = kb_begin; kb < kb_end; ++kb) {
+                const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;
+#pragma unroll
+                for (int i = 0; i < NK; ++i) {
+                    const int s0 = s_base + 16 * i + 4 * grp;
+                    if (s0 + 3 < Tk)
+                        *reinterpret_cast<float4*>(out_row + s0) =
+                            make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                    else
+                        for (int e = 0; e < 4; ++e)
+                            if (s0 + e < Tk) out_row[s0 + e] = -INFINITY;
+                }
+            }
+        }
+        return;
+    }
+
+    // stage q^I (all heads, padded to a multiple of 8 with zeros), w and qmix
+    const int HP = (HI + 7) & ~7;
+    for (int id = tid; id < 16 * HP * 8; id += kResWaves * 64) {
+        const int c = id & 7, rest = id >> 3;
+        const int h = rest % HP, tok = rest / HP;
+        const int tr = min(t0 + tok, Tq - 1);
+        const v4i v = (h < HI) ? *reinterpret_cast<const v4i*>(q_idx + ((int64_t)tr * HI + h) * 128 + c * 16)
+                               : v4i{0, 0, 0, 0};
+        *reinterpret_cast<v4i*>(&q_lds[h][tok][c * 16]) = v;
+    }
+    for (int id = tid; id < 16 * HP; id += kResWaves * 64) {
+        const int h = id % HP, tok = id / HP;
+        w_lds[h][tok] = (h < HI) ? w[(int64_t)min(t0 + tok, Tq - 1) * HI + h] : 0.f;
+    }
+    for (int id = tid; id < 16 * 32; id += kResWaves * 64) {
+        const int c = id & 31, tok = id >> 5;
+        *reinterpret_cast<v4i*>(&qm_lds[tok][c * 8]) =
+            *reinterpret_cast<const v4i*>(qmix + (int64_t)min(t0 + tok, Tq - 1) * 256 + c * 8);
+    }
+    __syncthreads();
+
+    const float qs = 0.5f * q_scale[tc];              // (linear + |x| terms) / 2
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+        const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;
+        if (s_base >= Tk) break;
+        if ((int64_t)s_base > pos_hi) {               // wave tile above the diagonal
+            if (t_ok) {
+#pragma unroll
+                for (int i = 0; i < NK; ++i) {
+                    const int s0 = s_base + 16 * i + 4 * grp;
+                    if (s0 + 3 < Tk)
+                        *reinterpret_cast<float4*>(out_row + s0) =
+                            make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                    else
+                        for (int e = 0; e < 4; ++e)
+                            if (s0 + e < Tk) out_row[s0 + e] = -INFINITY;
+                }
+            }
+            continue;
+        }
+        // keys (A operands) of this wave: 16 NK keys, 32 bytes per lane per tile
+        v8i a[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int s = s_base + 16 * i + col;
+            a[i] = (s < Tk) ? load32B(k_idx + (int64_t)s * 128 + grp * 32) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        // accumulators start at the linear term qmix . k (bf16 matrix core)
+        float acc[NK][4];
+        {
+            const uint16_t* qm = &qm_lds[col][grp * 32];
+            v8bf bh[4], bl[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                bh[m] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 8 * m));
+                bl[m] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 128 + 8 * m));
+            }
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                v4f lin = zero;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const v8bf ka = fp8x8_to_bf16(a[i], m);
+                    lin = mfma_bf16_16x16x32(ka, bh[m], lin);
+                    lin = mfma_bf16_16x16x32(ka, bl[m], lin);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][e] = lin[e];
+            }
+        }
+        // head loop: the B operand (q^I of head j for the 16 tokens) is read from LDS one
+        // head ahead, and the |x| epilogue of head j-1 follows the MFMAs of head j
+        v4f dprev[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) dprev[i] = zero;
+        float wprev = 0.f;
+        const uint8_t* qbase = &q_lds[0][col][grp * 32];
+        v4i nlo = *reinterpret_cast<const v4i*>(qbase);
+        v4i nhi = *reinterpret_cast<const v4i*>(qbase + 16);
+        float nw = w_lds[0][col];
+        for (int j0 = 0; j0 < HP; j0 += 8) {
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                const int j = j0 + hh;
+                const v8i bq = {nlo.x, nlo.y, nlo.z, nlo.w, nhi.x, nhi.y, nhi.z, nhi.w};
+                const float wj = nw;
+                const int jn = (j + 1 < HP) ? j + 1 : j;
+                nlo = *reinterpret_cast<const v4i*>(qbase + jn * 16 * kQPitch);
+                nhi = *reinterpret_cast<const v4i*>(qbase + jn * 16 * kQPitch + 16);
+                nw = w_lds[jn][col];
+                v4f dcur[NK];
+#pragma unroll
+                for (int i = 0; i < NK; ++i) dcur[i] = mfma_fp8_16x16x128(a[i], bq, zero);
+#pragma unroll
+                for (int i = 0; i < NK; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
+#pragma unroll
+                for (int i = 0; i < NK; ++i) dprev[i] = dcur[i];
+                wprev = wj;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
+        if (!t_ok) continue;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int s0 = s_base + 16 * i + 4 * grp;
+            float r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = s0 + e;
+                const float ks = (s < Tk) ? k_scale[s] : 0.f;
+                r[e] = ((int64_t)s <= pos) ? acc[i][e] * (qs * ks) : -INFINITY;
+            }
+            if (s0 + 3 < Tk) {
+                *reinterpret_cast<float4*>(out_row + s0) = make_float4(r[0], r[1], r[2], r[3]);
+            } else {
+                for (int e = 0; e < 4; ++e)
+                    if (s0 + e < Tk) out_row[s0 + e] = r[e];
+            }
         }
     }
 }
@@ -262,9 +609,11 @@ __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
 
 }  // namespace
 
+size_t index_fp8_workspace_bytes(int Tq) { return (size_t)Tq * 256 * sizeof(uint16_t); }
+
 hipError_t launch_index_fp8(const uint8_t* q_idx, const float* q_scale, const float* w,
                             const uint8_t* k_idx, const float* k_scale, int Tq, int Tk, int HI,
-                            int64_t q_pos0, float* scores, int64_t ld, hipStream_t stream)
+                            int64_t q_pos0, float* scores, int64_t ld, void* ws, hipStream_t stream)
 {
     constexpr int NK = 8;
     const int n_tt = (Tq + 15) / 16;
@@ -272,8 +621,26 @@ hipError_t launch_index_fp8(const uint8_t* q_idx, const float* q_scale, const fl
     const int64_t n = (int64_t)n_tt * n_kb;
     if (n == 0) return hipSuccess;
     if (n > INT32_MAX) return hipErrorInvalidValue;
+    uint16_t* qmix = static_cast<uint16_t*>(ws);
+    hipLaunchKernelGGL(qmix_kernel, dim3((Tq + 3) / 4), dim3(256), 0, stream, q_idx, w, Tq, HI, qmix);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (HI <= kResHeads) {
+        // key blocks of 1024; each workgroup takes a group of up to 16 of them so the
+        // one-time q^I staging is amortised, while keeping >= 8 workgroups per CU in total
+        const int n_kb1 = (Tk + kResWaves * 16 * kResNK - 1) / (kResWaves * 16 * kResNK);
+        int kg = n_kb1 / 8;
+        kg = kg < 1 ? 1 : (kg > 16 ? 16 : kg);
+        const int n_kg = (n_kb1 + kg - 1) / kg;
+        const int64_t nw = (int64_t)n_tt * n_kg;
+        if (nw > INT32_MAX) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(index_fp8_resident_kernel<kResNK>, dim3((unsigned)nw), dim3(kResWaves * 64), 0, stream,
+                           q_idx, q_scale, w, k_idx, k_scale, qmix, Tq, Tk, HI, q_pos0, scores, ld,
+                           n_kb1, n_kg, kg);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(index_fp8_kernel<NK>, dim3((unsigned)n), dim3(256), 0, stream, q_idx,
-                       q_scale, w, k_idx, k_scale, Tq, Tk, HI, q_pos0, scores, ld, n_kb);
+                       q_scale, w, k_idx, k_scale, qmix, Tq, Tk, HI, q_pos0, scores, ld, n_kb);
     return hipGetLastError();
 }
 

@@ -8,9 +8,12 @@
 namespace dsa {
 
 // Lightning indexer, contiguous keys (prefill).  Row i is position q_pos0 + i.
+// The FP8 kernel needs index_fp8_workspace_bytes(Tq) bytes of device scratch.
+size_t index_fp8_workspace_bytes(int Tq);
 hipError_t launch_index_fp8(const uint8_t* q_idx, const float* q_scale, const float* w,
                             const uint8_t* k_idx, const float* k_scale, int Tq, int Tk, int HI,
-                            int64_t q_pos0, float* scores, int64_t ld, hipStream_t stream);
+                            int64_t q_pos0, float* scores, int64_t ld, void* ws,
+                            hipStream_t stream);
 hipError_t launch_index_f32(const float* q_idx, const float* w, const float* k_idx, int Tq,
                             int Tk, int HI, int dI, int64_t q_pos0, float* scores, int64_t ld,
                             hipStream_t stream);

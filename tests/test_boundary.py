@@ -50,7 +50,7 @@ def _st(lib, fn, *args):
 
 def test_index_scores_argument_checks(lib):
     f = lib.dsa_index_scores
-    ok = [A, A, A, A, A, dsa.DSA_FP8_E4M3, 16, 16, 64, 128, 0, A, 16, None]
+    ok = [A, A, A, A, A, dsa.DSA_FP8_E4M3, 16, 16, 64, 128, 0, A, 16, A, 1 << 20, None]
     assert f(*ok[:0], None, *ok[1:]) == 1                      # NULL q_idx
     assert b"q_idx" in lib.dsa_last_error()
     bad = list(ok); bad[0] = MIS
@@ -73,6 +73,13 @@ def test_index_scores_argument_checks(lib):
     assert f(*bad) == 1                                         # FP8 needs scales
     bad = list(ok); bad[5] = dsa.DSA_F32; bad[9] = 64; bad[8] = 32
     assert f(*bad) == 2                                         # fp32: HI * dI > 1024
+    n = lib.dsa_index_scores_workspace_size(16, 64, 128, dsa.DSA_FP8_E4M3)
+    assert n >= 16 * 512
+    assert lib.dsa_index_scores_workspace_size(16, 8, 64, dsa.DSA_F32) == 0
+    bad = list(ok); bad[14] = n - 1
+    assert f(*bad) == 3                                         # FP8 indexer scratch too small
+    bad = list(ok); bad[13] = None
+    assert f(*bad) == 3
 
 
 def test_topk_argument_checks(lib):
