@@ -5,20 +5,23 @@
 // position so that the selection is deterministic (Keye-VL-2.0 report section
 // 5.2.1), listed in ascending position order.
 //
-// Exact radix select on an order-preserving 32-bit key.  One workgroup of 1024
-// threads owns a row:
-//   1. min / max of the row's keys;
-//   2. radix passes over key - min, most significant digit first, with the
-//      first digit placed at the top set bit of (max - min) so that the bins
-//      spread over the scores actually present (scores of one row usually
-//      span only a few binades, which a fixed exponent-first digit would
-//      crowd into a handful of bins); each pass builds an LDS histogram of the
-//      elements still tied with the prefix and picks the bin holding the k-th
-//      largest; it stops early when that bin is taken whole;
-//   3. one ordered compaction pass: elements above the threshold, plus the
-//      first `need` elements equal to it in position order; a block-wide
-//      prefix sum gives every selected element its output slot directly, so
-//      the output comes out ascending with no sort.
+// One workgroup of 1024 threads owns a row; scores are compared through an
+// order-preserving 32-bit key (-0 and +0 map to the same key).
+//   1. A sample of the row (256 runs of 16 contiguous scores) gives, by an
+//      exact select in LDS, a key that is a lower bound for the k-th largest
+//      with high probability (the sample rank is padded by about 3 sigma).
+//   2. One pass over the row copies every score at or above that bound, with
+//      its position, into LDS in position order (block-wide prefix sums).
+//   3. If that candidate set holds at least k and fits in LDS, an exact radix
+//      select among the candidates finds the k-th largest key and how many of
+//      the keys equal to it to take; an ordered compaction of the candidates
+//      then writes the selection directly in ascending position order, ties
+//      resolved to the lower positions.
+//   4. Otherwise (the sample misjudged, or too many ties) the same exact select
+//      and compaction run over the row in global memory: correct for every
+//      input, only slower.
+// Radix selects place their first digit at the top set bit of (max - min) of
+// the keys involved, so the bins spread over the values actually present.
 // Rows with t + 1 <= k need no selection and read nothing (they take 0..t).
 #include "device_common.h"
 #include "internal.h"
@@ -82,7 +85,7 @@ __device__ __forceinline__ uint32_t block_reduce_minmax(uint32_t mn, uint32_t mx
     return a;
 }
 
-// Four consecutive elements starting at i (multiple of 4); missing ones get `fill`.
+// Four consecutive elements starting at i (multiple of 4); missing ones read as 0.
 __device__ __forceinline__ void load4(const float* __restrict__ src, int64_t i, int64_t n,
                                       float v[4]) {
     if (i + 3 < n) {
@@ -93,13 +96,115 @@ __device__ __forceinline__ void load4(const float* __restrict__ src, int64_t i, 
     }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+// Range of the keys get(0..m).
+template <class Get>
+__device__ __forceinline__ void key_range(Get get, int64_t m, uint32_t* red, uint32_t& kmin,
+                                          uint32_t& kmax) {
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    for (int64_t i = threadIdx.x; i < m; i += kTopkThreads) {
+        const uint32_t k = get(i);
+        mn = min(mn, k);
+        mx = max(mx, k);
+    }
+    kmin = block_reduce_minmax(mn, mx, red, &kmax);
+}
+
+// Exact select of the R-th largest (1 <= R <= m) of the keys get(0..m), all in
+// [kmin, kmax].  On return an element is above the threshold iff
+// ((key - kmin) & mask) > prefix and tied with it iff == prefix; `need` of the
+// tied elements complete the R.
+template <class Get>
+__device__ void radix_select(Get get, int64_t m, uint32_t R, uint32_t kmin, uint32_t kmax,
+                             uint32_t* hist, uint32_t* wsum, uint32_t* sh, uint32_t& prefix,
+                             uint32_t& mask, uint32_t& need) {
+    const int tid = threadIdx.x;
+    const uint32_t range = kmax - kmin;
+    int hi = range ? 32 - __clz(range) : 0;
+    prefix = 0;
+    mask = 0;
+    need = R;
+    while (hi > 0) {
+        const int lo = hi > kDigitBits ? hi - kDigitBits : 0;
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+        __syncthreads();
+        for (int64_t i = tid; i < m; i += kTopkThreads) {
+            const uint32_t rel = get(i) - kmin;
+            if ((rel & mask) == prefix) atomicAdd(&hist[(rel >> lo) & dmask], 1u);
+        }
+        __syncthreads();
+        // bins in descending order: thread t takes bins 2047-2t and 2046-2t
+        const uint32_t h0 = hist[kBins - 1 - 2 * tid], h1 = hist[kBins - 2 - 2 * tid];
+        uint32_t total;
+        const uint32_t above = block_excl_scan(h0 + h1, wsum, &total);
+        if (above < need && need <= above + h0) {
+            sh[0] = kBins - 1 - 2 * tid;
+            sh[1] = above;
+        } else if (above + h0 < need && need <= above + h0 + h1) {
+            sh[0] = kBins - 2 - 2 * tid;
+            sh[1] = above + h0;
+        }
+        __syncthreads();
+        const uint32_t bin = sh[0];
+        need -= sh[1];
+        const uint32_t in_bin = hist[bin];
+        prefix |= bin << lo;
+        mask |= dmask << lo;
+        __syncthreads();                              // hist is rebuilt by the next pass
+        hi = lo;
+        if (in_bin == need) break;                    // the whole bin is taken
+    }
+}
+
+// Ordered compaction: element i (in position order) is selected when above the
+// threshold, or tied and among the first `need` tied ones; its output slot is
+// (# above before it) + min(# tied before it, need).
+template <class Get, class Pos>
+__device__ void compact(Get get, Pos pos_of, int64_t m, uint32_t kmin, uint32_t prefix,
+                        uint32_t mask, uint32_t need, uint32_t* wsum, int32_t* __restrict__ out) {
+    const int tid = threadIdx.x;
+    uint32_t gt_base = 0, eq_base = 0;
+    for (int64_t c0 = 0; c0 < m; c0 += 4 * kTopkThreads) {
+        const int64_t i0 = c0 + (int64_t)tid * 4;
+        uint32_t gt = 0, eq = 0, cnt = 0;
+        for (int e = 0; e < 4; ++e) {
+            if (i0 + e < m) {
+                const uint32_t r = (get(i0 + e) - kmin) & mask;
+                if (r > prefix) { gt |= 1u << e; ++cnt; }
+                else if (r == prefix) { eq |= 1u << e; cnt += 1u << 16; }
+            }
+        }
+        uint32_t total;
+        const uint32_t excl = block_excl_scan(cnt, wsum, &total);
+        uint32_t gt_before = gt_base + (excl & 0xffffu);
+        uint32_t eq_before = eq_base + (excl >> 16);
+        for (int e = 0; e < 4; ++e) {
+            if (gt & (1u << e)) {
+                out[gt_before + min(eq_before, need)] = pos_of(i0 + e);
+                ++gt_before;
+            } else if (eq & (1u << e)) {
+                if (eq_before < need) out[gt_before + eq_before] = pos_of(i0 + e);
+                ++eq_before;
+            }
+        }
+        gt_base += total & 0xffffu;
+        eq_base += total >> 16;
+    }
+}
+
+constexpr int kCap = 8192;                // LDS candidate capacity
+constexpr int kSampleRuns = 256;          // sample: 256 runs of 16 contiguous scores
+constexpr int kSample = kSampleRuns * 16;
+
+__global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, int Tk, int64_t q_pos0,
     const int32_t* __restrict__ row_len, int k, int32_t* __restrict__ idx)
 {
+    __shared__ uint32_t ck[kCap];             // candidate keys, in position order
+    __shared__ int32_t ci[kCap];              // their positions (the sample reuses this array)
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t wsum[2 * kTopkWaves];
-    __shared__ uint32_t s_bin, s_above;
+    __shared__ uint32_t sh[4];
 
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
@@ -116,96 +221,107 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
         return;
     }
     const float* __restrict__ src = scores + (int64_t)row * ld;
+    int64_t m;                                        // number of candidates in LDS
+    bool in_lds = true;
 
-    // 1. key range of the row
-    uint32_t mn = 0xffffffffu, mx = 0u;
-    for (int64_t i = (int64_t)tid * 4; i < n; i += 4 * kTopkThreads) {
-        float v[4];
-        load4(src, i, n, v);
-        for (int e = 0; e < 4; ++e) {
-            if (i + e < n) {
-                const uint32_t key = order_key(v[e]);
-                mn = min(mn, key);
-                mx = max(mx, key);
-            }
+    if (n <= kCap) {
+        for (int64_t i = tid; i < n; i += kTopkThreads) {
+            ck[i] = order_key(src[i]);
+            ci[i] = (int32_t)i;
         }
-    }
-    uint32_t kmax;
-    const uint32_t kmin = block_reduce_minmax(mn, mx, wsum, &kmax);
-    const uint32_t range = kmax - kmin;
-    int hi = range ? 32 - __clz(range) : 0;           // bits of (key - kmin) that vary
-
-    // 2. radix passes on rel = key - kmin, digits of <= 11 bits from the top
-    uint32_t prefix = 0, mask = 0;                    // rel & mask == prefix: still tied
-    uint32_t need = (uint32_t)k;                      // still to take among the tied
-    while (hi > 0) {
-        const int lo = hi > kDigitBits ? hi - kDigitBits : 0;
-        const uint32_t dmask = (1u << (hi - lo)) - 1u;
-        for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+        m = n;
         __syncthreads();
-        for (int64_t i = (int64_t)tid * 4; i < n; i += 4 * kTopkThreads) {
+    } else {
+        // 1. sample -> lower bound for the k-th largest key
+        uint32_t* smp = reinterpret_cast<uint32_t*>(ci);
+        {
+            const int run = tid >> 2, part = tid & 3;
+            const int64_t base = ((int64_t)run * n / kSampleRuns) & ~(int64_t)3;
             float v[4];
-            load4(src, i, n, v);
-            for (int e = 0; e < 4; ++e) {
-                if (i + e < n) {
-                    const uint32_t rel = order_key(v[e]) - kmin;
-                    if ((rel & mask) == prefix) atomicAdd(&hist[(rel >> lo) & dmask], 1u);
+            load4(src, base + 4 * part, n, v);
+            for (int e = 0; e < 4; ++e) smp[4 * tid + e] = order_key(v[e]);
+        }
+        __syncthreads();
+        const double r = (double)k * kSample / (double)n;
+        uint32_t r_lo = (uint32_t)ceil(r + 3.0 * sqrt(r) + 8.0);
+        if (r_lo > (uint32_t)kSample) r_lo = kSample;
+        auto get_s = [&](int64_t i) { return smp[i]; };
+        uint32_t smin, smax, sp, sm, sn;
+        key_range(get_s, kSample, wsum, smin, smax);
+        radix_select(get_s, kSample, r_lo, smin, smax, hist, wsum, sh, sp, sm, sn);
+        const uint32_t bound = smin + sp;             // <= the r_lo-th largest sample key
+        __syncthreads();                              // the sample is dead from here on
+
+        // 2. one pass: every score with key >= bound, in position order, into LDS.
+        //    16 consecutive scores per thread per step; the next step's loads are
+        //    issued before this step's prefix sum so the row streams at full rate.
+        constexpr int kPer = 8;
+        constexpr int64_t kStepLen = (int64_t)kPer * kTopkThreads;
+        uint32_t base_cnt = 0;
+        float4 cur[kPer / 4], nxt[kPer / 4];
+        auto fetch = [&](int64_t c0, float4* dst) {
+            const int64_t i0 = c0 + (int64_t)tid * kPer;
+#pragma unroll
+            for (int q = 0; q < kPer / 4; ++q) {
+                float v[4];
+                load4(src, i0 + 4 * q, n, v);
+                dst[q] = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        };
+        fetch(0, cur);
+        for (int64_t c0 = 0; c0 < n; c0 += kStepLen) {
+            if (c0 + kStepLen < n) fetch(c0 + kStepLen, nxt);
+            const int64_t i0 = c0 + (int64_t)tid * kPer;
+            uint32_t flag = 0, cnt = 0;
+#pragma unroll
+            for (int q = 0; q < kPer / 4; ++q) {
+                const float v[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * q + e;
+                    if (i0 + j < n && order_key(v[e]) >= bound) { flag |= 1u << j; ++cnt; }
                 }
             }
+            uint32_t total;
+            uint32_t p = base_cnt + block_excl_scan(cnt, wsum, &total);
+            if (flag) {
+#pragma unroll
+                for (int q = 0; q < kPer / 4; ++q) {
+                    const float v[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 4 * q + e;
+                        if (flag & (1u << j)) {
+                            if (p < (uint32_t)kCap) { ck[p] = order_key(v[e]); ci[p] = (int32_t)(i0 + j); }
+                            ++p;
+                        }
+                    }
+                }
+            }
+            base_cnt += total;
+#pragma unroll
+            for (int q = 0; q < kPer / 4; ++q) cur[q] = nxt[q];
         }
         __syncthreads();
-        // bins in descending order: thread t takes bins 2047-2t and 2046-2t
-        const uint32_t h0 = hist[kBins - 1 - 2 * tid], h1 = hist[kBins - 2 - 2 * tid];
-        uint32_t total;
-        const uint32_t above = block_excl_scan(h0 + h1, wsum, &total);
-        if (above < need && need <= above + h0) {
-            s_bin = kBins - 1 - 2 * tid;
-            s_above = above;
-        } else if (above + h0 < need && need <= above + h0 + h1) {
-            s_bin = kBins - 2 - 2 * tid;
-            s_above = above + h0;
-        }
-        __syncthreads();
-        const uint32_t bin = s_bin;
-        need -= s_above;
-        const uint32_t in_bin = hist[bin];
-        prefix |= bin << lo;
-        mask |= dmask << lo;
-        __syncthreads();                              // hist is rebuilt by the next pass
-        hi = lo;
-        if (in_bin == need) break;                    // the whole bin is taken
+        m = base_cnt;
+        in_lds = m >= (int64_t)k && m <= kCap;
     }
 
-    // 3. ordered compaction: position of an element = (# above before it) +
-    //    min(# tied before it, need)
-    uint32_t gt_base = 0, eq_base = 0;
-    for (int64_t c0 = 0; c0 < n; c0 += 4 * kTopkThreads) {
-        const int64_t i0 = c0 + (int64_t)tid * 4;
-        float v[4];
-        load4(src, i0, n, v);
-        uint32_t gt = 0, eq = 0, cnt = 0;
-        for (int e = 0; e < 4; ++e) {
-            if (i0 + e < n) {
-                const uint32_t r = (order_key(v[e]) - kmin) & mask;
-                if (r > prefix) { gt |= 1u << e; ++cnt; }
-                else if (r == prefix) { eq |= 1u << e; cnt += 1u << 16; }
-            }
-        }
-        uint32_t total;
-        const uint32_t excl = block_excl_scan(cnt, wsum, &total);
-        uint32_t gt_before = gt_base + (excl & 0xffffu);
-        uint32_t eq_before = eq_base + (excl >> 16);
-        for (int e = 0; e < 4; ++e) {
-            if (gt & (1u << e)) {
-                out[gt_before + min(eq_before, need)] = (int32_t)(i0 + e);
-                ++gt_before;
-            } else if (eq & (1u << e)) {
-                if (eq_before < need) out[gt_before + eq_before] = (int32_t)(i0 + e);
-                ++eq_before;
-            }
-        }
-        gt_base += total & 0xffffu;
-        eq_base += total >> 16;
+    uint32_t kmin, kmax, prefix, mask, need;
+    if (in_lds) {
+        // 3. exact select among the candidates
+        auto get_c = [&](int64_t i) { return ck[i]; };
+        auto pos_c = [&](int64_t i) { return ci[i]; };
+        key_range(get_c, m, wsum, kmin, kmax);
+        radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
+        compact(get_c, pos_c, m, kmin, prefix, mask, need, wsum, out);
+    } else {
+        // 4. fallback: the same exact select and compaction over the row in memory
+        auto get_g = [&](int64_t i) { return order_key(src[i]); };
+        auto pos_g = [&](int64_t i) { return (int32_t)i; };
+        key_range(get_g, n, wsum, kmin, kmax);
+        radix_select(get_g, n, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
+        compact(get_g, pos_g, n, kmin, prefix, mask, need, wsum, out);
     }
 }
 

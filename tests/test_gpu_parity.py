@@ -117,6 +117,26 @@ def test_topk_exact_vs_oracle_same_scores(L, k, kind):
         assert np.array_equal(got[0], ref[0]), "row %d" % r
 
 
+def test_topk_fallback_paths_exact():
+    """Rows that defeat the sampled threshold: (a) so many ties at the k-th value that the
+    candidates overflow the on-chip buffer, (b) large values only inside the sampled runs so
+    the sampled bound overshoots and too few candidates survive.  Both must still be exact."""
+    _say("topk fallbacks")
+    rng = np.random.default_rng(17)
+    k = 2048
+    n = 100000
+    a = rng.integers(0, 3, n).astype(np.float32)               # (a) heavy ties
+    b = (rng.standard_normal(n) * 0.01).astype(np.float32)     # (b) small values everywhere ...
+    runs = [((r * n) // 256) & ~3 for r in range(256)]
+    big = rng.choice(256, 13, replace=False)
+    for r in big:                                              # ... large ones in 13 sampled runs
+        b[runs[r]:runs[r] + 16] = 1000.0 + rng.random(16).astype(np.float32)
+    for row in (a, b):
+        got = _gpu_topk(row[None, :], n, k, q_pos0=n - 1)
+        ref, _ = oracle.topk(row[None, :].astype(np.float64), [n - 1], k)
+        assert np.array_equal(got[0], ref[0])
+
+
 def test_topk_many_rows_one_call():
     """A chunk of consecutive rows in one launch (row i at position q_pos0 + i)."""
     _say("topk many rows")
