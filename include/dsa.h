@@ -101,7 +101,10 @@ dsa_status_t dsa_index_scores(const void* q_idx, const float* q_scale, const flo
  * followed by -1.  Rows with p + 1 <= k need no selection and read nothing.
  * Scores are expected finite; NaN orders above +inf (positive NaN) or below
  * -inf (negative NaN).  1 <= k <= 8192; ld_scores >= Tk >= q_pos0 + Tq.
- * Workspace: dsa_topk_workspace_size() bytes (may be 0; ws may then be NULL).
+ * Workspace: dsa_topk_workspace_size() bytes (0 for many rows; ws may then be
+ * NULL).  For few long rows a workspace of that size lets the library split each
+ * row across workgroups and merge the parts; without it the result is the same,
+ * computed by one workgroup per row.
  */
 size_t dsa_topk_workspace_size(int Tq, int Tk, int k);
 dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int Tq, int Tk, int64_t q_pos0,
@@ -170,7 +173,8 @@ dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_
  * k_cache / v_cache [num_blocks, block_size, G, d] (dtype);
  * block_table int32 [B, max_blocks]; seq_lens int32 [B] (device).
  * A sequence length outside [1, max_blocks * block_size] yields a zero output
- * row and an index row of -1.  dI must be 128; dtype DSA_BF16 or DSA_F32.
+ * row and an index row of -1.  dI must be 128 and block_size 64 (one cache block
+ * is one 64-key indexer step); dtype DSA_BF16 or DSA_F32.
  * out [B, Hq, d]; idx_out (nullable) [B, topk].
  * Workspace: dsa_decode_workspace_size() bytes.
  */

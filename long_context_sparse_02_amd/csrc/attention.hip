@@ -40,16 +40,20 @@ struct KVStep {
     uint32_t valid;                       // bit r: entry r of the step is a usable position
 };
 
+// Row of the K/V arrays holding entry e of a query's index list, or -1 when the
+// entry is padding, out of range, or maps to a block outside the cache.  Every
+// load here is unconditional (clamped to valid memory) so that the compiler keeps
+// the gather of the next step in flight instead of waiting at branch joins.
 template <bool PAGED>
 __device__ __forceinline__ int resolve_row(const AttnArgs& p, const int32_t* __restrict__ idx_row,
                                            int e, int k_end, int seq, int64_t len) {
-    if (e >= k_end) return -1;
-    const int s = idx_row[e];
-    if (s < 0 || s >= len) return -1;
-    if (!PAGED) return s;
-    const int blk = p.block_table[(int64_t)seq * p.max_blocks + s / p.block_size];
-    if (blk < 0 || blk >= p.n_kv) return -1;
-    return blk * p.block_size + s % p.block_size;
+    const int s = idx_row[min(e, k_end - 1)];
+    bool ok = e < k_end && s >= 0 && s < len;
+    if (!PAGED) return ok ? s : -1;
+    const int sc = ok ? s : 0;
+    const int blk = p.block_table[(int64_t)seq * p.max_blocks + sc / p.block_size];
+    ok = ok && blk >= 0 && blk < p.n_kv;
+    return ok ? blk * p.block_size + sc % p.block_size : -1;
 }
 
 template <bool PAGED>
@@ -62,17 +66,20 @@ __device__ __forceinline__ void load_step(const AttnArgs& p, const int32_t* __re
     const int G = p.G;
     const uint16_t* __restrict__ K = static_cast<const uint16_t*>(p.k);
     const uint16_t* __restrict__ V = static_cast<const uint16_t*>(p.v);
-    const int ra = __shfl(prow, col, 64), rb = __shfl(prow, 16 + col, 64);
-    const v4i z = {0, 0, 0, 0};
+    // invalid entries read row 0 (in bounds); their logits are masked to -inf and their V
+    // values zeroed below, so whatever row 0 holds cannot reach the result
+    const int ra = max(__shfl(prow, col, 64), 0), rb = max(__shfl(prow, 16 + col, 64), 0);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        st.ka[m] = ra >= 0 ? *reinterpret_cast<const v4i*>(K + ((int64_t)ra * G + g) * 128 + grp * 32 + 8 * m) : z;
-        st.kb[m] = rb >= 0 ? *reinterpret_cast<const v4i*>(K + ((int64_t)rb * G + g) * 128 + grp * 32 + 8 * m) : z;
+        st.ka[m] = *reinterpret_cast<const v4i*>(K + ((int64_t)ra * G + g) * 128 + grp * 32 + 8 * m);
+        st.kb[m] = *reinterpret_cast<const v4i*>(K + ((int64_t)rb * G + g) * 128 + grp * 32 + 8 * m);
     }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int r = __shfl(prow, (lane >> 4) + 4 * it, 64);
-        st.vv[it] = r >= 0 ? *reinterpret_cast<const v4i*>(V + ((int64_t)r * G + g) * 128 + (lane & 15) * 8) : z;
+        const v4i x = *reinterpret_cast<const v4i*>(V + ((int64_t)max(r, 0) * G + g) * 128 + (lane & 15) * 8);
+        const int keep = r >= 0 ? -1 : 0;
+        st.vv[it] = v4i{x.x & keep, x.y & keep, x.z & keep, x.w & keep};
     }
 }
 
@@ -96,9 +103,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
         len = p.seq_lens ? (int64_t)p.seq_lens[seq] : cap;
         if (len > cap) len = 0;
     }
+    if (p.n_kv <= 0) len = 0;                         // nothing can be gathered
     const int32_t* __restrict__ idx_row = p.idx + (int64_t)row * p.topk;
     const int k_begin = split * per_split;
-    const int k_end = min(p.topk, k_begin + per_split);
+    const int k_end = len > 0 ? min(p.topk, k_begin + per_split) : k_begin;
     const float scale = p.sm_scale * kLog2e;
     const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
     uint16_t* vtile = &vt[wave][0][0];
@@ -218,9 +226,10 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs p, int ns
         len = p.seq_lens ? (int64_t)p.seq_lens[seq] : cap;
         if (len > cap) len = 0;
     }
+    if (p.n_kv <= 0) len = 0;
     const int32_t* __restrict__ idx_row = p.idx + (int64_t)row * p.topk;
     const int k_begin = split * per_split;
-    const int k_end = min(p.topk, k_begin + per_split);
+    const int k_end = len > 0 ? min(p.topk, k_begin + per_split) : k_begin;
     const float* __restrict__ Q = static_cast<const float*>(p.q);
     const float* __restrict__ K = static_cast<const float*>(p.k);
     const float* __restrict__ V = static_cast<const float*>(p.v);

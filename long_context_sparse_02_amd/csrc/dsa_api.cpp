@@ -158,15 +158,15 @@ DSA_EXPORT dsa_status_t dsa_index_scores(const void* q_idx, const float* q_scale
 }
 
 DSA_EXPORT size_t dsa_topk_workspace_size(int Tq, int Tk, int k) {
-    (void)Tq; (void)Tk; (void)k;
-    return 0;
+    if (Tq <= 0 || Tk <= 0 || k <= 0) return 0;
+    const size_t n = dsa::topk_workspace_bytes(Tq, Tk, k);
+    return n ? round_up(n) : 0;
 }
 
 DSA_EXPORT dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int Tq, int Tk,
                                  int64_t q_pos0, int k, int32_t* idx, void* ws, size_t ws_bytes,
                                  hipStream_t stream) {
     g_err[0] = 0;
-    (void)ws; (void)ws_bytes;
     REQUIRE(Tq >= 0 && Tk >= 0 && q_pos0 >= 0, DSA_ERR_INVALID_ARG, "negative size or position");
     REQUIRE((int64_t)Tk >= q_pos0 + Tq, DSA_ERR_INVALID_ARG,
             "Tk (%d) must cover every query's prefix (q_pos0 + Tq = %lld)", Tk, (long long)(q_pos0 + Tq));
@@ -175,7 +175,11 @@ DSA_EXPORT dsa_status_t dsa_topk(const float* scores, int64_t ld_scores, int Tq,
     REQUIRE_PTR4(idx);
     REQUIRE(ld_scores >= Tk && ld_scores % 4 == 0, DSA_ERR_INVALID_ARG,
             "ld_scores (%lld) must be >= Tk (%d) and a multiple of 4", (long long)ld_scores, Tk);
-    hipError_t e = dsa::launch_topk(scores, ld_scores, Tq, Tk, q_pos0, nullptr, k, idx, stream);
+    REQUIRE_OPT_PTR(ws);
+    // a workspace smaller than the size query is simply not used (single-pass rows)
+    const size_t need = dsa::topk_workspace_bytes(Tq, Tk, k);
+    void* use_ws = (ws && ws_bytes >= need && need) ? ws : nullptr;
+    hipError_t e = dsa::launch_topk(scores, ld_scores, Tq, Tk, q_pos0, nullptr, k, idx, use_ws, stream);
     return e == hipSuccess ? DSA_OK : hip_fail(e, "top-k launch");
 }
 
@@ -296,7 +300,8 @@ DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v,
                          idx_dtype, rows, tk, HI, dI, pos0, scores, plan.ld, index_ws, stream);
         if (st != DSA_OK) return st;
         int32_t* idx_c = idx_out ? idx_out + (int64_t)r0 * topk : idx_ws;
-        hipError_t e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c, stream);
+        hipError_t e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c,
+                                        nullptr, stream);
         if (e != hipSuccess) return hip_fail(e, "top-k launch");
         st = run_attn(static_cast<const char*>(q) + r0 * qrow, k, v, dtype, tk, nullptr, 0, 0,
                       nullptr, nullptr, idx_c, rows, topk, Hq, G, d, sm_scale,
@@ -311,7 +316,7 @@ namespace {
 struct DecodePlan {
     int64_t ld;
     int nsplit;
-    size_t scores_bytes, idx_bytes, part_bytes, total;
+    size_t scores_bytes, idx_bytes, part_bytes, topk_bytes, total;
 };
 
 DecodePlan plan_decode(int B, int max_blocks, int block_size, int topk, int Hq, int d) {
@@ -321,7 +326,8 @@ DecodePlan plan_decode(int B, int max_blocks, int block_size, int topk, int Hq, 
     p.idx_bytes = round_up((size_t)B * topk * sizeof(int32_t));
     p.nsplit = dsa::attn_num_splits(B, topk);
     p.part_bytes = round_up(dsa::attn_partials_bytes(B, p.nsplit, Hq, d));
-    p.total = p.scores_bytes + p.idx_bytes + p.part_bytes;
+    p.topk_bytes = round_up(dsa::topk_workspace_bytes(B, (int)((int64_t)max_blocks * block_size), topk));
+    p.total = p.scores_bytes + p.idx_bytes + p.part_bytes + p.topk_bytes;
     return p;
 }
 
@@ -350,6 +356,8 @@ DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float
     REQUIRE((int64_t)num_blocks * block_size < INT32_MAX, DSA_ERR_UNSUPPORTED,
             "paged cache holds too many tokens");
     REQUIRE(dI == 128, DSA_ERR_UNSUPPORTED, "decode indexer needs dI == 128 (got %d)", dI);
+    REQUIRE(block_size == 64, DSA_ERR_UNSUPPORTED, "decode needs 64-token cache blocks (got %d)",
+            block_size);
     REQUIRE(HI >= 1 && HI <= 128 && HI % 4 == 0, DSA_ERR_UNSUPPORTED,
             "decode indexer needs HI %% 4 == 0 and HI <= 128 (got %d)", HI);
     dsa_status_t st = check_attn_shape(dtype, Hq, G, d, topk);
@@ -366,6 +374,8 @@ DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float
     float* scores = reinterpret_cast<float*>(base);
     int32_t* idx_c = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + plan.scores_bytes);
     float* partials = reinterpret_cast<float*>(base + plan.scores_bytes + plan.idx_bytes);
+    void* topk_ws = plan.topk_bytes ? base + plan.scores_bytes + plan.idx_bytes + plan.part_bytes
+                                    : nullptr;
     const int cap = max_blocks * block_size;
 
     hipError_t e = dsa::launch_index_fp8_paged(
@@ -373,7 +383,7 @@ DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float
         kidx_scale, block_table, seq_lens, B, num_blocks, max_blocks, block_size, HI, scores,
         plan.ld, stream);
     if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
-    e = dsa::launch_topk(scores, plan.ld, B, cap, 0, seq_lens, topk, idx_c, stream);
+    e = dsa::launch_topk(scores, plan.ld, B, cap, 0, seq_lens, topk, idx_c, topk_ws, stream);
     if (e != hipSuccess) return hip_fail(e, "decode top-k launch");
     return run_attn(q, k_cache, v_cache, dtype, num_blocks, block_table, max_blocks, block_size,
                     nullptr, seq_lens, idx_c, B, topk, Hq, G, d, sm_scale, out, partials,

@@ -522,8 +522,15 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
 // A (rows) = 16 indexer heads, B (columns) = 16 keys: a lane's four results are
 // four heads of one key, reduced in-lane (ReLU, w) and then across the four
 // lane groups; all HI/16 head tiles stay in registers for the whole key loop.
-constexpr int kDecKeysPerWave = 512;   // 8 iterations of 64 keys
-constexpr int kDecKeysPerWG = kIdxWaves * kDecKeysPerWave;
+// The kernel is bound by the k^I stream (132 bytes per key), so each wave owns
+// kDecPagesPerWave consecutive pages, reads their block ids once, and keeps the
+// next page's codes and scales in flight while it computes the current page.
+constexpr int kDecPagesPerWave = 8;
+
+struct PageRegs {
+    v8i k[4];          // four 16-key tiles of the page (this lane: key 16 u + col, slice grp)
+    float scale;       // k_scale of key `lane` of the page
+};
 
 __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
@@ -532,16 +539,18 @@ __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
     const int32_t* __restrict__ seq_lens, int num_blocks, int max_blocks, int block_size, int HI,
     float* __restrict__ scores, int64_t ld, int n_split)
 {
+    // block_size is 64 here (checked by the launcher): one page = one 64-key iteration
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     const int b = work / n_split, sp = work - b * n_split;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int64_t cap = (int64_t)max_blocks * block_size;
+    const int64_t cap = (int64_t)max_blocks * 64;
     const int64_t len = seq_lens[b];
-    if (len < 1 || len > cap) return;
-    const int64_t s_begin = (int64_t)sp * kDecKeysPerWG + (int64_t)wave * kDecKeysPerWave;
-    if (s_begin >= len) return;
-    const int64_t s_end = min(len, s_begin + kDecKeysPerWave);
+    if (len < 1 || len > cap || num_blocks <= 0) return;
+    const int page0 = (sp * kIdxWaves + wave) * kDecPagesPerWave;
+    const int n_pages = (int)((len + 63) >> 6);
+    if (page0 >= n_pages) return;
+    const int np = min(kDecPagesPerWave, n_pages - page0);
 
     // query head tiles (A) and their weights: tile m covers heads 16 m .. 16 m + 15
     const int n_ht = (HI + 15) >> 4;
@@ -560,25 +569,27 @@ __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
         }
     }
     const float qs = q_scale[b];
-    const int32_t* bt = block_table + (int64_t)b * max_blocks;
+    // block ids of this wave's pages (-1 when outside the cache)
+    int blk_l = -1;
+    if (lane < np) {
+        const int v = block_table[(int64_t)b * max_blocks + page0 + lane];
+        blk_l = (v >= 0 && v < num_blocks) ? v : -1;
+    }
+    // unconditional loads (an invalid block reads block 0 and is masked to -inf
+    // afterwards): no branch around them, so the next page stays in flight
+    auto fetch = [&](int i, PageRegs& r) {
+        const int blk = __shfl(blk_l, i, 64);
+        const int64_t base = (int64_t)(blk < 0 ? 0 : blk) * 64;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r.k[u] = load32B(kcache + (base + 16 * u + col) * 128 + grp * 32);
+        r.scale = kscale[base + lane];
+    };
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     float* __restrict__ out = scores + (int64_t)b * ld;
-
-    for (int64_t s0 = s_begin; s0 < s_end; s0 += 64) {
-        // four 16-key tiles; this lane's key in tile u is s0 + 16 u + col
-        v8i kb[4];
-        int64_t row[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t s = s0 + 16 * u + col;
-            row[u] = -1;
-            if (s < s_end) {
-                const int blk = bt[s / block_size];
-                if (blk >= 0 && blk < num_blocks) row[u] = (int64_t)blk * block_size + s % block_size;
-            }
-            kb[u] = row[u] >= 0 ? load32B(kcache + row[u] * 128 + grp * 32)
-                                : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+    PageRegs cur, nxt;
+    fetch(0, cur);
+    for (int i = 0; i < np; ++i) {
+        fetch(min(i + 1, np - 1), nxt);               // the last one re-reads this page (L2)
         float part[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -586,24 +597,23 @@ __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 if (m < n_ht) {
-                    const v4f d = mfma_fp8_16x16x128(qa[m], kb[u], zero);
+                    const v4f d = mfma_fp8_16x16x128(qa[m], cur.k[u], zero);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc += wv[m][i] * fmaxf(d[i], 0.f);
+                    for (int e = 0; e < 4; ++e) acc += wv[m][e] * fmaxf(d[e], 0.f);
                 }
             }
             acc += __shfl_xor(acc, 16, 64);
             acc += __shfl_xor(acc, 32, 64);
             part[u] = acc;
         }
-        // lane group u writes tile u: 64 consecutive keys per store instruction
+        // lane group u holds tile u's sums: lane l writes key 16 (l / 16) + l % 16 = l
         float mine = part[0];
 #pragma unroll
         for (int u = 1; u < 4; ++u) mine = (grp == u) ? part[u] : mine;
-        int64_t my_row = row[0];
-#pragma unroll
-        for (int u = 1; u < 4; ++u) my_row = (grp == u) ? row[u] : my_row;
-        const int64_t s = s0 + lane;
-        if (s < s_end) out[s] = (my_row >= 0) ? mine * (qs * kscale[my_row]) : -INFINITY;
+        const int64_t s = (int64_t)(page0 + i) * 64 + lane;
+        const bool valid = __shfl(blk_l, i, 64) >= 0;
+        if (s < len) out[s] = valid ? mine * (qs * cur.scale) : -INFINITY;
+        cur = nxt;
     }
 }
 
@@ -661,8 +671,9 @@ hipError_t launch_index_fp8_paged(const uint8_t* q_idx, const float* q_scale, co
                                   int num_blocks, int max_blocks, int block_size, int HI,
                                   float* scores, int64_t ld, hipStream_t stream)
 {
-    const int64_t cap = (int64_t)max_blocks * block_size;
-    const int n_split = (int)((cap + kDecKeysPerWG - 1) / kDecKeysPerWG);
+    if (block_size != 64) return hipErrorInvalidValue;
+    const int pages_per_wg = kIdxWaves * kDecPagesPerWave;
+    const int n_split = (max_blocks + pages_per_wg - 1) / pages_per_wg;
     const int64_t n = (int64_t)B * n_split;
     if (n == 0) return hipSuccess;
     if (n > INT32_MAX) return hipErrorInvalidValue;

@@ -26,9 +26,11 @@ hipError_t launch_index_fp8_paged(const uint8_t* q_idx, const float* q_scale, co
                                   float* scores, int64_t ld, hipStream_t stream);
 
 // Top-k per row.  Candidates of row i: 0 .. n_i-1 with n_i = q_pos0 + i + 1, or
-// n_i = clamp(row_len[i], 0, Tk) when row_len is given.
+// n_i = row_len[i] when row_len is given (0 if outside [0, Tk]).  With a workspace of
+// topk_workspace_bytes() bytes, few long rows are split into segments and merged.
+size_t topk_workspace_bytes(int Tq, int Tk, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t q_pos0,
-                       const int32_t* row_len, int k, int32_t* idx, hipStream_t stream);
+                       const int32_t* row_len, int k, int32_t* idx, void* ws, hipStream_t stream);
 
 struct AttnArgs {
     const void* q; const void* k; const void* v; void* out;

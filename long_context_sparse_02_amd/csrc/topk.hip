@@ -196,9 +196,25 @@ constexpr int kCap = 8192;                // LDS candidate capacity
 constexpr int kSampleRuns = 256;          // sample: 256 runs of 16 contiguous scores
 constexpr int kSample = kSampleRuns * 16;
 
+// Row length of workgroup row `row`: q_pos0 + row + 1, or row_len[row] when given
+// (an out-of-range length means no candidates).
+__device__ __forceinline__ int64_t row_length(int row, int Tk, int64_t q_pos0,
+                                              const int32_t* __restrict__ row_len) {
+    if (!row_len) return q_pos0 + row + 1;
+    const int64_t n = row_len[row];
+    return (n < 0 || n > Tk) ? 0 : n;
+}
+
+// With nseg == 1 a workgroup selects the top-k of a whole row into idx.  With
+// nseg > 1 (rows too few to fill the GPU) workgroup (row, sg) selects the top-k
+// of the row's positions [sg * seg_len, (sg + 1) * seg_len) into its slot of
+// idx ([rows, nseg, k], ascending absolute positions, -1 padded); the union of
+// the segments' selections contains the row's selection, ties included (each
+// segment keeps its lowest-position ties), and topk_merge_kernel finishes it.
 __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
     const float* __restrict__ scores, int64_t ld, int Tk, int64_t q_pos0,
-    const int32_t* __restrict__ row_len, int k, int32_t* __restrict__ idx)
+    const int32_t* __restrict__ row_len, int k, int nseg, int64_t seg_len,
+    int32_t* __restrict__ idx)
 {
     __shared__ uint32_t ck[kCap];             // candidate keys, in position order
     __shared__ int32_t ci[kCap];              // their positions (the sample reuses this array)
@@ -206,28 +222,25 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
     __shared__ uint32_t wsum[2 * kTopkWaves];
     __shared__ uint32_t sh[4];
 
-    const int row = blockIdx.x;
+    const int row = blockIdx.x / nseg, sg = blockIdx.x - row * nseg;
     const int tid = threadIdx.x;
-    int64_t n;
-    if (row_len) {
-        n = row_len[row];
-        if (n < 0 || n > Tk) n = 0;                   // invalid length: no candidates
-    } else {
-        n = q_pos0 + row + 1;
-    }
-    int32_t* __restrict__ out = idx + (int64_t)row * k;
+    const int64_t n_row = row_length(row, Tk, q_pos0, row_len);
+    const int64_t begin = nseg > 1 ? (int64_t)sg * seg_len : 0;
+    int64_t n = nseg > 1 ? min(seg_len, n_row - begin) : n_row;
+    if (n < 0) n = 0;
+    int32_t* __restrict__ out = idx + (int64_t)blockIdx.x * k;
     if (n <= k) {                                     // short row: everything is selected
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? (int32_t)(begin + i) : -1;
         return;
     }
-    const float* __restrict__ src = scores + (int64_t)row * ld;
+    const float* __restrict__ src = scores + (int64_t)row * ld + begin;
     int64_t m;                                        // number of candidates in LDS
     bool in_lds = true;
 
     if (n <= kCap) {
         for (int64_t i = tid; i < n; i += kTopkThreads) {
             ck[i] = order_key(src[i]);
-            ci[i] = (int32_t)i;
+            ci[i] = (int32_t)(begin + i);
         }
         m = n;
         __syncthreads();
@@ -292,7 +305,7 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
                     for (int e = 0; e < 4; ++e) {
                         const int j = 4 * q + e;
                         if (flag & (1u << j)) {
-                            if (p < (uint32_t)kCap) { ck[p] = order_key(v[e]); ci[p] = (int32_t)(i0 + j); }
+                            if (p < (uint32_t)kCap) { ck[p] = order_key(v[e]); ci[p] = (int32_t)(begin + i0 + j); }
                             ++p;
                         }
                     }
@@ -318,21 +331,104 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
     } else {
         // 4. fallback: the same exact select and compaction over the row in memory
         auto get_g = [&](int64_t i) { return order_key(src[i]); };
-        auto pos_g = [&](int64_t i) { return (int32_t)i; };
+        auto pos_g = [&](int64_t i) { return (int32_t)(begin + i); };
         key_range(get_g, n, wsum, kmin, kmax);
         radix_select(get_g, n, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
         compact(get_g, pos_g, n, kmin, prefix, mask, need, wsum, out);
     }
 }
 
+// Second stage of a segmented top-k: the nseg * k candidate positions of a row
+// (ascending within and across segments) are gathered, with their scores, into
+// LDS in position order and the exact select + ordered compaction produce the
+// row's final ascending set.
+__global__ __launch_bounds__(kTopkThreads, 2) void topk_merge_kernel(
+    const float* __restrict__ scores, int64_t ld, int Tk, int64_t q_pos0,
+    const int32_t* __restrict__ row_len, int k, int nseg, const int32_t* __restrict__ cand,
+    int32_t* __restrict__ idx)
+{
+    __shared__ uint32_t ck[kCap];
+    __shared__ int32_t ci[kCap];
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t wsum[2 * kTopkWaves];
+    __shared__ uint32_t sh[4];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t n = row_length(row, Tk, q_pos0, row_len);
+    int32_t* __restrict__ out = idx + (int64_t)row * k;
+    if (n <= k) {
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+        return;
+    }
+    const float* __restrict__ src = scores + (int64_t)row * ld;
+    const int32_t* __restrict__ c = cand + (int64_t)row * nseg * k;
+    const int total_in = nseg * k;                    // <= kCap (checked by the launcher)
+    uint32_t base_cnt = 0;
+    for (int c0 = 0; c0 < total_in; c0 += 4 * kTopkThreads) {
+        const int i0 = c0 + tid * 4;
+        int32_t pos[4];
+        uint32_t flag = 0, cnt = 0;
+        for (int e = 0; e < 4; ++e) {
+            pos[e] = (i0 + e < total_in) ? c[i0 + e] : -1;
+            if (pos[e] >= 0) { flag |= 1u << e; ++cnt; }
+        }
+        uint32_t total;
+        uint32_t p = base_cnt + block_excl_scan(cnt, wsum, &total);
+        for (int e = 0; e < 4; ++e) {
+            if (flag & (1u << e)) {
+                ck[p] = order_key(src[pos[e]]);
+                ci[p] = pos[e];
+                ++p;
+            }
+        }
+        base_cnt += total;
+    }
+    __syncthreads();
+    const int64_t m = base_cnt;
+    auto get_c = [&](int64_t i) { return ck[i]; };
+    auto pos_c = [&](int64_t i) { return ci[i]; };
+    uint32_t kmin, kmax, prefix, mask, need;
+    key_range(get_c, m, wsum, kmin, kmax);
+    radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
+    compact(get_c, pos_c, m, kmin, prefix, mask, need, wsum, out);
+}
+
 }  // namespace
 
+int topk_num_segments(int Tq, int Tk, int k)
+{
+    // few rows: split each row so that >= 256 workgroups stream the scores
+    if (Tq <= 0 || Tq >= 128 || (int64_t)Tk < 4 * (int64_t)k) return 1;
+    int nseg = kCap / k;
+    if (nseg > 8) nseg = 8;
+    while (nseg > 1 && (int64_t)Tq * nseg > 512) nseg >>= 1;
+    return nseg < 2 ? 1 : nseg;
+}
+
+size_t topk_workspace_bytes(int Tq, int Tk, int k)
+{
+    const int nseg = topk_num_segments(Tq, Tk, k);
+    return nseg > 1 ? (size_t)Tq * nseg * k * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t q_pos0,
-                       const int32_t* row_len, int k, int32_t* idx, hipStream_t stream)
+                       const int32_t* row_len, int k, int32_t* idx, void* ws, hipStream_t stream)
 {
     if (Tq == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, scores, ld, Tk,
-                       q_pos0, row_len, k, idx);
+    const int nseg = ws ? topk_num_segments(Tq, Tk, k) : 1;
+    if (nseg == 1) {
+        hipLaunchKernelGGL(topk_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, scores, ld, Tk,
+                           q_pos0, row_len, k, 1, (int64_t)Tk, idx);
+        return hipGetLastError();
+    }
+    const int64_t seg_len = ((int64_t)Tk + nseg - 1) / nseg;
+    int32_t* cand = static_cast<int32_t*>(ws);
+    hipLaunchKernelGGL(topk_kernel, dim3(Tq * nseg), dim3(kTopkThreads), 0, stream, scores, ld, Tk,
+                       q_pos0, row_len, k, nseg, seg_len, cand);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, scores, ld, Tk,
+                       q_pos0, row_len, k, nseg, cand, idx);
     return hipGetLastError();
 }
 

@@ -95,7 +95,8 @@ def test_topk_argument_checks(lib):
     assert f(*bad) == 1
     bad = list(ok); bad[1] = 17
     assert f(*bad) == 1
-    assert lib.dsa_topk_workspace_size(8, 16, 4) == 0
+    assert lib.dsa_topk_workspace_size(8192, 131072, 2048) == 0   # many rows: one pass each
+    assert lib.dsa_topk_workspace_size(64, 262144, 2048) >= 64 * 4 * 2048 * 4   # few long rows: split
 
 
 def test_attention_argument_checks(lib):
@@ -135,7 +136,9 @@ def test_prefill_and_decode_workspace_checks(lib):
     assert fd(*dargs) == 3
     dargs[19] = 64
     assert fd(*dargs) == 2                                      # decode dI must be 128
-    dargs[19] = 128; dargs[10] = None
+    dargs[19] = 128; dargs[14] = 16
+    assert fd(*dargs) == 2                                      # 64-token blocks only
+    dargs[14] = 64; dargs[10] = None
     assert fd(*dargs) == 1                                      # seq_lens NULL
 
 

@@ -137,6 +137,34 @@ def test_topk_fallback_paths_exact():
         assert np.array_equal(got[0], ref[0])
 
 
+def test_topk_few_long_rows_split_and_merged():
+    """Few long rows (the decode shape) run as segments plus a merge when a workspace is given;
+    the sets must equal the oracle's on the same scores, including a row with heavy ties."""
+    _say("topk segmented")
+    rng = np.random.default_rng(23)
+    Tq, Tk, k = 6, 70000, 2048
+    s = rng.standard_normal((Tq, Tk)).astype(np.float32)
+    s[2] = rng.integers(0, 4, Tk).astype(np.float32)          # ties across segment borders
+    s[3, :5000] = 7.0                                         # all the best in the first segment
+    lens = np.array([Tk, Tk - 1, 50001, 30000, 2048, 1], dtype=np.int32)
+    ld = (Tk + 3) // 4 * 4
+    buf = torch.zeros((Tq, ld), dtype=torch.float32)
+    buf[:, :Tk] = torch.from_numpy(s)
+    sc = buf.to(DEV)
+    # through the decode path's row lengths: one call of dsa_decode-style top-k via the public API
+    # uses q_pos0 positions, so emulate per-row lengths with one call per row
+    for r in range(Tq):
+        n = int(lens[r])
+        row = sc[r:r + 1].contiguous()
+        idx = torch.empty(1, k, dtype=torch.int32, device=DEV)
+        nws = dsa.dsa_topk_workspace_size(1, n, k)
+        ws = dsa.workspace(nws) if nws else None
+        dsa.dsa_topk(row, ld, 1, n, n - 1, k, idx, ws, nws)
+        torch.cuda.synchronize()
+        ref, _ = oracle.topk(s[r:r + 1, :n].astype(np.float64), [n - 1], k)
+        assert np.array_equal(to_np(idx)[0], ref[0]), "row %d" % r
+
+
 def test_topk_many_rows_one_call():
     """A chunk of consecutive rows in one launch (row i at position q_pos0 + i)."""
     _say("topk many rows")
