@@ -186,6 +186,20 @@ def run_prefill_bench(args, dsa, W, torch):
     return cfg, x, idx, out, ms_step, kern, fused_ms, same
 
 
+def adjacent_union(idx, L, k, groups=64, width=16, seed=0):
+    """Mean number of distinct positions selected by `width` adjacent queries, over
+    `groups` seeded groups of rows with t >= k (the structure statistic of adjacent-query
+    Top-KV deduplication)."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    starts = torch.randint(k, L - width, (groups,), generator=g).tolist()
+    sizes = []
+    for s0 in starts:
+        sel = idx[s0:s0 + width].reshape(-1)
+        sizes.append(int(torch.unique(sel[sel >= 0]).numel()))
+    return sum(sizes) / len(sizes)
+
+
 def run_profile_kernel(args, dsa, W, torch):
     """One kernel of the staged prefill, on one chunk, for counter collection."""
     cfg = W.ALL[args.workload]
@@ -341,6 +355,7 @@ def main():
         "roofline": roofline,
         "kernels": kern,
         "fused_prefill_ms": round(fused_ms, 3), "fused_equals_staged": same,
+        "adjacent16_union": round(adjacent_union(idx, cfg.L, cfg.k), 1),
     }
     del x, idx, out
     torch.cuda.empty_cache()

@@ -337,12 +337,16 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 
 }  // namespace
 
+#ifndef DSA_ATTN_MIN_SPLIT
+#define DSA_ATTN_MIN_SPLIT 128
+#endif
+
 int attn_num_splits(int Tq, int topk)
 {
-    // Enough workgroups to fill 256 CUs several times over; splits of >= 128 positions.
+    // Enough workgroups to fill 256 CUs several times over; splits of >= DSA_ATTN_MIN_SPLIT positions.
     if (Tq >= 2048) return 1;
     int ns = 1;
-    while ((int64_t)Tq * ns < 2048 && topk / (ns * 2) >= 128) ns *= 2;
+    while ((int64_t)Tq * ns < 2048 && topk / (ns * 2) >= DSA_ATTN_MIN_SPLIT) ns *= 2;
     return ns;
 }
 

@@ -525,13 +525,17 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
 // The kernel is bound by the k^I stream (132 bytes per key), so each wave owns
 // kDecPagesPerWave consecutive pages, reads their block ids once, and keeps the
 // next page's codes and scales in flight while it computes the current page.
-constexpr int kDecPagesPerWave = 8;
+#ifndef DSA_DEC_PAGES_PER_WAVE
+#define DSA_DEC_PAGES_PER_WAVE 8
+#endif
+constexpr int kDecPagesPerWave = DSA_DEC_PAGES_PER_WAVE;
 
 struct PageRegs {
     v8i k[4];          // four 16-key tiles of the page (this lane: key 16 u + col, slice grp)
     float scale;       // k_scale of key `lane` of the page
 };
 
+template <int NHT>                                 // 16-head tiles held in registers
 __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ kcache,
@@ -553,19 +557,17 @@ __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
     const int np = min(kDecPagesPerWave, n_pages - page0);
 
     // query head tiles (A) and their weights: tile m covers heads 16 m .. 16 m + 15
-    const int n_ht = (HI + 15) >> 4;
-    v8i qa[8];
-    float wv[8][4];
+    v8i qa[NHT];
+    float wv[NHT][4];
     const uint8_t* qrow = q_idx + (int64_t)b * HI * 128;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < NHT; ++m) {
         const int h = 16 * m + col;
-        qa[m] = (m < n_ht && h < HI) ? load32B(qrow + (int64_t)h * 128 + grp * 32)
-                                     : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        qa[m] = (h < HI) ? load32B(qrow + (int64_t)h * 128 + grp * 32) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int hh = 16 * m + 4 * grp + i;
-            wv[m][i] = (m < n_ht && hh < HI) ? w[(int64_t)b * HI + hh] : 0.f;
+            wv[m][i] = (hh < HI) ? w[(int64_t)b * HI + hh] : 0.f;
         }
     }
     const float qs = q_scale[b];
@@ -595,12 +597,10 @@ __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
         for (int u = 0; u < 4; ++u) {
             float acc = 0.f;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                if (m < n_ht) {
-                    const v4f d = mfma_fp8_16x16x128(qa[m], cur.k[u], zero);
+            for (int m = 0; m < NHT; ++m) {
+                const v4f d = mfma_fp8_16x16x128(qa[m], cur.k[u], zero);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc += wv[m][e] * fmaxf(d[e], 0.f);
-                }
+                for (int e = 0; e < 4; ++e) acc += wv[m][e] * fmaxf(d[e], 0.f);
             }
             acc += __shfl_xor(acc, 16, 64);
             acc += __shfl_xor(acc, 32, 64);
@@ -677,9 +677,14 @@ hipError_t launch_index_fp8_paged(const uint8_t* q_idx, const float* q_scale, co
     const int64_t n = (int64_t)B * n_split;
     if (n == 0) return hipSuccess;
     if (n > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(index_fp8_paged_kernel, dim3((unsigned)n), dim3(256), 0, stream, q_idx,
-                       q_scale, w, kidx_cache, kidx_scale, block_table, seq_lens, num_blocks,
-                       max_blocks, block_size, HI, scores, ld, n_split);
+    if (HI <= 64)
+        hipLaunchKernelGGL(index_fp8_paged_kernel<4>, dim3((unsigned)n), dim3(256), 0, stream, q_idx,
+                           q_scale, w, kidx_cache, kidx_scale, block_table, seq_lens, num_blocks,
+                           max_blocks, block_size, HI, scores, ld, n_split);
+    else
+        hipLaunchKernelGGL(index_fp8_paged_kernel<8>, dim3((unsigned)n), dim3(256), 0, stream, q_idx,
+                           q_scale, w, kidx_cache, kidx_scale, block_table, seq_lens, num_blocks,
+                           max_blocks, block_size, HI, scores, ld, n_split);
     return hipGetLastError();
 }
 
