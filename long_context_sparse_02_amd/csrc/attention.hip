@@ -8,10 +8,11 @@
 // bf16 kernel: one workgroup (4 waves) per query row, wave w handles groups
 // w, w+4, ...; all the row's heads share the one gathered index list.  Per
 // step of 32 selected positions a wave
-//   - gathers the 32 K rows of its group straight into MFMA operand registers
-//     (each lane reads 64 contiguous bytes of one row, four lanes cover the
-//     256-byte row) and the 32 V rows with 16-byte coalesced loads into a
-//     per-wave LDS tile;
+//   - gathers the 32 K rows and 32 V rows of its group with full-line requests
+//     (16 lanes cover one 256-byte row, one instruction four rows) and stores
+//     them into per-wave LDS tiles: the gather is bound by the number of
+//     outstanding L1 misses per CU, so whole-line requests matter more than the
+//     extra LDS round trip for K;
 //   - computes S^T = K q^T on the bf16 16x16x32 matrix core (rows = positions,
 //     columns = the group's heads, padded to 16);
 //   - runs an online softmax in the exp2 domain; a lane's softmax values are
@@ -34,8 +35,7 @@ constexpr int kVPitch = 136;              // LDS row pitch of the V tile (bf16 e
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct KVStep {
-    v4i ka[4];                            // K tile rows 0..15  (this lane: row col, 64 bytes)
-    v4i kb[4];                            // K tile rows 16..31
+    v4i kk[8];                            // K rows (lane >> 4) + 4 it, 16 bytes each
     v4i vv[8];                            // V rows (lane >> 4) + 4 it, 16 bytes each
     uint32_t valid;                       // bit r: entry r of the step is a usable position
 };
@@ -66,21 +66,20 @@ __device__ __forceinline__ void load_step(const AttnArgs& p, const int32_t* __re
     const int G = p.G;
     const uint16_t* __restrict__ K = static_cast<const uint16_t*>(p.k);
     const uint16_t* __restrict__ V = static_cast<const uint16_t*>(p.v);
-    // invalid entries read row 0 (in bounds); their logits are masked to -inf and their V
-    // values zeroed below, so whatever row 0 holds cannot reach the result
-    const int ra = max(__shfl(prow, col, 64), 0), rb = max(__shfl(prow, 16 + col, 64), 0);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        st.ka[m] = *reinterpret_cast<const v4i*>(K + ((int64_t)ra * G + g) * 128 + grp * 32 + 8 * m);
-        st.kb[m] = *reinterpret_cast<const v4i*>(K + ((int64_t)rb * G + g) * 128 + grp * 32 + 8 * m);
-    }
+    // Both K and V rows are gathered with full-line requests: lane l reads 16 bytes of row
+    // (l >> 4) + 4 it, so one instruction covers four whole 256-byte rows.  Invalid entries
+    // read row 0 (in bounds); their logits are masked to -inf and their V values zeroed, so
+    // whatever row 0 holds cannot reach the result.
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int r = __shfl(prow, (lane >> 4) + 4 * it, 64);
-        const v4i x = *reinterpret_cast<const v4i*>(V + ((int64_t)max(r, 0) * G + g) * 128 + (lane & 15) * 8);
+        const int64_t off = ((int64_t)max(r, 0) * G + g) * 128 + (lane & 15) * 8;
+        st.kk[it] = *reinterpret_cast<const v4i*>(K + off);
+        const v4i x = *reinterpret_cast<const v4i*>(V + off);
         const int keep = r >= 0 ? -1 : 0;
         st.vv[it] = v4i{x.x & keep, x.y & keep, x.z & keep, x.w & keep};
     }
+    (void)col; (void)grp;
 }
 
 template <bool PAGED>
@@ -89,6 +88,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
                                                                   float* __restrict__ partials)
 {
     __shared__ __attribute__((aligned(16))) uint16_t vt[kAttnWaves][kStep][kVPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t kt[kAttnWaves][kStep][kVPitch];
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     const int row = work / nsplit, split = work - row * nsplit;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -110,6 +110,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
     const float scale = p.sm_scale * kLog2e;
     const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
     uint16_t* vtile = &vt[wave][0][0];
+    uint16_t* ktile = &kt[wave][0][0];
 
     for (int g = wave; g < p.G; g += kAttnWaves) {
         const int head = g * hpg + col;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             v4i x = {0, 0, 0, 0};
-            if (col < hpg) x = *reinterpret_cast<const v4i*>(Q + ((int64_t)row * p.Hq + head) * 128 + grp * 32 + 8 * m);
+            if (col < hpg) x = *reinterpret_cast<const v4i*>(Q + ((int64_t)row * p.Hq + head) * 128 + (4 * m + grp) * 8);
             qb[m] = __builtin_bit_cast(v8bf, x);
         }
         float m_run = -INFINITY, l_part = 0.f;
@@ -128,26 +129,33 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
         KVStep cur, nxt;
         if (k_begin < k_end) load_step<PAGED>(p, idx_row, k_begin, k_end, seq, len, g, lane, cur);
         for (int kb0 = k_begin; kb0 < k_end; kb0 += kStep) {
-            // V rows of this step into the wave's LDS tile
+            // K and V rows of this step into the wave's LDS tiles
 #pragma unroll
-            for (int it = 0; it < 8; ++it)
-                *reinterpret_cast<v4i*>(vtile + ((lane >> 4) + 4 * it) * kVPitch + (lane & 15) * 8) = cur.vv[it];
+            for (int it = 0; it < 8; ++it) {
+                const int off = ((lane >> 4) + 4 * it) * kVPitch + (lane & 15) * 8;
+                *reinterpret_cast<v4i*>(ktile + off) = cur.kk[it];
+                *reinterpret_cast<v4i*>(vtile + off) = cur.vv[it];
+            }
+            const uint32_t valid = cur.valid;
             if (kb0 + kStep < k_end)
                 load_step<PAGED>(p, idx_row, kb0 + kStep, k_end, seq, len, g, lane, nxt);
 
-            // S^T (positions x heads) for the two 16-position tiles
+            // S^T (positions x heads) for the two 16-position tiles; MFMA m takes head dims
+            // 8 (4 m + grp) .. +8 from lane group grp, the same slots as the q operand
             v4f sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                sa = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, cur.ka[m]), qb[m], sa);
-                sb = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, cur.kb[m]), qb[m], sb);
+                const v4i ka = *reinterpret_cast<const v4i*>(ktile + col * kVPitch + (4 * m + grp) * 8);
+                const v4i kb = *reinterpret_cast<const v4i*>(ktile + (16 + col) * kVPitch + (4 * m + grp) * 8);
+                sa = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, ka), qb[m], sa);
+                sb = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, kb), qb[m], sb);
             }
             float sl[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * grp + i;
-                sl[i] = ((cur.valid >> r) & 1u) ? sa[i] * scale : -INFINITY;
-                sl[4 + i] = ((cur.valid >> (16 + r)) & 1u) ? sb[i] * scale : -INFINITY;
+                sl[i] = ((valid >> r) & 1u) ? sa[i] * scale : -INFINITY;
+                sl[4 + i] = ((valid >> (16 + r)) & 1u) ? sb[i] * scale : -INFINITY;
             }
             float mx = sl[0];
 #pragma unroll
