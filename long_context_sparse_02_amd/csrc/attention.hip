@@ -346,7 +346,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 }  // namespace
 
 #ifndef DSA_ATTN_MIN_SPLIT
-#define DSA_ATTN_MIN_SPLIT 128
+#define DSA_ATTN_MIN_SPLIT 256
 #endif
 
 int attn_num_splits(int Tq, int topk)

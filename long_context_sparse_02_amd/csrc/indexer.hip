@@ -521,64 +521,75 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
 // Paged decode indexer: one query token per sequence, keys in a paged cache.
 // A (rows) = 16 indexer heads, B (columns) = 16 keys: a lane's four results are
 // four heads of one key, reduced in-lane (ReLU, w) and then across the four
-// lane groups; all HI/16 head tiles stay in registers for the whole key loop.
-// The kernel is bound by the k^I stream (132 bytes per key), so each wave owns
-// kDecPagesPerWave consecutive pages, reads their block ids once, and keeps the
-// next page's codes and scales in flight while it computes the current page.
+// lane groups.  The kernel is bound by the k^I stream (132 bytes per key), so
+// registers go to pages in flight: the workgroup's four waves share the query's
+// head tiles and weights through LDS, each wave owns kDecPagesPerWave
+// consecutive pages, reads their block ids once, and keeps the next
+// kDecDepth pages' codes and scales in flight while it computes the current one.
 #ifndef DSA_DEC_PAGES_PER_WAVE
 #define DSA_DEC_PAGES_PER_WAVE 8
 #endif
+#ifndef DSA_DEC_DEPTH
+#define DSA_DEC_DEPTH 1
+#endif
 constexpr int kDecPagesPerWave = DSA_DEC_PAGES_PER_WAVE;
+static_assert(kDecPagesPerWave >= 1 && kDecPagesPerWave <= 64, "block ids live one per lane");
+constexpr int kDecDepth = DSA_DEC_DEPTH;
+constexpr int kDecQPitch = 144;                    // bytes per head row in LDS (conflict-free b128 reads)
 
 struct PageRegs {
     v8i k[4];          // four 16-key tiles of the page (this lane: key 16 u + col, slice grp)
     float scale;       // k_scale of key `lane` of the page
 };
 
-template <int NHT>                                 // 16-head tiles held in registers
-__global__ __launch_bounds__(256) void index_fp8_paged_kernel(
+#ifndef DSA_DEC_WAVES
+#define DSA_DEC_WAVES 4
+#endif
+template <int NHT>                                 // 16-head tiles of the query
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_DEC_WAVES)))
+void index_fp8_paged_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ kcache,
     const float* __restrict__ kscale, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int num_blocks, int max_blocks, int block_size, int HI,
     float* __restrict__ scores, int64_t ld, int n_split)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[16 * NHT * kDecQPitch];
+    __shared__ __attribute__((aligned(16))) float w_lds[16 * NHT];
     // block_size is 64 here (checked by the launcher): one page = one 64-key iteration
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     const int b = work / n_split, sp = work - b * n_split;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int64_t cap = (int64_t)max_blocks * 64;
-    const int64_t len = seq_lens[b];
-    if (len < 1 || len > cap || num_blocks <= 0) return;
     const int page0 = (sp * kIdxWaves + wave) * kDecPagesPerWave;
-    const int n_pages = (int)((len + 63) >> 6);
-    if (page0 >= n_pages) return;
-    const int np = min(kDecPagesPerWave, n_pages - page0);
 
-    // query head tiles (A) and their weights: tile m covers heads 16 m .. 16 m + 15
-    v8i qa[NHT];
-    float wv[NHT][4];
+    // 1. one round trip for everything the pages depend on: the sequence length,
+    //    the block ids of this wave's pages (clamped into the table row), the
+    //    query's head rows (heads >= HI read head HI-1 and are zeroed) and weights
+    const int64_t len = seq_lens[b];
+    const int bt = block_table[(int64_t)b * max_blocks +
+                               min(page0 + min(lane, kDecPagesPerWave - 1), max_blocks - 1)];
+    constexpr int kQChunks = 16 * NHT * 8;         // 16-byte chunks of the head tiles
+    constexpr int kQPer = (kQChunks + 255) / 256;
+    v4i qv[kQPer];
     const uint8_t* qrow = q_idx + (int64_t)b * HI * 128;
 #pragma unroll
-    for (int m = 0; m < NHT; ++m) {
-        const int h = 16 * m + col;
-        qa[m] = (h < HI) ? load32B(qrow + (int64_t)h * 128 + grp * 32) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = 16 * m + 4 * grp + i;
-            wv[m][i] = (hh < HI) ? w[(int64_t)b * HI + hh] : 0.f;
-        }
+    for (int r = 0; r < kQPer; ++r) {
+        const int c = min(tid + 256 * r, kQChunks - 1), h = c >> 3;
+        qv[r] = *reinterpret_cast<const v4i*>(qrow + (int64_t)min(h, HI - 1) * 128 + (c & 7) * 16);
     }
+    const float wq = w[(int64_t)b * HI + min(tid, HI - 1)];
     const float qs = q_scale[b];
-    // block ids of this wave's pages (-1 when outside the cache)
-    int blk_l = -1;
-    if (lane < np) {
-        const int v = block_table[(int64_t)b * max_blocks + page0 + lane];
-        blk_l = (v >= 0 && v < num_blocks) ? v : -1;
-    }
+
+    const int64_t cap = (int64_t)max_blocks * 64;
+    if (len < 1 || len > cap || num_blocks <= 0) return;       // uniform over the workgroup
+    const int n_pages = (int)((len + 63) >> 6);
+    if (sp * kIdxWaves * kDecPagesPerWave >= n_pages) return;   // uniform over the workgroup
+    const int np = max(0, min(kDecPagesPerWave, n_pages - page0));
+    // 2. block ids of this wave's pages (-1 when outside the cache)
+    const int blk_l = (lane < np && bt >= 0 && bt < num_blocks) ? bt : -1;
     // unconditional loads (an invalid block reads block 0 and is masked to -inf
-    // afterwards): no branch around them, so the next page stays in flight
+    // afterwards): no branch around them, so the next pages stay in flight
     auto fetch = [&](int i, PageRegs& r) {
         const int blk = __shfl(blk_l, i, 64);
         const int64_t base = (int64_t)(blk < 0 ? 0 : blk) * 64;
@@ -586,34 +597,70 @@ __global__ __launch_bounds__(256) void index_fp8_paged_kernel(
         for (int u = 0; u < 4; ++u) r.k[u] = load32B(kcache + (base + 16 * u + col) * 128 + grp * 32);
         r.scale = kscale[base + lane];
     };
+    const int last = max(np - 1, 0);
+    PageRegs ring[kDecDepth + 1];
+    float res[kDecPagesPerWave];                   // scores, stored after the page loop
+#pragma unroll
+    for (int i = 0; i < kDecDepth; ++i) fetch(min(i, last), ring[i]);
+    // 3. stage the head tiles and weights while the first pages are in flight
+#pragma unroll
+    for (int r = 0; r < kQPer; ++r) {
+        const int c = tid + 256 * r;
+        if (c < kQChunks) {
+            const int h = c >> 3;
+            *reinterpret_cast<v4i*>(q_lds + h * kDecQPitch + (c & 7) * 16) =
+                (h < HI) ? qv[r] : v4i{0, 0, 0, 0};
+        }
+    }
+    if (tid < 16 * NHT) w_lds[tid] = (tid < HI) ? wq : 0.f;
+    __syncthreads();
+
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     float* __restrict__ out = scores + (int64_t)b * ld;
-    PageRegs cur, nxt;
-    fetch(0, cur);
-    for (int i = 0; i < np; ++i) {
-        fetch(min(i + 1, np - 1), nxt);               // the last one re-reads this page (L2)
-        float part[4];
+    // fully unrolled (a rolled loop makes the compiler wait on in-flight pages at
+    // the back edge): ring slots are compile-time constants
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            float acc = 0.f;
+    for (int i = 0; i < kDecPagesPerWave; ++i) {
+        if (i >= np) break;
+        fetch(min(i + kDecDepth, last), ring[(i + kDecDepth) % (kDecDepth + 1)]);
+        const PageRegs& cur = ring[i % (kDecDepth + 1)];
+        // keep the compiler from hoisting the loop-invariant LDS tiles into registers
+        asm volatile("" ::: "memory");
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < NHT; ++m) {
-                const v4f d = mfma_fp8_16x16x128(qa[m], cur.k[u], zero);
+        for (int m = 0; m < NHT; ++m) {
+            const uint8_t* qa_p = q_lds + (16 * m + col) * kDecQPitch + grp * 32;
+            v8i qa;
+            const v4i lo = *reinterpret_cast<const v4i*>(qa_p);
+            const v4i hi = *reinterpret_cast<const v4i*>(qa_p + 16);
+            qa[0] = lo[0]; qa[1] = lo[1]; qa[2] = lo[2]; qa[3] = lo[3];
+            qa[4] = hi[0]; qa[5] = hi[1]; qa[6] = hi[2]; qa[7] = hi[3];
+            const v4f wv = *reinterpret_cast<const v4f*>(w_lds + 16 * m + 4 * grp);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc += wv[m][e] * fmaxf(d[e], 0.f);
+            for (int u = 0; u < 4; ++u) {
+                const v4f d = mfma_fp8_16x16x128(qa, cur.k[u], zero);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[u] += wv[e] * fmaxf(d[e], 0.f);
             }
-            acc += __shfl_xor(acc, 16, 64);
-            acc += __shfl_xor(acc, 32, 64);
-            part[u] = acc;
         }
-        // lane group u holds tile u's sums: lane l writes key 16 (l / 16) + l % 16 = l
-        float mine = part[0];
-#pragma unroll
-        for (int u = 1; u < 4; ++u) mine = (grp == u) ? part[u] : mine;
-        const int64_t s = (int64_t)(page0 + i) * 64 + lane;
+        // acc[u] at lane (col, grp) is key 16 u + col over heads 4 grp .. 4 grp + 3 of
+        // each tile; a two-step exchange leaves lane l with key l summed over all heads
+        const bool b1 = grp & 2, b0 = grp & 1;
+        float k0 = b1 ? acc[2] : acc[0], k1 = b1 ? acc[3] : acc[1];
+        const float t0 = b1 ? acc[0] : acc[2], t1 = b1 ? acc[1] : acc[3];
+        k0 += __shfl_xor(t0, 32, 64);
+        k1 += __shfl_xor(t1, 32, 64);
+        float mine = b0 ? k1 : k0;
+        mine += __shfl_xor(b0 ? k0 : k1, 16, 64);
         const bool valid = __shfl(blk_l, i, 64) >= 0;
-        if (s < len) out[s] = valid ? mine * (qs * cur.scale) : -INFINITY;
-        cur = nxt;
+        res[i] = valid ? mine * (qs * cur.scale) : -INFINITY;
+    }
+    // score stores interleaved with the page stream slow it down: issue them last
+#pragma unroll
+    for (int i = 0; i < kDecPagesPerWave; ++i) {
+        if (i >= np) break;
+        const int64_t s = (int64_t)(page0 + i) * 64 + lane;
+        if (s < len) out[s] = res[i];
     }
 }
 

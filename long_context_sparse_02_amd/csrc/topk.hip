@@ -161,7 +161,8 @@ __device__ void radix_select(Get get, int64_t m, uint32_t R, uint32_t kmin, uint
 // (# above before it) + min(# tied before it, need).
 template <class Get, class Pos>
 __device__ void compact(Get get, Pos pos_of, int64_t m, uint32_t kmin, uint32_t prefix,
-                        uint32_t mask, uint32_t need, uint32_t* wsum, int32_t* __restrict__ out) {
+                        uint32_t mask, uint32_t need, uint32_t* wsum, int32_t* __restrict__ out,
+                        uint32_t* __restrict__ out_key = nullptr) {
     const int tid = threadIdx.x;
     uint32_t gt_base = 0, eq_base = 0;
     for (int64_t c0 = 0; c0 < m; c0 += 4 * kTopkThreads) {
@@ -180,10 +181,15 @@ __device__ void compact(Get get, Pos pos_of, int64_t m, uint32_t kmin, uint32_t 
         uint32_t eq_before = eq_base + (excl >> 16);
         for (int e = 0; e < 4; ++e) {
             if (gt & (1u << e)) {
-                out[gt_before + min(eq_before, need)] = pos_of(i0 + e);
+                const uint32_t slot = gt_before + min(eq_before, need);
+                out[slot] = pos_of(i0 + e);
+                if (out_key) out_key[slot] = get(i0 + e);
                 ++gt_before;
             } else if (eq & (1u << e)) {
-                if (eq_before < need) out[gt_before + eq_before] = pos_of(i0 + e);
+                if (eq_before < need) {
+                    out[gt_before + eq_before] = pos_of(i0 + e);
+                    if (out_key) out_key[gt_before + eq_before] = get(i0 + e);
+                }
                 ++eq_before;
             }
         }
@@ -229,11 +235,18 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
     int64_t n = nseg > 1 ? min(seg_len, n_row - begin) : n_row;
     if (n < 0) n = 0;
     int32_t* __restrict__ out = idx + (int64_t)blockIdx.x * k;
+    // segments also hand their keys to the merge stage (second half of the buffer)
+    uint32_t* __restrict__ out_key =
+        nseg > 1 ? reinterpret_cast<uint32_t*>(idx + (int64_t)gridDim.x * k) + (int64_t)blockIdx.x * k
+                 : nullptr;
+    const float* __restrict__ src = scores + (int64_t)row * ld + begin;
     if (n <= k) {                                     // short row: everything is selected
-        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? (int32_t)(begin + i) : -1;
+        for (int i = tid; i < k; i += kTopkThreads) {
+            out[i] = i < n ? (int32_t)(begin + i) : -1;
+            if (out_key && i < n) out_key[i] = order_key(src[i]);
+        }
         return;
     }
-    const float* __restrict__ src = scores + (int64_t)row * ld + begin;
     int64_t m;                                        // number of candidates in LDS
     bool in_lds = true;
 
@@ -327,28 +340,30 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
         auto pos_c = [&](int64_t i) { return ci[i]; };
         key_range(get_c, m, wsum, kmin, kmax);
         radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
-        compact(get_c, pos_c, m, kmin, prefix, mask, need, wsum, out);
+        compact(get_c, pos_c, m, kmin, prefix, mask, need, wsum, out, out_key);
     } else {
         // 4. fallback: the same exact select and compaction over the row in memory
         auto get_g = [&](int64_t i) { return order_key(src[i]); };
         auto pos_g = [&](int64_t i) { return (int32_t)(begin + i); };
         key_range(get_g, n, wsum, kmin, kmax);
         radix_select(get_g, n, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
-        compact(get_g, pos_g, n, kmin, prefix, mask, need, wsum, out);
+        compact(get_g, pos_g, n, kmin, prefix, mask, need, wsum, out, out_key);
     }
 }
 
-// Second stage of a segmented top-k: the nseg * k candidate positions of a row
-// (ascending within and across segments) are gathered, with their scores, into
-// LDS in position order and the exact select + ordered compaction produce the
-// row's final ascending set.
-__global__ __launch_bounds__(kTopkThreads, 2) void topk_merge_kernel(
+// Second stage of a segmented top-k: the nseg * k candidates of a row (positions
+// ascending within and across segments, with their keys) are copied into LDS in
+// position order and the exact select + ordered compaction produce the row's
+// final ascending set.
+constexpr int kMergeCap = 8192;           // merge stage: up to 4 segments of k = 2048
+
+__global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
     const float* __restrict__ scores, int64_t ld, int Tk, int64_t q_pos0,
     const int32_t* __restrict__ row_len, int k, int nseg, const int32_t* __restrict__ cand,
     int32_t* __restrict__ idx)
 {
-    __shared__ uint32_t ck[kCap];
-    __shared__ int32_t ci[kCap];
+    __shared__ uint32_t ck[kMergeCap];
+    __shared__ int32_t ci[kMergeCap];
     __shared__ uint32_t hist[kBins];
     __shared__ uint32_t wsum[2 * kTopkWaves];
     __shared__ uint32_t sh[4];
@@ -360,9 +375,10 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_merge_kernel(
         for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
         return;
     }
-    const float* __restrict__ src = scores + (int64_t)row * ld;
     const int32_t* __restrict__ c = cand + (int64_t)row * nseg * k;
-    const int total_in = nseg * k;                    // <= kCap (checked by the launcher)
+    const uint32_t* __restrict__ ckey =
+        reinterpret_cast<const uint32_t*>(cand + (int64_t)gridDim.x * nseg * k) + (int64_t)row * nseg * k;
+    const int total_in = nseg * k;                    // <= kMergeCap (checked by the launcher)
     uint32_t base_cnt = 0;
     for (int c0 = 0; c0 < total_in; c0 += 4 * kTopkThreads) {
         const int i0 = c0 + tid * 4;
@@ -376,7 +392,7 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_merge_kernel(
         uint32_t p = base_cnt + block_excl_scan(cnt, wsum, &total);
         for (int e = 0; e < 4; ++e) {
             if (flag & (1u << e)) {
-                ck[p] = order_key(src[pos[e]]);
+                ck[p] = ckey[i0 + e];
                 ci[p] = pos[e];
                 ++p;
             }
@@ -399,7 +415,7 @@ int topk_num_segments(int Tq, int Tk, int k)
 {
     // few rows: split each row so that >= 256 workgroups stream the scores
     if (Tq <= 0 || Tq >= 128 || (int64_t)Tk < 4 * (int64_t)k) return 1;
-    int nseg = kCap / k;
+    int nseg = kMergeCap / k;
     if (nseg > 8) nseg = 8;
     while (nseg > 1 && (int64_t)Tq * nseg > 512) nseg >>= 1;
     return nseg < 2 ? 1 : nseg;
@@ -408,7 +424,7 @@ int topk_num_segments(int Tq, int Tk, int k)
 size_t topk_workspace_bytes(int Tq, int Tk, int k)
 {
     const int nseg = topk_num_segments(Tq, Tk, k);
-    return nseg > 1 ? (size_t)Tq * nseg * k * sizeof(int32_t) : 0;
+    return nseg > 1 ? (size_t)Tq * nseg * k * 2 * sizeof(int32_t) : 0;   // positions + keys
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t q_pos0,
