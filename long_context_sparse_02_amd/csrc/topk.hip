@@ -7,11 +7,13 @@
 //
 // One workgroup of 1024 threads owns a row; scores are compared through an
 // order-preserving 32-bit key (-0 and +0 map to the same key).
-//   1. A sample of the row (256 runs of 16 contiguous scores) gives, by an
-//      exact select in LDS, a key that is a lower bound for the k-th largest
-//      with high probability (the sample rank is padded by about 3 sigma).
+//   1. A sample of the row (256 runs of 16 contiguous scores) gives, by two
+//      radix digits of a select in LDS, a key that is a lower bound for the k-th
+//      largest with high probability (the sample rank is padded by about 3
+//      sigma, the bound is the low edge of that sample key's bin).
 //   2. One pass over the row copies every score at or above that bound, with
-//      its position, into LDS in position order (block-wide prefix sums).
+//      its position, into LDS in position order (block-wide prefix sums), with
+//      two steps of loads in flight; the first two are issued before step 1.
 //   3. If that candidate set holds at least k and fits in LDS, an exact radix
 //      select among the candidates finds the k-th largest key and how many of
 //      the keys equal to it to take; an ordered compaction of the candidates
@@ -112,11 +114,12 @@ __device__ __forceinline__ void key_range(Get get, int64_t m, uint32_t* red, uin
 // Exact select of the R-th largest (1 <= R <= m) of the keys get(0..m), all in
 // [kmin, kmax].  On return an element is above the threshold iff
 // ((key - kmin) & mask) > prefix and tied with it iff == prefix; `need` of the
-// tied elements complete the R.
+// tied elements complete the R.  Stopped after max_passes digits, kmin + prefix
+// is still a lower bound for the R-th largest key (the low edge of its bin).
 template <class Get>
 __device__ void radix_select(Get get, int64_t m, uint32_t R, uint32_t kmin, uint32_t kmax,
                              uint32_t* hist, uint32_t* wsum, uint32_t* sh, uint32_t& prefix,
-                             uint32_t& mask, uint32_t& need) {
+                             uint32_t& mask, uint32_t& need, int max_passes = 32) {
     const int tid = threadIdx.x;
     const uint32_t range = kmax - kmin;
     int hi = range ? 32 - __clz(range) : 0;
@@ -152,7 +155,7 @@ __device__ void radix_select(Get get, int64_t m, uint32_t R, uint32_t kmin, uint
         mask |= dmask << lo;
         __syncthreads();                              // hist is rebuilt by the next pass
         hi = lo;
-        if (in_bin == need) break;                    // the whole bin is taken
+        if (in_bin == need || --max_passes == 0) break;   // the whole bin is taken, or bound only
     }
 }
 
@@ -217,7 +220,7 @@ __device__ __forceinline__ int64_t row_length(int row, int Tk, int64_t q_pos0,
 // idx ([rows, nseg, k], ascending absolute positions, -1 padded); the union of
 // the segments' selections contains the row's selection, ties included (each
 // segment keeps its lowest-position ties), and topk_merge_kernel finishes it.
-__global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
+__global__ __launch_bounds__(kTopkThreads, 8) void topk_kernel(   // 8 waves per SIMD: two workgroups per CU
     const float* __restrict__ scores, int64_t ld, int Tk, int64_t q_pos0,
     const int32_t* __restrict__ row_len, int k, int nseg, int64_t seg_len,
     int32_t* __restrict__ idx)
@@ -258,15 +261,36 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
         m = n;
         __syncthreads();
     } else {
-        // 1. sample -> lower bound for the k-th largest key
+        // The streamed loads below are unconditional, from quad addresses clamped to
+        // the last whole quad of the row (a branch around a load makes the compiler
+        // wait for every load in flight where the paths join); the pass covers the
+        // n_main = n & ~3 positions of whole quads, and the <= 3 tail positions follow it.
+        const int64_t n_main = n & ~(int64_t)3;       // > kCap
+        const int64_t last4 = n_main - 4;
+        auto quad = [&](int64_t i) { return *reinterpret_cast<const float4*>(src + min(i, last4)); };
+
+        // 1. sample -> lower bound for the k-th largest key (runs start on quads and
+        //    end well inside the row)
         uint32_t* smp = reinterpret_cast<uint32_t*>(ci);
-        {
-            const int run = tid >> 2, part = tid & 3;
-            const int64_t base = ((int64_t)run * n / kSampleRuns) & ~(int64_t)3;
-            float v[4];
-            load4(src, base + 4 * part, n, v);
-            for (int e = 0; e < 4; ++e) smp[4 * tid + e] = order_key(v[e]);
-        }
+        const int run = tid >> 2, part = tid & 3;
+        const float4 sv = quad((((int64_t)run * n / kSampleRuns) & ~(int64_t)3) + 4 * part);
+
+        // the first two steps of the pass below stream in while the sample is ranked
+        constexpr int kPer = 8;                       // consecutive scores per thread per step
+        constexpr int64_t kStepLen = (int64_t)kPer * kTopkThreads;
+        auto fetch = [&](int64_t c0, float4* dst) {
+            const int64_t i0 = c0 + (int64_t)tid * kPer;
+#pragma unroll
+            for (int q = 0; q < kPer / 4; ++q) dst[q] = quad(i0 + 4 * q);
+        };
+        float4 b0[kPer / 4], b1[kPer / 4], b2[kPer / 4];
+        fetch(0, b0);
+        fetch(kStepLen, b1);
+
+        smp[4 * tid + 0] = order_key(sv.x);
+        smp[4 * tid + 1] = order_key(sv.y);
+        smp[4 * tid + 2] = order_key(sv.z);
+        smp[4 * tid + 3] = order_key(sv.w);
         __syncthreads();
         const double r = (double)k * kSample / (double)n;
         uint32_t r_lo = (uint32_t)ceil(r + 3.0 * sqrt(r) + 8.0);
@@ -274,29 +298,18 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
         auto get_s = [&](int64_t i) { return smp[i]; };
         uint32_t smin, smax, sp, sm, sn;
         key_range(get_s, kSample, wsum, smin, smax);
-        radix_select(get_s, kSample, r_lo, smin, smax, hist, wsum, sh, sp, sm, sn);
+        // two digits are enough: the bin's low edge sits at most one bin width (2^-22
+        // of the sample's key range) below the r_lo-th largest sample key.  (Keys are
+        // not linear in the value, so one 2^-11 bin can span a large value range.)
+        radix_select(get_s, kSample, r_lo, smin, smax, hist, wsum, sh, sp, sm, sn, 2);
         const uint32_t bound = smin + sp;             // <= the r_lo-th largest sample key
         __syncthreads();                              // the sample is dead from here on
 
-        // 2. one pass: every score with key >= bound, in position order, into LDS.
-        //    16 consecutive scores per thread per step; the next step's loads are
-        //    issued before this step's prefix sum so the row streams at full rate.
-        constexpr int kPer = 8;
-        constexpr int64_t kStepLen = (int64_t)kPer * kTopkThreads;
+        // 2. one pass: every score with key >= bound, in position order, into LDS,
+        //    kPer consecutive scores per thread per step and two steps in flight
+        //    (a three-slot ring, unrolled so that every slot is a fixed register set)
         uint32_t base_cnt = 0;
-        float4 cur[kPer / 4], nxt[kPer / 4];
-        auto fetch = [&](int64_t c0, float4* dst) {
-            const int64_t i0 = c0 + (int64_t)tid * kPer;
-#pragma unroll
-            for (int q = 0; q < kPer / 4; ++q) {
-                float v[4];
-                load4(src, i0 + 4 * q, n, v);
-                dst[q] = make_float4(v[0], v[1], v[2], v[3]);
-            }
-        };
-        fetch(0, cur);
-        for (int64_t c0 = 0; c0 < n; c0 += kStepLen) {
-            if (c0 + kStepLen < n) fetch(c0 + kStepLen, nxt);
+        auto step = [&](int64_t c0, const float4* cur) {
             const int64_t i0 = c0 + (int64_t)tid * kPer;
             uint32_t flag = 0, cnt = 0;
 #pragma unroll
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 4 * q + e;
-                    if (i0 + j < n && order_key(v[e]) >= bound) { flag |= 1u << j; ++cnt; }
+                    if (i0 + j < n_main && order_key(v[e]) >= bound) { flag |= 1u << j; ++cnt; }
                 }
             }
             uint32_t total;
@@ -325,8 +338,25 @@ __global__ __launch_bounds__(kTopkThreads, 2) void topk_kernel(
                 }
             }
             base_cnt += total;
-#pragma unroll
-            for (int q = 0; q < kPer / 4; ++q) cur[q] = nxt[q];
+        };
+        for (int64_t c0 = 0; c0 < n_main; c0 += 3 * kStepLen) {
+            fetch(c0 + 2 * kStepLen, b2);
+            step(c0, b0);
+            if (c0 + kStepLen >= n_main) break;
+            fetch(c0 + 3 * kStepLen, b0);
+            step(c0 + kStepLen, b1);
+            if (c0 + 2 * kStepLen >= n_main) break;
+            fetch(c0 + 4 * kStepLen, b1);
+            step(c0 + 2 * kStepLen, b2);
+        }
+        if (n_main < n) {                             // tail: one position per thread
+            const int64_t i = n_main + tid;
+            uint32_t key = 0, take = 0;
+            if (i < n) { key = order_key(src[i]); take = key >= bound; }
+            uint32_t total;
+            const uint32_t p = base_cnt + block_excl_scan(take, wsum, &total);
+            if (take && p < (uint32_t)kCap) { ck[p] = key; ci[p] = (int32_t)(begin + i); }
+            base_cnt += total;
         }
         __syncthreads();
         m = base_cnt;
@@ -437,7 +467,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t 
                            q_pos0, row_len, k, 1, (int64_t)Tk, idx);
         return hipGetLastError();
     }
-    const int64_t seg_len = ((int64_t)Tk + nseg - 1) / nseg;
+    const int64_t seg_len = (((int64_t)Tk + nseg - 1) / nseg + 3) & ~(int64_t)3;   // segments start on quads
     int32_t* cand = static_cast<int32_t*>(ws);
     hipLaunchKernelGGL(topk_kernel, dim3(Tq * nseg), dim3(kTopkThreads), 0, stream, scores, ld, Tk,
                        q_pos0, row_len, k, nseg, seg_len, cand);
