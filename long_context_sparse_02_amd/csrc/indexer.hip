@@ -388,35 +388,44 @@ void index_fp8_resident_kernel(
             }
             continue;
         }
-        // keys (A operands) of this wave: 16 NK keys, 32 bytes per lane per tile
+        // keys (A operands) of this wave, 16 NK keys, 32 bytes per lane per tile, and the
+        // scale of key 16 i + col: unconditional loads from rows clamped into the array
+        // (keys s >= Tk lie above the diagonal and are masked below), so no branch makes
+        // the compiler wait for them before it has to
         v8i a[NK];
+        float ksl[NK];
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
-            const int s = s_base + 16 * i + col;
-            a[i] = (s < Tk) ? load32B(k_idx + (int64_t)s * 128 + grp * 32) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            const int s = min(s_base + 16 * i + col, Tk - 1);
+            a[i] = load32B(k_idx + (int64_t)s * 128 + grp * 32);
+            ksl[i] = k_scale[s];
         }
-        // accumulators start at the linear term qmix . k (bf16 matrix core)
+        // all of the block's loads are in flight before any math: keep the compiler
+        // from sinking some of them below the first uses of the others
+        asm volatile("" ::: "memory");
+        // accumulators start at the linear term qmix . k (bf16 matrix core), one
+        // 32-wide slice m of the contraction at a time for every tile
         float acc[NK][4];
         {
             const uint16_t* qm = &qm_lds[col][grp * 32];
-            v8bf bh[4], bl[4];
+            v4f lin[NK];
+#pragma unroll
+            for (int i = 0; i < NK; ++i) lin[i] = zero;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                bh[m] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 8 * m));
-                bl[m] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 128 + 8 * m));
-            }
+                const v8bf bh = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 8 * m));
+                const v8bf bl = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 128 + 8 * m));
 #pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                v4f lin = zero;
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int i = 0; i < NK; ++i) {
                     const v8bf ka = fp8x8_to_bf16(a[i], m);
-                    lin = mfma_bf16_16x16x32(ka, bh[m], lin);
-                    lin = mfma_bf16_16x16x32(ka, bl[m], lin);
+                    lin[i] = mfma_bf16_16x16x32(ka, bh, lin[i]);
+                    lin[i] = mfma_bf16_16x16x32(ka, bl, lin[i]);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][e] = lin[e];
             }
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][e] = lin[i][e];
         }
         // head loop: the B operand (q^I of head j for the 16 tokens) is read from LDS one
         // head ahead, and the |x| epilogue of head j-1 follows the MFMAs of head j
@@ -454,7 +463,8 @@ void index_fp8_resident_kernel(
         for (int i = 0; i < NK; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
-        if (!t_ok) continue;
+        // every lane takes part in the scale shuffles (no early exit for tokens past Tq),
+        // and every path consumes the scale loads before the next block reuses them
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int s0 = s_base + 16 * i + 4 * grp;
@@ -462,9 +472,10 @@ void index_fp8_resident_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s = s0 + e;
-                const float ks = (s < Tk) ? k_scale[s] : 0.f;
+                const float ks = __shfl(ksl[i], 4 * grp + e, 64);   // lane 4 grp + e loaded key s
                 r[e] = ((int64_t)s <= pos) ? acc[i][e] * (qs * ks) : -INFINITY;
             }
+            if (!t_ok) continue;
             if (s0 + 3 < Tk) {
                 *reinterpret_cast<float4*>(out_row + s0) = make_float4(r[0], r[1], r[2], r[3]);
             } else {
