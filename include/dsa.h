@@ -151,8 +151,23 @@ dsa_status_t dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, ds
  * q [Tq, Hq, d], k / v [Tk, G, d] (dtype), q_idx / q_scale / w [Tq, ...] and
  * k_idx / k_scale [Tk, ...] as in dsa_index_scores, out [Tq, Hq, d].
  * idx_out (nullable) [Tq, topk] receives every row's Omega as dsa_topk writes it.
+ *
+ * Results equal those of dsa_index_scores -> dsa_topk -> dsa_sparse_gqa_attn
+ * bit for bit.  For an FP8 indexer with HI <= 64 and topk <= 8192, chunks
+ * whose rows see 48K to 512K keys take a candidate path instead of writing
+ * full score rows: the indexer first scores about Tk/64 sampled keys per row,
+ * a lower bound for each row's topk-th score is taken from the samples
+ * (padded by 5 sigma in rank), the indexer then keeps only the scores at or
+ * above the bound (at most 8192 per row), and Omega is selected exactly from
+ * those.  A row whose kept scores cannot give the exact answer (fewer than
+ * topk, or more than 8192 of them; about 1e-7 per row on generic data, but
+ * certain with massive ties) makes the library redo its whole chunk over full
+ * score rows, on the device and without a host synchronisation.
+ *
  * Workspace: dsa_prefill_workspace_size() bytes; it holds one chunk's fp32
- * score matrix (chunk_rows x Tk) and, when idx_out is NULL, its index sets.
+ * score matrix (chunk_rows x Tk), its index sets when idx_out is NULL, the
+ * samples (chunk_rows x up to 8192 fp32), the candidate lists (chunk_rows x
+ * 8192 x 8 bytes) and per-row bounds and counters.
  */
 size_t dsa_prefill_workspace_size(int Tq, int64_t q_pos0, int chunk_rows, int topk);
 dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_t dtype,

@@ -45,6 +45,13 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return x * q + (x < r ? x : r) + slot;
 }
 
+// Larger float -> larger unsigned key; -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;

@@ -51,6 +51,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
     do { if ((p) && !aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); } while (0)
 
 constexpr size_t kAlign = 256;
+constexpr int kCandMinKeys = 49152;          // fused prefill: candidate path from this many keys
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ld_for(int64_t Tk) { return (Tk + 3) / 4 * 4; }
 
@@ -240,20 +241,31 @@ struct PrefillPlan {
     int chunk;
     int64_t Tk;
     int64_t ld;
-    size_t scores_bytes, idx_bytes, index_bytes, total;
+    int S;                                     // samples per row of the largest chunk
+    size_t scores_bytes, idx_bytes, index_bytes;
+    size_t samples_bytes, tau_bytes, cnt_bytes, cand_bytes, flag_bytes, total;
 };
 
-// The workspace holds one chunk's scores, its index sets, and the indexer's scratch
-// (sized for FP8, the larger of the two indexer paths).
+// The workspace holds one chunk's scores, its index sets and the indexer's scratch (sized for
+// FP8, the larger of the two indexer paths), plus the candidate pipeline's buffers: samples,
+// per-row bounds and counters, candidate lists and the fallback flag.
 PrefillPlan plan_prefill(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
     PrefillPlan p;
     p.chunk = (chunk_rows <= 0 || chunk_rows > Tq) ? Tq : chunk_rows;
     p.Tk = q_pos0 + Tq;
     p.ld = ld_for(p.Tk);
+    p.S = p.Tk <= INT32_MAX ? dsa::fused_sample_count((int)p.Tk) : -1;
+    const int S = p.S > 0 ? p.S : 0;
     p.scores_bytes = round_up((size_t)p.chunk * p.ld * sizeof(float));
     p.idx_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
     p.index_bytes = indexer_ws_bytes(p.chunk, DSA_FP8_E4M3);
-    p.total = p.scores_bytes + p.idx_bytes + p.index_bytes;
+    p.samples_bytes = round_up((size_t)p.chunk * S * sizeof(float));
+    p.tau_bytes = round_up((size_t)p.chunk * sizeof(uint32_t));
+    p.cnt_bytes = round_up((size_t)p.chunk * sizeof(int32_t));
+    p.cand_bytes = round_up((size_t)p.chunk * dsa::kCandCap * sizeof(uint2));
+    p.flag_bytes = kAlign;
+    p.total = p.scores_bytes + p.idx_bytes + p.index_bytes + p.samples_bytes + p.tau_bytes +
+              p.cnt_bytes + p.cand_bytes + p.flag_bytes;
     return p;
 }
 
@@ -286,23 +298,62 @@ DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v,
     REQUIRE(ws && aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
             "prefill needs %zu workspace bytes (got %zu%s)", plan.total, ws_bytes,
             ws ? "" : ", ws is NULL");
-    float* scores = static_cast<float*>(ws);
-    int32_t* idx_ws = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan.scores_bytes);
-    void* index_ws = static_cast<char*>(ws) + plan.scores_bytes + plan.idx_bytes;
+    char* wp = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(wp);                    wp += plan.scores_bytes;
+    int32_t* idx_ws = reinterpret_cast<int32_t*>(wp);                wp += plan.idx_bytes;
+    void* index_ws = wp;                                             wp += plan.index_bytes;
+    float* samples = reinterpret_cast<float*>(wp);                   wp += plan.samples_bytes;
+    float* tau = reinterpret_cast<float*>(wp);                       wp += plan.tau_bytes;
+    int32_t* cnt = reinterpret_cast<int32_t*>(wp);                   wp += plan.cnt_bytes;
+    uint2* cand = reinterpret_cast<uint2*>(wp);                      wp += plan.cand_bytes;
+    int* fallback = reinterpret_cast<int*>(wp);
     const size_t qrow = (size_t)Hq * d * (dtype == DSA_BF16 ? 2 : 4);
     const size_t qirow = (size_t)HI * dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
+    // The candidate pipeline needs the resident FP8 indexer and a bounded candidate list;
+    // other shapes run the indexer and top-k over full score rows.
+    const bool cand_path = idx_dtype == DSA_FP8_E4M3 && HI <= 64 && topk <= dsa::kCandCap;
     for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
         const int rows = (Tq - r0 < plan.chunk) ? Tq - r0 : plan.chunk;
         const int64_t pos0 = q_pos0 + r0;
         const int tk = (int)(pos0 + rows);                     // keys this chunk can see
-        st = run_indexer(static_cast<const char*>(q_idx) + r0 * qirow,
-                         q_scale ? q_scale + r0 : nullptr, w + (int64_t)r0 * HI, k_idx, k_scale,
-                         idx_dtype, rows, tk, HI, dI, pos0, scores, plan.ld, index_ws, stream);
-        if (st != DSA_OK) return st;
+        const void* qi_c = static_cast<const char*>(q_idx) + r0 * qirow;
+        const float* qs_c = q_scale ? q_scale + r0 : nullptr;
+        const float* w_c = w + (int64_t)r0 * HI;
         int32_t* idx_c = idx_out ? idx_out + (int64_t)r0 * topk : idx_ws;
-        hipError_t e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c,
-                                        nullptr, stream);
-        if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        // short prefixes: streaming the full score rows costs less than the sample pass and
+        // the per-row select (measured break-even near 40K keys)
+        const int S = cand_path && tk >= kCandMinKeys ? dsa::fused_sample_count(tk) : -1;
+        hipError_t e = hipSuccess;
+        if (S >= 0) {
+            // sampled bound -> candidates at or above it -> exact select from the candidates;
+            // a row whose candidates cannot give the exact answer raises the fallback flag,
+            // and the two gated launches then redo the chunk over full score rows
+            const auto* qi8 = static_cast<const uint8_t*>(qi_c);
+            const auto* ki8 = static_cast<const uint8_t*>(k_idx);
+            e = dsa::launch_index_fp8_sample(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI, pos0,
+                                             samples, S, index_ws, stream);
+            if (e == hipSuccess)
+                e = dsa::launch_topk_bound(samples, S, rows, pos0, topk, tau, cnt, fallback, stream);
+            if (e == hipSuccess)
+                e = dsa::launch_index_fp8_candidates(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI,
+                                                     pos0, tau, cnt, cand, dsa::kCandCap,
+                                                     index_ws, stream);
+            if (e == hipSuccess)
+                e = dsa::launch_topk_select(cand, cnt, rows, pos0, topk, idx_c, fallback, stream);
+            if (e == hipSuccess)
+                e = dsa::launch_index_fp8(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI, pos0, scores,
+                                          plan.ld, index_ws, stream, fallback, true);
+            if (e == hipSuccess)
+                e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c, nullptr,
+                                     stream, fallback);
+            if (e != hipSuccess) return hip_fail(e, "prefill selection launch");
+        } else {
+            st = run_indexer(qi_c, qs_c, w_c, k_idx, k_scale, idx_dtype, rows, tk, HI, dI, pos0,
+                             scores, plan.ld, index_ws, stream);
+            if (st != DSA_OK) return st;
+            e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c, nullptr, stream);
+            if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        }
         st = run_attn(static_cast<const char*>(q) + r0 * qrow, k, v, dtype, tk, nullptr, 0, 0,
                       nullptr, nullptr, idx_c, rows, topk, Hq, G, d, sm_scale,
                       static_cast<char*>(out) + r0 * qrow, nullptr, 0, stream);

@@ -284,6 +284,15 @@ void index_fp8_kernel(
 // waves per SIMD drifting out of phase, one wave's matrix-core work overlaps
 // another's vector ALU work and memory waits (a wave's own VALU and MFMA
 // instructions do not overlap on gfx950).
+//
+// Three output modes share the arithmetic, so a score is the same bits in each:
+//   kModeScores      every causal score of the chunk into scores[row, s] (-inf above the
+//                    diagonal), optionally gated by a device flag (*run_if != 0);
+//   kModeSample      the scores of S sampled key positions per token tile (stratified over
+//                    [0, t0] with a hashed offset in each stratum) into samples[row, j];
+//   kModeCandidates  only the causal scores >= tau[row] (a finite bound), appended as
+//                    (key, position) pairs to the row's list (atomic counter per row; at most
+//                    cap pairs are stored, the counter keeps counting).
 #ifndef DSA_IDX_RES_NK
 #define DSA_IDX_RES_NK 4
 #endif
@@ -293,14 +302,34 @@ void index_fp8_kernel(
 constexpr int kResHeads = 64;
 constexpr int kResWaves = DSA_IDX_RES_WAVES;
 constexpr int kResNK = DSA_IDX_RES_NK;
+constexpr int kModeScores = 0, kModeSample = 1, kModeCandidates = 2;
 
-template <int NK>
+// Sampled key position j of a token tile whose first token sees keys 0 .. n0-1: one key in
+// each of S equal strata of [0, n0), at a hashed offset inside its stratum.
+__device__ __forceinline__ int sample_pos(int j, int S, int n0, int tile) {
+    const int lo = (int)((int64_t)j * n0 / S);
+    const int hi = (int)((int64_t)(j + 1) * n0 / S);
+    uint32_t h = (uint32_t)j * 0x9E3779B1u ^ (uint32_t)tile * 0x85EBCA77u;
+    h ^= h >> 15; h *= 0x2C1B3C6Du; h ^= h >> 12;
+    const int width = hi - lo;
+    return width > 1 ? lo + (int)(h % (uint32_t)width) : min(lo, n0 - 1);
+}
+
+struct ResOut {
+    float* scores; int64_t ld;                  // kModeScores
+    const int* run_if;                          // kModeScores: skip unless *run_if != 0 (nullable)
+    float* samples; int S;                      // kModeSample: [rows, S]
+    const float* tau; int32_t* cnt;             // kModeCandidates: per-row bound and counter
+    uint2* cand; int cap;                       //   [rows, cap] of (order key, position)
+};
+
+template <int NK, int MODE>
 __global__ __launch_bounds__(kResWaves * 64) __attribute__((amdgpu_waves_per_eu(kResWaves / 4, kResWaves / 4)))
 void index_fp8_resident_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const uint16_t* __restrict__ qmix, int Tq, int Tk,
-    int HI, int64_t q_pos0, float* __restrict__ scores, int64_t ld, int n_kb, int n_kg, int kg)
+    int HI, int64_t q_pos0, ResOut o, int n_kb, int n_kg, int kg)
 {
     constexpr int kKeysPerWave = 16 * NK;
     constexpr int kKeysPerBlock = kResWaves * kKeysPerWave;
@@ -308,6 +337,7 @@ void index_fp8_resident_kernel(
     __shared__ float w_lds[kResHeads][16];
     __shared__ __attribute__((aligned(16))) uint16_t qm_lds[16][264];   // padded rows: no bank conflicts
 
+    if (MODE == kModeScores && o.run_if && *o.run_if == 0) return;
     // key-group-major order: the workgroups resident on one XCD share a key group (hot in
     // that XCD's L2) and differ in their token tiles
     const int work = xcd_remap(blockIdx.x, gridDim.x);
@@ -324,11 +354,13 @@ void index_fp8_resident_kernel(
     const int64_t pos = q_pos0 + t;
     const int64_t pos_hi = q_pos0 + min(t0 + 15, Tq - 1);
     const int kb_begin = g * kg, kb_end = min(n_kb, kb_begin + kg);
-    float* __restrict__ out_row = scores + (int64_t)tc * ld;
+    // keys the tile's first token sees (the sample strata cover them)
+    const int n0 = (int)min<int64_t>(q_pos0 + t0 + 1, Tk);
+    float* __restrict__ out_row = MODE == kModeScores ? o.scores + (int64_t)tc * o.ld : nullptr;
 
-    // whole group above the diagonal: only -inf to write
-    if ((int64_t)kb_begin * kKeysPerBlock > pos_hi) {
-        if (t_ok) {
+    // whole group above the diagonal: only -inf to write (or nothing)
+    if (MODE != kModeSample && (int64_t)kb_begin * kKeysPerBlock > pos_hi) {
+        if (MODE == kModeScores && t_ok) {
             for (int kb = kb_begin; kb < kb_end; ++kb) {
                 const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;
 #pragma unroll
@@ -368,13 +400,16 @@ void index_fp8_resident_kernel(
     __syncthreads();
 
     const float qs = 0.5f * q_scale[tc];              // (linear + |x| terms) / 2
+    const float tau_t = MODE == kModeCandidates ? o.tau[tc] : 0.f;
+    const int pos32 = (int)pos;                       // pos < Tk <= INT32_MAX
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const int n_keys = MODE == kModeSample ? o.S : Tk;   // logical keys of this launch
 
     for (int kb = kb_begin; kb < kb_end; ++kb) {
-        const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;
-        if (s_base >= Tk) break;
-        if ((int64_t)s_base > pos_hi) {               // wave tile above the diagonal
-            if (t_ok) {
+        const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;   // logical key index
+        if (s_base >= n_keys) break;
+        if (MODE != kModeSample && (int64_t)s_base > pos_hi) {   // wave tile above the diagonal
+            if (MODE == kModeScores && t_ok) {
 #pragma unroll
                 for (int i = 0; i < NK; ++i) {
                     const int s0 = s_base + 16 * i + 4 * grp;
@@ -396,7 +431,8 @@ void index_fp8_resident_kernel(
         float ksl[NK];
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
-            const int s = min(s_base + 16 * i + col, Tk - 1);
+            const int s = MODE == kModeSample ? sample_pos(min(s_base + 16 * i + col, n_keys - 1), o.S, n0, tt)
+                                              : min(s_base + 16 * i + col, Tk - 1);
             a[i] = load32B(k_idx + (int64_t)s * 128 + grp * 32);
             ksl[i] = k_scale[s];
         }
@@ -467,20 +503,61 @@ void index_fp8_resident_kernel(
         // and every path consumes the scale loads before the next block reuses them
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
-            const int s0 = s_base + 16 * i + 4 * grp;
-            float r[4];
+            // causal limit in 32 bits: key s0 + e is visible iff e <= pos - s0
+            const int lim = pos32 - (s_base + 16 * i + 4 * grp);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int s = s0 + e;
-                const float ks = __shfl(ksl[i], 4 * grp + e, 64);   // lane 4 grp + e loaded key s
-                r[e] = ((int64_t)s <= pos) ? acc[i][e] * (qs * ks) : -INFINITY;
+                const float ks = __shfl(ksl[i], 4 * grp + e, 64);   // lane 4 grp + e loaded key s0 + e
+                const float r = acc[i][e] * (qs * ks);
+                acc[i][e] = (MODE == kModeSample || e <= lim) ? r : -INFINITY;
             }
-            if (!t_ok) continue;
-            if (s0 + 3 < Tk) {
-                *reinterpret_cast<float4*>(out_row + s0) = make_float4(r[0], r[1], r[2], r[3]);
+        }
+        if (MODE == kModeCandidates) {
+            // lane (col, grp) holds keys s_base + 16 i + 4 grp + e of token col; keep the ones
+            // at or above the row's bound (entries above the diagonal hold -inf, below any
+            // bound; the bound is finite) and reserve room with one atomic per token
+            uint32_t keep = 0;
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) keep |= (acc[i][e] >= tau_t ? 1u : 0u) << (4 * i + e);
+            if (!t_ok) keep = 0;
+            // counts over the token's four lanes (grp 0..3) with lane-xor exchanges only
+            const uint32_t c = __popc(keep);
+            const uint32_t x1 = __shfl_xor(c, 16, 64);        // grp ^ 1
+            const uint32_t pair = c + x1;
+            const uint32_t x2 = __shfl_xor(pair, 32, 64);     // the other pair
+            const uint32_t total = pair + x2;
+            uint32_t b0 = 0;
+            if (grp == 0 && total) b0 = (uint32_t)atomicAdd(o.cnt + t, (int)total);
+            const uint32_t b1 = b0 + __shfl_xor(b0, 16, 64);
+            uint32_t off = b1 + __shfl_xor(b1, 32, 64);       // the token's base (from grp 0)
+            off += ((grp & 2) ? x2 : 0u) + ((grp & 1) ? x1 : 0u);
+            // rows of this token tile start at the uniform t0 * cap; 32-bit offsets within
+            uint2* __restrict__ dst = o.cand + (int64_t)t0 * o.cap;
+            const uint32_t row_off = (uint32_t)col * (uint32_t)o.cap;
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (keep & (1u << (4 * i + e))) {
+                        if (off < (uint32_t)o.cap)
+                            dst[row_off + off] = make_uint2(order_key(acc[i][e]),
+                                                            (uint32_t)(s_base + 16 * i + 4 * grp + e));
+                        ++off;
+                    }
+            continue;
+        }
+        if (!t_ok) continue;
+        float* __restrict__ dst = MODE == kModeSample ? o.samples + (int64_t)tc * o.S : out_row;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int s0 = s_base + 16 * i + 4 * grp;
+            if (MODE == kModeSample || s0 + 3 < Tk) {
+                *reinterpret_cast<float4*>(dst + s0) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
             } else {
                 for (int e = 0; e < 4; ++e)
-                    if (s0 + e < Tk) out_row[s0 + e] = r[e];
+                    if (s0 + e < Tk) dst[s0 + e] = acc[i][e];
             }
         }
     }
@@ -679,9 +756,45 @@ void index_fp8_paged_kernel(
 
 size_t index_fp8_workspace_bytes(int Tq) { return (size_t)Tq * 256 * sizeof(uint16_t); }
 
+namespace {
+
+hipError_t launch_qmix(const uint8_t* q_idx, const float* w, int Tq, int HI, void* ws,
+                       hipStream_t stream)
+{
+    hipLaunchKernelGGL(qmix_kernel, dim3((Tq + 3) / 4), dim3(256), 0, stream, q_idx, w, Tq, HI,
+                       static_cast<uint16_t*>(ws));
+    return hipGetLastError();
+}
+
+// The resident kernel over n_keys logical keys in blocks of 1024; each workgroup takes a
+// group of up to kg_max of them so the one-time q^I staging is amortised, while keeping
+// >= 8 workgroups per CU in total.
+template <int MODE>
+hipError_t launch_resident(const uint8_t* q_idx, const float* q_scale, const float* w,
+                           const uint8_t* k_idx, const float* k_scale, int Tq, int Tk, int HI,
+                           int64_t q_pos0, const ResOut& o, int n_keys, int kg_max, void* ws,
+                           hipStream_t stream)
+{
+    const int n_tt = (Tq + 15) / 16;
+    const int n_kb1 = (n_keys + kResWaves * 16 * kResNK - 1) / (kResWaves * 16 * kResNK);
+    if (n_tt == 0 || n_kb1 == 0) return hipSuccess;
+    int kg = n_kb1 / 8;
+    kg = kg < 1 ? 1 : (kg > kg_max ? kg_max : kg);
+    const int n_kg = (n_kb1 + kg - 1) / kg;
+    const int64_t nw = (int64_t)n_tt * n_kg;
+    if (nw > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((index_fp8_resident_kernel<kResNK, MODE>), dim3((unsigned)nw), dim3(kResWaves * 64),
+                       0, stream, q_idx, q_scale, w, k_idx, k_scale,
+                       static_cast<const uint16_t*>(ws), Tq, Tk, HI, q_pos0, o, n_kb1, n_kg, kg);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_index_fp8(const uint8_t* q_idx, const float* q_scale, const float* w,
                             const uint8_t* k_idx, const float* k_scale, int Tq, int Tk, int HI,
-                            int64_t q_pos0, float* scores, int64_t ld, void* ws, hipStream_t stream)
+                            int64_t q_pos0, float* scores, int64_t ld, void* ws, hipStream_t stream,
+                            const int* run_if, bool qmix_ready)
 {
     constexpr int NK = 8;
     const int n_tt = (Tq + 15) / 16;
@@ -689,27 +802,48 @@ hipError_t launch_index_fp8(const uint8_t* q_idx, const float* q_scale, const fl
     const int64_t n = (int64_t)n_tt * n_kb;
     if (n == 0) return hipSuccess;
     if (n > INT32_MAX) return hipErrorInvalidValue;
-    uint16_t* qmix = static_cast<uint16_t*>(ws);
-    hipLaunchKernelGGL(qmix_kernel, dim3((Tq + 3) / 4), dim3(256), 0, stream, q_idx, w, Tq, HI, qmix);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (HI <= kResHeads) {
-        // key blocks of 1024; each workgroup takes a group of up to 16 of them so the
-        // one-time q^I staging is amortised, while keeping >= 8 workgroups per CU in total
-        const int n_kb1 = (Tk + kResWaves * 16 * kResNK - 1) / (kResWaves * 16 * kResNK);
-        int kg = n_kb1 / 8;
-        kg = kg < 1 ? 1 : (kg > 16 ? 16 : kg);
-        const int n_kg = (n_kb1 + kg - 1) / kg;
-        const int64_t nw = (int64_t)n_tt * n_kg;
-        if (nw > INT32_MAX) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(index_fp8_resident_kernel<kResNK>, dim3((unsigned)nw), dim3(kResWaves * 64), 0, stream,
-                           q_idx, q_scale, w, k_idx, k_scale, qmix, Tq, Tk, HI, q_pos0, scores, ld,
-                           n_kb1, n_kg, kg);
-        return hipGetLastError();
+    if (!qmix_ready) {
+        const hipError_t e = launch_qmix(q_idx, w, Tq, HI, ws, stream);
+        if (e != hipSuccess) return e;
     }
+    if (HI <= kResHeads) {
+        ResOut o = {};
+        o.scores = scores; o.ld = ld; o.run_if = run_if;
+        return launch_resident<kModeScores>(q_idx, q_scale, w, k_idx, k_scale, Tq, Tk, HI, q_pos0,
+                                            o, Tk, 16, ws, stream);
+    }
+    if (run_if) return hipErrorInvalidValue;            // gating exists on the resident path only
     hipLaunchKernelGGL(index_fp8_kernel<NK>, dim3((unsigned)n), dim3(256), 0, stream, q_idx,
-                       q_scale, w, k_idx, k_scale, qmix, Tq, Tk, HI, q_pos0, scores, ld, n_kb);
+                       q_scale, w, k_idx, k_scale, static_cast<const uint16_t*>(ws), Tq, Tk, HI,
+                       q_pos0, scores, ld, n_kb);
     return hipGetLastError();
+}
+
+hipError_t launch_index_fp8_sample(const uint8_t* q_idx, const float* q_scale, const float* w,
+                                   const uint8_t* k_idx, const float* k_scale, int Tq, int Tk,
+                                   int HI, int64_t q_pos0, float* samples, int S, void* ws,
+                                   hipStream_t stream)
+{
+    if (HI > kResHeads || S < 0 || S % (kResWaves * 16 * kResNK) != 0) return hipErrorInvalidValue;
+    const hipError_t e = launch_qmix(q_idx, w, Tq, HI, ws, stream);
+    if (e != hipSuccess || S == 0) return e;            // S == 0: the pre-pass only
+    ResOut o = {};
+    o.samples = samples; o.S = S;
+    return launch_resident<kModeSample>(q_idx, q_scale, w, k_idx, k_scale, Tq, Tk, HI, q_pos0, o,
+                                        S, 2, ws, stream);
+}
+
+hipError_t launch_index_fp8_candidates(const uint8_t* q_idx, const float* q_scale,
+                                       const float* w, const uint8_t* k_idx,
+                                       const float* k_scale, int Tq, int Tk, int HI,
+                                       int64_t q_pos0, const float* tau, int32_t* cnt,
+                                       uint2* cand, int cap, void* ws, hipStream_t stream)
+{
+    if (HI > kResHeads) return hipErrorInvalidValue;
+    ResOut o = {};
+    o.tau = tau; o.cnt = cnt; o.cand = cand; o.cap = cap;
+    return launch_resident<kModeCandidates>(q_idx, q_scale, w, k_idx, k_scale, Tq, Tk, HI, q_pos0,
+                                            o, Tk, 16, ws, stream);
 }
 
 hipError_t launch_index_f32(const float* q_idx, const float* w, const float* k_idx, int Tq,

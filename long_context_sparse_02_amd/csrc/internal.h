@@ -9,11 +9,29 @@ namespace dsa {
 
 // Lightning indexer, contiguous keys (prefill).  Row i is position q_pos0 + i.
 // The FP8 kernel needs index_fp8_workspace_bytes(Tq) bytes of device scratch.
+// run_if (nullable): the launch does nothing unless *run_if != 0 when it runs (resident
+// path only).  qmix_ready: the workspace already holds this chunk's qmix pre-pass.
 size_t index_fp8_workspace_bytes(int Tq);
 hipError_t launch_index_fp8(const uint8_t* q_idx, const float* q_scale, const float* w,
                             const uint8_t* k_idx, const float* k_scale, int Tq, int Tk, int HI,
                             int64_t q_pos0, float* scores, int64_t ld, void* ws,
-                            hipStream_t stream);
+                            hipStream_t stream, const int* run_if = nullptr,
+                            bool qmix_ready = false);
+// Candidate pipeline of the fused prefill (FP8, HI <= 64).  Sample: the qmix pre-pass, then
+// the scores of S sampled keys per row (S a multiple of 1024, or 0 for the pre-pass alone)
+// into samples [Tq, S].
+// Candidates (qmix ready): every causal score >= tau[row] appended to
+// row's list cand [Tq, cap] as (order key, position); cnt[row] counts all of them (it must
+// start at 0) and may exceed cap, in which case only cap pairs were stored.
+hipError_t launch_index_fp8_sample(const uint8_t* q_idx, const float* q_scale, const float* w,
+                                   const uint8_t* k_idx, const float* k_scale, int Tq, int Tk,
+                                   int HI, int64_t q_pos0, float* samples, int S, void* ws,
+                                   hipStream_t stream);
+hipError_t launch_index_fp8_candidates(const uint8_t* q_idx, const float* q_scale,
+                                       const float* w, const uint8_t* k_idx,
+                                       const float* k_scale, int Tq, int Tk, int HI,
+                                       int64_t q_pos0, const float* tau, int32_t* cnt,
+                                       uint2* cand, int cap, void* ws, hipStream_t stream);
 hipError_t launch_index_f32(const float* q_idx, const float* w, const float* k_idx, int Tq,
                             int Tk, int HI, int dI, int64_t q_pos0, float* scores, int64_t ld,
                             hipStream_t stream);
@@ -30,7 +48,20 @@ hipError_t launch_index_fp8_paged(const uint8_t* q_idx, const float* q_scale, co
 // topk_workspace_bytes() bytes, few long rows are split into segments and merged.
 size_t topk_workspace_bytes(int Tq, int Tk, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t q_pos0,
-                       const int32_t* row_len, int k, int32_t* idx, void* ws, hipStream_t stream);
+                       const int32_t* row_len, int k, int32_t* idx, void* ws, hipStream_t stream,
+                       const int* run_if = nullptr);
+// Fused-prefill selection.  Bound: for each row of n = q_pos0 + row + 1 > cap candidates, a
+// lower bound for the k-th largest score from the row's S samples, padded so that it fails
+// (fewer than k scores at or above it, or more than cap) with probability ~1e-7; rows with
+// n <= cap get -FLT_MAX (every causal score is a candidate).  It also zeroes cnt and
+// *fallback.  Select: Omega of each row from its candidate list (ascending, ties to the lower
+// position, -1 padded); a row whose list cannot give an exact answer sets *fallback = 1.
+constexpr int kCandCap = 8192;
+int fused_sample_count(int Tk);
+hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0, int k,
+                             float* tau, int32_t* cnt, int* fallback, hipStream_t stream);
+hipError_t launch_topk_select(const uint2* cand, const int32_t* cnt, int Tq, int64_t q_pos0,
+                              int k, int32_t* idx, int* fallback, hipStream_t stream);
 
 struct AttnArgs {
     const void* q; const void* k; const void* v; void* out;

@@ -25,6 +25,8 @@
 // Radix selects place their first digit at the top set bit of (max - min) of
 // the keys involved, so the bins spread over the values actually present.
 // Rows with t + 1 <= k need no selection and read nothing (they take 0..t).
+#include <cfloat>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -35,13 +37,6 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
-
-// Larger float -> larger unsigned key; -0 and +0 map to the same key.
-__device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 #pragma unroll
@@ -223,8 +218,9 @@ __device__ __forceinline__ int64_t row_length(int row, int Tk, int64_t q_pos0,
 __global__ __launch_bounds__(kTopkThreads, 8) void topk_kernel(   // 8 waves per SIMD: two workgroups per CU
     const float* __restrict__ scores, int64_t ld, int Tk, int64_t q_pos0,
     const int32_t* __restrict__ row_len, int k, int nseg, int64_t seg_len,
-    int32_t* __restrict__ idx)
+    int32_t* __restrict__ idx, const int* __restrict__ run_if)
 {
+    if (run_if && *run_if == 0) return;              // gated launch with nothing to do
     __shared__ uint32_t ck[kCap];             // candidate keys, in position order
     __shared__ int32_t ci[kCap];              // their positions (the sample reuses this array)
     __shared__ uint32_t hist[kBins];
@@ -439,6 +435,167 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
     compact(get_c, pos_c, m, kmin, prefix, mask, need, wsum, out);
 }
 
+// ---- fused prefill: bound from a sample, exact select from a candidate list ----
+
+// In-place ascending bitonic sort of a[0..len) (len <= cap of the array, padded to the next
+// power of two with 0xffffffff, which must fit in the array).
+__device__ void bitonic_sort_asc(uint32_t* a, int len) {
+    const int tid = threadIdx.x;
+    int P = 1;
+    while (P < len) P <<= 1;
+    for (int i = len + tid; i < P; i += kTopkThreads) a[i] = 0xffffffffu;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < (P >> 1); i += kTopkThreads) {
+                const int lo = 2 * stride * (i / stride) + (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool asc = (lo & size) == 0;
+                const uint32_t x = a[lo], y = a[hi];
+                if ((x > y) == asc) { a[lo] = y; a[hi] = x; }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Lower bound of row `row`'s k-th largest score from its S samples (see launch_topk_bound).
+__global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
+    const float* __restrict__ samples, int S, int64_t q_pos0, int k, float* __restrict__ tau,
+    int32_t* __restrict__ cnt, int* __restrict__ fallback)
+{
+    __shared__ uint32_t smp[kCandCap];
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t wsum[2 * kTopkWaves];
+    __shared__ uint32_t sh[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    if (tid == 0) {
+        cnt[row] = 0;
+        if (row == 0) *fallback = 0;
+    }
+    const int64_t n = q_pos0 + row + 1;
+    if (n <= kCandCap || S <= 0) {                   // every causal score is a candidate
+        if (tid == 0) tau[row] = -FLT_MAX;
+        return;
+    }
+    const float* __restrict__ src = samples + (int64_t)row * S;
+    for (int i = tid; i < S; i += kTopkThreads) smp[i] = order_key(src[i]);
+    __syncthreads();
+    // rank of the bound among the samples: the expected rank of the k-th largest score,
+    // r = k S / n, padded by 5 sigma (+8): fewer than k scores at or above the bound needs
+    // >= r_lo samples above the k-th largest score, a ~1e-7 tail event
+    const double r = (double)k * S / (double)n;
+    uint32_t r_lo = (uint32_t)ceil(r + 5.0 * sqrt(r) + 8.0);
+    if (r_lo > (uint32_t)S) r_lo = S;
+    auto get_s = [&](int64_t i) { return smp[i]; };
+    uint32_t smin, smax, sp, sm, sn;
+    key_range(get_s, S, wsum, smin, smax);
+    radix_select(get_s, S, r_lo, smin, smax, hist, wsum, sh, sp, sm, sn, 2);
+    // back to a float: a score is >= it exactly when its key is >= the bound key (the key
+    // lies between two sample keys, so it is a finite value's key)
+    if (tid == 0) {
+        const uint32_t key = smin + sp;
+        const uint32_t u = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+        tau[row] = __uint_as_float(u);
+    }
+}
+
+// Omega of one row from its candidate list: exact select of the k-th largest key, the
+// candidates above it plus the lowest-position ties, sorted ascending.
+__global__ __launch_bounds__(kTopkThreads, 8) void topk_select_kernel(
+    const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, int64_t q_pos0, int k,
+    int32_t* __restrict__ idx, int* __restrict__ fallback)
+{
+    __shared__ uint32_t ck[kCandCap];                 // keys, later the selected positions
+    __shared__ uint32_t ci[kCandCap];                 // positions, later the tied positions
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t wsum[2 * kTopkWaves];
+    __shared__ uint32_t sh[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int64_t n = q_pos0 + row + 1;
+    int32_t* __restrict__ out = idx + (int64_t)row * k;
+    if (n <= k) {
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+        return;
+    }
+    const int m = cnt[row];
+    if (m < k || m > kCandCap) {                      // the bound missed: exact path for the chunk
+        if (tid == 0) *fallback = 1;
+        return;
+    }
+    const uint2* __restrict__ src = cand + (int64_t)row * kCandCap;
+    for (int i = tid; i < m; i += kTopkThreads) {
+        const uint2 c = src[i];
+        ck[i] = c.x;
+        ci[i] = c.y;
+    }
+    __syncthreads();
+    auto get_c = [&](int64_t i) { return ck[i]; };
+    uint32_t kmin, kmax, prefix, mask, need;
+    key_range(get_c, m, wsum, kmin, kmax);
+    radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
+    // split in place: positions above the threshold to ck[0..), tied positions to ci[0..)
+    // (an element's new slot never exceeds its old index, and a step's elements are all
+    // read before any is written)
+    uint32_t n_gt = 0, n_eq = 0;
+    for (int c0 = 0; c0 < m; c0 += 4 * kTopkThreads) {
+        const int i0 = c0 + tid * 4;
+        uint32_t key[4], pos[4], gt = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            key[e] = 0; pos[e] = 0;
+            if (i0 + e < m) {
+                key[e] = ck[i0 + e];
+                pos[e] = ci[i0 + e];
+                const uint32_t rel = (key[e] - kmin) & mask;
+                if (rel > prefix) gt |= 1u << e;
+                else if (rel == prefix) eq |= 1u << e;
+            }
+        }
+        uint32_t total;
+        const uint32_t excl = block_excl_scan(__popc(gt) | (__popc(eq) << 16), wsum, &total);
+        uint32_t pg = n_gt + (excl & 0xffffu), pe = n_eq + (excl >> 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (gt & (1u << e)) ck[pg++] = pos[e];
+            else if (eq & (1u << e)) ci[pe++] = pos[e];
+        }
+        n_gt += total & 0xffffu;
+        n_eq += total >> 16;
+        __syncthreads();
+    }
+    // the need lowest tied positions complete the set
+    if (n_eq > need) bitonic_sort_asc(ci, (int)n_eq);
+    for (int j = tid; j < (int)need; j += kTopkThreads) ck[n_gt + j] = ci[j];
+    __syncthreads();
+    if (n > 32 * (int64_t)kCandCap) {                // no room for a bitmap of the row
+        bitonic_sort_asc(ck, k);
+        for (int i = tid; i < k; i += kTopkThreads) out[i] = (int32_t)ck[i];
+        return;
+    }
+    // ascending order through a bitmap of the row's positions (in ci, now free): each
+    // thread owns a run of words, and a prefix sum of their bit counts places its positions
+    const int nw = (int)((n + 31) >> 5);
+    for (int i = tid; i < nw; i += kTopkThreads) ci[i] = 0u;
+    __syncthreads();
+    for (int j = tid; j < k; j += kTopkThreads) atomicOr(&ci[ck[j] >> 5], 1u << (ck[j] & 31u));
+    __syncthreads();
+    const int wpt = (nw + kTopkThreads - 1) / kTopkThreads;
+    const int w0 = tid * wpt, w1 = min(w0 + wpt, nw);
+    uint32_t c = 0;
+    for (int i = w0; i < w1; ++i) c += __popc(ci[i]);
+    uint32_t total;
+    uint32_t p = block_excl_scan(c, wsum, &total);
+    for (int i = w0; i < w1; ++i) {
+        uint32_t word = ci[i];
+        while (word) {
+            const int b = __ffs(word) - 1;
+            out[p++] = i * 32 + b;
+            word &= word - 1u;
+        }
+    }
+}
+
 }  // namespace
 
 int topk_num_segments(int Tq, int Tk, int k)
@@ -458,23 +615,55 @@ size_t topk_workspace_bytes(int Tq, int Tk, int k)
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t q_pos0,
-                       const int32_t* row_len, int k, int32_t* idx, void* ws, hipStream_t stream)
+                       const int32_t* row_len, int k, int32_t* idx, void* ws, hipStream_t stream,
+                       const int* run_if)
 {
     if (Tq == 0) return hipSuccess;
     const int nseg = ws ? topk_num_segments(Tq, Tk, k) : 1;
+    if (nseg > 1 && run_if) return hipErrorInvalidValue;   // gating exists for one pass only
     if (nseg == 1) {
         hipLaunchKernelGGL(topk_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, scores, ld, Tk,
-                           q_pos0, row_len, k, 1, (int64_t)Tk, idx);
+                           q_pos0, row_len, k, 1, (int64_t)Tk, idx, run_if);
         return hipGetLastError();
     }
     const int64_t seg_len = (((int64_t)Tk + nseg - 1) / nseg + 3) & ~(int64_t)3;   // segments start on quads
     int32_t* cand = static_cast<int32_t*>(ws);
     hipLaunchKernelGGL(topk_kernel, dim3(Tq * nseg), dim3(kTopkThreads), 0, stream, scores, ld, Tk,
-                       q_pos0, row_len, k, nseg, seg_len, cand);
+                       q_pos0, row_len, k, nseg, seg_len, cand, run_if);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_merge_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, scores, ld, Tk,
                        q_pos0, row_len, k, nseg, cand, idx);
+    return hipGetLastError();
+}
+
+int fused_sample_count(int Tk)
+{
+    // about one sample per 64 candidates (at least 2048), so that the padded bound keeps
+    // the expected candidate count near k (1 + 5/sqrt(32) + 8/32) and far below kCandCap
+    if (Tk <= kCandCap) return 0;
+    int S = (Tk / 64 + 1023) / 1024 * 1024;
+    if (S < 2048) S = 2048;
+    return S > kCandCap ? -1 : S;                    // -1: too long for the candidate path
+}
+
+hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0, int k,
+                             float* tau, int32_t* cnt, int* fallback, hipStream_t stream)
+{
+    if (Tq == 0) return hipSuccess;
+    if (S > kCandCap) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(topk_bound_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, samples, S,
+                       q_pos0, k, tau, cnt, fallback);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_select(const uint2* cand, const int32_t* cnt, int Tq, int64_t q_pos0,
+                              int k, int32_t* idx, int* fallback, hipStream_t stream)
+{
+    if (Tq == 0) return hipSuccess;
+    if (k > kCandCap) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(topk_select_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, cand, cnt,
+                       q_pos0, k, idx, fallback);
     return hipGetLastError();
 }
 

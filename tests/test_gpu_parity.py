@@ -357,6 +357,53 @@ def test_prefill_edge_sizes():
                     cfg.sm_scale, 0, x["q"], None, ws, ws.numel())
 
 
+def _staged_prefill(x, k, sm_scale, G):
+    """The layer through the separate entry points over full score rows."""
+    Tk = x["k_idx"].shape[0]
+    scores = dsa.index_scores(x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"])
+    idx = dsa.topk(scores, Tk, k)
+    del scores
+    out = dsa.sparse_gqa_attn(x["q"], x["k"], x["v"], idx, G, sm_scale, split=False)
+    return out, idx
+
+
+@pytest.mark.parametrize("L,k,chunk,keys", [(20000, 2048, 4096, "clustered"), (20000, 512, 6000, "iid"),
+                                            (12289, 2048, 0, "iid"), (9000, 1024, 2500, "clustered")])
+def test_prefill_candidate_path_equals_staged(L, k, chunk, keys):
+    """The fused prefill selects from sampled-bound candidate lists; its Omega and output must
+    be bitwise those of the indexer + top-k + attention entry points over full score rows
+    (rows beyond 8192 positions take the sampled bound, the others every causal score)."""
+    cfg = W.scaled(W.PREFILL_32K, L=L, k=k, keys=keys, seed=L + k)
+    _say("candidate path vs staged", L, k, chunk, keys)
+    x = W.prefill_inputs(cfg, DEV)
+    out, idx = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
+                           x["k_scale"], k, cfg.sm_scale, chunk_rows=chunk, return_idx=True)
+    out_s, idx_s = _staged_prefill(x, k, cfg.sm_scale, cfg.G)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_s)
+    assert torch.equal(out, out_s)
+
+
+def test_prefill_ties_take_the_exact_fallback():
+    """One key for every position: each row's scores all tie, so a row longer than the
+    candidate capacity overflows its list and its chunk is redone over full score rows; the
+    result must still be positions 0..k-1 (ties to the lower position), as in the staged path."""
+    L, k = 10000, 2048
+    cfg = W.scaled(W.PREFILL_32K, L=L, k=k, seed=77)
+    x = W.prefill_inputs(cfg, DEV)
+    x["k_idx"] = x["k_idx"][:1].expand_as(x["k_idx"]).contiguous()
+    x["k_scale"] = x["k_scale"][:1].expand_as(x["k_scale"]).contiguous()
+    out, idx = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
+                           x["k_scale"], k, cfg.sm_scale, chunk_rows=2048, return_idx=True)
+    out_s, idx_s = _staged_prefill(x, k, cfg.sm_scale, cfg.G)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_s) and torch.equal(out, out_s)
+    ii = to_np(idx)
+    for t in (0, 100, 2047, 2048, 5000, 8191, 8192, 9999):
+        n = min(k, t + 1)
+        assert ii[t, :n].tolist() == list(range(n)) and np.all(ii[t, n:] == -1)
+
+
 @pytest.mark.parametrize("name", ["prefill_32k", "prefill_128k_clustered", "prefill_256k_multimodal"])
 def test_prefill_full_size_sampled(name):
     """Full-size workloads in the benchmark's chunking, checked on stratified rows."""
