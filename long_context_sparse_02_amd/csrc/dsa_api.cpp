@@ -333,13 +333,15 @@ DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v,
             e = dsa::launch_index_fp8_sample(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI, pos0,
                                              samples, S, index_ws, stream);
             if (e == hipSuccess)
-                e = dsa::launch_topk_bound(samples, S, rows, pos0, topk, tau, cnt, fallback, stream);
+                e = dsa::launch_topk_bound(samples, S, rows, pos0, nullptr, 0, topk, tau, cnt, fallback,
+                                           stream);
             if (e == hipSuccess)
                 e = dsa::launch_index_fp8_candidates(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI,
                                                      pos0, tau, cnt, cand, dsa::kCandCap,
                                                      index_ws, stream);
             if (e == hipSuccess)
-                e = dsa::launch_topk_select(cand, cnt, rows, pos0, topk, idx_c, fallback, stream);
+                e = dsa::launch_topk_select(cand, cnt, rows, pos0, nullptr, 0, topk, idx_c, fallback,
+                                            stream);
             if (e == hipSuccess)
                 e = dsa::launch_index_fp8(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI, pos0, scores,
                                           plan.ld, index_ws, stream, fallback, true);
@@ -367,18 +369,32 @@ namespace {
 struct DecodePlan {
     int64_t ld;
     int nsplit;
-    size_t scores_bytes, idx_bytes, part_bytes, topk_bytes, total;
+    int S;                                     // samples per sequence (candidate path), or -1
+    size_t scores_bytes, idx_bytes, part_bytes, topk_bytes;
+    size_t samples_bytes, tau_bytes, cnt_bytes, cand_bytes, flag_bytes, total;
 };
 
+// Scores of every sequence, index sets, attention partials, the segmented top-k's scratch,
+// and the candidate pipeline's buffers (as for the prefill, one row per sequence).
 DecodePlan plan_decode(int B, int max_blocks, int block_size, int topk, int Hq, int d) {
     DecodePlan p;
-    p.ld = ld_for((int64_t)max_blocks * block_size);
+    const int max_len = (int)((int64_t)max_blocks * block_size);
+    p.ld = ld_for(max_len);
     p.scores_bytes = round_up((size_t)B * p.ld * sizeof(float));
     p.idx_bytes = round_up((size_t)B * topk * sizeof(int32_t));
     p.nsplit = dsa::attn_num_splits(B, topk);
     p.part_bytes = round_up(dsa::attn_partials_bytes(B, p.nsplit, Hq, d));
-    p.topk_bytes = round_up(dsa::topk_workspace_bytes(B, (int)((int64_t)max_blocks * block_size), topk));
-    p.total = p.scores_bytes + p.idx_bytes + p.part_bytes + p.topk_bytes;
+    p.topk_bytes = round_up(dsa::topk_workspace_bytes(B, max_len, topk));
+    p.S = max_len >= kCandMinKeys ? dsa::fused_sample_count(max_len) : -1;
+    const int S = p.S > 0 ? p.S : 0;
+    const bool cand = p.S > 0;
+    p.samples_bytes = round_up((size_t)B * S * sizeof(float));
+    p.tau_bytes = cand ? round_up((size_t)B * sizeof(float)) : 0;
+    p.cnt_bytes = cand ? round_up((size_t)B * sizeof(int32_t)) : 0;
+    p.cand_bytes = cand ? round_up((size_t)B * dsa::kCandCap * sizeof(uint2)) : 0;
+    p.flag_bytes = cand ? kAlign : 0;
+    p.total = p.scores_bytes + p.idx_bytes + p.part_bytes + p.topk_bytes + p.samples_bytes +
+              p.tau_bytes + p.cnt_bytes + p.cand_bytes + p.flag_bytes;
     return p;
 }
 
@@ -421,21 +437,56 @@ DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float
     const DecodePlan plan = plan_decode(B, max_blocks, block_size, topk, Hq, d);
     REQUIRE(ws && aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
             "decode needs %zu workspace bytes (got %zu%s)", plan.total, ws_bytes, ws ? "" : ", ws is NULL");
-    char* base = static_cast<char*>(ws);
-    float* scores = reinterpret_cast<float*>(base);
-    int32_t* idx_c = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + plan.scores_bytes);
-    float* partials = reinterpret_cast<float*>(base + plan.scores_bytes + plan.idx_bytes);
-    void* topk_ws = plan.topk_bytes ? base + plan.scores_bytes + plan.idx_bytes + plan.part_bytes
-                                    : nullptr;
-    const int cap = max_blocks * block_size;
+    char* wp = static_cast<char*>(ws);
+    float* scores = reinterpret_cast<float*>(wp);                    wp += plan.scores_bytes;
+    int32_t* idx_ws = reinterpret_cast<int32_t*>(wp);                wp += plan.idx_bytes;
+    float* partials = reinterpret_cast<float*>(wp);                  wp += plan.part_bytes;
+    void* topk_ws = plan.topk_bytes ? wp : nullptr;                  wp += plan.topk_bytes;
+    float* samples = reinterpret_cast<float*>(wp);                   wp += plan.samples_bytes;
+    float* tau = reinterpret_cast<float*>(wp);                       wp += plan.tau_bytes;
+    int32_t* cnt = reinterpret_cast<int32_t*>(wp);                   wp += plan.cnt_bytes;
+    uint2* cand = reinterpret_cast<uint2*>(wp);                      wp += plan.cand_bytes;
+    int* fallback = reinterpret_cast<int*>(wp);
+    int32_t* idx_c = idx_out ? idx_out : idx_ws;
+    const int max_len = max_blocks * block_size;
+    const auto* qi8 = static_cast<const uint8_t*>(q_idx);
+    const auto* kc8 = static_cast<const uint8_t*>(kidx_cache);
 
-    hipError_t e = dsa::launch_index_fp8_paged(
-        static_cast<const uint8_t*>(q_idx), q_scale, w, static_cast<const uint8_t*>(kidx_cache),
-        kidx_scale, block_table, seq_lens, B, num_blocks, max_blocks, block_size, HI, scores,
-        plan.ld, stream);
-    if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
-    e = dsa::launch_topk(scores, plan.ld, B, cap, 0, seq_lens, topk, idx_c, topk_ws, stream);
-    if (e != hipSuccess) return hip_fail(e, "decode top-k launch");
+    hipError_t e = hipSuccess;
+    if (plan.S > 0 && HI <= 64 && topk <= dsa::kCandCap) {
+        // sampled bound -> candidates at or above it -> exact select; if any sequence's
+        // candidates cannot give the exact answer, the two gated launches redo the step over
+        // full score rows (as in the prefill)
+        e = dsa::launch_index_fp8_paged_sample(qi8, q_scale, w, kc8, kidx_scale, block_table,
+                                               seq_lens, B, num_blocks, max_blocks, block_size,
+                                               HI, samples, plan.S, stream);
+        if (e == hipSuccess)
+            e = dsa::launch_topk_bound(samples, plan.S, B, 0, seq_lens, max_len, topk, tau, cnt,
+                                       fallback, stream);
+        if (e == hipSuccess)
+            e = dsa::launch_index_fp8_paged_candidates(qi8, q_scale, w, kc8, kidx_scale,
+                                                       block_table, seq_lens, B, num_blocks,
+                                                       max_blocks, block_size, HI, tau, cnt,
+                                                       cand, dsa::kCandCap, stream);
+        if (e == hipSuccess)
+            e = dsa::launch_topk_select(cand, cnt, B, 0, seq_lens, max_len, topk, idx_c, fallback,
+                                        stream);
+        if (e == hipSuccess)
+            e = dsa::launch_index_fp8_paged(qi8, q_scale, w, kc8, kidx_scale, block_table,
+                                            seq_lens, B, num_blocks, max_blocks, block_size, HI,
+                                            scores, plan.ld, stream, fallback);
+        if (e == hipSuccess)
+            e = dsa::launch_topk(scores, plan.ld, B, max_len, 0, seq_lens, topk, idx_c, nullptr,
+                                 stream, fallback);
+        if (e != hipSuccess) return hip_fail(e, "decode selection launch");
+    } else {
+        e = dsa::launch_index_fp8_paged(qi8, q_scale, w, kc8, kidx_scale, block_table, seq_lens,
+                                        B, num_blocks, max_blocks, block_size, HI, scores,
+                                        plan.ld, stream);
+        if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
+        e = dsa::launch_topk(scores, plan.ld, B, max_len, 0, seq_lens, topk, idx_c, topk_ws, stream);
+        if (e != hipSuccess) return hip_fail(e, "decode top-k launch");
+    }
     return run_attn(q, k_cache, v_cache, dtype, num_blocks, block_table, max_blocks, block_size,
                     nullptr, seq_lens, idx_c, B, topk, Hq, G, d, sm_scale, out, partials,
                     plan.part_bytes, stream);

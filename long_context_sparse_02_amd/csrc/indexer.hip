@@ -633,30 +633,46 @@ struct PageRegs {
 #ifndef DSA_DEC_WAVES
 #define DSA_DEC_WAVES 4
 #endif
-template <int NHT>                                 // 16-head tiles of the query
+// Output modes, as in the prefill kernel: every score of the sequence into scores[b, s];
+// the scores of S sampled positions (per-key stratified, hashed offsets) into
+// samples[b, j] (a "page" is then 64 consecutive samples); or only the scores >= tau[b]
+// appended as (order key, position) to the sequence's list, one atomic per wave.
+struct PagedOut {
+    float* scores; int64_t ld; const int* run_if;
+    float* samples; int S;
+    const float* tau; int32_t* cnt; uint2* cand; int cap;
+};
+
+// Sampled keys cost two dependent round trips per page (block id, then key) and a sample
+// launch is small, so its waves take fewer pages each.
+template <int MODE> constexpr int paged_ppw() { return MODE == kModeSample ? 2 : kDecPagesPerWave; }
+
+template <int NHT, int MODE>                       // 16-head tiles of the query
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_DEC_WAVES)))
 void index_fp8_paged_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ kcache,
     const float* __restrict__ kscale, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int num_blocks, int max_blocks, int block_size, int HI,
-    float* __restrict__ scores, int64_t ld, int n_split)
+    PagedOut o, int n_split)
 {
+    constexpr int PPW = paged_ppw<MODE>();
     __shared__ __attribute__((aligned(16))) uint8_t q_lds[16 * NHT * kDecQPitch];
     __shared__ __attribute__((aligned(16))) float w_lds[16 * NHT];
+    if (MODE == kModeScores && o.run_if && *o.run_if == 0) return;
     // block_size is 64 here (checked by the launcher): one page = one 64-key iteration
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     const int b = work / n_split, sp = work - b * n_split;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int page0 = (sp * kIdxWaves + wave) * kDecPagesPerWave;
+    const int page0 = (sp * kIdxWaves + wave) * PPW;
 
     // 1. one round trip for everything the pages depend on: the sequence length,
     //    the block ids of this wave's pages (clamped into the table row), the
     //    query's head rows (heads >= HI read head HI-1 and are zeroed) and weights
     const int64_t len = seq_lens[b];
-    const int bt = block_table[(int64_t)b * max_blocks +
-                               min(page0 + min(lane, kDecPagesPerWave - 1), max_blocks - 1)];
+    const int bt = MODE == kModeSample ? 0 : block_table[(int64_t)b * max_blocks +
+                               min(page0 + min(lane, PPW - 1), max_blocks - 1)];
     constexpr int kQChunks = 16 * NHT * 8;         // 16-byte chunks of the head tiles
     constexpr int kQPer = (kQChunks + 255) / 256;
     v4i qv[kQPer];
@@ -668,26 +684,44 @@ void index_fp8_paged_kernel(
     }
     const float wq = w[(int64_t)b * HI + min(tid, HI - 1)];
     const float qs = q_scale[b];
+    const float tau_b = MODE == kModeCandidates ? o.tau[b] : 0.f;
 
     const int64_t cap = (int64_t)max_blocks * 64;
     if (len < 1 || len > cap || num_blocks <= 0) return;       // uniform over the workgroup
-    const int n_pages = (int)((len + 63) >> 6);
-    if (sp * kIdxWaves * kDecPagesPerWave >= n_pages) return;   // uniform over the workgroup
-    const int np = max(0, min(kDecPagesPerWave, n_pages - page0));
+    // pages of this launch: the sequence's key pages, or S / 64 pages of samples
+    const int n_pages = MODE == kModeSample ? o.S / 64 : (int)((len + 63) >> 6);
+    if (sp * kIdxWaves * PPW >= n_pages) return;   // uniform over the workgroup
+    const int np = max(0, min(PPW, n_pages - page0));
     // 2. block ids of this wave's pages (-1 when outside the cache)
     const int blk_l = (lane < np && bt >= 0 && bt < num_blocks) ? bt : -1;
+    const int last = max(np - 1, 0);
     // unconditional loads (an invalid block reads block 0 and is masked to -inf
     // afterwards): no branch around them, so the next pages stay in flight
     auto fetch = [&](int i, PageRegs& r) {
+        if (MODE == kModeSample) {
+            // lane (col, grp) loads sample 64 pg + 16 u + col of tile u, and the scale of
+            // sample 64 pg + lane (tile grp); an invalid block id reads row 0 and is masked
+            const int pg = page0 + i;
+            int srow = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int pos = sample_pos(min(pg * 64 + 16 * u + col, o.S - 1), o.S, (int)len, b);
+                const int blk = block_table[(int64_t)b * max_blocks + (pos >> 6)];
+                const int row = (blk >= 0 && blk < num_blocks) ? blk * 64 + (pos & 63) : -1;
+                r.k[u] = load32B(kcache + (int64_t)max(row, 0) * 128 + grp * 32);
+                if (u == grp) srow = row;
+            }
+            r.scale = srow >= 0 ? kscale[srow] : -INFINITY;   // -inf scale marks the sample invalid
+            return;
+        }
         const int blk = __shfl(blk_l, i, 64);
         const int64_t base = (int64_t)(blk < 0 ? 0 : blk) * 64;
 #pragma unroll
         for (int u = 0; u < 4; ++u) r.k[u] = load32B(kcache + (base + 16 * u + col) * 128 + grp * 32);
         r.scale = kscale[base + lane];
     };
-    const int last = max(np - 1, 0);
     PageRegs ring[kDecDepth + 1];
-    float res[kDecPagesPerWave];                   // scores, stored after the page loop
+    float res[PPW];                   // scores, stored after the page loop
 #pragma unroll
     for (int i = 0; i < kDecDepth; ++i) fetch(min(i, last), ring[i]);
     // 3. stage the head tiles and weights while the first pages are in flight
@@ -704,11 +738,10 @@ void index_fp8_paged_kernel(
     __syncthreads();
 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    float* __restrict__ out = scores + (int64_t)b * ld;
     // fully unrolled (a rolled loop makes the compiler wait on in-flight pages at
     // the back edge): ring slots are compile-time constants
 #pragma unroll
-    for (int i = 0; i < kDecPagesPerWave; ++i) {
+    for (int i = 0; i < PPW; ++i) {
         if (i >= np) break;
         fetch(min(i + kDecDepth, last), ring[(i + kDecDepth) % (kDecDepth + 1)]);
         const PageRegs& cur = ring[i % (kDecDepth + 1)];
@@ -740,15 +773,45 @@ void index_fp8_paged_kernel(
         k1 += __shfl_xor(t1, 32, 64);
         float mine = b0 ? k1 : k0;
         mine += __shfl_xor(b0 ? k0 : k1, 16, 64);
-        const bool valid = __shfl(blk_l, i, 64) >= 0;
-        res[i] = valid ? mine * (qs * cur.scale) : -INFINITY;
+        if (MODE == kModeSample) {
+            res[i] = cur.scale == -INFINITY ? -INFINITY : mine * (qs * cur.scale);
+        } else {
+            const bool valid = __shfl(blk_l, i, 64) >= 0;
+            res[i] = valid ? mine * (qs * cur.scale) : -INFINITY;
+        }
+    }
+    if (MODE == kModeCandidates) {
+        // keep the sequence's keys at or above its bound (invalid and out-of-range keys
+        // hold -inf or are excluded); one atomic per wave reserves the room
+        uint64_t kept[PPW];
+        uint32_t total = 0;
+#pragma unroll
+        for (int i = 0; i < PPW; ++i) {
+            const int64_t s = (int64_t)(page0 + i) * 64 + lane;
+            kept[i] = __ballot(i < np && s < len && res[i] >= tau_b);
+            total += __popcll(kept[i]);
+        }
+        uint32_t base = 0;
+        if (lane == 0 && total) base = (uint32_t)atomicAdd(o.cnt + b, (int)total);
+        base = __shfl(base, 0, 64);
+        uint2* __restrict__ dst = o.cand + (int64_t)b * o.cap;
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+        for (int i = 0; i < PPW; ++i) {
+            const uint32_t slot = base + __popcll(kept[i] & below);
+            if (((kept[i] >> lane) & 1ull) && slot < (uint32_t)o.cap)
+                dst[slot] = make_uint2(order_key(res[i]), (uint32_t)((page0 + i) * 64 + lane));
+            base += __popcll(kept[i]);
+        }
+        return;
     }
     // score stores interleaved with the page stream slow it down: issue them last
+    float* __restrict__ out = MODE == kModeSample ? o.samples + (int64_t)b * o.S : o.scores + (int64_t)b * o.ld;
 #pragma unroll
-    for (int i = 0; i < kDecPagesPerWave; ++i) {
+    for (int i = 0; i < PPW; ++i) {
         if (i >= np) break;
         const int64_t s = (int64_t)(page0 + i) * 64 + lane;
-        if (s < len) out[s] = res[i];
+        if (MODE == kModeSample || s < len) out[s] = res[i];
     }
 }
 
@@ -857,27 +920,76 @@ hipError_t launch_index_f32(const float* q_idx, const float* w, const float* k_i
     return hipGetLastError();
 }
 
-hipError_t launch_index_fp8_paged(const uint8_t* q_idx, const float* q_scale, const float* w,
-                                  const uint8_t* kidx_cache, const float* kidx_scale,
-                                  const int32_t* block_table, const int32_t* seq_lens, int B,
-                                  int num_blocks, int max_blocks, int block_size, int HI,
-                                  float* scores, int64_t ld, hipStream_t stream)
+namespace {
+
+// pages: pages per sequence the launch walks (max_blocks for keys, S / 64 for samples)
+template <int MODE>
+hipError_t launch_paged(const uint8_t* q_idx, const float* q_scale, const float* w,
+                        const uint8_t* kidx_cache, const float* kidx_scale,
+                        const int32_t* block_table, const int32_t* seq_lens, int B, int num_blocks,
+                        int max_blocks, int block_size, int HI, const PagedOut& o, int pages,
+                        hipStream_t stream)
 {
     if (block_size != 64) return hipErrorInvalidValue;
-    const int pages_per_wg = kIdxWaves * kDecPagesPerWave;
-    const int n_split = (max_blocks + pages_per_wg - 1) / pages_per_wg;
+    const int pages_per_wg = kIdxWaves * paged_ppw<MODE>();
+    const int n_split = (pages + pages_per_wg - 1) / pages_per_wg;
     const int64_t n = (int64_t)B * n_split;
     if (n == 0) return hipSuccess;
     if (n > INT32_MAX) return hipErrorInvalidValue;
     if (HI <= 64)
-        hipLaunchKernelGGL(index_fp8_paged_kernel<4>, dim3((unsigned)n), dim3(256), 0, stream, q_idx,
-                           q_scale, w, kidx_cache, kidx_scale, block_table, seq_lens, num_blocks,
-                           max_blocks, block_size, HI, scores, ld, n_split);
+        hipLaunchKernelGGL((index_fp8_paged_kernel<4, MODE>), dim3((unsigned)n), dim3(256), 0, stream,
+                           q_idx, q_scale, w, kidx_cache, kidx_scale, block_table, seq_lens,
+                           num_blocks, max_blocks, block_size, HI, o, n_split);
     else
-        hipLaunchKernelGGL(index_fp8_paged_kernel<8>, dim3((unsigned)n), dim3(256), 0, stream, q_idx,
-                           q_scale, w, kidx_cache, kidx_scale, block_table, seq_lens, num_blocks,
-                           max_blocks, block_size, HI, scores, ld, n_split);
+        hipLaunchKernelGGL((index_fp8_paged_kernel<8, MODE>), dim3((unsigned)n), dim3(256), 0, stream,
+                           q_idx, q_scale, w, kidx_cache, kidx_scale, block_table, seq_lens,
+                           num_blocks, max_blocks, block_size, HI, o, n_split);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_fp8_paged(const uint8_t* q_idx, const float* q_scale, const float* w,
+                                  const uint8_t* kidx_cache, const float* kidx_scale,
+                                  const int32_t* block_table, const int32_t* seq_lens, int B,
+                                  int num_blocks, int max_blocks, int block_size, int HI,
+                                  float* scores, int64_t ld, hipStream_t stream, const int* run_if)
+{
+    PagedOut o = {};
+    o.scores = scores; o.ld = ld; o.run_if = run_if;
+    return launch_paged<kModeScores>(q_idx, q_scale, w, kidx_cache, kidx_scale, block_table,
+                                     seq_lens, B, num_blocks, max_blocks, block_size, HI, o,
+                                     max_blocks, stream);
+}
+
+hipError_t launch_index_fp8_paged_sample(const uint8_t* q_idx, const float* q_scale,
+                                         const float* w, const uint8_t* kidx_cache,
+                                         const float* kidx_scale, const int32_t* block_table,
+                                         const int32_t* seq_lens, int B, int num_blocks,
+                                         int max_blocks, int block_size, int HI, float* samples,
+                                         int S, hipStream_t stream)
+{
+    if (S <= 0 || S % 64 != 0) return hipErrorInvalidValue;
+    PagedOut o = {};
+    o.samples = samples; o.S = S;
+    return launch_paged<kModeSample>(q_idx, q_scale, w, kidx_cache, kidx_scale, block_table,
+                                     seq_lens, B, num_blocks, max_blocks, block_size, HI, o,
+                                     S / 64, stream);
+}
+
+hipError_t launch_index_fp8_paged_candidates(const uint8_t* q_idx, const float* q_scale,
+                                             const float* w, const uint8_t* kidx_cache,
+                                             const float* kidx_scale, const int32_t* block_table,
+                                             const int32_t* seq_lens, int B, int num_blocks,
+                                             int max_blocks, int block_size, int HI,
+                                             const float* tau, int32_t* cnt, uint2* cand, int cap,
+                                             hipStream_t stream)
+{
+    PagedOut o = {};
+    o.tau = tau; o.cnt = cnt; o.cand = cand; o.cap = cap;
+    return launch_paged<kModeCandidates>(q_idx, q_scale, w, kidx_cache, kidx_scale, block_table,
+                                         seq_lens, B, num_blocks, max_blocks, block_size, HI, o,
+                                         max_blocks, stream);
 }
 
 }  // namespace dsa

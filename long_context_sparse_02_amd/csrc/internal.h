@@ -41,7 +41,24 @@ hipError_t launch_index_fp8_paged(const uint8_t* q_idx, const float* q_scale, co
                                   const uint8_t* kidx_cache, const float* kidx_scale,
                                   const int32_t* block_table, const int32_t* seq_lens, int B,
                                   int num_blocks, int max_blocks, int block_size, int HI,
-                                  float* scores, int64_t ld, hipStream_t stream);
+                                  float* scores, int64_t ld, hipStream_t stream,
+                                  const int* run_if = nullptr);
+// Candidate pipeline of the decode step, as for the prefill: the scores of S sampled
+// positions of each sequence (S a multiple of 64) into samples [B, S], then every score
+// >= tau[b] appended to the sequence's list cand [B, cap] (cnt[b] must start at 0).
+hipError_t launch_index_fp8_paged_sample(const uint8_t* q_idx, const float* q_scale,
+                                         const float* w, const uint8_t* kidx_cache,
+                                         const float* kidx_scale, const int32_t* block_table,
+                                         const int32_t* seq_lens, int B, int num_blocks,
+                                         int max_blocks, int block_size, int HI, float* samples,
+                                         int S, hipStream_t stream);
+hipError_t launch_index_fp8_paged_candidates(const uint8_t* q_idx, const float* q_scale,
+                                             const float* w, const uint8_t* kidx_cache,
+                                             const float* kidx_scale, const int32_t* block_table,
+                                             const int32_t* seq_lens, int B, int num_blocks,
+                                             int max_blocks, int block_size, int HI,
+                                             const float* tau, int32_t* cnt, uint2* cand, int cap,
+                                             hipStream_t stream);
 
 // Top-k per row.  Candidates of row i: 0 .. n_i-1 with n_i = q_pos0 + i + 1, or
 // n_i = row_len[i] when row_len is given (0 if outside [0, Tk]).  With a workspace of
@@ -58,10 +75,14 @@ hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t 
 // position, -1 padded); a row whose list cannot give an exact answer sets *fallback = 1.
 constexpr int kCandCap = 8192;
 int fused_sample_count(int Tk);
-hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0, int k,
-                             float* tau, int32_t* cnt, int* fallback, hipStream_t stream);
+// row_len (nullable): row lengths n = row_len[row] instead of q_pos0 + row + 1 (rows with a
+// length outside [1, max_len] select nothing: an index row of -1).
+hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0,
+                             const int32_t* row_len, int max_len, int k, float* tau, int32_t* cnt,
+                             int* fallback, hipStream_t stream);
 hipError_t launch_topk_select(const uint2* cand, const int32_t* cnt, int Tq, int64_t q_pos0,
-                              int k, int32_t* idx, int* fallback, hipStream_t stream);
+                              const int32_t* row_len, int max_len, int k, int32_t* idx,
+                              int* fallback, hipStream_t stream);
 
 struct AttnArgs {
     const void* q; const void* k; const void* v; void* out;

@@ -461,8 +461,8 @@ __device__ void bitonic_sort_asc(uint32_t* a, int len) {
 
 // Lower bound of row `row`'s k-th largest score from its S samples (see launch_topk_bound).
 __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
-    const float* __restrict__ samples, int S, int64_t q_pos0, int k, float* __restrict__ tau,
-    int32_t* __restrict__ cnt, int* __restrict__ fallback)
+    const float* __restrict__ samples, int S, int64_t q_pos0, const int32_t* __restrict__ row_len,
+    int max_len, int k, float* __restrict__ tau, int32_t* __restrict__ cnt, int* __restrict__ fallback)
 {
     __shared__ uint32_t smp[kCandCap];
     __shared__ uint32_t hist[kBins];
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
         cnt[row] = 0;
         if (row == 0) *fallback = 0;
     }
-    const int64_t n = q_pos0 + row + 1;
+    const int64_t n = row_len ? row_length(row, max_len, 0, row_len) : q_pos0 + row + 1;
     if (n <= kCandCap || S <= 0) {                   // every causal score is a candidate
         if (tid == 0) tau[row] = -FLT_MAX;
         return;
@@ -503,8 +503,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
 // Omega of one row from its candidate list: exact select of the k-th largest key, the
 // candidates above it plus the lowest-position ties, sorted ascending.
 __global__ __launch_bounds__(kTopkThreads, 8) void topk_select_kernel(
-    const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, int64_t q_pos0, int k,
-    int32_t* __restrict__ idx, int* __restrict__ fallback)
+    const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, int64_t q_pos0,
+    const int32_t* __restrict__ row_len, int max_len, int k, int32_t* __restrict__ idx,
+    int* __restrict__ fallback)
 {
     __shared__ uint32_t ck[kCandCap];                 // keys, later the selected positions
     __shared__ uint32_t ci[kCandCap];                 // positions, later the tied positions
@@ -512,9 +513,9 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_select_kernel(
     __shared__ uint32_t wsum[2 * kTopkWaves];
     __shared__ uint32_t sh[4];
     const int row = blockIdx.x, tid = threadIdx.x;
-    const int64_t n = q_pos0 + row + 1;
+    const int64_t n = row_len ? row_length(row, max_len, 0, row_len) : q_pos0 + row + 1;
     int32_t* __restrict__ out = idx + (int64_t)row * k;
-    if (n <= k) {
+    if (n <= k) {                                     // (n = 0: an invalid length, all -1)
         for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
         return;
     }
@@ -647,23 +648,25 @@ int fused_sample_count(int Tk)
     return S > kCandCap ? -1 : S;                    // -1: too long for the candidate path
 }
 
-hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0, int k,
-                             float* tau, int32_t* cnt, int* fallback, hipStream_t stream)
+hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0,
+                             const int32_t* row_len, int max_len, int k, float* tau, int32_t* cnt,
+                             int* fallback, hipStream_t stream)
 {
     if (Tq == 0) return hipSuccess;
     if (S > kCandCap) return hipErrorInvalidValue;
     hipLaunchKernelGGL(topk_bound_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, samples, S,
-                       q_pos0, k, tau, cnt, fallback);
+                       q_pos0, row_len, max_len, k, tau, cnt, fallback);
     return hipGetLastError();
 }
 
 hipError_t launch_topk_select(const uint2* cand, const int32_t* cnt, int Tq, int64_t q_pos0,
-                              int k, int32_t* idx, int* fallback, hipStream_t stream)
+                              const int32_t* row_len, int max_len, int k, int32_t* idx,
+                              int* fallback, hipStream_t stream)
 {
     if (Tq == 0) return hipSuccess;
     if (k > kCandCap) return hipErrorInvalidValue;
     hipLaunchKernelGGL(topk_select_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, cand, cnt,
-                       q_pos0, k, idx, fallback);
+                       q_pos0, row_len, max_len, k, idx, fallback);
     return hipGetLastError();
 }
 

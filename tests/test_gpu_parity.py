@@ -528,6 +528,48 @@ def test_decode_equals_prefill_last_row():
         assert (out_p[-1].float() - out_d[0].float()).abs().max().item() <= 2e-2
 
 
+def test_decode_candidate_path_equals_full_rows():
+    """The same sequences decoded with a block table of 640 columns (40K keys: full score
+    rows and the top-k kernel) and padded to 1024 columns (64K: the sampled-bound candidate
+    path) give bitwise the same index sets and outputs."""
+    cfg = W.scaled(W.DECODE_PAGED, B=12, Lmin=1, Lmax=40960, k=2048, seed=91)
+    lens = torch.tensor([1, 2047, 2048, 2049, 8192, 8193, 9000, 12345, 20000, 33333, 40000, 40960])
+    x = W.decode_inputs(cfg, DEV, lens=lens)
+    assert x["max_blocks"] == 640
+    args = (x["q"], x["q_idx"], x["q_scale"], x["w"], x["kidx_cache"], x["kidx_scale"],
+            x["k_cache"], x["v_cache"])
+    out_a, idx_a = dsa.decode(*args, x["block_table"], x["seq_lens"], cfg.k, cfg.sm_scale,
+                              return_idx=True)
+    wide = torch.full((cfg.B, 1024), -1, dtype=torch.int32, device=DEV)
+    wide[:, :640] = x["block_table"]
+    out_b, idx_b = dsa.decode(*args, wide, x["seq_lens"], cfg.k, cfg.sm_scale, return_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_b)
+    assert torch.equal(out_a, out_b)
+
+
+def test_decode_ties_take_the_exact_fallback():
+    """One key for every position: each sequence's scores all tie, its candidate list
+    overflows, and the step is redone over full score rows: positions 0..k-1."""
+    cfg = W.scaled(W.DECODE_PAGED, B=3, Lmin=50000, Lmax=70000, k=2048, seed=92)
+    x = W.decode_inputs(cfg, DEV, lens=torch.tensor([50000, 9000, 70000]))
+    x["kidx_cache"] = x["kidx_cache"][:1, :1].expand_as(x["kidx_cache"]).contiguous()
+    x["kidx_scale"] = x["kidx_scale"][:1, :1].expand_as(x["kidx_scale"]).contiguous()
+    out, idx = dsa.decode(x["q"], x["q_idx"], x["q_scale"], x["w"], x["kidx_cache"], x["kidx_scale"],
+                          x["k_cache"], x["v_cache"], x["block_table"], x["seq_lens"], cfg.k,
+                          cfg.sm_scale, return_idx=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(idx), np.tile(np.arange(cfg.k, dtype=np.int32), (cfg.B, 1)))
+
+
+def test_decode_candidate_path_vs_oracle():
+    """Mid-size sequences on the candidate path, every sequence against the oracle."""
+    cfg = W.scaled(W.DECODE_PAGED, B=6, Lmin=8000, Lmax=100000, k=2048, seed=93)
+    lens = torch.tensor([8000, 8193, 30000, 61111, 99999, 100000])
+    x = W.decode_inputs(cfg, DEV, lens=lens)
+    _decode_and_check(cfg, x, list(range(cfg.B)), "decode candidates")
+
+
 @pytest.mark.parametrize("name", ["decode_paged_64x32k-256k", "decode_paged_64x256k"])
 def test_decode_full_size_sampled(name):
     cfg = W.ALL[name]
