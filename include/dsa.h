@@ -191,6 +191,13 @@ dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_
  * row and an index row of -1.  dI must be 128 and block_size 64 (one cache block
  * is one 64-key indexer step); dtype DSA_BF16 or DSA_F32.
  * out [B, Hq, d]; idx_out (nullable) [B, topk].
+ * When max_blocks * block_size is 48K..512K, HI <= 64 and topk <= 8192 the
+ * step takes the same sampled-bound candidate path as dsa_prefill (scores of
+ * about max_len/64 sampled positions per sequence, a padded lower bound of the
+ * topk-th score, only the scores above it kept, exact selection, and a
+ * device-side redo of the step over full score rows if any sequence's kept
+ * scores cannot give the exact answer); the results are those of the full
+ * score rows bit for bit.
  * Workspace: dsa_decode_workspace_size() bytes.
  */
 size_t dsa_decode_workspace_size(int B, int max_blocks, int block_size, int topk, int Hq, int d);
