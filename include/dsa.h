@@ -170,6 +170,15 @@ dsa_status_t dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, ds
  * 8192 x 8 bytes) and per-row bounds and counters.
  */
 size_t dsa_prefill_workspace_size(int Tq, int64_t q_pos0, int chunk_rows, int topk);
+/*
+ * Diagnostics of the candidate path: the byte offset, within a prefill
+ * workspace of these arguments, of two int32 counters that a dsa_prefill call
+ * taking the candidate path rewrites: [0] the chunks that took it, [1] the rows
+ * whose candidates could not give the exact answer (their chunks were redone
+ * over full score rows).  A call that takes the path for no chunk leaves them
+ * untouched.  Returns SIZE_MAX for invalid sizes.
+ */
+size_t dsa_prefill_stats_offset(int Tq, int64_t q_pos0, int chunk_rows, int topk);
 dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_t dtype,
                          const void* q_idx, const float* q_scale, const float* w,
                          const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype,
@@ -201,6 +210,9 @@ dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_
  * Workspace: dsa_decode_workspace_size() bytes.
  */
 size_t dsa_decode_workspace_size(int B, int max_blocks, int block_size, int topk, int Hq, int d);
+/* As dsa_prefill_stats_offset, for a decode workspace ([0] = 1 when the step took the
+ * candidate path); SIZE_MAX when these shapes never take it. */
+size_t dsa_decode_stats_offset(int B, int max_blocks, int block_size, int topk, int Hq, int d);
 dsa_status_t dsa_decode(const void* q, const void* q_idx, const float* q_scale, const float* w,
                         const void* kidx_cache, const float* kidx_scale, const void* k_cache,
                         const void* v_cache, dsa_dtype_t dtype, const int32_t* block_table,

@@ -28,8 +28,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "D
 EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_index_scores_workspace_size", "dsa_index_scores",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_gqa_attn_workspace_size",
-           "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill",
-           "dsa_decode_workspace_size", "dsa_decode"]
+           "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
+           "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode"]
 
 
 class DSAError(RuntimeError):
@@ -66,9 +66,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_sparse_gqa_attn_workspace_size": ([I, I, I, I], SZ),
             "dsa_sparse_gqa_attn": ([P, P, P, I, I, P, I, I, P, P, P, I, I, I, I, I, F, P, P, SZ, P], I),
             "dsa_prefill_workspace_size": ([I, I64, I, I], SZ),
+            "dsa_prefill_stats_offset": ([I, I64, I, I], SZ),
             "dsa_prefill": ([P, P, P, I, P, P, P, P, P, I, I, I64, I, I, I, I, I, I, F, I, P, P, P,
                              SZ, P], I),
             "dsa_decode_workspace_size": ([I, I, I, I, I, I], SZ),
+            "dsa_decode_stats_offset": ([I, I, I, I, I, I], SZ),
             "dsa_decode": ([P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, I, F, P, P,
                             P, SZ, P], I),
         }
@@ -163,6 +165,22 @@ def dsa_decode_workspace_size(B, max_blocks, block_size, topk, Hq, d) -> int:
     return load_library().dsa_decode_workspace_size(B, max_blocks, block_size, topk, Hq, d)
 
 
+def dsa_prefill_stats_offset(Tq, q_pos0, chunk_rows, topk) -> int:
+    return load_library().dsa_prefill_stats_offset(Tq, q_pos0, chunk_rows, topk)
+
+
+def dsa_decode_stats_offset(B, max_blocks, block_size, topk, Hq, d) -> int:
+    return load_library().dsa_decode_stats_offset(B, max_blocks, block_size, topk, Hq, d)
+
+
+def read_stats(ws, offset):
+    """The two candidate-path counters (chunks on the path, rows redone) of a workspace."""
+    import torch
+    if offset < 0 or offset >= (1 << 63):
+        return None
+    return ws.view(torch.uint8)[offset:offset + 8].view(torch.int32).tolist()
+
+
 def dsa_decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, dtype, block_table,
                seq_lens, B, num_blocks, max_blocks, block_size, Hq, G, d, HI, dI, topk, sm_scale,
                out, idx_out, ws, ws_bytes, stream=None):
@@ -219,9 +237,15 @@ def sparse_gqa_attn(q, k, v, idx, G, sm_scale, block_table=None, block_size=0, r
     return out
 
 
+def _zero_stats(ws, off):
+    if 0 <= off < (1 << 63):
+        ws.view(__import__("torch").uint8)[off:off + 8].zero_()
+
+
 def prefill(q, k, v, q_idx, q_scale, w, k_idx, k_scale, topk, sm_scale, chunk_rows=0, q_pos0=0,
-            return_idx=False, ws=None, stream=None):
-    """Fused DSA prefill; returns out (and idx if return_idx)."""
+            return_idx=False, ws=None, stream=None, return_stats=False):
+    """Fused DSA prefill; returns out (and idx if return_idx, and the candidate-path
+    counters [chunks on the path, rows redone] if return_stats)."""
     import torch
     Tq, Hq, d = q.shape
     G = k.shape[1]
@@ -231,15 +255,22 @@ def prefill(q, k, v, q_idx, q_scale, w, k_idx, k_scale, topk, sm_scale, chunk_ro
     n = dsa_prefill_workspace_size(Tq, q_pos0, chunk_rows, topk)
     if ws is None or ws.numel() < n:
         ws = workspace(n, q.device)
+    off = dsa_prefill_stats_offset(Tq, q_pos0, chunk_rows, topk) if return_stats else -1
+    if return_stats:
+        _zero_stats(ws, off)
     dsa_prefill(q, k, v, dtype_code(q), q_idx, q_scale, w, k_idx, k_scale, dtype_code(q_idx), Tq,
                 q_pos0, Hq, G, d, HI, dI, topk, sm_scale, chunk_rows, out, idx, ws, ws.numel(),
                 stream)
-    return (out, idx) if return_idx else out
+    res = (out, idx) if return_idx else (out,)
+    if return_stats:
+        res = res + (read_stats(ws, off),)
+    return res if len(res) > 1 else res[0]
 
 
 def decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, block_table, seq_lens,
-           topk, sm_scale, return_idx=False, ws=None, stream=None):
-    """One paged DSA decode step; returns out (and idx if return_idx)."""
+           topk, sm_scale, return_idx=False, ws=None, stream=None, return_stats=False):
+    """One paged DSA decode step; returns out (and idx if return_idx, and the candidate-path
+    counters if return_stats: None when these shapes never take the path)."""
     import torch
     B, Hq, d = q.shape
     _, HI, dI = q_idx.shape
@@ -250,7 +281,13 @@ def decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, block
     n = dsa_decode_workspace_size(B, max_blocks, bs, topk, Hq, d)
     if ws is None or ws.numel() < n:
         ws = workspace(n, q.device)
+    off = dsa_decode_stats_offset(B, max_blocks, bs, topk, Hq, d) if return_stats else -1
+    if return_stats:
+        _zero_stats(ws, off)
     dsa_decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, dtype_code(q),
                block_table, seq_lens, B, NB, max_blocks, bs, Hq, G, d, HI, dI, topk, sm_scale, out,
                idx, ws, ws.numel(), stream)
-    return (out, idx) if return_idx else out
+    res = (out, idx) if return_idx else (out,)
+    if return_stats:
+        res = res + (read_stats(ws, off),)
+    return res if len(res) > 1 else res[0]

@@ -276,6 +276,12 @@ DSA_EXPORT size_t dsa_prefill_workspace_size(int Tq, int64_t q_pos0, int chunk_r
     return plan_prefill(Tq, q_pos0, chunk_rows, topk).total;
 }
 
+DSA_EXPORT size_t dsa_prefill_stats_offset(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
+    if (Tq <= 0 || q_pos0 < 0 || topk <= 0) return (size_t)-1;
+    const PrefillPlan p = plan_prefill(Tq, q_pos0, chunk_rows, topk);
+    return p.total - p.flag_bytes + sizeof(int);
+}
+
 DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_t dtype,
                                     const void* q_idx, const float* q_scale, const float* w,
                                     const void* k_idx, const float* k_scale,
@@ -312,6 +318,7 @@ DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v,
     // The candidate pipeline needs the resident FP8 indexer and a bounded candidate list;
     // other shapes run the indexer and top-k over full score rows.
     const bool cand_path = idx_dtype == DSA_FP8_E4M3 && HI <= 64 && topk <= dsa::kCandCap;
+    bool first_cand = true;
     for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
         const int rows = (Tq - r0 < plan.chunk) ? Tq - r0 : plan.chunk;
         const int64_t pos0 = q_pos0 + r0;
@@ -334,7 +341,8 @@ DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v,
                                              samples, S, index_ws, stream);
             if (e == hipSuccess)
                 e = dsa::launch_topk_bound(samples, S, rows, pos0, nullptr, 0, topk, tau, cnt, fallback,
-                                           stream);
+                                           first_cand ? 1 : 0, stream);
+            first_cand = false;
             if (e == hipSuccess)
                 e = dsa::launch_index_fp8_candidates(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI,
                                                      pos0, tau, cnt, cand, dsa::kCandCap,
@@ -406,6 +414,13 @@ DSA_EXPORT size_t dsa_decode_workspace_size(int B, int max_blocks, int block_siz
     return plan_decode(B, max_blocks, block_size, topk, Hq, d).total;
 }
 
+DSA_EXPORT size_t dsa_decode_stats_offset(int B, int max_blocks, int block_size, int topk, int Hq,
+                                          int d) {
+    if (B <= 0 || max_blocks <= 0 || block_size <= 0 || topk <= 0 || Hq <= 0 || d <= 0) return (size_t)-1;
+    const DecodePlan p = plan_decode(B, max_blocks, block_size, topk, Hq, d);
+    return p.flag_bytes ? p.total - p.flag_bytes + sizeof(int) : (size_t)-1;
+}
+
 DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float* q_scale,
                                    const float* w, const void* kidx_cache, const float* kidx_scale,
                                    const void* k_cache, const void* v_cache, dsa_dtype_t dtype,
@@ -462,7 +477,7 @@ DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float
                                                HI, samples, plan.S, stream);
         if (e == hipSuccess)
             e = dsa::launch_topk_bound(samples, plan.S, B, 0, seq_lens, max_len, topk, tau, cnt,
-                                       fallback, stream);
+                                       fallback, 1, stream);
         if (e == hipSuccess)
             e = dsa::launch_index_fp8_paged_candidates(qi8, q_scale, w, kc8, kidx_scale,
                                                        block_table, seq_lens, B, num_blocks,

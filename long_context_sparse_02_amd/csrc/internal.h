@@ -70,16 +70,18 @@ hipError_t launch_topk(const float* scores, int64_t ld, int Tq, int Tk, int64_t 
 // Fused-prefill selection.  Bound: for each row of n = q_pos0 + row + 1 > cap candidates, a
 // lower bound for the k-th largest score from the row's S samples, padded so that it fails
 // (fewer than k scores at or above it, or more than cap) with probability ~1e-7; rows with
-// n <= cap get -FLT_MAX (every causal score is a candidate).  It also zeroes cnt and
-// *fallback.  Select: Omega of each row from its candidate list (ascending, ties to the lower
-// position, -1 padded); a row whose list cannot give an exact answer sets *fallback = 1.
+// n <= cap get -FLT_MAX (every causal score is a candidate).  It also zeroes cnt.  Select:
+// Omega of each row from its candidate list (ascending, ties to the lower position, -1
+// padded).  fallback points to int[3]: [0] the chunk's flag, zeroed by the bound launch and
+// set by a row whose list cannot give the exact answer; [1] candidate chunks and [2] such
+// rows in this call (reset by the bound launch of the call's first candidate chunk, `first`).
 constexpr int kCandCap = 8192;
 int fused_sample_count(int Tk);
 // row_len (nullable): row lengths n = row_len[row] instead of q_pos0 + row + 1 (rows with a
 // length outside [1, max_len] select nothing: an index row of -1).
 hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0,
                              const int32_t* row_len, int max_len, int k, float* tau, int32_t* cnt,
-                             int* fallback, hipStream_t stream);
+                             int* fallback, int first, hipStream_t stream);
 hipError_t launch_topk_select(const uint2* cand, const int32_t* cnt, int Tq, int64_t q_pos0,
                               const int32_t* row_len, int max_len, int k, int32_t* idx,
                               int* fallback, hipStream_t stream);

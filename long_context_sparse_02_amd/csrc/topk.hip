@@ -462,7 +462,8 @@ __device__ void bitonic_sort_asc(uint32_t* a, int len) {
 // Lower bound of row `row`'s k-th largest score from its S samples (see launch_topk_bound).
 __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
     const float* __restrict__ samples, int S, int64_t q_pos0, const int32_t* __restrict__ row_len,
-    int max_len, int k, float* __restrict__ tau, int32_t* __restrict__ cnt, int* __restrict__ fallback)
+    int max_len, int k, float* __restrict__ tau, int32_t* __restrict__ cnt, int* __restrict__ fallback,
+    int first)
 {
     __shared__ uint32_t smp[kCandCap];
     __shared__ uint32_t hist[kBins];
@@ -471,7 +472,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
     const int row = blockIdx.x, tid = threadIdx.x;
     if (tid == 0) {
         cnt[row] = 0;
-        if (row == 0) *fallback = 0;
+        if (row == 0) {                               // flag of this chunk; call statistics
+            fallback[0] = 0;
+            if (first) { fallback[1] = 1; fallback[2] = 0; } else { fallback[1] += 1; }
+        }
     }
     const int64_t n = row_len ? row_length(row, max_len, 0, row_len) : q_pos0 + row + 1;
     if (n <= kCandCap || S <= 0) {                   // every causal score is a candidate
@@ -521,7 +525,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_select_kernel(
     }
     const int m = cnt[row];
     if (m < k || m > kCandCap) {                      // the bound missed: exact path for the chunk
-        if (tid == 0) *fallback = 1;
+        if (tid == 0) { fallback[0] = 1; atomicAdd(fallback + 2, 1); }
         return;
     }
     const uint2* __restrict__ src = cand + (int64_t)row * kCandCap;
@@ -650,12 +654,12 @@ int fused_sample_count(int Tk)
 
 hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0,
                              const int32_t* row_len, int max_len, int k, float* tau, int32_t* cnt,
-                             int* fallback, hipStream_t stream)
+                             int* fallback, int first, hipStream_t stream)
 {
     if (Tq == 0) return hipSuccess;
     if (S > kCandCap) return hipErrorInvalidValue;
     hipLaunchKernelGGL(topk_bound_kernel, dim3(Tq), dim3(kTopkThreads), 0, stream, samples, S,
-                       q_pos0, row_len, max_len, k, tau, cnt, fallback);
+                       q_pos0, row_len, max_len, k, tau, cnt, fallback, first);
     return hipGetLastError();
 }
 

@@ -267,10 +267,13 @@ def test_sparse_attn_paged_equals_contiguous(dtype):
 
 def _prefill_and_check(cfg, x, rows, chunk, what, dtype):
     L, k = cfg.L, cfg.k
-    out, idx = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
-                           x["k_scale"], k, cfg.sm_scale, chunk_rows=chunk, return_idx=True)
+    out, idx, stats = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"],
+                                  x["k_idx"], x["k_scale"], k, cfg.sm_scale, chunk_rows=chunk,
+                                  return_idx=True, return_stats=True)
     torch.cuda.synchronize()
-    _say("  prefill done", what)
+    _say("  prefill done", what, "candidate-path counters", stats)
+    if cfg.idx_dtype == "fp8" and cfg.HI <= 64:
+        assert stats == [_cand_chunks(L, 0, chunk), 0]
     idt = oracle.FP8_E4M3 if cfg.idx_dtype == "fp8" else oracle.F32
     qi, w = to_np(x["q_idx"][rows]), to_np(x["w"][rows])
     qs = None if x["q_scale"] is None else to_np(x["q_scale"][rows])
@@ -357,6 +360,12 @@ def test_prefill_edge_sizes():
                     cfg.sm_scale, 0, x["q"], None, ws, ws.numel())
 
 
+def _cand_chunks(Tq, q_pos0, chunk):
+    """Chunks of a prefill call that take the candidate path (they see >= 48K keys)."""
+    C = chunk if 0 < chunk < Tq else Tq
+    return sum(1 for r0 in range(0, Tq, C) if q_pos0 + min(Tq, r0 + C) >= 49152)
+
+
 def _staged_prefill(x, k, sm_scale, G):
     """The layer through the separate entry points over full score rows."""
     Tk = x["k_idx"].shape[0]
@@ -367,18 +376,44 @@ def _staged_prefill(x, k, sm_scale, G):
     return out, idx
 
 
-@pytest.mark.parametrize("L,k,chunk,keys", [(20000, 2048, 4096, "clustered"), (20000, 512, 6000, "iid"),
-                                            (12289, 2048, 0, "iid"), (9000, 1024, 2500, "clustered")])
+@pytest.mark.parametrize("L,k,chunk,keys", [(56000, 2048, 8192, "clustered"), (52000, 512, 0, "iid"),
+                                            (50001, 2048, 7000, "iid"), (20000, 1024, 2500, "clustered")])
 def test_prefill_candidate_path_equals_staged(L, k, chunk, keys):
-    """The fused prefill selects from sampled-bound candidate lists; its Omega and output must
-    be bitwise those of the indexer + top-k + attention entry points over full score rows
-    (rows beyond 8192 positions take the sampled bound, the others every causal score)."""
+    """The fused prefill selects from sampled-bound candidate lists in chunks that see >= 48K
+    keys (rows beyond 8192 positions take the sampled bound, the others every causal score)
+    and over full score rows below that; its Omega and output must be bitwise those of the
+    indexer + top-k + attention entry points over full score rows."""
     cfg = W.scaled(W.PREFILL_32K, L=L, k=k, keys=keys, seed=L + k)
     _say("candidate path vs staged", L, k, chunk, keys)
     x = W.prefill_inputs(cfg, DEV)
-    out, idx = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
-                           x["k_scale"], k, cfg.sm_scale, chunk_rows=chunk, return_idx=True)
+    out, idx, stats = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"],
+                                  x["k_idx"], x["k_scale"], k, cfg.sm_scale, chunk_rows=chunk,
+                                  return_idx=True, return_stats=True)
     out_s, idx_s = _staged_prefill(x, k, cfg.sm_scale, cfg.G)
+    torch.cuda.synchronize()
+    _say("  candidate chunks %d, rows redone %d" % tuple(stats))
+    assert stats == [_cand_chunks(L, 0, chunk), 0]
+    assert torch.equal(idx, idx_s)
+    assert torch.equal(out, out_s)
+
+
+def test_prefill_continuation_candidate_path_equals_staged():
+    """A continuation chunk (queries at positions q_pos0.., the prefix already cached) on the
+    candidate path equals the separate entry points bit for bit."""
+    L, q0, k = 60000, 52000, 2048
+    cfg = W.scaled(W.PREFILL_32K, L=L, k=k, keys="clustered", seed=123)
+    x = W.prefill_inputs(cfg, DEV)
+    sl = slice(q0, L)
+    q, qi, qs, w = (x["q"][sl].contiguous(), x["q_idx"][sl].contiguous(),
+                    x["q_scale"][sl].contiguous(), x["w"][sl].contiguous())
+    out, idx, stats = dsa.prefill(q, x["k"], x["v"], qi, qs, w, x["k_idx"], x["k_scale"], k,
+                                  cfg.sm_scale, chunk_rows=3000, q_pos0=q0, return_idx=True,
+                                  return_stats=True)
+    assert stats == [3, 0]
+    scores = dsa.index_scores(qi, qs, w, x["k_idx"], x["k_scale"], q_pos0=q0)
+    idx_s = dsa.topk(scores, L, k, q_pos0=q0)
+    del scores
+    out_s = dsa.sparse_gqa_attn(q, x["k"], x["v"], idx_s, cfg.G, cfg.sm_scale, split=False)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx_s)
     assert torch.equal(out, out_s)
@@ -388,18 +423,22 @@ def test_prefill_ties_take_the_exact_fallback():
     """One key for every position: each row's scores all tie, so a row longer than the
     candidate capacity overflows its list and its chunk is redone over full score rows; the
     result must still be positions 0..k-1 (ties to the lower position), as in the staged path."""
-    L, k = 10000, 2048
+    L, k = 50000, 2048
     cfg = W.scaled(W.PREFILL_32K, L=L, k=k, seed=77)
     x = W.prefill_inputs(cfg, DEV)
     x["k_idx"] = x["k_idx"][:1].expand_as(x["k_idx"]).contiguous()
     x["k_scale"] = x["k_scale"][:1].expand_as(x["k_scale"]).contiguous()
-    out, idx = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
-                           x["k_scale"], k, cfg.sm_scale, chunk_rows=2048, return_idx=True)
+    # the last two chunks (rows 45056.., seeing 49152 and 50000 keys) take the candidate path
+    # and overflow
+    out, idx, stats = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"],
+                                  x["k_idx"], x["k_scale"], k, cfg.sm_scale, chunk_rows=4096,
+                                  return_idx=True, return_stats=True)
     out_s, idx_s = _staged_prefill(x, k, cfg.sm_scale, cfg.G)
     torch.cuda.synchronize()
+    assert stats[0] == _cand_chunks(L, 0, 4096) == 2 and stats[1] > 0   # redone over full rows
     assert torch.equal(idx, idx_s) and torch.equal(out, out_s)
     ii = to_np(idx)
-    for t in (0, 100, 2047, 2048, 5000, 8191, 8192, 9999):
+    for t in (0, 100, 2047, 2048, 5000, 8191, 8192, 45056, 49999):
         n = min(k, t + 1)
         assert ii[t, :n].tolist() == list(range(n)) and np.all(ii[t, n:] == -1)
 
@@ -443,11 +482,14 @@ def _compact_sequences(x, seqs, bs):
 
 
 def _decode_and_check(cfg, x, seqs, what):
-    out, idx = dsa.decode(x["q"], x["q_idx"], x["q_scale"], x["w"], x["kidx_cache"], x["kidx_scale"],
-                          x["k_cache"], x["v_cache"], x["block_table"], x["seq_lens"], cfg.k,
-                          cfg.sm_scale, return_idx=True)
+    out, idx, stats = dsa.decode(x["q"], x["q_idx"], x["q_scale"], x["w"], x["kidx_cache"],
+                                 x["kidx_scale"], x["k_cache"], x["v_cache"], x["block_table"],
+                                 x["seq_lens"], cfg.k, cfg.sm_scale, return_idx=True,
+                                 return_stats=True)
     torch.cuda.synchronize()
-    _say("  decode done", what)
+    _say("  decode done", what, "candidate-path counters", stats)
+    if stats is not None:                              # on the candidate path: no row redone
+        assert stats == [1, 0]
     c = _compact_sequences(x, seqs, cfg.block)
     s_t = torch.tensor(seqs)
     # oracle indexer scores (for the band) on the compacted caches
@@ -542,8 +584,10 @@ def test_decode_candidate_path_equals_full_rows():
                               return_idx=True)
     wide = torch.full((cfg.B, 1024), -1, dtype=torch.int32, device=DEV)
     wide[:, :640] = x["block_table"]
-    out_b, idx_b = dsa.decode(*args, wide, x["seq_lens"], cfg.k, cfg.sm_scale, return_idx=True)
+    out_b, idx_b, stats = dsa.decode(*args, wide, x["seq_lens"], cfg.k, cfg.sm_scale,
+                                     return_idx=True, return_stats=True)
     torch.cuda.synchronize()
+    assert stats == [1, 0]
     assert torch.equal(idx_a, idx_b)
     assert torch.equal(out_a, out_b)
 
@@ -555,10 +599,12 @@ def test_decode_ties_take_the_exact_fallback():
     x = W.decode_inputs(cfg, DEV, lens=torch.tensor([50000, 9000, 70000]))
     x["kidx_cache"] = x["kidx_cache"][:1, :1].expand_as(x["kidx_cache"]).contiguous()
     x["kidx_scale"] = x["kidx_scale"][:1, :1].expand_as(x["kidx_scale"]).contiguous()
-    out, idx = dsa.decode(x["q"], x["q_idx"], x["q_scale"], x["w"], x["kidx_cache"], x["kidx_scale"],
-                          x["k_cache"], x["v_cache"], x["block_table"], x["seq_lens"], cfg.k,
-                          cfg.sm_scale, return_idx=True)
+    out, idx, stats = dsa.decode(x["q"], x["q_idx"], x["q_scale"], x["w"], x["kidx_cache"],
+                                 x["kidx_scale"], x["k_cache"], x["v_cache"], x["block_table"],
+                                 x["seq_lens"], cfg.k, cfg.sm_scale, return_idx=True,
+                                 return_stats=True)
     torch.cuda.synchronize()
+    assert stats[0] == 1 and stats[1] == cfg.B      # every sequence overflowed its list
     assert np.array_equal(to_np(idx), np.tile(np.arange(cfg.k, dtype=np.int32), (cfg.B, 1)))
 
 
