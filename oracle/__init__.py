@@ -59,6 +59,8 @@ def _load():
             lib.oracle_decode.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I,
                                           I, D, P, I, P, P, P]
             lib.oracle_decode.restype = None
+            lib.oracle_quantize_e4m3.argtypes = [P, I, I, I, P, P]
+            lib.oracle_quantize_e4m3.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = I
             _lib = lib
@@ -203,3 +205,17 @@ def decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, dtype
                       _ptr(seq_lens), block_table.shape[1], int(block_size), HI, dI, Hq, G, d,
                       int(k), float(sm_scale), _ptr(seqs), n, _ptr(idx), _ptr(kth), _ptr(out))
     return idx, kth, out
+
+
+def quantize_e4m3(x, x_dtype=F32):
+    """Per-token E4M3 codes and scales of x [T, ...] (F32 or BF16 input).
+
+    Returns (codes uint8 of x's shape, scale float32 [T])."""
+    lib = _load()
+    x = _np(x, np.float32 if x_dtype == F32 else np.uint16)
+    T = x.shape[0]
+    n = int(np.prod(x.shape[1:])) if x.ndim > 1 else 1
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scale = np.empty(T, dtype=np.float32)
+    lib.oracle_quantize_e4m3(_ptr(x), x_dtype, T, n, _ptr(codes), _ptr(scale))
+    return codes, scale

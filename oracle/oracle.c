@@ -342,6 +342,54 @@ void oracle_decode(const void* q, const uint8_t* q_idx, const float* q_scale, co
     }
 }
 
+/* ------------------------------------------------------- FP8 quantisation */
+
+/* The indexer runs on FP8 inputs (Keye-VL-2.0 report, section 2.3.1; the
+ * xllm-io review credits FP8 for the indexer's efficiency).  The pages give no
+ * recipe; the reading used throughout is per-token absmax scaling into OCP
+ * E4M3: scale = amax / 448 over the token's values (1 when amax = 0), each
+ * value divided by the scale in fp32, clamped to [-448, 448], and rounded to
+ * the nearest E4M3 value with ties to the even code.  The rounding here is the
+ * plain definition: the nearest of the 127 non-negative finite E4M3 values by
+ * exhaustive search. */
+static uint8_t e4m3_nearest(float v)
+{
+    const int neg = signbit(v) != 0;
+    const double a = fabs((double)v);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c < 127; ++c) {                    /* 0x00 .. 0x7E, ascending values */
+        const double d = fabs(oracle_e4m3_to_double((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) { best = c; best_d = d; }
+    }
+    return (uint8_t)(best | (neg ? 0x80 : 0));
+}
+
+void oracle_quantize_e4m3(const void* x, int x_dtype, int T, int n, uint8_t* codes, float* scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        float amax = 0.f;
+        for (int i = 0; i < n; ++i) {
+            const int64_t o = (int64_t)t * n + i;
+            const float v = x_dtype == ORACLE_BF16 ? (float)bf16_to_double(((const uint16_t*)x)[o])
+                                                   : ((const float*)x)[o];
+            if (fabsf(v) > amax) amax = fabsf(v);
+        }
+        const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+        scale[t] = s;
+        for (int i = 0; i < n; ++i) {
+            const int64_t o = (int64_t)t * n + i;
+            const float v = x_dtype == ORACLE_BF16 ? (float)bf16_to_double(((const uint16_t*)x)[o])
+                                                   : ((const float*)x)[o];
+            float y = v / s;
+            if (y > 448.0f) y = 448.0f;
+            if (y < -448.0f) y = -448.0f;
+            codes[o] = e4m3_nearest(y);
+        }
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -54,6 +54,11 @@ void oracle_decode(const void* q, const uint8_t* q_idx, const float* q_scale, co
                    int k, double sm_scale, const int32_t* seqs, int nseqs,
                    int32_t* idx_out, double* kth_out, double* out);
 
+/* Per-token E4M3 quantisation of x [T, n] (ORACLE_F32 or ORACLE_BF16): codes [T, n],
+ * scale [T] = amax / 448 (1 for an all-zero row); codes = nearest E4M3 of clamp(x / scale),
+ * ties to the even code. */
+void oracle_quantize_e4m3(const void* x, int x_dtype, int T, int n, uint8_t* codes, float* scale);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

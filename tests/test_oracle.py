@@ -401,3 +401,58 @@ def test_decode_equals_prefill_row_through_block_table():
         assert np.array_equal(i2[0], idx[t])
         assert kth2[0] == kth[t]
         assert np.allclose(o2[0], out[t], atol=1e-13)
+
+
+# ------------------------------------------------------------ FP8 quantisation
+
+def _quant_torch(x):
+    """Per-token absmax E4M3 quantisation with torch's own float8 cast (the harness recipe)."""
+    return quantize_e4m3_per_token(torch.as_tensor(x))
+
+
+def test_quantize_matches_torch_float8_cast():
+    """The oracle's exhaustive-search rounding against torch's float8_e4m3fn conversion, on
+    normal rows, heavy-tailed rows, rows of tiny values (subnormal codes) and an all-zero row."""
+    g = np.random.default_rng(11)
+    rows = [g.standard_normal(512), g.standard_cauchy(512), g.standard_normal(512) * 1e-6,
+            np.zeros(512), np.concatenate([[448.0], g.uniform(-448, 448, 511)])]
+    x = np.stack(rows).astype(np.float32)
+    codes, scale = oracle.quantize_e4m3(x)
+    tc, ts = _quant_torch(x)
+    assert np.array_equal(scale, ts.numpy())
+    assert np.array_equal(codes, tc.numpy())
+    assert scale[3] == 1.0 and np.all(codes[3] == 0)
+
+
+def test_quantize_rounds_ties_to_even_codes():
+    """Hand-worked row with scale exactly 1 (the row's absmax is 448): exact E4M3 values keep
+    their codes, and values half way between two codes go to the even code."""
+    vals = [448.0, 0.5, 1.5, 3.25, -2.0,
+            1.0625,      # between 1.0 (0x38) and 1.125 (0x39): even -> 0x38
+            1.1875,      # between 1.125 (0x39) and 1.25 (0x3A): even -> 0x3A
+            1.5 * 2 ** -9,   # between codes 1 and 2 (subnormals): even -> 0x02
+            7.5 * 2 ** -9,   # between the largest subnormal 0x07 and 2^-6 (0x08): -> 0x08
+            432.0]       # between 416 (0x7D) and 448 (0x7E): even -> 0x7E
+    want = [0x7E, 0x30, 0x3C, 0x45, 0xC0, 0x38, 0x3A, 0x02, 0x08, 0x7E]
+    codes, scale = oracle.quantize_e4m3(np.array([vals], dtype=np.float32))
+    assert scale[0] == 1.0
+    assert codes[0].tolist() == want
+
+
+def test_quantize_decode_roundtrip_is_identity():
+    """Every finite code decoded (scale 1: the row holds 448) quantises back to itself."""
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    vals = np.array([[oracle.e4m3_to_double(c) for c in finite]], dtype=np.float32)
+    codes, scale = oracle.quantize_e4m3(vals)
+    assert scale[0] == 1.0
+    got = codes[0].tolist()
+    for c, q in zip(finite, got):
+        assert q == c or (c == 0x80 and q == 0x80), (hex(c), hex(q))
+
+
+def test_quantize_bf16_input_matches_float_input():
+    g = np.random.default_rng(12)
+    x = torch.from_numpy(g.standard_normal((4, 256)).astype(np.float32)).to(torch.bfloat16)
+    c1, s1 = oracle.quantize_e4m3(x, oracle.BF16)
+    c2, s2 = oracle.quantize_e4m3(x.float().numpy(), oracle.F32)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
