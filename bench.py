@@ -7,7 +7,9 @@ processed in 8K-query chunks, on seeded synthetic inputs already resident in
 HBM, through the one-call entry point dsa_prefill.  ``value`` is prefill
 tokens per second of that call.  The paged decode step (64 sequences at
 256K, and at lengths drawn from 32K..256K) is timed in a second region and
-reported under ``decode``.
+reported under ``decode``, with the step before it (the new token's indexer
+query quantised to FP8 and its K/V/k^I appended into the paged caches) timed
+alone and together with the decode step.
 
 The same prefill is also run through the separate entry points (indexer over
 full score rows, top-k, attention) with HIP events recorded on the launch
@@ -267,6 +269,35 @@ def run_decode_bench(args, dsa, W, torch, name):
     e1.record(stream)
     torch.cuda.synchronize()
     us_step = e0.elapsed_time(e1) / steps * 1e3
+
+    # the step before decode: the new token's indexer query quantised (one scale per token
+    # over its H^I x d_I values) and its K/V/k^I appended at position len - 1
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed + 1000)
+    qi_f = torch.randn(cfg.B, cfg.HI * cfg.dI, generator=gen, device="cuda").bfloat16()
+    kidx_f = torch.randn(cfg.B, cfg.dI, generator=gen, device="cuda").bfloat16()
+    k_new = torch.randn(cfg.B, cfg.G, cfg.d, generator=gen, device="cuda").bfloat16()
+    v_new = torch.randn(cfg.B, cfg.G, cfg.d, generator=gen, device="cuda").bfloat16()
+    pos = (x["seq_lens"] - 1).contiguous()
+    q_idx_flat = x["q_idx"].view(cfg.B, -1)
+
+    def prep():
+        dsa.dsa_quantize_e4m3(qi_f, dsa.DSA_BF16, cfg.B, cfg.HI * cfg.dI, q_idx_flat, x["q_scale"],
+                              stream)
+        dsa.dsa_cache_append(k_new, v_new, dsa.DSA_BF16, kidx_f, dsa.DSA_BF16, pos,
+                             x["block_table"], cfg.B, x["NB"], x["max_blocks"], cfg.block, cfg.G,
+                             cfg.d, cfg.dI, x["k_cache"], x["v_cache"], x["kidx_cache"],
+                             x["kidx_scale"], stream)
+    timed = {}
+    for what, fn in (("prep", prep), ("serving", lambda: (prep(), step()))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        timed[what] = e0.elapsed_time(e1) / steps * 1e3
     lens = x["seq_lens"].long().cpu()
     # algorithmic bytes: indexer keys (codes + scale) + score write/read + gather + q/out
     key_bytes = int(lens.sum()) * (cfg.dI + 4)
@@ -278,7 +309,9 @@ def run_decode_bench(args, dsa, W, torch, name):
            "us_per_token": round(us_step / cfg.B, 3),
            "mean_len": float(lens.float().mean()), "algorithmic_bytes": total,
            "achieved_GBps": round(total / (us_step * 1e-6) / 1e9, 1),
-           "hbm_frac": round(total / (us_step * 1e-6) / PEAK["hbm"], 4)}
+           "hbm_frac": round(total / (us_step * 1e-6) / PEAK["hbm"], 4),
+           "us_quantize_and_append": round(timed["prep"], 2),
+           "us_per_serving_step": round(timed["serving"], 2)}
     del x, ws
     torch.cuda.empty_cache()
     return res

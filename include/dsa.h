@@ -221,6 +221,45 @@ dsa_status_t dsa_decode(const void* q, const void* q_idx, const float* q_scale, 
                         float sm_scale, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/*
+ * Per-token FP8 quantisation of indexer vectors (the FP8 inputs of report
+ * section 2.3.1's indexer; the pages give no recipe, and this is the reading
+ * every call above assumes): for each row t of x [T, n],
+ *   scale[t] = max_i |x[t, i]| / 448   (1 when the row is all zeros),
+ *   codes[t, i] = the E4M3 code nearest to clamp(x[t, i] / scale[t], -448, 448),
+ *                 ties to the code with an even last bit,
+ * with both divisions in fp32, correctly rounded.  x: fp32 or bf16 [T, n]
+ * (x_dtype DSA_F32 or DSA_BF16, 4-byte aligned); codes uint8 [T, n] (any
+ * alignment); scale float [T].  Rows of q^I [T, HI * dI] are quantised with
+ * n = HI * dI (one scale per query token, the layout dsa_index_scores reads);
+ * rows of k^I with n = dI.  Non-finite inputs are not supported.  No workspace.
+ */
+dsa_status_t dsa_quantize_e4m3(const void* x, dsa_dtype_t x_dtype, int T, int n, uint8_t* codes,
+                               float* scale, hipStream_t stream);
+
+/*
+ * Cache append (report section 5.3 serves decode from paged caches): writes
+ * one new token per sequence b into the caches that dsa_decode reads, at
+ * absolute position positions[b] (device int32 [B]) of sequence b:
+ *   slot = block_table[b, positions[b] / block_size] * block_size
+ *          + positions[b] % block_size
+ *   k_cache[slot] = k_new[b], v_cache[slot] = v_new[b]     (rows of G * d, dtype)
+ *   kidx_cache[slot], kidx_scale[slot] = dsa_quantize_e4m3 of kidx_new[b] (dI values)
+ * k_new / v_new [B, G, d] (dtype DSA_BF16 or DSA_F32; a row of G * d elements
+ * must be a multiple of 16 bytes); kidx_new [B, dI] fp32 or bf16 (kidx_dtype),
+ * 4-byte aligned; caches laid out as for dsa_decode.  A position outside
+ * [0, max_blocks * block_size) or a block-table entry outside [0, num_blocks)
+ * skips that sequence (nothing written).  The caller gives every sequence its
+ * own slot: two sequences writing one slot race.  A decode step after the
+ * append passes seq_lens[b] = positions[b] + 1.  No workspace.
+ */
+dsa_status_t dsa_cache_append(const void* k_new, const void* v_new, dsa_dtype_t dtype,
+                              const void* kidx_new, dsa_dtype_t kidx_dtype,
+                              const int32_t* positions, const int32_t* block_table, int B,
+                              int num_blocks, int max_blocks, int block_size, int G, int d, int dI,
+                              void* k_cache, void* v_cache, uint8_t* kidx_cache,
+                              float* kidx_scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

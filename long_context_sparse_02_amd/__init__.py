@@ -9,7 +9,8 @@ calls raise.
 
 Functions named ``dsa_*`` mirror the C entry points one to one.  ``prefill``
 and ``decode`` are conveniences that allocate outputs and workspace with torch
-and call ``dsa_prefill`` / ``dsa_decode``.
+and call ``dsa_prefill`` / ``dsa_decode``; ``quantize_e4m3`` and ``cache_append``
+do the same for the step before decode.
 """
 from __future__ import annotations
 
@@ -29,7 +30,8 @@ EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_index_scores_workspace_size", "dsa_index_scores",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_gqa_attn_workspace_size",
            "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
-           "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode"]
+           "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
+           "dsa_quantize_e4m3", "dsa_cache_append"]
 
 
 class DSAError(RuntimeError):
@@ -73,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_decode_stats_offset": ([I, I, I, I, I, I], SZ),
             "dsa_decode": ([P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, I, F, P, P,
                             P, SZ, P], I),
+            "dsa_quantize_e4m3": ([P, I, I, I, P, P, P], I),
+            "dsa_cache_append": ([P, P, I, P, I, P, P, I, I, I, I, I, I, I, P, P, P, P, P], I),
         }
         for name in EXPORTS:
             fn = getattr(lib, name)
@@ -291,3 +295,40 @@ def decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, block
     if return_stats:
         res = res + (read_stats(ws, off),)
     return res if len(res) > 1 else res[0]
+
+
+def dsa_quantize_e4m3(x, x_dtype, T, n, codes, scale, stream=None):
+    _check(load_library().dsa_quantize_e4m3(_ptr(x), x_dtype, T, n, _ptr(codes), _ptr(scale),
+                                            _stream(stream)))
+
+
+def dsa_cache_append(k_new, v_new, dtype, kidx_new, kidx_dtype, positions, block_table, B,
+                     num_blocks, max_blocks, block_size, G, d, dI, k_cache, v_cache, kidx_cache,
+                     kidx_scale, stream=None):
+    _check(load_library().dsa_cache_append(
+        _ptr(k_new), _ptr(v_new), dtype, _ptr(kidx_new), kidx_dtype, _ptr(positions),
+        _ptr(block_table), B, num_blocks, max_blocks, block_size, G, d, dI, _ptr(k_cache),
+        _ptr(v_cache), _ptr(kidx_cache), _ptr(kidx_scale), _stream(stream)))
+
+
+def quantize_e4m3(x, stream=None):
+    """Per-row E4M3 quantisation of x [..., n] (fp32 or bf16): returns (codes uint8 [..., n],
+    scale float32 [...]), one scale per row of the last dimension."""
+    import torch
+    n = x.shape[-1]
+    T = x.numel() // n if n else 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    dsa_quantize_e4m3(x, dtype_code(x), T, n, codes, scale, stream)
+    return codes, scale
+
+
+def cache_append(k_new, v_new, kidx_new, positions, block_table, k_cache, v_cache, kidx_cache,
+                 kidx_scale, stream=None):
+    """Write one token per sequence (k_new / v_new [B, G, d], kidx_new [B, dI]) into the paged
+    caches in place, at positions [B] (int32, device) through block_table [B, max_blocks]."""
+    B, G, d = k_new.shape
+    NB, bs = k_cache.shape[:2]
+    dsa_cache_append(k_new, v_new, dtype_code(k_new), kidx_new, dtype_code(kidx_new), positions,
+                     block_table, B, NB, block_table.shape[1], bs, G, d, kidx_new.shape[-1],
+                     k_cache, v_cache, kidx_cache, kidx_scale, stream)

@@ -506,3 +506,49 @@ DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float
                     nullptr, seq_lens, idx_c, B, topk, Hq, G, d, sm_scale, out, partials,
                     plan.part_bytes, stream);
 }
+
+DSA_EXPORT dsa_status_t dsa_quantize_e4m3(const void* x, dsa_dtype_t x_dtype, int T, int n,
+                                          uint8_t* codes, float* scale, hipStream_t stream) {
+    g_err[0] = 0;
+    REQUIRE(T >= 0 && n >= 1, DSA_ERR_INVALID_ARG, "bad size (T=%d, n=%d)", T, n);
+    REQUIRE(x_dtype == DSA_F32 || x_dtype == DSA_BF16, DSA_ERR_UNSUPPORTED,
+            "quantisation input must be F32 or BF16 (got %d)", (int)x_dtype);
+    if (T == 0) return DSA_OK;
+    REQUIRE_PTR4(x); REQUIRE_PTR4(scale);
+    REQUIRE(codes != nullptr, DSA_ERR_INVALID_ARG, "codes is NULL");
+    const hipError_t e = dsa::launch_quantize_e4m3(x, x_dtype == DSA_BF16, T, n, codes, scale, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "quantisation launch");
+}
+
+DSA_EXPORT dsa_status_t dsa_cache_append(const void* k_new, const void* v_new, dsa_dtype_t dtype,
+                                         const void* kidx_new, dsa_dtype_t kidx_dtype,
+                                         const int32_t* positions, const int32_t* block_table,
+                                         int B, int num_blocks, int max_blocks, int block_size,
+                                         int G, int d, int dI, void* k_cache, void* v_cache,
+                                         uint8_t* kidx_cache, float* kidx_scale,
+                                         hipStream_t stream) {
+    g_err[0] = 0;
+    REQUIRE(B >= 0 && num_blocks >= 0 && max_blocks >= 1 && block_size >= 1, DSA_ERR_INVALID_ARG,
+            "bad size (B=%d, num_blocks=%d, max_blocks=%d, block_size=%d)", B, num_blocks,
+            max_blocks, block_size);
+    REQUIRE(dtype == DSA_BF16 || dtype == DSA_F32, DSA_ERR_UNSUPPORTED,
+            "K/V dtype must be BF16 or F32 (got %d)", (int)dtype);
+    REQUIRE(kidx_dtype == DSA_F32 || kidx_dtype == DSA_BF16, DSA_ERR_UNSUPPORTED,
+            "indexer key input must be F32 or BF16 (got %d)", (int)kidx_dtype);
+    REQUIRE(G >= 1 && d >= 1 && dI >= 1, DSA_ERR_INVALID_ARG, "bad head sizes (G=%d, d=%d, dI=%d)",
+            G, d, dI);
+    const int64_t row_bytes = (int64_t)G * d * (dtype == DSA_BF16 ? 2 : 4);
+    REQUIRE(row_bytes % 16 == 0 && row_bytes <= INT32_MAX, DSA_ERR_UNSUPPORTED,
+            "a K/V row (G * d elements) must be a multiple of 16 bytes");
+    REQUIRE((int64_t)max_blocks * block_size <= INT32_MAX, DSA_ERR_UNSUPPORTED,
+            "max_blocks * block_size too large");
+    if (B == 0) return DSA_OK;
+    REQUIRE_PTR(k_new); REQUIRE_PTR(v_new); REQUIRE_PTR4(kidx_new); REQUIRE_PTR4(positions);
+    REQUIRE_PTR4(block_table); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
+    REQUIRE_PTR4(kidx_scale);
+    REQUIRE(kidx_cache != nullptr, DSA_ERR_INVALID_ARG, "kidx_cache is NULL");
+    const hipError_t e = dsa::launch_cache_append(
+        k_new, v_new, (int)row_bytes, kidx_new, kidx_dtype == DSA_BF16, dI, positions, block_table,
+        B, num_blocks, max_blocks, block_size, k_cache, v_cache, kidx_cache, kidx_scale, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "cache append launch");
+}

@@ -99,4 +99,16 @@ int attn_num_splits(int Tq, int topk);
 size_t attn_partials_bytes(int Tq, int nsplit, int Hq, int d);
 hipError_t launch_sparse_attn(const AttnArgs& a, int nsplit, float* partials, hipStream_t stream);
 
+// Per-token E4M3 quantisation of x [T, n] (fp32, or bf16 when x_bf16): codes [T, n], scale [T].
+hipError_t launch_quantize_e4m3(const void* x, int x_bf16, int T, int n, uint8_t* codes,
+                                float* scale, hipStream_t stream);
+// Append one token per sequence into the paged caches (rows of kv_row_bytes, a multiple of
+// 16; kidx_new fp32 or bf16 [B, dI], quantised on the way in).
+hipError_t launch_cache_append(const void* k_new, const void* v_new, int kv_row_bytes,
+                               const void* kidx_new, int kidx_bf16, int dI,
+                               const int32_t* positions, const int32_t* block_table, int B,
+                               int num_blocks, int max_blocks, int block_size, void* k_cache,
+                               void* v_cache, uint8_t* kidx_cache, float* kidx_scale,
+                               hipStream_t stream);
+
 }  // namespace dsa

@@ -27,7 +27,7 @@ def lib():
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -147,3 +147,31 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         dsa._ptr(x)
+
+
+def test_quantize_and_cache_append_argument_checks(lib):
+    q = lib.dsa_quantize_e4m3
+    assert q(A, dsa.DSA_F32, 0, 128, None, None, None) == 0           # nothing to do
+    assert q(A, dsa.DSA_FP8_E4M3, 4, 128, A, A, None) == 2             # input must be f32/bf16
+    assert q(None, dsa.DSA_F32, 4, 128, A, A, None) == 1 and b"x" in lib.dsa_last_error()
+    assert q(A, dsa.DSA_BF16, 4, 128, A, 0x10002, None) == 1           # scale misaligned
+    assert q(A, dsa.DSA_F32, -1, 128, A, A, None) == 1
+    assert q(A, dsa.DSA_F32, 4, 0, A, A, None) == 1
+    c = lib.dsa_cache_append
+    ok = [A, A, dsa.DSA_BF16, A, dsa.DSA_F32, A, A, 8, 100, 64, 64, 4, 128, 128, A, A, A, A, None]
+    bad = list(ok); bad[7] = 0
+    assert c(*bad) == 0                                                # B = 0: nothing queued
+    bad = list(ok); bad[0] = MIS
+    assert c(*bad) == 1 and b"k_new" in lib.dsa_last_error()
+    bad = list(ok); bad[2] = dsa.DSA_FP8_E4M3
+    assert c(*bad) == 2
+    bad = list(ok); bad[4] = dsa.DSA_FP8_E4M3
+    assert c(*bad) == 2
+    bad = list(ok); bad[11], bad[12] = 1, 4                            # 8-byte K/V rows
+    assert c(*bad) == 2 and b"16 bytes" in lib.dsa_last_error()
+    bad = list(ok); bad[5] = None
+    assert c(*bad) == 1 and b"positions" in lib.dsa_last_error()
+    bad = list(ok); bad[16] = None
+    assert c(*bad) == 1 and b"kidx_cache" in lib.dsa_last_error()
+    bad = list(ok); bad[10] = 0
+    assert c(*bad) == 1

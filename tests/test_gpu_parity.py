@@ -623,3 +623,126 @@ def test_decode_full_size_sampled(name):
     x = W.decode_inputs(cfg, DEV)
     seqs = [0, 17, 63]
     _decode_and_check(cfg, x, seqs, name)
+
+
+# ------------------------------------------------ quantisation and cache append
+
+def _quant_rows(T, n, seed):
+    """Rows over many decades, plus rows with exact rounding ties, zeros and tiny values."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, n, generator=g) * torch.exp(torch.randn(T, 1, generator=g) * 4)
+    x[0] = 0.0                                          # all zero: scale 1, every code 0
+    if T > 1:
+        x[1] = -0.0
+    if T > 2 and n >= 8:
+        # amax 448 gives scale 1 exactly, so these land on E4M3 midpoints: 17 between 16
+        # and 18, 2^-10 between 0 and 2^-9, 3 * 2^-10 between 2^-9 and 2^-8, 1.0625 between
+        # 1 and 1.125, 216 between 208 and 224 -- ties go to the even code
+        x[2, :8] = torch.tensor([448.0, 17.0, -17.0, 2.0 ** -10, 3 * 2.0 ** -10,
+                                 -3 * 2.0 ** -10, 1.0625, 216.0])
+        x[2, 8:] = 0.25
+    if T > 3:
+        x[3] = 1e-30 * torch.randn(n, generator=g)      # scale far below 1
+    return x
+
+
+@pytest.mark.parametrize("T,n", [(1, 1), (7, 300), (1000, 128), (33, 64 * 128)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_quantize_e4m3_bit_exact_vs_oracle(T, n, dt):
+    x = _quant_rows(T, n, seed=T * 7 + n)
+    if dt == "bf16":
+        x = x.bfloat16()
+    codes, scale = dsa.quantize_e4m3(x.to(DEV))
+    torch.cuda.synchronize()
+    ref_c, ref_s = oracle.quantize_e4m3(x, oracle.BF16 if dt == "bf16" else oracle.F32)
+    assert np.array_equal(to_np(scale).view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(to_np(codes), ref_c)
+    if dt == "f32":                                    # the inputs' own quantiser agrees
+        wc, ws = W.quantize_e4m3_per_token(x)
+        assert np.array_equal(to_np(codes), to_np(wc)) and torch.equal(scale.cpu(), ws)
+
+
+def test_quantize_e4m3_query_layout_and_empty():
+    """q^I [T, H^I, d_I] takes one scale per token (n = H^I * d_I); T = 0 is a no-op."""
+    qi = torch.randn(5, 64, 128, generator=torch.Generator().manual_seed(3))
+    codes, scale = dsa.quantize_e4m3(qi.reshape(5, -1).to(DEV))
+    torch.cuda.synchronize()
+    ref_c, ref_s = oracle.quantize_e4m3(qi)
+    assert np.array_equal(to_np(codes).reshape(5, 64, 128), ref_c)
+    assert np.array_equal(to_np(scale), ref_s)
+    c0, s0 = dsa.quantize_e4m3(torch.empty(0, 128, device=DEV))
+    assert c0.shape == (0, 128) and s0.shape == (0,)
+
+
+def _append_case(dt, seed):
+    """Caches of 56 blocks of 64 tokens, 6 sequences of up to 8 blocks each."""
+    g = torch.Generator().manual_seed(seed)
+    el = torch.bfloat16 if dt == "bf16" else torch.float32
+    NB, bs, G, d, dI, B, MB = 56, 64, 4, 128, 128, 6, 8
+    perm = torch.randperm(NB, generator=g).to(torch.int32)
+    table = perm[:B * MB].view(B, MB).clone()
+    table[4, 3:] = -1                                   # unallocated tail
+    pos = torch.tensor([0, 63, 64, 511, 3 * 64 + 5, 200], dtype=torch.int32)
+    c = {"k_cache": torch.randn(NB, bs, G, d, generator=g).to(el),
+         "v_cache": torch.randn(NB, bs, G, d, generator=g).to(el),
+         "kidx_cache": torch.randint(0, 255, (NB, bs, dI), generator=g, dtype=torch.uint8),
+         "kidx_scale": torch.rand(NB, bs, generator=g)}
+    new = {"k": torch.randn(B, G, d, generator=g).to(el), "v": torch.randn(B, G, d, generator=g).to(el),
+           "kidx": torch.randn(B, dI, generator=g) * 3}
+    return c, new, table, pos
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_cache_append_bit_exact(dt):
+    c, new, table, pos = _append_case(dt, seed=11 if dt == "bf16" else 12)
+    pos[5] = 8 * 64                                     # beyond max_blocks * block_size: skipped
+    bs = 64
+    ref = {k: v.clone() for k, v in c.items()}
+    codes, scale = oracle.quantize_e4m3(new["kidx"])
+    written = 0
+    for b in range(len(pos)):
+        p = int(pos[b])
+        if not 0 <= p < table.shape[1] * bs or table[b, p // bs] < 0:
+            continue
+        blk, off = int(table[b, p // bs]), p % bs
+        ref["k_cache"][blk, off] = new["k"][b]
+        ref["v_cache"][blk, off] = new["v"][b]
+        ref["kidx_cache"][blk, off] = torch.from_numpy(codes[b])
+        ref["kidx_scale"][blk, off] = float(scale[b])
+        written += 1
+    assert written == 4                                 # sequence 4's block is unallocated
+    g = {k: v.to(DEV) for k, v in c.items()}
+    dsa.cache_append(new["k"].to(DEV), new["v"].to(DEV), new["kidx"].to(DEV), pos.to(DEV),
+                     table.to(DEV), g["k_cache"], g["v_cache"], g["kidx_cache"], g["kidx_scale"])
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(g[k].cpu(), ref[k]), k
+
+
+def test_append_then_decode_serving_step():
+    """A decode step from float inputs: q^I quantised on the GPU, the new token appended
+    into the caches, then the decode step; checked against the oracle on the results."""
+    cfg = W.scaled(W.DECODE_PAGED, B=5, Lmin=100, Lmax=70000, k=2048, seed=94)
+    lens = torch.tensor([100, 4097, 30001, 65535, 70000])
+    x = W.decode_inputs(cfg, DEV, lens=lens)
+    g = torch.Generator(device=DEV).manual_seed(5)
+    qi = torch.randn(cfg.B, cfg.HI, cfg.dI, generator=g, device=DEV)
+    kf = torch.randn(cfg.B, cfg.dI, generator=g, device=DEV).bfloat16()
+    k_new = torch.randn(cfg.B, cfg.G, cfg.d, generator=g, device=DEV).bfloat16() * 0.1
+    v_new = torch.randn(cfg.B, cfg.G, cfg.d, generator=g, device=DEV).bfloat16()
+    pos = (x["seq_lens"] - 1).contiguous()              # the query token itself is the new one
+    x["q_idx"], x["q_scale"] = dsa.quantize_e4m3(qi.view(cfg.B, -1))
+    x["q_idx"] = x["q_idx"].view(cfg.B, cfg.HI, cfg.dI)
+    dsa.cache_append(k_new, v_new, kf, pos, x["block_table"], x["k_cache"], x["v_cache"],
+                     x["kidx_cache"], x["kidx_scale"])
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_e4m3(qi.cpu())
+    assert np.array_equal(to_np(x["q_idx"]), rc) and np.array_equal(to_np(x["q_scale"]), rs)
+    kc, ks = oracle.quantize_e4m3(kf.cpu(), oracle.BF16)
+    bt = x["block_table"].cpu()
+    for b in range(cfg.B):
+        p = int(pos[b])
+        blk = int(bt[b, p // cfg.block])
+        assert np.array_equal(to_np(x["kidx_cache"][blk, p % cfg.block]), kc[b])
+        assert torch.equal(x["k_cache"][blk, p % cfg.block], k_new[b])
+    _decode_and_check(cfg, x, list(range(cfg.B)), "append + decode")
