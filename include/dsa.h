@@ -187,6 +187,33 @@ dsa_status_t dsa_prefill(const void* q, const void* k, const void* v, dsa_dtype_
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Packed variable-length prefill (report section 5.1.2: DSA for batches of
+ * sequences of different lengths): nseq sequences packed along the token
+ * dimension, sequence i holding tokens cu_seqlens[i] .. cu_seqlens[i+1] - 1 of
+ * every per-token array.  Each sequence is an independent causal prefill: its
+ * rows see only its own keys, scores exist only over its own prefix, and the
+ * top-k runs only over that region, so every sequence's results are those of
+ * dsa_prefill on it alone (q_pos0 = 0), bit for bit.
+ *
+ * cu_seqlens: int32 [nseq + 1] in HOST memory, cu_seqlens[0] = 0, non-decreasing;
+ *   empty sequences are allowed.  T = cu_seqlens[nseq] tokens in total.
+ * q, k, v, q_idx, q_scale, w, k_idx, k_scale, out: as for dsa_prefill with T rows.
+ * idx_out (nullable) int32 [T, topk]: Omega of each row as positions LOCAL to its
+ *   sequence (0-based; add cu_seqlens[i] for rows of the packed arrays), -1 padded.
+ * chunk_rows: query rows per chunk within each sequence (0 = whole sequence).
+ * Workspace: dsa_prefill_workspace_size(max_len, 0, chunk_rows, topk) bytes, max_len
+ *   being the longest sequence; the candidate-path counters of the whole call are at
+ *   dsa_prefill_stats_offset(max_len, 0, chunk_rows, topk).  The sequences run one
+ *   after another on `stream`, sharing the workspace.
+ */
+dsa_status_t dsa_prefill_varlen(const void* q, const void* k, const void* v, dsa_dtype_t dtype,
+                                const void* q_idx, const float* q_scale, const float* w,
+                                const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype,
+                                const int32_t* cu_seqlens, int nseq, int Hq, int G, int d, int HI,
+                                int dI, int topk, float sm_scale, int chunk_rows, void* out,
+                                int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Paged decode step (report section 5.3): one new query per sequence b, at
  * position seq_lens[b] - 1, whose own K/V/k^I entries are already in the
  * caches.  Runs the FP8 indexer over the sequence's paged indexer keys, the

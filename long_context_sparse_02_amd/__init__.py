@@ -30,7 +30,7 @@ EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_index_scores_workspace_size", "dsa_index_scores",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_gqa_attn_workspace_size",
            "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
-           "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
+           "dsa_prefill", "dsa_prefill_varlen", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
            "dsa_quantize_e4m3", "dsa_cache_append"]
 
 
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_prefill_stats_offset": ([I, I64, I, I], SZ),
             "dsa_prefill": ([P, P, P, I, P, P, P, P, P, I, I, I64, I, I, I, I, I, I, F, I, P, P, P,
                              SZ, P], I),
+            "dsa_prefill_varlen": ([P, P, P, I, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P,
+                                    P, P, SZ, P], I),
             "dsa_decode_workspace_size": ([I, I, I, I, I, I], SZ),
             "dsa_decode_stats_offset": ([I, I, I, I, I, I], SZ),
             "dsa_decode": ([P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, I, F, P, P,
@@ -332,3 +334,44 @@ def cache_append(k_new, v_new, kidx_new, positions, block_table, k_cache, v_cach
     dsa_cache_append(k_new, v_new, dtype_code(k_new), kidx_new, dtype_code(kidx_new), positions,
                      block_table, B, NB, block_table.shape[1], bs, G, d, kidx_new.shape[-1],
                      k_cache, v_cache, kidx_cache, kidx_scale, stream)
+
+
+def dsa_prefill_varlen(q, k, v, dtype, q_idx, q_scale, w, k_idx, k_scale, idx_dtype, cu_seqlens,
+                       nseq, Hq, G, d, HI, dI, topk, sm_scale, chunk_rows, out, idx_out=None,
+                       ws=None, ws_bytes=0, stream=None):
+    """cu_seqlens: a host sequence of nseq + 1 ints (list, numpy array or CPU tensor)."""
+    cu = (ctypes.c_int32 * (nseq + 1))(*[int(c) for c in list(cu_seqlens)[:nseq + 1]])
+    _check(load_library().dsa_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), dtype, _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx),
+        _ptr(k_scale), idx_dtype, ctypes.cast(cu, ctypes.c_void_p), nseq, Hq, G, d, HI, dI, topk,
+        float(sm_scale), chunk_rows, _ptr(out), _ptr(idx_out), _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def prefill_varlen(q, k, v, q_idx, q_scale, w, k_idx, k_scale, cu_seqlens, topk, sm_scale,
+                   chunk_rows=0, return_idx=False, ws=None, stream=None, return_stats=False):
+    """Packed variable-length prefill: sequence i is tokens cu_seqlens[i] .. cu_seqlens[i+1]-1
+    of every array.  Returns out (and idx with positions local to each sequence, and the
+    candidate-path counters, as for ``prefill``)."""
+    import torch
+    cu = [int(c) for c in list(cu_seqlens)]
+    nseq = len(cu) - 1
+    T, Hq, d = q.shape
+    G = k.shape[1]
+    _, HI, dI = q_idx.shape
+    out = torch.empty_like(q)
+    idx = torch.empty(T, topk, dtype=torch.int32, device=q.device) if return_idx else None
+    max_len = max([b - a for a, b in zip(cu[:-1], cu[1:])] + [0])
+    n = dsa_prefill_workspace_size(max_len, 0, chunk_rows, topk) if max_len > 0 else 0
+    if ws is None or ws.numel() < n:
+        ws = workspace(max(n, 256), q.device)
+    off = dsa_prefill_stats_offset(max_len, 0, chunk_rows, topk) if return_stats and max_len else -1
+    if return_stats:
+        _zero_stats(ws, off)
+    dsa_prefill_varlen(q, k, v, dtype_code(q), q_idx, q_scale, w, k_idx, k_scale,
+                       dtype_code(q_idx), cu, nseq, Hq, G, d, HI, dI, topk, sm_scale, chunk_rows,
+                       out, idx, ws, ws.numel(), stream)
+    res = (out, idx) if return_idx else (out,)
+    if return_stats:
+        res = res + (read_stats(ws, off) if off >= 0 else [0, 0],)
+    return res if len(res) > 1 else res[0]

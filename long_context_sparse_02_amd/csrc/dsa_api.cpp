@@ -4,6 +4,7 @@
 // stream with no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -241,20 +242,23 @@ struct PrefillPlan {
     int chunk;
     int64_t Tk;
     int64_t ld;
-    int S;                                     // samples per row of the largest chunk
+    int S;                                     // samples per row: the most any chunk takes
     size_t scores_bytes, idx_bytes, index_bytes;
     size_t samples_bytes, tau_bytes, cnt_bytes, cand_bytes, flag_bytes, total;
 };
 
 // The workspace holds one chunk's scores, its index sets and the indexer's scratch (sized for
 // FP8, the larger of the two indexer paths), plus the candidate pipeline's buffers: samples,
-// per-row bounds and counters, candidate lists and the fallback flag.
+// per-row bounds and counters, candidate lists and the fallback flag.  A chunk's sample count
+// grows with the keys it sees until the candidate path ends (fused_sample_count < 0), so the
+// sample buffer is sized for the longest prefix that still takes the path.
 PrefillPlan plan_prefill(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
     PrefillPlan p;
     p.chunk = (chunk_rows <= 0 || chunk_rows > Tq) ? Tq : chunk_rows;
     p.Tk = q_pos0 + Tq;
     p.ld = ld_for(p.Tk);
-    p.S = p.Tk <= INT32_MAX ? dsa::fused_sample_count((int)p.Tk) : -1;
+    const int64_t last_cand_tk = 64LL * dsa::kCandCap - 1;
+    p.S = dsa::fused_sample_count((int)std::min<int64_t>(p.Tk, last_cand_tk));
     const int S = p.S > 0 ? p.S : 0;
     p.scores_bytes = round_up((size_t)p.chunk * p.ld * sizeof(float));
     p.idx_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
@@ -267,6 +271,108 @@ PrefillPlan plan_prefill(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
     p.total = p.scores_bytes + p.idx_bytes + p.index_bytes + p.samples_bytes + p.tau_bytes +
               p.cnt_bytes + p.cand_bytes + p.flag_bytes;
     return p;
+}
+
+struct PrefillBuffers {
+    float* scores; int32_t* idx_ws; void* index_ws; float* samples; float* tau; int32_t* cnt;
+    uint2* cand; int* fallback;
+    int chunk; int S;                          // capacities: rows per chunk, samples per row
+};
+
+PrefillBuffers carve_prefill(void* ws, const PrefillPlan& plan) {
+    PrefillBuffers b;
+    char* wp = static_cast<char*>(ws);
+    b.scores = reinterpret_cast<float*>(wp);                         wp += plan.scores_bytes;
+    b.idx_ws = reinterpret_cast<int32_t*>(wp);                       wp += plan.idx_bytes;
+    b.index_ws = wp;                                                 wp += plan.index_bytes;
+    b.samples = reinterpret_cast<float*>(wp);                        wp += plan.samples_bytes;
+    b.tau = reinterpret_cast<float*>(wp);                            wp += plan.tau_bytes;
+    b.cnt = reinterpret_cast<int32_t*>(wp);                          wp += plan.cnt_bytes;
+    b.cand = reinterpret_cast<uint2*>(wp);                           wp += plan.cand_bytes;
+    b.fallback = reinterpret_cast<int*>(wp);
+    b.chunk = plan.chunk;
+    b.S = plan.S > 0 ? plan.S : 0;
+    return b;
+}
+
+struct PrefillArgs {
+    const void* q; const void* k; const void* v; dsa_dtype_t dtype;
+    const void* q_idx; const float* q_scale; const float* w; const void* k_idx;
+    const float* k_scale; dsa_dtype_t idx_dtype;
+    int Hq, G, d, HI, dI, topk; float sm_scale;
+    void* out; int32_t* idx_out;
+};
+
+// One sequence's prefill (arguments already checked): query rows q_pos0 .. q_pos0 + Tq - 1,
+// keys 0 .. q_pos0 + Tq - 1, in chunks of at most b.chunk rows.  `first_cand` is true until a
+// chunk of the call has taken the candidate path (the first one clears the counters).
+dsa_status_t run_prefill(const PrefillArgs& a, int Tq, int64_t q_pos0, const PrefillBuffers& b,
+                         bool& first_cand, hipStream_t stream) {
+    const size_t qrow = (size_t)a.Hq * a.d * (a.dtype == DSA_BF16 ? 2 : 4);
+    const size_t qirow = (size_t)a.HI * a.dI * (a.idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
+    const int topk = a.topk, HI = a.HI;
+    // The candidate pipeline needs the resident FP8 indexer and a bounded candidate list;
+    // other shapes run the indexer and top-k over full score rows.
+    const bool cand_path = a.idx_dtype == DSA_FP8_E4M3 && HI <= 64 && topk <= dsa::kCandCap;
+    const int64_t ld = ld_for(q_pos0 + Tq);
+    for (int r0 = 0; r0 < Tq; r0 += b.chunk) {
+        const int rows = (Tq - r0 < b.chunk) ? Tq - r0 : b.chunk;
+        const int64_t pos0 = q_pos0 + r0;
+        const int tk = (int)(pos0 + rows);                     // keys this chunk can see
+        const void* qi_c = static_cast<const char*>(a.q_idx) + r0 * qirow;
+        const float* qs_c = a.q_scale ? a.q_scale + r0 : nullptr;
+        const float* w_c = a.w + (int64_t)r0 * HI;
+        int32_t* idx_c = a.idx_out ? a.idx_out + (int64_t)r0 * topk : b.idx_ws;
+        // short prefixes: streaming the full score rows costs less than the sample pass and
+        // the per-row select (measured break-even near 40K keys)
+        int S = cand_path && tk >= kCandMinKeys ? dsa::fused_sample_count(tk) : -1;
+        if (S > b.S) S = -1;                                   // (cannot happen: S grows with tk)
+        dsa_status_t st;
+        hipError_t e = hipSuccess;
+        if (tk <= topk) {
+            // every row of the chunk keeps its whole prefix: the top-k writes 0..t without
+            // reading scores, so none are computed
+            e = dsa::launch_topk(b.scores, ld, rows, tk, pos0, nullptr, topk, idx_c, nullptr, stream);
+            if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        } else if (S >= 0) {
+            // sampled bound -> candidates at or above it -> exact select from the candidates;
+            // a row whose candidates cannot give the exact answer raises the fallback flag,
+            // and the two gated launches then redo the chunk over full score rows
+            const auto* qi8 = static_cast<const uint8_t*>(qi_c);
+            const auto* ki8 = static_cast<const uint8_t*>(a.k_idx);
+            e = dsa::launch_index_fp8_sample(qi8, qs_c, w_c, ki8, a.k_scale, rows, tk, HI, pos0,
+                                             b.samples, S, b.index_ws, stream);
+            if (e == hipSuccess)
+                e = dsa::launch_topk_bound(b.samples, S, rows, pos0, nullptr, 0, topk, b.tau, b.cnt,
+                                           b.fallback, first_cand ? 1 : 0, stream);
+            first_cand = false;
+            if (e == hipSuccess)
+                e = dsa::launch_index_fp8_candidates(qi8, qs_c, w_c, ki8, a.k_scale, rows, tk, HI,
+                                                     pos0, b.tau, b.cnt, b.cand, dsa::kCandCap,
+                                                     b.index_ws, stream);
+            if (e == hipSuccess)
+                e = dsa::launch_topk_select(b.cand, b.cnt, rows, pos0, nullptr, 0, topk, idx_c,
+                                            b.fallback, stream);
+            if (e == hipSuccess)
+                e = dsa::launch_index_fp8(qi8, qs_c, w_c, ki8, a.k_scale, rows, tk, HI, pos0,
+                                          b.scores, ld, b.index_ws, stream, b.fallback, true);
+            if (e == hipSuccess)
+                e = dsa::launch_topk(b.scores, ld, rows, tk, pos0, nullptr, topk, idx_c, nullptr,
+                                     stream, b.fallback);
+            if (e != hipSuccess) return hip_fail(e, "prefill selection launch");
+        } else {
+            st = run_indexer(qi_c, qs_c, w_c, a.k_idx, a.k_scale, a.idx_dtype, rows, tk, HI, a.dI,
+                             pos0, b.scores, ld, b.index_ws, stream);
+            if (st != DSA_OK) return st;
+            e = dsa::launch_topk(b.scores, ld, rows, tk, pos0, nullptr, topk, idx_c, nullptr, stream);
+            if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        }
+        st = run_attn(static_cast<const char*>(a.q) + r0 * qrow, a.k, a.v, a.dtype, tk, nullptr, 0,
+                      0, nullptr, nullptr, idx_c, rows, topk, a.Hq, a.G, a.d, a.sm_scale,
+                      static_cast<char*>(a.out) + r0 * qrow, nullptr, 0, stream);
+        if (st != DSA_OK) return st;
+    }
+    return DSA_OK;
 }
 
 }  // namespace
@@ -304,69 +410,69 @@ DSA_EXPORT dsa_status_t dsa_prefill(const void* q, const void* k, const void* v,
     REQUIRE(ws && aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
             "prefill needs %zu workspace bytes (got %zu%s)", plan.total, ws_bytes,
             ws ? "" : ", ws is NULL");
-    char* wp = static_cast<char*>(ws);
-    float* scores = reinterpret_cast<float*>(wp);                    wp += plan.scores_bytes;
-    int32_t* idx_ws = reinterpret_cast<int32_t*>(wp);                wp += plan.idx_bytes;
-    void* index_ws = wp;                                             wp += plan.index_bytes;
-    float* samples = reinterpret_cast<float*>(wp);                   wp += plan.samples_bytes;
-    float* tau = reinterpret_cast<float*>(wp);                       wp += plan.tau_bytes;
-    int32_t* cnt = reinterpret_cast<int32_t*>(wp);                   wp += plan.cnt_bytes;
-    uint2* cand = reinterpret_cast<uint2*>(wp);                      wp += plan.cand_bytes;
-    int* fallback = reinterpret_cast<int*>(wp);
-    const size_t qrow = (size_t)Hq * d * (dtype == DSA_BF16 ? 2 : 4);
-    const size_t qirow = (size_t)HI * dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
-    // The candidate pipeline needs the resident FP8 indexer and a bounded candidate list;
-    // other shapes run the indexer and top-k over full score rows.
-    const bool cand_path = idx_dtype == DSA_FP8_E4M3 && HI <= 64 && topk <= dsa::kCandCap;
+    const PrefillArgs a{q, k, v, dtype, q_idx, q_scale, w, k_idx, k_scale, idx_dtype,
+                        Hq, G, d, HI, dI, topk, sm_scale, out, idx_out};
     bool first_cand = true;
-    for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
-        const int rows = (Tq - r0 < plan.chunk) ? Tq - r0 : plan.chunk;
-        const int64_t pos0 = q_pos0 + r0;
-        const int tk = (int)(pos0 + rows);                     // keys this chunk can see
-        const void* qi_c = static_cast<const char*>(q_idx) + r0 * qirow;
-        const float* qs_c = q_scale ? q_scale + r0 : nullptr;
-        const float* w_c = w + (int64_t)r0 * HI;
-        int32_t* idx_c = idx_out ? idx_out + (int64_t)r0 * topk : idx_ws;
-        // short prefixes: streaming the full score rows costs less than the sample pass and
-        // the per-row select (measured break-even near 40K keys)
-        const int S = cand_path && tk >= kCandMinKeys ? dsa::fused_sample_count(tk) : -1;
-        hipError_t e = hipSuccess;
-        if (S >= 0) {
-            // sampled bound -> candidates at or above it -> exact select from the candidates;
-            // a row whose candidates cannot give the exact answer raises the fallback flag,
-            // and the two gated launches then redo the chunk over full score rows
-            const auto* qi8 = static_cast<const uint8_t*>(qi_c);
-            const auto* ki8 = static_cast<const uint8_t*>(k_idx);
-            e = dsa::launch_index_fp8_sample(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI, pos0,
-                                             samples, S, index_ws, stream);
-            if (e == hipSuccess)
-                e = dsa::launch_topk_bound(samples, S, rows, pos0, nullptr, 0, topk, tau, cnt, fallback,
-                                           first_cand ? 1 : 0, stream);
-            first_cand = false;
-            if (e == hipSuccess)
-                e = dsa::launch_index_fp8_candidates(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI,
-                                                     pos0, tau, cnt, cand, dsa::kCandCap,
-                                                     index_ws, stream);
-            if (e == hipSuccess)
-                e = dsa::launch_topk_select(cand, cnt, rows, pos0, nullptr, 0, topk, idx_c, fallback,
-                                            stream);
-            if (e == hipSuccess)
-                e = dsa::launch_index_fp8(qi8, qs_c, w_c, ki8, k_scale, rows, tk, HI, pos0, scores,
-                                          plan.ld, index_ws, stream, fallback, true);
-            if (e == hipSuccess)
-                e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c, nullptr,
-                                     stream, fallback);
-            if (e != hipSuccess) return hip_fail(e, "prefill selection launch");
-        } else {
-            st = run_indexer(qi_c, qs_c, w_c, k_idx, k_scale, idx_dtype, rows, tk, HI, dI, pos0,
-                             scores, plan.ld, index_ws, stream);
-            if (st != DSA_OK) return st;
-            e = dsa::launch_topk(scores, plan.ld, rows, tk, pos0, nullptr, topk, idx_c, nullptr, stream);
-            if (e != hipSuccess) return hip_fail(e, "top-k launch");
-        }
-        st = run_attn(static_cast<const char*>(q) + r0 * qrow, k, v, dtype, tk, nullptr, 0, 0,
-                      nullptr, nullptr, idx_c, rows, topk, Hq, G, d, sm_scale,
-                      static_cast<char*>(out) + r0 * qrow, nullptr, 0, stream);
+    return run_prefill(a, Tq, q_pos0, carve_prefill(ws, plan), first_cand, stream);
+}
+
+DSA_EXPORT dsa_status_t dsa_prefill_varlen(const void* q, const void* k, const void* v,
+                                           dsa_dtype_t dtype, const void* q_idx,
+                                           const float* q_scale, const float* w,
+                                           const void* k_idx, const float* k_scale,
+                                           dsa_dtype_t idx_dtype, const int32_t* cu_seqlens,
+                                           int nseq, int Hq, int G, int d, int HI, int dI,
+                                           int topk, float sm_scale, int chunk_rows, void* out,
+                                           int32_t* idx_out, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+    g_err[0] = 0;
+    REQUIRE(nseq >= 0, DSA_ERR_INVALID_ARG, "negative number of sequences (%d)", nseq);
+    REQUIRE(cu_seqlens != nullptr, DSA_ERR_INVALID_ARG, "cu_seqlens is NULL");
+    REQUIRE(cu_seqlens[0] == 0, DSA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)",
+            cu_seqlens[0]);
+    int max_len = 0;
+    for (int i = 0; i < nseq; ++i) {
+        const int len = cu_seqlens[i + 1] - cu_seqlens[i];
+        REQUIRE(cu_seqlens[i + 1] >= cu_seqlens[i], DSA_ERR_INVALID_ARG,
+                "cu_seqlens must not decrease (entry %d: %d after %d)", i + 1, cu_seqlens[i + 1],
+                cu_seqlens[i]);
+        if (len > max_len) max_len = len;
+    }
+    const int T = cu_seqlens[nseq];
+    REQUIRE(T <= INT32_MAX - 4, DSA_ERR_UNSUPPORTED, "batch too long");
+    // the longest sequence fixes the shapes every check below needs
+    dsa_status_t st = check_indexer(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, max_len,
+                                    max_len, HI, dI, 0);
+    if (st != DSA_OK) return st;
+    st = check_attn_shape(dtype, Hq, G, d, topk);
+    if (st != DSA_OK) return st;
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(out);
+    REQUIRE_OPT_PTR4(idx_out);
+    if (max_len == 0) return DSA_OK;
+    const PrefillPlan plan = plan_prefill(max_len, 0, chunk_rows, topk);
+    REQUIRE(ws && aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
+            "varlen prefill needs %zu workspace bytes (got %zu%s)", plan.total, ws_bytes,
+            ws ? "" : ", ws is NULL");
+    const PrefillBuffers b = carve_prefill(ws, plan);
+    const size_t qrow = (size_t)Hq * d * (dtype == DSA_BF16 ? 2 : 4);
+    const size_t kvrow = (size_t)G * d * (dtype == DSA_BF16 ? 2 : 4);
+    const size_t qirow = (size_t)HI * dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
+    const size_t kirow = (size_t)dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
+    bool first_cand = true;
+    for (int i = 0; i < nseq; ++i) {
+        const int64_t s0 = cu_seqlens[i];
+        const int len = cu_seqlens[i + 1] - cu_seqlens[i];
+        if (len == 0) continue;
+        const PrefillArgs a{static_cast<const char*>(q) + s0 * qrow,
+                            static_cast<const char*>(k) + s0 * kvrow,
+                            static_cast<const char*>(v) + s0 * kvrow, dtype,
+                            static_cast<const char*>(q_idx) + s0 * qirow,
+                            q_scale ? q_scale + s0 : nullptr, w + s0 * HI,
+                            static_cast<const char*>(k_idx) + s0 * kirow,
+                            k_scale ? k_scale + s0 : nullptr, idx_dtype, Hq, G, d, HI, dI, topk,
+                            sm_scale, static_cast<char*>(out) + s0 * qrow,
+                            idx_out ? idx_out + s0 * topk : nullptr};
+        st = run_prefill(a, len, 0, b, first_cand, stream);
         if (st != DSA_OK) return st;
     }
     return DSA_OK;

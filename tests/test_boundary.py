@@ -175,3 +175,28 @@ def test_quantize_and_cache_append_argument_checks(lib):
     assert c(*bad) == 1 and b"kidx_cache" in lib.dsa_last_error()
     bad = list(ok); bad[10] = 0
     assert c(*bad) == 1
+
+
+def test_prefill_varlen_argument_checks(lib):
+    f = lib.dsa_prefill_varlen
+
+    def cu(*v):
+        return ctypes.cast((ctypes.c_int32 * len(v))(*v), ctypes.c_void_p)
+    n = lib.dsa_prefill_workspace_size(3000, 0, 1024, 2048)
+    args = [A, A, A, dsa.DSA_BF16, A, A, A, A, A, dsa.DSA_FP8_E4M3, cu(0, 1000, 1000, 4000), 3,
+            32, 4, 128, 64, 128, 2048, 0.1, 1024, A, None, A, n - 1, None]
+    assert f(*args) == 3 and b"workspace" in lib.dsa_last_error()   # sized by the longest
+    args[10] = None
+    assert f(*args) == 1 and b"cu_seqlens" in lib.dsa_last_error()
+    args[10] = cu(1, 1000)
+    args[11] = 1
+    assert f(*args) == 1 and b"cu_seqlens[0]" in lib.dsa_last_error()
+    args[10] = cu(0, 1000, 999)
+    args[11] = 2
+    assert f(*args) == 1 and b"decrease" in lib.dsa_last_error()
+    args[10] = cu(0, 0, 0)
+    assert f(*args) == 0                                             # only empty sequences
+    args[10] = cu(0, 100)
+    args[11] = 1
+    args[15] = 6
+    assert f(*args) == 2                                             # FP8 needs HI % 4 == 0

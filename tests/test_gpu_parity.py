@@ -274,6 +274,14 @@ def _prefill_and_check(cfg, x, rows, chunk, what, dtype):
     _say("  prefill done", what, "candidate-path counters", stats)
     if cfg.idx_dtype == "fp8" and cfg.HI <= 64:
         assert stats == [_cand_chunks(L, 0, chunk), 0]
+    _check_rows_vs_oracle(cfg, x, out, idx, rows, what, dtype)
+    return out, idx
+
+
+def _check_rows_vs_oracle(cfg, x, out, idx, rows, what, dtype):
+    """Omega (within the tolerance band) and outputs of `rows` of a one-sequence prefill
+    against the oracle."""
+    k = cfg.k
     idt = oracle.FP8_E4M3 if cfg.idx_dtype == "fp8" else oracle.F32
     qi, w = to_np(x["q_idx"][rows]), to_np(x["w"][rows])
     qs = None if x["q_scale"] is None else to_np(x["q_scale"][rows])
@@ -298,7 +306,6 @@ def _prefill_and_check(cfg, x, rows, chunk, what, dtype):
                                      cfg.Hq, cfg.G, cfg.sm_scale)
     err = check_attn(bf16_to_f64(to_np(out[rows])), ref_out, dtype, what)
     _say("  %s: %d rows ok, %d band-swapped members, attn max err %.2e" % (what, len(rows), differ, err))
-    return out, idx
 
 
 def test_prefill_tiny_f32_config_full():
@@ -746,3 +753,89 @@ def test_append_then_decode_serving_step():
         assert np.array_equal(to_np(x["kidx_cache"][blk, p % cfg.block]), kc[b])
         assert torch.equal(x["k_cache"][blk, p % cfg.block], k_new[b])
     _decode_and_check(cfg, x, list(range(cfg.B)), "append + decode")
+
+
+# ------------------------------------------------------- packed variable-length prefill
+
+def _seq_slice(x, a, b):
+    return {key: (None if x[key] is None else x[key][a:b].contiguous())
+            for key in ("q", "k", "v", "q_idx", "q_scale", "w", "k_idx", "k_scale")}
+
+
+def _varlen_vs_separate(cfg, lens, chunk, what):
+    x = W.packed_prefill_inputs(cfg, lens, DEV)
+    cu = x["cu_seqlens"]
+    out, idx, stats = dsa.prefill_varlen(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"],
+                                         x["k_idx"], x["k_scale"], cu, cfg.k, cfg.sm_scale,
+                                         chunk_rows=chunk, return_idx=True, return_stats=True)
+    torch.cuda.synchronize()
+    _say("  %s: varlen done, counters %s" % (what, stats))
+    n_cand = 0
+    for i in range(len(lens)):
+        a, b = cu[i], cu[i + 1]
+        if b == a:
+            continue
+        s = _seq_slice(x, a, b)
+        o1, i1 = dsa.prefill(s["q"], s["k"], s["v"], s["q_idx"], s["q_scale"], s["w"], s["k_idx"],
+                             s["k_scale"], cfg.k, cfg.sm_scale, chunk_rows=chunk, return_idx=True)
+        torch.cuda.synchronize()
+        assert torch.equal(idx[a:b], i1), (what, i)
+        assert torch.equal(out[a:b], o1), (what, i)
+        n_cand += _cand_chunks(b - a, 0, chunk)
+    if cfg.idx_dtype == "fp8" and cfg.HI <= 64:
+        assert stats == [n_cand, 0]
+    return x, out, idx
+
+
+@pytest.mark.parametrize("chunk", [1024, 0])
+def test_prefill_varlen_equals_separate_calls(chunk):
+    """Every sequence of a packed batch (empty, single-token, exactly k, just above k,
+    ragged lengths) is bitwise the one-sequence prefill of it."""
+    cfg = W.scaled(W.PREFILL_32K, L=1, k=2048, seed=310)
+    lens = [0, 1, 17, 2048, 2049, 3000, 0, 5003, 700]
+    _varlen_vs_separate(cfg, lens, chunk, "varlen chunk=%d" % chunk)
+
+
+def test_prefill_varlen_vs_oracle():
+    """A small packed batch checked row by row against the oracle, each sequence on its own."""
+    cfg = W.scaled(W.PREFILL_32K, L=1, k=256, seed=320)
+    lens = [300, 2500, 1, 777]
+    x, out, idx = _varlen_vs_separate(cfg, lens, 512, "varlen oracle")
+    cu = x["cu_seqlens"]
+    for i, n in enumerate(lens):
+        a = cu[i]
+        s = _seq_slice(x, a, a + n)
+        rows = list(range(0, n, 1 if n <= 800 else 3))
+        _check_rows_vs_oracle(W.scaled(cfg, L=n), s, out[a:a + n], idx[a:a + n], rows,
+                              "varlen seq %d" % i, "bf16")
+
+
+def test_prefill_varlen_candidate_path():
+    """Long sequences in a packed batch take the candidate path, each as on its own."""
+    cfg = W.scaled(W.PREFILL_32K, L=1, k=2048, keys="clustered", seed=330)
+    _varlen_vs_separate(cfg, [50001, 3000, 60000], 8192, "varlen candidates")
+
+
+def test_prefill_past_the_candidate_range():
+    """A call whose last chunk sees more keys than the candidate path takes (524288) while
+    an earlier chunk still takes it: the sample buffer must be sized for that earlier chunk.
+    Compared bit for bit with the separate entry points over full score rows."""
+    L, q0, k = 528192, 520000, 2048
+    cfg = W.scaled(W.PREFILL_32K, L=L, k=k, seed=340)
+    # keys of the whole prefix; queries (64 indexer heads) only for the rows computed
+    x = W.prefill_inputs(W.scaled(cfg, HI=4), DEV)
+    xq = W.prefill_inputs(W.scaled(cfg, L=L - q0, seed=341), DEV)
+    q, qi, qs, w = xq["q"], xq["q_idx"], xq["q_scale"], xq["w"]
+    out, idx, stats = dsa.prefill(q, x["k"], x["v"], qi, qs, w, x["k_idx"], x["k_scale"], k,
+                                  cfg.sm_scale, chunk_rows=4096, q_pos0=q0, return_idx=True,
+                                  return_stats=True)
+    torch.cuda.synchronize()
+    _say("  past the candidate range: counters", stats)
+    assert stats == [1, 0]                       # rows seeing <= 524096 keys: one chunk
+    scores = dsa.index_scores(qi, qs, w, x["k_idx"], x["k_scale"], q_pos0=q0)
+    idx_s = dsa.topk(scores, L, k, q_pos0=q0)
+    del scores
+    out_s = dsa.sparse_gqa_attn(q, x["k"], x["v"], idx_s, cfg.G, cfg.sm_scale, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_s)
+    assert torch.equal(out, out_s)

@@ -197,6 +197,30 @@ def decode_inputs(cfg: DecodeConfig, device="cpu", lens: Optional[torch.Tensor] 
     return out
 
 
+def packed_lengths(n: int, Lmin: int, Lmax: int, seed: int) -> list:
+    """Seeded sequence lengths for a packed batch, uniform in [Lmin, Lmax]."""
+    g = _gen(seed, 12, "cpu")
+    return torch.randint(Lmin, Lmax + 1, (n,), generator=g).tolist()
+
+
+def packed_prefill_inputs(cfg: PrefillConfig, lens, device="cpu") -> dict:
+    """A packed batch: sequence i is ``prefill_inputs`` of ``cfg`` with L = lens[i] and seed
+    cfg.seed + i, the sequences concatenated along the token dimension.  Adds ``cu_seqlens``
+    (a list of len(lens) + 1 offsets)."""
+    parts = [prefill_inputs(dataclasses.replace(cfg, L=int(n), seed=cfg.seed + i), device)
+             for i, n in enumerate(lens) if n > 0]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + int(n))
+    out = {"cu_seqlens": cu}
+    for key in ("q", "k", "v", "q_idx", "q_scale", "w", "k_idx", "k_scale"):
+        if parts and parts[0][key] is not None:
+            out[key] = torch.cat([p[key] for p in parts]).contiguous()
+        else:
+            out[key] = None
+    return out
+
+
 def scaled(cfg, **changes):
     """A copy of ``cfg`` with some fields replaced (smaller test variants)."""
     return dataclasses.replace(cfg, **changes)
