@@ -18,7 +18,8 @@ and its algorithmic rate (FP8 FLOPs for the indexer, bytes for top-k and the
 attention gather); the dominant kernel, the attention, which both paths run
 identically, is reported as ``roofline``.  Both paths must give identical
 index sets and outputs.  The CPU oracle, timed on a stratified sample of
-query rows, is reported as ``cpu_baseline``.
+query rows, is reported as ``cpu_baseline``.  A packed batch of 16 sequences of 2K..14K tokens
+through dsa_prefill_varlen is reported under ``packed_prefill``.
 """
 from __future__ import annotations
 
@@ -49,6 +50,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=96)
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-packed", action="store_true")
     p.add_argument("--profile-kernel", choices=["index", "topk", "attn"], default=None,
                    help="profiling driver: run only this kernel on one chunk of the workload "
                         "(--profile-chunk, default the last) --profile-reps times, print nothing else")
@@ -317,6 +319,45 @@ def run_decode_bench(args, dsa, W, torch, name):
     return res
 
 
+def run_packed_bench(args, dsa, W, torch):
+    """Packed variable-length prefill: 16 sequences of 2K..14K tokens (seeded, clustered keys,
+    the 128K layer's shapes), one dsa_prefill_varlen call per step."""
+    cfg = W.scaled(W.PREFILL_128K, L=1, seed=1010)
+    lens = W.packed_lengths(16, 2048, 14336, cfg.seed)
+    log("generating packed batch", lens)
+    x = W.packed_prefill_inputs(cfg, lens, "cuda")
+    cu = x["cu_seqlens"]
+    T = cu[-1]
+    max_len = max(lens)
+    out = torch.empty_like(x["q"])
+    n = dsa.dsa_prefill_workspace_size(max_len, 0, cfg.chunk, cfg.k)
+    ws = dsa.workspace(n)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dsa.dsa_prefill_varlen(x["q"], x["k"], x["v"], dsa.DSA_BF16, x["q_idx"], x["q_scale"],
+                               x["w"], x["k_idx"], x["k_scale"], dsa.DSA_FP8_E4M3, cu, len(lens),
+                               cfg.Hq, cfg.G, cfg.d, cfg.HI, cfg.dI, cfg.k, cfg.sm_scale,
+                               cfg.chunk, out, None, ws, ws.numel(), stream)
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(3, args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    res = {"workload": "prefill_packed_16x2k-14k", "sequences": len(lens), "tokens": T,
+           "max_len": max_len, "ms_per_step": round(ms, 3),
+           "tokens_per_s": round(T / (ms * 1e-3), 1)}
+    del x, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args, cfg, x, torch):
     """The oracle on a stratified sample of query rows of the same workload."""
     import numpy as np
@@ -397,6 +438,8 @@ def main():
     }
     del x, idx, out
     torch.cuda.empty_cache()
+    if not args.no_packed:
+        result["packed_prefill"] = run_packed_bench(args, dsa, W, torch)
     if not args.no_decode:
         result["decode"] = [run_decode_bench(args, dsa, W, torch, n)
                             for n in args.decode_workloads.split(",") if n]
