@@ -82,14 +82,81 @@ __device__ void quantize_row(const T* __restrict__ x, int64_t row, int n, uint8_
     }
 }
 
+// The same for rows of at most kQuantThreads * kVecLoads 16-byte pieces (n a multiple of the
+// values per piece, x and codes 16-byte aligned): every thread issues all of its loads at
+// once and keeps the values in registers between the maximum and the rounding.
+constexpr int kVecLoads = 8;
+
+template <class T> struct Piece;
+template <> struct Piece<float> {
+    static constexpr int N = 4;
+    __device__ static void get(const v4i& r, float* v) {
+        for (int i = 0; i < 4; ++i) v[i] = __int_as_float(r[i]);
+    }
+    __device__ static void put(uint8_t* dst, const uint8_t* c) {
+        *reinterpret_cast<uint32_t*>(dst) = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
+    }
+};
+template <> struct Piece<uint16_t> {
+    static constexpr int N = 8;
+    __device__ static void get(const v4i& r, float* v) {
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float((uint32_t)r[i] << 16);
+            v[2 * i + 1] = __uint_as_float((uint32_t)r[i] & 0xffff0000u);
+        }
+    }
+    __device__ static void put(uint8_t* dst, const uint8_t* c) {
+        const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | ((uint32_t)c[3] << 24);
+        const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | ((uint32_t)c[7] << 24);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    }
+};
+
 template <class T>
+__device__ void quantize_row_vec(const T* __restrict__ src, int n, uint8_t* __restrict__ dst,
+                                 float* __restrict__ scale_out, float* red)
+{
+    constexpr int N = Piece<T>::N;
+    const int tid = threadIdx.x;
+    const int np = n / N;
+    float v[kVecLoads][N];
+    v4i raw[kVecLoads];
+#pragma unroll
+    for (int l = 0; l < kVecLoads; ++l)              // clamped, unconditional loads
+        raw[l] = reinterpret_cast<const v4i*>(src)[min(tid + l * kQuantThreads, np - 1)];
+    float amax = 0.f;
+#pragma unroll
+    for (int l = 0; l < kVecLoads; ++l) {
+        Piece<T>::get(raw[l], v[l]);
+        if (tid + l * kQuantThreads < np)
+#pragma unroll
+            for (int i = 0; i < N; ++i) amax = fmaxf(amax, fabsf(v[l][i]));
+    }
+    amax = block_max(amax, red);
+    const float s = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+    if (tid == 0) *scale_out = s;
+#pragma unroll
+    for (int l = 0; l < kVecLoads; ++l) {
+        const int piece = tid + l * kQuantThreads;
+        if (piece < np) {
+            uint8_t c[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                c[i] = e4m3_rne(fminf(fmaxf(__fdiv_rn(v[l][i], s), -448.f), 448.f));
+            Piece<T>::put(dst + (int64_t)piece * N, c);
+        }
+    }
+}
+
+template <class T, bool VEC>
 __global__ __launch_bounds__(kQuantThreads) void quantize_e4m3_kernel(const T* __restrict__ x, int n,
                                                                       uint8_t* __restrict__ codes,
                                                                       float* __restrict__ scale)
 {
     __shared__ float red[kQuantThreads / 64];
     const int64_t row = blockIdx.x;
-    quantize_row(x, row, n, codes + row * n, scale + row, red);
+    if (VEC) quantize_row_vec(x + row * n, n, codes + row * n, scale + row, red);
+    else quantize_row(x, row, n, codes + row * n, scale + row, red);
 }
 
 // One workgroup per sequence: K and V rows copied (16-byte pieces), the k^I row quantised.
@@ -124,12 +191,19 @@ hipError_t launch_quantize_e4m3(const void* x, int x_bf16, int T, int n, uint8_t
                                 float* scale, hipStream_t stream)
 {
     if (T == 0) return hipSuccess;
-    if (x_bf16)
-        hipLaunchKernelGGL(quantize_e4m3_kernel<uint16_t>, dim3(T), dim3(kQuantThreads), 0, stream,
-                           static_cast<const uint16_t*>(x), n, codes, scale);
-    else
-        hipLaunchKernelGGL(quantize_e4m3_kernel<float>, dim3(T), dim3(kQuantThreads), 0, stream,
-                           static_cast<const float*>(x), n, codes, scale);
+    const int per = x_bf16 ? 8 : 4;                   // values per 16-byte piece
+    const bool vec = n % per == 0 && n / per <= kQuantThreads * kVecLoads &&
+                     (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(codes) & 15) == 0;
+    if (x_bf16) {
+        const auto* xb = static_cast<const uint16_t*>(x);
+        if (vec) hipLaunchKernelGGL((quantize_e4m3_kernel<uint16_t, true>), dim3(T), dim3(kQuantThreads), 0, stream, xb, n, codes, scale);
+        else hipLaunchKernelGGL((quantize_e4m3_kernel<uint16_t, false>), dim3(T), dim3(kQuantThreads), 0, stream, xb, n, codes, scale);
+    } else {
+        const auto* xf = static_cast<const float*>(x);
+        if (vec) hipLaunchKernelGGL((quantize_e4m3_kernel<float, true>), dim3(T), dim3(kQuantThreads), 0, stream, xf, n, codes, scale);
+        else hipLaunchKernelGGL((quantize_e4m3_kernel<float, false>), dim3(T), dim3(kQuantThreads), 0, stream, xf, n, codes, scale);
+    }
     return hipGetLastError();
 }
 
