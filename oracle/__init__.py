@@ -6,9 +6,11 @@ shares no code with the C source here (``oracle.c``).
 
 The functions follow the formulas of the Kwai Keye-VL-2.0 report (xllm-io
 review page, section "核心公式"; report section 2.3): the lightning indexer
-score, the Top-k index set and GQA sparse aggregation.  Every result is
-float64.  See ``oracle.c`` for the arithmetic and the readings of points the
-pages leave open.
+score, the Top-k index set and GQA sparse aggregation, and on the training
+side (``oracle_train.c``; report section 2.3.3 and the review page's sparse
+adaptation loss) the attention backward and the sparse indexer loss.  Every
+result is float64.  See the C sources for the arithmetic and the readings of
+points the pages leave open.
 """
 from __future__ import annotations
 
@@ -21,6 +23,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_SRC_TRAIN = os.path.join(_HERE, "oracle_train.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
@@ -31,10 +34,11 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile oracle.c into liboracle.so with the host C compiler (no -ffast-math)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+    newest = max(os.path.getmtime(p) for p in (_SRC, _SRC_TRAIN, os.path.join(_HERE, "oracle.h")))
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-               "-o", tmp, _SRC, "-lm"]
+               "-o", tmp, _SRC, _SRC_TRAIN, "-lm"]
         subprocess.run(cmd, check=True, cwd=_HERE)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -61,6 +65,16 @@ def _load():
             lib.oracle_decode.restype = None
             lib.oracle_quantize_e4m3.argtypes = [P, I, I, I, P, P]
             lib.oracle_quantize_e4m3.restype = None
+            lib.oracle_attn_lse.argtypes = [P, P, P, I, P, I, I, I, I, I, D, P, P]
+            lib.oracle_attn_lse.restype = None
+            lib.oracle_attn_bwd.argtypes = [P, P, P, I, P, I, I, I, I, I, I, D, P, P, P, P]
+            lib.oracle_attn_bwd.restype = None
+            lib.oracle_indexer_kl.argtypes = [P, P, I, P, I, I, I, I, I, D, P, P, P]
+            lib.oracle_indexer_kl.restype = None
+            lib.oracle_index_scores_at.argtypes = [P, P, P, P, P, I, I, I, I, P, I, P]
+            lib.oracle_index_scores_at.restype = None
+            lib.oracle_index_scores_bwd.argtypes = [P, P, P, P, P, I, I, I, I, I, P, I, P, P, P, P]
+            lib.oracle_index_scores_bwd.restype = None
             lib.oracle_num_threads.argtypes = []
             lib.oracle_num_threads.restype = I
             _lib = lib
@@ -219,3 +233,86 @@ def quantize_e4m3(x, x_dtype=F32):
     scale = np.empty(T, dtype=np.float32)
     lib.oracle_quantize_e4m3(_ptr(x), x_dtype, T, n, _ptr(codes), _ptr(scale))
     return codes, scale
+
+
+# ------------------------------------------------------------------ training side
+
+def _attn_arrays(q, k, v, dtype, idx):
+    el = np.float32 if dtype == F32 else np.uint16
+    return _np(q, el), _np(k, el), (None if v is None else _np(v, el)), _np(idx, np.int32)
+
+
+def attn_lse(q, k, v, dtype, idx, G, sm_scale):
+    """(out float64 [T, Hq, d], lse float64 [T, Hq]) of the attention over idx."""
+    lib = _load()
+    q, k, v, idx = _attn_arrays(q, k, v, dtype, idx)
+    T, Hq, d = q.shape
+    out = np.empty((T, Hq, d), dtype=np.float64)
+    lse = np.empty((T, Hq), dtype=np.float64)
+    lib.oracle_attn_lse(_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(idx), idx.shape[1], T, Hq, G, d,
+                        float(sm_scale), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def attn_bwd(q, k, v, dtype, idx, G, sm_scale, dout):
+    """(dq [T,Hq,d], dk [Tk,G,d], dv [Tk,G,d]) float64: gradients of sum(dout * out)."""
+    lib = _load()
+    q, k, v, idx = _attn_arrays(q, k, v, dtype, idx)
+    dout = _np(dout, np.float32 if dtype == F32 else np.uint16)
+    T, Hq, d = q.shape
+    Tk = k.shape[0]
+    dq = np.empty((T, Hq, d), dtype=np.float64)
+    dk = np.empty((Tk, G, d), dtype=np.float64)
+    dv = np.empty((Tk, G, d), dtype=np.float64)
+    lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), dtype, _ptr(idx), idx.shape[1], T, Tk, Hq, G,
+                        d, float(sm_scale), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq, dk, dv
+
+
+def indexer_kl(q, k, dtype, idx, G, sm_scale, vals):
+    """(kl float64 [T], dI float64 [T, kk]) of the sparse indexer loss."""
+    lib = _load()
+    q, k, _, idx = _attn_arrays(q, k, None, dtype, idx)
+    T, Hq, d = q.shape
+    vals = np.ascontiguousarray(np.asarray(vals, dtype=np.float64))
+    kl = np.empty(T, dtype=np.float64)
+    dI = np.empty(idx.shape, dtype=np.float64)
+    lib.oracle_indexer_kl(_ptr(q), _ptr(k), dtype, _ptr(idx), idx.shape[1], T, Hq, G, d,
+                          float(sm_scale), _ptr(vals), _ptr(kl), _ptr(dI))
+    return kl, dI
+
+
+def _indexer_arrays(q_idx, q_scale, w, k_idx, k_scale, idx_dtype):
+    el = np.uint8 if idx_dtype == FP8_E4M3 else np.float32
+    return (_np(q_idx, el), _np(q_scale, np.float32), _np(w, np.float32), _np(k_idx, el),
+            _np(k_scale, np.float32))
+
+
+def index_scores_at(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, idx):
+    """vals float64 [T, kk] = I[t, idx[t, i]] (-inf for padding)."""
+    lib = _load()
+    q_idx, q_scale, w, k_idx, k_scale = _indexer_arrays(q_idx, q_scale, w, k_idx, k_scale, idx_dtype)
+    idx = _np(idx, np.int32)
+    T, HI, dI = q_idx.shape
+    vals = np.empty(idx.shape, dtype=np.float64)
+    lib.oracle_index_scores_at(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+                               idx_dtype, T, HI, dI, _ptr(idx), idx.shape[1], _ptr(vals))
+    return vals
+
+
+def index_scores_bwd(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, idx, g):
+    """(dq_idx [T,HI,dI], dw [T,HI], dk_idx [Tk,dI]) float64: gradients of
+    sum g[t,i] * I[t, idx[t,i]] with respect to the dequantised indexer inputs."""
+    lib = _load()
+    q_idx, q_scale, w, k_idx, k_scale = _indexer_arrays(q_idx, q_scale, w, k_idx, k_scale, idx_dtype)
+    idx = _np(idx, np.int32)
+    g = np.ascontiguousarray(np.asarray(g, dtype=np.float64))
+    T, HI, dI = q_idx.shape
+    Tk = k_idx.shape[0]
+    dq = np.empty((T, HI, dI), dtype=np.float64)
+    dw = np.empty((T, HI), dtype=np.float64)
+    dk = np.empty((Tk, dI), dtype=np.float64)
+    lib.oracle_index_scores_bwd(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+                                idx_dtype, T, Tk, HI, dI, _ptr(idx), idx.shape[1], _ptr(g),
+                                _ptr(dq), _ptr(dw), _ptr(dk))
+    return dq, dw, dk

@@ -59,6 +59,39 @@ void oracle_decode(const void* q, const uint8_t* q_idx, const float* q_scale, co
  * ties to the even code. */
 void oracle_quantize_e4m3(const void* x, int x_dtype, int T, int n, uint8_t* codes, float* scale);
 
+/* ---- training side (oracle_train.c): all arrays of T rows, contiguous K/V [Tk, G, d] ---- */
+
+/* Attention over idx as oracle_sparse_gqa_attn, plus lse[t, h] = ln sum_i exp(logit_i)
+ * (-inf for a row without valid entries, whose output is 0). */
+void oracle_attn_lse(const void* q, const void* k, const void* v, int dtype, const int32_t* idx,
+                     int kk, int T, int Hq, int G, int d, double sm_scale, double* out,
+                     double* lse);
+
+/* Gradients of sum dout * out with respect to q [T,Hq,d], k and v [Tk,G,d] (overwritten);
+ * dout [T, Hq, d] in `dtype`. */
+void oracle_attn_bwd(const void* q, const void* k, const void* v, int dtype, const int32_t* idx,
+                     int kk, int T, int Tk, int Hq, int G, int d, double sm_scale,
+                     const void* dout, double* dq, double* dk, double* dv);
+
+/* Sparse indexer loss per row, kl[t] = sum_g KL(p[t,:,g] || softmax(vals[t,:])) over the
+ * valid entries of idx[t,:] (p = mean attention probability of the group's heads), and
+ * dI[t,i] = d kl[t] / d vals[t,i] (0 for padding).  vals [T, kk] = I[t, idx[t,i]]. */
+void oracle_indexer_kl(const void* q, const void* k, int dtype, const int32_t* idx, int kk, int T,
+                       int Hq, int G, int d, double sm_scale, const double* vals, double* kl,
+                       double* dI);
+
+/* vals[t, i] = I[t, idx[t, i]] (-inf for padding). */
+void oracle_index_scores_at(const void* q_idx, const float* q_scale, const float* w,
+                            const void* k_idx, const float* k_scale, int idx_dtype, int T,
+                            int HI, int dI, const int32_t* idx, int kk, double* vals);
+
+/* Gradients of sum_{t,i} g[t,i] * I[t, idx[t,i]] with respect to the dequantised q^I
+ * [T,HI,dI], w [T,HI] and k^I [Tk,dI] (overwritten). */
+void oracle_index_scores_bwd(const void* q_idx, const float* q_scale, const float* w,
+                             const void* k_idx, const float* k_scale, int idx_dtype, int T,
+                             int Tk, int HI, int dI, const int32_t* idx, int kk, const double* g,
+                             double* dq_idx, double* dw, double* dk_idx);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

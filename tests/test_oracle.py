@@ -456,3 +456,202 @@ def test_quantize_bf16_input_matches_float_input():
     c1, s1 = oracle.quantize_e4m3(x, oracle.BF16)
     c2, s2 = oracle.quantize_e4m3(x.float().numpy(), oracle.F32)
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+# ------------------------------------------------------------------ training side
+#
+# The backward and the indexer loss are pinned to torch's float64 autograd of the
+# forward formulas (library differentiation, independent of the oracle's hand-written
+# gradients), to central finite differences of the oracle's own (separately pinned)
+# forward, and to closed forms.
+
+def _train_case(rng, T, Tk, Hq, G, d, kk, pad=True):
+    """f32 inputs on a 2^-6 grid (so small perturbations stay exact), causal-looking index
+    lists with -1 padding."""
+    q = (rng.integers(-64, 65, (T, Hq, d)) / 64.0).astype(np.float32)
+    k = (rng.integers(-64, 65, (Tk, G, d)) / 64.0).astype(np.float32)
+    v = (rng.integers(-64, 65, (Tk, G, d)) / 64.0).astype(np.float32)
+    idx = np.full((T, kk), -1, dtype=np.int32)
+    for t in range(T):
+        n = rng.integers(1, kk + 1) if pad else kk
+        idx[t, :n] = np.sort(rng.choice(Tk, size=n, replace=False))
+    return q, k, v, idx
+
+
+def _torch_attn(q, k, v, idx, G, sm_scale):
+    """out [T,Hq,d] of float64 torch tensors (autograd-able) by gather + masked softmax."""
+    T, Hq, d = q.shape
+    hpg = Hq // G
+    valid = torch.from_numpy(idx >= 0)
+    ii = torch.from_numpy(np.maximum(idx, 0)).long()
+    kg = k[ii]                                     # [T, kk, G, d]
+    vg = v[ii]
+    g_of_h = torch.arange(Hq) // hpg
+    kh = kg[:, :, g_of_h, :]                       # [T, kk, Hq, d]
+    vh = vg[:, :, g_of_h, :]
+    logits = sm_scale * torch.einsum("thd,tkhd->thk", q, kh)
+    logits = logits.masked_fill(~valid[:, None, :], float("-inf"))
+    p = torch.softmax(logits, dim=-1)
+    return torch.einsum("thk,tkhd->thd", p, vh), p, logits
+
+
+def test_attn_lse_matches_torch_logsumexp():
+    rng = np.random.default_rng(41)
+    q, k, v, idx = _train_case(rng, T=6, Tk=9, Hq=4, G=2, d=8, kk=5)
+    out, lse = oracle.attn_lse(q, k, v, oracle.F32, idx, 2, 0.35)
+    o_t, _, logits = _torch_attn(*(torch.from_numpy(a).double() for a in (q, k, v)), idx, 2, 0.35)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, dim=-1).numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out, o_t.numpy(), rtol=0, atol=1e-12)
+    # a single selected position: lse is its logit and the output its V row
+    one = np.full_like(idx, -1)
+    one[:, 0] = 3
+    out1, lse1 = oracle.attn_lse(q, k, v, oracle.F32, one, 2, 0.35)
+    np.testing.assert_allclose(out1[:, :2], np.broadcast_to(v[3, 0], (6, 2, 8)), atol=1e-12)
+    np.testing.assert_allclose(lse1[:, 0], 0.35 * np.einsum("td,d->t", q[:, 0].astype(np.float64),
+                                                            k[3, 0].astype(np.float64)), atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_attn_bwd_matches_autograd(dtype):
+    rng = np.random.default_rng(42)
+    T, Tk, Hq, G, d, kk, sm = 7, 11, 8, 2, 16, 6, 0.3
+    q, k, v, idx = _train_case(rng, T, Tk, Hq, G, d, kk)
+    dout = (rng.integers(-64, 65, (T, Hq, d)) / 64.0).astype(np.float32)
+    arrs = [q, k, v, dout]
+    if dtype == "bf16":                            # grid values are exact in bf16
+        arrs = [torch.from_numpy(a).bfloat16() for a in arrs]
+        od = oracle.BF16
+    else:
+        od = oracle.F32
+    dq, dk, dv = oracle.attn_bwd(arrs[0], arrs[1], arrs[2], od, idx, G, sm, arrs[3])
+    qt, kt, vt = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    out, _, _ = _torch_attn(qt, kt, vt, idx, G, sm)
+    (out * torch.from_numpy(dout).double()).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=0, atol=1e-11)
+    # positions nobody selected get no gradient
+    unused = np.setdiff1d(np.arange(Tk), idx[idx >= 0])
+    assert np.all(dk[unused] == 0) and np.all(dv[unused] == 0)
+
+
+def test_attn_bwd_central_differences_of_the_forward():
+    rng = np.random.default_rng(43)
+    T, Tk, Hq, G, d, kk, sm = 4, 6, 4, 2, 8, 4, 0.5
+    q, k, v, idx = _train_case(rng, T, Tk, Hq, G, d, kk, pad=False)
+    dout = (rng.integers(-64, 65, (T, Hq, d)) / 64.0)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, oracle.F32, idx, G, sm, dout.astype(np.float32))
+
+    def loss(q_, k_, v_):
+        return float((oracle.sparse_gqa_attn(q_, k_, v_, oracle.F32, idx, Hq, G, sm) * dout).sum())
+    h = 2.0 ** -10
+    for arr, grad, pos in ((q, dq, (1, 2, 3)), (k, dk, (int(idx[0, 1]), 1, 5)),
+                           (v, dv, (int(idx[2, 0]), 0, 7))):
+        plus, minus = arr.copy(), arr.copy()
+        plus[pos] += h
+        minus[pos] -= h
+        args_p = [plus if a is arr else a for a in (q, k, v)]
+        args_m = [minus if a is arr else a for a in (q, k, v)]
+        fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert abs(fd - grad[pos]) <= 1e-5 * max(1.0, abs(fd)), (pos, fd, grad[pos])
+
+
+def _torch_kl(q, k, idx, G, sm, vals):
+    """kl [T] from torch float64 (vals autograd-able)."""
+    T, Hq, d = q.shape
+    qd, kd = torch.from_numpy(q).double(), torch.from_numpy(k).double()
+    _, p, _ = _torch_attn(qd, kd, kd, idx, G, sm)          # v unused
+    pg = p.view(T, G, Hq // G, -1).mean(dim=2)              # [T, G, kk]
+    valid = torch.from_numpy(idx >= 0)
+    logq = torch.log_softmax(vals.masked_fill(~valid, float("-inf")), dim=-1)
+    logq = logq.masked_fill(~valid, 0.0)
+    terms = torch.special.xlogy(pg, pg) - pg * logq[:, None, :]
+    return terms.sum(dim=(1, 2))
+
+
+def test_indexer_kl_matches_autograd():
+    rng = np.random.default_rng(44)
+    T, Tk, Hq, G, d, kk, sm = 6, 10, 8, 4, 8, 7, 0.4
+    q, k, _, idx = _train_case(rng, T, Tk, Hq, G, d, kk)
+    vals = rng.normal(size=(T, kk))
+    vals[idx < 0] = -np.inf
+    kl, dI = oracle.indexer_kl(q, k, oracle.F32, idx, G, sm, vals)
+    vt = torch.tensor(np.where(idx >= 0, vals, 0.0), requires_grad=True)
+    kt = _torch_kl(q, k, idx, G, sm, vt)
+    kt.sum().backward()
+    np.testing.assert_allclose(kl, kt.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dI, np.where(idx >= 0, vt.grad.numpy(), 0.0), rtol=0, atol=1e-12)
+    assert np.all(kl >= -1e-12)                    # a KL divergence is never negative
+    np.testing.assert_allclose(dI.sum(axis=1), 0.0, atol=1e-12)   # softmax gradients sum to 0
+
+
+def test_indexer_kl_vanishes_when_the_indexer_matches_the_target():
+    """One KV group: the target is the mean head distribution; scores equal to its log
+    (plus any constant) give KL = 0 and a zero gradient."""
+    rng = np.random.default_rng(45)
+    T, Tk, Hq, G, d, kk, sm = 5, 9, 4, 1, 8, 6, 0.7
+    q, k, _, idx = _train_case(rng, T, Tk, Hq, G, d, kk)
+    _, p, _ = _torch_attn(torch.from_numpy(q).double(), torch.from_numpy(k).double(),
+                          torch.from_numpy(k).double(), idx, G, sm)
+    target = p.mean(dim=1).numpy()                              # [T, kk]
+    vals = np.where(idx >= 0, np.log(np.maximum(target, 1e-300)) + 3.25, -np.inf)
+    kl, dI = oracle.indexer_kl(q, k, oracle.F32, idx, G, sm, vals)
+    np.testing.assert_allclose(kl, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dI, 0.0, atol=1e-12)
+
+
+def _torch_indexer(qi, w, ki, idx):
+    """I[t, idx[t,i]] in float64 torch from dequantised inputs (autograd-able)."""
+    ii = torch.from_numpy(np.maximum(idx, 0)).long()
+    kg = ki[ii]                                            # [T, kk, dI]
+    x = torch.einsum("tjd,tkd->tjk", qi, kg)              # [T, HI, kk]
+    return (w[:, :, None] * torch.relu(x)).sum(dim=1)     # [T, kk]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_indexer_scores_at_and_backward_match_autograd(fp8):
+    rng = np.random.default_rng(46)
+    T, Tk, HI, dI, kk = 5, 12, 4, 8, 6
+    _, _, _, idx = _train_case(rng, T, Tk, 2, 1, 4, kk)
+    w = rng.normal(size=(T, HI)).astype(np.float32)         # signed weights
+    if fp8:
+        qc = rng.integers(0, 256, (T, HI, dI), dtype=np.uint8)
+        kc = rng.integers(0, 256, (Tk, dI), dtype=np.uint8)
+        qc[(qc & 0x7F) == 0x7F] = 0x38                       # no NaN codes
+        kc[(kc & 0x7F) == 0x7F] = 0x38
+        qs = rng.uniform(0.01, 0.1, T).astype(np.float32)
+        ks = rng.uniform(0.01, 0.1, Tk).astype(np.float32)
+        lut = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+        qd, kd = lut[qc] * qs[:, None, None], lut[kc] * ks[:, None]
+        args = (qc, qs, w, kc, ks, oracle.FP8_E4M3)
+    else:
+        qd = rng.normal(size=(T, HI, dI)).astype(np.float32)
+        kd = rng.normal(size=(Tk, dI)).astype(np.float32)
+        args = (qd, None, w, kd, None, oracle.F32)
+    vals = oracle.index_scores_at(*args, idx)
+    g = rng.normal(size=(T, kk))
+    dq, dw, dk = oracle.index_scores_bwd(*args, idx, g)
+    qt = torch.tensor(np.asarray(qd, dtype=np.float64), requires_grad=True)
+    kt = torch.tensor(np.asarray(kd, dtype=np.float64), requires_grad=True)
+    wt = torch.tensor(w.astype(np.float64), requires_grad=True)
+    It = _torch_indexer(qt, wt, kt, idx)
+    valid = idx >= 0
+    np.testing.assert_allclose(np.where(valid, vals, 0), np.where(valid, It.detach().numpy(), 0),
+                               rtol=1e-12, atol=1e-12)
+    assert np.all(vals[~valid] == -np.inf)
+    (It * torch.from_numpy(np.where(valid, g, 0.0))).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_scores_at_equal_full_rows_gathered():
+    rng = np.random.default_rng(47)
+    T, HI, dI, k = 40, 8, 128, 16
+    qc, qs, w, kc, ks = _rand_fp8_case(rng, T, HI, dI)
+    full = oracle.index_scores(qc, qs, w, kc, ks, oracle.FP8_E4M3)
+    idx, _ = oracle.topk(full, np.arange(T, dtype=np.int64), k)
+    vals = oracle.index_scores_at(qc, qs, w, kc, ks, oracle.FP8_E4M3, idx)
+    valid = idx >= 0
+    np.testing.assert_allclose(vals[valid], np.take_along_axis(full, np.maximum(idx, 0), 1)[valid],
+                               rtol=1e-13, atol=1e-13)
