@@ -208,29 +208,45 @@ static void deq_key(const void* k_idx, const float* k_scale, int idx_dtype, int6
                      : (double)((const float*)k_idx)[s * dI + i];
 }
 
+/* x = q^I[t,j] . k^I[s] of the dequantised vectors.  For FP8 the dot product of the codes
+ * is taken exactly in integer units of 2^-9 (as in the forward oracle), so a product that is
+ * exactly zero stays zero and the ReLU decision is exact. */
+static double indexer_dot(const void* q_idx, const float* q_scale, const void* k_idx,
+                          const float* k_scale, int idx_dtype, int64_t t, int j, int64_t s, int HI,
+                          int dI)
+{
+    if (idx_dtype == ORACLE_FP8_E4M3) {
+        const uint8_t* qc = (const uint8_t*)q_idx + (t * HI + j) * (int64_t)dI;
+        const uint8_t* kc = (const uint8_t*)k_idx + s * dI;
+        int64_t dot = 0;
+        int nan;
+        for (int e = 0; e < dI; ++e)
+            dot += oracle_e4m3_to_units(qc[e], &nan) * oracle_e4m3_to_units(kc[e], &nan);
+        return (double)q_scale[t] * (double)k_scale[s] * ldexp((double)dot, -18);
+    }
+    const float* q = (const float*)q_idx + (t * HI + j) * (int64_t)dI;
+    const float* k = (const float*)k_idx + s * dI;
+    double dot = 0.0;
+    for (int e = 0; e < dI; ++e) dot += (double)q[e] * (double)k[e];
+    return dot;
+}
+
 void oracle_index_scores_at(const void* q_idx, const float* q_scale, const float* w,
                             const void* k_idx, const float* k_scale, int idx_dtype, int T,
                             int HI, int dI, const int32_t* idx, int kk, double* vals)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int t = 0; t < T; ++t) {
-        double* qv = (double*)malloc((size_t)HI * dI * sizeof(double));
-        double* kv = (double*)malloc((size_t)dI * sizeof(double));
-        deq_query(q_idx, q_scale, idx_dtype, t, HI, dI, qv);
         for (int i = 0; i < kk; ++i) {
             int s = idx[(int64_t)t * kk + i];
             if (s < 0) { vals[(int64_t)t * kk + i] = -INFINITY; continue; }
-            deq_key(k_idx, k_scale, idx_dtype, s, dI, kv);
             double acc = 0.0;
             for (int j = 0; j < HI; ++j) {
-                double x = 0.0;
-                for (int e = 0; e < dI; ++e) x += qv[(int64_t)j * dI + e] * kv[e];
+                double x = indexer_dot(q_idx, q_scale, k_idx, k_scale, idx_dtype, t, j, s, HI, dI);
                 acc += (double)w[(int64_t)t * HI + j] * (x > 0.0 ? x : 0.0);
             }
             vals[(int64_t)t * kk + i] = acc;
         }
-        free(qv);
-        free(kv);
     }
 }
 
@@ -253,8 +269,7 @@ void oracle_index_scores_bwd(const void* q_idx, const float* q_scale, const floa
             double gi = g[(int64_t)t * kk + i];
             deq_key(k_idx, k_scale, idx_dtype, s, dI, kv);
             for (int j = 0; j < HI; ++j) {
-                double x = 0.0;
-                for (int e = 0; e < dI; ++e) x += qv[(int64_t)j * dI + e] * kv[e];
+                double x = indexer_dot(q_idx, q_scale, k_idx, k_scale, idx_dtype, t, j, s, HI, dI);
                 if (x <= 0.0) continue;               /* ReLU'(x) = 0 for x <= 0 */
                 double wj = (double)w[(int64_t)t * HI + j];
                 dw[(int64_t)t * HI + j] += gi * x;
