@@ -287,6 +287,39 @@ dsa_status_t dsa_cache_append(const void* k_new, const void* v_new, dsa_dtype_t 
                               void* k_cache, void* v_cache, uint8_t* kidx_cache,
                               float* kidx_scale, hipStream_t stream);
 
+/*
+ * ---- Training side: the sparse adaptation stage of report section 2.3.3 ----
+ * The indexer is trained with L = sum_t sum_g KL(p[t,S_t,g] || softmax(I[t,S_t])),
+ * S_t = Omega_t (review page, "核心公式", sparse adaptation loss), keeping only the
+ * post-top-k indexer scores in the forward (report section 5.1.2).
+ */
+
+/*
+ * Indexer scores at the selected positions: vals[t, i] = I[t, idx[t, i]] for t < Tq,
+ * i < topk (the score of dsa_index_scores), -INFINITY where idx[t, i] is -1 or outside
+ * [0, Tk).  FP8 only (dI = 128, 1 <= HI <= 128).  q_idx [Tq, HI, dI], q_scale [Tq],
+ * w [Tq, HI], k_idx [Tk, dI], k_scale [Tk], idx int32 [Tq, topk] -> vals float [Tq, topk].
+ * Computed in fp32 from the decoded codes.  No workspace.
+ */
+dsa_status_t dsa_index_scores_at(const void* q_idx, const float* q_scale, const float* w,
+                                 const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype,
+                                 int Tq, int Tk, int HI, int dI, const int32_t* idx, int topk,
+                                 float* vals, hipStream_t stream);
+
+/*
+ * Backward of dsa_index_scores_at: given g float [Tq, topk] = dL/dvals, the gradients of L
+ * with respect to the dequantised indexer inputs (FP8 rounding taken as the identity,
+ * ReLU'(0) = 0):  dq_idx float [Tq, HI, dI] and dw float [Tq, HI] are written; dk_idx
+ * float [Tk, dI] is ACCUMULATED with atomic adds (zero it first; the order of the adds, and
+ * so the last bits, vary between runs).  Entries of idx that are -1 or out of range
+ * contribute nothing.  FP8 only, dI = 128, 1 <= HI <= 64.  No workspace.
+ */
+dsa_status_t dsa_index_scores_at_bwd(const void* q_idx, const float* q_scale, const float* w,
+                                     const void* k_idx, const float* k_scale,
+                                     dsa_dtype_t idx_dtype, int Tq, int Tk, int HI, int dI,
+                                     const int32_t* idx, int topk, const float* g,
+                                     float* dq_idx, float* dw, float* dk_idx, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_gqa_attn_workspace_size",
            "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
            "dsa_prefill", "dsa_prefill_varlen", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
-           "dsa_quantize_e4m3", "dsa_cache_append"]
+           "dsa_quantize_e4m3", "dsa_cache_append", "dsa_index_scores_at",
+           "dsa_index_scores_at_bwd"]
 
 
 class DSAError(RuntimeError):
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                             P, SZ, P], I),
             "dsa_quantize_e4m3": ([P, I, I, I, P, P, P], I),
             "dsa_cache_append": ([P, P, I, P, I, P, P, I, I, I, I, I, I, I, P, P, P, P, P], I),
+            "dsa_index_scores_at": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P], I),
+            "dsa_index_scores_at_bwd": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P, P, P, P], I),
         }
         for name in EXPORTS:
             fn = getattr(lib, name)
@@ -375,3 +378,41 @@ def prefill_varlen(q, k, v, q_idx, q_scale, w, k_idx, k_scale, cu_seqlens, topk,
     if return_stats:
         res = res + (read_stats(ws, off) if off >= 0 else [0, 0],)
     return res if len(res) > 1 else res[0]
+
+
+# ------------------------------------------------------------------ training side
+
+def dsa_index_scores_at(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, idx, topk,
+                        vals, stream=None):
+    _check(load_library().dsa_index_scores_at(
+        _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale), idx_dtype, Tq, Tk, HI,
+        dI, _ptr(idx), topk, _ptr(vals), _stream(stream)))
+
+
+def dsa_index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, idx,
+                            topk, g, dq_idx, dw, dk_idx, stream=None):
+    _check(load_library().dsa_index_scores_at_bwd(
+        _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale), idx_dtype, Tq, Tk, HI,
+        dI, _ptr(idx), topk, _ptr(g), _ptr(dq_idx), _ptr(dw), _ptr(dk_idx), _stream(stream)))
+
+
+def index_scores_at(q_idx, q_scale, w, k_idx, k_scale, idx, stream=None):
+    """I[t, idx[t, i]] (fp32 [Tq, topk], -inf for padding) of FP8 indexer inputs."""
+    import torch
+    Tq, HI, dI = q_idx.shape
+    vals = torch.empty(idx.shape, dtype=torch.float32, device=q_idx.device)
+    dsa_index_scores_at(q_idx, q_scale, w, k_idx, k_scale, DSA_FP8_E4M3, Tq, k_idx.shape[0], HI,
+                        dI, idx, idx.shape[1], vals, stream)
+    return vals
+
+
+def index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, idx, g, stream=None):
+    """(dq_idx [Tq, HI, dI], dw [Tq, HI], dk_idx [Tk, dI]) fp32 gradients of sum g * vals."""
+    import torch
+    Tq, HI, dI = q_idx.shape
+    dq = torch.empty(Tq, HI, dI, dtype=torch.float32, device=q_idx.device)
+    dw = torch.empty(Tq, HI, dtype=torch.float32, device=q_idx.device)
+    dk = torch.zeros(k_idx.shape[0], dI, dtype=torch.float32, device=q_idx.device)
+    dsa_index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, DSA_FP8_E4M3, Tq, k_idx.shape[0],
+                            HI, dI, idx, idx.shape[1], g, dq, dw, dk, stream)
+    return dq, dw, dk

@@ -658,3 +658,57 @@ DSA_EXPORT dsa_status_t dsa_cache_append(const void* k_new, const void* v_new, d
         B, num_blocks, max_blocks, block_size, k_cache, v_cache, kidx_cache, kidx_scale, stream);
     return e == hipSuccess ? DSA_OK : hip_fail(e, "cache append launch");
 }
+
+namespace {
+
+dsa_status_t check_index_at(const void* q_idx, const float* q_scale, const float* w,
+                            const void* k_idx, const float* k_scale, dsa_dtype_t idx_dtype,
+                            int Tq, int Tk, int HI, int dI, const int32_t* idx, int topk,
+                            int max_heads) {
+    REQUIRE(Tq >= 0 && Tk >= 0 && topk >= 1, DSA_ERR_INVALID_ARG,
+            "bad size (Tq=%d, Tk=%d, topk=%d)", Tq, Tk, topk);
+    REQUIRE(idx_dtype == DSA_FP8_E4M3, DSA_ERR_UNSUPPORTED,
+            "the training-side indexer takes FP8 inputs (got dtype %d)", (int)idx_dtype);
+    REQUIRE(dI == 128, DSA_ERR_UNSUPPORTED, "FP8 indexer needs dI == 128 (got %d)", dI);
+    REQUIRE(HI >= 1 && HI <= max_heads, DSA_ERR_UNSUPPORTED, "HI must be 1..%d (got %d)",
+            max_heads, HI);
+    REQUIRE_PTR(q_idx); REQUIRE_PTR4(q_scale); REQUIRE_PTR4(w); REQUIRE_PTR(k_idx);
+    REQUIRE_PTR4(k_scale); REQUIRE_PTR4(idx);
+    return DSA_OK;
+}
+
+}  // namespace
+
+DSA_EXPORT dsa_status_t dsa_index_scores_at(const void* q_idx, const float* q_scale,
+                                            const float* w, const void* k_idx,
+                                            const float* k_scale, dsa_dtype_t idx_dtype, int Tq,
+                                            int Tk, int HI, int dI, const int32_t* idx, int topk,
+                                            float* vals, hipStream_t stream) {
+    g_err[0] = 0;
+    dsa_status_t st = check_index_at(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI,
+                                     idx, topk, 128);
+    if (st != DSA_OK) return st;
+    REQUIRE_PTR4(vals);
+    const hipError_t e = dsa::launch_index_at(static_cast<const uint8_t*>(q_idx), q_scale, w,
+                                              static_cast<const uint8_t*>(k_idx), k_scale, Tq, Tk,
+                                              HI, idx, topk, vals, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer-at launch");
+}
+
+DSA_EXPORT dsa_status_t dsa_index_scores_at_bwd(const void* q_idx, const float* q_scale,
+                                                const float* w, const void* k_idx,
+                                                const float* k_scale, dsa_dtype_t idx_dtype,
+                                                int Tq, int Tk, int HI, int dI,
+                                                const int32_t* idx, int topk, const float* g,
+                                                float* dq_idx, float* dw, float* dk_idx,
+                                                hipStream_t stream) {
+    g_err[0] = 0;
+    dsa_status_t st = check_index_at(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI,
+                                     idx, topk, 64);
+    if (st != DSA_OK) return st;
+    REQUIRE_PTR4(g); REQUIRE_PTR(dq_idx); REQUIRE_PTR4(dw); REQUIRE_PTR(dk_idx);
+    const hipError_t e = dsa::launch_index_at_bwd(static_cast<const uint8_t*>(q_idx), q_scale, w,
+                                                  static_cast<const uint8_t*>(k_idx), k_scale, Tq,
+                                                  Tk, HI, idx, topk, g, dq_idx, dw, dk_idx, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer backward launch");
+}

@@ -111,4 +111,13 @@ hipError_t launch_cache_append(const void* k_new, const void* v_new, int kv_row_
                                void* v_cache, uint8_t* kidx_cache, float* kidx_scale,
                                hipStream_t stream);
 
+// Training side: indexer scores at the selected positions and their backward (FP8, dI = 128).
+hipError_t launch_index_at(const uint8_t* q_idx, const float* q_scale, const float* w,
+                           const uint8_t* k_idx, const float* k_scale, int T, int Tk, int HI,
+                           const int32_t* idx, int topk, float* vals, hipStream_t stream);
+hipError_t launch_index_at_bwd(const uint8_t* q_idx, const float* q_scale, const float* w,
+                               const uint8_t* k_idx, const float* k_scale, int T, int Tk, int HI,
+                               const int32_t* idx, int topk, const float* g, float* dq, float* dw,
+                               float* dk, hipStream_t stream);
+
 }  // namespace dsa

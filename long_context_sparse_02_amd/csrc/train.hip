@@ -1,0 +1,242 @@
+// train.hip -- the training side of the DSA layer for gfx950: the lightning
+// indexer at the selected positions and its backward.
+//
+// The sparse adaptation stage of the Keye-VL-2.0 report (section 2.3.3; xllm-io
+// review page, "核心公式", sparse adaptation loss) trains the indexer with
+//   L = sum_t sum_g KL( p[t, S_t, g] || softmax(I[t, S_t]) ),  S_t = Omega_t,
+// and the report's section 5.1.2 keeps only the post-top-k indexer scores
+// I[t, Omega_t] in the forward.  These kernels compute those scores and, given
+// dL/dI[t, Omega_t[i]], the gradients with respect to the dequantised indexer
+// inputs q^I, w and k^I (FP8 rounding taken as the identity, ReLU'(0) = 0):
+//   x[t,j,s] = q^I[t,j] . k^I[s],    I[t,s] = sum_j w[t,j] ReLU(x[t,j,s]),
+//   G[t,j,s] = dI[t,s] w[t,j] [x > 0],
+//   dw[t,j]  = sum_s dI[t,s] ReLU(x[t,j,s]),
+//   dq[t,j]  = sum_s G[t,j,s] k^I[s],     dk[s] += sum_j G[t,j,s] q^I[t,j].
+// FP8 inputs (OCP E4M3 codes, per-token fp32 scales), d_I = 128.  The work per
+// row is H^I * d_I multiply-adds per selected position for each product; the
+// kernels run it on the vector ALU in fp32 from the decoded codes (exact
+// values), one workgroup per query row.
+#include "device_common.h"
+#include "internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kIxThreads = 256;
+constexpr int kIxBlock = 256;              // selected positions per block (one per thread)
+constexpr int kIxHIMax = 64;               // indexer heads handled by the backward
+constexpr int kIxGPitch = kIxHIMax + 4;    // LDS row pitch of the per-position head gradients
+
+// OCP E4M3 code -> value (finite codes; the two NaN codes are not expected here)
+__device__ __forceinline__ float e4m3_value(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ uint32_t code_at(const v4i* kc, int e)
+{
+    return ((uint32_t)kc[e >> 4][(e >> 2) & 3] >> ((e & 3) * 8)) & 255u;
+}
+
+// Raw dot products (code values, scales not applied) of the key codes kc (128 codes in
+// registers) with heads j0 .. j0 + 15 of the row's decoded query qv [HI][128] in LDS.
+__device__ __forceinline__ void head_dots16(const float* qv, int j0, int HI, const v4i* kc,
+                                            float* acc)
+{
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.f;
+    for (int e4 = 0; e4 < 32; ++e4) {
+        float kv[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) kv[b] = e4m3_value(code_at(kc, 4 * e4 + b));
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            if (j0 + jj < HI) {
+                const float4 q4 = *reinterpret_cast<const float4*>(qv + (j0 + jj) * 128 + 4 * e4);
+                acc[jj] += q4.x * kv[0] + q4.y * kv[1] + q4.z * kv[2] + q4.w * kv[3];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void load_query(const uint8_t* __restrict__ q_idx, int64_t t, int HI,
+                                           float* qv)
+{
+    const uint8_t* src = q_idx + t * HI * 128;
+    for (int i = threadIdx.x; i < HI * 128; i += kIxThreads) qv[i] = e4m3_value(src[i]);
+}
+
+__device__ __forceinline__ void load_key(const uint8_t* __restrict__ k_idx, int s, v4i* kc)
+{
+    const v4i* src = reinterpret_cast<const v4i*>(k_idx + (int64_t)s * 128);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kc[c] = src[c];
+}
+
+// vals[t, i] = I[t, idx[t, i]]; -inf where the entry is padding or out of range.
+__global__ __launch_bounds__(kIxThreads) void index_at_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int Tk, int HI,
+    const int32_t* __restrict__ idx, int topk, float* __restrict__ vals)
+{
+    __shared__ __attribute__((aligned(16))) float qv[128 * 128];
+    __shared__ float wl[128];
+    const int64_t t = blockIdx.x;
+    load_query(q_idx, t, HI, qv);
+    for (int j = threadIdx.x; j < HI; j += kIxThreads) wl[j] = w[t * HI + j];
+    __syncthreads();
+    const float qs = q_scale[t];
+    for (int i = threadIdx.x; i < topk; i += kIxThreads) {
+        const int s = idx[t * topk + i];
+        float out = -INFINITY;
+        if (s >= 0 && s < Tk) {
+            v4i kc[8];
+            load_key(k_idx, s, kc);
+            const float sc = qs * k_scale[s];
+            float I = 0.f;
+            for (int j0 = 0; j0 < HI; j0 += 16) {
+                float acc[16];
+                head_dots16(qv, j0, HI, kc, acc);
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj)
+                    if (j0 + jj < HI) I += wl[j0 + jj] * fmaxf(acc[jj] * sc, 0.f);
+            }
+            out = I;
+        }
+        vals[t * topk + i] = out;
+    }
+}
+
+// Backward, one workgroup per query row, blocks of 256 selected positions:
+//  A  thread = position p: the H^I dot products, stored as r[p, j] = dI_p ReLU(x[j, p])
+//     in LDS (r != 0 exactly where x > 0, when dI_p != 0, so G[j, p] = dI_p w_j [r != 0]);
+//  B  thread = (d_I column e, half of the block), for each position p of its half:
+//     dk[s_p, e] += q_scale sum_j G[j,p] q[j,e]  (one coalesced atomic add per position
+//     and wave), dq[j, e] += G[j,p] k_scale[p] k[p,e] in registers, and dw[e] += r[p, e]
+//     for the threads whose column is a head index.
+__global__ __launch_bounds__(kIxThreads) void index_at_bwd_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int Tk, int HI,
+    const int32_t* __restrict__ idx, int topk, const float* __restrict__ g,
+    float* __restrict__ dq, float* __restrict__ dw, float* __restrict__ dk)
+{
+    __shared__ __attribute__((aligned(16))) float qv[kIxHIMax * 128];          // 32 KB
+    __shared__ __attribute__((aligned(16))) float rl[kIxBlock * kIxGPitch];    // 68 KB
+    __shared__ __attribute__((aligned(16))) uint8_t kcl[kIxBlock * 128];       // 32 KB
+    __shared__ float ksl[kIxBlock];
+    __shared__ float gl[kIxBlock];
+    __shared__ int sl[kIxBlock];
+    __shared__ __attribute__((aligned(16))) float wl[kIxHIMax];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    load_query(q_idx, t, HI, qv);
+    for (int j = tid; j < kIxHIMax; j += kIxThreads) wl[j] = j < HI ? w[t * HI + j] : 0.f;
+    __syncthreads();
+    const float qs = q_scale[t];
+    const int e = tid & 127, half = tid >> 7;
+    float qcol[kIxHIMax];                       // q[j, e] of this thread's column
+#pragma unroll
+    for (int j = 0; j < kIxHIMax; ++j) qcol[j] = j < HI ? qv[j * 128 + e] : 0.f;
+    float dqa[kIxHIMax];                        // dq[j, e] over this thread's positions
+#pragma unroll
+    for (int j = 0; j < kIxHIMax; ++j) dqa[j] = 0.f;
+    float dwa = 0.f;                            // dw[e] (e < HI) over this thread's positions
+
+    for (int i0 = 0; i0 < topk; i0 += kIxBlock) {
+        {   // A: thread = position i0 + tid
+            const int i = i0 + tid;
+            const int s = i < topk ? idx[t * topk + i] : -1;
+            const bool ok = s >= 0 && s < Tk;
+            const float gi = ok ? g[t * topk + i] : 0.f;
+            float* rrow = rl + tid * kIxGPitch;
+            sl[tid] = ok ? s : -1;
+            gl[tid] = gi;
+            if (ok) {
+                v4i kc[8];
+                load_key(k_idx, s, kc);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) reinterpret_cast<v4i*>(kcl + tid * 128)[c] = kc[c];
+                const float ks = k_scale[s];
+                ksl[tid] = ks;
+                const float sc = qs * ks;
+                for (int j0 = 0; j0 < HI; j0 += 16) {
+                    float acc[16];
+                    head_dots16(qv, j0, HI, kc, acc);
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj)
+                        if (j0 + jj < HI) rrow[j0 + jj] = gi * fmaxf(acc[jj] * sc, 0.f);
+                }
+                for (int j = HI; j < kIxHIMax; ++j) rrow[j] = 0.f;
+            } else {
+                ksl[tid] = 0.f;
+                for (int j = 0; j < kIxHIMax; ++j) rrow[j] = 0.f;
+            }
+        }
+        __syncthreads();
+        // B: thread = column e, positions half*128 .. +128 of the block
+        for (int pp = 0; pp < kIxBlock / 2; ++pp) {
+            const int p = half * (kIxBlock / 2) + pp;
+            const int s = sl[p];
+            if (s < 0) continue;                          // uniform across the wave
+            const float* rrow = rl + p * kIxGPitch;
+            const float gi = gl[p];
+            const float kv = e4m3_value(kcl[p * 128 + e]) * ksl[p];
+            if (e < HI) dwa += rrow[e];
+            float a = 0.f;
+#pragma unroll
+            for (int j = 0; j < kIxHIMax; j += 4) {
+                const float4 r4 = *reinterpret_cast<const float4*>(rrow + j);
+                const float4 w4 = *reinterpret_cast<const float4*>(wl + j);
+                const float g0 = r4.x != 0.f ? gi * w4.x : 0.f, g1 = r4.y != 0.f ? gi * w4.y : 0.f;
+                const float g2 = r4.z != 0.f ? gi * w4.z : 0.f, g3 = r4.w != 0.f ? gi * w4.w : 0.f;
+                a += g0 * qcol[j] + g1 * qcol[j + 1] + g2 * qcol[j + 2] + g3 * qcol[j + 3];
+                dqa[j] += g0 * kv;
+                dqa[j + 1] += g1 * kv;
+                dqa[j + 2] += g2 * kv;
+                dqa[j + 3] += g3 * kv;
+            }
+            atomicAdd(dk + (int64_t)s * 128 + e, a * qs);
+        }
+        __syncthreads();
+    }
+    // the two halves of each column meet in LDS (reusing rl)
+    float* red = rl;                                      // [2][64][128] floats fit in rl
+#pragma unroll
+    for (int j = 0; j < kIxHIMax; ++j) red[(half * kIxHIMax + j) * 128 + e] = dqa[j];
+    if (e < kIxHIMax) red[2 * kIxHIMax * 128 + half * kIxHIMax + e] = dwa;
+    __syncthreads();
+    for (int i = tid; i < HI * 128; i += kIxThreads) {
+        const int j = i >> 7, c = i & 127;
+        dq[(t * HI + j) * 128 + c] = red[j * 128 + c] + red[(kIxHIMax + j) * 128 + c];
+    }
+    for (int j = tid; j < HI; j += kIxThreads)
+        dw[t * HI + j] = red[2 * kIxHIMax * 128 + j] + red[2 * kIxHIMax * 128 + kIxHIMax + j];
+}
+
+}  // namespace
+
+hipError_t launch_index_at(const uint8_t* q_idx, const float* q_scale, const float* w,
+                           const uint8_t* k_idx, const float* k_scale, int T, int Tk, int HI,
+                           const int32_t* idx, int topk, float* vals, hipStream_t stream)
+{
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(index_at_kernel, dim3(T), dim3(kIxThreads), 0, stream, q_idx, q_scale, w,
+                       k_idx, k_scale, Tk, HI, idx, topk, vals);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_at_bwd(const uint8_t* q_idx, const float* q_scale, const float* w,
+                               const uint8_t* k_idx, const float* k_scale, int T, int Tk, int HI,
+                               const int32_t* idx, int topk, const float* g, float* dq, float* dw,
+                               float* dk, hipStream_t stream)
+{
+    if (T == 0) return hipSuccess;
+    if (HI > kIxHIMax) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(index_at_bwd_kernel, dim3(T), dim3(kIxThreads), 0, stream, q_idx, q_scale,
+                       w, k_idx, k_scale, Tk, HI, idx, topk, g, dq, dw, dk);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

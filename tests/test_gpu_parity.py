@@ -839,3 +839,81 @@ def test_prefill_past_the_candidate_range():
     torch.cuda.synchronize()
     assert torch.equal(idx, idx_s)
     assert torch.equal(out, out_s)
+
+
+# ------------------------------------------------------------------ training side
+
+def _int_code_indexer(rng, T, Tk, HI):
+    """FP8 indexer inputs whose codes are the integers -4..4: every dot product is an exact
+    integer in fp32 as in double, so both sides take the same ReLU decisions."""
+    lut = np.array([0x00, 0x38, 0x40, 0x44, 0x48], dtype=np.uint8)   # 0, 1, 2, 3, 4
+
+    def codes(shape):
+        mag = rng.integers(0, 5, shape)
+        sign = rng.integers(0, 2, shape).astype(np.uint8) << 7
+        c = lut[mag] | sign
+        c[mag == 0] = 0
+        return c
+    qc, kc = codes((T, HI, 128)), codes((Tk, 128))
+    qs = rng.uniform(0.5, 2.0, T).astype(np.float32)
+    ks = rng.uniform(0.5, 2.0, Tk).astype(np.float32)
+    w = rng.normal(size=(T, HI)).astype(np.float32)
+    return qc, qs, w, kc, ks
+
+
+def _rand_index_lists(rng, T, Tk, topk, pad=True):
+    idx = np.full((T, topk), -1, dtype=np.int32)
+    for t in range(T):
+        n = topk if not pad or t % 3 else int(rng.integers(1, topk + 1))
+        idx[t, :n] = np.sort(rng.choice(Tk, size=n, replace=False))
+    return idx
+
+
+def _dev(*arrays):
+    return [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in arrays]
+
+
+def test_index_scores_at_vs_oracle():
+    """Scores at the prefill's own selected positions, quantised Gaussian inputs."""
+    cfg = W.scaled(W.PREFILL_32K, L=3000, k=2048, keys="clustered", seed=350)
+    x = W.prefill_inputs(cfg, DEV)
+    _, idx = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
+                         x["k_scale"], cfg.k, cfg.sm_scale, return_idx=True)
+    vals = dsa.index_scores_at(x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"], idx)
+    torch.cuda.synchronize()
+    rows = list(range(0, cfg.L, 7))
+    r_t = torch.tensor(rows)
+    ref = oracle.index_scores_at(to_np(x["q_idx"][r_t]), to_np(x["q_scale"][r_t]),
+                                 to_np(x["w"][r_t]), to_np(x["k_idx"]), to_np(x["k_scale"]),
+                                 oracle.FP8_E4M3, to_np(idx[r_t]))
+    got = to_np(vals[r_t]).astype(np.float64)
+    valid = to_np(idx[r_t]) >= 0
+    assert np.all(got[~valid] == -np.inf) and np.all(np.isfinite(got[valid]))
+    err = np.abs(got - ref)[valid]
+    bound = 1e-3 * np.abs(ref[valid]) + 1e-6 * np.abs(ref[valid]).max()
+    assert np.all(err <= bound), float((err / bound).max())
+
+
+@pytest.mark.parametrize("T,Tk,HI,topk", [(200, 2500, 64, 256), (48, 5000, 64, 2048),
+                                          (37, 900, 16, 300)])
+def test_index_scores_at_bwd_vs_oracle(T, Tk, HI, topk):
+    rng = np.random.default_rng(T + topk)
+    qc, qs, w, kc, ks = _int_code_indexer(rng, T, Tk, HI)
+    idx = _rand_index_lists(rng, T, Tk, topk)
+    g = rng.normal(size=(T, topk)).astype(np.float32)
+    g[idx < 0] = 0.0
+    args = _dev(qc, qs, w, kc, ks, idx, g)
+    vals = dsa.index_scores_at(*args[:6])
+    dq, dw, dk = dsa.index_scores_at_bwd(*args)
+    torch.cuda.synchronize()
+    ref_v = oracle.index_scores_at(qc, qs, w, kc, ks, oracle.FP8_E4M3, idx)
+    rq, rw, rk = oracle.index_scores_bwd(qc, qs, w, kc, ks, oracle.FP8_E4M3, idx, g)
+    valid = idx >= 0
+    np.testing.assert_allclose(to_np(vals)[valid], ref_v[valid], rtol=1e-5,
+                               atol=1e-6 * np.abs(ref_v[valid]).max())
+    for name, got, ref in (("dq", dq, rq), ("dw", dw, rw), ("dk", dk, rk)):
+        got = to_np(got).astype(np.float64)
+        err = np.abs(got - ref).max()
+        scale = np.abs(ref).max()
+        _say("  indexer bwd %s: max err %.3e of max |ref| %.3e" % (name, err, scale))
+        assert err <= 2e-5 * scale, name
