@@ -320,6 +320,41 @@ dsa_status_t dsa_index_scores_at_bwd(const void* q_idx, const float* q_scale, co
                                      const int32_t* idx, int topk, const float* g,
                                      float* dq_idx, float* dw, float* dk_idx, hipStream_t stream);
 
+/*
+ * Sparse attention forward that also keeps what the backward needs: as dsa_sparse_gqa_attn
+ * over contiguous K/V [n_kv, G, d], plus lse float [Tq, Hq] = ln sum_{s in Omega_t}
+ * exp(sm_scale q . K[s]) per query head (-INFINITY for a row with no valid entry).
+ * Workspace: dsa_sparse_gqa_attn_workspace_size() bytes (may be NULL for Tq >= 2048).
+ */
+dsa_status_t dsa_sparse_gqa_attn_lse(const void* q, const void* k, const void* v,
+                                     dsa_dtype_t dtype, int n_kv, const int32_t* idx, int Tq,
+                                     int topk, int Hq, int G, int d, float sm_scale, void* out,
+                                     float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward of the sparse GQA attention, with the sparse indexer loss fused in (report
+ * section 5.1.2: the attention backward recomputes the softmax, so the loss's target is
+ * reduced there).  BF16, contiguous K/V, d = 128.  From the forward's out and lse and the
+ * incoming gradient dout [Tq, Hq, d] (bf16), with P = exp(sm_scale q.K[s] - lse) over the
+ * valid entries s of idx[t, :]:
+ *   dq [Tq, Hq, d] (bf16, written) = sm_scale sum_s dS_s K[s],  dS_s = P_s (dout.V[s] - dout.out);
+ *   dk, dv float [n_kv, G, d] ACCUMULATED with atomic adds (zero them first; the order of the
+ *   adds, and so the last bits, vary between runs): dk[s] += sm_scale sum_h dS_s q_h,
+ *   dv[s] += sum_h P_s dout_h over each group's heads.
+ * When vals float [Tq, topk] (= dsa_index_scores_at at idx) is given (topk <= 2048), also
+ *   kl float [Tq]: sum_g KL(p[t,:,g] || softmax(vals[t,:])) over the valid entries, p[t,s,g]
+ *     the mean of the group's heads' P (report section 2.3.3, sparse adaptation loss),
+ *   dI float [Tq, topk]: d kl[t] / d vals[t, i] = G softmax(vals[t,:])_i - sum_g p[t,i,g]
+ *     (0 for padding), ready for dsa_index_scores_at_bwd.
+ * vals, kl and dI may all be NULL.  No workspace.
+ */
+dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v,
+                                     dsa_dtype_t dtype, int n_kv, const int32_t* idx, int Tq,
+                                     int topk, int Hq, int G, int d, float sm_scale,
+                                     const void* out, const void* dout, const float* lse,
+                                     void* dq, float* dk, float* dv, const float* vals, float* kl,
+                                     float* dI, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
            "dsa_prefill", "dsa_prefill_varlen", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
            "dsa_quantize_e4m3", "dsa_cache_append", "dsa_index_scores_at",
-           "dsa_index_scores_at_bwd"]
+           "dsa_index_scores_at_bwd", "dsa_sparse_gqa_attn_lse", "dsa_sparse_gqa_attn_bwd"]
 
 
 class DSAError(RuntimeError):
@@ -82,6 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_cache_append": ([P, P, I, P, I, P, P, I, I, I, I, I, I, I, P, P, P, P, P], I),
             "dsa_index_scores_at": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P], I),
             "dsa_index_scores_at_bwd": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P, P, P, P], I),
+            "dsa_sparse_gqa_attn_lse": ([P, P, P, I, I, P, I, I, I, I, I, F, P, P, P, SZ, P], I),
+            "dsa_sparse_gqa_attn_bwd": ([P, P, P, I, I, P, I, I, I, I, I, F, P, P, P, P, P, P, P, P,
+                                         P, P], I),
         }
         for name in EXPORTS:
             fn = getattr(lib, name)
@@ -416,3 +419,48 @@ def index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, idx, g, stream=None):
     dsa_index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, DSA_FP8_E4M3, Tq, k_idx.shape[0],
                             HI, dI, idx, idx.shape[1], g, dq, dw, dk, stream)
     return dq, dw, dk
+
+
+def dsa_sparse_gqa_attn_lse(q, k, v, dtype, n_kv, idx, Tq, topk, Hq, G, d, sm_scale, out, lse,
+                            ws=None, ws_bytes=0, stream=None):
+    _check(load_library().dsa_sparse_gqa_attn_lse(
+        _ptr(q), _ptr(k), _ptr(v), dtype, n_kv, _ptr(idx), Tq, topk, Hq, G, d, float(sm_scale),
+        _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dsa_sparse_gqa_attn_bwd(q, k, v, dtype, n_kv, idx, Tq, topk, Hq, G, d, sm_scale, out, dout,
+                            lse, dq, dk, dv, vals=None, kl=None, dI=None, stream=None):
+    _check(load_library().dsa_sparse_gqa_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), dtype, n_kv, _ptr(idx), Tq, topk, Hq, G, d, float(sm_scale),
+        _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(vals), _ptr(kl),
+        _ptr(dI), _stream(stream)))
+
+
+def sparse_gqa_attn_lse(q, k, v, idx, G, sm_scale, stream=None):
+    """(out, lse fp32 [Tq, Hq]) of the attention over contiguous K/V."""
+    import torch
+    Tq, Hq, d = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty(Tq, Hq, dtype=torch.float32, device=q.device)
+    n = dsa_sparse_gqa_attn_workspace_size(Tq, idx.shape[1], Hq, d)
+    ws = workspace(n, q.device) if n else None
+    dsa_sparse_gqa_attn_lse(q, k, v, dtype_code(q), k.shape[0], idx, Tq, idx.shape[1], Hq, G, d,
+                            sm_scale, out, lse, ws, n, stream)
+    return out, lse
+
+
+def sparse_gqa_attn_bwd(q, k, v, idx, G, sm_scale, out, dout, lse, vals=None, stream=None):
+    """(dq bf16, dk fp32, dv fp32[, kl, dI]) of the attention (and the sparse indexer loss when
+    vals, the indexer scores at idx, is given)."""
+    import torch
+    Tq, Hq, d = q.shape
+    dq = torch.empty_like(q)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=q.device)
+    kl = dI = None
+    if vals is not None:
+        kl = torch.empty(Tq, dtype=torch.float32, device=q.device)
+        dI = torch.empty(idx.shape, dtype=torch.float32, device=q.device)
+    dsa_sparse_gqa_attn_bwd(q, k, v, dtype_code(q), k.shape[0], idx, Tq, idx.shape[1], Hq, G, d,
+                            sm_scale, out, dout, lse, dq, dk, dv, vals, kl, dI, stream)
+    return (dq, dk, dv) if vals is None else (dq, dk, dv, kl, dI)

@@ -33,6 +33,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kStep = 32;                 // selected positions per step
 constexpr int kVPitch = 136;              // LDS row pitch of the V tile (bf16 elements)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct KVStep {
     v4i kk[8];                            // K rows (lane >> 4) + 4 it, 16 bytes each
@@ -202,6 +203,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
                     const uint32_t hi = f32_to_bf16_bits(o[dt][2] * inv) | ((uint32_t)f32_to_bf16_bits(o[dt][3] * inv) << 16);
                     *reinterpret_cast<uint2*>(outp + dt * 16 + 4 * grp) = make_uint2(lo, hi);
                 }
+                // natural-log log-sum-exp of the logits (m_run is in the scaled log2 domain)
+                if (p.lse && grp == 0) p.lse[(int64_t)row * p.Hq + head] = (m_run + __log2f(l)) * kLn2;
             } else {
                 float* part = partials + (((int64_t)row * nsplit + split) * p.Hq + head) * (128 + 2);
 #pragma unroll
@@ -211,6 +214,267 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
             }
         }
     }
+}
+
+// Backward of the bf16 attention (contiguous K/V), with the sparse indexer loss fused in
+// (Keye-VL-2.0 report section 5.1.2: the sparse-attention backward already recomputes the
+// softmax, so the indexer's KL target is reduced there instead of being stored).  One
+// workgroup per query row, wave = KV group as in the forward.  Per step of 32 selected
+// positions a wave gathers the K and V rows of its group into LDS and, from the forward's
+// log-sum-exp,
+//   S^T = K q^T, dP^T = V dO^T              (bf16 matrix core, rows = positions)
+//   P = exp(S - lse), dS = P (dP - D),      D = dO . O per head
+//   dq^T += K^T dS                          (kept in registers for the whole row)
+//   dV^T = dO^T P^T, dK^T = q^T dS^T        (per 16 positions; P and dS pass through LDS
+//                                            to become B operands, the results through LDS
+//                                            to become 64-lane atomic adds of whole rows)
+// and, when the indexer scores at Omega_t are given, the group-mean attention
+// p[t,s,g] = mean_h P goes into an LDS row sum; at the end of the row the kernel writes
+// dI = G softmax(I[t,Omega_t]) - sum_g p and the row's KL sum_g sum_s p ln(p / softmax(I)).
+constexpr int kBwdMaxTopk = 2048;
+constexpr int kStagePitch = 132;           // floats per staged position row
+
+__global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t vt[kAttnWaves][kStep][kVPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t kt[kAttnWaves][kStep][kVPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t pst[kAttnWaves][2][kStep][16];
+    __shared__ float psum[kBwdMaxTopk];
+    __shared__ float red[kAttnWaves];
+    const int row = xcd_remap(blockIdx.x, gridDim.x);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int hpg = p.Hq / p.G;
+    const int topk = p.topk;
+    const bool kl_on = p.vals != nullptr;
+    const int32_t* __restrict__ idx_row = p.idx + (int64_t)row * topk;
+    const float scale2 = p.sm_scale * kLog2e;
+    const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
+    const uint16_t* __restrict__ O = static_cast<const uint16_t*>(p.out);
+    const uint16_t* __restrict__ dO = static_cast<const uint16_t*>(p.dout);
+    AttnArgs a;
+    a.q = p.q; a.k = p.k; a.v = p.v; a.out = nullptr; a.idx = p.idx; a.Tq = p.Tq; a.topk = topk;
+    a.Hq = p.Hq; a.G = p.G; a.d = 128; a.sm_scale = p.sm_scale; a.n_kv = p.n_kv;
+    a.block_table = nullptr; a.max_blocks = 0; a.block_size = 0; a.row_seq = nullptr;
+    a.seq_lens = nullptr; a.bf16 = 1;
+    const int64_t len = p.n_kv > 0 ? p.n_kv : 0;
+    const int k_end = len > 0 ? topk : 0;
+
+    // the indexer's softmax over the row's valid entries: its max and log normaliser
+    float mI = 0.f, lnZ = 0.f;
+    if (kl_on) {
+        float m = -INFINITY;
+        for (int i = tid; i < topk; i += 256) {
+            psum[i] = 0.f;
+            const int s = idx_row[i];
+            if (s >= 0 && s < len) m = fmaxf(m, p.vals[(int64_t)row * topk + i]);
+        }
+        m = wave_max(m);
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
+        float z = 0.f;
+        for (int i = tid; i < topk; i += 256) {
+            const int s = idx_row[i];
+            if (s >= 0 && s < len) z += expf(p.vals[(int64_t)row * topk + i] - m);
+        }
+        z = wave_sum(z);
+        if (lane == 0) red[wave] = z;
+        __syncthreads();
+        z = red[0] + red[1] + red[2] + red[3];
+        __syncthreads();
+        mI = m;
+        lnZ = logf(z);
+    }
+
+    float plogp = 0.f;                                  // sum of p ln p over this wave's groups
+    for (int g = wave; g < p.G; g += kAttnWaves) {
+        const int head = g * hpg + col;
+        const bool hv = col < hpg;
+        v8bf qb[4], dob[4];
+        float D = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            v4i x = {0, 0, 0, 0}, y = {0, 0, 0, 0}, o = {0, 0, 0, 0};
+            if (hv) {
+                const int64_t off = ((int64_t)row * p.Hq + head) * 128 + (4 * m + grp) * 8;
+                x = *reinterpret_cast<const v4i*>(Q + off);
+                y = *reinterpret_cast<const v4i*>(dO + off);
+                o = *reinterpret_cast<const v4i*>(O + off);
+            }
+            qb[m] = __builtin_bit_cast(v8bf, x);
+            dob[m] = __builtin_bit_cast(v8bf, y);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                D += bf16_bits_to_f32((uint16_t)y[j]) * bf16_bits_to_f32((uint16_t)o[j]) +
+                     bf16_bits_to_f32((uint16_t)((uint32_t)y[j] >> 16)) *
+                         bf16_bits_to_f32((uint16_t)((uint32_t)o[j] >> 16));
+        }
+        D += __shfl_xor(D, 16, 64);
+        D += __shfl_xor(D, 32, 64);
+        const float lse2 = hv ? p.lse[(int64_t)row * p.Hq + head] * kLog2e : 0.f;
+        // A operands of dK^T = q^T dS^T and dV^T = dO^T P^T: row = head dim, k = head 8 grp + j
+        v8bf qT[8], doT[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            v8s xq, xo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int h = 8 * grp + j;
+                const bool ok = grp < 2 && h < hpg;
+                const int64_t off = ((int64_t)row * p.Hq + g * hpg + (ok ? h : 0)) * 128 + dt * 16 + col;
+                xq[j] = ok ? (short)Q[off] : (short)0;
+                xo[j] = ok ? (short)dO[off] : (short)0;
+            }
+            qT[dt] = __builtin_bit_cast(v8bf, xq);
+            doT[dt] = __builtin_bit_cast(v8bf, xo);
+        }
+        v4f dqa[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) dqa[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+        uint16_t* ktile = &kt[wave][0][0];
+        uint16_t* vtile = &vt[wave][0][0];
+        float* stage = reinterpret_cast<float*>(ktile);  // 16 x kStagePitch floats fit the K tile
+
+        for (int kb0 = 0; kb0 < k_end; kb0 += kStep) {
+            KVStep cur;
+            load_step<false>(a, idx_row, kb0, k_end, 0, len, g, lane, cur);
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int off = ((lane >> 4) + 4 * it) * kVPitch + (lane & 15) * 8;
+                *reinterpret_cast<v4i*>(ktile + off) = cur.kk[it];
+                *reinterpret_cast<v4i*>(vtile + off) = cur.vv[it];
+            }
+            const uint32_t valid = cur.valid;
+            __builtin_amdgcn_wave_barrier();
+            v4f sa = {0.f, 0.f, 0.f, 0.f}, sb = sa, pa = sa, pb = sa;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int c = (4 * m + grp) * 8;
+                const v4i ka = *reinterpret_cast<const v4i*>(ktile + col * kVPitch + c);
+                const v4i kb = *reinterpret_cast<const v4i*>(ktile + (16 + col) * kVPitch + c);
+                const v4i va = *reinterpret_cast<const v4i*>(vtile + col * kVPitch + c);
+                const v4i vb = *reinterpret_cast<const v4i*>(vtile + (16 + col) * kVPitch + c);
+                sa = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, ka), qb[m], sa);
+                sb = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, kb), qb[m], sb);
+                pa = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, va), dob[m], pa);
+                pb = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, vb), dob[m], pb);
+            }
+            float P[8], dS[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * grp + i;
+                const bool va_ = hv && ((valid >> r) & 1u), vb_ = hv && ((valid >> (16 + r)) & 1u);
+                P[i] = va_ ? exp2f(sa[i] * scale2 - lse2) : 0.f;
+                P[4 + i] = vb_ ? exp2f(sb[i] * scale2 - lse2) : 0.f;
+                dS[i] = P[i] * (pa[i] - D);
+                dS[4 + i] = P[4 + i] * (pb[i] - D);
+            }
+            if (kl_on) {
+                float ps[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ps[i] = P[i];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) ps[i] += __shfl_xor(ps[i], o, 64);
+                if (col == 0) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int r = i < 4 ? 4 * grp + i : 16 + 4 * grp + (i - 4);
+                        if ((valid >> r) & 1u) {
+                            const float pg = ps[i] / (float)hpg;
+                            atomicAdd(&psum[kb0 + r], pg);
+                            if (pg > 0.f) plogp += pg * logf(pg);
+                        }
+                    }
+                }
+            }
+            // dq^T += K^T dS
+            v8s dsb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dsb[i] = (short)f32_to_bf16_bits(dS[i]);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                v8s kta;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kta[j] = (short)ktile[(4 * grp + j) * kVPitch + dt * 16 + col];
+                    kta[4 + j] = (short)ktile[(16 + 4 * grp + j) * kVPitch + dt * 16 + col];
+                }
+                dqa[dt] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, kta),
+                                             __builtin_bit_cast(v8bf, dsb), dqa[dt]);
+            }
+            // P and dS as [position][head] tiles
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pst[wave][0][4 * grp + i][col] = f32_to_bf16_bits(P[i]);
+                pst[wave][0][16 + 4 * grp + i][col] = f32_to_bf16_bits(P[4 + i]);
+                pst[wave][1][4 * grp + i][col] = (uint16_t)dsb[i];
+                pst[wave][1][16 + 4 * grp + i][col] = (uint16_t)dsb[4 + i];
+            }
+            __builtin_amdgcn_wave_barrier();
+            // dV (mat 0) and dK (mat 1), 16 positions at a time
+#pragma unroll
+            for (int mat = 0; mat < 2; ++mat) {
+                float* __restrict__ dst_base = mat ? p.dk : p.dv;
+                const float mul = mat ? p.sm_scale : 1.f;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    v4i bx = {0, 0, 0, 0};
+                    if (grp < 2) bx = *reinterpret_cast<const v4i*>(&pst[wave][mat][pt * 16 + col][8 * grp]);
+                    const v8bf bop = __builtin_bit_cast(v8bf, bx);
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) {
+                        const v4f acc = mfma_bf16_16x16x32(mat ? qT[dt] : doT[dt], bop,
+                                                           v4f{0.f, 0.f, 0.f, 0.f});
+                        *reinterpret_cast<v4f*>(stage + col * kStagePitch + dt * 16 + 4 * grp) = acc * mul;
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    for (int r = 0; r < 16; ++r) {
+                        const int pos = pt * 16 + r;
+                        if (!((valid >> pos) & 1u)) continue;       // uniform
+                        const int s = idx_row[kb0 + pos];
+                        float* dst = dst_base + ((int64_t)s * p.G + g) * 128;
+                        atomicAdd(dst + lane, stage[r * kStagePitch + lane]);
+                        atomicAdd(dst + 64 + lane, stage[r * kStagePitch + 64 + lane]);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                }
+            }
+        }
+        if (hv) {
+            uint16_t* dqp = static_cast<uint16_t*>(p.dq) + ((int64_t)row * p.Hq + head) * 128;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const v4f r = dqa[dt] * p.sm_scale;
+                const uint32_t lo = f32_to_bf16_bits(r[0]) | ((uint32_t)f32_to_bf16_bits(r[1]) << 16);
+                const uint32_t hi = f32_to_bf16_bits(r[2]) | ((uint32_t)f32_to_bf16_bits(r[3]) << 16);
+                *reinterpret_cast<uint2*>(dqp + dt * 16 + 4 * grp) = make_uint2(lo, hi);
+            }
+        }
+    }
+    if (!kl_on) return;
+    plogp = wave_sum(plogp);
+    __syncthreads();                                    // psum complete
+    if (lane == 0) red[wave] = plogp;
+    float cross = 0.f;
+    for (int i = tid; i < topk; i += 256) {
+        const int s = idx_row[i];
+        const bool ok = s >= 0 && s < len;
+        const float lq = ok ? p.vals[(int64_t)row * topk + i] - mI - lnZ : 0.f;   // ln softmax(I)
+        if (ok) cross += psum[i] * lq;
+        p.dI[(int64_t)row * topk + i] = ok ? (float)p.G * expf(lq) - psum[i] : 0.f;
+    }
+    cross = wave_sum(cross);
+    __syncthreads();
+    const float total_plogp = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    if (lane == 0) red[wave] = cross;
+    __syncthreads();
+    if (tid == 0) p.kl[row] = total_plogp - (red[0] + red[1] + red[2] + red[3]);
 }
 
 // fp32 kernel (vector ALU; exact-ish reference-grade path).  One workgroup per
@@ -306,6 +570,7 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs p, int ns
                 const float inv = l > 0.f ? 1.f / l : 0.f;
                 float* outp = static_cast<float*>(p.out) + ((int64_t)row * p.Hq + g * hpg + h) * 128;
                 *reinterpret_cast<float2*>(outp + 2 * lane) = make_float2(o0[h] * inv, o1[h] * inv);
+                if (p.lse && lane == 0) p.lse[(int64_t)row * p.Hq + g * hpg + h] = m_run[h] + logf(l);
             } else {
                 float* part = partials + (((int64_t)row * nsplit + split) * p.Hq + g * hpg + h) * (128 + 2);
                 part[2 * lane] = o0[h];
@@ -321,7 +586,8 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs p, int ns
 // Merge the nsplit partial softmax results of each (row, head).
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ partials,
                                                            int nsplit, int Hq, int bf16,
-                                                           void* __restrict__ out)
+                                                           void* __restrict__ out,
+                                                           float* __restrict__ lse)
 {
     const int row = blockIdx.x / Hq, head = blockIdx.x % Hq;
     const int dim = threadIdx.x;
@@ -338,6 +604,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
         }
     }
     const float r = L > 0.f ? acc / L : 0.f;
+    if (lse && dim == 0) lse[(int64_t)row * Hq + head] = M == -INFINITY ? -INFINITY : (M + __log2f(L)) * kLn2;
     const int64_t o = ((int64_t)row * Hq + head) * 128 + dim;
     if (bf16) static_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(r);
     else static_cast<float*>(out)[o] = r;
@@ -389,7 +656,15 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int nsplit, float* partials, hi
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nsplit == 1) return err;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Tq * a.Hq)), dim3(128), 0, stream, partials,
-                       nsplit, a.Hq, a.bf16, a.out);
+                       nsplit, a.Hq, a.bf16, a.out, a.lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, hipStream_t stream)
+{
+    if (a.Tq == 0) return hipSuccess;
+    if (a.vals && a.topk > kBwdMaxTopk) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sparse_attn_bwd_kernel, dim3((unsigned)a.Tq), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

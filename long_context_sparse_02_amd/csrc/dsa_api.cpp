@@ -712,3 +712,51 @@ DSA_EXPORT dsa_status_t dsa_index_scores_at_bwd(const void* q_idx, const float* 
                                                   Tk, HI, idx, topk, g, dq_idx, dw, dk_idx, stream);
     return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer backward launch");
 }
+
+DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_lse(const void* q, const void* k, const void* v,
+                                                dsa_dtype_t dtype, int n_kv, const int32_t* idx,
+                                                int Tq, int topk, int Hq, int G, int d,
+                                                float sm_scale, void* out, float* lse, void* ws,
+                                                size_t ws_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    dsa_status_t st = check_attn_shape(dtype, Hq, G, d, topk);
+    if (st != DSA_OK) return st;
+    REQUIRE(Tq >= 0 && n_kv >= 0, DSA_ERR_INVALID_ARG, "negative size (Tq=%d, n_kv=%d)", Tq, n_kv);
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR4(idx); REQUIRE_PTR(out);
+    REQUIRE_PTR4(lse); REQUIRE_OPT_PTR(ws);
+    dsa::AttnArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.idx = idx; a.Tq = Tq; a.topk = topk; a.Hq = Hq;
+    a.G = G; a.d = d; a.sm_scale = sm_scale; a.n_kv = n_kv; a.block_table = nullptr;
+    a.max_blocks = 0; a.block_size = 0; a.row_seq = nullptr; a.seq_lens = nullptr;
+    a.bf16 = dtype == DSA_BF16; a.lse = lse;
+    int nsplit = dsa::attn_num_splits(Tq, topk);
+    if (!ws || ws_bytes < dsa::attn_partials_bytes(Tq, nsplit, Hq, d)) nsplit = 1;
+    const hipError_t e = dsa::launch_sparse_attn(a, nsplit, static_cast<float*>(ws), stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "attention launch");
+}
+
+DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v,
+                                                dsa_dtype_t dtype, int n_kv, const int32_t* idx,
+                                                int Tq, int topk, int Hq, int G, int d,
+                                                float sm_scale, const void* out,
+                                                const void* dout, const float* lse, void* dq,
+                                                float* dk, float* dv, const float* vals,
+                                                float* kl, float* dI, hipStream_t stream) {
+    g_err[0] = 0;
+    dsa_status_t st = check_attn_shape(dtype, Hq, G, d, topk);
+    if (st != DSA_OK) return st;
+    REQUIRE(dtype == DSA_BF16, DSA_ERR_UNSUPPORTED, "the attention backward takes BF16 (got %d)",
+            (int)dtype);
+    REQUIRE(Tq >= 0 && n_kv >= 0, DSA_ERR_INVALID_ARG, "negative size (Tq=%d, n_kv=%d)", Tq, n_kv);
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR4(idx); REQUIRE_PTR(out);
+    REQUIRE_PTR(dout); REQUIRE_PTR4(lse); REQUIRE_PTR(dq); REQUIRE_PTR4(dk); REQUIRE_PTR4(dv);
+    if (vals) {
+        REQUIRE(topk <= 2048, DSA_ERR_UNSUPPORTED,
+                "the fused indexer loss takes topk <= 2048 (got %d)", topk);
+        REQUIRE_PTR4(vals); REQUIRE_PTR4(kl); REQUIRE_PTR4(dI);
+    }
+    const dsa::AttnBwdArgs a{q, k, v, out, dout, lse, idx, Tq, topk, Hq, G, n_kv, sm_scale,
+                             dq, dk, dv, vals, vals ? kl : nullptr, vals ? dI : nullptr};
+    const hipError_t e = dsa::launch_sparse_attn_bwd(a, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "attention backward launch");
+}

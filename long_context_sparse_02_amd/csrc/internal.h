@@ -93,7 +93,20 @@ struct AttnArgs {
     const int32_t* block_table; int max_blocks; int block_size;
     const int32_t* row_seq; const int32_t* seq_lens;
     int bf16;                                  // 1: bf16 I/O, 0: fp32 I/O
+    float* lse = nullptr;                      // optional [Tq, Hq]: natural-log log-sum-exp
 };
+// Backward of the bf16 attention over contiguous K/V (d = 128, heads per group <= 16), with
+// the sparse indexer loss fused in when vals is set (topk <= 2048 then).  dq is written (bf16);
+// dk, dv (fp32 [n_kv, G, d]) are accumulated with atomic adds; kl [Tq] and dI [Tq, topk] are
+// written when vals [Tq, topk] (the indexer scores at idx) is given.
+struct AttnBwdArgs {
+    const void* q; const void* k; const void* v; const void* out; const void* dout;
+    const float* lse; const int32_t* idx; int Tq; int topk; int Hq; int G; int n_kv;
+    float sm_scale;
+    void* dq; float* dk; float* dv;
+    const float* vals; float* kl; float* dI;
+};
+hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 // Splits used for a given shape when a workspace is available (1 = no split).
 int attn_num_splits(int Tq, int topk);
 size_t attn_partials_bytes(int Tq, int nsplit, int Hq, int d);

@@ -870,7 +870,13 @@ def _rand_index_lists(rng, T, Tk, topk, pad=True):
 
 
 def _dev(*arrays):
-    return [None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in arrays]
+    def one(a):
+        if a is None:
+            return None
+        if isinstance(a, torch.Tensor):
+            return a.contiguous().to(DEV)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return [one(a) for a in arrays]
 
 
 def test_index_scores_at_vs_oracle():
@@ -917,3 +923,60 @@ def test_index_scores_at_bwd_vs_oracle(T, Tk, HI, topk):
         scale = np.abs(ref).max()
         _say("  indexer bwd %s: max err %.3e of max |ref| %.3e" % (name, err, scale))
         assert err <= 2e-5 * scale, name
+
+
+def _attn_train_case(rng, T, Tk, Hq, G, topk, pad=True):
+    s = 1.0 / math.sqrt(128)
+    q = torch.from_numpy(rng.normal(size=(T, Hq, 128)) * s).bfloat16()
+    k = torch.from_numpy(rng.normal(size=(Tk, G, 128)) * s).bfloat16()
+    v = torch.from_numpy(rng.normal(size=(Tk, G, 128))).bfloat16()
+    dout = torch.from_numpy(rng.normal(size=(T, Hq, 128))).bfloat16()
+    idx = _rand_index_lists(rng, T, Tk, topk, pad)
+    return q, k, v, dout, idx
+
+
+@pytest.mark.parametrize("T,Tk,topk", [(300, 3000, 256), (37, 5000, 2048)])
+def test_attn_lse_vs_oracle(T, Tk, topk):
+    """Forward with its log-sum-exp, unsplit (300 rows) and split over workgroups (37 rows)."""
+    rng = np.random.default_rng(T + 7)
+    q, k, v, _, idx = _attn_train_case(rng, T, Tk, 32, 4, topk)
+    qd, kd, vd, idd = _dev(q, k, v, idx)
+    out, lse = dsa.sparse_gqa_attn_lse(qd, kd, vd, idd, 4, 1 / math.sqrt(128))
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.attn_lse(q, k, v, oracle.BF16, idx, 4, 1 / math.sqrt(128))
+    check_attn(bf16_to_f64(to_np(out)), ref_out, "bf16", "attn lse T=%d" % T)
+    err = np.abs(to_np(lse).astype(np.float64) - ref_lse).max()
+    _say("  lse max err %.2e" % err)
+    assert err <= 1e-4 * max(1.0, np.abs(ref_lse).max())
+
+
+@pytest.mark.parametrize("T,Tk,topk,G", [(64, 700, 256, 4), (24, 5000, 2048, 4), (40, 900, 100, 2)])
+def test_attn_bwd_and_indexer_kl_vs_oracle(T, Tk, topk, G):
+    """Attention backward (dq, and dk / dv summed over every row) and the fused sparse
+    indexer loss against the oracle.  Errors are bounded by the bf16 rounding of P and dS
+    that feed the matrix products (2^-9 relative per term) and of dq's output: 1e-2 of the
+    largest reference magnitude elementwise."""
+    rng = np.random.default_rng(T + topk)
+    Hq = 32
+    sm = 1 / math.sqrt(128)
+    q, k, v, dout, idx = _attn_train_case(rng, T, Tk, Hq, G, topk)
+    vals = rng.normal(size=(T, topk)).astype(np.float32)
+    vals[idx < 0] = -np.inf
+    qd, kd, vd, dod, idd, vald = _dev(q, k, v, dout, idx, vals)
+    out, lse = dsa.sparse_gqa_attn_lse(qd, kd, vd, idd, G, sm)
+    dq, dk, dv, kl, dI = dsa.sparse_gqa_attn_bwd(qd, kd, vd, idd, G, sm, out, dod, lse, vals=vald)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd(q, k, v, oracle.BF16, idx, G, sm, dout)
+    rkl, rdI = oracle.indexer_kl(q, k, oracle.BF16, idx, G, sm, vals.astype(np.float64))
+    for name, got, ref in (("dq", bf16_to_f64(to_np(dq)), rq), ("dk", to_np(dk), rk),
+                           ("dv", to_np(dv), rv)):
+        err = np.abs(np.asarray(got, dtype=np.float64) - ref).max()
+        _say("  attn bwd %s: max err %.3e of max |ref| %.3e" % (name, err, np.abs(ref).max()))
+        assert err <= 1e-2 * np.abs(ref).max(), name
+    err_kl = np.abs(to_np(kl).astype(np.float64) - rkl).max()
+    err_dI = np.abs(to_np(dI).astype(np.float64) - rdI).max()
+    _say("  kl max err %.3e (max %.3e), dI max err %.3e (max %.3e)"
+         % (err_kl, np.abs(rkl).max(), err_dI, np.abs(rdI).max()))
+    assert err_kl <= 1e-3 * np.abs(rkl).max() + 1e-6
+    assert err_dI <= 1e-3 * np.abs(rdI).max() + 1e-7
+    assert np.all(to_np(dI)[idx < 0] == 0)
