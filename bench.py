@@ -19,7 +19,10 @@ attention gather); the dominant kernel, the attention, which both paths run
 identically, is reported as ``roofline``.  Both paths must give identical
 index sets and outputs.  The CPU oracle, timed on a stratified sample of
 query rows, is reported as ``cpu_baseline``.  A packed batch of 16 sequences of 2K..14K tokens
-through dsa_prefill_varlen is reported under ``packed_prefill``.
+through dsa_prefill_varlen is reported under ``packed_prefill``, and one sparse-adaptation
+training step of the 32K layer (indexer scores at the selected positions, attention forward
+with log-sum-exp, attention backward with the fused indexer loss, indexer backward) under
+``train_step``.
 """
 from __future__ import annotations
 
@@ -51,6 +54,7 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=96)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-packed", action="store_true")
+    p.add_argument("--no-train", action="store_true")
     p.add_argument("--profile-kernel", choices=["index", "topk", "attn"], default=None,
                    help="profiling driver: run only this kernel on one chunk of the workload "
                         "(--profile-chunk, default the last) --profile-reps times, print nothing else")
@@ -358,6 +362,80 @@ def run_packed_bench(args, dsa, W, torch):
     return res
 
 
+# fp32 atomic adds measured on this GPU with 64-lane rows of consecutive floats (a plain
+# kernel adding into random 512-byte rows of a 64 MiB array): the ceiling of the scatter of
+# dK / dV and dk^I in the backward
+ATOMIC_FLOATS_PER_S = 330e9
+
+
+def run_train_bench(args, dsa, W, torch):
+    """One sparse-adaptation training step of the layer at 32K (report section 2.3.3): the
+    indexer scores at the selected positions, the attention forward with its log-sum-exp,
+    the attention backward with the fused indexer loss, and the indexer backward."""
+    cfg = W.PREFILL_32K
+    log("generating", cfg.name, "(training step)")
+    x = W.prefill_inputs(cfg, "cuda")
+    L, k, G = cfg.L, cfg.k, cfg.G
+    _, idx = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
+                         x["k_scale"], k, cfg.sm_scale, return_idx=True)
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed + 2000)
+    dout = torch.randn(x["q"].shape, generator=gen, device="cuda").bfloat16()
+    out = torch.empty_like(x["q"])
+    lse = torch.empty(L, cfg.Hq, dtype=torch.float32, device="cuda")
+    vals = torch.empty(L, k, dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(x["q"])
+    dk = torch.empty(x["k"].shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    kl = torch.empty(L, dtype=torch.float32, device="cuda")
+    dI = torch.empty(L, k, dtype=torch.float32, device="cuda")
+    dqi = torch.empty(x["q_idx"].shape, dtype=torch.float32, device="cuda")
+    dw = torch.empty(x["w"].shape, dtype=torch.float32, device="cuda")
+    dki = torch.empty(x["k_idx"].shape, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    BF, F8 = dsa.DSA_BF16, dsa.DSA_FP8_E4M3
+    parts = {
+        "index_at": lambda: dsa.dsa_index_scores_at(
+            x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"], F8, L, L, cfg.HI, cfg.dI,
+            idx, k, vals, stream),
+        "attn_fwd_lse": lambda: dsa.dsa_sparse_gqa_attn_lse(
+            x["q"], x["k"], x["v"], BF, L, idx, L, k, cfg.Hq, G, cfg.d, cfg.sm_scale, out, lse,
+            None, 0, stream),
+        "attn_bwd_kl": lambda: (dk.zero_(), dv.zero_(), dsa.dsa_sparse_gqa_attn_bwd(
+            x["q"], x["k"], x["v"], BF, L, idx, L, k, cfg.Hq, G, cfg.d, cfg.sm_scale, out, dout,
+            lse, dq, dk, dv, vals, kl, dI, stream)),
+        "index_at_bwd": lambda: (dki.zero_(), dsa.dsa_index_scores_at_bwd(
+            x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"], F8, L, L, cfg.HI, cfg.dI,
+            idx, k, dI, dqi, dw, dki, stream)),
+    }
+    for _ in range(max(1, args.warmup)):
+        for f in parts.values():
+            f()
+    torch.cuda.synchronize()
+    reps = max(2, args.steps)
+    ms = {}
+    for name, f in parts.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / reps
+    n_sel = int(torch.clamp(torch.arange(1, L + 1, device="cuda"), max=k).sum())
+    atom_attn = n_sel * G * cfg.d * 2
+    atom_ix = n_sel * cfg.dI
+    step = sum(ms.values())
+    res = {"workload": cfg.name + "_train_step", "tokens": L, "selected_pairs": n_sel,
+           "ms": {n: round(v, 3) for n, v in ms.items()}, "ms_per_step": round(step, 3),
+           "tokens_per_s": round(L / (step * 1e-3), 1),
+           "attn_bwd_atomic_frac": round(atom_attn / (ms["attn_bwd_kl"] * 1e-3) / ATOMIC_FLOATS_PER_S, 4),
+           "index_bwd_atomic_frac": round(atom_ix / (ms["index_at_bwd"] * 1e-3) / ATOMIC_FLOATS_PER_S, 4),
+           "mean_kl": round(float(kl.mean()), 5)}
+    del x, idx, out, lse, vals, dq, dk, dv, kl, dI, dqi, dw, dki, dout
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args, cfg, x, torch):
     """The oracle on a stratified sample of query rows of the same workload."""
     import numpy as np
@@ -440,6 +518,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_packed:
         result["packed_prefill"] = run_packed_bench(args, dsa, W, torch)
+    if not args.no_train:
+        result["train_step"] = run_train_bench(args, dsa, W, torch)
     if not args.no_decode:
         result["decode"] = [run_decode_bench(args, dsa, W, torch, n)
                             for n in args.decode_workloads.split(",") if n]

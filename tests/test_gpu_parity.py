@@ -980,3 +980,52 @@ def test_attn_bwd_and_indexer_kl_vs_oracle(T, Tk, topk, G):
     assert err_kl <= 1e-3 * np.abs(rkl).max() + 1e-6
     assert err_dI <= 1e-3 * np.abs(rdI).max() + 1e-7
     assert np.all(to_np(dI)[idx < 0] == 0)
+
+
+def test_train_step_full_size_sampled():
+    """The 32K layer's training step as the benchmark runs it: sampled rows of dq, the
+    indexer loss and dI, and of the indexer's dq^I and dw against the oracle; dV against its
+    global invariant (each row's probabilities sum to 1, so summing dV over positions gives
+    the sum of dout over rows and the group's heads)."""
+    cfg = W.PREFILL_32K
+    _say("training step", cfg.name)
+    x = W.prefill_inputs(cfg, DEV)
+    L, k, G, Hq = cfg.L, cfg.k, cfg.G, cfg.Hq
+    _, idx = dsa.prefill(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
+                         x["k_scale"], k, cfg.sm_scale, return_idx=True)
+    gen = torch.Generator(device=DEV).manual_seed(cfg.seed + 2000)
+    dout = torch.randn(x["q"].shape, generator=gen, device=DEV).bfloat16()
+    vals = dsa.index_scores_at(x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"], idx)
+    out, lse = dsa.sparse_gqa_attn_lse(x["q"], x["k"], x["v"], idx, G, cfg.sm_scale)
+    dq, dk, dv, kl, dI = dsa.sparse_gqa_attn_bwd(x["q"], x["k"], x["v"], idx, G, cfg.sm_scale,
+                                                 out, dout, lse, vals=vals)
+    dqi, dw, dki = dsa.index_scores_at_bwd(x["q_idx"], x["q_scale"], x["w"], x["k_idx"],
+                                           x["k_scale"], idx, dI)
+    torch.cuda.synchronize()
+    rows = [0, 1, 2047, 2048, 9000, 20011, L - 1]
+    r_t = torch.tensor(rows)
+    ki, vi = to_np(x["k"]), to_np(x["v"])
+    q_r, do_r, id_r = to_np(x["q"][r_t]), to_np(dout[r_t]), to_np(idx[r_t])
+    rq, _, _ = oracle.attn_bwd(q_r, ki, vi, oracle.BF16, id_r, G, cfg.sm_scale, do_r)
+    err = np.abs(bf16_to_f64(to_np(dq[r_t])) - rq).max()
+    _say("  dq sampled rows: max err %.3e of max |ref| %.3e" % (err, np.abs(rq).max()))
+    assert err <= 1e-2 * np.abs(rq).max()
+    vals_r = to_np(vals[r_t]).astype(np.float64)
+    rkl, rdI = oracle.indexer_kl(q_r, ki, oracle.BF16, id_r, G, cfg.sm_scale, vals_r)
+    np.testing.assert_allclose(to_np(kl[r_t]), rkl, rtol=1e-3, atol=1e-5)
+    assert np.abs(to_np(dI[r_t]) - rdI).max() <= 1e-3 * np.abs(rdI).max() + 1e-7
+    g_r = to_np(dI[r_t]).astype(np.float64)
+    rqi, rw, _ = oracle.index_scores_bwd(to_np(x["q_idx"][r_t]), to_np(x["q_scale"][r_t]),
+                                         to_np(x["w"][r_t]), to_np(x["k_idx"]), to_np(x["k_scale"]),
+                                         oracle.FP8_E4M3, id_r, g_r)
+    for name, got, ref in (("dq^I", to_np(dqi[r_t]), rqi), ("dw", to_np(dw[r_t]), rw)):
+        err = np.abs(got.astype(np.float64) - ref).max()
+        _say("  %s sampled rows: max err %.3e of max |ref| %.3e" % (name, err, np.abs(ref).max()))
+        assert err <= 1e-2 * np.abs(ref).max() + 1e-9, name
+    # dV summed over positions, per group, equals dout summed over rows and the group's heads
+    dv_sum = dv.double().sum(dim=0)                                     # [G, d]
+    do_sum = dout.double().view(L, G, Hq // G, 128).sum(dim=(0, 2))     # [G, d]
+    err = (dv_sum - do_sum).abs().max().item()
+    _say("  dV invariant: max err %.3e of max %.3e" % (err, do_sum.abs().max().item()))
+    assert err <= 1e-3 * do_sum.abs().max().item() + 1e-2
+    assert torch.isfinite(dk).all() and torch.isfinite(dki).all()
