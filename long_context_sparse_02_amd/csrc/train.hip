@@ -12,10 +12,10 @@
 //   G[t,j,s] = dI[t,s] w[t,j] [x > 0],
 //   dw[t,j]  = sum_s dI[t,s] ReLU(x[t,j,s]),
 //   dq[t,j]  = sum_s G[t,j,s] k^I[s],     dk[s] += sum_j G[t,j,s] q^I[t,j].
-// FP8 inputs (OCP E4M3 codes, per-token fp32 scales), d_I = 128.  The work per
-// row is H^I * d_I multiply-adds per selected position for each product; the
-// kernels run it on the vector ALU in fp32 from the decoded codes (exact
-// values), one workgroup per query row.
+// FP8 inputs (OCP E4M3 codes, per-token fp32 scales), d_I = 128, one workgroup
+// per query row.  The scores run on the FP8 matrix core (H^I a multiple of 16;
+// other head counts on the vector ALU from the decoded codes); the backward runs
+// on the vector ALU in fp32 from the decoded codes (exact values).
 #include "device_common.h"
 #include "internal.h"
 
@@ -106,6 +106,49 @@ __global__ __launch_bounds__(kIxThreads) void index_at_kernel(
             out = I;
         }
         vals[t * topk + i] = out;
+    }
+}
+
+// The same on the FP8 matrix core when H^I is a multiple of 16: a 16-head tile of the row's
+// query on A, 16 selected keys (gathered rows of codes) on B, so a lane's four results are
+// four heads of one key and the ReLU-weighted head sum stays in the lane until a final
+// exchange across the four lane groups.  Waves take key tiles in turn.
+template <int NHT>
+__global__ __launch_bounds__(kIxThreads) void index_at_mfma_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int Tk,
+    const int32_t* __restrict__ idx, int topk, float* __restrict__ vals)
+{
+    constexpr int HI = NHT * 16;
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    v8i qa[NHT];
+    float wv[NHT][4];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+        qa[ht] = *reinterpret_cast<const v8i*>(q_idx + (t * HI + ht * 16 + col) * 128 + grp * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[ht][i] = w[t * HI + ht * 16 + 4 * grp + i];
+    }
+    const float qs = q_scale[t];
+    for (int tile = wave; tile * 16 < topk; tile += kIxThreads / 64) {
+        const int i = tile * 16 + col;
+        const int s = i < topk ? idx[t * topk + i] : -1;
+        const bool ok = s >= 0 && s < Tk;
+        const int sr = ok ? s : 0;                      // in-bounds row for padding entries
+        const v8i kb = *reinterpret_cast<const v8i*>(k_idx + (int64_t)sr * 128 + grp * 32);
+        const float sc = qs * k_scale[sr];
+        float I = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+            const v4f x = mfma_fp8_16x16x128(qa[ht], kb, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) I += wv[ht][r] * fmaxf(x[r] * sc, 0.f);
+        }
+        I += __shfl_xor(I, 16, 64);
+        I += __shfl_xor(I, 32, 64);
+        if (grp == 0 && i < topk) vals[t * topk + i] = ok ? I : -INFINITY;
     }
 }
 
@@ -222,8 +265,16 @@ hipError_t launch_index_at(const uint8_t* q_idx, const float* q_scale, const flo
                            const int32_t* idx, int topk, float* vals, hipStream_t stream)
 {
     if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(index_at_kernel, dim3(T), dim3(kIxThreads), 0, stream, q_idx, q_scale, w,
-                       k_idx, k_scale, Tk, HI, idx, topk, vals);
+    const dim3 grid(T), block(kIxThreads);
+    switch (HI % 16 == 0 ? HI / 16 : 0) {
+    case 1: hipLaunchKernelGGL(index_at_mfma_kernel<1>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, vals); break;
+    case 2: hipLaunchKernelGGL(index_at_mfma_kernel<2>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, vals); break;
+    case 4: hipLaunchKernelGGL(index_at_mfma_kernel<4>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, vals); break;
+    case 8: hipLaunchKernelGGL(index_at_mfma_kernel<8>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, vals); break;
+    default:
+        hipLaunchKernelGGL(index_at_kernel, grid, block, 0, stream, q_idx, q_scale, w, k_idx,
+                           k_scale, Tk, HI, idx, topk, vals);
+    }
     return hipGetLastError();
 }
 

@@ -901,7 +901,7 @@ def test_index_scores_at_vs_oracle():
 
 
 @pytest.mark.parametrize("T,Tk,HI,topk", [(200, 2500, 64, 256), (48, 5000, 64, 2048),
-                                          (37, 900, 16, 300)])
+                                          (37, 900, 16, 300), (30, 700, 12, 200)])
 def test_index_scores_at_bwd_vs_oracle(T, Tk, HI, topk):
     rng = np.random.default_rng(T + topk)
     qc, qs, w, kc, ks = _int_code_indexer(rng, T, Tk, HI)
