@@ -258,6 +258,165 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_kernel(
         dw[t * HI + j] = red[2 * kIxHIMax * 128 + j] + red[2 * kIxHIMax * 128 + kIxHIMax + j];
 }
 
+// Backward on the matrix cores (H^I a multiple of 16, at most 64).  One workgroup per query
+// row; every wave walks all selected positions, 32 per step, and owns 32 of the 128 d_I
+// columns of both products.  Per step a wave
+//   - recomputes X = q^I k^T for all heads on the FP8 matrix core (heads on A, keys on B),
+//   - forms G = dI w [x > 0] and, in wave 0, accumulates dw = sum dI ReLU(x),
+//   - writes G through LDS as bf16 twice: heads x keys with the key scales folded in (A of
+//     dq = G K) and keys x heads (A of dk = G^T q), and stages the keys' codes,
+//   - accumulates dq [heads x its 32 columns] in registers (bf16 products of G and the key
+//     codes, which bf16 holds exactly) and computes dk [32 keys x its 32 columns], added to
+//     memory with 32-lane coalesced atomic adds.
+// G is rounded to bf16 for the two products (2^-9 relative per term).
+constexpr int kBwdKeys = 32;
+
+__device__ __forceinline__ uint16_t e4m3_bf16_bits(uint32_t c)
+{
+    return (uint16_t)(__float_as_uint(e4m3_value(c)) >> 16);   // exact: 4 significant bits
+}
+
+template <int NHT>
+__global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int Tk,
+    const int32_t* __restrict__ idx, int topk, const float* __restrict__ g,
+    float* __restrict__ dq, float* __restrict__ dw, float* __restrict__ dk)
+{
+    constexpr int HI = NHT * 16;
+    constexpr int NHC = (HI + 31) / 32;                  // 32-head chunks of the dk product
+    __shared__ __attribute__((aligned(16))) uint16_t ga[4][64][kBwdKeys + 8];   // heads x keys
+    __shared__ __attribute__((aligned(16))) uint16_t gb[4][kBwdKeys][64 + 8];   // keys x heads
+    __shared__ __attribute__((aligned(16))) uint8_t kcs[4][kBwdKeys][128 + 16]; // key codes
+    __shared__ __attribute__((aligned(16))) float st[4][kBwdKeys][32 + 4];      // dk staging
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int c0 = 32 * wave;                            // this wave's d_I columns
+    // heads beyond HI stay zero in the keys x heads tile
+    for (int i = lane; i < kBwdKeys * 72; i += 64) (&gb[wave][0][0])[i] = 0;
+    v8i qa[NHT];
+    float wv[NHT][4];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+        qa[ht] = *reinterpret_cast<const v8i*>(q_idx + (t * HI + ht * 16 + col) * 128 + grp * 32);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wv[ht][r] = w[t * HI + ht * 16 + 4 * grp + r];
+    }
+    // B operands of dk = G^T q: q codes (bf16, exact) for heads 32 hc + 8 grp + j, column d
+    v8bf qb[NHC][2];
+#pragma unroll
+    for (int hc = 0; hc < NHC; ++hc)
+#pragma unroll
+        for (int dtl = 0; dtl < 2; ++dtl) {
+            v8s x;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int h = 32 * hc + 8 * grp + j;
+                x[j] = h < HI ? (short)e4m3_bf16_bits(q_idx[(t * HI + h) * 128 + c0 + 16 * dtl + col]) : (short)0;
+            }
+            qb[hc][dtl] = __builtin_bit_cast(v8bf, x);
+        }
+    const float qs = q_scale[t];
+    v4f dqa[NHT][2];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) dqa[ht][0] = dqa[ht][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    float dwa[NHT][4];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dwa[ht][r] = 0.f;
+
+    for (int i0 = 0; i0 < topk; i0 += kBwdKeys) {
+        int sk[2];
+        bool okk[2];
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) {
+            const int i = i0 + 16 * kt2 + col;
+            const int s = i < topk ? idx[t * topk + i] : -1;
+            okk[kt2] = s >= 0 && s < Tk;
+            sk[kt2] = okk[kt2] ? s : 0;
+            const float gi = okk[kt2] ? g[t * topk + i] : 0.f;
+            const v8i kb = *reinterpret_cast<const v8i*>(k_idx + (int64_t)sk[kt2] * 128 + grp * 32);
+            *reinterpret_cast<v8i*>(&kcs[wave][16 * kt2 + col][grp * 32]) = kb;
+            const float ks = k_scale[sk[kt2]];
+            const float sc = qs * ks;
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht) {
+                const v4f x = mfma_fp8_16x16x128(qa[ht], kb, v4f{0.f, 0.f, 0.f, 0.f});
+                uint16_t gbits[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float xv = x[r] * sc;
+                    const float gv = xv > 0.f ? gi * wv[ht][r] : 0.f;
+                    if (wave == 0) dwa[ht][r] += gi * fmaxf(xv, 0.f);
+                    ga[wave][16 * ht + 4 * grp + r][16 * kt2 + col] = f32_to_bf16_bits(gv * ks);
+                    gbits[r] = f32_to_bf16_bits(gv);
+                }
+                *reinterpret_cast<uint2*>(&gb[wave][16 * kt2 + col][16 * ht + 4 * grp]) =
+                    make_uint2(gbits[0] | ((uint32_t)gbits[1] << 16), gbits[2] | ((uint32_t)gbits[3] << 16));
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // dq[heads, c0 .. c0 + 32) += G' K: A = G' (head row, keys 8 grp ..), B = key codes
+        v8bf kbop[2];
+#pragma unroll
+        for (int dtl = 0; dtl < 2; ++dtl) {
+            v8s x;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = (short)e4m3_bf16_bits(kcs[wave][8 * grp + j][c0 + 16 * dtl + col]);
+            kbop[dtl] = __builtin_bit_cast(v8bf, x);
+        }
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+            const v8bf a = *reinterpret_cast<const v8bf*>(&ga[wave][16 * ht + col][8 * grp]);
+            dqa[ht][0] = mfma_bf16_16x16x32(a, kbop[0], dqa[ht][0]);
+            dqa[ht][1] = mfma_bf16_16x16x32(a, kbop[1], dqa[ht][1]);
+        }
+        // dk[keys, c0 .. c0 + 32) = q_scale G^T q
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+            for (int dtl = 0; dtl < 2; ++dtl) {
+                v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int hc = 0; hc < NHC; ++hc) {
+                    const v8bf a = *reinterpret_cast<const v8bf*>(&gb[wave][16 * kt2 + col][32 * hc + 8 * grp]);
+                    acc = mfma_bf16_16x16x32(a, qb[hc][dtl], acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[wave][16 * kt2 + 4 * grp + r][16 * dtl + col] = acc[r] * qs;
+            }
+        __builtin_amdgcn_wave_barrier();
+        // 32 keys x 32 columns: two keys per instruction, 32 consecutive floats each
+        for (int m = 0; m < kBwdKeys / 2; ++m) {
+            const int key = 2 * m + (lane >> 5);
+            const int i = i0 + key;
+            const int s = i < topk ? idx[t * topk + i] : -1;
+            if (s >= 0 && s < Tk) atomicAdd(dk + (int64_t)s * 128 + c0 + (lane & 31), st[wave][key][lane & 31]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int dtl = 0; dtl < 2; ++dtl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dq[(t * HI + 16 * ht + 4 * grp + r) * 128 + c0 + 16 * dtl + col] = dqa[ht][dtl][r];
+    if (wave == 0) {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = dwa[ht][r];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+                if (col == 0) dw[t * HI + 16 * ht + 4 * grp + r] = v;
+            }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_index_at(const uint8_t* q_idx, const float* q_scale, const float* w,
@@ -285,8 +444,16 @@ hipError_t launch_index_at_bwd(const uint8_t* q_idx, const float* q_scale, const
 {
     if (T == 0) return hipSuccess;
     if (HI > kIxHIMax) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(index_at_bwd_kernel, dim3(T), dim3(kIxThreads), 0, stream, q_idx, q_scale,
-                       w, k_idx, k_scale, Tk, HI, idx, topk, g, dq, dw, dk);
+    const dim3 grid(T), block(kIxThreads);
+    switch (HI % 16 == 0 ? HI / 16 : 0) {
+    case 1: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<1>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk); break;
+    case 2: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<2>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk); break;
+    case 3: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<3>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk); break;
+    case 4: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<4>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk); break;
+    default:
+        hipLaunchKernelGGL(index_at_bwd_kernel, grid, block, 0, stream, q_idx, q_scale, w, k_idx,
+                           k_scale, Tk, HI, idx, topk, g, dq, dw, dk);
+    }
     return hipGetLastError();
 }
 

@@ -917,12 +917,15 @@ def test_index_scores_at_bwd_vs_oracle(T, Tk, HI, topk):
     valid = idx >= 0
     np.testing.assert_allclose(to_np(vals)[valid], ref_v[valid], rtol=1e-5,
                                atol=1e-6 * np.abs(ref_v[valid]).max())
+    # dw is accumulated in fp32; dq and dk take G = dI w [x > 0] rounded to bf16 into the
+    # matrix products (2^-9 relative per term) when H^I is a multiple of 16
+    mfma = HI % 16 == 0
     for name, got, ref in (("dq", dq, rq), ("dw", dw, rw), ("dk", dk, rk)):
         got = to_np(got).astype(np.float64)
         err = np.abs(got - ref).max()
         scale = np.abs(ref).max()
         _say("  indexer bwd %s: max err %.3e of max |ref| %.3e" % (name, err, scale))
-        assert err <= 2e-5 * scale, name
+        assert err <= (1e-2 if mfma and name != "dw" else 2e-5) * scale, name
 
 
 def _attn_train_case(rng, T, Tk, Hq, G, topk, pad=True):
