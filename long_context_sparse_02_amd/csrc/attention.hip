@@ -337,9 +337,9 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
         uint16_t* vtile = &vt[wave][0][0];
         float* stage = reinterpret_cast<float*>(ktile);  // 16 x kStagePitch floats fit the K tile
 
+        KVStep cur;
+        if (k_end > 0) load_step<false>(a, idx_row, 0, k_end, 0, len, g, lane, cur);
         for (int kb0 = 0; kb0 < k_end; kb0 += kStep) {
-            KVStep cur;
-            load_step<false>(a, idx_row, kb0, k_end, 0, len, g, lane, cur);
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
                 const int off = ((lane >> 4) + 4 * it) * kVPitch + (lane & 15) * 8;
@@ -406,6 +406,10 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
                 dqa[dt] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, kta),
                                              __builtin_bit_cast(v8bf, dsb), dqa[dt]);
             }
+            // the next step's gather goes out before this step's atomic adds, so that its
+            // wait does not queue behind them
+            if (kb0 + kStep < k_end) load_step<false>(a, idx_row, kb0 + kStep, k_end, 0, len, g, lane, cur);
+            asm volatile("" ::: "memory");
             // P and dS as [position][head] tiles
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
