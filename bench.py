@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--workload", default="prefill_128k_clustered")
     p.add_argument("--decode-workloads", default="decode_paged_64x256k,decode_paged_64x32k-256k")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=96)
+    p.add_argument("--cpu-rows", type=int, default=960)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-packed", action="store_true")
     p.add_argument("--no-train", action="store_true")
