@@ -229,7 +229,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
 //                                            to become B operands, the results through LDS
 //                                            to become 64-lane atomic adds of whole rows)
 // and, when the indexer scores at Omega_t are given, the group-mean attention
-// p[t,s,g] = mean_h P goes into an LDS row sum; at the end of the row the kernel writes
+// p[t,s,g] = mean_h P goes into a per-wave LDS row sum (summed in a fixed order, so the
+// loss and its gradient are deterministic); at the end of the row the kernel writes
 // dI = G softmax(I[t,Omega_t]) - sum_g p and the row's KL sum_g sum_s p ln(p / softmax(I)).
 constexpr int kBwdMaxTopk = 2048;
 constexpr int kStagePitch = 132;           // floats per staged position row
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
     __shared__ __attribute__((aligned(16))) uint16_t vt[kAttnWaves][kStep][kVPitch];
     __shared__ __attribute__((aligned(16))) uint16_t kt[kAttnWaves][kStep][kVPitch];
     __shared__ __attribute__((aligned(16))) uint16_t pst[kAttnWaves][2][kStep][16];
-    __shared__ float psum[kBwdMaxTopk];
+    __shared__ float psum[kAttnWaves][kBwdMaxTopk];   // per wave: sum over its groups of p
     __shared__ float red[kAttnWaves];
     const int row = xcd_remap(blockIdx.x, gridDim.x);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -265,7 +266,8 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
     if (kl_on) {
         float m = -INFINITY;
         for (int i = tid; i < topk; i += 256) {
-            psum[i] = 0.f;
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) psum[w][i] = 0.f;
             const int s = idx_row[i];
             if (s >= 0 && s < len) m = fmaxf(m, p.vals[(int64_t)row * topk + i]);
         }
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
                         const int r = i < 4 ? 4 * grp + i : 16 + 4 * grp + (i - 4);
                         if ((valid >> r) & 1u) {
                             const float pg = ps[i] / (float)hpg;
-                            atomicAdd(&psum[kb0 + r], pg);
+                            psum[wave][kb0 + r] += pg;      // one lane per position
                             if (pg > 0.f) plogp += pg * logf(pg);
                         }
                     }
@@ -469,8 +471,9 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
         const int s = idx_row[i];
         const bool ok = s >= 0 && s < len;
         const float lq = ok ? p.vals[(int64_t)row * topk + i] - mI - lnZ : 0.f;   // ln softmax(I)
-        if (ok) cross += psum[i] * lq;
-        p.dI[(int64_t)row * topk + i] = ok ? (float)p.G * expf(lq) - psum[i] : 0.f;
+        const float ps = (psum[0][i] + psum[1][i]) + (psum[2][i] + psum[3][i]);    // fixed order
+        if (ok) cross += ps * lq;
+        p.dI[(int64_t)row * topk + i] = ok ? (float)p.G * expf(lq) - ps : 0.f;
     }
     cross = wave_sum(cross);
     __syncthreads();

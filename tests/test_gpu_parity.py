@@ -1032,3 +1032,51 @@ def test_train_step_full_size_sampled():
     _say("  dV invariant: max err %.3e of max %.3e" % (err, do_sum.abs().max().item()))
     assert err <= 1e-3 * do_sum.abs().max().item() + 1e-2
     assert torch.isfinite(dk).all() and torch.isfinite(dki).all()
+
+
+def test_training_side_padding_and_out_of_range_entries():
+    """Rows whose index lists are all padding, and entries outside [0, Tk), contribute
+    nothing: scores -inf, zero dq / dI / KL for empty rows, and the same gradients as with those
+    entries replaced by -1 (checked against the oracle on the -1 version)."""
+    rng = np.random.default_rng(77)
+    T, Tk, HI, topk, G, Hq = 24, 600, 64, 128, 4, 32
+    sm = 1 / math.sqrt(128)
+    qc, qs, w, kc, ks = _int_code_indexer(rng, T, Tk, HI)
+    q, k, v, dout, idx = _attn_train_case(rng, T, Tk, Hq, G, topk)
+    idx[3, :] = -1                                   # an empty row
+    idx[7, :] = -1
+    bad = idx.copy()
+    bad[5, 10] = Tk + 3                              # out of range: skipped like padding
+    bad[9, 0] = 1 << 30
+    clean = bad.copy()
+    clean[(clean >= Tk)] = -1
+    g = rng.normal(size=(T, topk)).astype(np.float32)
+    outs = []
+    for lists in (bad, clean):
+        a = _dev(qc, qs, w, kc, ks, lists, g)
+        vals = dsa.index_scores_at(*a[:6])
+        dqi, dw, dki = dsa.index_scores_at_bwd(*a)
+        qd, kd, vd, dod, idd = _dev(q, k, v, dout, lists)
+        vals_a = torch.where(torch.isfinite(vals), vals, torch.zeros_like(vals)).contiguous()
+        vals_a[idd < 0] = float("-inf")
+        vals_a[idd >= Tk] = float("-inf")
+        out, lse = dsa.sparse_gqa_attn_lse(qd, kd, vd, idd, G, sm)
+        dq, dk, dv, kl, dI = dsa.sparse_gqa_attn_bwd(qd, kd, vd, idd, G, sm, out, dod, lse, vals=vals_a)
+        torch.cuda.synchronize()
+        outs.append([to_np(t) for t in (vals, dqi, dw, dki, out, lse, dq, dk, dv, kl, dI)])
+    vb, vc = outs[0][0], outs[1][0]
+    assert vb[5, 10] == -np.inf and vb[9, 0] == -np.inf and np.all(vb[3] == -np.inf)
+    np.testing.assert_array_equal(vb, vc)
+    for i, name in enumerate(("vals", "dq^I", "dw", "dk^I", "out", "lse", "dq", "dk", "dv", "kl", "dI")):
+        a_, b_ = outs[0][i].astype(np.float64), outs[1][i].astype(np.float64)
+        if name in ("dk^I", "dk", "dv"):             # atomic order differs between the calls
+            assert np.abs(a_ - b_).max() <= 1e-5 * max(1.0, np.abs(b_).max()), name
+        else:
+            np.testing.assert_array_equal(a_, b_, err_msg=name)
+    vals, dqi, dw, dki, out, lse, dq, dk, dv, kl, dI = outs[1]
+    for r in (3, 7):                                 # empty rows
+        assert np.all(lse[r] == -np.inf) and np.all(out[r] == 0) and np.all(dq[r] == 0)
+        assert kl[r] == 0 and np.all(dI[r] == 0) and np.all(dqi[r] == 0) and np.all(dw[r] == 0)
+    rq, rw, rk = oracle.index_scores_bwd(qc, qs, w, kc, ks, oracle.FP8_E4M3, clean, g)
+    assert np.abs(dqi - rq).max() <= 1e-2 * np.abs(rq).max()
+    assert np.abs(dki - rk).max() <= 1e-2 * np.abs(rk).max()
