@@ -200,3 +200,36 @@ def test_prefill_varlen_argument_checks(lib):
     args[11] = 1
     args[15] = 6
     assert f(*args) == 2                                             # FP8 needs HI % 4 == 0
+
+
+def test_training_side_argument_checks(lib):
+    f = lib.dsa_index_scores_at
+    ok = [A, A, A, A, A, dsa.DSA_FP8_E4M3, 16, 100, 64, 128, A, 2048, A, None]
+    bad = list(ok); bad[5] = dsa.DSA_F32
+    assert f(*bad) == 2                                          # FP8 only
+    bad = list(ok); bad[9] = 64
+    assert f(*bad) == 2                                          # dI must be 128
+    bad = list(ok); bad[12] = None
+    assert f(*bad) == 1 and b"vals" in lib.dsa_last_error()
+    fb = lib.dsa_index_scores_at_bwd
+    okb = [A, A, A, A, A, dsa.DSA_FP8_E4M3, 16, 100, 64, 128, A, 2048, A, A, A, A, None]
+    bad = list(okb); bad[8] = 128
+    assert fb(*bad) == 2                                         # the backward takes HI <= 64
+    bad = list(okb); bad[15] = None
+    assert fb(*bad) == 1 and b"dk_idx" in lib.dsa_last_error()
+    fl = lib.dsa_sparse_gqa_attn_lse
+    okl = [A, A, A, dsa.DSA_BF16, 100, A, 16, 2048, 32, 4, 128, 0.1, A, A, None, 0, None]
+    bad = list(okl); bad[13] = None
+    assert fl(*bad) == 1 and b"lse" in lib.dsa_last_error()
+    bad = list(okl); bad[10] = 64
+    assert fl(*bad) == 2
+    fw = lib.dsa_sparse_gqa_attn_bwd
+    okw = [A, A, A, dsa.DSA_BF16, 100, A, 16, 2048, 32, 4, 128, 0.1, A, A, A, A, A, A, A, A, A, None]
+    bad = list(okw); bad[3] = dsa.DSA_F32
+    assert fw(*bad) == 2 and b"BF16" in lib.dsa_last_error()
+    bad = list(okw); bad[7] = 4096
+    assert fw(*bad) == 2 and b"2048" in lib.dsa_last_error()  # the fused loss: topk <= 2048
+    bad = list(okw); bad[20] = None
+    assert fw(*bad) == 1 and b"dI" in lib.dsa_last_error()
+    bad = list(okw); bad[14] = None
+    assert fw(*bad) == 1 and b"lse" in lib.dsa_last_error()
