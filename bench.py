@@ -55,9 +55,10 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-packed", action="store_true")
     p.add_argument("--no-train", action="store_true")
-    p.add_argument("--profile-kernel", choices=["index", "topk", "attn"], default=None,
+    p.add_argument("--profile-kernel", choices=["index", "topk", "attn", "train"], default=None,
                    help="profiling driver: run only this kernel on one chunk of the workload "
-                        "(--profile-chunk, default the last) --profile-reps times, print nothing else")
+                        "(--profile-chunk, default the last) --profile-reps times, print nothing else; "
+                        "'train': only the 32K training step, printing its JSON record")
     p.add_argument("--profile-chunk", type=int, default=-1)
     p.add_argument("--profile-reps", type=int, default=2)
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -363,8 +364,8 @@ def run_packed_bench(args, dsa, W, torch):
 
 
 # fp32 atomic adds measured on this GPU with 64-lane rows of consecutive floats (a plain
-# kernel adding into random 512-byte rows of a 64 MiB array): the ceiling of the scatter of
-# dK / dV and dk^I in the backward
+# kernel adding into random 512-byte rows of a 64 MiB array; every add is executed on the
+# memory side, at any memory scope): the ceiling of the scatter of dk^I in the indexer backward
 ATOMIC_FLOATS_PER_S = 330e9
 
 
@@ -392,6 +393,7 @@ def run_train_bench(args, dsa, W, torch):
     dw = torch.empty(x["w"].shape, dtype=torch.float32, device="cuda")
     dki = torch.empty(x["k_idx"].shape, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    bws = dsa.workspace(dsa.dsa_sparse_gqa_attn_bwd_workspace_size(L, k, G, L))
     BF, F8 = dsa.DSA_BF16, dsa.DSA_FP8_E4M3
     parts = {
         "index_at": lambda: dsa.dsa_index_scores_at(
@@ -402,7 +404,7 @@ def run_train_bench(args, dsa, W, torch):
             None, 0, stream),
         "attn_bwd_kl": lambda: (dk.zero_(), dv.zero_(), dsa.dsa_sparse_gqa_attn_bwd(
             x["q"], x["k"], x["v"], BF, L, idx, L, k, cfg.Hq, G, cfg.d, cfg.sm_scale, out, dout,
-            lse, dq, dk, dv, vals, kl, dI, stream)),
+            lse, dq, dk, dv, vals, kl, dI, bws, bws.numel(), stream=stream)),
         "index_at_bwd": lambda: (dki.zero_(), dsa.dsa_index_scores_at_bwd(
             x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"], F8, L, L, cfg.HI, cfg.dI,
             idx, k, dI, dqi, dw, dki, stream)),
@@ -422,16 +424,19 @@ def run_train_bench(args, dsa, W, torch):
         torch.cuda.synchronize()
         ms[name] = e0.elapsed_time(e1) / reps
     n_sel = int(torch.clamp(torch.arange(1, L + 1, device="cuda"), max=k).sum())
-    atom_attn = n_sel * G * cfg.d * 2
+    # attention backward, staged: per selected pair and KV group the K and V rows gathered
+    # (2 x 256 B) and the dK / dV contribution written and read back (2 x 1 KiB)
+    attn_bytes = n_sel * G * (2 * cfg.d * 2 + 2 * 2 * cfg.d * 4)
     atom_ix = n_sel * cfg.dI
     step = sum(ms.values())
     res = {"workload": cfg.name + "_train_step", "tokens": L, "selected_pairs": n_sel,
            "ms": {n: round(v, 3) for n, v in ms.items()}, "ms_per_step": round(step, 3),
            "tokens_per_s": round(L / (step * 1e-3), 1),
-           "attn_bwd_atomic_frac": round(atom_attn / (ms["attn_bwd_kl"] * 1e-3) / ATOMIC_FLOATS_PER_S, 4),
+           "attn_bwd_bytes": attn_bytes,
+           "attn_bwd_hbm_frac": round(attn_bytes / (ms["attn_bwd_kl"] * 1e-3) / PEAK["hbm"], 4),
            "index_bwd_atomic_frac": round(atom_ix / (ms["index_at_bwd"] * 1e-3) / ATOMIC_FLOATS_PER_S, 4),
            "mean_kl": round(float(kl.mean()), 5)}
-    del x, idx, out, lse, vals, dq, dk, dv, kl, dI, dqi, dw, dki, dout
+    del x, idx, out, lse, vals, dq, dk, dv, kl, dI, dqi, dw, dki, dout, bws
     torch.cuda.empty_cache()
     return res
 
@@ -481,6 +486,10 @@ def main():
     import long_context_sparse_02_amd as dsa
     import workloads as W
     dsa.load_library()
+    if args.profile_kernel == "train":
+        # the 32K training step alone (warm-up and timed repetitions as --warmup / --steps)
+        print(json.dumps(run_train_bench(args, dsa, W, torch)), flush=True)
+        return
     if args.profile_kernel:
         run_profile_kernel(args, dsa, W, torch)
         return

@@ -338,22 +338,26 @@ dsa_status_t dsa_sparse_gqa_attn_lse(const void* q, const void* k, const void* v
  * incoming gradient dout [Tq, Hq, d] (bf16), with P = exp(sm_scale q.K[s] - lse) over the
  * valid entries s of idx[t, :]:
  *   dq [Tq, Hq, d] (bf16, written) = sm_scale sum_s dS_s K[s],  dS_s = P_s (dout.V[s] - dout.out);
- *   dk, dv float [n_kv, G, d] ACCUMULATED with atomic adds (zero them first; the order of the
- *   adds, and so the last bits, vary between runs): dk[s] += sm_scale sum_h dS_s q_h,
+ *   dk, dv float [n_kv, G, d] ACCUMULATED (zero them first): dk[s] += sm_scale sum_h dS_s q_h,
  *   dv[s] += sum_h P_s dout_h over each group's heads.
+ * With a workspace of dsa_sparse_gqa_attn_bwd_workspace_size() bytes the contributions are
+ * stored per (row, entry, group) for chunks of rows and summed per position in row order:
+ * dk and dv are then bit-reproducible.  With ws = NULL (ws_bytes 0) they are added with fp32
+ * atomic adds, whose order, and so the last bits, vary between runs.
  * When vals float [Tq, topk] (= dsa_index_scores_at at idx) is given (topk <= 2048), also
  *   kl float [Tq]: sum_g KL(p[t,:,g] || softmax(vals[t,:])) over the valid entries, p[t,s,g]
  *     the mean of the group's heads' P (report section 2.3.3, sparse adaptation loss),
  *   dI float [Tq, topk]: d kl[t] / d vals[t, i] = G softmax(vals[t,:])_i - sum_g p[t,i,g]
  *     (0 for padding), ready for dsa_index_scores_at_bwd.
- * vals, kl and dI may all be NULL.  No workspace.
+ * vals, kl and dI may all be NULL.
  */
+size_t dsa_sparse_gqa_attn_bwd_workspace_size(int Tq, int topk, int G, int n_kv);
 dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v,
                                      dsa_dtype_t dtype, int n_kv, const int32_t* idx, int Tq,
                                      int topk, int Hq, int G, int d, float sm_scale,
                                      const void* out, const void* dout, const float* lse,
                                      void* dq, float* dk, float* dv, const float* vals, float* kl,
-                                     float* dI, hipStream_t stream);
+                                     float* dI, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,8 @@ EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
            "dsa_prefill", "dsa_prefill_varlen", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
            "dsa_quantize_e4m3", "dsa_cache_append", "dsa_index_scores_at",
-           "dsa_index_scores_at_bwd", "dsa_sparse_gqa_attn_lse", "dsa_sparse_gqa_attn_bwd"]
+           "dsa_index_scores_at_bwd", "dsa_sparse_gqa_attn_lse", "dsa_sparse_gqa_attn_bwd_workspace_size",
+           "dsa_sparse_gqa_attn_bwd"]
 
 
 class DSAError(RuntimeError):
@@ -83,8 +84,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_index_scores_at": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P], I),
             "dsa_index_scores_at_bwd": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P, P, P, P], I),
             "dsa_sparse_gqa_attn_lse": ([P, P, P, I, I, P, I, I, I, I, I, F, P, P, P, SZ, P], I),
+            "dsa_sparse_gqa_attn_bwd_workspace_size": ([I, I, I, I], SZ),
             "dsa_sparse_gqa_attn_bwd": ([P, P, P, I, I, P, I, I, I, I, I, F, P, P, P, P, P, P, P, P,
-                                         P, P], I),
+                                         P, P, SZ, P], I),
         }
         for name in EXPORTS:
             fn = getattr(lib, name)
@@ -428,12 +430,17 @@ def dsa_sparse_gqa_attn_lse(q, k, v, dtype, n_kv, idx, Tq, topk, Hq, G, d, sm_sc
         _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def dsa_sparse_gqa_attn_bwd_workspace_size(Tq, topk, G, n_kv) -> int:
+    return load_library().dsa_sparse_gqa_attn_bwd_workspace_size(Tq, topk, G, n_kv)
+
+
 def dsa_sparse_gqa_attn_bwd(q, k, v, dtype, n_kv, idx, Tq, topk, Hq, G, d, sm_scale, out, dout,
-                            lse, dq, dk, dv, vals=None, kl=None, dI=None, stream=None):
+                            lse, dq, dk, dv, vals=None, kl=None, dI=None, ws=None, ws_bytes=0,
+                            stream=None):
     _check(load_library().dsa_sparse_gqa_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), dtype, n_kv, _ptr(idx), Tq, topk, Hq, G, d, float(sm_scale),
         _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(vals), _ptr(kl),
-        _ptr(dI), _stream(stream)))
+        _ptr(dI), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def sparse_gqa_attn_lse(q, k, v, idx, G, sm_scale, stream=None):
@@ -449,9 +456,11 @@ def sparse_gqa_attn_lse(q, k, v, idx, G, sm_scale, stream=None):
     return out, lse
 
 
-def sparse_gqa_attn_bwd(q, k, v, idx, G, sm_scale, out, dout, lse, vals=None, stream=None):
+def sparse_gqa_attn_bwd(q, k, v, idx, G, sm_scale, out, dout, lse, vals=None, staged=True,
+                        ws=None, stream=None):
     """(dq bf16, dk fp32, dv fp32[, kl, dI]) of the attention (and the sparse indexer loss when
-    vals, the indexer scores at idx, is given)."""
+    vals, the indexer scores at idx, is given).  staged: the deterministic reduction of dK / dV
+    through a workspace (else fp32 atomic adds)."""
     import torch
     Tq, Hq, d = q.shape
     dq = torch.empty_like(q)
@@ -461,6 +470,10 @@ def sparse_gqa_attn_bwd(q, k, v, idx, G, sm_scale, out, dout, lse, vals=None, st
     if vals is not None:
         kl = torch.empty(Tq, dtype=torch.float32, device=q.device)
         dI = torch.empty(idx.shape, dtype=torch.float32, device=q.device)
+    n = dsa_sparse_gqa_attn_bwd_workspace_size(Tq, idx.shape[1], G, k.shape[0]) if staged else 0
+    if n and (ws is None or ws.numel() < n):
+        ws = workspace(n, q.device)
     dsa_sparse_gqa_attn_bwd(q, k, v, dtype_code(q), k.shape[0], idx, Tq, idx.shape[1], Hq, G, d,
-                            sm_scale, out, dout, lse, dq, dk, dv, vals, kl, dI, stream)
+                            sm_scale, out, dout, lse, dq, dk, dv, vals, kl, dI,
+                            ws if n else None, ws.numel() if n else 0, stream)
     return (dq, dk, dv) if vals is None else (dq, dk, dv, kl, dI)

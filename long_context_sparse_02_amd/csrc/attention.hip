@@ -23,6 +23,8 @@
 // gather latency overlaps compute.  Long rows can be split across workgroups;
 // partial (max, sum, unnormalised output) triples are merged by a combine
 // kernel with the usual log-sum-exp rescaling.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
     __shared__ __attribute__((aligned(16))) uint16_t pst[kAttnWaves][2][kStep][16];
     __shared__ float psum[kAttnWaves][kBwdMaxTopk];   // per wave: sum over its groups of p
     __shared__ float red[kAttnWaves];
-    const int row = xcd_remap(blockIdx.x, gridDim.x);
+    const int row = p.r0 + xcd_remap(blockIdx.x, gridDim.x);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int hpg = p.Hq / p.G;
@@ -442,10 +444,19 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
                     for (int r = 0; r < 16; ++r) {
                         const int pos = pt * 16 + r;
                         if (!((valid >> pos) & 1u)) continue;       // uniform
-                        const int s = idx_row[kb0 + pos];
-                        float* dst = dst_base + ((int64_t)s * p.G + g) * 128;
-                        atomicAdd(dst + lane, stage[r * kStagePitch + lane]);
-                        atomicAdd(dst + 64 + lane, stage[r * kStagePitch + 64 + lane]);
+                        const float a0 = stage[r * kStagePitch + lane];
+                        const float a1 = stage[r * kStagePitch + 64 + lane];
+                        if (p.stg) {                     // streaming stores, reduced later
+                            const int64_t e = (int64_t)(row - p.r0) * topk + kb0 + pos;
+                            float* dst = p.stg + (e * p.G + g) * 256 + mat * 128;
+                            __builtin_nontemporal_store(a0, dst + lane);
+                            __builtin_nontemporal_store(a1, dst + 64 + lane);
+                        } else {
+                            const int s = idx_row[kb0 + pos];
+                            float* dst = dst_base + ((int64_t)s * p.G + g) * 128;
+                            atomicAdd(dst + lane, a0);
+                            atomicAdd(dst + 64 + lane, a1);
+                        }
                     }
                     __builtin_amdgcn_wave_barrier();
                 }
@@ -482,6 +493,118 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
     if (lane == 0) red[wave] = cross;
     __syncthreads();
     if (tid == 0) p.kl[row] = total_plogp - (red[0] + red[1] + red[2] + red[3]);
+}
+
+// ---- deterministic reduction of the staged dK / dV contributions of a chunk of rows ----
+// Each row holds a key at most once (its index list has distinct positions), so a key's
+// entries are identified by the rows that select it: a bitmask per key over the chunk's rows
+// gives each entry its rank among the key's entries without any sort, and the per-key sums
+// run in row order, independent of scheduling.
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void stage_mark_kernel(const int32_t* __restrict__ idx, int r0,
+                                                         int C, int topk, int n_kv, int W,
+                                                         uint32_t* __restrict__ mask)
+{
+    const int64_t n = (int64_t)C * topk;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+        const int t = (int)(e / topk);
+        const int s = idx[(int64_t)r0 * topk + e];
+        if (s >= 0 && s < n_kv) atomicOr(&mask[(int64_t)s * W + (t >> 5)], 1u << (t & 31));
+    }
+}
+
+__global__ __launch_bounds__(256) void stage_count_kernel(const uint32_t* __restrict__ mask,
+                                                          int n_kv, int W, int32_t* __restrict__ cnt)
+{
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= n_kv) return;
+    int c = 0;
+    for (int w = 0; w < W; ++w) c += __popc(mask[(int64_t)s * W + w]);
+    cnt[s] = c;
+}
+
+// In-place exclusive scan of cnt[0 .. n) by one workgroup; cnt[n] gets the total.
+__global__ __launch_bounds__(1024) void stage_scan_kernel(int32_t* __restrict__ cnt, int n)
+{
+    __shared__ int red[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (n + 1023) / 1024;
+    const int b = min(n, tid * per), e = min(n, b + per);
+    int local = 0;
+    for (int i = b; i < e; ++i) local += cnt[i];
+    int x = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(x, o, 64); if (lane >= o) x += y; }
+    if (lane == 63) red[wave] = x;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int w = 0; w < 16; ++w) { if (w < wave) base += red[w]; total += red[w]; }
+    int run = base + x - local;
+    for (int i = b; i < e; ++i) { const int c = cnt[i]; cnt[i] = run; run += c; }
+    if (tid == 0) cnt[n] = total;
+}
+
+__global__ __launch_bounds__(256) void stage_list_kernel(const int32_t* __restrict__ idx, int r0,
+                                                         int C, int topk, int n_kv, int W,
+                                                         const uint32_t* __restrict__ mask,
+                                                         const int32_t* __restrict__ offs,
+                                                         int32_t* __restrict__ list)
+{
+    const int64_t n = (int64_t)C * topk;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+        const int t = (int)(e / topk);
+        const int s = idx[(int64_t)r0 * topk + e];
+        if (s < 0 || s >= n_kv) continue;
+        const uint32_t* m = mask + (int64_t)s * W;
+        int rank = __popc(m[t >> 5] & ((1u << (t & 31)) - 1u));
+        for (int w = 0; w < (t >> 5); ++w) rank += __popc(m[w]);
+        list[offs[s] + rank] = (int32_t)e;
+    }
+}
+
+// One workgroup per key, one wave per group: sum the key's staged rows (256 floats: dV then
+// dK) in row order and add them into dv / dk.
+__global__ __launch_bounds__(256) void stage_reduce_kernel(const float* __restrict__ stg,
+                                                           const int32_t* __restrict__ offs,
+                                                           const int32_t* __restrict__ list,
+                                                           int G, float* __restrict__ dk,
+                                                           float* __restrict__ dv)
+{
+    const int s = blockIdx.x;
+    const int b = offs[s], e = offs[s + 1];
+    if (b == e) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int g = wave; g < G; g += 4) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        int j = b;
+        for (; j + 4 <= e; j += 4) {                     // four rows in flight, added in order
+            v4f x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                x[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4f*>(stg + ((int64_t)list[j + u] * G + g) * 256) + lane);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc.x += x[u][0]; acc.y += x[u][1]; acc.z += x[u][2]; acc.w += x[u][3];
+            }
+        }
+        for (; j < e; ++j) {
+            const v4f x = __builtin_nontemporal_load(
+                reinterpret_cast<const v4f*>(stg + ((int64_t)list[j] * G + g) * 256) + lane);
+            acc.x += x[0]; acc.y += x[1]; acc.z += x[2]; acc.w += x[3];
+        }
+        // lanes 0..31 hold dV[4 lane .. +4), lanes 32..63 dK[4 (lane - 32) .. +4)
+        float* dst = (lane < 32 ? dv : dk) + ((int64_t)s * G + g) * 128 + 4 * (lane & 31);
+        float4 o = *reinterpret_cast<float4*>(dst);
+        o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
+        *reinterpret_cast<float4*>(dst) = o;
+    }
 }
 
 // fp32 kernel (vector ALU; exact-ish reference-grade path).  One workgroup per
@@ -672,6 +795,24 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, hipStream_t stream)
     if (a.Tq == 0) return hipSuccess;
     if (a.vals && a.topk > kBwdMaxTopk) return hipErrorInvalidValue;
     hipLaunchKernelGGL(sparse_attn_bwd_kernel, dim3((unsigned)a.Tq), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage_reduce(const int32_t* idx, int r0, int C, int topk, int n_kv, int G,
+                               const float* stg, uint32_t* mask, int32_t* offs, int32_t* list,
+                               float* dk, float* dv, hipStream_t stream)
+{
+    if (C == 0 || n_kv == 0) return hipSuccess;
+    const int W = (C + 31) / 32;
+    const int64_t nm = (int64_t)n_kv * W, ne = (int64_t)C * topk;
+    const unsigned gm = (unsigned)std::min<int64_t>((nm + 255) / 256, 65536);
+    const unsigned ge = (unsigned)std::min<int64_t>((ne + 255) / 256, 65536);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(gm), dim3(256), 0, stream, mask, nm);
+    hipLaunchKernelGGL(stage_mark_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, n_kv, W, mask);
+    hipLaunchKernelGGL(stage_count_kernel, dim3((n_kv + 255) / 256), dim3(256), 0, stream, mask, n_kv, W, offs);
+    hipLaunchKernelGGL(stage_scan_kernel, dim3(1), dim3(1024), 0, stream, offs, n_kv);
+    hipLaunchKernelGGL(stage_list_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, n_kv, W, mask, offs, list);
+    hipLaunchKernelGGL(stage_reduce_kernel, dim3(n_kv), dim3(256), 0, stream, stg, offs, list, G, dk, dv);
     return hipGetLastError();
 }
 

@@ -735,13 +735,47 @@ DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_lse(const void* q, const void* k, co
     return e == hipSuccess ? DSA_OK : hip_fail(e, "attention launch");
 }
 
+namespace {
+
+// The staged (deterministic) backward works on chunks of query rows whose dK / dV
+// contributions (1 KiB per selected entry and KV group) fit this many bytes.
+constexpr size_t kStageBudget = size_t(4) << 30;
+
+struct BwdPlan {
+    int chunk;
+    size_t stg_bytes, mask_bytes, offs_bytes, list_bytes, total;
+};
+
+BwdPlan plan_bwd(int Tq, int topk, int G, int n_kv) {
+    BwdPlan p;
+    const size_t per_row = (size_t)topk * G * 256 * sizeof(float);
+    int64_t c = (int64_t)(kStageBudget / per_row) / 32 * 32;
+    if (c < 32) c = 32;
+    const int64_t tq32 = ((int64_t)Tq + 31) / 32 * 32;
+    p.chunk = (int)std::min<int64_t>(c, tq32);
+    p.stg_bytes = round_up((size_t)p.chunk * per_row);
+    p.mask_bytes = round_up((size_t)n_kv * (p.chunk / 32) * sizeof(uint32_t));
+    p.offs_bytes = round_up(((size_t)n_kv + 1) * sizeof(int32_t));
+    p.list_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
+    p.total = p.stg_bytes + p.mask_bytes + p.offs_bytes + p.list_bytes;
+    return p;
+}
+
+}  // namespace
+
+DSA_EXPORT size_t dsa_sparse_gqa_attn_bwd_workspace_size(int Tq, int topk, int G, int n_kv) {
+    if (Tq <= 0 || topk <= 0 || G <= 0 || n_kv <= 0) return 0;
+    return plan_bwd(Tq, topk, G, n_kv).total;
+}
+
 DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v,
                                                 dsa_dtype_t dtype, int n_kv, const int32_t* idx,
                                                 int Tq, int topk, int Hq, int G, int d,
                                                 float sm_scale, const void* out,
                                                 const void* dout, const float* lse, void* dq,
                                                 float* dk, float* dv, const float* vals,
-                                                float* kl, float* dI, hipStream_t stream) {
+                                                float* kl, float* dI, void* ws, size_t ws_bytes,
+                                                hipStream_t stream) {
     g_err[0] = 0;
     dsa_status_t st = check_attn_shape(dtype, Hq, G, d, topk);
     if (st != DSA_OK) return st;
@@ -755,8 +789,36 @@ DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, co
                 "the fused indexer loss takes topk <= 2048 (got %d)", topk);
         REQUIRE_PTR4(vals); REQUIRE_PTR4(kl); REQUIRE_PTR4(dI);
     }
-    const dsa::AttnBwdArgs a{q, k, v, out, dout, lse, idx, Tq, topk, Hq, G, n_kv, sm_scale,
-                             dq, dk, dv, vals, vals ? kl : nullptr, vals ? dI : nullptr};
-    const hipError_t e = dsa::launch_sparse_attn_bwd(a, stream);
-    return e == hipSuccess ? DSA_OK : hip_fail(e, "attention backward launch");
+    dsa::AttnBwdArgs a{q, k, v, out, dout, lse, idx, Tq, topk, Hq, G, n_kv, sm_scale,
+                       dq, dk, dv, vals, vals ? kl : nullptr, vals ? dI : nullptr};
+    if (!ws) {                                     // atomic adds straight into dk / dv
+        REQUIRE(ws_bytes == 0, DSA_ERR_WORKSPACE, "ws is NULL but ws_bytes is %zu", ws_bytes);
+        const hipError_t e = dsa::launch_sparse_attn_bwd(a, stream);
+        return e == hipSuccess ? DSA_OK : hip_fail(e, "attention backward launch");
+    }
+    if (Tq == 0 || n_kv == 0) {
+        const hipError_t e = dsa::launch_sparse_attn_bwd(a, stream);   // dq (zeros), kl, dI
+        return e == hipSuccess ? DSA_OK : hip_fail(e, "attention backward launch");
+    }
+    const BwdPlan plan = plan_bwd(Tq, topk, G, n_kv);
+    REQUIRE(aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
+            "the staged attention backward needs %zu workspace bytes (got %zu)", plan.total,
+            ws_bytes);
+    char* wp = static_cast<char*>(ws);
+    float* stg = reinterpret_cast<float*>(wp);              wp += plan.stg_bytes;
+    uint32_t* mask = reinterpret_cast<uint32_t*>(wp);       wp += plan.mask_bytes;
+    int32_t* offs = reinterpret_cast<int32_t*>(wp);         wp += plan.offs_bytes;
+    int32_t* list = reinterpret_cast<int32_t*>(wp);
+    for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
+        const int rows = std::min(plan.chunk, Tq - r0);
+        a.r0 = r0;
+        a.Tq = rows;
+        a.stg = stg;
+        hipError_t e = dsa::launch_sparse_attn_bwd(a, stream);
+        if (e == hipSuccess)
+            e = dsa::launch_stage_reduce(idx, r0, rows, topk, n_kv, G, stg, mask, offs, list, dk,
+                                         dv, stream);
+        if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+    }
+    return DSA_OK;
 }

@@ -105,8 +105,19 @@ struct AttnBwdArgs {
     float sm_scale;
     void* dq; float* dk; float* dv;
     const float* vals; float* kl; float* dI;
+    // Rows r0 .. r0 + Tq - 1 of the index lists are processed.  With stg set, the dK / dV
+    // contributions of entry e = (row - r0) * topk + i and group g are stored at
+    // stg[(e * G + g) * 256 + {0: dV, 128: dK} + 0..127] instead of being added atomically.
+    int r0 = 0;
+    float* stg = nullptr;
 };
 hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
+// The deterministic reduction of staged contributions (chunk of C rows starting at row r0):
+// mark each key's selecting rows in a bitmask [n_kv][C / 32], count and scan them into
+// offsets [n_kv + 1], list each key's entries in row order, and add their sums into dk / dv.
+hipError_t launch_stage_reduce(const int32_t* idx, int r0, int C, int topk, int n_kv, int G,
+                               const float* stg, uint32_t* mask, int32_t* offs, int32_t* list,
+                               float* dk, float* dv, hipStream_t stream);
 // Splits used for a given shape when a workspace is available (1 = no split).
 int attn_num_splits(int Tq, int topk);
 size_t attn_partials_bytes(int Tq, int nsplit, int Hq, int d);

@@ -224,7 +224,8 @@ def test_training_side_argument_checks(lib):
     bad = list(okl); bad[10] = 64
     assert fl(*bad) == 2
     fw = lib.dsa_sparse_gqa_attn_bwd
-    okw = [A, A, A, dsa.DSA_BF16, 100, A, 16, 2048, 32, 4, 128, 0.1, A, A, A, A, A, A, A, A, A, None]
+    okw = [A, A, A, dsa.DSA_BF16, 100, A, 16, 2048, 32, 4, 128, 0.1, A, A, A, A, A, A, A, A, A,
+           None, 0, None]
     bad = list(okw); bad[3] = dsa.DSA_F32
     assert fw(*bad) == 2 and b"BF16" in lib.dsa_last_error()
     bad = list(okw); bad[7] = 4096
@@ -233,3 +234,9 @@ def test_training_side_argument_checks(lib):
     assert fw(*bad) == 1 and b"dI" in lib.dsa_last_error()
     bad = list(okw); bad[14] = None
     assert fw(*bad) == 1 and b"lse" in lib.dsa_last_error()
+    n = lib.dsa_sparse_gqa_attn_bwd_workspace_size(16, 2048, 4, 100)
+    assert n >= 32 * 2048 * 4 * 1024                            # a chunk of staged contributions
+    bad = list(okw); bad[21] = A; bad[22] = n - 1
+    assert fw(*bad) == 3 and b"workspace" in lib.dsa_last_error()
+    bad = list(okw); bad[22] = 64                                # size without a buffer
+    assert fw(*bad) == 3
