@@ -363,12 +363,6 @@ def run_packed_bench(args, dsa, W, torch):
     return res
 
 
-# fp32 atomic adds measured on this GPU with 64-lane rows of consecutive floats (a plain
-# kernel adding into random 512-byte rows of a 64 MiB array; every add is executed on the
-# memory side, at any memory scope): the ceiling of the scatter of dk^I in the indexer backward
-ATOMIC_FLOATS_PER_S = 330e9
-
-
 def run_train_bench(args, dsa, W, torch):
     """One sparse-adaptation training step of the layer at 32K (report section 2.3.3): the
     indexer scores at the selected positions, the attention forward with its log-sum-exp,
@@ -394,6 +388,7 @@ def run_train_bench(args, dsa, W, torch):
     dki = torch.empty(x["k_idx"].shape, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     bws = dsa.workspace(dsa.dsa_sparse_gqa_attn_bwd_workspace_size(L, k, G, L))
+    iws = dsa.workspace(dsa.dsa_index_scores_at_bwd_workspace_size(L, L, cfg.HI, k))
     BF, F8 = dsa.DSA_BF16, dsa.DSA_FP8_E4M3
     parts = {
         "index_at": lambda: dsa.dsa_index_scores_at(
@@ -407,7 +402,7 @@ def run_train_bench(args, dsa, W, torch):
             lse, dq, dk, dv, vals, kl, dI, bws, bws.numel(), stream=stream)),
         "index_at_bwd": lambda: (dki.zero_(), dsa.dsa_index_scores_at_bwd(
             x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"], F8, L, L, cfg.HI, cfg.dI,
-            idx, k, dI, dqi, dw, dki, stream)),
+            idx, k, dI, dqi, dw, dki, iws, iws.numel(), stream=stream)),
     }
     for _ in range(max(1, args.warmup)):
         for f in parts.values():
@@ -425,18 +420,21 @@ def run_train_bench(args, dsa, W, torch):
         ms[name] = e0.elapsed_time(e1) / reps
     n_sel = int(torch.clamp(torch.arange(1, L + 1, device="cuda"), max=k).sum())
     # attention backward, staged: per selected pair and KV group the K and V rows gathered
-    # (2 x 256 B) and the dK / dV contribution written and read back (2 x 1 KiB)
+    # (2 x 256 B) and the dK / dV contribution written and read back (2 x 1 KiB); indexer
+    # backward, staged: per selected pair the key row (128 B + scale) gathered and the dk^I
+    # contribution written and read back (2 x 512 B)
     attn_bytes = n_sel * G * (2 * cfg.d * 2 + 2 * 2 * cfg.d * 4)
-    atom_ix = n_sel * cfg.dI
+    ix_bytes = n_sel * (cfg.dI + 4 + 2 * cfg.dI * 4)
     step = sum(ms.values())
     res = {"workload": cfg.name + "_train_step", "tokens": L, "selected_pairs": n_sel,
            "ms": {n: round(v, 3) for n, v in ms.items()}, "ms_per_step": round(step, 3),
            "tokens_per_s": round(L / (step * 1e-3), 1),
            "attn_bwd_bytes": attn_bytes,
            "attn_bwd_hbm_frac": round(attn_bytes / (ms["attn_bwd_kl"] * 1e-3) / PEAK["hbm"], 4),
-           "index_bwd_atomic_frac": round(atom_ix / (ms["index_at_bwd"] * 1e-3) / ATOMIC_FLOATS_PER_S, 4),
+           "index_bwd_bytes": ix_bytes,
+           "index_bwd_hbm_frac": round(ix_bytes / (ms["index_at_bwd"] * 1e-3) / PEAK["hbm"], 4),
            "mean_kl": round(float(kl.mean()), 5)}
-    del x, idx, out, lse, vals, dq, dk, dv, kl, dI, dqi, dw, dki, dout, bws
+    del x, idx, out, lse, vals, dq, dk, dv, kl, dI, dqi, dw, dki, dout, bws, iws
     torch.cuda.empty_cache()
     return res
 

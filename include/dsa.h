@@ -310,15 +310,20 @@ dsa_status_t dsa_index_scores_at(const void* q_idx, const float* q_scale, const 
  * Backward of dsa_index_scores_at: given g float [Tq, topk] = dL/dvals, the gradients of L
  * with respect to the dequantised indexer inputs (FP8 rounding taken as the identity,
  * ReLU'(0) = 0):  dq_idx float [Tq, HI, dI] and dw float [Tq, HI] are written; dk_idx
- * float [Tk, dI] is ACCUMULATED with atomic adds (zero it first; the order of the adds, and
- * so the last bits, vary between runs).  Entries of idx that are -1 or out of range
- * contribute nothing.  FP8 only, dI = 128, 1 <= HI <= 64.  No workspace.
+ * float [Tk, dI] is ACCUMULATED (zero it first).  Entries of idx that are -1 or out of range
+ * contribute nothing.  FP8 only, dI = 128, 1 <= HI <= 64.
+ * With a workspace of dsa_index_scores_at_bwd_workspace_size() bytes (nonzero when HI is a
+ * multiple of 16) the dk_idx contributions are stored per (row, entry) for chunks of rows and
+ * summed per position in row order: dk_idx is then bit-reproducible.  With ws = NULL
+ * (ws_bytes 0) they are added with fp32 atomic adds, whose order, and so the last bits, vary.
  */
+size_t dsa_index_scores_at_bwd_workspace_size(int Tq, int Tk, int HI, int topk);
 dsa_status_t dsa_index_scores_at_bwd(const void* q_idx, const float* q_scale, const float* w,
                                      const void* k_idx, const float* k_scale,
                                      dsa_dtype_t idx_dtype, int Tq, int Tk, int HI, int dI,
                                      const int32_t* idx, int topk, const float* g,
-                                     float* dq_idx, float* dw, float* dk_idx, hipStream_t stream);
+                                     float* dq_idx, float* dw, float* dk_idx, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
 
 /*
  * Sparse attention forward that also keeps what the backward needs: as dsa_sparse_gqa_attn

@@ -32,7 +32,7 @@ EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
            "dsa_prefill", "dsa_prefill_varlen", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
            "dsa_quantize_e4m3", "dsa_cache_append", "dsa_index_scores_at",
-           "dsa_index_scores_at_bwd", "dsa_sparse_gqa_attn_lse", "dsa_sparse_gqa_attn_bwd_workspace_size",
+           "dsa_index_scores_at_bwd_workspace_size", "dsa_index_scores_at_bwd", "dsa_sparse_gqa_attn_lse", "dsa_sparse_gqa_attn_bwd_workspace_size",
            "dsa_sparse_gqa_attn_bwd"]
 
 
@@ -82,7 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_quantize_e4m3": ([P, I, I, I, P, P, P], I),
             "dsa_cache_append": ([P, P, I, P, I, P, P, I, I, I, I, I, I, I, P, P, P, P, P], I),
             "dsa_index_scores_at": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P], I),
-            "dsa_index_scores_at_bwd": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P, P, P, P], I),
+            "dsa_index_scores_at_bwd_workspace_size": ([I, I, I, I], SZ),
+            "dsa_index_scores_at_bwd": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P, P, P, P, SZ, P], I),
             "dsa_sparse_gqa_attn_lse": ([P, P, P, I, I, P, I, I, I, I, I, F, P, P, P, SZ, P], I),
             "dsa_sparse_gqa_attn_bwd_workspace_size": ([I, I, I, I], SZ),
             "dsa_sparse_gqa_attn_bwd": ([P, P, P, I, I, P, I, I, I, I, I, F, P, P, P, P, P, P, P, P,
@@ -394,11 +395,16 @@ def dsa_index_scores_at(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI
         dI, _ptr(idx), topk, _ptr(vals), _stream(stream)))
 
 
+def dsa_index_scores_at_bwd_workspace_size(Tq, Tk, HI, topk) -> int:
+    return load_library().dsa_index_scores_at_bwd_workspace_size(Tq, Tk, HI, topk)
+
+
 def dsa_index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI, idx,
-                            topk, g, dq_idx, dw, dk_idx, stream=None):
+                            topk, g, dq_idx, dw, dk_idx, ws=None, ws_bytes=0, stream=None):
     _check(load_library().dsa_index_scores_at_bwd(
         _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale), idx_dtype, Tq, Tk, HI,
-        dI, _ptr(idx), topk, _ptr(g), _ptr(dq_idx), _ptr(dw), _ptr(dk_idx), _stream(stream)))
+        dI, _ptr(idx), topk, _ptr(g), _ptr(dq_idx), _ptr(dw), _ptr(dk_idx), _ptr(ws), ws_bytes,
+        _stream(stream)))
 
 
 def index_scores_at(q_idx, q_scale, w, k_idx, k_scale, idx, stream=None):
@@ -411,15 +417,21 @@ def index_scores_at(q_idx, q_scale, w, k_idx, k_scale, idx, stream=None):
     return vals
 
 
-def index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, idx, g, stream=None):
-    """(dq_idx [Tq, HI, dI], dw [Tq, HI], dk_idx [Tk, dI]) fp32 gradients of sum g * vals."""
+def index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, idx, g, staged=True, ws=None,
+                        stream=None):
+    """(dq_idx [Tq, HI, dI], dw [Tq, HI], dk_idx [Tk, dI]) fp32 gradients of sum g * vals;
+    staged: the deterministic reduction of dk_idx through a workspace when H^I allows it."""
     import torch
     Tq, HI, dI = q_idx.shape
     dq = torch.empty(Tq, HI, dI, dtype=torch.float32, device=q_idx.device)
     dw = torch.empty(Tq, HI, dtype=torch.float32, device=q_idx.device)
     dk = torch.zeros(k_idx.shape[0], dI, dtype=torch.float32, device=q_idx.device)
+    n = dsa_index_scores_at_bwd_workspace_size(Tq, k_idx.shape[0], HI, idx.shape[1]) if staged else 0
+    if n and (ws is None or ws.numel() < n):
+        ws = workspace(n, q_idx.device)
     dsa_index_scores_at_bwd(q_idx, q_scale, w, k_idx, k_scale, DSA_FP8_E4M3, Tq, k_idx.shape[0],
-                            HI, dI, idx, idx.shape[1], g, dq, dw, dk, stream)
+                            HI, dI, idx, idx.shape[1], g, dq, dw, dk, ws if n else None,
+                            ws.numel() if n else 0, stream)
     return dq, dw, dk
 
 

@@ -519,35 +519,56 @@ __global__ __launch_bounds__(256) void stage_mark_kernel(const int32_t* __restri
     }
 }
 
+// Exclusive prefix of the per-key entry counts in three passes: each block of 256 keys scans
+// its own counts and leaves its total in bsum; one workgroup scans the block totals; each key
+// then adds its block's offset.  offs[n_kv] gets the total.
 __global__ __launch_bounds__(256) void stage_count_kernel(const uint32_t* __restrict__ mask,
-                                                          int n_kv, int W, int32_t* __restrict__ cnt)
+                                                          int n_kv, int W, int32_t* __restrict__ offs,
+                                                          int32_t* __restrict__ bsum)
 {
+    __shared__ int red[4];
     const int s = blockIdx.x * 256 + threadIdx.x;
-    if (s >= n_kv) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int c = 0;
-    for (int w = 0; w < W; ++w) c += __popc(mask[(int64_t)s * W + w]);
-    cnt[s] = c;
+    if (s < n_kv)
+        for (int w = 0; w < W; ++w) c += __popc(mask[(int64_t)s * W + w]);
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(x, o, 64); if (lane >= o) x += y; }
+    if (lane == 63) red[wave] = x;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += red[w];
+    if (s < n_kv) offs[s] = base + x - c;
+    if (threadIdx.x == 255) bsum[blockIdx.x] = base + x;
 }
 
-// In-place exclusive scan of cnt[0 .. n) by one workgroup; cnt[n] gets the total.
-__global__ __launch_bounds__(1024) void stage_scan_kernel(int32_t* __restrict__ cnt, int n)
+__global__ __launch_bounds__(1024) void stage_scan_kernel(int32_t* __restrict__ bsum, int nb,
+                                                          int32_t* __restrict__ total)
 {
     __shared__ int red[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (n + 1023) / 1024;
-    const int b = min(n, tid * per), e = min(n, b + per);
+    const int per = (nb + 1023) / 1024;
+    const int b = min(nb, tid * per), e = min(nb, b + per);
     int local = 0;
-    for (int i = b; i < e; ++i) local += cnt[i];
+    for (int i = b; i < e; ++i) local += bsum[i];
     int x = local;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(x, o, 64); if (lane >= o) x += y; }
     if (lane == 63) red[wave] = x;
     __syncthreads();
-    int base = 0, total = 0;
-    for (int w = 0; w < 16; ++w) { if (w < wave) base += red[w]; total += red[w]; }
+    int base = 0, all = 0;
+    for (int w = 0; w < 16; ++w) { if (w < wave) base += red[w]; all += red[w]; }
     int run = base + x - local;
-    for (int i = b; i < e; ++i) { const int c = cnt[i]; cnt[i] = run; run += c; }
-    if (tid == 0) cnt[n] = total;
+    for (int i = b; i < e; ++i) { const int c = bsum[i]; bsum[i] = run; run += c; }
+    if (tid == 0) *total = all;
+}
+
+__global__ __launch_bounds__(256) void stage_add_kernel(int32_t* __restrict__ offs, int n_kv,
+                                                        const int32_t* __restrict__ bsum)
+{
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s < n_kv) offs[s] += bsum[blockIdx.x];
 }
 
 __global__ __launch_bounds__(256) void stage_list_kernel(const int32_t* __restrict__ idx, int r0,
@@ -605,6 +626,37 @@ __global__ __launch_bounds__(256) void stage_reduce_kernel(const float* __restri
         o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
         *reinterpret_cast<float4*>(dst) = o;
     }
+}
+
+// The same for rows of 128 floats with one destination (the indexer's dk^I): one wave per key.
+__global__ __launch_bounds__(64) void stage_reduce128_kernel(const float* __restrict__ stg,
+                                                             const int32_t* __restrict__ offs,
+                                                             const int32_t* __restrict__ list,
+                                                             float* __restrict__ dst)
+{
+    const int s = blockIdx.x;
+    const int b = offs[s], e = offs[s + 1];
+    if (b == e) return;
+    const int lane = threadIdx.x;
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    float ax = 0.f, ay = 0.f;
+    int j = b;
+    for (; j + 4 <= e; j += 4) {
+        v2f x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            x[u] = __builtin_nontemporal_load(reinterpret_cast<const v2f*>(stg + (int64_t)list[j + u] * 128) + lane);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) { ax += x[u][0]; ay += x[u][1]; }
+    }
+    for (; j < e; ++j) {
+        const v2f x = __builtin_nontemporal_load(reinterpret_cast<const v2f*>(stg + (int64_t)list[j] * 128) + lane);
+        ax += x[0]; ay += x[1];
+    }
+    float2* o = reinterpret_cast<float2*>(dst + (int64_t)s * 128) + lane;
+    float2 v = *o;
+    v.x += ax; v.y += ay;
+    *o = v;
 }
 
 // fp32 kernel (vector ALU; exact-ish reference-grade path).  One workgroup per
@@ -800,8 +852,9 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, hipStream_t stream)
 
 hipError_t launch_stage_reduce(const int32_t* idx, int r0, int C, int topk, int n_kv, int G,
                                const float* stg, uint32_t* mask, int32_t* offs, int32_t* list,
-                               float* dk, float* dv, hipStream_t stream)
+                               float* dk, float* dv, hipStream_t stream, int width)
 {
+    if (width != 256 && width != 128) return hipErrorInvalidValue;
     if (C == 0 || n_kv == 0) return hipSuccess;
     const int W = (C + 31) / 32;
     const int64_t nm = (int64_t)n_kv * W, ne = (int64_t)C * topk;
@@ -809,10 +862,16 @@ hipError_t launch_stage_reduce(const int32_t* idx, int r0, int C, int topk, int 
     const unsigned ge = (unsigned)std::min<int64_t>((ne + 255) / 256, 65536);
     hipLaunchKernelGGL(fill_u32_kernel, dim3(gm), dim3(256), 0, stream, mask, nm);
     hipLaunchKernelGGL(stage_mark_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, n_kv, W, mask);
-    hipLaunchKernelGGL(stage_count_kernel, dim3((n_kv + 255) / 256), dim3(256), 0, stream, mask, n_kv, W, offs);
-    hipLaunchKernelGGL(stage_scan_kernel, dim3(1), dim3(1024), 0, stream, offs, n_kv);
+    const int nb = (n_kv + 255) / 256;
+    int32_t* bsum = offs + n_kv + 1;                  // nb more entries after the offsets
+    hipLaunchKernelGGL(stage_count_kernel, dim3(nb), dim3(256), 0, stream, mask, n_kv, W, offs, bsum);
+    hipLaunchKernelGGL(stage_scan_kernel, dim3(1), dim3(1024), 0, stream, bsum, nb, offs + n_kv);
+    hipLaunchKernelGGL(stage_add_kernel, dim3(nb), dim3(256), 0, stream, offs, n_kv, bsum);
     hipLaunchKernelGGL(stage_list_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, n_kv, W, mask, offs, list);
-    hipLaunchKernelGGL(stage_reduce_kernel, dim3(n_kv), dim3(256), 0, stream, stg, offs, list, G, dk, dv);
+    if (width == 256)
+        hipLaunchKernelGGL(stage_reduce_kernel, dim3(n_kv), dim3(256), 0, stream, stg, offs, list, G, dk, dv);
+    else
+        hipLaunchKernelGGL(stage_reduce128_kernel, dim3(n_kv), dim3(64), 0, stream, stg, offs, list, dk);
     return hipGetLastError();
 }
 

@@ -695,22 +695,78 @@ DSA_EXPORT dsa_status_t dsa_index_scores_at(const void* q_idx, const float* q_sc
     return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer-at launch");
 }
 
+namespace {
+
+// Chunks of the staged indexer backward: at most 1024 rows (a 32-word row bitmask per key)
+// and 1 GiB of staged dk^I contributions (512 bytes per selected entry).
+struct IxBwdPlan {
+    int chunk;
+    size_t stg_bytes, mask_bytes, offs_bytes, list_bytes, total;
+};
+
+IxBwdPlan plan_ix_bwd(int Tq, int Tk, int topk) {
+    IxBwdPlan p;
+    const size_t per_row = (size_t)topk * 128 * sizeof(float);
+    int64_t c = (int64_t)((size_t(1) << 30) / per_row) / 32 * 32;
+    c = std::max<int64_t>(32, std::min<int64_t>(c, 1024));
+    const int64_t tq32 = ((int64_t)Tq + 31) / 32 * 32;
+    p.chunk = (int)std::min<int64_t>(c, tq32);
+    p.stg_bytes = round_up((size_t)p.chunk * per_row);
+    p.mask_bytes = round_up((size_t)Tk * (p.chunk / 32) * sizeof(uint32_t));
+    p.offs_bytes = round_up(((size_t)Tk + 1 + ((size_t)Tk + 255) / 256) * sizeof(int32_t));
+    p.list_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
+    p.total = p.stg_bytes + p.mask_bytes + p.offs_bytes + p.list_bytes;
+    return p;
+}
+
+}  // namespace
+
+DSA_EXPORT size_t dsa_index_scores_at_bwd_workspace_size(int Tq, int Tk, int HI, int topk) {
+    if (Tq <= 0 || Tk <= 0 || topk <= 0 || !dsa::index_at_bwd_stages(HI)) return 0;
+    return plan_ix_bwd(Tq, Tk, topk).total;
+}
+
 DSA_EXPORT dsa_status_t dsa_index_scores_at_bwd(const void* q_idx, const float* q_scale,
                                                 const float* w, const void* k_idx,
                                                 const float* k_scale, dsa_dtype_t idx_dtype,
                                                 int Tq, int Tk, int HI, int dI,
                                                 const int32_t* idx, int topk, const float* g,
                                                 float* dq_idx, float* dw, float* dk_idx,
-                                                hipStream_t stream) {
+                                                void* ws, size_t ws_bytes, hipStream_t stream) {
     g_err[0] = 0;
     dsa_status_t st = check_index_at(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI,
                                      idx, topk, 64);
     if (st != DSA_OK) return st;
     REQUIRE_PTR4(g); REQUIRE_PTR(dq_idx); REQUIRE_PTR4(dw); REQUIRE_PTR(dk_idx);
-    const hipError_t e = dsa::launch_index_at_bwd(static_cast<const uint8_t*>(q_idx), q_scale, w,
-                                                  static_cast<const uint8_t*>(k_idx), k_scale, Tq,
-                                                  Tk, HI, idx, topk, g, dq_idx, dw, dk_idx, stream);
-    return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer backward launch");
+    const auto* qi8 = static_cast<const uint8_t*>(q_idx);
+    const auto* ki8 = static_cast<const uint8_t*>(k_idx);
+    if (!ws) {                                     // atomic adds straight into dk_idx
+        REQUIRE(ws_bytes == 0, DSA_ERR_WORKSPACE, "ws is NULL but ws_bytes is %zu", ws_bytes);
+        const hipError_t e = dsa::launch_index_at_bwd(qi8, q_scale, w, ki8, k_scale, Tq, Tk, HI,
+                                                      idx, topk, g, dq_idx, dw, dk_idx, stream);
+        return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer backward launch");
+    }
+    REQUIRE(dsa::index_at_bwd_stages(HI), DSA_ERR_UNSUPPORTED,
+            "the staged indexer backward needs HI a multiple of 16 (got %d); pass ws = NULL", HI);
+    if (Tq == 0) return DSA_OK;
+    const IxBwdPlan plan = plan_ix_bwd(Tq, Tk, topk);
+    REQUIRE(aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
+            "the staged indexer backward needs %zu workspace bytes (got %zu)", plan.total, ws_bytes);
+    char* wp = static_cast<char*>(ws);
+    float* stg = reinterpret_cast<float*>(wp);              wp += plan.stg_bytes;
+    uint32_t* mask = reinterpret_cast<uint32_t*>(wp);       wp += plan.mask_bytes;
+    int32_t* offs = reinterpret_cast<int32_t*>(wp);         wp += plan.offs_bytes;
+    int32_t* list = reinterpret_cast<int32_t*>(wp);
+    for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
+        const int rows = std::min(plan.chunk, Tq - r0);
+        hipError_t e = dsa::launch_index_at_bwd(qi8, q_scale, w, ki8, k_scale, rows, Tk, HI, idx,
+                                                topk, g, dq_idx, dw, dk_idx, stream, r0, stg);
+        if (e == hipSuccess && Tk > 0)
+            e = dsa::launch_stage_reduce(idx, r0, rows, topk, Tk, 1, stg, mask, offs, list,
+                                         dk_idx, nullptr, stream, 128);
+        if (e != hipSuccess) return hip_fail(e, "indexer backward launch");
+    }
+    return DSA_OK;
 }
 
 DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_lse(const void* q, const void* k, const void* v,
@@ -755,7 +811,7 @@ BwdPlan plan_bwd(int Tq, int topk, int G, int n_kv) {
     p.chunk = (int)std::min<int64_t>(c, tq32);
     p.stg_bytes = round_up((size_t)p.chunk * per_row);
     p.mask_bytes = round_up((size_t)n_kv * (p.chunk / 32) * sizeof(uint32_t));
-    p.offs_bytes = round_up(((size_t)n_kv + 1) * sizeof(int32_t));
+    p.offs_bytes = round_up(((size_t)n_kv + 1 + ((size_t)n_kv + 255) / 256) * sizeof(int32_t));
     p.list_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
     p.total = p.stg_bytes + p.mask_bytes + p.offs_bytes + p.list_bytes;
     return p;

@@ -114,10 +114,13 @@ struct AttnBwdArgs {
 hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 // The deterministic reduction of staged contributions (chunk of C rows starting at row r0):
 // mark each key's selecting rows in a bitmask [n_kv][C / 32], count and scan them into
-// offsets [n_kv + 1], list each key's entries in row order, and add their sums into dk / dv.
+// offsets [n_kv + 1] (offs needs n_kv + 1 + ceil(n_kv / 256) entries: the block totals follow),
+// list each key's entries in row order, and add their sums into dk / dv.
+// width 256: rows of [dV 128 | dK 128] per group into dv / dk [n_kv, G, 128];
+// width 128: rows of 128 into dk [n_kv, 128] (G = 1, dv unused).
 hipError_t launch_stage_reduce(const int32_t* idx, int r0, int C, int topk, int n_kv, int G,
                                const float* stg, uint32_t* mask, int32_t* offs, int32_t* list,
-                               float* dk, float* dv, hipStream_t stream);
+                               float* dk, float* dv, hipStream_t stream, int width = 256);
 // Splits used for a given shape when a workspace is available (1 = no split).
 int attn_num_splits(int Tq, int topk);
 size_t attn_partials_bytes(int Tq, int nsplit, int Hq, int d);
@@ -139,9 +142,12 @@ hipError_t launch_cache_append(const void* k_new, const void* v_new, int kv_row_
 hipError_t launch_index_at(const uint8_t* q_idx, const float* q_scale, const float* w,
                            const uint8_t* k_idx, const float* k_scale, int T, int Tk, int HI,
                            const int32_t* idx, int topk, float* vals, hipStream_t stream);
+// Rows r0 .. r0 + T - 1.  With stg set (and H^I a multiple of 16), the dk contribution of
+// entry e = (row - r0) * topk + i is stored at stg[e * 128 .. +128) instead of added atomically.
 hipError_t launch_index_at_bwd(const uint8_t* q_idx, const float* q_scale, const float* w,
                                const uint8_t* k_idx, const float* k_scale, int T, int Tk, int HI,
                                const int32_t* idx, int topk, const float* g, float* dq, float* dw,
-                               float* dk, hipStream_t stream);
+                               float* dk, hipStream_t stream, int r0 = 0, float* stg = nullptr);
+bool index_at_bwd_stages(int HI);            // whether the staged form exists for this H^I
 
 }  // namespace dsa

@@ -281,7 +281,8 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, int Tk,
     const int32_t* __restrict__ idx, int topk, const float* __restrict__ g,
-    float* __restrict__ dq, float* __restrict__ dw, float* __restrict__ dk)
+    float* __restrict__ dq, float* __restrict__ dw, float* __restrict__ dk, int r0,
+    float* __restrict__ stg)
 {
     constexpr int HI = NHT * 16;
     constexpr int NHC = (HI + 31) / 32;                  // 32-head chunks of the dk product
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t gb[4][kBwdKeys][64 + 8];   // keys x heads
     __shared__ __attribute__((aligned(16))) uint8_t kcs[4][kBwdKeys][128 + 16]; // key codes
     __shared__ __attribute__((aligned(16))) float st[4][kBwdKeys][32 + 4];      // dk staging
-    const int64_t t = blockIdx.x;
+    const int64_t t = r0 + blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int c0 = 32 * wave;                            // this wave's d_I columns
@@ -393,7 +394,12 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
             const int key = 2 * m + (lane >> 5);
             const int i = i0 + key;
             const int s = i < topk ? idx[t * topk + i] : -1;
-            if (s >= 0 && s < Tk) atomicAdd(dk + (int64_t)s * 128 + c0 + (lane & 31), st[wave][key][lane & 31]);
+            if (s < 0 || s >= Tk) continue;
+            const float val = st[wave][key][lane & 31];
+            if (stg)                                     // streaming store, reduced later
+                __builtin_nontemporal_store(val, stg + ((t - r0) * topk + i) * 128 + c0 + (lane & 31));
+            else
+                atomicAdd(dk + (int64_t)s * 128 + c0 + (lane & 31), val);
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -437,20 +443,23 @@ hipError_t launch_index_at(const uint8_t* q_idx, const float* q_scale, const flo
     return hipGetLastError();
 }
 
+bool index_at_bwd_stages(int HI) { return HI % 16 == 0 && HI <= kIxHIMax; }
+
 hipError_t launch_index_at_bwd(const uint8_t* q_idx, const float* q_scale, const float* w,
                                const uint8_t* k_idx, const float* k_scale, int T, int Tk, int HI,
                                const int32_t* idx, int topk, const float* g, float* dq, float* dw,
-                               float* dk, hipStream_t stream)
+                               float* dk, hipStream_t stream, int r0, float* stg)
 {
     if (T == 0) return hipSuccess;
     if (HI > kIxHIMax) return hipErrorInvalidValue;
     const dim3 grid(T), block(kIxThreads);
     switch (HI % 16 == 0 ? HI / 16 : 0) {
-    case 1: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<1>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk); break;
-    case 2: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<2>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk); break;
-    case 3: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<3>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk); break;
-    case 4: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<4>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk); break;
+    case 1: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<1>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk, r0, stg); break;
+    case 2: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<2>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk, r0, stg); break;
+    case 3: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<3>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk, r0, stg); break;
+    case 4: hipLaunchKernelGGL(index_at_bwd_mfma_kernel<4>, grid, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, Tk, idx, topk, g, dq, dw, dk, r0, stg); break;
     default:
+        if (stg || r0) return hipErrorInvalidValue;    // the vector-ALU form adds atomically
         hipLaunchKernelGGL(index_at_bwd_kernel, grid, block, 0, stream, q_idx, q_scale, w, k_idx,
                            k_scale, Tk, HI, idx, topk, g, dq, dw, dk);
     }

@@ -212,11 +212,18 @@ def test_training_side_argument_checks(lib):
     bad = list(ok); bad[12] = None
     assert f(*bad) == 1 and b"vals" in lib.dsa_last_error()
     fb = lib.dsa_index_scores_at_bwd
-    okb = [A, A, A, A, A, dsa.DSA_FP8_E4M3, 16, 100, 64, 128, A, 2048, A, A, A, A, None]
+    okb = [A, A, A, A, A, dsa.DSA_FP8_E4M3, 16, 100, 64, 128, A, 2048, A, A, A, A, None, 0, None]
     bad = list(okb); bad[8] = 128
     assert fb(*bad) == 2                                         # the backward takes HI <= 64
     bad = list(okb); bad[15] = None
     assert fb(*bad) == 1 and b"dk_idx" in lib.dsa_last_error()
+    assert lib.dsa_index_scores_at_bwd_workspace_size(16, 100, 12, 2048) == 0   # no staged form
+    n = lib.dsa_index_scores_at_bwd_workspace_size(16, 100, 64, 2048)
+    assert n >= 32 * 2048 * 512
+    bad = list(okb); bad[16] = A; bad[17] = n - 1
+    assert fb(*bad) == 3 and b"workspace" in lib.dsa_last_error()
+    bad = list(okb); bad[8] = 12; bad[16] = A; bad[17] = n
+    assert fb(*bad) == 2 and b"multiple of 16" in lib.dsa_last_error()
     fl = lib.dsa_sparse_gqa_attn_lse
     okl = [A, A, A, dsa.DSA_BF16, 100, A, 16, 2048, 32, 4, 128, 0.1, A, A, None, 0, None]
     bad = list(okl); bad[13] = None
