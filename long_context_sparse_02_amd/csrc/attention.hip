@@ -229,7 +229,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
 //   dq^T += K^T dS                          (kept in registers for the whole row)
 //   dV^T = dO^T P^T, dK^T = q^T dS^T        (per 16 positions; P and dS pass through LDS
 //                                            to become B operands, the results through LDS
-//                                            to become 64-lane atomic adds of whole rows)
+//                                            into whole 512-byte rows: streamed to a staging
+//                                            buffer per (row, entry, group) and summed per
+//                                            position afterwards, or added atomically)
 // and, when the indexer scores at Omega_t are given, the group-mean attention
 // p[t,s,g] = mean_h P goes into a per-wave LDS row sum (summed in a fixed order, so the
 // loss and its gradient are deterministic); at the end of the row the kernel writes

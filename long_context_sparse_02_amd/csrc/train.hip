@@ -266,7 +266,8 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_kernel(
 //   - writes G through LDS as bf16 twice: heads x keys with the key scales folded in (A of
 //     dq = G K) and keys x heads (A of dk = G^T q), and stages the keys' codes,
 //   - accumulates dq [heads x its 32 columns] in registers (bf16 products of G and the key
-//     codes, which bf16 holds exactly) and computes dk [32 keys x its 32 columns], added to
+//     codes, which bf16 holds exactly) and computes dk [32 keys x its 32 columns], streamed
+//     to a staging buffer per (row, entry) and summed per position afterwards, or added to
 //     memory with 32-lane coalesced atomic adds.
 // G is rounded to bf16 for the two products (2^-9 relative per term).
 constexpr int kBwdKeys = 32;
