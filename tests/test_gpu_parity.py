@@ -1121,3 +1121,10 @@ def test_attn_bwd_staged_chunks_deterministic():
     valid_rows = torch.from_numpy((idx >= 0).any(axis=1)).to(DEV)
     do_sum = dout.to(DEV).double()[valid_rows].view(-1, G, Hq // G, 128).sum(dim=(0, 2))
     assert (dv_sum - do_sum).abs().max().item() <= 1e-3 * do_sum.abs().max().item() + 1e-3
+
+
+def test_prefill_varlen_fp32_tiny_layer():
+    """The tiny fp32 layer (fp32 indexer and attention) as a packed batch: each sequence is
+    bitwise its own prefill."""
+    cfg = W.scaled(W.TINY_F32, L=1, seed=360)
+    _varlen_vs_separate(cfg, [700, 0, 257, 1500, 1], 512, "varlen fp32")
