@@ -8,7 +8,8 @@ The functions follow the formulas of the Kwai Keye-VL-2.0 report (xllm-io
 review page, section "核心公式"; report section 2.3): the lightning indexer
 score, the Top-k index set and GQA sparse aggregation, and on the training
 side (``oracle_train.c``; report section 2.3.3 and the review page's sparse
-adaptation loss) the attention backward and the sparse indexer loss.  Every
+adaptation and dense warm-up losses) the attention backward and both indexer
+losses.  Every
 result is float64.  See the C sources for the arithmetic and the readings of
 points the pages leave open.
 """
@@ -71,6 +72,11 @@ def _load():
             lib.oracle_attn_bwd.restype = None
             lib.oracle_indexer_kl.argtypes = [P, P, I, P, I, I, I, I, I, D, P, P, P]
             lib.oracle_indexer_kl.restype = None
+            lib.oracle_indexer_warmup_kl.argtypes = [P, P, I, I, I, I64, I, I, I, D, P, P, P]
+            lib.oracle_indexer_warmup_kl.restype = None
+            lib.oracle_index_scores_bwd_dense.argtypes = [P, P, P, P, P, I, I, I, I, I, I64, P, P,
+                                                          P, P]
+            lib.oracle_index_scores_bwd_dense.restype = None
             lib.oracle_index_scores_at.argtypes = [P, P, P, P, P, I, I, I, I, P, I, P]
             lib.oracle_index_scores_at.restype = None
             lib.oracle_index_scores_bwd.argtypes = [P, P, P, P, P, I, I, I, I, I, P, I, P, P, P, P]
@@ -282,6 +288,22 @@ def indexer_kl(q, k, dtype, idx, G, sm_scale, vals):
     return kl, dI
 
 
+def indexer_warmup_kl(q, k, dtype, G, sm_scale, scores, q_pos0=0):
+    """(kl float64 [T], dI float64 [T, Tk]) of the dense warm-up indexer loss: row t at
+    position q_pos0 + t, its set every key s <= q_pos0 + t; scores [T, Tk] = I[t, s]."""
+    lib = _load()
+    q, k, _, _ = _attn_arrays(q, k, None, dtype, np.zeros((1, 1), np.int32))
+    T, Hq, d = q.shape
+    scores = np.ascontiguousarray(np.asarray(scores, dtype=np.float64))
+    Tk = scores.shape[1]
+    assert scores.shape[0] == T and k.shape[0] >= Tk
+    kl = np.empty(T, dtype=np.float64)
+    dI = np.empty((T, Tk), dtype=np.float64)
+    lib.oracle_indexer_warmup_kl(_ptr(q), _ptr(k), dtype, T, Tk, int(q_pos0), Hq, G, d,
+                                 float(sm_scale), _ptr(scores), _ptr(kl), _ptr(dI))
+    return kl, dI
+
+
 def _indexer_arrays(q_idx, q_scale, w, k_idx, k_scale, idx_dtype):
     el = np.uint8 if idx_dtype == FP8_E4M3 else np.float32
     return (_np(q_idx, el), _np(q_scale, np.float32), _np(w, np.float32), _np(k_idx, el),
@@ -315,4 +337,22 @@ def index_scores_bwd(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, idx, g):
     lib.oracle_index_scores_bwd(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
                                 idx_dtype, T, Tk, HI, dI, _ptr(idx), idx.shape[1], _ptr(g),
                                 _ptr(dq), _ptr(dw), _ptr(dk))
+    return dq, dw, dk
+
+
+def index_scores_bwd_dense(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, g, q_pos0=0):
+    """(dq_idx, dw, dk_idx) float64 for a dense g [T, Tk]: gradients of
+    sum_{t, s <= q_pos0 + t} g[t,s] * I[t,s]."""
+    lib = _load()
+    q_idx, q_scale, w, k_idx, k_scale = _indexer_arrays(q_idx, q_scale, w, k_idx, k_scale, idx_dtype)
+    g = np.ascontiguousarray(np.asarray(g, dtype=np.float64))
+    T, HI, dI = q_idx.shape
+    Tk = g.shape[1]
+    assert g.shape[0] == T and k_idx.shape[0] >= Tk
+    dq = np.empty((T, HI, dI), dtype=np.float64)
+    dw = np.empty((T, HI), dtype=np.float64)
+    dk = np.empty((Tk, dI), dtype=np.float64)
+    lib.oracle_index_scores_bwd_dense(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx),
+                                      _ptr(k_scale), idx_dtype, T, Tk, HI, dI, int(q_pos0),
+                                      _ptr(g), _ptr(dq), _ptr(dw), _ptr(dk))
     return dq, dw, dk

@@ -80,6 +80,13 @@ void oracle_indexer_kl(const void* q, const void* k, int dtype, const int32_t* i
                        int Hq, int G, int d, double sm_scale, const double* vals, double* kl,
                        double* dI);
 
+/* Dense warm-up indexer loss (report section 2.3.3; review page, "核心公式", dense warm-up
+ * loss): as oracle_indexer_kl with the set of row t the whole causal prefix
+ * {0 .. q_pos0 + t} (cut at Tk); scores [T, Tk] = I[t, s]; dI [T, Tk] (0 beyond the prefix). */
+void oracle_indexer_warmup_kl(const void* q, const void* k, int dtype, int T, int Tk,
+                              int64_t q_pos0, int Hq, int G, int d, double sm_scale,
+                              const double* scores, double* kl, double* dI);
+
 /* vals[t, i] = I[t, idx[t, i]] (-inf for padding). */
 void oracle_index_scores_at(const void* q_idx, const float* q_scale, const float* w,
                             const void* k_idx, const float* k_scale, int idx_dtype, int T,
@@ -91,6 +98,12 @@ void oracle_index_scores_bwd(const void* q_idx, const float* q_scale, const floa
                              const void* k_idx, const float* k_scale, int idx_dtype, int T,
                              int Tk, int HI, int dI, const int32_t* idx, int kk, const double* g,
                              double* dq_idx, double* dw, double* dk_idx);
+
+/* The same for a dense g [T, Tk]: row t takes g[t, s] for s <= q_pos0 + t only. */
+void oracle_index_scores_bwd_dense(const void* q_idx, const float* q_scale, const float* w,
+                                   const void* k_idx, const float* k_scale, int idx_dtype, int T,
+                                   int Tk, int HI, int dI, int64_t q_pos0, const double* g,
+                                   double* dq_idx, double* dw, double* dk_idx);
 
 int oracle_num_threads(void);
 

@@ -25,8 +25,12 @@
  *      sum_g ( softmax(I[t,Omega_t])_s - p[t,s,g] );
  *    the target is a constant (the report detaches the indexer's inputs from
  *    the main model, so the loss trains the indexer only);
+ *  - the dense warm-up loss of the same section (review page, "核心公式", dense
+ *    warm-up loss): the same divergence with the set of row t the whole causal
+ *    prefix, so it follows the sparse one with that set;
  *  - the indexer scores at the selected positions and the gradient of
- *    sum_{t,i} g[t,i] I[t, Omega_t[i]] with respect to the dequantised
+ *    sum_{t,i} g[t,i] I[t, Omega_t[i]] (or, for the warm-up loss, of
+ *    sum_{t, s <= pos} g[t,s] I[t,s]) with respect to the dequantised
  *    indexer inputs q^I, w and k^I (FP8 rounding taken as the identity;
  *    ReLU'(0) = 0).
  * Every step is in double; -1 entries of an index list are skipped.
@@ -150,38 +154,74 @@ void oracle_attn_bwd(const void* q, const void* k, const void* v, int dtype, con
     }
 }
 
+/* The loss of one row over the index list sel[0 .. kk) (entries -1 skipped) and its gradient
+ * with respect to the scores I[0 .. kk) of those entries; P, p, qI are scratch of kk doubles. */
+static double row_kl(const void* q, const void* k, int dtype, const int32_t* sel, int kk, int t,
+                     int Hq, int G, int d, double sm_scale, const double* I, double* dI, double* P,
+                     double* p, double* qI)
+{
+    int hpg = Hq / G;
+    /* the indexer's distribution over the set */
+    double m = -INFINITY, z = 0.0;
+    for (int i = 0; i < kk; ++i) if (sel[i] >= 0 && I[i] > m) m = I[i];
+    for (int i = 0; i < kk; ++i) z += sel[i] >= 0 ? exp(I[i] - m) : 0.0;
+    for (int i = 0; i < kk; ++i) qI[i] = sel[i] >= 0 ? exp(I[i] - m) / z : 0.0;
+    double loss = 0.0;
+    for (int i = 0; i < kk; ++i) dI[i] = 0.0;
+    for (int g = 0; g < G; ++g) {
+        for (int i = 0; i < kk; ++i) p[i] = 0.0;
+        for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
+            head_probs(q, k, dtype, sel, kk, t, h, g, Hq, G, d, sm_scale, P);
+            for (int i = 0; i < kk; ++i) p[i] += P[i] / hpg;
+        }
+        for (int i = 0; i < kk; ++i) {
+            if (sel[i] < 0) continue;
+            if (p[i] > 0.0) loss += p[i] * (log(p[i]) - log(qI[i]));
+            dI[i] += qI[i] - p[i];
+        }
+    }
+    return loss;
+}
+
 void oracle_indexer_kl(const void* q, const void* k, int dtype, const int32_t* idx, int kk, int T,
                        int Hq, int G, int d, double sm_scale, const double* vals, double* kl,
                        double* dI)
 {
-    int hpg = Hq / G;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int t = 0; t < T; ++t) {
-        const int32_t* sel = idx + (int64_t)t * kk;
-        const double* I = vals + (int64_t)t * kk;
-        double* P = (double*)malloc((size_t)(kk > 0 ? kk : 1) * sizeof(double));
-        double* p = (double*)malloc((size_t)(kk > 0 ? kk : 1) * sizeof(double));
-        double* qI = (double*)malloc((size_t)(kk > 0 ? kk : 1) * sizeof(double));
-        /* the indexer's distribution over the selected set */
-        double m = -INFINITY, z = 0.0;
-        for (int i = 0; i < kk; ++i) if (sel[i] >= 0 && I[i] > m) m = I[i];
-        for (int i = 0; i < kk; ++i) z += sel[i] >= 0 ? exp(I[i] - m) : 0.0;
-        for (int i = 0; i < kk; ++i) qI[i] = sel[i] >= 0 ? exp(I[i] - m) / z : 0.0;
-        double loss = 0.0;
-        for (int i = 0; i < kk; ++i) dI[(int64_t)t * kk + i] = 0.0;
-        for (int g = 0; g < G; ++g) {
-            for (int i = 0; i < kk; ++i) p[i] = 0.0;
-            for (int h = g * hpg; h < (g + 1) * hpg; ++h) {
-                head_probs(q, k, dtype, sel, kk, t, h, g, Hq, G, d, sm_scale, P);
-                for (int i = 0; i < kk; ++i) p[i] += P[i] / hpg;
-            }
-            for (int i = 0; i < kk; ++i) {
-                if (sel[i] < 0) continue;
-                if (p[i] > 0.0) loss += p[i] * (log(p[i]) - log(qI[i]));
-                dI[(int64_t)t * kk + i] += qI[i] - p[i];
-            }
-        }
-        kl[t] = loss;
+        size_t n = (size_t)(kk > 0 ? kk : 1) * sizeof(double);
+        double* P = (double*)malloc(n);
+        double* p = (double*)malloc(n);
+        double* qI = (double*)malloc(n);
+        kl[t] = row_kl(q, k, dtype, idx + (int64_t)t * kk, kk, t, Hq, G, d, sm_scale,
+                       vals + (int64_t)t * kk, dI + (int64_t)t * kk, P, p, qI);
+        free(P);
+        free(p);
+        free(qI);
+    }
+}
+
+/* The dense warm-up loss is the same divergence taken over every key of the causal prefix:
+ * row t sits at position q_pos0 + t and its set is {0, 1, .., q_pos0 + t} (cut at Tk). */
+void oracle_indexer_warmup_kl(const void* q, const void* k, int dtype, int T, int Tk,
+                              int64_t q_pos0, int Hq, int G, int d, double sm_scale,
+                              const double* scores, double* kl, double* dI)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < T; ++t) {
+        int64_t pos = q_pos0 + t;
+        int n = (int)(pos + 1 < Tk ? pos + 1 : Tk);
+        size_t bytes = (size_t)(n > 0 ? n : 1) * sizeof(double);
+        int32_t* sel = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+        double* P = (double*)malloc(bytes);
+        double* p = (double*)malloc(bytes);
+        double* qI = (double*)malloc(bytes);
+        for (int s = 0; s < n; ++s) sel[s] = s;
+        double* drow = dI + (int64_t)t * Tk;
+        kl[t] = row_kl(q, k, dtype, sel, n, t, Hq, G, d, sm_scale, scores + (int64_t)t * Tk, drow,
+                       P, p, qI);
+        for (int s = n; s < Tk; ++s) drow[s] = 0.0;
+        free(sel);
         free(P);
         free(p);
         free(qI);
@@ -250,6 +290,26 @@ void oracle_index_scores_at(const void* q_idx, const float* q_scale, const float
     }
 }
 
+/* Adds the gradients of gi * I[t,s] to dq (row t's HI x dI block), dw (row t's HI entries)
+ * and dk_idx; qv is row t's dequantised query, kv scratch of dI doubles. */
+static void add_score_grads(const void* q_idx, const float* q_scale, const float* w,
+                            const void* k_idx, const float* k_scale, int idx_dtype, int64_t t,
+                            int64_t s, double gi, int HI, int dI, const double* qv, double* kv,
+                            double* dq, double* dw, double* dk_idx)
+{
+    deq_key(k_idx, k_scale, idx_dtype, s, dI, kv);
+    for (int j = 0; j < HI; ++j) {
+        double x = indexer_dot(q_idx, q_scale, k_idx, k_scale, idx_dtype, t, j, s, HI, dI);
+        if (x <= 0.0) continue;               /* ReLU'(x) = 0 for x <= 0 */
+        double wj = (double)w[t * HI + j];
+        dw[j] += gi * x;
+        for (int e = 0; e < dI; ++e) {
+            dq[(int64_t)j * dI + e] += gi * wj * kv[e];
+            dk_idx[s * dI + e] += gi * wj * qv[(int64_t)j * dI + e];
+        }
+    }
+}
+
 void oracle_index_scores_bwd(const void* q_idx, const float* q_scale, const float* w,
                              const void* k_idx, const float* k_scale, int idx_dtype, int T,
                              int Tk, int HI, int dI, const int32_t* idx, int kk, const double* g,
@@ -266,19 +326,35 @@ void oracle_index_scores_bwd(const void* q_idx, const float* q_scale, const floa
         for (int i = 0; i < kk; ++i) {
             int s = idx[(int64_t)t * kk + i];
             if (s < 0) continue;
-            double gi = g[(int64_t)t * kk + i];
-            deq_key(k_idx, k_scale, idx_dtype, s, dI, kv);
-            for (int j = 0; j < HI; ++j) {
-                double x = indexer_dot(q_idx, q_scale, k_idx, k_scale, idx_dtype, t, j, s, HI, dI);
-                if (x <= 0.0) continue;               /* ReLU'(x) = 0 for x <= 0 */
-                double wj = (double)w[(int64_t)t * HI + j];
-                dw[(int64_t)t * HI + j] += gi * x;
-                for (int e = 0; e < dI; ++e) {
-                    dq[(int64_t)j * dI + e] += gi * wj * kv[e];
-                    dk_idx[(int64_t)s * dI + e] += gi * wj * qv[(int64_t)j * dI + e];
-                }
-            }
+            add_score_grads(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, t, s,
+                            g[(int64_t)t * kk + i], HI, dI, qv, kv, dq, dw + (int64_t)t * HI,
+                            dk_idx);
         }
+    }
+    free(qv);
+    free(kv);
+}
+
+/* The same gradients for a dense g [T, Tk] over the causal prefix: row t (position
+ * q_pos0 + t) takes g[t, s] for every s <= q_pos0 + t; the entries beyond are ignored. */
+void oracle_index_scores_bwd_dense(const void* q_idx, const float* q_scale, const float* w,
+                                   const void* k_idx, const float* k_scale, int idx_dtype, int T,
+                                   int Tk, int HI, int dI, int64_t q_pos0, const double* g,
+                                   double* dq_idx, double* dw, double* dk_idx)
+{
+    memset(dk_idx, 0, (size_t)Tk * dI * sizeof(double));
+    double* qv = (double*)malloc((size_t)HI * dI * sizeof(double));
+    double* kv = (double*)malloc((size_t)dI * sizeof(double));
+    for (int t = 0; t < T; ++t) {
+        deq_query(q_idx, q_scale, idx_dtype, t, HI, dI, qv);
+        double* dq = dq_idx + (int64_t)t * HI * dI;
+        memset(dq, 0, (size_t)HI * dI * sizeof(double));
+        for (int j = 0; j < HI; ++j) dw[(int64_t)t * HI + j] = 0.0;
+        int64_t last = q_pos0 + t < Tk - 1 ? q_pos0 + t : Tk - 1;
+        for (int64_t s = 0; s <= last; ++s)
+            add_score_grads(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, t, s,
+                            g[(int64_t)t * Tk + s], HI, dI, qv, kv, dq, dw + (int64_t)t * HI,
+                            dk_idx);
     }
     free(qv);
     free(kv);

@@ -655,3 +655,93 @@ def test_indexer_scores_at_equal_full_rows_gathered():
     valid = idx >= 0
     np.testing.assert_allclose(vals[valid], np.take_along_axis(full, np.maximum(idx, 0), 1)[valid],
                                rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------- dense warm-up indexer loss
+
+def _dense_case(rng, T, Tk, Hq, G, d, q_pos0):
+    q = (rng.integers(-64, 65, (T, Hq, d)) / 64.0).astype(np.float32)
+    k = (rng.integers(-64, 65, (Tk, G, d)) / 64.0).astype(np.float32)
+    pos = q_pos0 + np.arange(T)
+    causal = np.arange(Tk)[None, :] <= pos[:, None]          # [T, Tk]
+    scores = np.where(causal, rng.normal(size=(T, Tk)), -np.inf)
+    return q, k, causal, scores
+
+
+def test_warmup_kl_matches_dense_masked_softmax_autograd():
+    """Every row against torch float64 over the full causal score matrix: a masked softmax per
+    head, the mean over each group's heads, the log-softmax of I, and autograd for dI."""
+    rng = np.random.default_rng(48)
+    T, Tk, Hq, G, d, q_pos0, sm = 6, 11, 8, 4, 8, 4, 0.45
+    q, k, causal, scores = _dense_case(rng, T, Tk, Hq, G, d, q_pos0)
+    kl, dI = oracle.indexer_warmup_kl(q, k, oracle.F32, G, sm, scores, q_pos0=q_pos0)
+    qd, kd = torch.from_numpy(q).double(), torch.from_numpy(k).double()
+    hpg = Hq // G
+    kh = kd[:, torch.arange(Hq) // hpg, :]                     # [Tk, Hq, d]
+    logits = sm * torch.einsum("thd,shd->ths", qd, kh)         # [T, Hq, Tk]
+    mask = torch.from_numpy(causal)
+    P = torch.softmax(logits.masked_fill(~mask[:, None, :], float("-inf")), dim=-1)
+    pg = P.view(T, G, hpg, Tk).mean(dim=2)                     # [T, G, Tk]
+    It = torch.tensor(np.where(causal, scores, 0.0), requires_grad=True)
+    logq = torch.log_softmax(It.masked_fill(~mask, float("-inf")), dim=-1).masked_fill(~mask, 0.0)
+    loss = (torch.special.xlogy(pg, pg) - pg * logq[:, None, :]).sum(dim=(1, 2))
+    loss.sum().backward()
+    np.testing.assert_allclose(kl, loss.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dI, np.where(causal, It.grad.numpy(), 0.0), rtol=0, atol=1e-12)
+    assert np.all(dI[~causal] == 0.0)
+    np.testing.assert_allclose(dI.sum(axis=1), 0.0, atol=1e-12)
+
+
+def test_warmup_kl_uniform_target_closed_form():
+    """q = 0 makes every head attend uniformly to the n = pos + 1 keys of its prefix, so
+    KL[t] = G (-ln n - mean_s log softmax(I)_s) and dI = G (softmax(I) - 1/n); equal scores
+    then give KL = 0."""
+    rng = np.random.default_rng(49)
+    T, Tk, Hq, G, d, q_pos0, sm = 5, 9, 4, 2, 8, 2, 1.3
+    q, k, causal, scores = _dense_case(rng, T, Tk, Hq, G, d, q_pos0)
+    q[:] = 0.0
+    kl, dI = oracle.indexer_warmup_kl(q, k, oracle.F32, G, sm, scores, q_pos0=q_pos0)
+    for t in range(T):
+        n = q_pos0 + t + 1
+        row = scores[t, :n]
+        ls = row - row.max() - math.log(np.exp(row - row.max()).sum())
+        assert kl[t] == pytest.approx(G * (-math.log(n) - ls.mean()), rel=1e-12, abs=1e-12)
+        np.testing.assert_allclose(dI[t, :n], G * (np.exp(ls) - 1.0 / n), rtol=0, atol=1e-13)
+    flat = np.where(causal, 2.5, -np.inf)
+    kl0, dI0 = oracle.indexer_warmup_kl(q, k, oracle.F32, G, sm, flat, q_pos0=q_pos0)
+    np.testing.assert_allclose(kl0, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dI0, 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_index_scores_bwd_dense_matches_autograd(fp8):
+    """The dense indexer backward against torch float64 autograd of the whole score matrix
+    I[t, s] = sum_j w ReLU(q^I_j . k^I_s), with g applied on the causal part only."""
+    rng = np.random.default_rng(50)
+    T, Tk, HI, dI, q_pos0 = 5, 10, 4, 8, 3
+    w = rng.normal(size=(T, HI)).astype(np.float32)
+    if fp8:
+        qc = rng.integers(0, 256, (T, HI, dI), dtype=np.uint8)
+        kc = rng.integers(0, 256, (Tk, dI), dtype=np.uint8)
+        qc[(qc & 0x7F) == 0x7F] = 0x38
+        kc[(kc & 0x7F) == 0x7F] = 0x38
+        qs = rng.uniform(0.01, 0.1, T).astype(np.float32)
+        ks = rng.uniform(0.01, 0.1, Tk).astype(np.float32)
+        lut = np.array([oracle.e4m3_to_double(c) for c in range(256)])
+        qd, kd = lut[qc] * qs[:, None, None], lut[kc] * ks[:, None]
+        args = (qc, qs, w, kc, ks, oracle.FP8_E4M3)
+    else:
+        qd = rng.normal(size=(T, HI, dI)).astype(np.float32)
+        kd = rng.normal(size=(Tk, dI)).astype(np.float32)
+        args = (qd, None, w, kd, None, oracle.F32)
+    causal = np.arange(Tk)[None, :] <= (q_pos0 + np.arange(T))[:, None]
+    g = rng.normal(size=(T, Tk))
+    dq, dw, dk = oracle.index_scores_bwd_dense(*args, g, q_pos0=q_pos0)
+    qt = torch.tensor(np.asarray(qd, dtype=np.float64), requires_grad=True)
+    kt = torch.tensor(np.asarray(kd, dtype=np.float64), requires_grad=True)
+    wt = torch.tensor(w.astype(np.float64), requires_grad=True)
+    It = (wt[:, :, None] * torch.relu(torch.einsum("tjd,sd->tjs", qt, kt))).sum(dim=1)
+    (It * torch.from_numpy(np.where(causal, g, 0.0))).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-12, atol=1e-12)
