@@ -161,11 +161,13 @@ static double row_kl(const void* q, const void* k, int dtype, const int32_t* sel
                      double* p, double* qI)
 {
     int hpg = Hq / G;
-    /* the indexer's distribution over the set */
+    /* the indexer's distribution over the set; qI holds its logarithm I - logsumexp(I), which
+     * stays finite where exp underflows */
     double m = -INFINITY, z = 0.0;
     for (int i = 0; i < kk; ++i) if (sel[i] >= 0 && I[i] > m) m = I[i];
     for (int i = 0; i < kk; ++i) z += sel[i] >= 0 ? exp(I[i] - m) : 0.0;
-    for (int i = 0; i < kk; ++i) qI[i] = sel[i] >= 0 ? exp(I[i] - m) / z : 0.0;
+    double lz = m + log(z);
+    for (int i = 0; i < kk; ++i) qI[i] = sel[i] >= 0 ? I[i] - lz : 0.0;
     double loss = 0.0;
     for (int i = 0; i < kk; ++i) dI[i] = 0.0;
     for (int g = 0; g < G; ++g) {
@@ -176,8 +178,8 @@ static double row_kl(const void* q, const void* k, int dtype, const int32_t* sel
         }
         for (int i = 0; i < kk; ++i) {
             if (sel[i] < 0) continue;
-            if (p[i] > 0.0) loss += p[i] * (log(p[i]) - log(qI[i]));
-            dI[i] += qI[i] - p[i];
+            if (p[i] > 0.0) loss += p[i] * (log(p[i]) - qI[i]);
+            dI[i] += exp(qI[i]) - p[i];
         }
     }
     return loss;

@@ -745,3 +745,20 @@ def test_index_scores_bwd_dense_matches_autograd(fp8):
     np.testing.assert_allclose(dq, qt.grad.numpy(), rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(dw, wt.grad.numpy(), rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_kl_finite_when_scores_lie_far_below_the_max():
+    """A score 1000 below the row's best makes exp underflow in double; the divergence is
+    still the finite value of the definition.  q = 0 (uniform target over the two keys):
+    KL = G (-ln 2 - (1/2) sum_s log softmax(I)_s) with log softmax = (-ln(1 + e^-1000), -1000)."""
+    T, Tk, Hq, G, d, sm = 2, 2, 4, 2, 8, 1.0
+    q = np.zeros((T, Hq, d), dtype=np.float32)
+    k = np.ones((Tk, G, d), dtype=np.float32)
+    scores = np.array([[0.0, -np.inf], [0.0, -1000.0]])
+    kl, dI = oracle.indexer_warmup_kl(q, k, oracle.F32, G, sm, scores)
+    assert kl[0] == 0.0
+    assert kl[1] == pytest.approx(G * (-math.log(2.0) + 500.0), rel=1e-14)
+    np.testing.assert_allclose(dI[1], [G * (1.0 - 0.5), G * (0.0 - 0.5)], atol=1e-15)
+    idx = np.array([[0, -1], [0, 1]], dtype=np.int32)
+    kl2, _ = oracle.indexer_kl(q, k, oracle.F32, idx, G, sm, np.where(idx >= 0, scores, -np.inf))
+    assert np.isfinite(kl2).all() and kl2[1] == pytest.approx(kl[1], rel=1e-14)
