@@ -364,6 +364,55 @@ dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v
                                      void* dq, float* dk, float* dv, const float* vals, float* kl,
                                      float* dI, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * ---- Training side: the dense warm-up stage of report section 2.3.3 ----
+ * Before the sparse stage the indexer is trained against the dense attention with
+ * L = sum_t sum_g KL(p[t,:,g] || softmax(I[t,:])) over every key s <= t (review page,
+ * "核心公式", dense warm-up loss).  One step: dsa_index_scores (the full causal rows of I),
+ * dsa_indexer_warmup_kl (turns them into dL/dI in place), dsa_index_scores_bwd_dense.
+ * Rows may be processed in chunks (q_pos0 > 0), as in prefill.
+ */
+
+/*
+ * Dense warm-up loss and its gradient.  q [Tq, Hq, d] and K [Tk, G, d] bf16 (d = 128) are the
+ * main attention's query heads (row t at position q_pos0 + t) and keys; head h belongs to
+ * group h / (Hq / G).  p[t,s,g] is the mean over the group's heads of
+ * softmax_s(sm_scale q_h . K[s, g]) over s <= q_pos0 + t; lse float [Tq, Hq] (natural log of
+ * that softmax's normaliser, as a dense attention forward returns it) may be passed to skip
+ * its computation, or NULL.  scores float [Tq, ld_scores] holds I[t, s] for s <= q_pos0 + t
+ * (as dsa_index_scores writes it) and is overwritten there with
+ *   dL/dI[t, s] = G softmax(I[t, 0..pos])_s - sum_g p[t,s,g];
+ * entries beyond the prefix are left as they are.  kl float [Tq] receives
+ * sum_g KL(p[t,:,g] || softmax(I[t,:])).  The target p is a constant (the indexer's inputs are
+ * detached from the main model).  Supported: Hq / G in {1, 2} or a multiple of 4, with
+ * G * max(1, Hq / G / 4) <= 8; Tk >= q_pos0 + Tq.  fp32 softmax from bf16 matrix-core scores.
+ * No workspace; deterministic.
+ */
+dsa_status_t dsa_indexer_warmup_kl(const void* q, const void* k, dsa_dtype_t dtype, int Tq, int Tk,
+                                   int64_t q_pos0, int Hq, int G, int d, float sm_scale,
+                                   const float* lse, float* scores, int64_t ld_scores, float* kl,
+                                   hipStream_t stream);
+
+/*
+ * Backward of the dense indexer scores: given g float [Tq, ld_g] = dL/dI[t, s] for
+ * s <= q_pos0 + t (entries beyond are ignored), the gradients with respect to the
+ * dequantised indexer inputs (FP8 rounding taken as the identity, ReLU'(0) = 0):
+ * dq_idx float [Tq, HI, dI] and dw float [Tq, HI] are written; dk_idx float [Tk, dI] is
+ * ACCUMULATED (zero it first; chunks of rows add into it in call order).  FP8 only,
+ * dI = 128, HI in {16, 32, 48, 64}; scales non-negative (as the quantiser makes them).
+ * The gradient G = dI w [x > 0] is rounded to bf16 for the two matrix-core products.
+ * Workspace: dsa_index_scores_bwd_dense_workspace_size() bytes (bf16 copies of the codes and
+ * partial sums of dk_idx over ranges of rows, added in a fixed order): every output is
+ * bit-reproducible.
+ */
+size_t dsa_index_scores_bwd_dense_workspace_size(int Tq, int Tk, int HI);
+dsa_status_t dsa_index_scores_bwd_dense(const void* q_idx, const float* q_scale, const float* w,
+                                        const void* k_idx, const float* k_scale,
+                                        dsa_dtype_t idx_dtype, int Tq, int Tk, int HI, int dI,
+                                        int64_t q_pos0, const float* g, int64_t ld_g,
+                                        float* dq_idx, float* dw, float* dk_idx, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

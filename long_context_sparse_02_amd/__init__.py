@@ -33,7 +33,8 @@ EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_prefill", "dsa_prefill_varlen", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
            "dsa_quantize_e4m3", "dsa_cache_append", "dsa_index_scores_at",
            "dsa_index_scores_at_bwd_workspace_size", "dsa_index_scores_at_bwd", "dsa_sparse_gqa_attn_lse", "dsa_sparse_gqa_attn_bwd_workspace_size",
-           "dsa_sparse_gqa_attn_bwd"]
+           "dsa_sparse_gqa_attn_bwd", "dsa_indexer_warmup_kl",
+           "dsa_index_scores_bwd_dense_workspace_size", "dsa_index_scores_bwd_dense"]
 
 
 class DSAError(RuntimeError):
@@ -88,6 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_sparse_gqa_attn_bwd_workspace_size": ([I, I, I, I], SZ),
             "dsa_sparse_gqa_attn_bwd": ([P, P, P, I, I, P, I, I, I, I, I, F, P, P, P, P, P, P, P, P,
                                          P, P, SZ, P], I),
+            "dsa_indexer_warmup_kl": ([P, P, I, I, I, I64, I, I, I, F, P, P, I64, P, P], I),
+            "dsa_index_scores_bwd_dense_workspace_size": ([I, I, I], SZ),
+            "dsa_index_scores_bwd_dense": ([P, P, P, P, P, I, I, I, I, I, I64, P, I64, P, P, P, P,
+                                            SZ, P], I),
         }
         for name in EXPORTS:
             fn = getattr(lib, name)
@@ -489,3 +494,53 @@ def sparse_gqa_attn_bwd(q, k, v, idx, G, sm_scale, out, dout, lse, vals=None, st
                             sm_scale, out, dout, lse, dq, dk, dv, vals, kl, dI,
                             ws if n else None, ws.numel() if n else 0, stream)
     return (dq, dk, dv) if vals is None else (dq, dk, dv, kl, dI)
+
+
+def dsa_indexer_warmup_kl(q, k, dtype, Tq, Tk, q_pos0, Hq, G, d, sm_scale, lse, scores, ld_scores,
+                          kl, stream=None):
+    _check(load_library().dsa_indexer_warmup_kl(
+        _ptr(q), _ptr(k), dtype, Tq, Tk, q_pos0, Hq, G, d, float(sm_scale), _ptr(lse),
+        _ptr(scores), ld_scores, _ptr(kl), _stream(stream)))
+
+
+def dsa_index_scores_bwd_dense_workspace_size(Tq, Tk, HI) -> int:
+    return load_library().dsa_index_scores_bwd_dense_workspace_size(Tq, Tk, HI)
+
+
+def dsa_index_scores_bwd_dense(q_idx, q_scale, w, k_idx, k_scale, idx_dtype, Tq, Tk, HI, dI,
+                               q_pos0, g, ld_g, dq_idx, dw, dk_idx, ws=None, ws_bytes=0,
+                               stream=None):
+    _check(load_library().dsa_index_scores_bwd_dense(
+        _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale), idx_dtype, Tq, Tk, HI, dI,
+        q_pos0, _ptr(g), ld_g, _ptr(dq_idx), _ptr(dw), _ptr(dk_idx), _ptr(ws), ws_bytes,
+        _stream(stream)))
+
+
+def indexer_warmup_kl(q, k, G, sm_scale, scores, Tk, q_pos0=0, lse=None, stream=None):
+    """Dense warm-up loss: kl [Tq] fp32; scores [Tq, ld] (I over the causal prefix) is
+    overwritten in place with dL/dI."""
+    import torch
+    Tq, Hq, d = q.shape
+    kl = torch.empty(Tq, dtype=torch.float32, device=q.device)
+    dsa_indexer_warmup_kl(q, k, dtype_code(q), Tq, Tk, q_pos0, Hq, G, d, sm_scale, lse, scores,
+                          scores.shape[1], kl, stream)
+    return kl
+
+
+def index_scores_bwd_dense(q_idx, q_scale, w, k_idx, k_scale, g, Tk, q_pos0=0, dk=None, ws=None,
+                           stream=None):
+    """(dq_idx [Tq, HI, dI], dw [Tq, HI], dk_idx [Tk, dI]) fp32 gradients of
+    sum_{s <= pos} g[t, s] I[t, s]; dk (if given) is accumulated into."""
+    import torch
+    Tq, HI, dI = q_idx.shape
+    dq = torch.empty(Tq, HI, dI, dtype=torch.float32, device=q_idx.device)
+    dw = torch.empty(Tq, HI, dtype=torch.float32, device=q_idx.device)
+    if dk is None:
+        dk = torch.zeros(Tk, dI, dtype=torch.float32, device=q_idx.device)
+    n = dsa_index_scores_bwd_dense_workspace_size(Tq, Tk, HI)
+    if n and (ws is None or ws.numel() < n):
+        ws = workspace(n, q_idx.device)
+    dsa_index_scores_bwd_dense(q_idx, q_scale, w, k_idx, k_scale, DSA_FP8_E4M3, Tq, Tk, HI, dI,
+                               q_pos0, g, g.shape[1], dq, dw, dk, ws if n else None,
+                               ws.numel() if n else 0, stream)
+    return dq, dw, dk

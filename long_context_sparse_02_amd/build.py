@@ -26,7 +26,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-fno-strict-alia
 # the compiler would canonicalise every matrix-core result first, doubling the
 # vector-ALU work of its inner loop.  Indexer inputs are finite FP8 values.
 EXTRA = {"indexer.hip": ["-fno-honor-nans"]}
-SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "cache.hip", "train.hip", "dsa_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "cache.hip", "train.hip", "warmup.hip", "dsa_api.cpp"]
 
 
 def _hipcc() -> str:

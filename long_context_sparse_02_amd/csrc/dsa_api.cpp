@@ -878,3 +878,69 @@ DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, co
     }
     return DSA_OK;
 }
+
+// ---- Dense warm-up stage (report section 2.3.3; review page, dense warm-up loss) ----
+
+DSA_EXPORT dsa_status_t dsa_indexer_warmup_kl(const void* q, const void* k, dsa_dtype_t dtype,
+                                              int Tq, int Tk, int64_t q_pos0, int Hq, int G,
+                                              int d, float sm_scale, const float* lse,
+                                              float* scores, int64_t ld_scores, float* kl,
+                                              hipStream_t stream) {
+    g_err[0] = 0;
+    REQUIRE(dtype == DSA_BF16, DSA_ERR_UNSUPPORTED, "the warm-up loss takes BF16 q and K (got %d)",
+            (int)dtype);
+    REQUIRE(d == 128, DSA_ERR_UNSUPPORTED, "head size d must be 128 (got %d)", d);
+    REQUIRE(G >= 1 && Hq >= 1 && Hq % G == 0, DSA_ERR_INVALID_ARG,
+            "Hq (%d) must be a positive multiple of G (%d)", Hq, G);
+    REQUIRE(dsa::warmup_kl_supported(Hq, G), DSA_ERR_UNSUPPORTED,
+            "the warm-up loss takes Hq/G in {1, 2} or a multiple of 4, with G * max(1, Hq/G/4) <= 8 "
+            "(got Hq=%d, G=%d)", Hq, G);
+    REQUIRE(Tq >= 0 && Tk >= 0 && q_pos0 >= 0, DSA_ERR_INVALID_ARG, "negative size or position");
+    REQUIRE((int64_t)Tk >= q_pos0 + Tq, DSA_ERR_INVALID_ARG,
+            "Tk (%d) must cover every query's prefix (q_pos0 + Tq = %lld)", Tk,
+            (long long)(q_pos0 + Tq));
+    REQUIRE(ld_scores >= Tk, DSA_ERR_INVALID_ARG, "ld_scores (%lld) must be >= Tk (%d)",
+            (long long)ld_scores, Tk);
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR4(scores); REQUIRE_OPT_PTR4(lse); REQUIRE_PTR4(kl);
+    const hipError_t e = dsa::launch_warmup_kl(static_cast<const uint16_t*>(q),
+                                               static_cast<const uint16_t*>(k), Tq, Tk, q_pos0, Hq,
+                                               G, sm_scale, lse, scores, ld_scores, kl, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "warm-up loss launch");
+}
+
+DSA_EXPORT size_t dsa_index_scores_bwd_dense_workspace_size(int Tq, int Tk, int HI) {
+    if (Tq <= 0 || Tk <= 0 || HI <= 0 || HI % 16 || HI > 64) return 0;
+    return round_up(dsa::plan_warmup_bwd(Tq, Tk, HI).total);
+}
+
+DSA_EXPORT dsa_status_t dsa_index_scores_bwd_dense(const void* q_idx, const float* q_scale,
+                                                   const float* w, const void* k_idx,
+                                                   const float* k_scale, dsa_dtype_t idx_dtype,
+                                                   int Tq, int Tk, int HI, int dI, int64_t q_pos0,
+                                                   const float* g, int64_t ld_g, float* dq_idx,
+                                                   float* dw, float* dk_idx, void* ws,
+                                                   size_t ws_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    REQUIRE(idx_dtype == DSA_FP8_E4M3, DSA_ERR_UNSUPPORTED,
+            "the training-side indexer takes FP8 inputs (got dtype %d)", (int)idx_dtype);
+    REQUIRE(dI == 128, DSA_ERR_UNSUPPORTED, "FP8 indexer needs dI == 128 (got %d)", dI);
+    REQUIRE(HI >= 16 && HI <= 64 && HI % 16 == 0, DSA_ERR_UNSUPPORTED,
+            "the dense indexer backward takes HI in {16, 32, 48, 64} (got %d)", HI);
+    REQUIRE(Tq >= 0 && Tk >= 0 && q_pos0 >= 0, DSA_ERR_INVALID_ARG, "negative size or position");
+    REQUIRE((int64_t)Tk >= q_pos0 + Tq, DSA_ERR_INVALID_ARG,
+            "Tk (%d) must cover every query's prefix (q_pos0 + Tq = %lld)", Tk,
+            (long long)(q_pos0 + Tq));
+    REQUIRE(ld_g >= Tk, DSA_ERR_INVALID_ARG, "ld_g (%lld) must be >= Tk (%d)", (long long)ld_g, Tk);
+    REQUIRE_PTR(q_idx); REQUIRE_PTR4(q_scale); REQUIRE_PTR4(w); REQUIRE_PTR(k_idx);
+    REQUIRE_PTR4(k_scale); REQUIRE_PTR4(g); REQUIRE_PTR(dq_idx); REQUIRE_PTR4(dw);
+    REQUIRE_PTR(dk_idx);
+    if (Tq == 0) return DSA_OK;
+    const size_t need = round_up(dsa::plan_warmup_bwd(Tq, Tk, HI).total);
+    REQUIRE(ws && aligned16(ws) && ws_bytes >= need, DSA_ERR_WORKSPACE,
+            "the dense indexer backward needs %zu workspace bytes (got %zu%s)", need, ws_bytes,
+            ws ? "" : ", ws is NULL");
+    const hipError_t e = dsa::launch_warmup_ix_bwd(
+        static_cast<const uint8_t*>(q_idx), q_scale, w, static_cast<const uint8_t*>(k_idx), k_scale,
+        Tq, Tk, HI, q_pos0, g, ld_g, dq_idx, dw, dk_idx, ws, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "dense indexer backward launch");
+}

@@ -150,4 +150,19 @@ hipError_t launch_index_at_bwd(const uint8_t* q_idx, const float* q_scale, const
                                float* dk, hipStream_t stream, int r0 = 0, float* stg = nullptr);
 bool index_at_bwd_stages(int HI);            // whether the staged form exists for this H^I
 
+// Dense warm-up stage of the indexer's training (warmup.hip).
+bool warmup_kl_supported(int Hq, int G);
+hipError_t launch_warmup_kl(const uint16_t* q, const uint16_t* k, int Tq, int Tk, int64_t q_pos0,
+                            int Hq, int G, float sm_scale, const float* lse, float* scores,
+                            int64_t ld, float* kl, hipStream_t stream);
+struct WarmupBwdPlan {
+    int ldk, kblocks, nsplit, rows_per_split;
+    size_t kt_bytes, qt_bytes, part_bytes, total;
+};
+WarmupBwdPlan plan_warmup_bwd(int Tq, int Tk, int HI);
+hipError_t launch_warmup_ix_bwd(const uint8_t* q_idx, const float* q_scale, const float* w,
+                                const uint8_t* k_idx, const float* k_scale, int Tq, int Tk, int HI,
+                                int64_t q_pos0, const float* g, int64_t ld, float* dq, float* dw,
+                                float* dk, void* ws, hipStream_t stream);
+
 }  // namespace dsa

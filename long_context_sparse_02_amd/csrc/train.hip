@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_kernel(
 //     codes, which bf16 holds exactly) and computes dk [32 keys x its 32 columns], streamed
 //     to a staging buffer per (row, entry) and summed per position afterwards, or added to
 //     memory with 32-lane coalesced atomic adds.
-// G is rounded to bf16 for the two products (2^-9 relative per term).
+// G is rounded to bf16 for the two products (2^-8 relative per term, bf16's unit roundoff).
 constexpr int kBwdKeys = 32;
 
 __device__ __forceinline__ uint16_t e4m3_bf16_bits(uint32_t c)

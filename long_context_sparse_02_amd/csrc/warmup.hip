@@ -1,0 +1,653 @@
+// warmup.hip -- the dense warm-up stage of the indexer's training, for gfx950.
+//
+// Section 2.3.3 of the Keye-VL-2.0 report trains the lightning indexer first
+// against the dense attention (xllm-io review page, "核心公式", dense warm-up
+// loss):  L = sum_t sum_g KL( p[t,:,g] || softmax(I[t,:]) ),  the sums over
+// every key s <= t, with p[t,:,g] the attention of KV group g's query heads
+// (their mean; the indexer's inputs are detached from the main model, so p is
+// a constant).  This file holds
+//  - warmup_kl_kernel: per query row the log-sum-exp of each head (unless the
+//    caller passes it), then p, the row's KL and dL/dI[t,s] = G softmax(I)_s -
+//    sum_g p[t,s,g], written over the scores in place.  Scores are bf16
+//    matrix-core products with fp32 accumulation, softmax in fp32;
+//  - the backward of the dense indexer scores, given dL/dI over the causal
+//    prefix: dq^I and dw (one query row per wave, keys streamed through LDS) and
+//    dk^I (keys owned by workgroups, query rows streamed, partial sums over row
+//    ranges added in a fixed order), both on the FP8 and bf16 matrix cores:
+//      x = q^I[t,j] . k^I[s] (FP8 codes, exact products), G = dI w [x > 0],
+//      dq[t,j] = sum_s G k^I[s],  dk[s] = sum_{t,j} G q^I[t,j],
+//      dw[t,j] = sum_s dI ReLU(x),
+//    with G rounded to bf16 for the two products (2^-8 relative per term) and the
+//    FP8 codes' values exact in bf16.  Nothing is added atomically, so every
+//    output is bit-reproducible.
+#include <algorithm>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWuRows = 16;          // query rows per workgroup of the loss kernel
+constexpr int kWuKeys = 16;          // keys per step of the loss kernel
+
+__device__ __forceinline__ v8bf load8bf(const uint16_t* p) {
+    return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(p));
+}
+
+// One step of an online log2-sum-exp2 with a single exp2: (mx, sm) describes
+// sum 2^(y - mx) = sm over the values seen so far.
+__device__ __forceinline__ void lse_step(float y, bool valid, float& mx, float& sm) {
+    const float d = y - mx;                       // +inf while nothing was seen
+    const float e = exp2f(-fabsf(d));
+    const float up = fmaf(sm, e, 1.f), keep = sm + e;
+    sm = valid ? (d > 0.f ? up : keep) : sm;
+    mx = valid ? fmaxf(mx, y) : mx;
+}
+
+// Merge of two (mx, sm) pairs.
+__device__ __forceinline__ void lse_merge(float& mx, float& sm, float mo, float so) {
+    const float mn = fmaxf(mx, mo);
+    const float a = mx == mn ? 1.f : exp2f(mx - mn);
+    const float b = mo == mn ? 1.f : exp2f(mo - mn);
+    sm = sm * a + so * b;
+    mx = mn;
+}
+
+__device__ __forceinline__ void lse_reduce16(float& mx, float& sm) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        const float mo = __shfl_xor(mx, o, 64), so = __shfl_xor(sm, o, 64);
+        lse_merge(mx, sm, mo, so);
+    }
+}
+
+// Workgroup: G * WPG waves for 16 query rows t0 .. t0+15; wave w serves KV group
+// g = w / WPG, query heads g HPG + (w % WPG) HPW + hh, hh < HPW (HPW = min(HPG, 4)
+// heads per wave, WPG = HPG / HPW waves per group).  A wave keeps the A operands of
+// its 16 rows x HPW heads (M rows m = r HPW + hh, 16 per tile) in registers and
+// streams its group's keys 16 at a time as the B operand.
+// Pass 1 (without lse): per (row, head) online log-sum-exp, one exp2 per score,
+// merged over the 16 key lanes at the end; and per row the log-sum-exp of I.
+// Pass 2: each wave's share of p[t,s,g] = mean_h 2^(S log2e sm_scale - lse2[t,h])
+// into LDS, then per (row, key) the groups are combined: KL terms and dI.
+template <int HPW>
+__global__ __launch_bounds__(512) void warmup_kl_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int Tq, int Tk,
+    int64_t q_pos0, int Hq, int G, int HPG, float sm_scale, const float* __restrict__ lse_in,
+    float* __restrict__ scores, int64_t ld, float* __restrict__ kl)
+{
+    constexpr int MT = HPW;                              // M tiles per wave (16 rows x HPW)
+    __shared__ float pbuf[2][8][kWuRows][kWuKeys + 1];
+    __shared__ float lse_i2[kWuRows];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int WPG = HPG / HPW, NW = G * WPG;
+    const int g = wave / WPG;
+    const int hbase = g * HPG + (wave % WPG) * HPW;     // first query head of this wave
+    const int blk = gridDim.x - 1 - blockIdx.x;          // longest rows first
+    const int t0 = blk * kWuRows;
+    const int rows = min(kWuRows, Tq - t0);
+    const int64_t p0 = q_pos0 + t0;
+    const int nkeys = (int)min<int64_t>(p0 + rows, (int64_t)Tk);
+    const float c2 = sm_scale * kLog2e;
+
+    v8bf qa[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + col, r = m / HPW, hh = m % HPW;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (r < rows)
+                qa[mt][ks] = load8bf(q + ((int64_t)(t0 + r) * Hq + hbase + hh) * 128 + 32 * ks + 8 * grp);
+            else
+                qa[mt][ks] = __builtin_bit_cast(v8bf, v4i{0, 0, 0, 0});
+        }
+    }
+    // rows of the I part handled by this lane: r = wave + NW (grp + 4 j), j < nj
+    constexpr int NJ = 4;
+    const int nj = max(1, kWuRows / (4 * NW));
+
+    float lse2[MT][4];
+    {
+        float mx[MT][4], sm[MT][4], mxi[NJ], smi[NJ];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { mx[mt][i] = -INFINITY; sm[mt][i] = 0.f; }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) { mxi[j] = -INFINITY; smi[j] = 0.f; }
+        for (int s0 = 0; s0 < nkeys; s0 += kWuKeys) {
+            const int s = s0 + col;
+            if (!lse_in) {
+                const uint16_t* kp = k + ((int64_t)min(s, Tk - 1) * G + g) * 128 + 8 * grp;
+                v8bf kb[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) kb[ks] = load8bf(kp + 32 * ks);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = (16 * mt + 4 * grp + i) / HPW;
+                        lse_step(acc[i] * c2, r < rows && s <= p0 + r, mx[mt][i], sm[mt][i]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                if (j >= nj) break;
+                const int r = wave + NW * (grp + 4 * j);
+                const bool valid = r < rows && s <= p0 + r;
+                const float y = valid ? scores[(int64_t)(t0 + r) * ld + s] * kLog2e : 0.f;
+                lse_step(y, valid, mxi[j], smi[j]);
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * mt + 4 * grp + i, r = m / HPW, hh = m % HPW;
+                if (lse_in) {
+                    lse2[mt][i] = r < rows ? lse_in[(int64_t)(t0 + r) * Hq + hbase + hh] * kLog2e : 0.f;
+                } else {
+                    lse_reduce16(mx[mt][i], sm[mt][i]);
+                    lse2[mt][i] = mx[mt][i] + log2f(sm[mt][i]);
+                }
+            }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (j >= nj) break;
+            lse_reduce16(mxi[j], smi[j]);
+            const int r = wave + NW * (grp + 4 * j);
+            if (col == 0 && r < kWuRows) lse_i2[r] = mxi[j] + log2f(smi[j]);
+        }
+    }
+    __syncthreads();
+
+    float kacc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) kacc[j] = 0.f;
+    const float inv_h = 1.f / (float)HPG;
+    int b = 0;
+    for (int s0 = 0; s0 < nkeys; s0 += kWuKeys, b ^= 1) {
+        const int s = s0 + col;
+        const uint16_t* kp = k + ((int64_t)min(s, Tk - 1) * G + g) * 128 + 8 * grp;
+        v8bf kb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[ks] = load8bf(kp + 32 * ks);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc);
+            float e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = (16 * mt + 4 * grp + i) / HPW;
+                e[i] = (r < rows && s <= p0 + r) ? exp2f(fmaf(acc[i], c2, -lse2[mt][i])) : 0.f;
+            }
+            // this wave's heads of one row sum to its share of p
+            if constexpr (HPW == 4) {
+                pbuf[b][wave][4 * mt + grp][col] = ((e[0] + e[1]) + (e[2] + e[3])) * inv_h;
+            } else if constexpr (HPW == 2) {
+                pbuf[b][wave][8 * mt + 2 * grp][col] = (e[0] + e[1]) * inv_h;
+                pbuf[b][wave][8 * mt + 2 * grp + 1][col] = (e[2] + e[3]) * inv_h;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pbuf[b][wave][16 * mt + 4 * grp + i][col] = e[i] * inv_h;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (j >= nj) break;
+            const int r = wave + NW * (grp + 4 * j);
+            if (r < rows && s <= p0 + r) {
+                float* sp = scores + (int64_t)(t0 + r) * ld + s;
+                const float I = *sp;
+                const float l2 = fmaf(I, kLog2e, -lse_i2[r]);     // log2 softmax(I)_s
+                const float qi = exp2f(l2);
+                const float lq = l2 * kLn2;
+                float psum = 0.f, term = 0.f;
+                for (int gg = 0; gg < G; ++gg) {
+                    float p = 0.f;
+                    for (int u = 0; u < WPG; ++u) p += pbuf[b][gg * WPG + u][r][col];
+                    psum += p;
+                    term += p > 0.f ? p * (logf(p) - lq) : 0.f;
+                }
+                *sp = (float)G * qi - psum;
+                kacc[j] += term;
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        if (j >= nj) break;
+        float v = kacc[j];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+        const int r = wave + NW * (grp + 4 * j);
+        if (col == 0 && r < rows) kl[t0 + r] = v;
+    }
+}
+
+// OCP E4M3 code -> bf16 bits of its value (exact: at most 4 significant bits)
+__device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (uint16_t)((__float_as_uint(mag) >> 16) | ((c & 0x80u) << 8));
+}
+
+// dst[n][c][r] = bf16 value of the code src[n][r][c] for r < R (0 for R <= r < ldR),
+// c < 128: 64 x 64 tiles through LDS.  Grid (N * ceil(ldR / 64), 2), 256 threads.
+__global__ __launch_bounds__(256) void codes_to_bf16_t_kernel(
+    const uint8_t* __restrict__ src, uint16_t* __restrict__ dst, int R, int ldR,
+    int64_t src_n, int64_t dst_n)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][64 + 8];
+    const int rtiles = (ldR + 63) / 64;
+    const int64_t n = blockIdx.x / rtiles;
+    const int r0 = (blockIdx.x % rtiles) * 64, c0 = blockIdx.y * 64;
+    const int tid = threadIdx.x;
+    {
+        const int r = r0 + tid / 4, cc = 16 * (tid % 4);
+        v4i x = {0, 0, 0, 0};
+        if (r < R) x = *reinterpret_cast<const v4i*>(src + n * src_n + (int64_t)r * 128 + c0 + cc);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            tile[cc + e][tid / 4] = e4m3_to_bf16(((uint32_t)x[e >> 2] >> ((e & 3) * 8)) & 255u);
+    }
+    __syncthreads();
+    const int c = tid / 4, rr = 16 * (tid % 4);
+    if (r0 + rr < ldR) {
+        uint16_t* d = dst + n * dst_n + (int64_t)(c0 + c) * ldR + r0 + rr;
+        const v4i* sp = reinterpret_cast<const v4i*>(&tile[c][rr]);
+        reinterpret_cast<v4i*>(d)[0] = sp[0];
+        reinterpret_cast<v4i*>(d)[1] = sp[1];
+    }
+}
+
+constexpr int kQbWaves = 8;          // query rows (one per wave) per workgroup, dq kernel
+constexpr int kQbKeys = 32;          // keys per step
+
+// dq^I and dw: wave w of the workgroup owns query row t = t0 + w (all HI heads, all
+// 128 columns: NHT x 8 accumulator tiles).  Per step of 32 keys the workgroup
+// stages the key codes and their bf16 values (transposed, [column][key]) in LDS;
+// each wave computes x^T (keys on A, its heads on B), G, dw, and then
+// dq += G' K with A = G' = bf16(G k_scale) (its head rows, keys as K) and B = the
+// keys' bf16 code values.  K slot j of lane group grp stands for key
+// 16 (j / 4) + 4 grp + j % 4 on both operands.
+template <int NHT>
+__global__ __launch_bounds__(512) void warmup_ix_bwd_q_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
+    const uint16_t* __restrict__ kt_bf, int ldk, int Tq, int Tk, int64_t q_pos0,
+    const float* __restrict__ gI, int64_t ld, float* __restrict__ dq, float* __restrict__ dw)
+{
+    constexpr int HI = 16 * NHT;
+    __shared__ __attribute__((aligned(16))) uint8_t kc[2][kQbKeys][128 + 16];
+    __shared__ __attribute__((aligned(16))) uint16_t kt[2][128][kQbKeys + 8];
+    __shared__ __attribute__((aligned(16))) uint8_t qcs[kQbWaves][HI][128 + 16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int blk = gridDim.x - 1 - blockIdx.x;          // longest rows first
+    const int t0 = blk * kQbWaves;
+    const int t = t0 + wave;
+    const bool row_ok = t < Tq;
+    const int64_t pos = q_pos0 + t;
+    const int tl = min(t0 + kQbWaves, Tq) - 1;
+    const int nkeys = (int)min<int64_t>(q_pos0 + tl + 1, (int64_t)Tk);
+
+    // the wave's query row codes (B operands of x^T), read from LDS at every step
+    for (int e = lane; e < HI * 8; e += 64) {
+        const v4i v = row_ok ? *reinterpret_cast<const v4i*>(q_idx + ((int64_t)t * HI + e / 8) * 128 + 16 * (e % 8))
+                             : v4i{0, 0, 0, 0};
+        *reinterpret_cast<v4i*>(&qcs[wave][e / 8][16 * (e % 8)]) = v;
+    }
+    float wv[NHT];
+    const float qs = row_ok ? q_scale[t] : 0.f;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) wv[ht] = row_ok && qs > 0.f ? w[(int64_t)t * HI + 16 * ht + col] : 0.f;
+    v4f acc[NHT][8];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ht][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+    float dwa[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) dwa[ht] = 0.f;
+
+    // staging: threads 0..255 copy 16 code bytes each, all 512 copy 8 bf16 each
+    auto fetch = [&](int s0, v4i& cbytes, v4i& bvals) {
+        if (tid < 256) {
+            const int key = s0 + tid / 8;
+            cbytes = key < Tk ? *reinterpret_cast<const v4i*>(k_idx + (int64_t)key * 128 + 16 * (tid % 8))
+                              : v4i{0, 0, 0, 0};
+        }
+        bvals = *reinterpret_cast<const v4i*>(kt_bf + (int64_t)(tid / 4) * ldk + s0 + 8 * (tid % 4));
+    };
+    auto stash = [&](int buf, const v4i& cbytes, const v4i& bvals) {
+        if (tid < 256) *reinterpret_cast<v4i*>(&kc[buf][tid / 8][16 * (tid % 8)]) = cbytes;
+        *reinterpret_cast<v4i*>(&kt[buf][tid / 4][8 * (tid % 4)]) = bvals;
+    };
+    v4i cb = {0, 0, 0, 0}, bv = {0, 0, 0, 0};
+    if (nkeys > 0) {
+        fetch(0, cb, bv);
+        stash(0, cb, bv);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int s0 = 0; s0 < nkeys; s0 += kQbKeys, buf ^= 1) {
+        const bool more = s0 + kQbKeys < nkeys;
+        if (more) fetch(s0 + kQbKeys, cb, bv);
+        if (row_ok && s0 <= pos) {
+            // with non-negative scales x q_scale k_scale > 0 exactly when x > 0 and both
+            // scales are positive; a zero q_scale zeroes wv, a zero k_scale zeroes gk
+            float gk[2][4];
+#pragma unroll
+            for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = s0 + 16 * kt2 + 4 * grp + i;
+                    const bool ok = s <= pos && s < Tk;
+                    gk[kt2][i] = ok ? gI[(int64_t)t * ld + s] * k_scale[s] : 0.f;
+                }
+            v8bf ga[NHT];
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht) {
+                v8s bits;
+                const v8i qb = *reinterpret_cast<const v8i*>(&qcs[wave][16 * ht + col][32 * grp]);
+#pragma unroll
+                for (int kt2 = 0; kt2 < 2; ++kt2) {
+                    const v8i a = *reinterpret_cast<const v8i*>(&kc[buf][16 * kt2 + col][32 * grp]);
+                    const v4f x = mfma_fp8_16x16x128(a, qb, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool on = x[i] > 0.f;
+                        dwa[ht] += on ? gk[kt2][i] * x[i] : 0.f;
+                        bits[4 * kt2 + i] = (short)f32_to_bf16_bits(on ? gk[kt2][i] * wv[ht] : 0.f);
+                    }
+                }
+                ga[ht] = __builtin_bit_cast(v8bf, bits);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const uint2 lo = *reinterpret_cast<const uint2*>(&kt[buf][16 * ct + col][4 * grp]);
+                const uint2 hi = *reinterpret_cast<const uint2*>(&kt[buf][16 * ct + col][16 + 4 * grp]);
+                const v8bf kb = __builtin_bit_cast(v8bf, v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y});
+#pragma unroll
+                for (int ht = 0; ht < NHT; ++ht) acc[ht][ct] = mfma_bf16_16x16x32(ga[ht], kb, acc[ht][ct]);
+            }
+        }
+        if (more) stash(buf ^ 1, cb, bv);
+        __syncthreads();
+    }
+    if (!row_ok) return;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dq[((int64_t)t * HI + 16 * ht + 4 * grp + i) * 128 + 16 * ct + col] = acc[ht][ct][i];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+        float v = dwa[ht];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (grp == 0) dw[(int64_t)t * HI + 16 * ht + col] = v * qs;
+    }
+}
+
+constexpr int kKbWaves = 8;          // waves per workgroup, dk kernel
+constexpr int kKbKeysW = 32;         // keys per wave
+constexpr int kKbKeys = kKbWaves * kKbKeysW;
+
+// dk^I partial sums: workgroup (key block kb, row range sp) owns 256 keys (32 per wave)
+// and streams the query rows of its range that see them, one row per step (codes,
+// w and the bf16 values [column][head] staged in LDS).  Per row a wave computes x
+// (the row's heads on A, its keys on B), G' = bf16(G q_scale), and
+// dk += G'^T Q with A = G'^T (its keys, heads as K) and B = the row's bf16 code values.
+// K slot j of lane group grp stands for head 32 hc + 16 (j / 4) + 4 grp + j % 4.
+// part[sp][s][c] receives the sum over the range's rows (zeros where none applies).
+template <int NHT>
+__global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale,
+    const uint16_t* __restrict__ qt_bf, int Tq, int Tk, int64_t q_pos0, const float* __restrict__ gI,
+    int64_t ld, int rows_per_split, int ldk, float* __restrict__ part)
+{
+    constexpr int HI = 16 * NHT;
+    constexpr int NHC = (NHT + 1) / 2;
+    __shared__ __attribute__((aligned(16))) uint8_t qc[2][HI][128 + 16];
+    __shared__ __attribute__((aligned(16))) uint16_t qt[2][128][HI + 8];
+    __shared__ float wl[2][HI];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int kb = blockIdx.x, sp = blockIdx.y;
+    const int sw = kb * kKbKeys + wave * kKbKeysW;      // this wave's first key
+    const int sb = kb * kKbKeys;                        // the workgroup's first key
+    const int64_t first = max<int64_t>((int64_t)sp * rows_per_split, (int64_t)sb - q_pos0);
+    const int r_begin = (int)min<int64_t>(max<int64_t>(first, 0), (int64_t)Tq);
+    const int r_end = min(Tq, (sp + 1) * rows_per_split);
+
+    v8i kbop[2];
+    float ksc[2];
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+        const int s = sw + 16 * kt2 + col;
+        kbop[kt2] = s < Tk ? *reinterpret_cast<const v8i*>(k_idx + (int64_t)s * 128 + 32 * grp)
+                           : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        ksc[kt2] = s < Tk ? k_scale[s] : 0.f;
+    }
+    v4f acc[2][8];
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[kt2][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // staging of one row: HI x 128 code bytes (16 per thread) and 128 x HI bf16 values
+    // (8 per piece, NV pieces per thread)
+    constexpr int kCodeThreads = HI * 8;
+    constexpr int NV = (HI * 16 + 511) / 512;
+    auto fetch = [&](int t, v4i& cbytes, v4i* bvals, float& wvl) {
+        if (tid < kCodeThreads)
+            cbytes = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)t * HI + tid / 8) * 128 + 16 * (tid % 8));
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int piece = tid + 512 * u;
+            if (piece < HI * 16)
+                bvals[u] = *reinterpret_cast<const v4i*>(qt_bf + (int64_t)t * 128 * HI + (int64_t)piece * 8);
+        }
+        if (tid < HI) wvl = w[(int64_t)t * HI + tid];
+    };
+    auto stash = [&](int buf, const v4i& cbytes, const v4i* bvals, float wvl) {
+        if (tid < kCodeThreads) *reinterpret_cast<v4i*>(&qc[buf][tid / 8][16 * (tid % 8)]) = cbytes;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int piece = tid + 512 * u;
+            if (piece < HI * 16) {
+                const int e = piece * 8;                     // element e of the [128][HI] row
+                *reinterpret_cast<v4i*>(&qt[buf][e / HI][e % HI]) = bvals[u];
+            }
+        }
+        if (tid < HI) wl[buf][tid] = wvl;
+    };
+    v4i cb = {0, 0, 0, 0}, bv[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) bv[u] = v4i{0, 0, 0, 0};
+    float wvl = 0.f;
+    if (r_begin < r_end) {
+        fetch(r_begin, cb, bv, wvl);
+        stash(0, cb, bv, wvl);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int t = r_begin; t < r_end; ++t, buf ^= 1) {
+        const bool more = t + 1 < r_end;
+        if (more) fetch(t + 1, cb, bv, wvl);
+        const int64_t pos = q_pos0 + t;
+        if (sw <= pos) {
+            const float qs = q_scale[t];
+            float gg[2];
+#pragma unroll
+            for (int kt2 = 0; kt2 < 2; ++kt2) {
+                const int s = sw + 16 * kt2 + col;
+                gg[kt2] = (s <= pos && s < Tk) ? gI[(int64_t)t * ld + s] : 0.f;
+            }
+            v8bf ga[2][NHC];
+#pragma unroll
+            for (int kt2 = 0; kt2 < 2; ++kt2) {
+                v8s bits[NHC];
+#pragma unroll
+                for (int hc = 0; hc < NHC; ++hc) bits[hc] = v8s{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (int ht = 0; ht < NHT; ++ht) {
+                    const v8i a = *reinterpret_cast<const v8i*>(&qc[buf][16 * ht + col][32 * grp]);
+                    const v4f x = mfma_fp8_16x16x128(a, kbop[kt2], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float xv = x[i] * qs * ksc[kt2];
+                        const float gv = xv > 0.f ? gg[kt2] * wl[buf][16 * ht + 4 * grp + i] : 0.f;
+                        bits[ht / 2][4 * (ht % 2) + i] = (short)f32_to_bf16_bits(gv * qs);
+                    }
+                }
+#pragma unroll
+                for (int hc = 0; hc < NHC; ++hc) ga[kt2][hc] = __builtin_bit_cast(v8bf, bits[hc]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int hc = 0; hc < NHC; ++hc) {
+                    const uint2 lo = *reinterpret_cast<const uint2*>(&qt[buf][16 * ct + col][32 * hc + 4 * grp]);
+                    uint2 hi = {0u, 0u};
+                    if (32 * hc + 16 < HI)
+                        hi = *reinterpret_cast<const uint2*>(&qt[buf][16 * ct + col][32 * hc + 16 + 4 * grp]);
+                    const v8bf qbv = __builtin_bit_cast(v8bf, v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y});
+#pragma unroll
+                    for (int kt2 = 0; kt2 < 2; ++kt2) acc[kt2][ct] = mfma_bf16_16x16x32(ga[kt2][hc], qbv, acc[kt2][ct]);
+                }
+        }
+        if (more) stash(buf ^ 1, cb, bv, wvl);
+        __syncthreads();
+    }
+    float* pp = part + (int64_t)sp * ldk * 128;
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = sw + 16 * kt2 + 4 * grp + i;
+            if (s < ldk) {
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) pp[(int64_t)s * 128 + 16 * ct + col] = acc[kt2][ct][i];
+            }
+        }
+}
+
+// dk[s][c] += sum over sp = 0 .. nsplit-1 of part[sp][s][c], in that order.
+__global__ __launch_bounds__(256) void warmup_dk_sum_kernel(const float* __restrict__ part, int nsplit,
+                                                            int64_t stride, int64_t n4,
+                                                            float* __restrict__ dk)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    float4 a = reinterpret_cast<float4*>(dk)[i];
+    for (int sp = 0; sp < nsplit; ++sp) {
+        const float4 b = reinterpret_cast<const float4*>(part + sp * stride)[i];
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    reinterpret_cast<float4*>(dk)[i] = a;
+}
+
+}  // namespace
+
+bool warmup_kl_supported(int Hq, int G)
+{
+    if (G < 1 || Hq % G) return false;
+    const int hpg = Hq / G;
+    if (hpg != 1 && hpg != 2 && hpg % 4) return false;
+    const int hpw = hpg < 4 ? hpg : 4;
+    return G * (hpg / hpw) <= 8;
+}
+
+hipError_t launch_warmup_kl(const uint16_t* q, const uint16_t* k, int Tq, int Tk, int64_t q_pos0,
+                            int Hq, int G, float sm_scale, const float* lse, float* scores,
+                            int64_t ld, float* kl, hipStream_t stream)
+{
+    if (Tq == 0) return hipSuccess;
+    if (!warmup_kl_supported(Hq, G)) return hipErrorInvalidValue;
+    const int hpg = Hq / G, hpw = hpg < 4 ? hpg : 4;
+    const dim3 grid((Tq + kWuRows - 1) / kWuRows), block(64 * G * (hpg / hpw));
+    switch (hpw) {
+    case 1: hipLaunchKernelGGL(warmup_kl_kernel<1>, grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl); break;
+    case 2: hipLaunchKernelGGL(warmup_kl_kernel<2>, grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl); break;
+    default: hipLaunchKernelGGL(warmup_kl_kernel<4>, grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl); break;
+    }
+    return hipGetLastError();
+}
+
+WarmupBwdPlan plan_warmup_bwd(int Tq, int Tk, int HI)
+{
+    WarmupBwdPlan p;
+    p.ldk = (Tk + 63) / 64 * 64;
+    p.kblocks = (Tk + kKbKeys - 1) / kKbKeys;
+    // enough workgroups to fill the chip: split the query rows into ranges
+    const int want = 1024;
+    p.nsplit = Tq > 0 ? std::max(1, std::min((want + p.kblocks - 1) / p.kblocks, (Tq + 63) / 64)) : 1;
+    p.rows_per_split = Tq > 0 ? (Tq + p.nsplit - 1) / p.nsplit : 1;
+    p.kt_bytes = (size_t)128 * p.ldk * 2;
+    p.qt_bytes = (size_t)Tq * 128 * HI * 2;
+    p.part_bytes = (size_t)p.nsplit * p.ldk * 128 * 4;
+    auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+    p.total = up(p.kt_bytes) + up(p.qt_bytes) + up(p.part_bytes);
+    return p;
+}
+
+hipError_t launch_warmup_ix_bwd(const uint8_t* q_idx, const float* q_scale, const float* w,
+                                const uint8_t* k_idx, const float* k_scale, int Tq, int Tk, int HI,
+                                int64_t q_pos0, const float* g, int64_t ld, float* dq, float* dw,
+                                float* dk, void* ws, hipStream_t stream)
+{
+    if (Tq == 0 || Tk == 0) return hipSuccess;
+    if (HI % 16 != 0 || HI > 64) return hipErrorInvalidValue;
+    const WarmupBwdPlan p = plan_warmup_bwd(Tq, Tk, HI);
+    auto up = [](size_t n) { return (n + 255) / 256 * 256; };
+    char* wp = static_cast<char*>(ws);
+    uint16_t* kt = reinterpret_cast<uint16_t*>(wp);   wp += up(p.kt_bytes);
+    uint16_t* qt = reinterpret_cast<uint16_t*>(wp);   wp += up(p.qt_bytes);
+    float* part = reinterpret_cast<float*>(wp);
+    hipLaunchKernelGGL(codes_to_bf16_t_kernel, dim3(p.ldk / 64, 2), dim3(256), 0, stream, k_idx,
+                       kt, Tk, p.ldk, (int64_t)0, (int64_t)0);
+    hipLaunchKernelGGL(codes_to_bf16_t_kernel, dim3(Tq, 2), dim3(256), 0, stream, q_idx, qt, HI, HI,
+                       (int64_t)HI * 128, (int64_t)HI * 128);
+    const dim3 gq((Tq + kQbWaves - 1) / kQbWaves), gk(p.kblocks, p.nsplit), block(512);
+    switch (HI / 16) {
+    case 1:
+        hipLaunchKernelGGL(warmup_ix_bwd_q_kernel<1>, gq, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, kt, p.ldk, Tq, Tk, q_pos0, g, ld, dq, dw);
+        hipLaunchKernelGGL(warmup_ix_bwd_k_kernel<1>, gk, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, qt, Tq, Tk, q_pos0, g, ld, p.rows_per_split, p.ldk, part);
+        break;
+    case 2:
+        hipLaunchKernelGGL(warmup_ix_bwd_q_kernel<2>, gq, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, kt, p.ldk, Tq, Tk, q_pos0, g, ld, dq, dw);
+        hipLaunchKernelGGL(warmup_ix_bwd_k_kernel<2>, gk, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, qt, Tq, Tk, q_pos0, g, ld, p.rows_per_split, p.ldk, part);
+        break;
+    case 3:
+        hipLaunchKernelGGL(warmup_ix_bwd_q_kernel<3>, gq, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, kt, p.ldk, Tq, Tk, q_pos0, g, ld, dq, dw);
+        hipLaunchKernelGGL(warmup_ix_bwd_k_kernel<3>, gk, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, qt, Tq, Tk, q_pos0, g, ld, p.rows_per_split, p.ldk, part);
+        break;
+    case 4:
+        hipLaunchKernelGGL(warmup_ix_bwd_q_kernel<4>, gq, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, kt, p.ldk, Tq, Tk, q_pos0, g, ld, dq, dw);
+        hipLaunchKernelGGL(warmup_ix_bwd_k_kernel<4>, gk, block, 0, stream, q_idx, q_scale, w, k_idx, k_scale, qt, Tq, Tk, q_pos0, g, ld, p.rows_per_split, p.ldk, part);
+        break;
+    }
+    const int64_t n4 = (int64_t)Tk * 128 / 4;
+    hipLaunchKernelGGL(warmup_dk_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
+                       part, p.nsplit, (int64_t)p.ldk * 128, n4, dk);
+    return hipGetLastError();
+}
+
+}  // namespace dsa

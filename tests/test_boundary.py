@@ -247,3 +247,44 @@ def test_training_side_argument_checks(lib):
     assert fw(*bad) == 3 and b"workspace" in lib.dsa_last_error()
     bad = list(okw); bad[22] = 64                                # size without a buffer
     assert fw(*bad) == 3
+
+
+def test_warmup_argument_checks(lib):
+    """Every call below carries one bad argument, so validation fails before any launch."""
+    f = lib.dsa_indexer_warmup_kl
+    ok = [A, A, dsa.DSA_BF16, 16, 100, 84, 32, 4, 128, 0.1, None, A, 100, A, None]
+    bad = list(ok); bad[2] = dsa.DSA_F32
+    assert f(*bad) == 2 and b"BF16" in lib.dsa_last_error()
+    bad = list(ok); bad[8] = 64
+    assert f(*bad) == 2                                          # d must be 128
+    bad = list(ok); bad[6] = 48; bad[7] = 8                      # 6 heads per group
+    assert f(*bad) == 2
+    bad = list(ok); bad[6] = 128; bad[7] = 4                     # 4 groups x 8 waves each
+    assert f(*bad) == 2
+    bad = list(ok); bad[5] = 85                                  # last row's prefix beyond Tk
+    assert f(*bad) == 1 and b"prefix" in lib.dsa_last_error()
+    bad = list(ok); bad[12] = 99
+    assert f(*bad) == 1 and b"ld_scores" in lib.dsa_last_error()
+    bad = list(ok); bad[13] = None
+    assert f(*bad) == 1 and b"kl" in lib.dsa_last_error()
+    bad = list(ok); bad[10] = A + 2; bad[13] = None              # misaligned lse caught first
+    assert f(*bad) == 1 and b"lse" in lib.dsa_last_error()
+    fb = lib.dsa_index_scores_bwd_dense
+    okb = [A, A, A, A, A, dsa.DSA_FP8_E4M3, 16, 100, 64, 128, 84, A, 100, A, A, A, None, 0, None]
+    bad = list(okb); bad[5] = dsa.DSA_F32
+    assert fb(*bad) == 2
+    bad = list(okb); bad[8] = 12
+    assert fb(*bad) == 2 and b"HI" in lib.dsa_last_error()
+    bad = list(okb); bad[8] = 128
+    assert fb(*bad) == 2
+    bad = list(okb); bad[10] = 90
+    assert fb(*bad) == 1 and b"prefix" in lib.dsa_last_error()
+    bad = list(okb); bad[15] = None
+    assert fb(*bad) == 1 and b"dk_idx" in lib.dsa_last_error()
+    assert lib.dsa_index_scores_bwd_dense_workspace_size(16, 100, 12) == 0
+    n = lib.dsa_index_scores_bwd_dense_workspace_size(16, 100, 64)
+    assert n >= 16 * 128 * 64 * 2 + 128 * 128 * 2               # bf16 copies of the codes
+    bad = list(okb)                                              # no workspace
+    assert fb(*bad) == 3 and b"workspace" in lib.dsa_last_error()
+    bad = list(okb); bad[16] = A; bad[17] = n - 1
+    assert fb(*bad) == 3

@@ -926,7 +926,7 @@ def test_index_scores_at_bwd_vs_oracle(T, Tk, HI, topk):
     np.testing.assert_allclose(to_np(vals)[valid], ref_v[valid], rtol=1e-5,
                                atol=1e-6 * np.abs(ref_v[valid]).max())
     # dw is accumulated in fp32; dq and dk take G = dI w [x > 0] rounded to bf16 into the
-    # matrix products (2^-9 relative per term) when H^I is a multiple of 16
+    # matrix products (2^-8 relative per term, the unit roundoff of bf16) when H^I is a multiple of 16
     mfma = HI % 16 == 0
     for name, got, ref in (("dq", dq, rq), ("dw", dw, rw), ("dk", dk, rk)):
         got = to_np(got).astype(np.float64)
@@ -965,7 +965,7 @@ def test_attn_lse_vs_oracle(T, Tk, topk):
 def test_attn_bwd_and_indexer_kl_vs_oracle(T, Tk, topk, G):
     """Attention backward (dq, and dk / dv summed over every row) and the fused sparse
     indexer loss against the oracle.  Errors are bounded by the bf16 rounding of P and dS
-    that feed the matrix products (2^-9 relative per term) and of dq's output: 1e-2 of the
+    that feed the matrix products (2^-8 relative per term) and of dq's output: 1e-2 of the
     largest reference magnitude elementwise."""
     rng = np.random.default_rng(T + topk)
     Hq = 32
