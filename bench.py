@@ -55,7 +55,9 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-packed", action="store_true")
     p.add_argument("--no-train", action="store_true")
-    p.add_argument("--profile-kernel", choices=["index", "topk", "attn", "train"], default=None,
+    p.add_argument("--no-warmup-stage", action="store_true",
+                   help="skip the dense warm-up training step")
+    p.add_argument("--profile-kernel", choices=["index", "topk", "attn", "train", "warmup"], default=None,
                    help="profiling driver: run only this kernel on one chunk of the workload "
                         "(--profile-chunk, default the last) --profile-reps times, print nothing else; "
                         "'train': only the 32K training step, printing its JSON record")
@@ -439,6 +441,74 @@ def run_train_bench(args, dsa, W, torch):
     return res
 
 
+def run_warmup_bench(args, dsa, W, torch):
+    """One dense warm-up training step of the layer at 32K (report section 2.3.3): the indexer's
+    full causal score rows, the warm-up loss with dL/dI written over them (the heads'
+    log-sum-exp computed, not given), and the dense indexer backward."""
+    cfg = W.PREFILL_32K
+    log("generating", cfg.name, "(warm-up step)")
+    x = W.prefill_inputs(cfg, "cuda")
+    L, G, HI, dI, Hq, d = cfg.L, cfg.G, cfg.HI, cfg.dI, cfg.Hq, cfg.d
+    ld = (L + 3) // 4 * 4
+    scores = torch.empty(L, ld, dtype=torch.float32, device="cuda")
+    kl = torch.empty(L, dtype=torch.float32, device="cuda")
+    dqi = torch.empty(x["q_idx"].shape, dtype=torch.float32, device="cuda")
+    dw = torch.empty(x["w"].shape, dtype=torch.float32, device="cuda")
+    dki = torch.empty(x["k_idx"].shape, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    F8 = dsa.DSA_FP8_E4M3
+    n_ix = dsa.dsa_index_scores_workspace_size(L, HI, dI, F8)
+    ixws = dsa.workspace(n_ix) if n_ix else None
+    bws = dsa.workspace(dsa.dsa_index_scores_bwd_dense_workspace_size(L, L, HI))
+    parts = {
+        "index_scores": lambda: dsa.dsa_index_scores(
+            x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"], F8, L, L, HI, dI, 0,
+            scores, ld, ixws, n_ix, stream),
+        "warmup_kl": lambda: dsa.dsa_indexer_warmup_kl(
+            x["q"], x["k"], dsa.DSA_BF16, L, L, 0, Hq, G, d, cfg.sm_scale, None, scores, ld, kl,
+            stream),
+        "index_bwd_dense": lambda: (dki.zero_(), dsa.dsa_index_scores_bwd_dense(
+            x["q_idx"], x["q_scale"], x["w"], x["k_idx"], x["k_scale"], F8, L, L, HI, dI, 0,
+            scores, ld, dqi, dw, dki, bws, bws.numel(), stream)),
+    }
+    # the parts run in order on the stream (the loss consumes the scores, the backward dI), so
+    # each is timed inside full steps: events around every part of every step
+    for _ in range(max(1, args.warmup)):
+        for f in parts.values():
+            f()
+    torch.cuda.synchronize()
+    reps = max(2, args.steps)
+    ev = {n: [] for n in parts}
+    for _ in range(reps):
+        for name, f in parts.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            f()
+            e1.record(stream)
+            ev[name].append((e0, e1))
+    torch.cuda.synchronize()
+    ms = {n: sum(a.elapsed_time(b) for a, b in v) / reps for n, v in ev.items()}
+    pairs = L * (L + 1) // 2
+    # algorithmic work per causal pair: the indexer 2 H^I d_I FP8 FLOP; the loss the scores of
+    # every query head, 2 Hq d bf16 FLOP (computed twice here: once for the log-sum-exp); the
+    # backward x once more (FP8) and the two products with G (2 x 2 H^I d_I bf16 FLOP)
+    ix_flop = pairs * 2 * HI * dI
+    kl_flop = pairs * 2 * Hq * d
+    bwd_f8, bwd_bf = pairs * 2 * HI * dI, pairs * 4 * HI * dI
+    step = sum(ms.values())
+    res = {"workload": cfg.name + "_warmup_step", "tokens": L, "causal_pairs": pairs,
+           "ms": {n: round(v, 3) for n, v in ms.items()}, "ms_per_step": round(step, 3),
+           "tokens_per_s": round(L / (step * 1e-3), 1),
+           "index_mfma_frac": round(ix_flop / (ms["index_scores"] * 1e-3) / PEAK["fp8"], 4),
+           "kl_mfma_frac": round(kl_flop / (ms["warmup_kl"] * 1e-3) / PEAK["bf16"], 4),
+           "bwd_mfma_frac": round((bwd_f8 / PEAK["fp8"] + bwd_bf / PEAK["bf16"])
+                                  / (ms["index_bwd_dense"] * 1e-3), 4),
+           "mean_kl": round(float(kl.mean()), 5)}
+    del x, scores, kl, dqi, dw, dki, ixws, bws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args, cfg, x, torch):
     """The oracle on a stratified sample of query rows of the same workload."""
     import numpy as np
@@ -484,6 +554,9 @@ def main():
     import long_context_sparse_02_amd as dsa
     import workloads as W
     dsa.load_library()
+    if args.profile_kernel == "warmup":
+        print(json.dumps(run_warmup_bench(args, dsa, W, torch)), flush=True)
+        return
     if args.profile_kernel == "train":
         # the 32K training step alone (warm-up and timed repetitions as --warmup / --steps)
         print(json.dumps(run_train_bench(args, dsa, W, torch)), flush=True)
@@ -527,6 +600,8 @@ def main():
         result["packed_prefill"] = run_packed_bench(args, dsa, W, torch)
     if not args.no_train:
         result["train_step"] = run_train_bench(args, dsa, W, torch)
+    if not args.no_warmup_stage:
+        result["warmup_step"] = run_warmup_bench(args, dsa, W, torch)
     if not args.no_decode:
         result["decode"] = [run_decode_bench(args, dsa, W, torch, n)
                             for n in args.decode_workloads.split(",") if n]

@@ -37,11 +37,25 @@ __device__ __forceinline__ v8bf load8bf(const uint16_t* p) {
     return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(p));
 }
 
+// The hardware's exp2 and log2 (no rescaling around subnormal results: exp2 of an argument
+// below -126 gives 0, which only drops probabilities under 2^-126).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Two floats rounded to bf16 (to nearest even, by the hardware's packed conversion).
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ int pack_bf16x2(float a, float b) {
+    bf2v r;
+    r.x = (__bf16)a;
+    r.y = (__bf16)b;
+    return __builtin_bit_cast(int, r);
+}
+
 // One step of an online log2-sum-exp2 with a single exp2: (mx, sm) describes
 // sum 2^(y - mx) = sm over the values seen so far.
 __device__ __forceinline__ void lse_step(float y, bool valid, float& mx, float& sm) {
     const float d = y - mx;                       // +inf while nothing was seen
-    const float e = exp2f(-fabsf(d));
+    const float e = ex2(-fabsf(d));
     const float up = fmaf(sm, e, 1.f), keep = sm + e;
     sm = valid ? (d > 0.f ? up : keep) : sm;
     mx = valid ? fmaxf(mx, y) : mx;
@@ -50,8 +64,8 @@ __device__ __forceinline__ void lse_step(float y, bool valid, float& mx, float& 
 // Merge of two (mx, sm) pairs.
 __device__ __forceinline__ void lse_merge(float& mx, float& sm, float mo, float so) {
     const float mn = fmaxf(mx, mo);
-    const float a = mx == mn ? 1.f : exp2f(mx - mn);
-    const float b = mo == mn ? 1.f : exp2f(mo - mn);
+    const float a = mx == mn ? 1.f : ex2(mx - mn);
+    const float b = mo == mn ? 1.f : ex2(mo - mn);
     sm = sm * a + so * b;
     mx = mn;
 }
@@ -73,7 +87,7 @@ __device__ __forceinline__ void lse_reduce16(float& mx, float& sm) {
 // merged over the 16 key lanes at the end; and per row the log-sum-exp of I.
 // Pass 2: each wave's share of p[t,s,g] = mean_h 2^(S log2e sm_scale - lse2[t,h])
 // into LDS, then per (row, key) the groups are combined: KL terms and dI.
-template <int HPW>
+template <int HPW, int NJ>
 __global__ __launch_bounds__(512) void warmup_kl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int Tq, int Tk,
     int64_t q_pos0, int Hq, int G, int HPG, float sm_scale, const float* __restrict__ lse_in,
@@ -107,8 +121,28 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
         }
     }
     // rows of the I part handled by this lane: r = wave + NW (grp + 4 j), j < nj
-    constexpr int NJ = 4;
-    const int nj = max(1, kWuRows / (4 * NW));
+    // (NJ = max(1, 16 / (4 NW)) as instantiated; rows past 15 are skipped)
+    const int nj = NJ;
+
+    // the wave's group's keys s0 .. s0+15 as B operands (key s0 + col, 8 bf16 per k step)
+    auto load_keys = [&](int s0, v8bf* kb) {
+        const uint16_t* kp = k + ((int64_t)min(s0 + col, Tk - 1) * G + g) * 128 + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[ks] = load8bf(kp + 32 * ks);
+    };
+    // the I part's scores of key s0 + col (rows r = wave + NW (grp + 4 j)); every lane loads
+    // from a valid address (clamped), so the loads issue unconditionally
+    auto load_scores = [&](int s0, float* y) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r = wave + NW * (grp + 4 * j);
+            const bool valid = j < nj && r < rows && s0 + col <= p0 + r;
+            const int rc = min(r, rows - 1);
+            const int64_t sc = min<int64_t>(s0 + col, p0 + rc);
+            const float v = scores[(int64_t)(t0 + rc) * ld + sc];
+            y[j] = valid ? v : -INFINITY;
+        }
+    };
 
     float lse2[MT][4];
     {
@@ -119,33 +153,63 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
             for (int i = 0; i < 4; ++i) { mx[mt][i] = -INFINITY; sm[mt][i] = 0.f; }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) { mxi[j] = -INFINITY; smi[j] = 0.f; }
-        for (int s0 = 0; s0 < nkeys; s0 += kWuKeys) {
+        // one step of keys s0 .. s0+15 with operands kb / yi, while the next step's are
+        // loaded into kn / yn (two register sets used in turn: no copies between steps)
+        auto step1 = [&](int s0, const v8bf* kb, const float* yi, v8bf* kn, float* yn) {
             const int s = s0 + col;
+            // keys past some row's position occur only in the last steps (edge)
+            const bool edge = (int64_t)s0 + kWuKeys - 1 > p0;
+            if (!lse_in) load_keys(s0 + kWuKeys, kn);       // past the end: clamped, unused
+            load_scores(s0 + kWuKeys, yn);
             if (!lse_in) {
-                const uint16_t* kp = k + ((int64_t)min(s, Tk - 1) * G + g) * 128 + 8 * grp;
-                v8bf kb[4];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kb[ks] = load8bf(kp + 32 * ks);
+                v4f acc[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    v4f acc = {0.f, 0.f, 0.f, 0.f};
+                    acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc);
+                    for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc[mt]);
+                }
+                // running sums are kept against a reference mx that is raised only when a
+                // score exceeds it by more than 2^16 (one exp2 per score otherwise)
+                float dd[MT][4];
+                bool big = false;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int r = (16 * mt + 4 * grp + i) / HPW;
-                        lse_step(acc[i] * c2, r < rows && s <= p0 + r, mx[mt][i], sm[mt][i]);
+                        dd[mt][i] = fmaf(acc[mt][i], c2, -mx[mt][i]);
+                        if (edge && s > p0 + (16 * mt + 4 * grp + i) / HPW) dd[mt][i] = -INFINITY;
+                        big |= dd[mt][i] > 16.f;
                     }
+                if (__any(big)) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float y = acc[mt][i] * c2;
+                            const bool ok = !edge || s <= p0 + (16 * mt + 4 * grp + i) / HPW;
+                            const float nm = ok ? fmaxf(mx[mt][i], y) : mx[mt][i];
+                            const float ns = sm[mt][i] * ex2(mx[mt][i] - nm) + ex2(y - nm);
+                            sm[mt][i] = ok && nm != -INFINITY ? ns : sm[mt][i];
+                            mx[mt][i] = nm;
+                        }
+                } else {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sm[mt][i] += ex2(dd[mt][i]);
                 }
             }
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                if (j >= nj) break;
-                const int r = wave + NW * (grp + 4 * j);
-                const bool valid = r < rows && s <= p0 + r;
-                const float y = valid ? scores[(int64_t)(t0 + r) * ld + s] * kLog2e : 0.f;
-                lse_step(y, valid, mxi[j], smi[j]);
-            }
+            for (int j = 0; j < NJ; ++j) lse_step(yi[j] * kLog2e, yi[j] != -INFINITY, mxi[j], smi[j]);
+        };
+        v8bf ka[4], kb2[4];
+        float ya[NJ], yb[NJ];
+        if (!lse_in) load_keys(0, ka);
+        load_scores(0, ya);
+        for (int s0 = 0; s0 < nkeys; s0 += 2 * kWuKeys) {
+            step1(s0, ka, ya, kb2, yb);
+            if (s0 + kWuKeys < nkeys) step1(s0 + kWuKeys, kb2, yb, ka, ya);
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -156,7 +220,7 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
                     lse2[mt][i] = r < rows ? lse_in[(int64_t)(t0 + r) * Hq + hbase + hh] * kLog2e : 0.f;
                 } else {
                     lse_reduce16(mx[mt][i], sm[mt][i]);
-                    lse2[mt][i] = mx[mt][i] + log2f(sm[mt][i]);
+                    lse2[mt][i] = mx[mt][i] + lg2(sm[mt][i]);
                 }
             }
 #pragma unroll
@@ -164,7 +228,7 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
             if (j >= nj) break;
             lse_reduce16(mxi[j], smi[j]);
             const int r = wave + NW * (grp + 4 * j);
-            if (col == 0 && r < kWuRows) lse_i2[r] = mxi[j] + log2f(smi[j]);
+            if (col == 0 && r < kWuRows) lse_i2[r] = mxi[j] + lg2(smi[j]);
         }
     }
     __syncthreads();
@@ -173,23 +237,25 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) kacc[j] = 0.f;
     const float inv_h = 1.f / (float)HPG;
-    int b = 0;
-    for (int s0 = 0; s0 < nkeys; s0 += kWuKeys, b ^= 1) {
+    auto step2 = [&](int s0, int b, const v8bf* kb, const float* yi, v8bf* kn, float* yn) {
         const int s = s0 + col;
-        const uint16_t* kp = k + ((int64_t)min(s, Tk - 1) * G + g) * 128 + 8 * grp;
-        v8bf kb[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[ks] = load8bf(kp + 32 * ks);
+        const bool edge = (int64_t)s0 + kWuKeys - 1 > p0;
+        load_keys(s0 + kWuKeys, kn);                        // past the end: clamped, unused
+        load_scores(s0 + kWuKeys, yn);
+        v4f acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc);
+            for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
             float e[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = (16 * mt + 4 * grp + i) / HPW;
-                e[i] = (r < rows && s <= p0 + r) ? exp2f(fmaf(acc[i], c2, -lse2[mt][i])) : 0.f;
+                e[i] = ex2(fmaf(acc[mt][i], c2, -lse2[mt][i]));
+                if (edge) e[i] = s <= p0 + (16 * mt + 4 * grp + i) / HPW ? e[i] : 0.f;
             }
             // this wave's heads of one row sum to its share of p
             if constexpr (HPW == 4) {
@@ -205,24 +271,31 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            if (j >= nj) break;
             const int r = wave + NW * (grp + 4 * j);
-            if (r < rows && s <= p0 + r) {
+            if (yi[j] != -INFINITY) {                      // a valid (row, key) of the I part
                 float* sp = scores + (int64_t)(t0 + r) * ld + s;
-                const float I = *sp;
-                const float l2 = fmaf(I, kLog2e, -lse_i2[r]);     // log2 softmax(I)_s
-                const float qi = exp2f(l2);
-                const float lq = l2 * kLn2;
-                float psum = 0.f, term = 0.f;
+                const float l2 = fmaf(yi[j], kLog2e, -lse_i2[r]);  // log2 softmax(I)_s
+                const float qi = ex2(l2);
+                float psum = 0.f, term = 0.f;                     // term in log2 units
                 for (int gg = 0; gg < G; ++gg) {
                     float p = 0.f;
                     for (int u = 0; u < WPG; ++u) p += pbuf[b][gg * WPG + u][r][col];
                     psum += p;
-                    term += p > 0.f ? p * (logf(p) - lq) : 0.f;
+                    term += p > 1e-37f ? p * (lg2(p) - l2) : 0.f;
                 }
                 *sp = (float)G * qi - psum;
                 kacc[j] += term;
             }
+        }
+    };
+    {
+        v8bf ka[4], kb2[4];
+        float ya[NJ], yb[NJ];
+        load_keys(0, ka);
+        load_scores(0, ya);
+        for (int s0 = 0; s0 < nkeys; s0 += 2 * kWuKeys) {
+            step2(s0, 0, ka, ya, kb2, yb);
+            if (s0 + kWuKeys < nkeys) step2(s0 + kWuKeys, 1, kb2, yb, ka, ya);
         }
     }
 #pragma unroll
@@ -232,7 +305,7 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
         const int r = wave + NW * (grp + 4 * j);
-        if (col == 0 && r < rows) kl[t0 + r] = v;
+        if (col == 0 && r < rows) kl[t0 + r] = v * kLn2;
     }
 }
 
@@ -293,6 +366,7 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_q_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t kc[2][kQbKeys][128 + 16];
     __shared__ __attribute__((aligned(16))) uint16_t kt[2][128][kQbKeys + 8];
     __shared__ __attribute__((aligned(16))) uint8_t qcs[kQbWaves][HI][128 + 16];
+    __shared__ __attribute__((aligned(16))) float gks[2][kQbWaves][kQbKeys];   // g x k_scale
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int blk = gridDim.x - 1 - blockIdx.x;          // longest rows first
@@ -322,58 +396,68 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_q_kernel(
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) dwa[ht] = 0.f;
 
-    // staging: threads 0..255 copy 16 code bytes each, all 512 copy 8 bf16 each
-    auto fetch = [&](int s0, v4i& cbytes, v4i& bvals) {
-        if (tid < 256) {
-            const int key = s0 + tid / 8;
-            cbytes = key < Tk ? *reinterpret_cast<const v4i*>(k_idx + (int64_t)key * 128 + 16 * (tid % 8))
-                              : v4i{0, 0, 0, 0};
-        }
-        bvals = *reinterpret_cast<const v4i*>(kt_bf + (int64_t)(tid / 4) * ldk + s0 + 8 * (tid % 4));
+    // All global reads of a step are the next step's staging, issued at the top of the step
+    // from clamped (valid) addresses and stored to LDS at its end: the key codes, their bf16
+    // values [column][key], and g[t, s] k_scale[s] of the workgroup's 8 rows (0 where s is
+    // past the row's position or Tk), one float per thread.
+    auto fetch = [&](int s0, v4i& cbytes, v4i& bvals, float* gsv) {
+        const int s0c = min(s0, ldk - kQbKeys);
+        const int key = min(s0c + (tid & 255) / 8, Tk - 1);
+        cbytes = *reinterpret_cast<const v4i*>(k_idx + (int64_t)key * 128 + 16 * (tid % 8));
+        bvals = *reinterpret_cast<const v4i*>(kt_bf + (int64_t)(tid / 4) * ldk + s0c + 8 * (tid % 4));
+        const int rr = min(t0 + (tid & 255) / kQbKeys, Tq - 1);
+        const int64_t sg = s0 + (tid & 255) % kQbKeys, pr = q_pos0 + rr;
+        gsv[0] = gI[(int64_t)rr * ld + min<int64_t>(sg, pr)];
+        gsv[1] = k_scale[(int)min<int64_t>(sg, (int64_t)Tk - 1)];
     };
-    auto stash = [&](int buf, const v4i& cbytes, const v4i& bvals) {
-        if (tid < 256) *reinterpret_cast<v4i*>(&kc[buf][tid / 8][16 * (tid % 8)]) = cbytes;
+    // the product is formed when stored, so that the loads stay in flight during the step
+    auto stash = [&](int s0, int buf, const v4i& cbytes, const v4i& bvals, const float* gsv) {
+        if (tid < 256) {
+            *reinterpret_cast<v4i*>(&kc[buf][tid / 8][16 * (tid % 8)]) = cbytes;
+            const int64_t sg = s0 + tid % kQbKeys, pr = q_pos0 + t0 + tid / kQbKeys;
+            gks[buf][tid / kQbKeys][tid % kQbKeys] = sg <= pr && sg < Tk ? gsv[0] * gsv[1] : 0.f;
+        }
         *reinterpret_cast<v4i*>(&kt[buf][tid / 4][8 * (tid % 4)]) = bvals;
     };
     v4i cb = {0, 0, 0, 0}, bv = {0, 0, 0, 0};
+    float gsv[2] = {0.f, 0.f};
     if (nkeys > 0) {
-        fetch(0, cb, bv);
-        stash(0, cb, bv);
+        fetch(0, cb, bv, gsv);
+        stash(0, 0, cb, bv, gsv);
     }
     __syncthreads();
     int buf = 0;
     for (int s0 = 0; s0 < nkeys; s0 += kQbKeys, buf ^= 1) {
         const bool more = s0 + kQbKeys < nkeys;
-        if (more) fetch(s0 + kQbKeys, cb, bv);
+        fetch(s0 + kQbKeys, cb, bv, gsv);                 // past the end: clamped, unused
         if (row_ok && s0 <= pos) {
             // with non-negative scales x q_scale k_scale > 0 exactly when x > 0 and both
             // scales are positive; a zero q_scale zeroes wv, a zero k_scale zeroes gk
             float gk[2][4];
 #pragma unroll
-            for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s = s0 + 16 * kt2 + 4 * grp + i;
-                    const bool ok = s <= pos && s < Tk;
-                    gk[kt2][i] = ok ? gI[(int64_t)t * ld + s] * k_scale[s] : 0.f;
-                }
+            for (int kt2 = 0; kt2 < 2; ++kt2) {
+                const float4 v = *reinterpret_cast<const float4*>(&gks[buf][wave][16 * kt2 + 4 * grp]);
+                gk[kt2][0] = v.x; gk[kt2][1] = v.y; gk[kt2][2] = v.z; gk[kt2][3] = v.w;
+            }
             v8bf ga[NHT];
 #pragma unroll
             for (int ht = 0; ht < NHT; ++ht) {
-                v8s bits;
+                int pk[4];
                 const v8i qb = *reinterpret_cast<const v8i*>(&qcs[wave][16 * ht + col][32 * grp]);
 #pragma unroll
                 for (int kt2 = 0; kt2 < 2; ++kt2) {
                     const v8i a = *reinterpret_cast<const v8i*>(&kc[buf][16 * kt2 + col][32 * grp]);
                     const v4f x = mfma_fp8_16x16x128(a, qb, v4f{0.f, 0.f, 0.f, 0.f});
+                    float gv[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const bool on = x[i] > 0.f;
-                        dwa[ht] += on ? gk[kt2][i] * x[i] : 0.f;
-                        bits[4 * kt2 + i] = (short)f32_to_bf16_bits(on ? gk[kt2][i] * wv[ht] : 0.f);
+                        dwa[ht] = fmaf(gk[kt2][i], fmaxf(x[i], 0.f), dwa[ht]);
+                        gv[i] = x[i] > 0.f ? gk[kt2][i] * wv[ht] : 0.f;
                     }
+                    pk[2 * kt2] = pack_bf16x2(gv[0], gv[1]);
+                    pk[2 * kt2 + 1] = pack_bf16x2(gv[2], gv[3]);
                 }
-                ga[ht] = __builtin_bit_cast(v8bf, bits);
+                ga[ht] = __builtin_bit_cast(v8bf, v4i{pk[0], pk[1], pk[2], pk[3]});
             }
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
@@ -384,7 +468,7 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_q_kernel(
                 for (int ht = 0; ht < NHT; ++ht) acc[ht][ct] = mfma_bf16_16x16x32(ga[ht], kb, acc[ht][ct]);
             }
         }
-        if (more) stash(buf ^ 1, cb, bv);
+        if (more) stash(s0 + kQbKeys, buf ^ 1, cb, bv, gsv);
         __syncthreads();
     }
     if (!row_ok) return;
@@ -426,7 +510,8 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
     constexpr int NHC = (NHT + 1) / 2;
     __shared__ __attribute__((aligned(16))) uint8_t qc[2][HI][128 + 16];
     __shared__ __attribute__((aligned(16))) uint16_t qt[2][128][HI + 8];
-    __shared__ float wl[2][HI];
+    __shared__ __attribute__((aligned(16))) float wl[2][HI];
+    __shared__ float gsl[2][kKbKeys];                    // g[t, s] q_scale[t], 0 where inapplicable
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int kb = blockIdx.x, sp = blockIdx.y;
@@ -451,22 +536,30 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) acc[kt2][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // staging of one row: HI x 128 code bytes (16 per thread) and 128 x HI bf16 values
-    // (8 per piece, NV pieces per thread)
+    // All global reads of a step are the next row's staging, issued at the top of the step
+    // from clamped (valid) addresses and stored to LDS at its end: the row's codes, its bf16
+    // values [column][head], w, and g[t, s] q_scale[t] for the workgroup's 256 keys (0 where
+    // s is past the row's position or Tk, or a scale is zero).  Threads past a piece count
+    // repeat pieces.
     constexpr int kCodeThreads = HI * 8;
     constexpr int NV = (HI * 16 + 511) / 512;
-    auto fetch = [&](int t, v4i& cbytes, v4i* bvals, float& wvl) {
-        if (tid < kCodeThreads)
-            cbytes = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)t * HI + tid / 8) * 128 + 16 * (tid % 8));
+    auto fetch = [&](int t, v4i& cbytes, v4i* bvals, float& wvl, float* gsv) {
+        const int tr = min(t, Tq - 1);
+        const int ci = tid % kCodeThreads;
+        cbytes = *reinterpret_cast<const v4i*>(q_idx + ((int64_t)tr * HI + ci / 8) * 128 + 16 * (ci % 8));
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int piece = tid + 512 * u;
-            if (piece < HI * 16)
-                bvals[u] = *reinterpret_cast<const v4i*>(qt_bf + (int64_t)t * 128 * HI + (int64_t)piece * 8);
+            const int piece = (tid + 512 * u) % (HI * 16);
+            bvals[u] = *reinterpret_cast<const v4i*>(qt_bf + (int64_t)tr * 128 * HI + (int64_t)piece * 8);
         }
-        if (tid < HI) wvl = w[(int64_t)t * HI + tid];
+        wvl = w[(int64_t)tr * HI + tid % HI];
+        const int64_t sg = sb + (tid & (kKbKeys - 1)), pr = q_pos0 + tr;
+        gsv[0] = gI[(int64_t)tr * ld + min<int64_t>(sg, pr)];
+        gsv[1] = k_scale[(int)min<int64_t>(sg, (int64_t)Tk - 1)];
+        gsv[2] = q_scale[tr];
     };
-    auto stash = [&](int buf, const v4i& cbytes, const v4i* bvals, float wvl) {
+    // the product is formed when stored, so that the loads stay in flight during the step
+    auto stash = [&](int t, int buf, const v4i& cbytes, const v4i* bvals, float wvl, const float* gsv) {
         if (tid < kCodeThreads) *reinterpret_cast<v4i*>(&qc[buf][tid / 8][16 * (tid % 8)]) = cbytes;
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -477,48 +570,52 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
             }
         }
         if (tid < HI) wl[buf][tid] = wvl;
+        if (tid < kKbKeys) {
+            const int64_t sg = sb + tid, pr = q_pos0 + t;
+            gsl[buf][tid] = sg <= pr && sg < Tk && gsv[1] > 0.f && gsv[2] > 0.f ? gsv[0] * gsv[2] : 0.f;
+        }
     };
     v4i cb = {0, 0, 0, 0}, bv[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) bv[u] = v4i{0, 0, 0, 0};
-    float wvl = 0.f;
+    float wvl = 0.f, gsv[3] = {0.f, 0.f, 0.f};
     if (r_begin < r_end) {
-        fetch(r_begin, cb, bv, wvl);
-        stash(0, cb, bv, wvl);
+        fetch(r_begin, cb, bv, wvl, gsv);
+        stash(r_begin, 0, cb, bv, wvl, gsv);
     }
     __syncthreads();
     int buf = 0;
     for (int t = r_begin; t < r_end; ++t, buf ^= 1) {
         const bool more = t + 1 < r_end;
-        if (more) fetch(t + 1, cb, bv, wvl);
         const int64_t pos = q_pos0 + t;
+        fetch(t + 1, cb, bv, wvl, gsv);                     // past the end: clamped, unused
         if (sw <= pos) {
-            const float qs = q_scale[t];
-            float gg[2];
+            // with non-negative scales x q_scale k_scale > 0 exactly when x > 0 and both
+            // scales are positive (zero scales zeroed gsl)
+            float gq[2];
 #pragma unroll
-            for (int kt2 = 0; kt2 < 2; ++kt2) {
-                const int s = sw + 16 * kt2 + col;
-                gg[kt2] = (s <= pos && s < Tk) ? gI[(int64_t)t * ld + s] : 0.f;
-            }
+            for (int kt2 = 0; kt2 < 2; ++kt2) gq[kt2] = gsl[buf][wave * kKbKeysW + 16 * kt2 + col];
             v8bf ga[2][NHC];
 #pragma unroll
             for (int kt2 = 0; kt2 < 2; ++kt2) {
-                v8s bits[NHC];
+                int pk[NHC][4];
 #pragma unroll
-                for (int hc = 0; hc < NHC; ++hc) bits[hc] = v8s{0, 0, 0, 0, 0, 0, 0, 0};
+                for (int hc = 0; hc < NHC; ++hc) pk[hc][0] = pk[hc][1] = pk[hc][2] = pk[hc][3] = 0;
 #pragma unroll
                 for (int ht = 0; ht < NHT; ++ht) {
                     const v8i a = *reinterpret_cast<const v8i*>(&qc[buf][16 * ht + col][32 * grp]);
                     const v4f x = mfma_fp8_16x16x128(a, kbop[kt2], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float xv = x[i] * qs * ksc[kt2];
-                        const float gv = xv > 0.f ? gg[kt2] * wl[buf][16 * ht + 4 * grp + i] : 0.f;
-                        bits[ht / 2][4 * (ht % 2) + i] = (short)f32_to_bf16_bits(gv * qs);
-                    }
+                    const float4 w4 = *reinterpret_cast<const float4*>(&wl[buf][16 * ht + 4 * grp]);
+                    const float g0 = x[0] > 0.f ? gq[kt2] * w4.x : 0.f;
+                    const float g1 = x[1] > 0.f ? gq[kt2] * w4.y : 0.f;
+                    const float g2 = x[2] > 0.f ? gq[kt2] * w4.z : 0.f;
+                    const float g3 = x[3] > 0.f ? gq[kt2] * w4.w : 0.f;
+                    pk[ht / 2][2 * (ht % 2)] = pack_bf16x2(g0, g1);
+                    pk[ht / 2][2 * (ht % 2) + 1] = pack_bf16x2(g2, g3);
                 }
 #pragma unroll
-                for (int hc = 0; hc < NHC; ++hc) ga[kt2][hc] = __builtin_bit_cast(v8bf, bits[hc]);
+                for (int hc = 0; hc < NHC; ++hc)
+                    ga[kt2][hc] = __builtin_bit_cast(v8bf, v4i{pk[hc][0], pk[hc][1], pk[hc][2], pk[hc][3]});
             }
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct)
@@ -533,7 +630,7 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
                     for (int kt2 = 0; kt2 < 2; ++kt2) acc[kt2][ct] = mfma_bf16_16x16x32(ga[kt2][hc], qbv, acc[kt2][ct]);
                 }
         }
-        if (more) stash(buf ^ 1, cb, bv, wvl);
+        if (more) stash(t + 1, buf ^ 1, cb, bv, wvl, gsv);
         __syncthreads();
     }
     float* pp = part + (int64_t)sp * ldk * 128;
@@ -581,13 +678,22 @@ hipError_t launch_warmup_kl(const uint16_t* q, const uint16_t* k, int Tq, int Tk
 {
     if (Tq == 0) return hipSuccess;
     if (!warmup_kl_supported(Hq, G)) return hipErrorInvalidValue;
-    const int hpg = Hq / G, hpw = hpg < 4 ? hpg : 4;
-    const dim3 grid((Tq + kWuRows - 1) / kWuRows), block(64 * G * (hpg / hpw));
-    switch (hpw) {
-    case 1: hipLaunchKernelGGL(warmup_kl_kernel<1>, grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl); break;
-    case 2: hipLaunchKernelGGL(warmup_kl_kernel<2>, grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl); break;
-    default: hipLaunchKernelGGL(warmup_kl_kernel<4>, grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl); break;
+    const int hpg = Hq / G, hpw = hpg < 4 ? hpg : 4, nw = G * (hpg / hpw);
+    const int nj = nw >= 4 ? 1 : 4 / nw;
+    const dim3 grid((Tq + kWuRows - 1) / kWuRows), block(64 * nw);
+#define WU_KL(H, J) hipLaunchKernelGGL((warmup_kl_kernel<H, J>), grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl)
+    switch (hpw * 8 + nj) {
+    case 9: WU_KL(1, 1); break;
+    case 10: WU_KL(1, 2); break;
+    case 12: WU_KL(1, 4); break;
+    case 17: WU_KL(2, 1); break;
+    case 18: WU_KL(2, 2); break;
+    case 20: WU_KL(2, 4); break;
+    case 33: WU_KL(4, 1); break;
+    case 34: WU_KL(4, 2); break;
+    default: WU_KL(4, 4); break;
     }
+#undef WU_KL
     return hipGetLastError();
 }
 

@@ -71,7 +71,8 @@ def _check_kl(kl, dI, rkl, rdI, I, G, what, I_err=None):
 @pytest.mark.parametrize("L,q_pos0,Hq,G,with_lse", [
     (300, 0, 32, 4, False), (700, 411, 32, 4, False), (400, 150, 32, 4, True),
     (333, 0, 8, 2, False), (260, 37, 16, 1, False), (200, 0, 4, 4, False),
-    (250, 90, 8, 4, False), (230, 0, 32, 8, True)])
+    (250, 90, 8, 4, False), (230, 0, 32, 8, True), (150, 20, 4, 1, False),
+    (170, 0, 4, 2, False), (130, 0, 1, 1, False), (140, 33, 2, 2, True)])
 def test_warmup_kl_vs_oracle(L, q_pos0, Hq, G, with_lse):
     _say("warm-up kl L=%d q_pos0=%d Hq=%d G=%d lse=%s" % (L, q_pos0, Hq, G, with_lse))
     cfg, x = _case(L, Hq, G, seed=L + Hq + G)
