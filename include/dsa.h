@@ -384,7 +384,7 @@ dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v
  *   dL/dI[t, s] = G softmax(I[t, 0..pos])_s - sum_g p[t,s,g];
  * entries beyond the prefix are left as they are.  kl float [Tq] receives
  * sum_g KL(p[t,:,g] || softmax(I[t,:])).  The target p is a constant (the indexer's inputs are
- * detached from the main model).  Supported: Hq / G in {1, 2} or a multiple of 4, with
+ * detached from the main model).  Supported: Hq / G in {1, 2, 4, 8, 16} with
  * G * max(1, Hq / G / 4) <= 8; Tk >= q_pos0 + Tq.  fp32 softmax from bf16 matrix-core scores.
  * No workspace; deterministic.
  */

@@ -893,7 +893,7 @@ DSA_EXPORT dsa_status_t dsa_indexer_warmup_kl(const void* q, const void* k, dsa_
     REQUIRE(G >= 1 && Hq >= 1 && Hq % G == 0, DSA_ERR_INVALID_ARG,
             "Hq (%d) must be a positive multiple of G (%d)", Hq, G);
     REQUIRE(dsa::warmup_kl_supported(Hq, G), DSA_ERR_UNSUPPORTED,
-            "the warm-up loss takes Hq/G in {1, 2} or a multiple of 4, with G * max(1, Hq/G/4) <= 8 "
+            "the warm-up loss takes Hq/G in {1, 2, 4, 8, 16} with G * max(1, Hq/G/4) <= 8 "
             "(got Hq=%d, G=%d)", Hq, G);
     REQUIRE(Tq >= 0 && Tk >= 0 && q_pos0 >= 0, DSA_ERR_INVALID_ARG, "negative size or position");
     REQUIRE((int64_t)Tk >= q_pos0 + Tq, DSA_ERR_INVALID_ARG,

@@ -87,7 +87,7 @@ __device__ __forceinline__ void lse_reduce16(float& mx, float& sm) {
 // merged over the 16 key lanes at the end; and per row the log-sum-exp of I.
 // Pass 2: each wave's share of p[t,s,g] = mean_h 2^(S log2e sm_scale - lse2[t,h])
 // into LDS, then per (row, key) the groups are combined: KL terms and dI.
-template <int HPW, int NJ>
+template <int HPW, int NJ, int WPG>
 __global__ __launch_bounds__(512) void warmup_kl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int Tq, int Tk,
     int64_t q_pos0, int Hq, int G, int HPG, float sm_scale, const float* __restrict__ lse_in,
@@ -98,14 +98,15 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
     __shared__ float lse_i2[kWuRows];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int WPG = HPG / HPW, NW = G * WPG;
+    const int NW = G * WPG;                              // WPG = HPG / HPW
+
     const int g = wave / WPG;
     const int hbase = g * HPG + (wave % WPG) * HPW;     // first query head of this wave
     const int blk = gridDim.x - 1 - blockIdx.x;          // longest rows first
     const int t0 = blk * kWuRows;
     const int rows = min(kWuRows, Tq - t0);
-    const int64_t p0 = q_pos0 + t0;
-    const int nkeys = (int)min<int64_t>(p0 + rows, (int64_t)Tk);
+    const int p0 = (int)(q_pos0 + t0);                  // positions fit in int (Tk is an int)
+    const int nkeys = min(p0 + rows, Tk);
     const float c2 = sm_scale * kLog2e;
 
     v8bf qa[MT][4];
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
             const int r = wave + NW * (grp + 4 * j);
             const bool valid = j < nj && r < rows && s0 + col <= p0 + r;
             const int rc = min(r, rows - 1);
-            const int64_t sc = min<int64_t>(s0 + col, p0 + rc);
+            const int sc = min(s0 + col, p0 + rc);
             const float v = scores[(int64_t)(t0 + rc) * ld + sc];
             y[j] = valid ? v : -INFINITY;
         }
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
         auto step1 = [&](int s0, const v8bf* kb, const float* yi, v8bf* kn, float* yn) {
             const int s = s0 + col;
             // keys past some row's position occur only in the last steps (edge)
-            const bool edge = (int64_t)s0 + kWuKeys - 1 > p0;
+            const bool edge = s0 + kWuKeys - 1 > p0;
             if (!lse_in) load_keys(s0 + kWuKeys, kn);       // past the end: clamped, unused
             load_scores(s0 + kWuKeys, yn);
             if (!lse_in) {
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
     const float inv_h = 1.f / (float)HPG;
     auto step2 = [&](int s0, int b, const v8bf* kb, const float* yi, v8bf* kn, float* yn) {
         const int s = s0 + col;
-        const bool edge = (int64_t)s0 + kWuKeys - 1 > p0;
+        const bool edge = s0 + kWuKeys - 1 > p0;
         load_keys(s0 + kWuKeys, kn);                        // past the end: clamped, unused
         load_scores(s0 + kWuKeys, yn);
         v4f acc[MT];
@@ -253,9 +254,10 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
         for (int mt = 0; mt < MT; ++mt) {
             float e[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                e[i] = ex2(fmaf(acc[mt][i], c2, -lse2[mt][i]));
-                if (edge) e[i] = s <= p0 + (16 * mt + 4 * grp + i) / HPW ? e[i] : 0.f;
+            for (int i = 0; i < 4; ++i) e[i] = ex2(fmaf(acc[mt][i], c2, -lse2[mt][i]));
+            if (edge) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) e[i] = s <= p0 + (16 * mt + 4 * grp + i) / HPW ? e[i] : 0.f;
             }
             // this wave's heads of one row sum to its share of p
             if constexpr (HPW == 4) {
@@ -276,10 +278,15 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
                 float* sp = scores + (int64_t)(t0 + r) * ld + s;
                 const float l2 = fmaf(yi[j], kLog2e, -lse_i2[r]);  // log2 softmax(I)_s
                 const float qi = ex2(l2);
+                // the NW <= 8 waves' parts (group gg: parts gg WPG .. gg WPG + WPG-1), read
+                // from clamped slots without branches and dropped past G
                 float psum = 0.f, term = 0.f;                     // term in log2 units
-                for (int gg = 0; gg < G; ++gg) {
+#pragma unroll
+                for (int gg = 0; gg < 8 / WPG; ++gg) {
                     float p = 0.f;
-                    for (int u = 0; u < WPG; ++u) p += pbuf[b][gg * WPG + u][r][col];
+#pragma unroll
+                    for (int u = 0; u < WPG; ++u) p += pbuf[b][min(gg * WPG + u, NW - 1)][r][col];
+                    p = gg < G ? p : 0.f;
                     psum += p;
                     term += p > 1e-37f ? p * (lg2(p) - l2) : 0.f;
                 }
@@ -667,7 +674,7 @@ bool warmup_kl_supported(int Hq, int G)
 {
     if (G < 1 || Hq % G) return false;
     const int hpg = Hq / G;
-    if (hpg != 1 && hpg != 2 && hpg % 4) return false;
+    if (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8 && hpg != 16) return false;
     const int hpw = hpg < 4 ? hpg : 4;
     return G * (hpg / hpw) <= 8;
 }
@@ -678,20 +685,24 @@ hipError_t launch_warmup_kl(const uint16_t* q, const uint16_t* k, int Tq, int Tk
 {
     if (Tq == 0) return hipSuccess;
     if (!warmup_kl_supported(Hq, G)) return hipErrorInvalidValue;
-    const int hpg = Hq / G, hpw = hpg < 4 ? hpg : 4, nw = G * (hpg / hpw);
+    const int hpg = Hq / G, hpw = hpg < 4 ? hpg : 4, wpg = hpg / hpw, nw = G * wpg;
     const int nj = nw >= 4 ? 1 : 4 / nw;
     const dim3 grid((Tq + kWuRows - 1) / kWuRows), block(64 * nw);
-#define WU_KL(H, J) hipLaunchKernelGGL((warmup_kl_kernel<H, J>), grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl)
-    switch (hpw * 8 + nj) {
-    case 9: WU_KL(1, 1); break;
-    case 10: WU_KL(1, 2); break;
-    case 12: WU_KL(1, 4); break;
-    case 17: WU_KL(2, 1); break;
-    case 18: WU_KL(2, 2); break;
-    case 20: WU_KL(2, 4); break;
-    case 33: WU_KL(4, 1); break;
-    case 34: WU_KL(4, 2); break;
-    default: WU_KL(4, 4); break;
+#define WU_KL(H, J, W) hipLaunchKernelGGL((warmup_kl_kernel<H, J, W>), grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl)
+    switch ((hpw * 8 + wpg) * 8 + nj) {
+    case (1 * 8 + 1) * 8 + 1: WU_KL(1, 1, 1); break;
+    case (1 * 8 + 1) * 8 + 2: WU_KL(1, 2, 1); break;
+    case (1 * 8 + 1) * 8 + 4: WU_KL(1, 4, 1); break;
+    case (2 * 8 + 1) * 8 + 1: WU_KL(2, 1, 1); break;
+    case (2 * 8 + 1) * 8 + 2: WU_KL(2, 2, 1); break;
+    case (2 * 8 + 1) * 8 + 4: WU_KL(2, 4, 1); break;
+    case (4 * 8 + 1) * 8 + 1: WU_KL(4, 1, 1); break;
+    case (4 * 8 + 1) * 8 + 2: WU_KL(4, 2, 1); break;
+    case (4 * 8 + 1) * 8 + 4: WU_KL(4, 4, 1); break;
+    case (4 * 8 + 2) * 8 + 1: WU_KL(4, 1, 2); break;
+    case (4 * 8 + 2) * 8 + 2: WU_KL(4, 2, 2); break;
+    case (4 * 8 + 4) * 8 + 1: WU_KL(4, 1, 4); break;
+    default: return hipErrorInvalidValue;
     }
 #undef WU_KL
     return hipGetLastError();
