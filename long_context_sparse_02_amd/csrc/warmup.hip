@@ -496,10 +496,11 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_q_kernel(
 }
 
 constexpr int kKbWaves = 8;          // waves per workgroup, dk kernel
-constexpr int kKbKeysW = 32;         // keys per wave
+constexpr int kKbKeysW = 48;         // keys per wave
+constexpr int kKbKT = kKbKeysW / 16;  // 16-key tiles per wave
 constexpr int kKbKeys = kKbWaves * kKbKeysW;
 
-// dk^I partial sums: workgroup (key block kb, row range sp) owns 256 keys (32 per wave)
+// dk^I partial sums: workgroup (key block kb, row range sp) owns 384 keys (48 per wave)
 // and streams the query rows of its range that see them, one row per step (codes,
 // w and the bf16 values [column][head] staged in LDS).  Per row a wave computes x
 // (the row's heads on A, its keys on B), G' = bf16(G q_scale), and
@@ -528,24 +529,24 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
     const int r_begin = (int)min<int64_t>(max<int64_t>(first, 0), (int64_t)Tq);
     const int r_end = min(Tq, (sp + 1) * rows_per_split);
 
-    v8i kbop[2];
-    float ksc[2];
+    v8i kbop[kKbKT];
+    float ksc[kKbKT];
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
+    for (int kt2 = 0; kt2 < kKbKT; ++kt2) {
         const int s = sw + 16 * kt2 + col;
         kbop[kt2] = s < Tk ? *reinterpret_cast<const v8i*>(k_idx + (int64_t)s * 128 + 32 * grp)
                            : v8i{0, 0, 0, 0, 0, 0, 0, 0};
         ksc[kt2] = s < Tk ? k_scale[s] : 0.f;
     }
-    v4f acc[2][8];
+    v4f acc[kKbKT][8];
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
+    for (int kt2 = 0; kt2 < kKbKT; ++kt2)
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) acc[kt2][ct] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // All global reads of a step are the next row's staging, issued at the top of the step
     // from clamped (valid) addresses and stored to LDS at its end: the row's codes, its bf16
-    // values [column][head], w, and g[t, s] q_scale[t] for the workgroup's 256 keys (0 where
+    // values [column][head], w, and g[t, s] q_scale[t] for the workgroup's 384 keys (0 where
     // s is past the row's position or Tk, or a scale is zero).  Threads past a piece count
     // repeat pieces.
     constexpr int kCodeThreads = HI * 8;
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
             bvals[u] = *reinterpret_cast<const v4i*>(qt_bf + (int64_t)tr * 128 * HI + (int64_t)piece * 8);
         }
         wvl = w[(int64_t)tr * HI + tid % HI];
-        const int64_t sg = sb + (tid & (kKbKeys - 1)), pr = q_pos0 + tr;
+        const int64_t sg = sb + tid % kKbKeys, pr = q_pos0 + tr;
         gsv[0] = gI[(int64_t)tr * ld + min<int64_t>(sg, pr)];
         gsv[1] = k_scale[(int)min<int64_t>(sg, (int64_t)Tk - 1)];
         gsv[2] = q_scale[tr];
@@ -599,12 +600,12 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
         if (sw <= pos) {
             // with non-negative scales x q_scale k_scale > 0 exactly when x > 0 and both
             // scales are positive (zero scales zeroed gsl)
-            float gq[2];
+            float gq[kKbKT];
 #pragma unroll
-            for (int kt2 = 0; kt2 < 2; ++kt2) gq[kt2] = gsl[buf][wave * kKbKeysW + 16 * kt2 + col];
-            v8bf ga[2][NHC];
+            for (int kt2 = 0; kt2 < kKbKT; ++kt2) gq[kt2] = gsl[buf][wave * kKbKeysW + 16 * kt2 + col];
+            v8bf ga[kKbKT][NHC];
 #pragma unroll
-            for (int kt2 = 0; kt2 < 2; ++kt2) {
+            for (int kt2 = 0; kt2 < kKbKT; ++kt2) {
                 int pk[NHC][4];
 #pragma unroll
                 for (int hc = 0; hc < NHC; ++hc) pk[hc][0] = pk[hc][1] = pk[hc][2] = pk[hc][3] = 0;
@@ -634,7 +635,7 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
                         hi = *reinterpret_cast<const uint2*>(&qt[buf][16 * ct + col][32 * hc + 16 + 4 * grp]);
                     const v8bf qbv = __builtin_bit_cast(v8bf, v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y});
 #pragma unroll
-                    for (int kt2 = 0; kt2 < 2; ++kt2) acc[kt2][ct] = mfma_bf16_16x16x32(ga[kt2][hc], qbv, acc[kt2][ct]);
+                    for (int kt2 = 0; kt2 < kKbKT; ++kt2) acc[kt2][ct] = mfma_bf16_16x16x32(ga[kt2][hc], qbv, acc[kt2][ct]);
                 }
         }
         if (more) stash(t + 1, buf ^ 1, cb, bv, wvl, gsv);
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
     }
     float* pp = part + (int64_t)sp * ldk * 128;
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
+    for (int kt2 = 0; kt2 < kKbKT; ++kt2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = sw + 16 * kt2 + 4 * grp + i;
