@@ -32,6 +32,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kWuRows = 16;          // query rows per workgroup of the loss kernel
 constexpr int kWuKeys = 16;          // keys per step of the loss kernel
+constexpr int kWuChunk = 4;          // steps per barrier in the loss kernel's second pass
 
 __device__ __forceinline__ v8bf load8bf(const uint16_t* p) {
     return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(p));
@@ -88,13 +89,13 @@ __device__ __forceinline__ void lse_reduce16(float& mx, float& sm) {
 // Pass 2: each wave's share of p[t,s,g] = mean_h 2^(S log2e sm_scale - lse2[t,h])
 // into LDS, then per (row, key) the groups are combined: KL terms and dI.
 template <int HPW, int NJ, int WPG>
-__global__ __launch_bounds__(512) void warmup_kl_kernel(
+__global__ __launch_bounds__(NJ == 4 ? 64 : NJ == 2 ? 128 : 512) void warmup_kl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int Tq, int Tk,
     int64_t q_pos0, int Hq, int G, int HPG, float sm_scale, const float* __restrict__ lse_in,
     float* __restrict__ scores, int64_t ld, float* __restrict__ kl)
 {
     constexpr int MT = HPW;                              // M tiles per wave (16 rows x HPW)
-    __shared__ float pbuf[2][8][kWuRows][kWuKeys + 1];
+    __shared__ float pbuf[2][8][kWuRows][kWuChunk * kWuKeys + 1];
     __shared__ float lse_i2[kWuRows];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -131,18 +132,19 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kb[ks] = load8bf(kp + 32 * ks);
     };
-    // the I part's scores of key s0 + col (rows r = wave + NW (grp + 4 j)); every lane loads
+    // the I part's score of key s0 + col, row r = wave + NW (grp + 4 j); every lane loads
     // from a valid address (clamped), so the loads issue unconditionally
+    auto score_at = [&](int s0, int j) -> float {
+        const int r = wave + NW * (grp + 4 * j);
+        const bool valid = j < nj && r < rows && s0 + col <= p0 + r;
+        const int rc = min(r, rows - 1);
+        const int sc = min(s0 + col, p0 + rc);
+        const float v = scores[(int64_t)(t0 + rc) * ld + sc];
+        return valid ? v : -INFINITY;
+    };
     auto load_scores = [&](int s0, float* y) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int r = wave + NW * (grp + 4 * j);
-            const bool valid = j < nj && r < rows && s0 + col <= p0 + r;
-            const int rc = min(r, rows - 1);
-            const int sc = min(s0 + col, p0 + rc);
-            const float v = scores[(int64_t)(t0 + rc) * ld + sc];
-            y[j] = valid ? v : -INFINITY;
-        }
+        for (int j = 0; j < NJ; ++j) y[j] = score_at(s0, j);
     };
 
     float lse2[MT][4];
@@ -172,14 +174,17 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
                 }
                 // running sums are kept against a reference mx that is raised only when a
                 // score exceeds it by more than 2^16 (one exp2 per score otherwise)
+                // key s is valid for row r when r >= lim (no branch between the matrix core's
+                // results and their first reads)
+                const int lim = edge ? s - p0 : -kWuRows;
                 float dd[MT][4];
                 bool big = false;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        dd[mt][i] = fmaf(acc[mt][i], c2, -mx[mt][i]);
-                        if (edge && s > p0 + (16 * mt + 4 * grp + i) / HPW) dd[mt][i] = -INFINITY;
+                        const float d = fmaf(acc[mt][i], c2, -mx[mt][i]);
+                        dd[mt][i] = (16 * mt + 4 * grp + i) / HPW >= lim ? d : -INFINITY;
                         big |= dd[mt][i] > 16.f;
                     }
                 if (__any(big)) {
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float y = acc[mt][i] * c2;
-                            const bool ok = !edge || s <= p0 + (16 * mt + 4 * grp + i) / HPW;
+                            const bool ok = (16 * mt + 4 * grp + i) / HPW >= lim;
                             const float nm = ok ? fmaxf(mx[mt][i], y) : mx[mt][i];
                             const float ns = sm[mt][i] * ex2(mx[mt][i] - nm) + ex2(y - nm);
                             sm[mt][i] = ok && nm != -INFINITY ? ns : sm[mt][i];
@@ -238,11 +243,14 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) kacc[j] = 0.f;
     const float inv_h = 1.f / (float)HPG;
-    auto step2 = [&](int s0, int b, const v8bf* kb, const float* yi, v8bf* kn, float* yn) {
+    // Pass 2 in chunks of kWuChunk key steps per barrier: each step writes the wave's share
+    // of p for its 16 keys into the chunk's columns; after the barrier the I part combines the
+    // groups for all the chunk's keys.  Steps past nkeys run on clamped keys and are masked.
+    v8bf ka[4], kb2[4];
+    auto step2 = [&](int s0, int b, int u, const v8bf* kb, v8bf* kn) {
         const int s = s0 + col;
         const bool edge = s0 + kWuKeys - 1 > p0;
         load_keys(s0 + kWuKeys, kn);                        // past the end: clamped, unused
-        load_scores(s0 + kWuKeys, yn);
         v4f acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -250,59 +258,80 @@ __global__ __launch_bounds__(512) void warmup_kl_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc[mt]);
         }
+        const int cc = u * kWuKeys + col;                   // the key's column in the chunk
+        // key s is valid for row r when r >= lim, applied by selects: no branch between the
+        // matrix core's results and their first reads
+        const int lim = edge ? s - p0 : -kWuRows;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             float e[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) e[i] = ex2(fmaf(acc[mt][i], c2, -lse2[mt][i]));
-            if (edge) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) e[i] = s <= p0 + (16 * mt + 4 * grp + i) / HPW ? e[i] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const float v = ex2(fmaf(acc[mt][i], c2, -lse2[mt][i]));
+                e[i] = (16 * mt + 4 * grp + i) / HPW >= lim ? v : 0.f;
             }
             // this wave's heads of one row sum to its share of p
             if constexpr (HPW == 4) {
-                pbuf[b][wave][4 * mt + grp][col] = ((e[0] + e[1]) + (e[2] + e[3])) * inv_h;
+                pbuf[b][wave][4 * mt + grp][cc] = ((e[0] + e[1]) + (e[2] + e[3])) * inv_h;
             } else if constexpr (HPW == 2) {
-                pbuf[b][wave][8 * mt + 2 * grp][col] = (e[0] + e[1]) * inv_h;
-                pbuf[b][wave][8 * mt + 2 * grp + 1][col] = (e[2] + e[3]) * inv_h;
+                pbuf[b][wave][8 * mt + 2 * grp][cc] = (e[0] + e[1]) * inv_h;
+                pbuf[b][wave][8 * mt + 2 * grp + 1][cc] = (e[2] + e[3]) * inv_h;
             } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pbuf[b][wave][16 * mt + 4 * grp + i][col] = e[i] * inv_h;
+                for (int i = 0; i < 4; ++i) pbuf[b][wave][16 * mt + 4 * grp + i][cc] = e[i] * inv_h;
             }
+        }
+    };
+    auto chunk2 = [&](int c0, int b, float (*yc)[kWuChunk], float (*yn)[kWuChunk]) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int u = 0; u < kWuChunk; ++u) yn[j][u] = score_at(c0 + (kWuChunk + u) * kWuKeys, j);
+#pragma unroll
+        for (int u = 0; u < kWuChunk; u += 2) {
+            step2(c0 + u * kWuKeys, b, u, ka, kb2);
+            step2(c0 + (u + 1) * kWuKeys, b, u + 1, kb2, ka);
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int r = wave + NW * (grp + 4 * j);
-            if (yi[j] != -INFINITY) {                      // a valid (row, key) of the I part
-                float* sp = scores + (int64_t)(t0 + r) * ld + s;
-                const float l2 = fmaf(yi[j], kLog2e, -lse_i2[r]);  // log2 softmax(I)_s
-                const float qi = ex2(l2);
-                // the NW <= 8 waves' parts (group gg: parts gg WPG .. gg WPG + WPG-1), read
-                // from clamped slots without branches and dropped past G
-                float psum = 0.f, term = 0.f;                     // term in log2 units
 #pragma unroll
-                for (int gg = 0; gg < 8 / WPG; ++gg) {
-                    float p = 0.f;
+            for (int u = 0; u < kWuChunk; ++u) {
+                if (yc[j][u] != -INFINITY) {               // a valid (row, key) of the I part
+                    const int cc = u * kWuKeys + col;
+                    float* sp = scores + (int64_t)(t0 + r) * ld + c0 + cc;
+                    const float l2 = fmaf(yc[j][u], kLog2e, -lse_i2[r]);  // log2 softmax(I)_s
+                    const float qi = ex2(l2);
+                    // the NW <= 8 waves' parts (group gg: parts gg WPG .. gg WPG + WPG-1),
+                    // read from clamped slots without branches and dropped past G
+                    float psum = 0.f, term = 0.f;                 // term in log2 units
 #pragma unroll
-                    for (int u = 0; u < WPG; ++u) p += pbuf[b][min(gg * WPG + u, NW - 1)][r][col];
-                    p = gg < G ? p : 0.f;
-                    psum += p;
-                    term += p > 1e-37f ? p * (lg2(p) - l2) : 0.f;
+                    for (int gg = 0; gg < 8 / WPG; ++gg) {
+                        float p = 0.f;
+#pragma unroll
+                        for (int w2 = 0; w2 < WPG; ++w2) p += pbuf[b][min(gg * WPG + w2, NW - 1)][r][cc];
+                        p = gg < G ? p : 0.f;
+                        psum += p;
+                        term += p > 1e-37f ? p * (lg2(p) - l2) : 0.f;
+                    }
+                    *sp = (float)G * qi - psum;
+                    kacc[j] += term;
                 }
-                *sp = (float)G * qi - psum;
-                kacc[j] += term;
             }
         }
     };
     {
-        v8bf ka[4], kb2[4];
-        float ya[NJ], yb[NJ];
+        float ya[NJ][kWuChunk], yb[NJ][kWuChunk];
         load_keys(0, ka);
-        load_scores(0, ya);
-        for (int s0 = 0; s0 < nkeys; s0 += 2 * kWuKeys) {
-            step2(s0, 0, ka, ya, kb2, yb);
-            if (s0 + kWuKeys < nkeys) step2(s0 + kWuKeys, 1, kb2, yb, ka, ya);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int u = 0; u < kWuChunk; ++u) ya[j][u] = score_at(u * kWuKeys, j);
+        constexpr int kC = kWuChunk * kWuKeys;
+        for (int c0 = 0; c0 < nkeys; c0 += 2 * kC) {
+            chunk2(c0, 0, ya, yb);
+            if (c0 + kC < nkeys) chunk2(c0 + kC, 1, yb, ya);
         }
     }
 #pragma unroll
