@@ -258,23 +258,35 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_kernel(
         dw[t * HI + j] = red[2 * kIxHIMax * 128 + j] + red[2 * kIxHIMax * 128 + kIxHIMax + j];
 }
 
-// Backward on the matrix cores (H^I a multiple of 16, at most 64).  One workgroup per query
-// row; every wave walks all selected positions, 32 per step, and owns 32 of the 128 d_I
-// columns of both products.  Per step a wave
-//   - recomputes X = q^I k^T for all heads on the FP8 matrix core (heads on A, keys on B),
-//   - forms G = dI w [x > 0] and, in wave 0, accumulates dw = sum dI ReLU(x),
-//   - writes G through LDS as bf16 twice: heads x keys with the key scales folded in (A of
-//     dq = G K) and keys x heads (A of dk = G^T q), and stages the keys' codes,
-//   - accumulates dq [heads x its 32 columns] in registers (bf16 products of G and the key
-//     codes, which bf16 holds exactly) and computes dk [32 keys x its 32 columns], streamed
-//     to a staging buffer per (row, entry) and summed per position afterwards, or added to
-//     memory with 32-lane coalesced atomic adds.
+// Backward on the matrix cores (H^I a multiple of 16, at most 64).  One workgroup (4 waves)
+// per query row walks the row's selected positions, 32 per step:
+//   - the workgroup stages the step's key codes, key scales and dI in LDS, loaded during the
+//     step before;
+//   - wave w (w < H^I / 16) computes X = q^I k^T for head tile w (heads on A, keys on B) on
+//     the FP8 matrix core, forms G = dI w [x > 0], accumulates dw for its heads, and writes G
+//     as bf16 twice into tiles shared by the workgroup: heads x keys with the key scales
+//     folded in (A of dq = G K) and keys x heads (A of dk = G^T q);
+//   - after a barrier every wave takes 32 of the 128 d_I columns of both products: dq [all
+//     heads x its columns] accumulates in registers (bf16 products of G and the key codes,
+//     which bf16 holds exactly); dk [32 keys x its columns] passes through LDS to the staging
+//     buffer per (row, entry) in 16-byte stores (summed per position afterwards), or to
+//     memory with atomic adds.
 // G is rounded to bf16 for the two products (2^-8 relative per term, bf16's unit roundoff).
 constexpr int kBwdKeys = 32;
 
 __device__ __forceinline__ uint16_t e4m3_bf16_bits(uint32_t c)
 {
     return (uint16_t)(__float_as_uint(e4m3_value(c)) >> 16);   // exact: 4 significant bits
+}
+
+// Two floats rounded to bf16 (to nearest even, by the hardware's packed conversion).
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    bf2v r;
+    r.x = (__bf16)a;
+    r.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 template <int NHT>
@@ -287,23 +299,25 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
 {
     constexpr int HI = NHT * 16;
     constexpr int NHC = (HI + 31) / 32;                  // 32-head chunks of the dk product
-    __shared__ __attribute__((aligned(16))) uint16_t ga[4][64][kBwdKeys + 8];   // heads x keys
-    __shared__ __attribute__((aligned(16))) uint16_t gb[4][kBwdKeys][64 + 8];   // keys x heads
-    __shared__ __attribute__((aligned(16))) uint8_t kcs[4][kBwdKeys][128 + 16]; // key codes
+    __shared__ __attribute__((aligned(16))) uint16_t ga[2][64][kBwdKeys + 8];   // heads x keys
+    __shared__ __attribute__((aligned(16))) uint16_t gb[2][kBwdKeys][64 + 8];   // keys x heads
+    __shared__ __attribute__((aligned(16))) uint8_t kcs[2][kBwdKeys][128 + 16]; // key codes
     __shared__ __attribute__((aligned(16))) float st[4][kBwdKeys][32 + 4];      // dk staging
+    __shared__ float gil[2][kBwdKeys], ksl[2][kBwdKeys];                        // dI, k scale
+    __shared__ int posl[2][kBwdKeys];                                           // s, or -1
     const int64_t t = r0 + blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int c0 = 32 * wave;                            // this wave's d_I columns
-    // heads beyond HI stay zero in the keys x heads tile
-    for (int i = lane; i < kBwdKeys * 72; i += 64) (&gb[wave][0][0])[i] = 0;
-    v8i qa[NHT];
-    float wv[NHT][4];
+    // heads beyond HI stay zero in the keys x heads tiles
+    for (int i = tid; i < 2 * kBwdKeys * 72; i += kIxThreads) (&gb[0][0][0])[i] = 0;
+    const bool xw = wave < NHT;                          // this wave owns head tile `wave`
+    v8i qa = {0, 0, 0, 0, 0, 0, 0, 0};
+    float wv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (xw) {
+        qa = *reinterpret_cast<const v8i*>(q_idx + (t * HI + 16 * wave + col) * 128 + grp * 32);
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-        qa[ht] = *reinterpret_cast<const v8i*>(q_idx + (t * HI + ht * 16 + col) * 128 + grp * 32);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wv[ht][r] = w[t * HI + ht * 16 + 4 * grp + r];
+        for (int r = 0; r < 4; ++r) wv[r] = w[t * HI + 16 * wave + 4 * grp + r];
     }
     // B operands of dk = G^T q: q codes (bf16, exact) for heads 32 hc + 8 grp + j, column d
     v8bf qb[NHC][2];
@@ -323,55 +337,85 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
     v4f dqa[NHT][2];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) dqa[ht][0] = dqa[ht][1] = v4f{0.f, 0.f, 0.f, 0.f};
-    float dwa[NHT][4];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dwa[ht][r] = 0.f;
+    float dwa[4] = {0.f, 0.f, 0.f, 0.f};
 
-    for (int i0 = 0; i0 < topk; i0 += kBwdKeys) {
-        int sk[2];
-        bool okk[2];
+    // staging of a step: thread tid copies 16 code bytes of entry i0 + tid / 8 (from a valid
+    // row: invalid entries read row 0 and are marked -1); every eighth thread also its dI
+    // and key scale.  Positions are read two steps ahead, so the step's code loads do not
+    // wait on them.
+    const int kk = (tid & 255) / 8, part = tid % 8;
+    auto pos_at = [&](int i0) -> int {
+        const int i = i0 + kk;
+        const int s = idx[t * topk + min(i, topk - 1)];
+        return (i < topk && s >= 0 && s < Tk) ? s : -1;
+    };
+    auto fetch = [&](int i0, int sv, v4i& cb, float& gv, float& kv) {
+        const int sc = sv >= 0 ? sv : 0;
+        cb = *reinterpret_cast<const v4i*>(k_idx + (int64_t)sc * 128 + 16 * part);
+        gv = g[t * topk + min(i0 + kk, topk - 1)];
+        kv = k_scale[sc];
+    };
+    auto stash = [&](int buf, const v4i& cb, int sv, float gv, float kv) {
+        if (tid < 256) {
+            *reinterpret_cast<v4i*>(&kcs[buf][kk][16 * part]) = cb;
+            if (part == 0) {
+                posl[buf][kk] = sv;
+                gil[buf][kk] = sv >= 0 ? gv : 0.f;
+                ksl[buf][kk] = sv >= 0 ? kv : 0.f;
+            }
+        }
+    };
+    int s_next;                                          // positions of the next step
+    {
+        const int sv = pos_at(0);
+        s_next = pos_at(kBwdKeys);
+        v4i cb;
+        float gv, kv;
+        fetch(0, sv, cb, gv, kv);
+        stash(0, cb, sv, gv, kv);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int i0 = 0; i0 < topk; i0 += kBwdKeys, buf ^= 1) {
+        const bool more = i0 + kBwdKeys < topk;
+        const int s_after = pos_at(i0 + 2 * kBwdKeys);   // past the end: clamped, unused
+        v4i cb = {0, 0, 0, 0};
+        float gv = 0.f, kv = 0.f;
+        fetch(i0 + kBwdKeys, s_next, cb, gv, kv);        // past the end: clamped, unused
+        // G for this wave's head tile
+        if (xw) {
 #pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) {
-            const int i = i0 + 16 * kt2 + col;
-            const int s = i < topk ? idx[t * topk + i] : -1;
-            okk[kt2] = s >= 0 && s < Tk;
-            sk[kt2] = okk[kt2] ? s : 0;
-            const float gi = okk[kt2] ? g[t * topk + i] : 0.f;
-            const v8i kb = *reinterpret_cast<const v8i*>(k_idx + (int64_t)sk[kt2] * 128 + grp * 32);
-            *reinterpret_cast<v8i*>(&kcs[wave][16 * kt2 + col][grp * 32]) = kb;
-            const float ks = k_scale[sk[kt2]];
-            const float sc = qs * ks;
-#pragma unroll
-            for (int ht = 0; ht < NHT; ++ht) {
-                const v4f x = mfma_fp8_16x16x128(qa[ht], kb, v4f{0.f, 0.f, 0.f, 0.f});
-                uint16_t gbits[4];
+            for (int kt2 = 0; kt2 < 2; ++kt2) {
+                const int key = 16 * kt2 + col;
+                const v8i kb = *reinterpret_cast<const v8i*>(&kcs[buf][key][grp * 32]);
+                const v4f x = mfma_fp8_16x16x128(qa, kb, v4f{0.f, 0.f, 0.f, 0.f});
+                const float gi = gil[buf][key], ks = ksl[buf][key];
+                const float sc = qs * ks;
+                float gvv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float xv = x[r] * sc;
-                    const float gv = xv > 0.f ? gi * wv[ht][r] : 0.f;
-                    if (wave == 0) dwa[ht][r] += gi * fmaxf(xv, 0.f);
-                    ga[wave][16 * ht + 4 * grp + r][16 * kt2 + col] = f32_to_bf16_bits(gv * ks);
-                    gbits[r] = f32_to_bf16_bits(gv);
+                    gvv[r] = xv > 0.f ? gi * wv[r] : 0.f;
+                    dwa[r] = fmaf(gi, fmaxf(xv, 0.f), dwa[r]);
+                    ga[buf][16 * wave + 4 * grp + r][key] = (uint16_t)(pack_bf16x2(gvv[r] * ks, 0.f) & 0xffffu);
                 }
-                *reinterpret_cast<uint2*>(&gb[wave][16 * kt2 + col][16 * ht + 4 * grp]) =
-                    make_uint2(gbits[0] | ((uint32_t)gbits[1] << 16), gbits[2] | ((uint32_t)gbits[3] << 16));
+                *reinterpret_cast<uint2*>(&gb[buf][key][16 * wave + 4 * grp]) =
+                    make_uint2(pack_bf16x2(gvv[0], gvv[1]), pack_bf16x2(gvv[2], gvv[3]));
             }
         }
-        __builtin_amdgcn_wave_barrier();
+        __syncthreads();
         // dq[heads, c0 .. c0 + 32) += G' K: A = G' (head row, keys 8 grp ..), B = key codes
         v8bf kbop[2];
 #pragma unroll
         for (int dtl = 0; dtl < 2; ++dtl) {
             v8s x;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = (short)e4m3_bf16_bits(kcs[wave][8 * grp + j][c0 + 16 * dtl + col]);
+            for (int j = 0; j < 8; ++j) x[j] = (short)e4m3_bf16_bits(kcs[buf][8 * grp + j][c0 + 16 * dtl + col]);
             kbop[dtl] = __builtin_bit_cast(v8bf, x);
         }
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
-            const v8bf a = *reinterpret_cast<const v8bf*>(&ga[wave][16 * ht + col][8 * grp]);
+            const v8bf a = *reinterpret_cast<const v8bf*>(&ga[buf][16 * ht + col][8 * grp]);
             dqa[ht][0] = mfma_bf16_16x16x32(a, kbop[0], dqa[ht][0]);
             dqa[ht][1] = mfma_bf16_16x16x32(a, kbop[1], dqa[ht][1]);
         }
@@ -383,26 +427,40 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
                 v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int hc = 0; hc < NHC; ++hc) {
-                    const v8bf a = *reinterpret_cast<const v8bf*>(&gb[wave][16 * kt2 + col][32 * hc + 8 * grp]);
+                    const v8bf a = *reinterpret_cast<const v8bf*>(&gb[buf][16 * kt2 + col][32 * hc + 8 * grp]);
                     acc = mfma_bf16_16x16x32(a, qb[hc][dtl], acc);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) st[wave][16 * kt2 + 4 * grp + r][16 * dtl + col] = acc[r] * qs;
             }
         __builtin_amdgcn_wave_barrier();
-        // 32 keys x 32 columns: two keys per instruction, 32 consecutive floats each
-        for (int m = 0; m < kBwdKeys / 2; ++m) {
-            const int key = 2 * m + (lane >> 5);
-            const int i = i0 + key;
-            const int s = i < topk ? idx[t * topk + i] : -1;
-            if (s < 0 || s >= Tk) continue;
-            const float val = st[wave][key][lane & 31];
-            if (stg)                                     // streaming store, reduced later
-                __builtin_nontemporal_store(val, stg + ((t - r0) * topk + i) * 128 + c0 + (lane & 31));
-            else
-                atomicAdd(dk + (int64_t)s * 128 + c0 + (lane & 31), val);
+        if (stg) {
+            // 32 keys x 32 columns in 16-byte pieces: a piece per lane and step, 8 keys per
+            // instruction (streaming stores, reduced later); entries past topk are skipped
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int f = (j * 64 + lane) * 4, key = f / 32, cc = f % 32;
+                const int i = i0 + key;
+                if (i < topk) {
+                    const float4 v = *reinterpret_cast<const float4*>(&st[wave][key][cc]);
+                    float4* dst = reinterpret_cast<float4*>(stg + ((t - r0) * topk + i) * 128 + c0 + cc);
+                    __builtin_nontemporal_store(v.x, &dst->x);
+                    __builtin_nontemporal_store(v.y, &dst->y);
+                    __builtin_nontemporal_store(v.z, &dst->z);
+                    __builtin_nontemporal_store(v.w, &dst->w);
+                }
+            }
+        } else {
+            // two keys per instruction, 32 consecutive floats each
+            for (int m = 0; m < kBwdKeys / 2; ++m) {
+                const int key = 2 * m + (lane >> 5);
+                const int s = posl[buf][key];
+                if (s >= 0) atomicAdd(dk + (int64_t)s * 128 + c0 + (lane & 31), st[wave][key][lane & 31]);
+            }
         }
-        __builtin_amdgcn_wave_barrier();
+        if (more) stash(buf ^ 1, cb, s_next, gv, kv);
+        s_next = s_after;
+        __syncthreads();
     }
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht)
@@ -411,16 +469,14 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 dq[(t * HI + 16 * ht + 4 * grp + r) * 128 + c0 + 16 * dtl + col] = dqa[ht][dtl][r];
-    if (wave == 0) {
+    if (xw) {
 #pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
+        for (int r = 0; r < 4; ++r) {
+            float v = dwa[r];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = dwa[ht][r];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-                if (col == 0) dw[t * HI + 16 * ht + 4 * grp + r] = v;
-            }
+            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+            if (col == 0) dw[t * HI + 16 * wave + 4 * grp + r] = v;
+        }
     }
 }
 
