@@ -443,17 +443,29 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
                         *reinterpret_cast<v4f*>(stage + col * kStagePitch + dt * 16 + 4 * grp) = acc * mul;
                     }
                     __builtin_amdgcn_wave_barrier();
-                    for (int r = 0; r < 16; ++r) {
-                        const int pos = pt * 16 + r;
-                        if (!((valid >> pos) & 1u)) continue;       // uniform
-                        const float a0 = stage[r * kStagePitch + lane];
-                        const float a1 = stage[r * kStagePitch + 64 + lane];
-                        if (p.stg) {                     // streaming stores, reduced later
-                            const int64_t e = (int64_t)(row - p.r0) * topk + kb0 + pos;
-                            float* dst = p.stg + (e * p.G + g) * 256 + mat * 128;
-                            __builtin_nontemporal_store(a0, dst + lane);
-                            __builtin_nontemporal_store(a1, dst + 64 + lane);
-                        } else {
+                    if (p.stg) {
+                        // streaming stores, reduced later: 16 bytes per lane, two positions
+                        // (512 bytes each) per instruction
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            const int r = 2 * m + (lane >> 5), c4 = 4 * (lane & 31);
+                            const int pos = pt * 16 + r;
+                            if ((valid >> pos) & 1u) {
+                                const float4 a = *reinterpret_cast<const float4*>(stage + r * kStagePitch + c4);
+                                const int64_t e = (int64_t)(row - p.r0) * topk + kb0 + pos;
+                                float4* dst = reinterpret_cast<float4*>(p.stg + (e * p.G + g) * 256 + mat * 128 + c4);
+                                __builtin_nontemporal_store(a.x, &dst->x);
+                                __builtin_nontemporal_store(a.y, &dst->y);
+                                __builtin_nontemporal_store(a.z, &dst->z);
+                                __builtin_nontemporal_store(a.w, &dst->w);
+                            }
+                        }
+                    } else {
+                        for (int r = 0; r < 16; ++r) {
+                            const int pos = pt * 16 + r;
+                            if (!((valid >> pos) & 1u)) continue;       // uniform
+                            const float a0 = stage[r * kStagePitch + lane];
+                            const float a1 = stage[r * kStagePitch + 64 + lane];
                             const int s = idx_row[kb0 + pos];
                             float* dst = dst_base + ((int64_t)s * p.G + g) * 128;
                             atomicAdd(dst + lane, a0);
