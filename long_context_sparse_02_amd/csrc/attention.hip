@@ -618,14 +618,14 @@ __global__ __launch_bounds__(256) void stage_reduce_kernel(const float* __restri
     for (int g = wave; g < G; g += 4) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         int j = b;
-        for (; j + 4 <= e; j += 4) {                     // four rows in flight, added in order
-            v4f x[4];
+        for (; j + 8 <= e; j += 8) {                     // eight rows in flight, added in order
+            v4f x[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 8; ++u)
                 x[u] = __builtin_nontemporal_load(
                     reinterpret_cast<const v4f*>(stg + ((int64_t)list[j + u] * G + g) * 256) + lane);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 acc.x += x[u][0]; acc.y += x[u][1]; acc.z += x[u][2]; acc.w += x[u][3];
             }
         }
@@ -655,13 +655,13 @@ __global__ __launch_bounds__(64) void stage_reduce128_kernel(const float* __rest
     typedef float v2f __attribute__((ext_vector_type(2)));
     float ax = 0.f, ay = 0.f;
     int j = b;
-    for (; j + 4 <= e; j += 4) {
-        v2f x[4];
+    for (; j + 8 <= e; j += 8) {                         // eight rows in flight, added in order
+        v2f x[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
             x[u] = __builtin_nontemporal_load(reinterpret_cast<const v2f*>(stg + (int64_t)list[j + u] * 128) + lane);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) { ax += x[u][0]; ay += x[u][1]; }
+        for (int u = 0; u < 8; ++u) { ax += x[u][0]; ay += x[u][1]; }
     }
     for (; j < e; ++j) {
         const v2f x = __builtin_nontemporal_load(reinterpret_cast<const v2f*>(stg + (int64_t)list[j] * 128) + lane);
