@@ -13,9 +13,10 @@
 //   dw[t,j]  = sum_s dI[t,s] ReLU(x[t,j,s]),
 //   dq[t,j]  = sum_s G[t,j,s] k^I[s],     dk[s] += sum_j G[t,j,s] q^I[t,j].
 // FP8 inputs (OCP E4M3 codes, per-token fp32 scales), d_I = 128, one workgroup
-// per query row.  The scores run on the FP8 matrix core (H^I a multiple of 16;
-// other head counts on the vector ALU from the decoded codes); the backward runs
-// on the vector ALU in fp32 from the decoded codes (exact values).
+// per query row.  For H^I a multiple of 16 the scores and the backward run on the
+// matrix cores (x on the FP8 one, the products with G in bf16); other head counts
+// run on the vector ALU in fp32 from the decoded codes (exact values), the
+// backward then adding dk^I atomically.
 #include "device_common.h"
 #include "internal.h"
 
