@@ -315,6 +315,17 @@ __device__ __forceinline__ int sample_pos(int j, int S, int n0, int tile) {
     return width > 1 ? lo + (int)(h % (uint32_t)width) : min(lo, n0 - 1);
 }
 
+// Token tiles of 16 rows, counted from the chunk's first, whose last token (position
+// q_pos0 + min(16 tt + 15, Tq - 1)) sees no key at or after k0: the tiles that have no causal
+// score in a key group starting at k0.
+__host__ __device__ inline int tiles_above(int64_t k0, int64_t q_pos0, int Tq, int n_tt) {
+    const int64_t d = k0 - q_pos0;
+    if (d >= Tq) return n_tt;
+    if (d <= 0) return 0;
+    const int64_t full = d / 16;            // tiles before the last one: 16 tt + 16 <= d
+    return full < n_tt - 1 ? (int)full : n_tt - 1;
+}
+
 struct ResOut {
     float* scores; int64_t ld;                  // kModeScores
     const int* run_if;                          // kModeScores: skip unless *run_if != 0 (nullable)
@@ -329,7 +340,7 @@ void index_fp8_resident_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ k_scale, const uint16_t* __restrict__ qmix, int Tq, int Tk,
-    int HI, int64_t q_pos0, ResOut o, int n_kb, int n_kg, int kg)
+    int HI, int64_t q_pos0, ResOut o, int n_kb, int n_kg, int kg, int n_work)
 {
     constexpr int kKeysPerWave = 16 * NK;
     constexpr int kKeysPerBlock = kResWaves * kKeysPerWave;
@@ -338,12 +349,24 @@ void index_fp8_resident_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t qm_lds[16][264];   // padded rows: no bank conflicts
 
     if (MODE == kModeScores && o.run_if && *o.run_if == 0) return;
-    // key-group-major order: the workgroups resident on one XCD share a key group (hot in
-    // that XCD's L2) and differ in their token tiles
-    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    // The first n_work workgroups are the (key group, token tile) pairs with causal scores,
+    // key-group-major and without the tiles wholly above the diagonal, so that equal
+    // contiguous shares of them (one per XCD) carry about equal work and the workgroups
+    // resident on one XCD share a key group (hot in that XCD's L2).  In kModeScores the
+    // workgroups after them fill the pairs above the diagonal with -inf.
     const int n_tt = (Tq + 15) / 16;
-    const int g = work / n_tt;
-    const int tt = work - g * n_tt;
+    const bool fill = (int)blockIdx.x >= n_work;
+    int g = 0, tt = 0;
+    {
+        int rem = fill ? (int)blockIdx.x - n_work : xcd_remap(blockIdx.x, n_work);
+        for (;; ++g) {
+            const int above = MODE == kModeSample
+                ? 0 : tiles_above((int64_t)g * kg * kKeysPerBlock, q_pos0, Tq, n_tt);
+            const int here = fill ? above : n_tt - above;
+            if (rem < here || g == n_kg - 1) { tt = (fill ? 0 : above) + rem; break; }
+            rem -= here;
+        }
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -358,20 +381,23 @@ void index_fp8_resident_kernel(
     const int n0 = (int)min<int64_t>(q_pos0 + t0 + 1, Tk);
     float* __restrict__ out_row = MODE == kModeScores ? o.scores + (int64_t)tc * o.ld : nullptr;
 
-    // whole group above the diagonal: only -inf to write (or nothing)
-    if (MODE != kModeSample && (int64_t)kb_begin * kKeysPerBlock > pos_hi) {
-        if (MODE == kModeScores && t_ok) {
-            for (int kb = kb_begin; kb < kb_end; ++kb) {
-                const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;
+    // whole group above the diagonal: only -inf to write.  Each wave fills whole token rows
+    // of the group's columns, 1 KiB per instruction.
+    if (MODE == kModeScores && fill) {
+        const int c_end = min(kb_end * kKeysPerBlock, Tk);
+        const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        static_assert(kResWaves == 16 || kResWaves == 8 || kResWaves == 4, "rows per wave");
 #pragma unroll
-                for (int i = 0; i < NK; ++i) {
-                    const int s0 = s_base + 16 * i + 4 * grp;
-                    if (s0 + 3 < Tk)
-                        *reinterpret_cast<float4*>(out_row + s0) =
-                            make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                    else
-                        for (int e = 0; e < 4; ++e)
-                            if (s0 + e < Tk) out_row[s0 + e] = -INFINITY;
+        for (int rr = 0; rr < 16 / kResWaves; ++rr) {
+            const int r = wave + rr * kResWaves;
+            if (t0 + r >= Tq) break;
+            float* __restrict__ row_w = o.scores + (int64_t)(t0 + r) * o.ld;
+            for (int c = kb_begin * kKeysPerBlock + 4 * lane; c < c_end; c += 256) {
+                if (c + 3 < c_end) {
+                    *reinterpret_cast<float4*>(row_w + c) = ninf;
+                } else {
+                    for (int e = 0; e < 4; ++e)
+                        if (c + e < c_end) row_w[c + e] = -INFINITY;
                 }
             }
         }
@@ -844,11 +870,19 @@ hipError_t launch_resident(const uint8_t* q_idx, const float* q_scale, const flo
     int kg = n_kb1 / 8;
     kg = kg < 1 ? 1 : (kg > kg_max ? kg_max : kg);
     const int n_kg = (n_kb1 + kg - 1) / kg;
-    const int64_t nw = (int64_t)n_tt * n_kg;
-    if (nw > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((index_fp8_resident_kernel<kResNK, MODE>), dim3((unsigned)nw), dim3(kResWaves * 64),
-                       0, stream, q_idx, q_scale, w, k_idx, k_scale,
-                       static_cast<const uint16_t*>(ws), Tq, Tk, HI, q_pos0, o, n_kb1, n_kg, kg);
+    if ((int64_t)n_tt * n_kg > INT32_MAX) return hipErrorInvalidValue;
+    // pairs (key group, token tile) with causal scores, and in kModeScores the -inf ones
+    int n_work = 0, n_fill = 0;
+    for (int g = 0; g < n_kg; ++g) {
+        const int above = MODE == kModeSample
+            ? 0 : tiles_above((int64_t)g * kg * kResWaves * 16 * kResNK, q_pos0, Tq, n_tt);
+        n_work += n_tt - above;
+        if (MODE == kModeScores) n_fill += above;
+    }
+    hipLaunchKernelGGL((index_fp8_resident_kernel<kResNK, MODE>), dim3((unsigned)(n_work + n_fill)),
+                       dim3(kResWaves * 64), 0, stream, q_idx, q_scale, w, k_idx, k_scale,
+                       static_cast<const uint16_t*>(ws), Tq, Tk, HI, q_pos0, o, n_kb1, n_kg, kg,
+                       n_work);
     return hipGetLastError();
 }
 

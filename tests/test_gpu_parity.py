@@ -33,7 +33,7 @@ def _fp8_case(L, HI=64, seed=0, clustered=False, dev=DEV):
 
 # ------------------------------------------------------------------ indexer
 
-@pytest.mark.parametrize("L,q_pos0", [(300, 0), (1100, 0), (777, 523)])
+@pytest.mark.parametrize("L,q_pos0", [(300, 0), (1100, 0), (777, 523), (1403, 0)])
 def test_index_scores_fp8_full(L, q_pos0):
     _say("index fp8", L, q_pos0)
     cfg, x = _fp8_case(L, seed=L)
