@@ -529,6 +529,15 @@ constexpr int kKbKeysW = 48;         // keys per wave
 constexpr int kKbKT = kKbKeysW / 16;  // 16-key tiles per wave
 constexpr int kKbKeys = kKbWaves * kKbKeysW;
 
+// Rows [r_begin, r_end) of row range sp that see key block kb: from the range's first row, or
+// from the first row whose position reaches the block's first key, to the range's end.
+__device__ __forceinline__ void split_rows(int kb, int sp, int rows_per_split, int Tq, int64_t q_pos0,
+                                           int& r_begin, int& r_end) {
+    const int64_t first = max<int64_t>((int64_t)sp * rows_per_split, (int64_t)kb * kKbKeys - q_pos0);
+    r_begin = (int)min<int64_t>(max<int64_t>(first, 0), (int64_t)Tq);
+    r_end = (int)min<int64_t>((int64_t)Tq, (int64_t)(sp + 1) * rows_per_split);
+}
+
 // dk^I partial sums: workgroup (key block kb, row range sp) owns 384 keys (48 per wave)
 // and streams the query rows of its range that see them, one row per step (codes,
 // w and the bf16 values [column][head] staged in LDS).  Per row a wave computes x
@@ -554,9 +563,9 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
     const int kb = blockIdx.x, sp = blockIdx.y;
     const int sw = kb * kKbKeys + wave * kKbKeysW;      // this wave's first key
     const int sb = kb * kKbKeys;                        // the workgroup's first key
-    const int64_t first = max<int64_t>((int64_t)sp * rows_per_split, (int64_t)sb - q_pos0);
-    const int r_begin = (int)min<int64_t>(max<int64_t>(first, 0), (int64_t)Tq);
-    const int r_end = min(Tq, (sp + 1) * rows_per_split);
+    int r_begin, r_end;
+    split_rows(kb, sp, rows_per_split, Tq, q_pos0, r_begin, r_end);
+    if (r_begin >= r_end) return;                       // no row sees these keys: no partial
 
     v8i kbop[kKbKT];
     float ksc[kKbKT];
@@ -616,10 +625,8 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
 #pragma unroll
     for (int u = 0; u < NV; ++u) bv[u] = v4i{0, 0, 0, 0};
     float wvl = 0.f, gsv[3] = {0.f, 0.f, 0.f};
-    if (r_begin < r_end) {
-        fetch(r_begin, cb, bv, wvl, gsv);
-        stash(r_begin, 0, cb, bv, wvl, gsv);
-    }
+    fetch(r_begin, cb, bv, wvl, gsv);
+    stash(r_begin, 0, cb, bv, wvl, gsv);
     __syncthreads();
     int buf = 0;
     for (int t = r_begin; t < r_end; ++t, buf ^= 1) {
@@ -683,15 +690,21 @@ __global__ __launch_bounds__(512) void warmup_ix_bwd_k_kernel(
         }
 }
 
-// dk[s][c] += sum over sp = 0 .. nsplit-1 of part[sp][s][c], in that order.
+// dk[s][c] += sum of part[sp][s][c] over the row ranges sp = 0 .. nsplit-1 that hold a row
+// seeing key s's block, in that order.
 __global__ __launch_bounds__(256) void warmup_dk_sum_kernel(const float* __restrict__ part, int nsplit,
-                                                            int64_t stride, int64_t n4,
+                                                            int64_t stride, int64_t n4, int rows_per_split,
+                                                            int Tq, int64_t q_pos0,
                                                             float* __restrict__ dk)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n4) return;
+    const int kb = (int)(i / (32 * kKbKeys));           // 32 float4 per key
     float4 a = reinterpret_cast<float4*>(dk)[i];
     for (int sp = 0; sp < nsplit; ++sp) {
+        int r_begin, r_end;
+        split_rows(kb, sp, rows_per_split, Tq, q_pos0, r_begin, r_end);
+        if (r_begin >= r_end) continue;
         const float4 b = reinterpret_cast<const float4*>(part + sp * stride)[i];
         a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
     }
@@ -743,8 +756,10 @@ WarmupBwdPlan plan_warmup_bwd(int Tq, int Tk, int HI)
     WarmupBwdPlan p;
     p.ldk = (Tk + 63) / 64 * 64;
     p.kblocks = (Tk + kKbKeys - 1) / kKbKeys;
-    // enough workgroups to fill the chip: split the query rows into ranges
-    const int want = 1024;
+    // split the query rows into ranges: about 4096 (key block, row range) pairs, of which
+    // the half below the diagonal does work, so that the last workgroups to start (one per
+    // CU at a time) leave little of the chip idle at the end
+    const int want = 4096;
     p.nsplit = Tq > 0 ? std::max(1, std::min((want + p.kblocks - 1) / p.kblocks, (Tq + 63) / 64)) : 1;
     p.rows_per_split = Tq > 0 ? (Tq + p.nsplit - 1) / p.nsplit : 1;
     p.kt_bytes = (size_t)128 * p.ldk * 2;
@@ -793,7 +808,7 @@ hipError_t launch_warmup_ix_bwd(const uint8_t* q_idx, const float* q_scale, cons
     }
     const int64_t n4 = (int64_t)Tk * 128 / 4;
     hipLaunchKernelGGL(warmup_dk_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                       part, p.nsplit, (int64_t)p.ldk * 128, n4, dk);
+                       part, p.nsplit, (int64_t)p.ldk * 128, n4, p.rows_per_split, Tq, q_pos0, dk);
     return hipGetLastError();
 }
 
