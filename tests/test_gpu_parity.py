@@ -49,6 +49,24 @@ def test_index_scores_fp8_full(L, q_pos0):
         check_scores(g[i, :L], ref[i], q_pos0 + i, "row %d" % i)
 
 
+@pytest.mark.parametrize("L,q0,q1", [(3001, 300, 800), (5000, 0, 37), (2100, 1030, 1047)])
+def test_index_scores_fp8_keys_past_the_last_row(L, q0, q1):
+    """Rows q0 .. q1-1 against all L keys: whole key groups lie above every row (their
+    workgroups only write -inf), and every entry past a row's position must be -inf."""
+    _say("index fp8 keys past the rows", L, q0, q1)
+    cfg, x = _fp8_case(L, seed=L + q0)
+    sl = slice(q0, q1)
+    scores = dsa.index_scores(x["q_idx"][sl].contiguous(), x["q_scale"][sl].contiguous(),
+                              x["w"][sl].contiguous(), x["k_idx"], x["k_scale"], q_pos0=q0)
+    torch.cuda.synchronize()
+    g = to_np(scores)
+    ref = oracle.index_scores(to_np(x["q_idx"][sl]), to_np(x["q_scale"][sl]), to_np(x["w"][sl]),
+                              to_np(x["k_idx"][:q1]), to_np(x["k_scale"][:q1]), oracle.FP8_E4M3,
+                              q_pos0=q0)
+    for i in range(q1 - q0):
+        check_scores(g[i, :L], ref[i], q0 + i, "row %d" % i)
+
+
 def test_index_scores_fp8_signed_w_and_small_heads():
     _say("index fp8 signed w, HI=4")
     cfg, x = _fp8_case(200, HI=4, seed=7)
