@@ -157,14 +157,17 @@ def _check_grads(got, ref, bounds, what):
         assert np.all(err <= lim), (what, name)
 
 
-@pytest.mark.parametrize("T,q_pos0,HI", [(200, 0, 64), (150, 333, 64), (97, 40, 16),
-                                          (120, 0, 48), (300, 700, 32)])
-def test_index_scores_bwd_dense_vs_oracle(T, q_pos0, HI):
+@pytest.mark.parametrize("T,q_pos0,HI,extra", [(200, 0, 64, 0), (150, 333, 64, 0), (97, 40, 16, 0),
+                                                (120, 0, 48, 0), (300, 700, 32, 0),
+                                                (100, 50, 64, 900)])
+def test_index_scores_bwd_dense_vs_oracle(T, q_pos0, HI, extra):
     """dq^I, dw and dk^I against the oracle; entries of g beyond each row's prefix are NaN and
-    must be ignored; two calls give identical bits; two row chunks accumulate dk^I."""
-    _say("dense indexer bwd T=%d q_pos0=%d HI=%d" % (T, q_pos0, HI))
+    must be ignored; two calls give identical bits; two row chunks accumulate dk^I.  With
+    `extra` keys past the last row's position, whole key blocks are seen by no row: their
+    dk^I must stay exactly zero."""
+    _say("dense indexer bwd T=%d q_pos0=%d HI=%d extra=%d" % (T, q_pos0, HI, extra))
     rng = np.random.default_rng(T + HI + q_pos0)
-    Tk = q_pos0 + T
+    Tk = q_pos0 + T + extra
     qc, qs, w, kc, ks = _int_indexer(rng, T, Tk, HI)
     causal = _causal_lists(T, Tk, q_pos0) >= 0
     ld = Tk + 4
@@ -185,6 +188,8 @@ def test_index_scores_bwd_dense_vs_oracle(T, q_pos0, HI):
     assert torch.equal(torch.cat([parts[0][0], parts[1][0]]), dq)     # per row: same work
     assert torch.equal(torch.cat([parts[0][1], parts[1][1]]), dw)
     assert (dkc - dk).abs().max().item() <= 1e-5 * dk.abs().max().item()
+    if extra:
+        assert torch.count_nonzero(dk[q_pos0 + T:]).item() == 0
     gd = np.where(causal, g[:, :Tk], 0.0).astype(np.float64)
     rq, rw, rk = oracle.index_scores_bwd_dense(qc, qs, w, kc, ks, oracle.FP8_E4M3, gd,
                                                q_pos0=q_pos0)
