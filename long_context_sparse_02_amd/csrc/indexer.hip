@@ -22,6 +22,20 @@
 // max and an fma.  On gfx950 a wave's vector ALU work does not overlap its own
 // matrix-core work, so halving it is worth about 1.3x on this kernel.
 //
+// The rewrite is exact algebra but not exact arithmetic: when most heads' dot
+// products are negative, the two terms nearly cancel and their rounding errors
+// (the FP8 matrix core aligns its products to the largest one with about 2^-15
+// of Sigma|products| of error; the bf16 hi + lo qmix carries 2^-17) are left
+// over a small or zero score.  So each score is checked: with A = sum_j w_j |x_j|
+// and L = qmix . k, a wave whose block holds any entry with
+// |A| + |L| > kCancel * |A + L| (at w >= 0: the negative heads outweigh the
+// positive ones 7 to 1) recomputes that block exactly in the direct form,
+// sum_j w_j max(x_j, 0), with x_j from the bf16 matrix core on the exact bf16
+// values of the codes (fp32 accumulation; exact zeros stay zero).  Measured on
+// gfx950 against the exact scores: below that ratio the rewrite's error stays
+// under a quarter of the score tolerance; Gaussian queries and keys almost
+// never reach it, so the check costs about two vector instructions per score.
+//
 // A wave keeps its NK key tiles (16*NK keys, 8 VGPRs each) in registers for the
 // whole head loop.  The four waves of a workgroup share the same 16 tokens, so
 // q^I is staged cooperatively in LDS, 8 heads (16 KB) at a time and
@@ -89,6 +103,46 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(const v8i& a, int m) {
     const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
     const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
     return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Cancellation guard of the |x| rewrite (see the file header).
+constexpr float kCancel = 15.f;
+
+// Guard metric of one entry: > 0 when the rewrite cannot be trusted for it.
+__device__ __forceinline__ float cancel_metric(float a, float l) {
+    return fabsf(a) + fabsf(l) - kCancel * fabsf(a + l);
+}
+
+// Exact direct form for NK key tiles of one wave: ex[i][e] = 2 sum_j w_j max(x_j, 0) for the
+// heads j0 .. j1-1 staged at q_row (head j at q_row + j * head_stride bytes; this lane's
+// 32-byte slice) with weights w_row[j * w_stride], added to ex.  x_j comes from the bf16 matrix
+// core on the exact bf16 values of the FP8 codes (fp32 accumulation).  ka: the key tiles'
+// bf16 operands.  Factor 2: the epilogue scales by q_scale / 2 for the rewrite's halves.
+template <int NK>
+__device__ __forceinline__ void exact_heads(const v8bf (&ka)[NK][4], const uint8_t* q_row,
+                                            int head_stride, const float* w_row, int w_stride,
+                                            int j0, int j1, float (&ex)[NK][4]) {
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    for (int j = j0; j < j1; ++j) {
+        const uint8_t* qp = q_row + j * head_stride;
+        const v4i lo = *reinterpret_cast<const v4i*>(qp);
+        const v4i hi = *reinterpret_cast<const v4i*>(qp + 16);
+        const v8i qc = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const float w2 = 2.f * w_row[j * w_stride];
+        v4f x[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) x[i] = zero;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const v8bf qb = fp8x8_to_bf16(qc, m);
+#pragma unroll
+            for (int i = 0; i < NK; ++i) x[i] = mfma_bf16_16x16x32(ka[i][m], qb, x[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ex[i][e] = fmaf(w2, fmaxf(x[i][e], 0.f), ex[i][e]);
+    }
 }
 
 constexpr int kHeadBatch = 8;            // indexer heads staged in LDS at a time
@@ -185,32 +239,13 @@ void index_fp8_kernel(
         if (tid < 16 * kHeadBatch) w_lds[buf][tid >> 4][tid & 15] = wstage;
     };
 
-    // accumulators start at the linear term qmix . k (bf16 matrix core)
+    // acc = sum_j w_j |x_j| over the head loop; the linear term qmix . k follows it
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     float acc[NK][4];
-    {
-        const uint16_t* qm = qmix + (int64_t)tc * 256 + grp * 32;
-        v8bf bh[4], bl[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            bh[m] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 8 * m));
-            bl[m] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 128 + 8 * m));
-        }
+    for (int i = 0; i < NK; ++i)
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            v4f lin = zero;
-            if (active) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const v8bf ka = fp8x8_to_bf16(a[i], m);
-                    lin = mfma_bf16_16x16x32(ka, bh[m], lin);
-                    lin = mfma_bf16_16x16x32(ka, bl[m], lin);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][e] = lin[e];
-        }
-    }
+        for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
     // the epilogue of "head -1" adds 0 * max(0, 0): no special first iteration
     v4f dprev[NK];
 #pragma unroll
@@ -247,14 +282,62 @@ void index_fp8_kernel(
         if (b + 1 < n_batch) store_batch(buf ^ 1);
         __syncthreads();
     }
-    if (!active) {
-        fill_masked();
-        return;
-    }
 #pragma unroll
     for (int i = 0; i < NK; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
+    // the linear term (bf16 matrix core) and the cancellation guard
+    bool redo = false;
+    if (active) {
+        const uint16_t* qm = qmix + (int64_t)tc * 256 + grp * 32;
+        float worst = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            v4f lin = zero;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const v8bf bh = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 8 * m));
+                const v8bf bl = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 128 + 8 * m));
+                const v8bf ka = fp8x8_to_bf16(a[i], m);
+                lin = mfma_bf16_16x16x32(ka, bh, lin);
+                lin = mfma_bf16_16x16x32(ka, bl, lin);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                worst = fmaxf(worst, cancel_metric(acc[i][e], lin[e]));
+                acc[i][e] += lin[e];
+            }
+        }
+        redo = __ballot(worst > 0.f) != 0;            // uniform over the wave
+    }
+    // a wave with an entry the rewrite cannot be trusted for recomputes its block exactly;
+    // the whole workgroup stages q^I again, one head batch at a time
+    if (__syncthreads_or(redo)) {
+        v8bf ka[NK][4];
+        if (redo) {
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) ka[i][m] = fp8x8_to_bf16(a[i], m);
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+        }
+        for (int b = 0; b < n_batch; ++b) {
+            load_batch(b);
+            store_batch(0);
+            __syncthreads();
+            if (redo)
+                exact_heads<NK>(ka, &q_lds[0][0][col][grp * 32], 16 * kQPitch, &w_lds[0][0][col],
+                                16, 0, kHeadBatch, acc);
+            __syncthreads();
+        }
+    }
+    if (!active) {
+        fill_masked();
+        return;
+    }
 
     if (!t_ok) return;
     const float qs = 0.5f * q_scale[tc];                // (linear + |x| terms) / 2
@@ -431,100 +514,14 @@ void index_fp8_resident_kernel(
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int n_keys = MODE == kModeSample ? o.S : Tk;   // logical keys of this launch
 
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-        const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;   // logical key index
-        if (s_base >= n_keys) break;
-        if (MODE != kModeSample && (int64_t)s_base > pos_hi) {   // wave tile above the diagonal
-            if (MODE == kModeScores && t_ok) {
-#pragma unroll
-                for (int i = 0; i < NK; ++i) {
-                    const int s0 = s_base + 16 * i + 4 * grp;
-                    if (s0 + 3 < Tk)
-                        *reinterpret_cast<float4*>(out_row + s0) =
-                            make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-                    else
-                        for (int e = 0; e < 4; ++e)
-                            if (s0 + e < Tk) out_row[s0 + e] = -INFINITY;
-                }
-            }
-            continue;
-        }
-        // keys (A operands) of this wave, 16 NK keys, 32 bytes per lane per tile, and the
-        // scale of key 16 i + col: unconditional loads from rows clamped into the array
-        // (keys s >= Tk lie above the diagonal and are masked below), so no branch makes
-        // the compiler wait for them before it has to
-        v8i a[NK];
-        float ksl[NK];
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int s = MODE == kModeSample ? sample_pos(min(s_base + 16 * i + col, n_keys - 1), o.S, n0, tt)
-                                              : min(s_base + 16 * i + col, Tk - 1);
-            a[i] = load32B(k_idx + (int64_t)s * 128 + grp * 32);
-            ksl[i] = k_scale[s];
-        }
-        // all of the block's loads are in flight before any math: keep the compiler
-        // from sinking some of them below the first uses of the others
-        asm volatile("" ::: "memory");
-        // accumulators start at the linear term qmix . k (bf16 matrix core), one
-        // 32-wide slice m of the contraction at a time for every tile
-        float acc[NK][4];
-        {
-            const uint16_t* qm = &qm_lds[col][grp * 32];
-            v4f lin[NK];
-#pragma unroll
-            for (int i = 0; i < NK; ++i) lin[i] = zero;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const v8bf bh = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 8 * m));
-                const v8bf bl = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 128 + 8 * m));
-#pragma unroll
-                for (int i = 0; i < NK; ++i) {
-                    const v8bf ka = fp8x8_to_bf16(a[i], m);
-                    lin[i] = mfma_bf16_16x16x32(ka, bh, lin[i]);
-                    lin[i] = mfma_bf16_16x16x32(ka, bl, lin[i]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < NK; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][e] = lin[i][e];
-        }
-        // head loop: the B operand (q^I of head j for the 16 tokens) is read from LDS one
-        // head ahead, and the |x| epilogue of head j-1 follows the MFMAs of head j
-        v4f dprev[NK];
-#pragma unroll
-        for (int i = 0; i < NK; ++i) dprev[i] = zero;
-        float wprev = 0.f;
-        const uint8_t* qbase = &q_lds[0][col][grp * 32];
-        v4i nlo = *reinterpret_cast<const v4i*>(qbase);
-        v4i nhi = *reinterpret_cast<const v4i*>(qbase + 16);
-        float nw = w_lds[0][col];
-        for (int j0 = 0; j0 < HP; j0 += 8) {
-#pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                const int j = j0 + hh;
-                const v8i bq = {nlo.x, nlo.y, nlo.z, nlo.w, nhi.x, nhi.y, nhi.z, nhi.w};
-                const float wj = nw;
-                const int jn = (j + 1 < HP) ? j + 1 : j;
-                nlo = *reinterpret_cast<const v4i*>(qbase + jn * 16 * kQPitch);
-                nhi = *reinterpret_cast<const v4i*>(qbase + jn * 16 * kQPitch + 16);
-                nw = w_lds[jn][col];
-                v4f dcur[NK];
-#pragma unroll
-                for (int i = 0; i < NK; ++i) dcur[i] = mfma_fp8_16x16x128(a[i], bq, zero);
-#pragma unroll
-                for (int i = 0; i < NK; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
-#pragma unroll
-                for (int i = 0; i < NK; ++i) dprev[i] = dcur[i];
-                wprev = wj;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NK; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
+    // key row of tile i of a wave block (sampled positions in kModeSample; rows >= Tk are
+    // clamped into the array: they lie above the diagonal and are masked)
+    auto key_row = [&](int s_base, int i) {
+        return MODE == kModeSample ? sample_pos(min(s_base + 16 * i + col, n_keys - 1), o.S, n0, tt)
+                                   : min(s_base + 16 * i + col, Tk - 1);
+    };
+    // scale, causal mask and output of one wave block (keys s_base ..) from its head sums
+    auto finish = [&](const int s_base, float (&acc)[NK][4], const float (&ksl)[NK]) {
         // every lane takes part in the scale shuffles (no early exit for tokens past Tq),
         // and every path consumes the scale loads before the next block reuses them
 #pragma unroll
@@ -572,9 +569,9 @@ void index_fp8_resident_kernel(
                                                             (uint32_t)(s_base + 16 * i + 4 * grp + e));
                         ++off;
                     }
-            continue;
+            return;
         }
-        if (!t_ok) continue;
+        if (!t_ok) return;
         float* __restrict__ dst = MODE == kModeSample ? o.samples + (int64_t)tc * o.S : out_row;
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
@@ -586,6 +583,141 @@ void index_fp8_resident_kernel(
                     if (s0 + e < Tk) dst[s0 + e] = acc[i][e];
             }
         }
+    };
+
+    uint32_t redo = 0;            // wave blocks (bit kb - kb_begin) to recompute exactly
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+        const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;   // logical key index
+        if (s_base >= n_keys) break;
+        if (MODE != kModeSample && (int64_t)s_base > pos_hi) {   // wave tile above the diagonal
+            if (MODE == kModeScores && t_ok) {
+#pragma unroll
+                for (int i = 0; i < NK; ++i) {
+                    const int s0 = s_base + 16 * i + 4 * grp;
+                    if (s0 + 3 < Tk)
+                        *reinterpret_cast<float4*>(out_row + s0) =
+                            make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                    else
+                        for (int e = 0; e < 4; ++e)
+                            if (s0 + e < Tk) out_row[s0 + e] = -INFINITY;
+                }
+            }
+            continue;
+        }
+        // keys (A operands) of this wave, 16 NK keys, 32 bytes per lane per tile, and the
+        // scale of key 16 i + col: unconditional loads from rows clamped into the array
+        // (keys s >= Tk lie above the diagonal and are masked below), so no branch makes
+        // the compiler wait for them before it has to
+        v8i a[NK];
+        float ksl[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int s = key_row(s_base, i);
+            a[i] = load32B(k_idx + (int64_t)s * 128 + grp * 32);
+            ksl[i] = k_scale[s];
+        }
+        // all of the block's loads are in flight before any math: keep the compiler
+        // from sinking some of them below the first uses of the others
+        asm volatile("" ::: "memory");
+        // head loop, acc = sum_j w_j |x_j|: the B operand (q^I of head j for the 16 tokens)
+        // is read from LDS one head ahead, and the |x| epilogue of head j-1 follows the
+        // MFMAs of head j
+        float acc[NK][4];
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+        v4f dprev[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) dprev[i] = zero;
+        float wprev = 0.f;
+        const uint8_t* qbase = &q_lds[0][col][grp * 32];
+        v4i nlo = *reinterpret_cast<const v4i*>(qbase);
+        v4i nhi = *reinterpret_cast<const v4i*>(qbase + 16);
+        float nw = w_lds[0][col];
+        for (int j0 = 0; j0 < HP; j0 += 8) {
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                const int j = j0 + hh;
+                const v8i bq = {nlo.x, nlo.y, nlo.z, nlo.w, nhi.x, nhi.y, nhi.z, nhi.w};
+                const float wj = nw;
+                const int jn = (j + 1 < HP) ? j + 1 : j;
+                nlo = *reinterpret_cast<const v4i*>(qbase + jn * 16 * kQPitch);
+                nhi = *reinterpret_cast<const v4i*>(qbase + jn * 16 * kQPitch + 16);
+                nw = w_lds[jn][col];
+                v4f dcur[NK];
+#pragma unroll
+                for (int i = 0; i < NK; ++i) dcur[i] = mfma_fp8_16x16x128(a[i], bq, zero);
+#pragma unroll
+                for (int i = 0; i < NK; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
+#pragma unroll
+                for (int i = 0; i < NK; ++i) dprev[i] = dcur[i];
+                wprev = wj;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wprev, fabsf(dprev[i][e]), acc[i][e]);
+        // the linear term qmix . k (bf16 matrix core), one 32-wide slice m of the contraction
+        // at a time for every tile, then the cancellation guard
+        {
+            const uint16_t* qm = &qm_lds[col][grp * 32];
+            v4f lin[NK];
+#pragma unroll
+            for (int i = 0; i < NK; ++i) lin[i] = zero;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const v8bf bh = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 8 * m));
+                const v8bf bl = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qm + 128 + 8 * m));
+#pragma unroll
+                for (int i = 0; i < NK; ++i) {
+                    const v8bf ka = fp8x8_to_bf16(a[i], m);
+                    lin[i] = mfma_bf16_16x16x32(ka, bh, lin[i]);
+                    lin[i] = mfma_bf16_16x16x32(ka, bl, lin[i]);
+                }
+            }
+            float worst = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    worst = fmaxf(worst, cancel_metric(acc[i][e], lin[i][e]));
+                    acc[i][e] += lin[i][e];
+                }
+            if (__ballot(worst > 0.f) != 0) {          // uniform over the wave
+                redo |= 1u << (kb - kb_begin);
+                continue;
+            }
+        }
+        finish(s_base, acc, ksl);
+    }
+    // blocks the rewrite cannot be trusted for: the direct form on the bf16 matrix core, one
+    // key tile at a time, codes and scales loaded again (after the main loop, so that its
+    // registers are free)
+    while (redo != 0) {
+        const int kb = kb_begin + __builtin_ctz(redo);
+        redo &= redo - 1;
+        const int s_base = kb * kKeysPerBlock + wave * kKeysPerWave;
+        float acc[NK][4];
+        float ksl[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int s = key_row(s_base, i);
+            const v8i ki = load32B(k_idx + (int64_t)s * 128 + grp * 32);
+            ksl[i] = k_scale[s];
+            v8bf ka[1][4];
+            float ex[1][4] = {{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ka[0][m] = fp8x8_to_bf16(ki, m);
+            exact_heads<1>(ka, &q_lds[0][col][grp * 32], 16 * kQPitch, &w_lds[0][col], 16, 0, HP,
+                           ex);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = ex[0][e];
+        }
+        finish(s_base, acc, ksl);
     }
 }
 

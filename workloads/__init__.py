@@ -224,3 +224,31 @@ def packed_prefill_inputs(cfg: PrefillConfig, lens, device="cpu") -> dict:
 def scaled(cfg, **changes):
     """A copy of ``cfg`` with some fields replaced (smaller test variants)."""
     return dataclasses.replace(cfg, **changes)
+
+
+def relu_dominated_indexer_inputs(L: int, HI: int = 64, seed: int = 0, n_zero: int = 40,
+                                  device="cpu") -> dict:
+    """Indexer inputs whose dot products are mostly negative, so that ReLU zeroes most heads.
+
+    A shared direction u ~ N(0, I) is added to every query head (q^I[t, j] = u + N(0, I)) and
+    key s points against it by a seeded amount: k^I[s] = -lambda_s u / |u| + N(0, I) with
+    lambda_s ~ U(0, 5).  For a typical pair from about half to all of its head dot products
+    are negative, and about half of all pairs score exactly 0.  The first ``n_zero`` tokens
+    have element-wise positive queries and element-wise negative keys, so among them every
+    dot product is negative and every score is exactly 0; two of them have all-zero keys.
+    w ~ U(0, 1).  FP8 codes as for the other workloads."""
+    gen = lambda i: _gen(seed, 40 + i, device)
+    u = torch.randn(128, generator=gen(0), device=device)
+    qi = u + torch.randn(L, HI, 128, generator=gen(1), device=device)
+    lam = torch.rand(L, 1, generator=gen(2), device=device) * 5.0
+    ki = -lam * (u / u.norm()) + torch.randn(L, 128, generator=gen(3), device=device)
+    z = min(n_zero, L)
+    qi[:z] = torch.randn(z, HI, 128, generator=gen(4), device=device).abs()
+    ki[:z] = -torch.randn(z, 128, generator=gen(5), device=device).abs()
+    if z > 3:
+        ki[1] = 0.0
+        ki[z - 2] = 0.0
+    out = {"w": torch.rand(L, HI, generator=gen(6), device=device)}
+    out["q_idx"], out["q_scale"] = quantize_e4m3_per_token(qi)
+    out["k_idx"], out["k_scale"] = quantize_e4m3_per_token(ki)
+    return out
