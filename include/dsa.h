@@ -249,6 +249,29 @@ dsa_status_t dsa_decode(const void* q, const void* q_idx, const float* q_scale, 
                         hipStream_t stream);
 
 /*
+ * dsa_decode without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, checks and results are those of dsa_decode (the same kernels,
+ * bit for bit); the workspace is a scratch area the library keeps in device memory on
+ * every GPU it runs on, held until the process ends, of dsa_decode_noalloc_max_workspace()
+ * bytes (96 MiB; the 64-sequence step over 256K-token caches needs about 82 MiB).  A step
+ * whose dsa_decode_workspace_size() exceeds that fails with DSA_ERR_WORKSPACE and queues
+ * nothing.  The step runs on the current device (`stream` must belong to it) and allocates
+ * and frees nothing.  All calls on one GPU share its scratch: calls that overlap on one GPU
+ * (on other streams or from other host threads) race, and the caller must order them.  No
+ * result depends on what an earlier call left in the scratch.  The candidate-path counters
+ * of dsa_decode_stats_offset() are not available.
+ */
+size_t dsa_decode_noalloc_max_workspace(void);
+dsa_status_t dsa_decode_noalloc(const void* q, const void* q_idx, const float* q_scale,
+                                const float* w, const void* kidx_cache, const float* kidx_scale,
+                                const void* k_cache, const void* v_cache, dsa_dtype_t dtype,
+                                const int32_t* block_table, const int32_t* seq_lens, int B,
+                                int num_blocks, int max_blocks, int block_size, int Hq, int G,
+                                int d, int HI, int dI, int topk, float sm_scale, void* out,
+                                int32_t* idx_out, hipStream_t stream);
+
+/*
  * Per-token FP8 quantisation of indexer vectors (the FP8 inputs of report
  * section 2.3.1's indexer; the pages give no recipe, and this is the reading
  * every call above assumes): for each row t of x [T, n],

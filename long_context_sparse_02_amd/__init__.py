@@ -31,6 +31,7 @@ EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_gqa_attn_workspace_size",
            "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
            "dsa_prefill", "dsa_prefill_varlen", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
+           "dsa_decode_noalloc_max_workspace", "dsa_decode_noalloc",
            "dsa_quantize_e4m3", "dsa_cache_append", "dsa_index_scores_at",
            "dsa_index_scores_at_bwd_workspace_size", "dsa_index_scores_at_bwd", "dsa_sparse_gqa_attn_lse", "dsa_sparse_gqa_attn_bwd_workspace_size",
            "dsa_sparse_gqa_attn_bwd", "dsa_indexer_warmup_kl",
@@ -80,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_decode_stats_offset": ([I, I, I, I, I, I], SZ),
             "dsa_decode": ([P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, I, F, P, P,
                             P, SZ, P], I),
+            "dsa_decode_noalloc_max_workspace": ([], SZ),
+            "dsa_decode_noalloc": ([P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, I,
+                                    F, P, P, P], I),
             "dsa_quantize_e4m3": ([P, I, I, I, P, P, P], I),
             "dsa_cache_append": ([P, P, I, P, I, P, P, I, I, I, I, I, I, I, P, P, P, P, P], I),
             "dsa_index_scores_at": ([P, P, P, P, P, I, I, I, I, I, P, I, P, P], I),
@@ -211,6 +215,20 @@ def dsa_decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, d
         _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def dsa_decode_noalloc_max_workspace() -> int:
+    return load_library().dsa_decode_noalloc_max_workspace()
+
+
+def dsa_decode_noalloc(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, dtype,
+                       block_table, seq_lens, B, num_blocks, max_blocks, block_size, Hq, G, d, HI,
+                       dI, topk, sm_scale, out, idx_out, stream=None):
+    _check(load_library().dsa_decode_noalloc(
+        _ptr(q), _ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(kidx_cache), _ptr(kidx_scale),
+        _ptr(k_cache), _ptr(v_cache), dtype, _ptr(block_table), _ptr(seq_lens), B, num_blocks,
+        max_blocks, block_size, Hq, G, d, HI, dI, topk, float(sm_scale), _ptr(out), _ptr(idx_out),
+        _stream(stream)))
+
+
 # ------------------------------------------------------------ conveniences
 
 def workspace(nbytes: int, device="cuda"):
@@ -311,6 +329,23 @@ def decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, block
     if return_stats:
         res = res + (read_stats(ws, off),)
     return res if len(res) > 1 else res[0]
+
+
+def decode_noalloc(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, block_table,
+                   seq_lens, topk, sm_scale, return_idx=False, stream=None):
+    """dsa_decode_noalloc: one paged DSA decode step on the library's own per-GPU scratch
+    (no workspace argument); returns out (and idx if return_idx)."""
+    import torch
+    B, Hq, d = q.shape
+    _, HI, dI = q_idx.shape
+    NB, bs, G, _ = k_cache.shape
+    max_blocks = block_table.shape[1]
+    out = torch.empty_like(q)
+    idx = torch.empty(B, topk, dtype=torch.int32, device=q.device) if return_idx else None
+    dsa_decode_noalloc(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache,
+                       dtype_code(q), block_table, seq_lens, B, NB, max_blocks, bs, Hq, G, d, HI,
+                       dI, topk, sm_scale, out, idx, stream)
+    return (out, idx) if return_idx else out
 
 
 def dsa_quantize_e4m3(x, x_dtype, T, n, codes, scale, stream=None):

@@ -26,6 +26,18 @@ dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
     return st;
 }
 
+}  // namespace
+
+dsa_status_t dsa::api_fail(dsa_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+namespace {
+
 dsa_status_t hip_fail(hipError_t e, const char* what) {
     return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -527,14 +539,16 @@ DSA_EXPORT size_t dsa_decode_stats_offset(int B, int max_blocks, int block_size,
     return p.flag_bytes ? p.total - p.flag_bytes + sizeof(int) : (size_t)-1;
 }
 
-DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float* q_scale,
-                                   const float* w, const void* kidx_cache, const float* kidx_scale,
-                                   const void* k_cache, const void* v_cache, dsa_dtype_t dtype,
-                                   const int32_t* block_table, const int32_t* seq_lens, int B,
-                                   int num_blocks, int max_blocks, int block_size, int Hq, int G,
-                                   int d, int HI, int dI, int topk, float sm_scale, void* out,
-                                   int32_t* idx_out, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+// Every argument check of the decode step except the workspace's (shared with the
+// no-allocation entry point).
+dsa_status_t dsa::decode_check_args(const void* q, const void* q_idx, const float* q_scale,
+                                    const float* w, const void* kidx_cache,
+                                    const float* kidx_scale, const void* k_cache,
+                                    const void* v_cache, dsa_dtype_t dtype,
+                                    const int32_t* block_table, const int32_t* seq_lens, int B,
+                                    int num_blocks, int max_blocks, int block_size, int Hq, int G,
+                                    int d, int HI, int dI, int topk, void* out,
+                                    int32_t* idx_out) {
     g_err[0] = 0;
     REQUIRE(B >= 0 && num_blocks >= 0, DSA_ERR_INVALID_ARG, "negative size (B=%d, num_blocks=%d)", B, num_blocks);
     REQUIRE(max_blocks >= 1 && block_size >= 1, DSA_ERR_INVALID_ARG,
@@ -554,7 +568,22 @@ DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float
     REQUIRE_PTR(kidx_cache); REQUIRE_PTR4(kidx_scale); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
     REQUIRE_PTR4(block_table); REQUIRE_PTR4(seq_lens); REQUIRE_PTR(out);
     REQUIRE_OPT_PTR4(idx_out);
-    if (B == 0) return DSA_OK;
+    return DSA_OK;
+}
+
+DSA_EXPORT dsa_status_t dsa_decode(const void* q, const void* q_idx, const float* q_scale,
+                                   const float* w, const void* kidx_cache, const float* kidx_scale,
+                                   const void* k_cache, const void* v_cache, dsa_dtype_t dtype,
+                                   const int32_t* block_table, const int32_t* seq_lens, int B,
+                                   int num_blocks, int max_blocks, int block_size, int Hq, int G,
+                                   int d, int HI, int dI, int topk, float sm_scale, void* out,
+                                   int32_t* idx_out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    const dsa_status_t st = dsa::decode_check_args(q, q_idx, q_scale, w, kidx_cache, kidx_scale,
+                                                   k_cache, v_cache, dtype, block_table, seq_lens,
+                                                   B, num_blocks, max_blocks, block_size, Hq, G,
+                                                   d, HI, dI, topk, out, idx_out);
+    if (st != DSA_OK || B == 0) return st;
     const DecodePlan plan = plan_decode(B, max_blocks, block_size, topk, Hq, d);
     REQUIRE(ws && aligned16(ws) && ws_bytes >= plan.total, DSA_ERR_WORKSPACE,
             "decode needs %zu workspace bytes (got %zu%s)", plan.total, ws_bytes, ws ? "" : ", ws is NULL");

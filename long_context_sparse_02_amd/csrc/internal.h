@@ -5,7 +5,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/dsa.h"
+
 namespace dsa {
+
+// Records the detail of a failure for dsa_last_error() (per thread) and returns st.
+dsa_status_t api_fail(dsa_status_t st, const char* fmt, ...);
+// Every argument check of dsa_decode except the workspace's; DSA_OK when they pass.
+dsa_status_t decode_check_args(const void* q, const void* q_idx, const float* q_scale,
+                               const float* w, const void* kidx_cache, const float* kidx_scale,
+                               const void* k_cache, const void* v_cache, dsa_dtype_t dtype,
+                               const int32_t* block_table, const int32_t* seq_lens, int B,
+                               int num_blocks, int max_blocks, int block_size, int Hq, int G,
+                               int d, int HI, int dI, int topk, void* out, int32_t* idx_out);
+// Bytes of the per-GPU device scratch behind dsa_decode_noalloc (the 64-sequence decode
+// step over 256K-token caches needs about 82 MiB).
+constexpr size_t kNoAllocScratchBytes = (size_t)96 << 20;
 
 // Lightning indexer, contiguous keys (prefill).  Row i is position q_pos0 + i.
 // The FP8 kernel needs index_fp8_workspace_bytes(Tq) bytes of device scratch.

@@ -142,6 +142,34 @@ def test_prefill_and_decode_workspace_checks(lib):
     assert fd(*dargs) == 1                                      # seq_lens NULL
 
 
+def test_decode_noalloc_checks(lib):
+    """The no-allocation decode step: its scratch limit, and the checks it shares with
+    dsa_decode (all on the host, before any device call)."""
+    cap = lib.dsa_decode_noalloc_max_workspace()
+    assert cap == 96 << 20
+    # the 64-sequence step over 256K-token caches fits
+    assert lib.dsa_decode_workspace_size(64, 4096, 64, 2048, 32, 128) <= cap
+    f = lib.dsa_decode_noalloc
+    dargs = [A, A, A, A, A, A, A, A, dsa.DSA_BF16, A, A, 128, 1000, 4096, 64, 32, 4, 128, 64, 128,
+             2048, 0.1, A, None, None]
+    assert lib.dsa_decode_workspace_size(128, 4096, 64, 2048, 32, 128) > cap
+    assert f(*dargs) == 3                                       # beyond the scratch
+    assert b"dsa_decode_noalloc" in lib.dsa_last_error()
+    dargs[11] = 64
+    dargs[19] = 64
+    assert f(*dargs) == 2                                       # dI must be 128
+    dargs[19] = 128; dargs[14] = 16
+    assert f(*dargs) == 2                                       # 64-token blocks only
+    dargs[14] = 64; dargs[10] = None
+    assert f(*dargs) == 1                                       # seq_lens NULL
+    dargs[10] = A; dargs[22] = MIS
+    assert f(*dargs) == 1                                       # out misaligned
+    dargs[22] = A; dargs[11] = -1
+    assert f(*dargs) == 1                                       # negative batch
+    dargs[11] = 0
+    assert f(*dargs) == 0                                       # empty batch: nothing to do
+
+
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(4, 4)
