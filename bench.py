@@ -18,8 +18,9 @@ and its algorithmic rate (FP8 FLOPs for the indexer, bytes for top-k and the
 attention gather); the dominant kernel, the attention, which both paths run
 identically, is reported as ``roofline``.  Both paths must give identical
 index sets and outputs.  The CPU oracle, timed on a stratified sample of
-query rows, is reported as ``cpu_baseline``.  A packed batch of 16 sequences of 2K..14K tokens
-through dsa_prefill_varlen is reported under ``packed_prefill``, and one sparse-adaptation
+query rows, is reported as ``cpu_baseline``.  Packed batches through dsa_prefill_varlen (16
+sequences of 2K..14K tokens, 64 of 1K..4K, 256 of 512) are reported under ``packed_prefill``,
+and one sparse-adaptation
 training step of the 32K layer (indexer scores at the selected positions, attention forward
 with log-sum-exp, attention backward with the fused indexer loss, indexer backward) under
 ``train_step``.
@@ -326,12 +327,19 @@ def run_decode_bench(args, dsa, W, torch, name):
     return res
 
 
-def run_packed_bench(args, dsa, W, torch):
-    """Packed variable-length prefill: 16 sequences of 2K..14K tokens (seeded, clustered keys,
-    the 128K layer's shapes), one dsa_prefill_varlen call per step."""
-    cfg = W.scaled(W.PREFILL_128K, L=1, seed=1010)
-    lens = W.packed_lengths(16, 2048, 14336, cfg.seed)
-    log("generating packed batch", lens)
+PACKED = [  # (name, sequences, shortest, longest, seed)
+    ("prefill_packed_16x2k-14k", 16, 2048, 14336, 1010),
+    ("prefill_packed_64x1k-4k", 64, 1024, 4096, 1011),
+    ("prefill_packed_256x512", 256, 512, 512, 1012),
+]
+
+
+def run_packed_bench(args, dsa, W, torch, name, n_seq, lmin, lmax, seed):
+    """Packed variable-length prefill: n_seq sequences of lmin..lmax tokens (seeded, clustered
+    keys, the 128K layer's shapes), one dsa_prefill_varlen call per step."""
+    cfg = W.scaled(W.PREFILL_128K, L=1, seed=seed)
+    lens = W.packed_lengths(n_seq, lmin, lmax, cfg.seed)
+    log("generating packed batch", name)
     x = W.packed_prefill_inputs(cfg, lens, "cuda")
     cu = x["cu_seqlens"]
     T = cu[-1]
@@ -357,7 +365,7 @@ def run_packed_bench(args, dsa, W, torch):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    res = {"workload": "prefill_packed_16x2k-14k", "sequences": len(lens), "tokens": T,
+    res = {"workload": name, "sequences": len(lens), "tokens": T,
            "max_len": max_len, "ms_per_step": round(ms, 3),
            "tokens_per_s": round(T / (ms * 1e-3), 1)}
     del x, ws, out
@@ -597,7 +605,7 @@ def main():
     del x, idx, out
     torch.cuda.empty_cache()
     if not args.no_packed:
-        result["packed_prefill"] = run_packed_bench(args, dsa, W, torch)
+        result["packed_prefill"] = [run_packed_bench(args, dsa, W, torch, *p) for p in PACKED]
     if not args.no_train:
         result["train_step"] = run_train_bench(args, dsa, W, torch)
     if not args.no_warmup_stage:

@@ -109,7 +109,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
     if (p.n_kv <= 0) len = 0;                         // nothing can be gathered
     const int32_t* __restrict__ idx_row = p.idx + (int64_t)row * p.topk;
     const int k_begin = split * per_split;
-    const int k_end = len > 0 ? min(p.topk, k_begin + per_split) : k_begin;
+    // the row's entries stop at its last valid one (short rows keep t + 1 of them)
+    const int k_end = len > 0 ? min(row_extent(idx_row, p.topk, lane), k_begin + per_split) : k_begin;
     const float scale = p.sm_scale * kLog2e;
     const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
     uint16_t* vtile = &vt[wave][0][0];
@@ -263,7 +264,9 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
     a.block_table = nullptr; a.max_blocks = 0; a.block_size = 0; a.row_seq = nullptr;
     a.seq_lens = nullptr; a.bf16 = 1;
     const int64_t len = p.n_kv > 0 ? p.n_kv : 0;
-    const int k_end = len > 0 ? topk : 0;
+    // entries after the row's last valid one are padding: they add nothing to any gradient,
+    // so the walk stops there (their dI is written as 0 below all the same)
+    const int k_end = len > 0 ? row_extent(idx_row, topk, lane) : 0;
 
     // the indexer's softmax over the row's valid entries: its max and log normaliser
     float mI = 0.f, lnZ = 0.f;
@@ -697,7 +700,7 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs p, int ns
     if (p.n_kv <= 0) len = 0;
     const int32_t* __restrict__ idx_row = p.idx + (int64_t)row * p.topk;
     const int k_begin = split * per_split;
-    const int k_end = len > 0 ? min(p.topk, k_begin + per_split) : k_begin;
+    const int k_end = len > 0 ? min(row_extent(idx_row, p.topk, lane), k_begin + per_split) : k_begin;
     const float* __restrict__ Q = static_cast<const float*>(p.q);
     const float* __restrict__ K = static_cast<const float*>(p.k);
     const float* __restrict__ V = static_cast<const float*>(p.v);

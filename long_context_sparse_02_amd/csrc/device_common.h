@@ -52,6 +52,31 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One past the last entry >= 0 of an index row of n entries (0 when there is none).  The
+// entries after it are padding, so a kernel that stops there computes what one walking the
+// whole row would: short rows (a position t < k keeps only t + 1 entries) cost what they hold.
+// A row whose last entry is valid costs one load; others are scanned from the end, 2048
+// entries per round trip in coalesced, unconditional loads.  Every lane of the wave must call
+// it (the result is wave-uniform).
+__device__ __forceinline__ int row_extent(const int32_t* __restrict__ idx_row, int n, int lane) {
+    if (n <= 0) return 0;
+    if (idx_row[n - 1] >= 0) return n;
+    for (int hi = n - 1; hi > 0; hi -= 2048) {
+        const int lo = hi > 2048 ? hi - 2048 : 0;
+        int best = -1;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int e = lo + 64 * j + lane;
+            const int v = idx_row[min(e, hi - 1)];
+            if (e < hi && v >= 0) best = e;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o, 64));
+        if (best >= 0) return best + 1;
+    }
+    return 0;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;

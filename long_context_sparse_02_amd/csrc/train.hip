@@ -187,8 +187,19 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_kernel(
 #pragma unroll
     for (int j = 0; j < kIxHIMax; ++j) dqa[j] = 0.f;
     float dwa = 0.f;                            // dw[e] (e < HI) over this thread's positions
+    // the walk stops after the row's last valid entry (its padding adds nothing)
+    int k_end = 0;
+    {
+        __shared__ int ext;
+        if (tid < 64) {
+            const int x = row_extent(idx + t * topk, topk, tid);
+            if (tid == 0) ext = x;
+        }
+        __syncthreads();
+        k_end = ext;
+    }
 
-    for (int i0 = 0; i0 < topk; i0 += kIxBlock) {
+    for (int i0 = 0; i0 < k_end; i0 += kIxBlock) {
         {   // A: thread = position i0 + tid
             const int i = i0 + tid;
             const int s = i < topk ? idx[t * topk + i] : -1;
@@ -376,9 +387,12 @@ __global__ __launch_bounds__(kIxThreads) void index_at_bwd_mfma_kernel(
         stash(0, cb, sv, gv, kv);
     }
     __syncthreads();
+    // the walk stops after the row's last valid entry (its padding adds nothing; staged
+    // entries past it are never read by the reduction, which skips padding)
+    const int k_end = row_extent(idx + t * topk, topk, lane);
     int buf = 0;
-    for (int i0 = 0; i0 < topk; i0 += kBwdKeys, buf ^= 1) {
-        const bool more = i0 + kBwdKeys < topk;
+    for (int i0 = 0; i0 < k_end; i0 += kBwdKeys, buf ^= 1) {
+        const bool more = i0 + kBwdKeys < k_end;
         const int s_after = pos_at(i0 + 2 * kBwdKeys);   // past the end: clamped, unused
         v4i cb = {0, 0, 0, 0};
         float gv = 0.f, kv = 0.f;
