@@ -47,9 +47,10 @@ struct KVStep {
 // entry is padding, out of range, or maps to a block outside the cache.  Every
 // load here is unconditional (clamped to valid memory) so that the compiler keeps
 // the gather of the next step in flight instead of waiting at branch joins.
-template <bool PAGED>
+template <bool PAGED, bool PREFIX = false>
 __device__ __forceinline__ int resolve_row(const AttnArgs& p, const int32_t* __restrict__ idx_row,
-                                           int e, int k_end, int seq, int64_t len) {
+                                           int e, int k_end, int seq, int64_t len, int base = 0) {
+    if (PREFIX) return e < k_end ? base + e : -1;       // entry e is position e of the sequence
     const int s = idx_row[min(e, k_end - 1)];
     bool ok = e < k_end && s >= 0 && s < len;
     if (!PAGED) return ok ? s : -1;
@@ -59,12 +60,12 @@ __device__ __forceinline__ int resolve_row(const AttnArgs& p, const int32_t* __r
     return ok ? blk * p.block_size + sc % p.block_size : -1;
 }
 
-template <bool PAGED>
+template <bool PAGED, bool PREFIX = false>
 __device__ __forceinline__ void load_step(const AttnArgs& p, const int32_t* __restrict__ idx_row,
                                           int kb0, int k_end, int seq, int64_t len, int g,
-                                          int lane, KVStep& st) {
+                                          int lane, KVStep& st, int base = 0) {
     const int col = lane & 15, grp = lane >> 4;
-    const int prow = resolve_row<PAGED>(p, idx_row, kb0 + (lane & 31), k_end, seq, len);
+    const int prow = resolve_row<PAGED, PREFIX>(p, idx_row, kb0 + (lane & 31), k_end, seq, len, base);
     st.valid = (uint32_t)__ballot(prow >= 0);
     const int G = p.G;
     const uint16_t* __restrict__ K = static_cast<const uint16_t*>(p.k);
@@ -85,11 +86,25 @@ __device__ __forceinline__ void load_step(const AttnArgs& p, const int32_t* __re
     (void)col; (void)grp;
 }
 
-template <bool PAGED>
+struct NoPrefix {};
+
+// Sequence of packed row `row` in a prefix launch: the largest i with start[i] <= row.
+__device__ __forceinline__ int prefix_seq(const PrefixRows& r, int row) {
+    int lo = 0, hi = r.n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (r.start[mid] <= row) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <bool PAGED, typename RowMap = NoPrefix>
 __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, int nsplit,
                                                                   int per_split,
-                                                                  float* __restrict__ partials)
+                                                                  float* __restrict__ partials,
+                                                                  RowMap rmap = RowMap{})
 {
+    constexpr bool PREFIX = !__is_same(RowMap, NoPrefix);
     __shared__ __attribute__((aligned(16))) uint16_t vt[kAttnWaves][kStep][kVPitch];
     __shared__ __attribute__((aligned(16))) uint16_t kt[kAttnWaves][kStep][kVPitch];
     const int work = xcd_remap(blockIdx.x, gridDim.x);
@@ -107,10 +122,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
         if (len > cap) len = 0;
     }
     if (p.n_kv <= 0) len = 0;                         // nothing can be gathered
-    const int32_t* __restrict__ idx_row = p.idx + (int64_t)row * p.topk;
+    const int32_t* __restrict__ idx_row = PREFIX ? nullptr : p.idx + (int64_t)row * p.topk;
     const int k_begin = split * per_split;
-    // the row's entries stop at its last valid one (short rows keep t + 1 of them)
-    const int k_end = len > 0 ? min(row_extent(idx_row, p.topk, lane), k_begin + per_split) : k_begin;
+    // the row's entries stop at its last valid one (short rows keep t + 1 of them); in a
+    // prefix launch the row's entries are the positions 0 .. t of its sequence
+    int base = 0, n_row;
+    if constexpr (PREFIX) {
+        base = rmap.start[prefix_seq(rmap, row)];
+        n_row = row - base + 1;
+    } else {
+        n_row = len > 0 ? row_extent(idx_row, p.topk, lane) : 0;
+    }
+    const int k_end = len > 0 ? min(n_row, k_begin + per_split) : k_begin;
     const float scale = p.sm_scale * kLog2e;
     const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
     uint16_t* vtile = &vt[wave][0][0];
@@ -131,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
         for (int dt = 0; dt < 8; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
         KVStep cur, nxt;
-        if (k_begin < k_end) load_step<PAGED>(p, idx_row, k_begin, k_end, seq, len, g, lane, cur);
+        if (k_begin < k_end) load_step<PAGED, PREFIX>(p, idx_row, k_begin, k_end, seq, len, g, lane, cur, base);
         for (int kb0 = k_begin; kb0 < k_end; kb0 += kStep) {
             // K and V rows of this step into the wave's LDS tiles
 #pragma unroll
@@ -142,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
             }
             const uint32_t valid = cur.valid;
             if (kb0 + kStep < k_end)
-                load_step<PAGED>(p, idx_row, kb0 + kStep, k_end, seq, len, g, lane, nxt);
+                load_step<PAGED, PREFIX>(p, idx_row, kb0 + kStep, k_end, seq, len, g, lane, nxt, base);
 
             // S^T (positions x heads) for the two 16-position tiles; MFMA m takes head dims
             // 8 (4 m + grp) .. +8 from lane group grp, the same slots as the q operand
@@ -856,6 +879,18 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int nsplit, float* partials, hi
     if (err != hipSuccess || nsplit == 1) return err;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Tq * a.Hq)), dim3(128), 0, stream, partials,
                        nsplit, a.Hq, a.bf16, a.out, a.lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_prefix(const AttnArgs& a, const PrefixRows& rows,
+                                     hipStream_t stream)
+{
+    if (a.Tq == 0) return hipSuccess;
+    if (!a.bf16 || a.block_table || rows.n < 1 || rows.n > kMaxPrefixSeqs ||
+        rows.start[rows.n] != a.Tq)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((sparse_attn_bf16_kernel<false, PrefixRows>), dim3((unsigned)a.Tq),
+                       dim3(256), 0, stream, a, 1, a.topk, nullptr, rows);
     return hipGetLastError();
 }
 

@@ -470,10 +470,51 @@ DSA_EXPORT dsa_status_t dsa_prefill_varlen(const void* q, const void* k, const v
     const size_t kvrow = (size_t)G * d * (dtype == DSA_BF16 ? 2 : 4);
     const size_t qirow = (size_t)HI * dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
     const size_t kirow = (size_t)dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
+    // Runs of consecutive sequences of at most topk tokens (bf16): every row keeps its whole
+    // prefix, so no score is needed, and up to kMaxPrefixSeqs of them share one attention
+    // launch (and one launch writing their index lists); rows and results are those of the
+    // per-sequence driver.  Longer sequences take the chunk driver one by one.
+    const bool batch_short = dtype == DSA_BF16;
+    int run0 = -1;                                  // first sequence of the open run
+    auto flush = [&](int i1) -> dsa_status_t {
+        const int i0 = run0;
+        run0 = -1;
+        const int64_t R0 = cu_seqlens[i0];
+        const int rows = cu_seqlens[i1] - cu_seqlens[i0];
+        if (rows == 0) return DSA_OK;
+        dsa::PrefixRows pr;
+        pr.n = i1 - i0;
+        for (int j = 0; j <= pr.n; ++j) pr.start[j] = cu_seqlens[i0 + j] - (int)R0;
+        hipError_t e = hipSuccess;
+        if (idx_out) e = dsa::launch_prefix_idx(pr, topk, idx_out + R0 * topk, stream);
+        if (e != hipSuccess) return hip_fail(e, "short-sequence index launch");
+        dsa::AttnArgs a;
+        a.q = static_cast<const char*>(q) + R0 * qrow;
+        a.k = static_cast<const char*>(k) + R0 * kvrow;
+        a.v = static_cast<const char*>(v) + R0 * kvrow;
+        a.out = static_cast<char*>(out) + R0 * qrow;
+        a.idx = nullptr; a.Tq = rows; a.topk = topk; a.Hq = Hq; a.G = G; a.d = d;
+        a.sm_scale = sm_scale; a.n_kv = rows; a.block_table = nullptr; a.max_blocks = 0;
+        a.block_size = 0; a.row_seq = nullptr; a.seq_lens = nullptr; a.bf16 = 1;
+        e = dsa::launch_sparse_attn_prefix(a, pr, stream);
+        return e == hipSuccess ? DSA_OK : hip_fail(e, "short-sequence attention launch");
+    };
     bool first_cand = true;
     for (int i = 0; i < nseq; ++i) {
         const int64_t s0 = cu_seqlens[i];
         const int len = cu_seqlens[i + 1] - cu_seqlens[i];
+        if (batch_short && len <= topk) {
+            if (run0 < 0) run0 = i;
+            if (i + 1 - run0 == dsa::kMaxPrefixSeqs) {
+                st = flush(i + 1);
+                if (st != DSA_OK) return st;
+            }
+            continue;
+        }
+        if (run0 >= 0) {
+            st = flush(i);
+            if (st != DSA_OK) return st;
+        }
         if (len == 0) continue;
         const PrefillArgs a{static_cast<const char*>(q) + s0 * qrow,
                             static_cast<const char*>(k) + s0 * kvrow,
@@ -487,6 +528,7 @@ DSA_EXPORT dsa_status_t dsa_prefill_varlen(const void* q, const void* k, const v
         st = run_prefill(a, len, 0, b, first_cand, stream);
         if (st != DSA_OK) return st;
     }
+    if (run0 >= 0) return flush(nseq);
     return DSA_OK;
 }
 

@@ -141,6 +141,23 @@ int attn_num_splits(int Tq, int topk);
 size_t attn_partials_bytes(int Tq, int nsplit, int Hq, int d);
 hipError_t launch_sparse_attn(const AttnArgs& a, int nsplit, float* partials, hipStream_t stream);
 
+// Many short sequences packed back to back in one launch, every row keeping its whole causal
+// prefix (a row at position t < k selects {0 .. t}): start[i] is the first row of sequence i
+// relative to the launch's first row, start[n] the launch's row count.  Passed by value as a
+// kernel argument, so one launch takes at most kMaxPrefixSeqs sequences.
+constexpr int kMaxPrefixSeqs = 256;
+struct PrefixRows {
+    int n;
+    int start[kMaxPrefixSeqs + 1];
+};
+// bf16 attention of such a launch (a.idx unused; a.q, a.k, a.v, a.out start at the launch's
+// first row, a.Tq = a.n_kv = start[n]); the same arithmetic as a full-row launch over the
+// index lists {0 .. t}.
+hipError_t launch_sparse_attn_prefix(const AttnArgs& a, const PrefixRows& rows,
+                                     hipStream_t stream);
+// The index lists of such a launch: idx[r, e] = e for e <= t, -1 after (rows start[n] x topk).
+hipError_t launch_prefix_idx(const PrefixRows& rows, int topk, int32_t* idx, hipStream_t stream);
+
 // Per-token E4M3 quantisation of x [T, n] (fp32, or bf16 when x_bf16): codes [T, n], scale [T].
 hipError_t launch_quantize_e4m3(const void* x, int x_bf16, int T, int n, uint8_t* codes,
                                 float* scale, hipStream_t stream);

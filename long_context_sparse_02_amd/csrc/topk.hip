@@ -652,6 +652,35 @@ int fused_sample_count(int Tk)
     return S > kCandCap ? -1 : S;                    // -1: too long for the candidate path
 }
 
+namespace {
+
+// Index lists of packed short sequences whose rows keep their whole prefix: row r at position
+// t of its sequence gets 0 .. t, then -1.  One workgroup per row, 16-byte stores.
+__global__ __launch_bounds__(256) void prefix_idx_kernel(PrefixRows rows, int topk,
+                                                         int32_t* __restrict__ idx)
+{
+    const int r = blockIdx.x;
+    int lo = 0, hi = rows.n - 1;                     // the row's sequence: largest start <= r
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (rows.start[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    const int t = r - rows.start[lo];
+    int32_t* __restrict__ out = idx + (int64_t)r * topk;
+    for (int e = threadIdx.x; e < topk; e += 256) out[e] = e <= t ? e : -1;
+}
+
+}  // namespace
+
+hipError_t launch_prefix_idx(const PrefixRows& rows, int topk, int32_t* idx, hipStream_t stream)
+{
+    if (rows.n < 1 || rows.n > kMaxPrefixSeqs) return hipErrorInvalidValue;
+    const int T = rows.start[rows.n];
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(prefix_idx_kernel, dim3((unsigned)T), dim3(256), 0, stream, rows, topk, idx);
+    return hipGetLastError();
+}
+
 hipError_t launch_topk_bound(const float* samples, int S, int Tq, int64_t q_pos0,
                              const int32_t* row_len, int max_len, int k, float* tau, int32_t* cnt,
                              int* fallback, int first, hipStream_t stream)

@@ -814,6 +814,24 @@ def test_prefill_varlen_equals_separate_calls(chunk):
     _varlen_vs_separate(cfg, lens, chunk, "varlen chunk=%d" % chunk)
 
 
+def test_prefill_varlen_many_short_sequences():
+    """More short sequences than one shared launch takes (runs of at most 256 sequences of
+    <= k tokens attend to their whole prefix together), with a long sequence and empty ones
+    in between: every sequence bitwise its own prefill, with and without index output."""
+    cfg = W.scaled(W.PREFILL_32K, L=1, k=512, seed=315)
+    rng = np.random.default_rng(315)
+    lens = [int(n) for n in rng.integers(0, 600, 300)]
+    lens[150] = 3000
+    lens[10] = 0
+    lens[299] = 512
+    x, out, idx = _varlen_vs_separate(cfg, lens, 1024, "varlen 300 short")
+    out2 = dsa.prefill_varlen(x["q"], x["k"], x["v"], x["q_idx"], x["q_scale"], x["w"],
+                              x["k_idx"], x["k_scale"], x["cu_seqlens"], cfg.k, cfg.sm_scale,
+                              chunk_rows=1024)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
 def test_prefill_varlen_vs_oracle():
     """A small packed batch checked row by row against the oracle, each sequence on its own."""
     cfg = W.scaled(W.PREFILL_32K, L=1, k=256, seed=320)
