@@ -17,7 +17,8 @@ stream around every launch: ``kernels`` gives each kernel's average duration
 and its algorithmic rate (FP8 FLOPs for the indexer, bytes for top-k and the
 attention gather); the dominant kernel, the attention, which both paths run
 identically, is reported as ``roofline``.  Both paths must give identical
-index sets and outputs.  The CPU oracle, timed on a stratified sample of
+index sets, and identical outputs outside the 16-row blocks of whole-prefix rows (which the
+one-call path sends to the deduplicated attention; ``fused_vs_staged``).  The CPU oracle, timed on a stratified sample of
 query rows, is reported as ``cpu_baseline``.  Packed batches through dsa_prefill_varlen (16
 sequences of 2K..14K tokens, 64 of 1K..4K, 256 of 512) are reported under ``packed_prefill``,
 and one sparse-adaptation
@@ -198,7 +199,13 @@ def run_prefill_bench(args, dsa, W, torch):
                         cfg.HI, cfg.dI, k, cfg.sm_scale, C, out2, idx2, ws, ws.numel(), stream)
     torch.cuda.synchronize()
     fused_ms = (time.perf_counter() - t1) / args.steps * 1e3
-    same = bool(torch.equal(out, out2)) and bool(torch.equal(idx, idx2))
+    # rows in 16-row blocks of whole prefixes take the deduplicated attention in dsa_prefill (the
+    # same terms, other rounding); everything else must be bitwise the staged path's
+    lim = L if L <= k else (k // 16) * 16
+    same = {"idx_equal": bool(torch.equal(idx, idx2)),
+            "out_equal_beyond_prefix_blocks": bool(torch.equal(out[lim:], out2[lim:])),
+            "prefix_block_rows": lim,
+            "prefix_block_max_abs_diff": float((out[:lim].float() - out2[:lim].float()).abs().max())}
     del ws
     return cfg, x, idx, out, ms_step, kern, fused_ms, same
 
@@ -599,7 +606,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": kern,
-        "staged_ms_per_step": round(ms_step, 3), "fused_equals_staged": same,
+        "staged_ms_per_step": round(ms_step, 3), "fused_vs_staged": same,
         "adjacent16_union": round(adjacent_union(idx, cfg.L, cfg.k), 1),
     }
     del x, idx, out

@@ -141,6 +141,33 @@ dsa_status_t dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, ds
                                  hipStream_t stream);
 
 /*
+ * GQA sparse attention with adjacent-query Top-KV deduplication (report section
+ * 5.3, sparse attention optimisation: adjacent queries select largely the same
+ * keys).  The rows are grouped in blocks of 16 by absolute position (row i is
+ * at position q_pos0 + i; a block holds positions 16 B .. 16 B + 15).  For each
+ * block the union of its rows' Omega is formed with a 16-bit mask per union
+ * position (which rows selected it); a marked block gathers each union
+ * position's K/V rows once and computes all its rows over the union, masking
+ * in the matrix products' accumulator layout the positions a row did not
+ * select.  The result is out as dsa_sparse_gqa_attn computes it for contiguous
+ * bf16 K/V (the same terms in the same order), up to the rounding of the
+ * online softmax's steps.  mode 0 marks a block when 2 x (union size) is below
+ * its number of selected entries (the measured cost of a union position, which
+ * every row of the block computes, against a selected entry of the per-query
+ * kernel); the other blocks run the per-query kernel.  mode 1 marks every
+ * block.  dsa_prefill makes the same mode-0 choice for every chunk.
+ * q, k, v, out, idx, n_kv: as dsa_sparse_gqa_attn with DSA_BF16, contiguous
+ * K/V, Hq == 8 G, d == 128, topk <= 2048, n_kv <= 262144; a row's entries
+ * must be distinct (as top-k produces them).  Workspace:
+ * dsa_sparse_gqa_attn_dedup_workspace_size() bytes.
+ */
+size_t dsa_sparse_gqa_attn_dedup_workspace_size(int Tq, int64_t q_pos0, int topk);
+dsa_status_t dsa_sparse_gqa_attn_dedup(const void* q, const void* k, const void* v, int n_kv,
+                                       const int32_t* idx, int Tq, int64_t q_pos0, int topk,
+                                       int Hq, int G, int d, float sm_scale, int mode, void* out,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Fused prefill of one sequence: indexer -> top-k -> sparse attention for the
  * Tq queries at positions q_pos0 .. q_pos0 + Tq - 1 over the Tk = q_pos0 + Tq
  * keys (report sections 2.3.1-2.3.2).  Queries are processed in chunks of

@@ -29,7 +29,8 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "D
 EXPORTS = ["dsa_status_string", "dsa_last_error", "dsa_version",
            "dsa_index_scores_workspace_size", "dsa_index_scores",
            "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_gqa_attn_workspace_size",
-           "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
+           "dsa_sparse_gqa_attn", "dsa_sparse_gqa_attn_dedup_workspace_size",
+           "dsa_sparse_gqa_attn_dedup", "dsa_prefill_workspace_size", "dsa_prefill_stats_offset",
            "dsa_prefill", "dsa_prefill_varlen", "dsa_decode_workspace_size", "dsa_decode_stats_offset", "dsa_decode",
            "dsa_decode_noalloc_max_workspace", "dsa_decode_noalloc",
            "dsa_quantize_e4m3", "dsa_cache_append", "dsa_index_scores_at",
@@ -71,6 +72,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "dsa_topk": ([P, I64, I, I, I64, I, P, P, SZ, P], I),
             "dsa_sparse_gqa_attn_workspace_size": ([I, I, I, I], SZ),
             "dsa_sparse_gqa_attn": ([P, P, P, I, I, P, I, I, P, P, P, I, I, I, I, I, F, P, P, SZ, P], I),
+            "dsa_sparse_gqa_attn_dedup_workspace_size": ([I, I64, I], SZ),
+            "dsa_sparse_gqa_attn_dedup": ([P, P, P, I, P, I, I64, I, I, I, I, F, I, P, P, SZ, P],
+                                          I),
             "dsa_prefill_workspace_size": ([I, I64, I, I], SZ),
             "dsa_prefill_stats_offset": ([I, I64, I, I], SZ),
             "dsa_prefill": ([P, P, P, I, P, P, P, P, P, I, I, I64, I, I, I, I, I, I, F, I, P, P, P,
@@ -197,12 +201,12 @@ def dsa_decode_stats_offset(B, max_blocks, block_size, topk, Hq, d) -> int:
     return load_library().dsa_decode_stats_offset(B, max_blocks, block_size, topk, Hq, d)
 
 
-def read_stats(ws, offset):
+def read_stats(ws, offset, n=2):
     """The two candidate-path counters (chunks on the path, rows redone) of a workspace."""
     import torch
     if offset < 0 or offset >= (1 << 63):
         return None
-    return ws.view(torch.uint8)[offset:offset + 8].view(torch.int32).tolist()
+    return ws.view(torch.uint8)[offset:offset + 4 * n].view(torch.int32).tolist()
 
 
 def dsa_decode(q, q_idx, q_scale, w, kidx_cache, kidx_scale, k_cache, v_cache, dtype, block_table,
@@ -275,9 +279,33 @@ def sparse_gqa_attn(q, k, v, idx, G, sm_scale, block_table=None, block_size=0, r
     return out
 
 
-def _zero_stats(ws, off):
+def _zero_stats(ws, off, n=2):
     if 0 <= off < (1 << 63):
-        ws.view(__import__("torch").uint8)[off:off + 8].zero_()
+        ws.view(__import__("torch").uint8)[off:off + 4 * n].zero_()
+
+
+def dsa_sparse_gqa_attn_dedup_workspace_size(Tq, q_pos0, topk) -> int:
+    return load_library().dsa_sparse_gqa_attn_dedup_workspace_size(Tq, q_pos0, topk)
+
+
+def dsa_sparse_gqa_attn_dedup(q, k, v, n_kv, idx, Tq, q_pos0, topk, Hq, G, d, sm_scale, mode, out,
+                              ws, ws_bytes, stream=None):
+    _check(load_library().dsa_sparse_gqa_attn_dedup(
+        _ptr(q), _ptr(k), _ptr(v), n_kv, _ptr(idx), Tq, q_pos0, topk, Hq, G, d, float(sm_scale),
+        mode, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def sparse_gqa_attn_dedup(q, k, v, idx, G, sm_scale, q_pos0=0, mode=0, stream=None):
+    """Attention with adjacent-query deduplication (bf16, contiguous K/V); returns out."""
+    import torch
+    Tq, Hq, d = q.shape
+    topk = idx.shape[1]
+    out = torch.empty_like(q)
+    n = dsa_sparse_gqa_attn_dedup_workspace_size(Tq, q_pos0, topk)
+    ws = workspace(max(n, 256), q.device)
+    dsa_sparse_gqa_attn_dedup(q, k, v, k.shape[0], idx, Tq, q_pos0, topk, Hq, G, d, sm_scale, mode,
+                              out, ws, ws.numel(), stream)
+    return out
 
 
 def prefill(q, k, v, q_idx, q_scale, w, k_idx, k_scale, topk, sm_scale, chunk_rows=0, q_pos0=0,

@@ -27,7 +27,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-fno-strict-alia
 # vector-ALU work of its inner loop.  Indexer inputs are finite FP8 values.
 EXTRA = {"indexer.hip": ["-fno-honor-nans"]}
 SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "cache.hip", "train.hip", "warmup.hip",
-           "noalloc.hip", "dsa_api.cpp"]
+           "dedup.hip", "noalloc.hip", "dsa_api.cpp"]
 
 
 def _hipcc() -> str:

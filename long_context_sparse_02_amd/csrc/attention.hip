@@ -47,10 +47,9 @@ struct KVStep {
 // entry is padding, out of range, or maps to a block outside the cache.  Every
 // load here is unconditional (clamped to valid memory) so that the compiler keeps
 // the gather of the next step in flight instead of waiting at branch joins.
-template <bool PAGED, bool PREFIX = false>
+template <bool PAGED>
 __device__ __forceinline__ int resolve_row(const AttnArgs& p, const int32_t* __restrict__ idx_row,
-                                           int e, int k_end, int seq, int64_t len, int base = 0) {
-    if (PREFIX) return e < k_end ? base + e : -1;       // entry e is position e of the sequence
+                                           int e, int k_end, int seq, int64_t len) {
     const int s = idx_row[min(e, k_end - 1)];
     bool ok = e < k_end && s >= 0 && s < len;
     if (!PAGED) return ok ? s : -1;
@@ -60,12 +59,12 @@ __device__ __forceinline__ int resolve_row(const AttnArgs& p, const int32_t* __r
     return ok ? blk * p.block_size + sc % p.block_size : -1;
 }
 
-template <bool PAGED, bool PREFIX = false>
+template <bool PAGED>
 __device__ __forceinline__ void load_step(const AttnArgs& p, const int32_t* __restrict__ idx_row,
                                           int kb0, int k_end, int seq, int64_t len, int g,
-                                          int lane, KVStep& st, int base = 0) {
+                                          int lane, KVStep& st) {
     const int col = lane & 15, grp = lane >> 4;
-    const int prow = resolve_row<PAGED, PREFIX>(p, idx_row, kb0 + (lane & 31), k_end, seq, len, base);
+    const int prow = resolve_row<PAGED>(p, idx_row, kb0 + (lane & 31), k_end, seq, len);
     st.valid = (uint32_t)__ballot(prow >= 0);
     const int G = p.G;
     const uint16_t* __restrict__ K = static_cast<const uint16_t*>(p.k);
@@ -86,32 +85,26 @@ __device__ __forceinline__ void load_step(const AttnArgs& p, const int32_t* __re
     (void)col; (void)grp;
 }
 
-struct NoPrefix {};
-
-// Sequence of packed row `row` in a prefix launch: the largest i with start[i] <= row.
-__device__ __forceinline__ int prefix_seq(const PrefixRows& r, int row) {
-    int lo = 0, hi = r.n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (r.start[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-template <bool PAGED, typename RowMap = NoPrefix>
+template <bool PAGED>
 __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, int nsplit,
                                                                   int per_split,
-                                                                  float* __restrict__ partials,
-                                                                  RowMap rmap = RowMap{})
+                                                                  float* __restrict__ partials)
 {
-    constexpr bool PREFIX = !__is_same(RowMap, NoPrefix);
     __shared__ __attribute__((aligned(16))) uint16_t vt[kAttnWaves][kStep][kVPitch];
     __shared__ __attribute__((aligned(16))) uint16_t kt[kAttnWaves][kStep][kVPitch];
-    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    // rows in groups of 16 dealt round-robin to the XCDs: adjacent rows share an L2, and rows
+    // of uneven cost (short rows first) spread evenly (a contiguous share per XCD left the XCDs
+    // holding short rows idle: 64 packed sequences of 1K..4K tokens 61.7 -> 31.9 ms)
+    const int work = xcd_interleave16(blockIdx.x, gridDim.x);
     const int row = work / nsplit, split = work - row * nsplit;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int hpg = p.Hq / p.G;
+    // rows the deduplicated attention computes: positions below prefix_skip (blocks of whole
+    // prefixes), or blocks the union kernel marked (uniform over the workgroup)
+    if (!PAGED && p.pos0 + row < p.prefix_skip) return;
+    if (!PAGED && p.dedup_info && p.dedup_info[3 * ((p.pos0 % kDedupRows + row) / kDedupRows) + 2])
+        return;
 
     int seq = 0;
     int64_t len = p.n_kv;
@@ -122,18 +115,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
         if (len > cap) len = 0;
     }
     if (p.n_kv <= 0) len = 0;                         // nothing can be gathered
-    const int32_t* __restrict__ idx_row = PREFIX ? nullptr : p.idx + (int64_t)row * p.topk;
+    const int32_t* __restrict__ idx_row = p.idx + (int64_t)row * p.topk;
     const int k_begin = split * per_split;
-    // the row's entries stop at its last valid one (short rows keep t + 1 of them); in a
-    // prefix launch the row's entries are the positions 0 .. t of its sequence
-    int base = 0, n_row;
-    if constexpr (PREFIX) {
-        base = rmap.start[prefix_seq(rmap, row)];
-        n_row = row - base + 1;
-    } else {
-        n_row = len > 0 ? row_extent(idx_row, p.topk, lane) : 0;
-    }
-    const int k_end = len > 0 ? min(n_row, k_begin + per_split) : k_begin;
+    // the row's entries stop at its last valid one (short rows keep t + 1 of them)
+    const int k_end = len > 0 ? min(row_extent(idx_row, p.topk, lane), k_begin + per_split) : k_begin;
     const float scale = p.sm_scale * kLog2e;
     const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
     uint16_t* vtile = &vt[wave][0][0];
@@ -154,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
         for (int dt = 0; dt < 8; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
         KVStep cur, nxt;
-        if (k_begin < k_end) load_step<PAGED, PREFIX>(p, idx_row, k_begin, k_end, seq, len, g, lane, cur, base);
+        if (k_begin < k_end) load_step<PAGED>(p, idx_row, k_begin, k_end, seq, len, g, lane, cur);
         for (int kb0 = k_begin; kb0 < k_end; kb0 += kStep) {
             // K and V rows of this step into the wave's LDS tiles
 #pragma unroll
@@ -165,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_bf16_kernel(AttnArgs p, in
             }
             const uint32_t valid = cur.valid;
             if (kb0 + kStep < k_end)
-                load_step<PAGED, PREFIX>(p, idx_row, kb0 + kStep, k_end, seq, len, g, lane, nxt, base);
+                load_step<PAGED>(p, idx_row, kb0 + kStep, k_end, seq, len, g, lane, nxt);
 
             // S^T (positions x heads) for the two 16-position tiles; MFMA m takes head dims
             // 8 (4 m + grp) .. +8 from lane group grp, the same slots as the q operand
@@ -270,7 +255,7 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(AttnBwdArgs p)
     __shared__ __attribute__((aligned(16))) uint16_t pst[kAttnWaves][2][kStep][16];
     __shared__ float psum[kAttnWaves][kBwdMaxTopk];   // per wave: sum over its groups of p
     __shared__ float red[kAttnWaves];
-    const int row = p.r0 + xcd_remap(blockIdx.x, gridDim.x);
+    const int row = p.r0 + xcd_interleave16(blockIdx.x, gridDim.x);   // as the forward
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int hpg = p.Hq / p.G;
@@ -882,15 +867,11 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int nsplit, float* partials, hi
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn_prefix(const AttnArgs& a, const PrefixRows& rows,
-                                     hipStream_t stream)
+hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t stream)
 {
-    if (a.Tq == 0) return hipSuccess;
-    if (!a.bf16 || a.block_table || rows.n < 1 || rows.n > kMaxPrefixSeqs ||
-        rows.start[rows.n] != a.Tq)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL((sparse_attn_bf16_kernel<false, PrefixRows>), dim3((unsigned)a.Tq),
-                       dim3(256), 0, stream, a, 1, a.topk, nullptr, rows);
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
     return hipGetLastError();
 }
 

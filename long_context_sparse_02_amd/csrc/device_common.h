@@ -45,6 +45,17 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return x * q + (x < r ? x : r) + slot;
 }
 
+// Workgroup id remapped so that groups of 16 consecutive work items run on one XCD and the
+// groups are dealt round-robin to the 8 XCDs: neighbouring items still share an XCD's L2, and
+// work whose cost varies along the items (short rows first) is spread evenly over the XCDs.
+// A bijection on [0, n): items past the last whole 128 keep their own id.
+__device__ __forceinline__ int xcd_interleave16(int b, int n) {
+    const int n_full = n & ~127;
+    if (b >= n_full) return b;
+    const int x = b & 7, k = b >> 3;
+    return ((((k >> 4) << 3) + x) << 4) + (k & 15);
+}
+
 // Larger float -> larger unsigned key; -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);

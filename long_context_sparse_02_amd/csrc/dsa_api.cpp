@@ -259,6 +259,13 @@ struct PrefillPlan {
     size_t samples_bytes, tau_bytes, cnt_bytes, cand_bytes, flag_bytes, total;
 };
 
+// Relative cost of one union position of a 16-row block (gathered once, computed for all 16
+// queries) against one selected (row, position) entry of the per-query attention, measured on
+// gfx950 (8K-row chunks of the 128K layer): the union kernels break even with the per-query
+// kernel at a union of about 28% of the selections.  A block takes the deduplicated attention
+// when kDedupKappa * union < selections.
+constexpr float kDedupKappa = 3.5f;
+
 // The workspace holds one chunk's scores, its index sets and the indexer's scratch (sized for
 // FP8, the larger of the two indexer paths), plus the candidate pipeline's buffers: samples,
 // per-row bounds and counters, candidate lists and the fallback flag.  A chunk's sample count
@@ -379,15 +386,99 @@ dsa_status_t run_prefill(const PrefillArgs& a, int Tq, int64_t q_pos0, const Pre
             e = dsa::launch_topk(b.scores, ld, rows, tk, pos0, nullptr, topk, idx_c, nullptr, stream);
             if (e != hipSuccess) return hip_fail(e, "top-k launch");
         }
-        st = run_attn(static_cast<const char*>(a.q) + r0 * qrow, a.k, a.v, a.dtype, tk, nullptr, 0,
-                      0, nullptr, nullptr, idx_c, rows, topk, a.Hq, a.G, a.d, a.sm_scale,
-                      static_cast<char*>(a.out) + r0 * qrow, nullptr, 0, stream);
+        // Rows in 16-row blocks of whole prefixes (every row of the block keeps all of its
+        // t + 1 positions) take the deduplicated attention: the block's union is its prefix
+        // and needs no union kernel.  The union attention wins clearly only there: on the
+        // workloads measured, other blocks' shared rows already hit in L2 for the per-query
+        // kernel (dsa_sparse_gqa_attn_dedup offers the union for any selection).
+        const void* q_c = static_cast<const char*>(a.q) + r0 * qrow;
+        void* out_c = static_cast<char*>(a.out) + r0 * qrow;
+        const int64_t lim = dsa::prefix_block_limit(q_pos0 + Tq, topk);
+        const bool dedup = a.dtype == DSA_BF16 && a.Hq == 8 * a.G && a.d == 128 && pos0 < lim;
+        if (dedup) {
+            dsa::PrefixBlocks pb;
+            pb.n = 1;
+            pb.row0[0] = (int)-pos0;
+            pb.kv0[0] = 0;
+            pb.len[0] = (int)(q_pos0 + Tq);
+            pb.blk0[0] = (int)(pos0 / dsa::kDedupRows);
+            const int64_t hi = std::min<int64_t>(pos0 + rows, lim);
+            pb.blk_start[0] = 0;
+            pb.blk_start[1] = (int)((hi + dsa::kDedupRows - 1) / dsa::kDedupRows) - pb.blk0[0];
+            dsa::AttnArgs at;
+            at.q = q_c; at.k = a.k; at.v = a.v; at.out = out_c; at.idx = idx_c; at.Tq = rows;
+            at.topk = topk; at.Hq = a.Hq; at.G = a.G; at.d = a.d; at.sm_scale = a.sm_scale;
+            at.n_kv = tk; at.block_table = nullptr; at.max_blocks = 0; at.block_size = 0;
+            at.row_seq = nullptr; at.seq_lens = nullptr; at.bf16 = 1;
+            e = dsa::launch_dedup_prefix_attn(at, pb, stream);
+            if (e != hipSuccess) return hip_fail(e, "prefix attention launch");
+            if (pos0 + rows > lim) {
+                at.pos0 = pos0;
+                at.prefix_skip = lim;
+                e = dsa::launch_sparse_attn(at, 1, nullptr, stream);
+                if (e != hipSuccess) return hip_fail(e, "attention launch");
+            }
+            continue;
+        }
+        st = run_attn(q_c, a.k, a.v, a.dtype, tk, nullptr, 0, 0, nullptr, nullptr, idx_c, rows,
+                      topk, a.Hq, a.G, a.d, a.sm_scale, out_c, nullptr, 0, stream);
         if (st != DSA_OK) return st;
     }
     return DSA_OK;
 }
 
 }  // namespace
+
+DSA_EXPORT size_t dsa_sparse_gqa_attn_dedup_workspace_size(int Tq, int64_t q_pos0, int topk) {
+    if (Tq <= 0 || q_pos0 < 0 || topk <= 0 || topk > dsa::kDedupMaxTopk) return 0;
+    const size_t nb = (size_t)dsa::dedup_blocks(Tq, q_pos0);
+    return round_up(nb * 3 * sizeof(int32_t)) + round_up(nb * dsa::kDedupRows * topk * 4) +
+           round_up(nb * dsa::kDedupRows * topk * 2) + kAlign;
+}
+
+DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_dedup(const void* q, const void* k, const void* v,
+                                                  int n_kv, const int32_t* idx, int Tq,
+                                                  int64_t q_pos0, int topk, int Hq, int G, int d,
+                                                  float sm_scale, int mode, void* out, void* ws,
+                                                  size_t ws_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    dsa_status_t st = check_attn_shape(DSA_BF16, Hq, G, d, topk);
+    if (st != DSA_OK) return st;
+    REQUIRE(Tq >= 0 && n_kv >= 0 && q_pos0 >= 0, DSA_ERR_INVALID_ARG,
+            "negative size or position (Tq=%d, n_kv=%d)", Tq, n_kv);
+    REQUIRE(mode == 0 || mode == 1, DSA_ERR_INVALID_ARG, "mode must be 0 or 1 (got %d)", mode);
+    REQUIRE(dsa::dedup_supported(Hq, G, d, topk, std::max(n_kv, 1), 1), DSA_ERR_UNSUPPORTED,
+            "deduplicated attention needs Hq == 8 G, d == 128, topk <= %d and n_kv <= %d",
+            dsa::kDedupMaxTopk, 32 * dsa::kDedupMaxWords);
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR4(idx); REQUIRE_PTR(out);
+    if (Tq == 0) return DSA_OK;
+    const size_t need = dsa_sparse_gqa_attn_dedup_workspace_size(Tq, q_pos0, topk);
+    REQUIRE(ws && aligned16(ws) && ws_bytes >= need, DSA_ERR_WORKSPACE,
+            "deduplicated attention needs %zu workspace bytes (got %zu%s)", need, ws_bytes,
+            ws ? "" : ", ws is NULL");
+    const size_t nb = (size_t)dsa::dedup_blocks(Tq, q_pos0);
+    char* wp = static_cast<char*>(ws);
+    int32_t* info = reinterpret_cast<int32_t*>(wp);   wp += round_up(nb * 3 * sizeof(int32_t));
+    int32_t* list = reinterpret_cast<int32_t*>(wp);   wp += round_up(nb * dsa::kDedupRows * topk * 4);
+    uint16_t* mask = reinterpret_cast<uint16_t*>(wp); wp += round_up(nb * dsa::kDedupRows * topk * 2);
+    int* counter = reinterpret_cast<int*>(wp);
+    hipError_t e = dsa::launch_fill_zero(reinterpret_cast<uint32_t*>(counter), 1, stream);
+    if (e == hipSuccess)
+        e = dsa::launch_dedup_union(idx, Tq, q_pos0, topk, n_kv, mode == 1 ? 0.f : kDedupKappa,
+                                    info, list, mask, counter, stream);
+    if (e != hipSuccess) return hip_fail(e, "dedup union launch");
+    dsa::AttnArgs at;
+    at.q = q; at.k = k; at.v = v; at.out = out; at.idx = idx; at.Tq = Tq; at.topk = topk;
+    at.Hq = Hq; at.G = G; at.d = d; at.sm_scale = sm_scale; at.n_kv = n_kv;
+    at.block_table = nullptr; at.max_blocks = 0; at.block_size = 0; at.row_seq = nullptr;
+    at.seq_lens = nullptr; at.bf16 = 1;
+    e = dsa::launch_dedup_attn(at, q_pos0, info, list, mask, stream);
+    if (e != hipSuccess) return hip_fail(e, "dedup attention launch");
+    at.dedup_info = info;
+    at.pos0 = q_pos0;
+    e = dsa::launch_sparse_attn(at, 1, nullptr, stream);
+    return e == hipSuccess ? DSA_OK : hip_fail(e, "attention launch");
+}
 
 DSA_EXPORT size_t dsa_prefill_workspace_size(int Tq, int64_t q_pos0, int chunk_rows, int topk) {
     if (Tq <= 0 || q_pos0 < 0 || topk <= 0) return 0;
@@ -470,11 +561,12 @@ DSA_EXPORT dsa_status_t dsa_prefill_varlen(const void* q, const void* k, const v
     const size_t kvrow = (size_t)G * d * (dtype == DSA_BF16 ? 2 : 4);
     const size_t qirow = (size_t)HI * dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
     const size_t kirow = (size_t)dI * (idx_dtype == DSA_FP8_E4M3 ? 1 : 4);
-    // Runs of consecutive sequences of at most topk tokens (bf16): every row keeps its whole
-    // prefix, so no score is needed, and up to kMaxPrefixSeqs of them share one attention
-    // launch (and one launch writing their index lists); rows and results are those of the
-    // per-sequence driver.  Longer sequences take the chunk driver one by one.
-    const bool batch_short = dtype == DSA_BF16;
+    // Runs of consecutive sequences of at most topk tokens (bf16, Hq == 8 G): every row keeps
+    // its whole prefix, so no score is needed, and up to kMaxPrefixSegs of them share one
+    // launch of the deduplicated prefix attention (and one launch writing their index lists):
+    // the same blocks and arithmetic as dsa_prefill on each alone.  Longer sequences take the
+    // chunk driver one by one.
+    const bool batch_short = dtype == DSA_BF16 && Hq == 8 * G && d == 128;
     int run0 = -1;                                  // first sequence of the open run
     auto flush = [&](int i1) -> dsa_status_t {
         const int i0 = run0;
@@ -482,11 +574,22 @@ DSA_EXPORT dsa_status_t dsa_prefill_varlen(const void* q, const void* k, const v
         const int64_t R0 = cu_seqlens[i0];
         const int rows = cu_seqlens[i1] - cu_seqlens[i0];
         if (rows == 0) return DSA_OK;
-        dsa::PrefixRows pr;
-        pr.n = i1 - i0;
-        for (int j = 0; j <= pr.n; ++j) pr.start[j] = cu_seqlens[i0 + j] - (int)R0;
+        dsa::SeqStarts ss;
+        dsa::PrefixBlocks pb;
+        ss.n = pb.n = i1 - i0;
+        pb.blk_start[0] = 0;
+        for (int j = 0; j < ss.n; ++j) {
+            const int st0 = cu_seqlens[i0 + j] - (int)R0;
+            const int len = cu_seqlens[i0 + j + 1] - cu_seqlens[i0 + j];
+            ss.start[j] = st0;
+            pb.row0[j] = pb.kv0[j] = st0;
+            pb.len[j] = len;
+            pb.blk0[j] = 0;
+            pb.blk_start[j + 1] = pb.blk_start[j] + (len + dsa::kDedupRows - 1) / dsa::kDedupRows;
+        }
+        ss.start[ss.n] = rows;
         hipError_t e = hipSuccess;
-        if (idx_out) e = dsa::launch_prefix_idx(pr, topk, idx_out + R0 * topk, stream);
+        if (idx_out) e = dsa::launch_prefix_idx(ss, topk, idx_out + R0 * topk, stream);
         if (e != hipSuccess) return hip_fail(e, "short-sequence index launch");
         dsa::AttnArgs a;
         a.q = static_cast<const char*>(q) + R0 * qrow;
@@ -496,7 +599,7 @@ DSA_EXPORT dsa_status_t dsa_prefill_varlen(const void* q, const void* k, const v
         a.idx = nullptr; a.Tq = rows; a.topk = topk; a.Hq = Hq; a.G = G; a.d = d;
         a.sm_scale = sm_scale; a.n_kv = rows; a.block_table = nullptr; a.max_blocks = 0;
         a.block_size = 0; a.row_seq = nullptr; a.seq_lens = nullptr; a.bf16 = 1;
-        e = dsa::launch_sparse_attn_prefix(a, pr, stream);
+        e = dsa::launch_dedup_prefix_attn(a, pb, stream);
         return e == hipSuccess ? DSA_OK : hip_fail(e, "short-sequence attention launch");
     };
     bool first_cand = true;
@@ -505,7 +608,7 @@ DSA_EXPORT dsa_status_t dsa_prefill_varlen(const void* q, const void* k, const v
         const int len = cu_seqlens[i + 1] - cu_seqlens[i];
         if (batch_short && len <= topk) {
             if (run0 < 0) run0 = i;
-            if (i + 1 - run0 == dsa::kMaxPrefixSeqs) {
+            if (i + 1 - run0 == dsa::kMaxPrefixSegs) {
                 st = flush(i + 1);
                 if (st != DSA_OK) return st;
             }

@@ -109,6 +109,12 @@ struct AttnArgs {
     const int32_t* row_seq; const int32_t* seq_lens;
     int bf16;                                  // 1: bf16 I/O, 0: fp32 I/O
     float* lse = nullptr;                      // optional [Tq, Hq]: natural-log log-sum-exp
+    // contiguous bf16 only: row i is at position pos0 + i.  Rows the deduplicated attention
+    // computes are skipped: positions below prefix_skip, and rows of 16-row blocks marked in
+    // dedup_info (the union kernel's per-block info of this launch's rows)
+    int64_t pos0 = 0;
+    int64_t prefix_skip = 0;
+    const int32_t* dedup_info = nullptr;
 };
 // Backward of the bf16 attention over contiguous K/V (d = 128, heads per group <= 16), with
 // the sparse indexer loss fused in when vals is set (topk <= 2048 then).  dq is written (bf16);
@@ -141,22 +147,59 @@ int attn_num_splits(int Tq, int topk);
 size_t attn_partials_bytes(int Tq, int nsplit, int Hq, int d);
 hipError_t launch_sparse_attn(const AttnArgs& a, int nsplit, float* partials, hipStream_t stream);
 
-// Many short sequences packed back to back in one launch, every row keeping its whole causal
-// prefix (a row at position t < k selects {0 .. t}): start[i] is the first row of sequence i
-// relative to the launch's first row, start[n] the launch's row count.  Passed by value as a
-// kernel argument, so one launch takes at most kMaxPrefixSeqs sequences.
-constexpr int kMaxPrefixSeqs = 256;
-struct PrefixRows {
+// Adjacent-query Top-KV deduplication (dedup.hip).  Blocks of kDedupRows adjacent query rows,
+// aligned to absolute positions (block b of a chunk starting at position q_pos0 holds its rows
+// at positions 16 (q_pos0 / 16 + b) .. + 15, so chunk sizes that are multiples of 16 give the
+// same blocks); the union kernel writes info[3 b .. 3 b + 2] = {union size, selections,
+// marked} per block,
+// and for a marked block (kappa * union < selections) the ascending union list[b, 0 .. U) and
+// the 16-bit masks of the rows that selected each position (list and mask rows of
+// kDedupRows * topk entries).  It adds the marked blocks to *counter.  The dedup attention
+// then computes the marked blocks' rows (bf16, Hq == 8 G, contiguous K/V); a per-query launch
+// given dedup_info computes the rest.
+constexpr int kDedupRows = 16;
+constexpr int kDedupMaxTopk = 2048;
+constexpr int kDedupMaxWords = 8192;         // positions < 262144
+bool dedup_supported(int Hq, int G, int d, int topk, int64_t n_pos, int bf16);
+// Positions below which every row of a sequence of len positions is in a whole-prefix block.
+int64_t prefix_block_limit(int64_t len, int topk);
+int dedup_blocks(int Tq, int64_t q_pos0);    // blocks of a chunk of Tq rows at q_pos0
+hipError_t launch_dedup_union(const int32_t* idx, int Tq, int64_t q_pos0, int topk, int n_pos,
+                              float kappa, int32_t* info, int32_t* ulist, uint16_t* umask,
+                              int* counter, hipStream_t stream);
+hipError_t launch_dedup_attn(const AttnArgs& a, int64_t q_pos0, const int32_t* info,
+                             const int32_t* ulist, const uint16_t* umask, hipStream_t stream);
+// n 32-bit zeros (a kernel, so that it may be captured into graphs).
+hipError_t launch_fill_zero(uint32_t* p, int64_t n, hipStream_t stream);
+
+// Blocks of whole-prefix rows: rows at positions t whose 16-row block (positions 16 B .. 16 B
+// + 15 of their sequence) holds only rows with t + 1 <= topk select {0 .. t}, so a block's union
+// is {0 .. min(16 B + 16, len) - 1} and a row's mask is u <= t: the deduplicated attention
+// needs no union kernel for them.  A launch covers up to kMaxPrefixSegs segments (a sequence,
+// or one chunk's part of it): segment i has its position 0 at launch row row0[i] and K/V row
+// kv0[i], len[i] positions in all, and the launch takes its blocks blk0[i] .. blk0[i] +
+// (blk_start[i + 1] - blk_start[i]) - 1; rows outside [0, Tq) of the launch are skipped.
+// Passed by value as a kernel argument.
+constexpr int kMaxPrefixSegs = 128;
+struct PrefixBlocks {
     int n;
-    int start[kMaxPrefixSeqs + 1];
+    int blk_start[kMaxPrefixSegs + 1];
+    int row0[kMaxPrefixSegs];
+    int kv0[kMaxPrefixSegs];
+    int len[kMaxPrefixSegs];
+    int blk0[kMaxPrefixSegs];
 };
-// bf16 attention of such a launch (a.idx unused; a.q, a.k, a.v, a.out start at the launch's
-// first row, a.Tq = a.n_kv = start[n]); the same arithmetic as a full-row launch over the
-// index lists {0 .. t}.
-hipError_t launch_sparse_attn_prefix(const AttnArgs& a, const PrefixRows& rows,
-                                     hipStream_t stream);
-// The index lists of such a launch: idx[r, e] = e for e <= t, -1 after (rows start[n] x topk).
-hipError_t launch_prefix_idx(const PrefixRows& rows, int topk, int32_t* idx, hipStream_t stream);
+// The deduplicated attention of such blocks (bf16, Hq == 8 G, contiguous K/V from a.k / a.v;
+// a.q, a.out: the launch's rows, a.Tq of them).
+hipError_t launch_dedup_prefix_attn(const AttnArgs& a, const PrefixBlocks& pb, hipStream_t stream);
+// Index lists of short sequences packed back to back (every row keeps its whole prefix):
+// start[i] is the first row of sequence i relative to the launch, start[n] the row count;
+// idx[r, e] = e for e <= t, -1 after.
+struct SeqStarts {
+    int n;
+    int start[kMaxPrefixSegs + 1];
+};
+hipError_t launch_prefix_idx(const SeqStarts& rows, int topk, int32_t* idx, hipStream_t stream);
 
 // Per-token E4M3 quantisation of x [T, n] (fp32, or bf16 when x_bf16): codes [T, n], scale [T].
 hipError_t launch_quantize_e4m3(const void* x, int x_bf16, int T, int n, uint8_t* codes,

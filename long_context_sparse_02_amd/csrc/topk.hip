@@ -656,7 +656,7 @@ namespace {
 
 // Index lists of packed short sequences whose rows keep their whole prefix: row r at position
 // t of its sequence gets 0 .. t, then -1.  One workgroup per row, 16-byte stores.
-__global__ __launch_bounds__(256) void prefix_idx_kernel(PrefixRows rows, int topk,
+__global__ __launch_bounds__(256) void prefix_idx_kernel(SeqStarts rows, int topk,
                                                          int32_t* __restrict__ idx)
 {
     const int r = blockIdx.x;
@@ -672,9 +672,9 @@ __global__ __launch_bounds__(256) void prefix_idx_kernel(PrefixRows rows, int to
 
 }  // namespace
 
-hipError_t launch_prefix_idx(const PrefixRows& rows, int topk, int32_t* idx, hipStream_t stream)
+hipError_t launch_prefix_idx(const SeqStarts& rows, int topk, int32_t* idx, hipStream_t stream)
 {
-    if (rows.n < 1 || rows.n > kMaxPrefixSeqs) return hipErrorInvalidValue;
+    if (rows.n < 1 || rows.n > kMaxPrefixSegs) return hipErrorInvalidValue;
     const int T = rows.start[rows.n];
     if (T == 0) return hipSuccess;
     hipLaunchKernelGGL(prefix_idx_kernel, dim3((unsigned)T), dim3(256), 0, stream, rows, topk, idx);

@@ -391,6 +391,18 @@ def _cand_chunks(Tq, q_pos0, chunk):
     return sum(1 for r0 in range(0, Tq, C) if q_pos0 + min(Tq, r0 + C) >= 49152)
 
 
+def _assert_out_matches_staged(out, out_s, L, k, q_pos0=0):
+    """Rows in 16-row blocks of whole prefixes (positions below 16 * floor(k / 16), or all when
+    L <= k) take the deduplicated attention in the fused prefill: the same terms with other
+    rounding, within the bf16 attention tolerance of the per-query kernel.  Every other row is
+    bitwise equal."""
+    lim = L if L <= k else (k // 16) * 16
+    n_pre = max(0, min(out.shape[0], lim - q_pos0))
+    assert torch.equal(out[n_pre:], out_s[n_pre:])
+    if n_pre:
+        assert (out[:n_pre].float() - out_s[:n_pre].float()).abs().max().item() <= 2e-2
+
+
 def _staged_prefill(x, k, sm_scale, G):
     """The layer through the separate entry points over full score rows."""
     Tk = x["k_idx"].shape[0]
@@ -406,8 +418,9 @@ def _staged_prefill(x, k, sm_scale, G):
 def test_prefill_candidate_path_equals_staged(L, k, chunk, keys):
     """The fused prefill selects from sampled-bound candidate lists in chunks that see >= 48K
     keys (rows beyond 8192 positions take the sampled bound, the others every causal score)
-    and over full score rows below that; its Omega and output must be bitwise those of the
-    indexer + top-k + attention entry points over full score rows."""
+    and over full score rows below that; its Omega must be bitwise that of the indexer +
+    top-k + attention entry points over full score rows, and so must its output outside the
+    blocks of deduplicated attention."""
     cfg = W.scaled(W.PREFILL_32K, L=L, k=k, keys=keys, seed=L + k)
     _say("candidate path vs staged", L, k, chunk, keys)
     x = W.prefill_inputs(cfg, DEV)
@@ -419,12 +432,13 @@ def test_prefill_candidate_path_equals_staged(L, k, chunk, keys):
     _say("  candidate chunks %d, rows redone %d" % tuple(stats))
     assert stats == [_cand_chunks(L, 0, chunk), 0]
     assert torch.equal(idx, idx_s)
-    assert torch.equal(out, out_s)
+    _assert_out_matches_staged(out, out_s, L, k)
 
 
 def test_prefill_continuation_candidate_path_equals_staged():
     """A continuation chunk (queries at positions q_pos0.., the prefix already cached) on the
-    candidate path equals the separate entry points bit for bit."""
+    candidate path equals the separate entry points bit for bit (Omega; the output outside
+    deduplicated blocks)."""
     L, q0, k = 60000, 52000, 2048
     cfg = W.scaled(W.PREFILL_32K, L=L, k=k, keys="clustered", seed=123)
     x = W.prefill_inputs(cfg, DEV)
@@ -441,7 +455,7 @@ def test_prefill_continuation_candidate_path_equals_staged():
     out_s = dsa.sparse_gqa_attn(q, x["k"], x["v"], idx_s, cfg.G, cfg.sm_scale, split=False)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx_s)
-    assert torch.equal(out, out_s)
+    _assert_out_matches_staged(out, out_s, L, k, q_pos0=q0)
 
 
 def test_prefill_ties_take_the_exact_fallback():
@@ -461,7 +475,8 @@ def test_prefill_ties_take_the_exact_fallback():
     out_s, idx_s = _staged_prefill(x, k, cfg.sm_scale, cfg.G)
     torch.cuda.synchronize()
     assert stats[0] == _cand_chunks(L, 0, 4096) == 2 and stats[1] > 0   # redone over full rows
-    assert torch.equal(idx, idx_s) and torch.equal(out, out_s)
+    assert torch.equal(idx, idx_s)
+    _assert_out_matches_staged(out, out_s, L, k)
     ii = to_np(idx)
     for t in (0, 100, 2047, 2048, 5000, 8191, 8192, 45056, 49999):
         n = min(k, t + 1)

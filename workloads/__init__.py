@@ -52,6 +52,8 @@ class PrefillConfig:
     cluster_std: float = 0.3
     vision_tokens: int = 3840   # multimodal: vision tokens per 15 s segment
     text_tokens: int = 128      # multimodal: text tokens per segment
+    queries: str = "iid"        # indexer queries: "iid", or "frames" (a centre per frame span)
+    query_std: float = 0.5      # "frames": noise around a query's frame centre
     seed: int = 0
 
     @property
@@ -138,6 +140,33 @@ def _indexer_keys(cfg: PrefillConfig, device) -> torch.Tensor:
     raise ValueError(cfg.keys)
 
 
+def _indexer_queries(cfg: PrefillConfig, device) -> torch.Tensor:
+    """q^I [L, HI, dI]: i.i.d. N(0, 1), or with frame structure: the tokens of one frame span
+    (cluster_span tokens; in the multimodal layout the vision tokens of one frame) share a
+    per-head N(0, I) centre and add query_std * N(0, 1); multimodal text tokens stay i.i.d.
+    Adjacent queries of one frame then pick mostly the same keys, as video tokens of one frame
+    do (report section 5.3: 16 adjacent queries need about 8K distinct keys at 128K)."""
+    L, HI, dI = cfg.L, cfg.HI, cfg.dI
+    noise = torch.randn(L, HI, dI, generator=_gen(cfg.seed, 4, device), device=device)
+    if cfg.queries == "iid":
+        return noise
+    if cfg.queries != "frames":
+        raise ValueError(cfg.queries)
+    pos = torch.arange(L, device=device)
+    if cfg.keys == "multimodal":
+        seg = cfg.vision_tokens + cfg.text_tokens
+        in_seg = pos % seg
+        frame = (pos // seg) * (cfg.vision_tokens // cfg.cluster_span) + in_seg // cfg.cluster_span
+        text = in_seg >= cfg.vision_tokens
+    else:
+        frame = pos // cfg.cluster_span
+        text = torch.zeros(L, dtype=torch.bool, device=device)
+    n_frames = int(frame.max().item()) + 1
+    centres = torch.randn(n_frames, HI, dI, generator=_gen(cfg.seed, 8, device), device=device)
+    q = centres[frame] + cfg.query_std * noise
+    return torch.where(text[:, None, None], noise, q)
+
+
 def prefill_inputs(cfg: PrefillConfig, device="cpu") -> dict:
     """All inputs of one prefill layer call, on ``device``."""
     L = cfg.L
@@ -147,7 +176,7 @@ def prefill_inputs(cfg: PrefillConfig, device="cpu") -> dict:
     out["q"] = (torch.randn(L, cfg.Hq, cfg.d, generator=_gen(cfg.seed, 1, device), device=device) * s).to(el)
     out["k"] = (torch.randn(L, cfg.G, cfg.d, generator=_gen(cfg.seed, 2, device), device=device) * s).to(el)
     out["v"] = (torch.randn(L, cfg.G, cfg.d, generator=_gen(cfg.seed, 3, device), device=device) * s).to(el)
-    qi = torch.randn(L, cfg.HI, cfg.dI, generator=_gen(cfg.seed, 4, device), device=device)
+    qi = _indexer_queries(cfg, device)
     ki = _indexer_keys(cfg, device)
     out["w"] = torch.rand(L, cfg.HI, generator=_gen(cfg.seed, 7, device), device=device)
     if cfg.idx_dtype == "fp8":
