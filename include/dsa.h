@@ -82,7 +82,10 @@ int dsa_version(void);
  * Workspace: dsa_index_scores_workspace_size() bytes of device memory (the FP8
  *   path keeps a per-token mix of the w-weighted indexer queries there: 512 bytes
  *   per query row; the fp32 path needs none and ws may be NULL).  The scores
- *   are computed as sum_j w ReLU(x_j) = 1/2 (sum_j w_j x_j + sum_j w_j |x_j|).
+ *   are computed as sum_j w ReLU(x_j) = 1/2 (sum_j w_j x_j + sum_j w_j |x_j|),
+ *   except where the two terms cancel (|A| + |L| > 15 |A + L|): those blocks are
+ *   recomputed in the direct form on exact bf16 products (an all-negative score is
+ *   exactly 0).
  */
 size_t dsa_index_scores_workspace_size(int Tq, int HI, int dI, dsa_dtype_t idx_dtype);
 dsa_status_t dsa_index_scores(const void* q_idx, const float* q_scale, const float* w,
@@ -366,6 +369,9 @@ dsa_status_t dsa_index_scores_at(const void* q_idx, const float* q_scale, const 
  * multiple of 16) the dk_idx contributions are stored per (row, entry) for chunks of rows and
  * summed per position in row order: dk_idx is then bit-reproducible.  With ws = NULL
  * (ws_bytes 0) they are added with fp32 atomic adds, whose order, and so the last bits, vary.
+ * A key listed more than once in a row (top-k never does so) counts every time in both forms;
+ * with a workspace its extra copies are added atomically after the ordered sums, so such rows
+ * lose only the bit-reproducibility.
  */
 size_t dsa_index_scores_at_bwd_workspace_size(int Tq, int Tk, int HI, int topk);
 dsa_status_t dsa_index_scores_at_bwd(const void* q_idx, const float* q_scale, const float* w,
@@ -398,7 +404,10 @@ dsa_status_t dsa_sparse_gqa_attn_lse(const void* q, const void* k, const void* v
  * With a workspace of dsa_sparse_gqa_attn_bwd_workspace_size() bytes the contributions are
  * stored per (row, entry, group) for chunks of rows and summed per position in row order:
  * dk and dv are then bit-reproducible.  With ws = NULL (ws_bytes 0) they are added with fp32
- * atomic adds, whose order, and so the last bits, vary between runs.
+ * atomic adds, whose order, and so the last bits, vary between runs.  A key listed more than
+ * once in a row (top-k never does so) counts every time, as in the forward; with a workspace
+ * its extra copies are added atomically after the ordered sums (those rows lose only the
+ * bit-reproducibility).
  * When vals float [Tq, topk] (= dsa_index_scores_at at idx) is given (topk <= 2048), also
  *   kl float [Tq]: sum_g KL(p[t,:,g] || softmax(vals[t,:])) over the valid entries, p[t,s,g]
  *     the mean of the group's heads' P (report section 2.3.3, sparse adaptation loss),

@@ -534,13 +534,46 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 
 __global__ __launch_bounds__(256) void stage_mark_kernel(const int32_t* __restrict__ idx, int r0,
                                                          int C, int topk, int n_kv, int W,
-                                                         uint32_t* __restrict__ mask)
+                                                         uint32_t* __restrict__ mask,
+                                                         uint8_t* __restrict__ dup)
 {
     const int64_t n = (int64_t)C * topk;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
         const int t = (int)(e / topk);
         const int s = idx[(int64_t)r0 * topk + e];
-        if (s >= 0 && s < n_kv) atomicOr(&mask[(int64_t)s * W + (t >> 5)], 1u << (t & 31));
+        uint8_t repeat = 0;
+        if (s >= 0 && s < n_kv) {
+            const uint32_t bit = 1u << (t & 31);
+            repeat = (atomicOr(&mask[(int64_t)s * W + (t >> 5)], bit) & bit) ? 1 : 0;
+        }
+        dup[e] = repeat;                   // every entry written: no clearing needed
+    }
+}
+
+// The contributions of repeated keys (entries marked in dup), added atomically after the
+// ordered per-key sums.  Lists of distinct keys mark nothing and this kernel only reads dup.
+__global__ __launch_bounds__(256) void stage_dup_add_kernel(const int32_t* __restrict__ idx, int r0,
+                                                            int C, int topk, int G, int width,
+                                                            const uint8_t* __restrict__ dup,
+                                                            const float* __restrict__ stg,
+                                                            float* __restrict__ dk,
+                                                            float* __restrict__ dv)
+{
+    const int64_t n = (int64_t)C * topk;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+        if (!dup[e]) continue;
+        const int s = idx[(int64_t)r0 * topk + e];
+        if (width == 128) {
+            for (int c = 0; c < 128; ++c) atomicAdd(dk + (int64_t)s * 128 + c, stg[e * 128 + c]);
+            continue;
+        }
+        for (int g = 0; g < G; ++g) {
+            const float* src = stg + (e * G + g) * 256;
+            for (int c = 0; c < 128; ++c) {
+                atomicAdd(dv + ((int64_t)s * G + g) * 128 + c, src[c]);
+                atomicAdd(dk + ((int64_t)s * G + g) * 128 + c, src[128 + c]);
+            }
+        }
     }
 }
 
@@ -600,13 +633,14 @@ __global__ __launch_bounds__(256) void stage_list_kernel(const int32_t* __restri
                                                          int C, int topk, int n_kv, int W,
                                                          const uint32_t* __restrict__ mask,
                                                          const int32_t* __restrict__ offs,
+                                                         const uint8_t* __restrict__ dup,
                                                          int32_t* __restrict__ list)
 {
     const int64_t n = (int64_t)C * topk;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
         const int t = (int)(e / topk);
         const int s = idx[(int64_t)r0 * topk + e];
-        if (s < 0 || s >= n_kv) continue;
+        if (s < 0 || s >= n_kv || dup[e]) continue;    // one listed entry per (key, row)
         const uint32_t* m = mask + (int64_t)s * W;
         int rank = __popc(m[t >> 5] & ((1u << (t & 31)) - 1u));
         for (int w = 0; w < (t >> 5); ++w) rank += __popc(m[w]);
@@ -885,7 +919,7 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, hipStream_t stream)
 
 hipError_t launch_stage_reduce(const int32_t* idx, int r0, int C, int topk, int n_kv, int G,
                                const float* stg, uint32_t* mask, int32_t* offs, int32_t* list,
-                               float* dk, float* dv, hipStream_t stream, int width)
+                               uint8_t* dup, float* dk, float* dv, hipStream_t stream, int width)
 {
     if (width != 256 && width != 128) return hipErrorInvalidValue;
     if (C == 0 || n_kv == 0) return hipSuccess;
@@ -894,17 +928,19 @@ hipError_t launch_stage_reduce(const int32_t* idx, int r0, int C, int topk, int 
     const unsigned gm = (unsigned)std::min<int64_t>((nm + 255) / 256, 65536);
     const unsigned ge = (unsigned)std::min<int64_t>((ne + 255) / 256, 65536);
     hipLaunchKernelGGL(fill_u32_kernel, dim3(gm), dim3(256), 0, stream, mask, nm);
-    hipLaunchKernelGGL(stage_mark_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, n_kv, W, mask);
+    hipLaunchKernelGGL(stage_mark_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, n_kv, W, mask, dup);
     const int nb = (n_kv + 255) / 256;
     int32_t* bsum = offs + n_kv + 1;                  // nb more entries after the offsets
     hipLaunchKernelGGL(stage_count_kernel, dim3(nb), dim3(256), 0, stream, mask, n_kv, W, offs, bsum);
     hipLaunchKernelGGL(stage_scan_kernel, dim3(1), dim3(1024), 0, stream, bsum, nb, offs + n_kv);
     hipLaunchKernelGGL(stage_add_kernel, dim3(nb), dim3(256), 0, stream, offs, n_kv, bsum);
-    hipLaunchKernelGGL(stage_list_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, n_kv, W, mask, offs, list);
+    hipLaunchKernelGGL(stage_list_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, n_kv, W, mask, offs, dup, list);
     if (width == 256)
         hipLaunchKernelGGL(stage_reduce_kernel, dim3(n_kv), dim3(256), 0, stream, stg, offs, list, G, dk, dv);
     else
         hipLaunchKernelGGL(stage_reduce128_kernel, dim3(n_kv), dim3(64), 0, stream, stg, offs, list, dk);
+    hipLaunchKernelGGL(stage_dup_add_kernel, dim3(ge), dim3(256), 0, stream, idx, r0, C, topk, G,
+                       width, dup, stg, dk, dv);
     return hipGetLastError();
 }
 

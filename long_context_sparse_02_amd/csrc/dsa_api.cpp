@@ -875,7 +875,7 @@ namespace {
 // and 1 GiB of staged dk^I contributions (512 bytes per selected entry).
 struct IxBwdPlan {
     int chunk;
-    size_t stg_bytes, mask_bytes, offs_bytes, list_bytes, total;
+    size_t stg_bytes, mask_bytes, offs_bytes, list_bytes, dup_bytes, total;
 };
 
 IxBwdPlan plan_ix_bwd(int Tq, int Tk, int topk) {
@@ -889,7 +889,8 @@ IxBwdPlan plan_ix_bwd(int Tq, int Tk, int topk) {
     p.mask_bytes = round_up((size_t)Tk * (p.chunk / 32) * sizeof(uint32_t));
     p.offs_bytes = round_up(((size_t)Tk + 1 + ((size_t)Tk + 255) / 256) * sizeof(int32_t));
     p.list_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
-    p.total = p.stg_bytes + p.mask_bytes + p.offs_bytes + p.list_bytes;
+    p.dup_bytes = round_up((size_t)p.chunk * topk);
+    p.total = p.stg_bytes + p.mask_bytes + p.offs_bytes + p.list_bytes + p.dup_bytes;
     return p;
 }
 
@@ -930,13 +931,14 @@ DSA_EXPORT dsa_status_t dsa_index_scores_at_bwd(const void* q_idx, const float* 
     float* stg = reinterpret_cast<float*>(wp);              wp += plan.stg_bytes;
     uint32_t* mask = reinterpret_cast<uint32_t*>(wp);       wp += plan.mask_bytes;
     int32_t* offs = reinterpret_cast<int32_t*>(wp);         wp += plan.offs_bytes;
-    int32_t* list = reinterpret_cast<int32_t*>(wp);
+    int32_t* list = reinterpret_cast<int32_t*>(wp);         wp += plan.list_bytes;
+    uint8_t* dup = reinterpret_cast<uint8_t*>(wp);
     for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
         const int rows = std::min(plan.chunk, Tq - r0);
         hipError_t e = dsa::launch_index_at_bwd(qi8, q_scale, w, ki8, k_scale, rows, Tk, HI, idx,
                                                 topk, g, dq_idx, dw, dk_idx, stream, r0, stg);
         if (e == hipSuccess && Tk > 0)
-            e = dsa::launch_stage_reduce(idx, r0, rows, topk, Tk, 1, stg, mask, offs, list,
+            e = dsa::launch_stage_reduce(idx, r0, rows, topk, Tk, 1, stg, mask, offs, list, dup,
                                          dk_idx, nullptr, stream, 128);
         if (e != hipSuccess) return hip_fail(e, "indexer backward launch");
     }
@@ -973,7 +975,7 @@ constexpr size_t kStageBudget = size_t(4) << 30;
 
 struct BwdPlan {
     int chunk;
-    size_t stg_bytes, mask_bytes, offs_bytes, list_bytes, total;
+    size_t stg_bytes, mask_bytes, offs_bytes, list_bytes, dup_bytes, total;
 };
 
 BwdPlan plan_bwd(int Tq, int topk, int G, int n_kv) {
@@ -987,7 +989,8 @@ BwdPlan plan_bwd(int Tq, int topk, int G, int n_kv) {
     p.mask_bytes = round_up((size_t)n_kv * (p.chunk / 32) * sizeof(uint32_t));
     p.offs_bytes = round_up(((size_t)n_kv + 1 + ((size_t)n_kv + 255) / 256) * sizeof(int32_t));
     p.list_bytes = round_up((size_t)p.chunk * topk * sizeof(int32_t));
-    p.total = p.stg_bytes + p.mask_bytes + p.offs_bytes + p.list_bytes;
+    p.dup_bytes = round_up((size_t)p.chunk * topk);
+    p.total = p.stg_bytes + p.mask_bytes + p.offs_bytes + p.list_bytes + p.dup_bytes;
     return p;
 }
 
@@ -1038,7 +1041,8 @@ DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, co
     float* stg = reinterpret_cast<float*>(wp);              wp += plan.stg_bytes;
     uint32_t* mask = reinterpret_cast<uint32_t*>(wp);       wp += plan.mask_bytes;
     int32_t* offs = reinterpret_cast<int32_t*>(wp);         wp += plan.offs_bytes;
-    int32_t* list = reinterpret_cast<int32_t*>(wp);
+    int32_t* list = reinterpret_cast<int32_t*>(wp);         wp += plan.list_bytes;
+    uint8_t* dup = reinterpret_cast<uint8_t*>(wp);
     for (int r0 = 0; r0 < Tq; r0 += plan.chunk) {
         const int rows = std::min(plan.chunk, Tq - r0);
         a.r0 = r0;
@@ -1046,7 +1050,7 @@ DSA_EXPORT dsa_status_t dsa_sparse_gqa_attn_bwd(const void* q, const void* k, co
         a.stg = stg;
         hipError_t e = dsa::launch_sparse_attn_bwd(a, stream);
         if (e == hipSuccess)
-            e = dsa::launch_stage_reduce(idx, r0, rows, topk, n_kv, G, stg, mask, offs, list, dk,
+            e = dsa::launch_stage_reduce(idx, r0, rows, topk, n_kv, G, stg, mask, offs, list, dup, dk,
                                          dv, stream);
         if (e != hipSuccess) return hip_fail(e, "attention backward launch");
     }

@@ -139,9 +139,14 @@ hipError_t launch_sparse_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
 // list each key's entries in row order, and add their sums into dk / dv.
 // width 256: rows of [dV 128 | dK 128] per group into dv / dk [n_kv, G, 128];
 // width 128: rows of 128 into dk [n_kv, 128] (G = 1, dv unused).
+// dup (C * topk bytes) marks the entries that repeat a key already listed earlier in their
+// row's list (whichever of the copies marks the bit first is listed); their contributions are
+// added atomically after the ordered sums, so repeated keys count every time, in an order that
+// is not reproducible (lists of distinct keys, as top-k gives, keep the reproducible sums).
 hipError_t launch_stage_reduce(const int32_t* idx, int r0, int C, int topk, int n_kv, int G,
                                const float* stg, uint32_t* mask, int32_t* offs, int32_t* list,
-                               float* dk, float* dv, hipStream_t stream, int width = 256);
+                               uint8_t* dup, float* dk, float* dv, hipStream_t stream,
+                               int width = 256);
 // Splits used for a given shape when a workspace is available (1 = no split).
 int attn_num_splits(int Tq, int topk);
 size_t attn_partials_bytes(int Tq, int nsplit, int Hq, int d);

@@ -1147,6 +1147,41 @@ def test_training_side_padding_and_out_of_range_entries():
     assert np.abs(dki - rk).max() <= 1e-2 * np.abs(rk).max()
 
 
+def test_training_side_repeated_keys():
+    """A key listed more than once in a row counts every time (as in the forward): the staged
+    (ordered) reductions of dK / dV and dk^I match the atomic-add forms and the oracle, which
+    takes every entry of a list as a term."""
+    rng = np.random.default_rng(91)
+    T, Tk, HI, topk, G, Hq = 40, 700, 64, 96, 4, 32
+    sm = 1 / math.sqrt(128)
+    qc, qs, w, kc, ks = _int_code_indexer(rng, T, Tk, HI)
+    q, k, v, dout, idx = _attn_train_case(rng, T, Tk, Hq, G, topk)
+    idx[2, 5] = idx[2, 9]                            # twice in one row
+    idx[4, 1] = idx[4, 2] = idx[4, 30]               # three times
+    idx[7, :] = idx[7, 0]                            # one key in every slot
+    idx[11, 3] = idx[12, 3]                          # the same key in two rows (as usual)
+    g = rng.normal(size=(T, topk)).astype(np.float32)
+    g[idx < 0] = 0.0
+    a = _dev(qc, qs, w, kc, ks, idx, g)
+    dqi, dw, dki = dsa.index_scores_at_bwd(*a)
+    dqi2, dw2, dki2 = dsa.index_scores_at_bwd(*a, staged=False)
+    qd, kd, vd, dod, idd = _dev(q, k, v, dout, idx)
+    out, lse = dsa.sparse_gqa_attn_lse(qd, kd, vd, idd, G, sm)
+    dq, dk, dv = dsa.sparse_gqa_attn_bwd(qd, kd, vd, idd, G, sm, out, dod, lse)
+    dq2, dk2, dv2 = dsa.sparse_gqa_attn_bwd(qd, kd, vd, idd, G, sm, out, dod, lse, staged=False)
+    torch.cuda.synchronize()
+    assert (dki - dki2).abs().max().item() <= 1e-5 * dki.abs().max().item()
+    assert (dk - dk2).abs().max().item() <= 1e-5 * dk.abs().max().item()
+    assert (dv - dv2).abs().max().item() <= 1e-5 * dv.abs().max().item()
+    _, _, rk = oracle.index_scores_bwd(qc, qs, w, kc, ks, oracle.FP8_E4M3, idx, g)
+    assert np.abs(to_np(dki) - rk).max() <= 1e-2 * np.abs(rk).max()
+    _, rk, rv = oracle.attn_bwd(q, k, v, oracle.BF16, idx, G, sm, dout)
+    for name, got, ref in (("dk", to_np(dk), rk), ("dv", to_np(dv), rv)):
+        err = np.abs(np.asarray(got, np.float64) - ref).max()
+        _say("  repeated keys, attn bwd %s: max err %.3e of max |ref| %.3e" % (name, err, np.abs(ref).max()))
+        assert err <= 1e-2 * np.abs(ref).max(), name
+
+
 def test_attn_bwd_staged_chunks_deterministic():
     """Rows spanning three chunks of the staged backward (512 rows at k = 2048, G = 4): dK / dV
     are bit-reproducible, agree with the atomic-add variant, and dV obeys its invariant."""
