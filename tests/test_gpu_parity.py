@@ -604,10 +604,18 @@ def test_decode_equals_prefill_last_row():
                               perm[None].to(DEV), torch.tensor([L], dtype=torch.int32, device=DEV),
                               cfg.k, cfg.sm_scale, return_idx=True)
     torch.cuda.synchronize()
+    # both selections lie in the oracle's tolerance band (they may differ inside it: the two
+    # paths round the scores differently), and each output matches the oracle on its own set
+    ref = oracle_row_scores(to_np(x["q_idx"][-1:]), to_np(x["q_scale"][-1:]), to_np(x["w"][-1:]),
+                            to_np(x["k_idx"]), to_np(x["k_scale"]), oracle.FP8_E4M3, [0],
+                            q_pos0=L - 1)[0]
+    for what, sel, o in (("prefill", idx_p[-1:], out_p[-1:]), ("decode", idx_d, out_d)):
+        check_band(to_np(sel)[0], ref, L - 1, cfg.k, what)
+        r_out = oracle.sparse_gqa_attn(to_np(x["q"][-1:]), to_np(x["k"]), to_np(x["v"]), oracle.BF16,
+                                       to_np(sel), cfg.Hq, cfg.G, cfg.sm_scale)
+        check_attn(bf16_to_f64(to_np(o)), r_out, "bf16", what)
     a, b = set(to_np(idx_p[-1]).tolist()), set(to_np(idx_d[0]).tolist())
-    assert len(a ^ b) <= 8, "decode and prefill sets differ by %d" % len(a ^ b)
-    if a == b:
-        assert (out_p[-1].float() - out_d[0].float()).abs().max().item() <= 2e-2
+    _say("  decode vs prefill: sets differ by %d members (inside the band)" % len(a ^ b))
 
 
 def test_decode_candidate_path_equals_full_rows():
@@ -661,7 +669,9 @@ def test_decode_full_size_sampled(name):
     cfg = W.ALL[name]
     _say("full-size decode", name)
     x = W.decode_inputs(cfg, DEV)
-    seqs = [0, 17, 63]
+    lens = x["seq_lens"].cpu()
+    # the shortest and longest sequences, and six more spread over the batch
+    seqs = sorted({int(lens.argmin()), int(lens.argmax()), 0, 9, 17, 31, 45, 63})
     _decode_and_check(cfg, x, seqs, name)
 
 
@@ -1054,7 +1064,8 @@ def test_train_step_full_size_sampled():
     """The 32K layer's training step as the benchmark runs it: sampled rows of dq, the
     indexer loss and dI, and of the indexer's dq^I and dw against the oracle; dV against its
     global invariant (each row's probabilities sum to 1, so summing dV over positions gives
-    the sum of dout over rows and the group's heads)."""
+    the sum of dout over rows and the group's heads); dK, dV and dk^I of sampled keys against
+    the oracle over every row that selects them."""
     cfg = W.PREFILL_32K
     _say("training step", cfg.name)
     x = W.prefill_inputs(cfg, DEV)
@@ -1097,6 +1108,22 @@ def test_train_step_full_size_sampled():
     _say("  dV invariant: max err %.3e of max %.3e" % (err, do_sum.abs().max().item()))
     assert err <= 1e-3 * do_sum.abs().max().item() + 1e-2
     assert torch.isfinite(dk).all() and torch.isfinite(dki).all()
+    # key-side gradients of sampled late keys: only rows at or after a key can select it, so
+    # the oracle sums the contributions of those few rows (all of their entries)
+    for s_key in (L - 17, L - 1000, L - 2000):          # about 1, 60 and 120 selecting rows
+        sel_rows = (torch.nonzero((idx[s_key:] == s_key).any(dim=1)).flatten() + s_key).cpu()
+        q_s, do_s, id_s = (to_np(t[sel_rows]) for t in (x["q"], dout, idx))
+        _, rk, rv = oracle.attn_bwd(q_s, ki, vi, oracle.BF16, id_s, G, cfg.sm_scale, do_s)
+        _, _, rki = oracle.index_scores_bwd(to_np(x["q_idx"][sel_rows]), to_np(x["q_scale"][sel_rows]),
+                                            to_np(x["w"][sel_rows]), to_np(x["k_idx"]),
+                                            to_np(x["k_scale"]), oracle.FP8_E4M3, id_s,
+                                            to_np(dI[sel_rows]).astype(np.float64))
+        for name, got, ref in (("dK", to_np(dk[s_key]), rk[s_key]), ("dV", to_np(dv[s_key]), rv[s_key]),
+                               ("dk^I", to_np(dki[s_key]), rki[s_key])):
+            err = np.abs(got.astype(np.float64) - ref).max()
+            _say("  %s of key %d (%d selecting rows): max err %.3e of max |ref| %.3e"
+                 % (name, s_key, len(sel_rows), err, np.abs(ref).max()))
+            assert err <= 1e-2 * np.abs(ref).max() + 1e-9, (name, s_key)
 
 
 def test_training_side_padding_and_out_of_range_entries():
