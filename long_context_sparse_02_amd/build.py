@@ -25,7 +25,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-fno-strict-alia
 # Per-source extra flags.  The indexer's ReLU is a plain max: with NaNs honoured
 # the compiler would canonicalise every matrix-core result first, doubling the
 # vector-ALU work of its inner loop.  Indexer inputs are finite FP8 values.
-EXTRA = {"indexer.hip": ["-fno-honor-nans"]}
+# The warm-up loss kernel's matrix-core results are read by vector code right away: with
+# them in VGPRs (not AGPRs) no copy per score is needed.
+EXTRA = {"indexer.hip": ["-fno-honor-nans"],
+         "warmup.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "cache.hip", "train.hip", "warmup.hip",
            "dedup.hip", "noalloc.hip", "dsa_api.cpp"]
 

@@ -80,26 +80,48 @@ __device__ __forceinline__ void lse_reduce16(float& mx, float& sm) {
 }
 
 // Workgroup: G * WPG waves for 16 query rows t0 .. t0+15; wave w serves KV group
-// g = w / WPG, query heads g HPG + (w % WPG) HPW + hh, hh < HPW (HPW = min(HPG, 4)
-// heads per wave, WPG = HPG / HPW waves per group).  A wave keeps the A operands of
-// its 16 rows x HPW heads (M rows m = r HPW + hh, 16 per tile) in registers and
-// streams its group's keys 16 at a time as the B operand.
-// Pass 1 (without lse): per (row, head) online log-sum-exp, one exp2 per score,
-// merged over the 16 key lanes at the end; and per row the log-sum-exp of I.
-// Pass 2: each wave's share of p[t,s,g] = mean_h 2^(S log2e sm_scale - lse2[t,h])
-// into LDS, then per (row, key) the groups are combined: KL terms and dI.
-template <int HPW, int NJ, int WPG>
-__global__ __launch_bounds__(NJ == 4 ? 64 : NJ == 2 ? 128 : 512) void warmup_kl_kernel(
+// g = w / WPG, query heads g HPG + (w % WPG) HPW + hh, hh < HPW (HPW = min(HPG, 8) heads per
+// wave, WPG = HPG / HPW waves per group), so that every key a wave loads meets 16 x HPW query
+// heads.  A wave keeps the A operands of its 16 rows x HPW heads in registers (M tiles of 16:
+// for HPW <= 4, M row m of the wave is row m / HPW, head m % HPW; for HPW = 8 tile mt holds
+// rows 4 (mt % 4) .. +3 with heads 4 (mt / 4) .. +3, so that the 8 heads of a row meet in one
+// lane) and streams its group's keys 16 at a time as the B operand.  Keys are walked in chunks
+// of 64; only the chunks that reach past some row's position (the last one or two) apply the
+// causal mask.
+// Both passes are software-pipelined: the work of one step (for HPW = 8: of half its tiles) is
+// a slot, and each stage interleaves the matrix-core products of the next slot with the
+// vector work on the current one; a key buffer is refilled as soon as its last slot's products
+// are issued, two steps ahead of its next use.
+// Pass 1 (without lse): per (row, head) the sum of 2^(S c2 - ref_row), c2 = sm_scale log2 e,
+// ref_row = c2 max_h S(row, h, key 0) over the row's first heads (key 0 is causal for every
+// row).  One exp2 per score and no rescaling; should a head's total leave [2^-80, FLT_MAX] (a
+// score more than 2^7 above ref, or a head far below the row's others) the wave walks its keys
+// again with a running maximum per (row, head).  Alongside, per row the log-sum-exp of I (rows
+// wave + NW j, one key per lane).
+// Pass 2, per chunk of 64 keys: each wave's share of p[t,s,g] = sum_h 2^(S c2 - lse2[t,h] -
+// log2 HPG) into LDS (and, when the wave holds its whole group, sum_s p log2 p per row in
+// registers); after the barrier the (row, key) pairs of the chunk, one per lane, combine the
+// groups within the next chunk's first stage: dI = G softmax(I)_s - sum_g p and the KL's
+// - sum_g p log2 softmax(I)_s.
+template <int HPW, int WPG, int NJ>
+__global__ __launch_bounds__(HPW == 8 ? 256 : NJ >= 16 ? 64 : NJ >= 8 ? 192 : NJ >= 4 ? 448 : 512)
+void warmup_kl_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int Tq, int Tk,
     int64_t q_pos0, int Hq, int G, int HPG, float sm_scale, const float* __restrict__ lse_in,
     float* __restrict__ scores, int64_t ld, float* __restrict__ kl)
 {
     constexpr int MT = HPW;                              // M tiles per wave (16 rows x HPW)
-    __shared__ float pbuf[2][8][kWuRows][kWuChunk * kWuKeys + 1];
+    constexpr int H = MT == 8 ? 2 : 1;                   // pipeline slots per step
+    constexpr int MP = MT / H;                           // tiles per slot
+    constexpr int GMAX = (HPW == 8 ? 4 : 8) / WPG;       // most groups a workgroup can hold
+    constexpr int KC = kWuChunk * kWuKeys;               // keys per chunk
+    constexpr int PP = KC + 16;                          // LDS pitch: the stores hit 64 banks
+    __shared__ float pbuf[2][8][kWuRows][PP];
     __shared__ float lse_i2[kWuRows];
+    __shared__ float klp[8][kWuRows];                    // per wave and row: sum p log2 p
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int NW = G * WPG;                              // WPG = HPG / HPW
+    const int NW = G * WPG;                              // waves (blockDim.x / 64)
 
     const int g = wave / WPG;
     const int hbase = g * HPG + (wave % WPG) * HPW;     // first query head of this wave
@@ -107,241 +129,409 @@ __global__ __launch_bounds__(NJ == 4 ? 64 : NJ == 2 ? 128 : 512) void warmup_kl_
     const int t0 = blk * kWuRows;
     const int rows = min(kWuRows, Tq - t0);
     const int p0 = (int)(q_pos0 + t0);                  // positions fit in int (Tk is an int)
-    const int nkeys = min(p0 + rows, Tk);
+    const int nkeys = p0 + rows;                         // keys 0 .. p0 + rows - 1 (<= Tk)
     const float c2 = sm_scale * kLog2e;
 
+    // (row, head) of M row mm of tile mt
+    auto m_row = [](int mt, int mm) { return HPW == 8 ? 4 * (mt & 3) + mm / 4 : (16 * mt + mm) / HPW; };
+    auto m_head = [](int mt, int mm) { return HPW == 8 ? 4 * (mt >> 2) + mm % 4 : (16 * mt + mm) % HPW; };
     v8bf qa[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + col, r = m / HPW, hh = m % HPW;
+        const int r = m_row(mt, col), hh = m_head(mt, col);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             if (r < rows)
                 qa[mt][ks] = load8bf(q + ((int64_t)(t0 + r) * Hq + hbase + hh) * 128 + 32 * ks + 8 * grp);
             else
                 qa[mt][ks] = __builtin_bit_cast(v8bf, v4i{0, 0, 0, 0});
+            // with 8 heads the operands go to the accumulation registers, which the matrix core
+            // reads directly, leaving the vector registers to the loop's other values
+            if constexpr (HPW == 8) asm volatile("" : "+a"(qa[mt][ks]));
         }
     }
-    // rows of the I part handled by this lane: r = wave + NW (grp + 4 j), j < nj
-    // (NJ = max(1, 16 / (4 NW)) as instantiated; rows past 15 are skipped)
-    const int nj = NJ;
+    // query row of this lane's accumulator element (mt, i); the lane's 4 rows are slots
+    // q = 0..3 (slot_of), row_q(q) their rows
+    auto row_of = [&](int mt, int i) { return m_row(mt, 4 * grp + i); };
+    auto slot_of = [](int mt, int i) { return HPW == 8 ? (mt & 3) : HPW == 4 ? mt : HPW == 2 ? 2 * mt + (i >> 1) : i; };
+    auto row_q = [&](int qs) {
+        return HPW >= 4 ? 4 * qs + grp : HPW == 2 ? 8 * (qs >> 1) + 2 * grp + (qs & 1) : 4 * grp + qs;
+    };
 
-    // the wave's group's keys s0 .. s0+15 as B operands (key s0 + col, 8 bf16 per k step)
+    // the wave's group's keys s0 .. s0+15 as B operands (key s0 + col, 8 bf16 per k step);
+    // keys past the last are clamped (loaded, never used)
     auto load_keys = [&](int s0, v8bf* kb) {
-        const uint16_t* kp = k + ((int64_t)min(s0 + col, Tk - 1) * G + g) * 128 + 8 * grp;
+        const uint16_t* kp = k + ((int64_t)min(s0 + col, nkeys - 1) * G + g) * 128 + 8 * grp;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) kb[ks] = load8bf(kp + 32 * ks);
     };
-    // the I part's score of key s0 + col, row r = wave + NW (grp + 4 j); every lane loads
-    // from a valid address (clamped), so the loads issue unconditionally
-    auto score_at = [&](int s0, int j) -> float {
-        const int r = wave + NW * (grp + 4 * j);
-        const bool valid = j < nj && r < rows && s0 + col <= p0 + r;
-        const int rc = min(r, rows - 1);
-        const int sc = min(s0 + col, p0 + rc);
-        const float v = scores[(int64_t)(t0 + rc) * ld + sc];
-        return valid ? v : -INFINITY;
-    };
-    auto load_scores = [&](int s0, float* y) {
+    // scores of the tiles of slot part (part * MP .. +MP-1) against keys kb
+    // (k steps outermost: consecutive products go to different tiles and never wait on each
+    // other)
+    auto qk_part = [&](const v8bf* kb, int part, v4f* acc) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) y[j] = score_at(s0, j);
+        for (int t = 0; t < MP; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int t = 0; t < MP; ++t) acc[t] = mfma_bf16_16x16x32(qa[part * MP + t][ks], kb[ks], acc[t]);
+    };
+    // instruction order within a stage: each matrix-core product of the next slot followed by
+    // a few vector instructions of the current one, then the stage ends
+    auto interleave = [&]() {
+#pragma unroll
+        for (int n = 0; n < MP * 4; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);      // three VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // the I part: rows wave + NW j (j < NJ; rows past the block's are skipped), key c0 + lane.
+    // Every load is issued, from a clamped address, and its value is used only a stage or more
+    // later (a use next to the load would wait for every load in flight, the key prefetches
+    // included); I_valid tells which values are inside the causal prefix.
+    auto load_I = [&](int c0, float* y) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r = wave + NW * j, rc = min(r, rows - 1), s = c0 + lane;
+            y[j] = scores[(int64_t)(t0 + rc) * ld + min(s, p0 + rc)];
+        }
+    };
+    auto I_valid = [&](int c0, int j) {
+        const int r = wave + NW * j;
+        return r < rows && c0 + lane <= p0 + r;
     };
 
     float lse2[MT][4];
     {
-        float mx[MT][4], sm[MT][4], mxi[NJ], smi[NJ];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { mx[mt][i] = -INFINITY; sm[mt][i] = 0.f; }
+        float mxi[NJ], smi[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) { mxi[j] = -INFINITY; smi[j] = 0.f; }
-        // one step of keys s0 .. s0+15 with operands kb / yi, while the next step's are
-        // loaded into kn / yn (two register sets used in turn: no copies between steps)
-        auto step1 = [&](int s0, const v8bf* kb, const float* yi, v8bf* kn, float* yn) {
-            const int s = s0 + col;
-            // keys past some row's position occur only in the last steps (edge)
-            const bool edge = s0 + kWuKeys - 1 > p0;
-            if (!lse_in) load_keys(s0 + kWuKeys, kn);       // past the end: clamped, unused
-            load_scores(s0 + kWuKeys, yn);
-            if (!lse_in) {
-                v4f acc[MT];
+        auto lse_I = [&](int c0, const float* y) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; ++j) lse_step(y[j] * kLog2e, I_valid(c0, j), mxi[j], smi[j]);
+        };
+        if (lse_in) {
+            // 4 chunks of loads in flight while the previous 4 are summed
+            float ya[4][NJ], yb[4][NJ];
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc[mt]);
+            for (int u = 0; u < 4; ++u) load_I(u * KC, ya[u]);
+            for (int c0 = 0; c0 < nkeys; c0 += 8 * KC) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) load_I(c0 + (4 + u) * KC, yb[u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) lse_I(c0 + u * KC, ya[u]);
+                if (c0 + 4 * KC >= nkeys) break;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) load_I(c0 + (8 + u) * KC, ya[u]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) lse_I(c0 + (4 + u) * KC, yb[u]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = m_row(mt, 4 * grp + i), hh = m_head(mt, 4 * grp + i);
+                    lse2[mt][i] = r < rows ? lse_in[(int64_t)(t0 + r) * Hq + hbase + hh] * kLog2e : 0.f;
                 }
-                // running sums are kept against a reference mx that is raised only when a
-                // score exceeds it by more than 2^16 (one exp2 per score otherwise)
-                // key s is valid for row r when r >= lim (no branch between the matrix core's
-                // results and their first reads)
-                const int lim = edge ? s - p0 : -kWuRows;
-                float dd[MT][4];
-                bool big = false;
+        } else {
+            float ref[4], sm[MT][4];
+            v8bf ka[4], kb[4];
+            v4f a0[MP], a1[MP];
+            load_keys(0, ka);
+            load_keys(kWuKeys, kb);
+            qk_part(ka, 0, a0);                              // slot 0: step 0, first tiles
+            if constexpr (H == 1) load_keys(2 * kWuKeys, ka);
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) ref[qs] = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < MP; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ref[slot_of(t, i)] = fmaxf(ref[slot_of(t, i)], a0[t][i] * c2);
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) ref[qs] = __shfl(ref[qs], lane & 48, 64);   // key 0: column 0
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm[mt][i] = 0.f;
+            // a stage: the sums of slot (s0, part) from cur while the matrix core forms slot
+            // (nxt_part) of the keys in src into nxt; refill (if any) then receives the keys
+            // at refill_s0
+            auto stage1 = [&](int s0, int part, const v4f* cur, v4f* nxt, const v8bf* src, int nxt_part,
+                              v8bf* refill, int refill_s0, bool edge, bool last, int c0, const float* y) {
+                qk_part(src, nxt_part, nxt);
+                if (refill) load_keys(refill_s0, refill);
+                const int lim = edge ? s0 + col - p0 : -kWuRows;   // key valid for rows >= lim
+#pragma unroll
+                for (int t = 0; t < MP; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int mt = part * MP + t;
+                        const float e = ex2(fmaf(cur[t][i], c2, -ref[slot_of(mt, i)]));
+                        sm[mt][i] += row_of(mt, i) >= lim ? e : 0.f;
+                    }
+                if (last) lse_I(c0, y);
+                interleave();
+            };
+            // the stages of one chunk (edge: only the steps below nkeys)
+            auto chunk1 = [&](int c0, bool edge) {
+                float y[NJ];
+                load_I(c0, y);
+                if constexpr (H == 1) {
+                    stage1(c0, 0, a0, a1, kb, 0, kb, c0 + 3 * kWuKeys, edge, false, c0, y);
+                    if (!edge || c0 + kWuKeys < nkeys)
+                        stage1(c0 + kWuKeys, 0, a1, a0, ka, 0, ka, c0 + 4 * kWuKeys, edge, false, c0, y);
+                    if (!edge || c0 + 2 * kWuKeys < nkeys)
+                        stage1(c0 + 2 * kWuKeys, 0, a0, a1, kb, 0, kb, c0 + 5 * kWuKeys, edge, false, c0, y);
+                    if (!edge || c0 + 3 * kWuKeys < nkeys)
+                        stage1(c0 + 3 * kWuKeys, 0, a1, a0, ka, 0, ka, c0 + 6 * kWuKeys, edge, !edge, c0, y);
+                } else {
+                    v8bf* none = nullptr;
+                    stage1(c0, 0, a0, a1, ka, 1, ka, c0 + 2 * kWuKeys, edge, false, c0, y);
+                    stage1(c0, 1, a1, a0, kb, 0, none, 0, edge, false, c0, y);
+                    if (!edge || c0 + kWuKeys < nkeys) {
+                        stage1(c0 + kWuKeys, 0, a0, a1, kb, 1, kb, c0 + 3 * kWuKeys, edge, false, c0, y);
+                        stage1(c0 + kWuKeys, 1, a1, a0, ka, 0, none, 0, edge, false, c0, y);
+                    }
+                    if (!edge || c0 + 2 * kWuKeys < nkeys) {
+                        stage1(c0 + 2 * kWuKeys, 0, a0, a1, ka, 1, ka, c0 + 4 * kWuKeys, edge, false, c0, y);
+                        stage1(c0 + 2 * kWuKeys, 1, a1, a0, kb, 0, none, 0, edge, false, c0, y);
+                    }
+                    if (!edge || c0 + 3 * kWuKeys < nkeys) {
+                        stage1(c0 + 3 * kWuKeys, 0, a0, a1, kb, 1, kb, c0 + 5 * kWuKeys, edge, false, c0, y);
+                        stage1(c0 + 3 * kWuKeys, 1, a1, a0, ka, 0, none, 0, edge, !edge, c0, y);
+                    }
+                }
+                if (edge) lse_I(c0, y);                      // (inside the last stage otherwise)
+            };
+            int c0 = 0;
+            for (; c0 + KC - 1 <= p0; c0 += KC) chunk1(c0, false);   // every key of the chunk is causal
+            for (; c0 < nkeys; c0 += KC) chunk1(c0, true);           // the last chunks: masked, ragged
+            // each head's total over the 16 key lanes
+            bool bad = false;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float s = sm[mt][i];
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+                    sm[mt][i] = s;
+                    bad |= !(s >= 0x1p-80f && s <= 3.4028235e38f);
+                }
+            if (__any(bad)) {
+                // the same sums with a running maximum per (row, head) (two exp2 per score),
+                // merged over the key lanes
+                float mx[MT][4];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) { mx[mt][i] = -INFINITY; sm[mt][i] = 0.f; }
+                for (int s0 = 0; s0 < nkeys; s0 += kWuKeys) {
+                    load_keys(s0, ka);
+                    const int lim = s0 + col - p0;
+#pragma unroll
+                    for (int part = 0; part < H; ++part) {
+                        v4f acc[MP];
+                        qk_part(ka, part, acc);
+#pragma unroll
+                        for (int t = 0; t < MP; ++t)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int mt = part * MP + t;
+                                const float y = acc[t][i] * c2;
+                                const float nm = fmaxf(mx[mt][i], y);
+                                const float ns = fmaf(sm[mt][i], ex2(mx[mt][i] - nm), ex2(y - nm));
+                                const bool ok = row_of(mt, i) >= lim;
+                                sm[mt][i] = ok ? ns : sm[mt][i];
+                                mx[mt][i] = ok ? nm : mx[mt][i];
+                            }
+                    }
+                }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float d = fmaf(acc[mt][i], c2, -mx[mt][i]);
-                        dd[mt][i] = (16 * mt + 4 * grp + i) / HPW >= lim ? d : -INFINITY;
-                        big |= dd[mt][i] > 16.f;
+                        lse_reduce16(mx[mt][i], sm[mt][i]);
+                        lse2[mt][i] = mx[mt][i] + lg2(sm[mt][i]);
                     }
-                if (__any(big)) {
+            } else {
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float y = acc[mt][i] * c2;
-                            const bool ok = (16 * mt + 4 * grp + i) / HPW >= lim;
-                            const float nm = ok ? fmaxf(mx[mt][i], y) : mx[mt][i];
-                            const float ns = sm[mt][i] * ex2(mx[mt][i] - nm) + ex2(y - nm);
-                            sm[mt][i] = ok && nm != -INFINITY ? ns : sm[mt][i];
-                            mx[mt][i] = nm;
-                        }
-                } else {
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) sm[mt][i] += ex2(dd[mt][i]);
-                }
+                    for (int i = 0; i < 4; ++i) lse2[mt][i] = ref[slot_of(mt, i)] + lg2(sm[mt][i]);
             }
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) lse_step(yi[j] * kLog2e, yi[j] != -INFINITY, mxi[j], smi[j]);
-        };
-        v8bf ka[4], kb2[4];
-        float ya[NJ], yb[NJ];
-        if (!lse_in) load_keys(0, ka);
-        load_scores(0, ya);
-        for (int s0 = 0; s0 < nkeys; s0 += 2 * kWuKeys) {
-            step1(s0, ka, ya, kb2, yb);
-            if (s0 + kWuKeys < nkeys) step1(s0 + kWuKeys, kb2, yb, ka, ya);
         }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 16 * mt + 4 * grp + i, r = m / HPW, hh = m % HPW;
-                if (lse_in) {
-                    lse2[mt][i] = r < rows ? lse_in[(int64_t)(t0 + r) * Hq + hbase + hh] * kLog2e : 0.f;
-                } else {
-                    lse_reduce16(mx[mt][i], sm[mt][i]);
-                    lse2[mt][i] = mx[mt][i] + lg2(sm[mt][i]);
-                }
-            }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            if (j >= nj) break;
-            lse_reduce16(mxi[j], smi[j]);
-            const int r = wave + NW * (grp + 4 * j);
-            if (col == 0 && r < kWuRows) lse_i2[r] = mxi[j] + lg2(smi[j]);
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float mo = __shfl_xor(mxi[j], o, 64), so = __shfl_xor(smi[j], o, 64);
+                lse_merge(mxi[j], smi[j], mo, so);
+            }
+            const int r = wave + NW * j;
+            if (lane == 0 && r < rows) lse_i2[r] = mxi[j] + lg2(smi[j]);
         }
     }
+    // 2^(S c2 - lse2h) is a head's probability divided by HPG (a power of two: exact)
+    const float lg_hpg = (float)(31 - __builtin_clz(HPG));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lse2[mt][i] += lg_hpg;
     __syncthreads();
 
     float kacc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) kacc[j] = 0.f;
-    const float inv_h = 1.f / (float)HPG;
-    // Pass 2 in chunks of kWuChunk key steps per barrier: each step writes the wave's share
-    // of p for its 16 keys into the chunk's columns; after the barrier the I part combines the
-    // groups for all the chunk's keys.  Steps past nkeys run on clamped keys and are masked.
-    v8bf ka[4], kb2[4];
-    auto step2 = [&](int s0, int b, int u, const v8bf* kb, v8bf* kn) {
-        const int s = s0 + col;
-        const bool edge = s0 + kWuKeys - 1 > p0;
-        load_keys(s0 + kWuKeys, kn);                        // past the end: clamped, unused
-        v4f acc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc[mt] = mfma_bf16_16x16x32(qa[mt][ks], kb[ks], acc[mt]);
-        }
-        const int cc = u * kWuKeys + col;                   // the key's column in the chunk
-        // key s is valid for row r when r >= lim, applied by selects: no branch between the
-        // matrix core's results and their first reads
-        const int lim = edge ? s - p0 : -kWuRows;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float e[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = ex2(fmaf(acc[mt][i], c2, -lse2[mt][i]));
-                e[i] = (16 * mt + 4 * grp + i) / HPW >= lim ? v : 0.f;
-            }
-            // this wave's heads of one row sum to its share of p
-            if constexpr (HPW == 4) {
-                pbuf[b][wave][4 * mt + grp][cc] = ((e[0] + e[1]) + (e[2] + e[3])) * inv_h;
-            } else if constexpr (HPW == 2) {
-                pbuf[b][wave][8 * mt + 2 * grp][cc] = (e[0] + e[1]) * inv_h;
-                pbuf[b][wave][8 * mt + 2 * grp + 1][cc] = (e[2] + e[3]) * inv_h;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pbuf[b][wave][16 * mt + 4 * grp + i][cc] = e[i] * inv_h;
-            }
-        }
+    // per row slot: sum_s p log2 p over the lane's keys (when the wave holds its whole group)
+    float kplp[4] = {0.f, 0.f, 0.f, 0.f};
+    float ep[4];                                         // HPW = 8: a row's first 4 heads
+    auto put = [&](int qs, int b, int cc, float p) {
+        pbuf[b][wave][row_q(qs)][cc] = p;
+        if constexpr (WPG == 1) kplp[qs] = fmaf(p, lg2(fmaxf(p, 1.17549435e-38f)), kplp[qs]);  // p = 0 adds 0
     };
-    auto chunk2 = [&](int c0, int b, float (*yc)[kWuChunk], float (*yn)[kWuChunk]) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int u = 0; u < kWuChunk; ++u) yn[j][u] = score_at(c0 + (kWuChunk + u) * kWuKeys, j);
-#pragma unroll
-        for (int u = 0; u < kWuChunk; u += 2) {
-            step2(c0 + u * kWuKeys, b, u, ka, kb2);
-            step2(c0 + (u + 1) * kWuKeys, b, u + 1, kb2, ka);
-        }
-        __syncthreads();
+    // the pairs of a chunk whose p is complete (pend): row wave + NW j, key c0 + lane.  Every
+    // pair is computed (reads stay inside the LDS arrays) and only the stores depend on validity.
+    auto comb_math = [&](int b, int c0, const float* y, float* dI, bool pend) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-            const int r = wave + NW * (grp + 4 * j);
+            const int r = min(wave + NW * j, kWuRows - 1);
+            float psum = 0.f, plp = 0.f;                         // plp in log2 units
+            // the groups' parts, read from clamped slots without branches and dropped past G
 #pragma unroll
-            for (int u = 0; u < kWuChunk; ++u) {
-                if (yc[j][u] != -INFINITY) {               // a valid (row, key) of the I part
-                    const int cc = u * kWuKeys + col;
-                    float* sp = scores + (int64_t)(t0 + r) * ld + c0 + cc;
-                    const float l2 = fmaf(yc[j][u], kLog2e, -lse_i2[r]);  // log2 softmax(I)_s
-                    const float qi = ex2(l2);
-                    // the NW <= 8 waves' parts (group gg: parts gg WPG .. gg WPG + WPG-1),
-                    // read from clamped slots without branches and dropped past G
-                    float psum = 0.f, term = 0.f;                 // term in log2 units
+            for (int gg = 0; gg < GMAX; ++gg) {
+                float p = 0.f;
 #pragma unroll
-                    for (int gg = 0; gg < 8 / WPG; ++gg) {
-                        float p = 0.f;
-#pragma unroll
-                        for (int w2 = 0; w2 < WPG; ++w2) p += pbuf[b][min(gg * WPG + w2, NW - 1)][r][cc];
-                        p = gg < G ? p : 0.f;
-                        psum += p;
-                        term += p > 1e-37f ? p * (lg2(p) - l2) : 0.f;
-                    }
-                    *sp = (float)G * qi - psum;
-                    kacc[j] += term;
-                }
+                for (int w2 = 0; w2 < WPG; ++w2) p += pbuf[b][min(gg * WPG + w2, NW - 1)][r][lane];
+                p = gg < G ? p : 0.f;
+                psum += p;
+                if constexpr (WPG > 1) plp = fmaf(p, lg2(fmaxf(p, 1.17549435e-38f)), plp);
             }
+            const float l2 = fmaf(y[j], kLog2e, -lse_i2[r]);             // log2 softmax(I)_s
+            dI[j] = fmaf((float)G, ex2(l2), -psum);
+            kacc[j] += pend && I_valid(c0, j) ? fmaf(-l2, psum, plp) : 0.f;
         }
     };
-    {
-        float ya[NJ][kWuChunk], yb[NJ][kWuChunk];
-        load_keys(0, ka);
+    auto comb_store = [&](int c0, const float* dI, bool pend) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
+            if (pend && I_valid(c0, j)) scores[(int64_t)(t0 + wave + NW * j) * ld + c0 + lane] = dI[j];
+    };
+    {
+        v8bf ka[4], kb[4];
+        v4f a0[MP], a1[MP];
+        load_keys(0, ka);
+        load_keys(kWuKeys, kb);
+        qk_part(ka, 0, a0);
+        if constexpr (H == 1) load_keys(2 * kWuKeys, ka);
+        // y: the I values of the chunk whose pairs are pending; dI: their gradients
+        float y[NJ], dI[NJ];
 #pragma unroll
-            for (int u = 0; u < kWuChunk; ++u) ya[j][u] = score_at(u * kWuKeys, j);
-        constexpr int kC = kWuChunk * kWuKeys;
-        for (int c0 = 0; c0 < nkeys; c0 += 2 * kC) {
-            chunk2(c0, 0, ya, yb);
-            if (c0 + kC < nkeys) chunk2(c0 + kC, 1, yb, ya);
+        for (int j = 0; j < NJ; ++j) y[j] = 0.f;
+        // a stage of pass 2: p of slot (s0, part) from cur into column 16 u + col of buffer b,
+        // with the next slot's products as in pass 1, and (comb) the pending chunk's pairs
+        auto stage2 = [&](int s0, int part, int u, int b, const v4f* cur, v4f* nxt, const v8bf* src,
+                          int nxt_part, v8bf* refill, int refill_s0, bool edge, bool comb, bool pend) {
+            qk_part(src, nxt_part, nxt);
+            if (refill) load_keys(refill_s0, refill);
+            const int lim = edge ? s0 + col - p0 : -kWuRows;
+            const int cc = u * kWuKeys + col;
+#pragma unroll
+            for (int t = 0; t < MP; ++t) {
+                const int mt = part * MP + t;
+                float e[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = ex2(fmaf(cur[t][i], c2, -lse2[mt][i]));
+                    e[i] = row_of(mt, i) >= lim ? v : 0.f;
+                }
+                // this wave's heads of one row sum to its share of p
+                if constexpr (HPW == 8) {
+                    if (part == 0) ep[t] = (e[0] + e[1]) + (e[2] + e[3]);
+                    else put(t, b, cc, ep[t] + ((e[0] + e[1]) + (e[2] + e[3])));
+                } else if constexpr (HPW == 4) {
+                    put(mt, b, cc, (e[0] + e[1]) + (e[2] + e[3]));
+                } else if constexpr (HPW == 2) {
+                    put(2 * mt, b, cc, e[0] + e[1]);
+                    put(2 * mt + 1, b, cc, e[2] + e[3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) put(i, b, cc, e[i]);
+                }
+            }
+            if (comb) comb_math(b ^ 1, s0 - KC, y, dI, pend);
+            interleave();
+        };
+        // chunk c0 into buffer b; its first stage combines the previous chunk (buffer b ^ 1)
+        // if pend, after which y receives this chunk's I values
+        auto chunk2 = [&](int c0, int b, bool edge, bool pend) {
+            v8bf* none = nullptr;
+            if constexpr (H == 1) {
+                stage2(c0, 0, 0, b, a0, a1, kb, 0, kb, c0 + 3 * kWuKeys, edge, true, pend);
+                comb_store(c0 - KC, dI, pend);
+                load_I(c0, y);
+                if (!edge || c0 + kWuKeys < nkeys)
+                    stage2(c0 + kWuKeys, 0, 1, b, a1, a0, ka, 0, ka, c0 + 4 * kWuKeys, edge, false, false);
+                if (!edge || c0 + 2 * kWuKeys < nkeys)
+                    stage2(c0 + 2 * kWuKeys, 0, 2, b, a0, a1, kb, 0, kb, c0 + 5 * kWuKeys, edge, false, false);
+                if (!edge || c0 + 3 * kWuKeys < nkeys)
+                    stage2(c0 + 3 * kWuKeys, 0, 3, b, a1, a0, ka, 0, ka, c0 + 6 * kWuKeys, edge, false, false);
+            } else {
+                stage2(c0, 0, 0, b, a0, a1, ka, 1, ka, c0 + 2 * kWuKeys, edge, true, pend);
+                comb_store(c0 - KC, dI, pend);
+                load_I(c0, y);
+                stage2(c0, 1, 0, b, a1, a0, kb, 0, none, 0, edge, false, false);
+                if (!edge || c0 + kWuKeys < nkeys) {
+                    stage2(c0 + kWuKeys, 0, 1, b, a0, a1, kb, 1, kb, c0 + 3 * kWuKeys, edge, false, false);
+                    stage2(c0 + kWuKeys, 1, 1, b, a1, a0, ka, 0, none, 0, edge, false, false);
+                }
+                if (!edge || c0 + 2 * kWuKeys < nkeys) {
+                    stage2(c0 + 2 * kWuKeys, 0, 2, b, a0, a1, ka, 1, ka, c0 + 4 * kWuKeys, edge, false, false);
+                    stage2(c0 + 2 * kWuKeys, 1, 2, b, a1, a0, kb, 0, none, 0, edge, false, false);
+                }
+                if (!edge || c0 + 3 * kWuKeys < nkeys) {
+                    stage2(c0 + 3 * kWuKeys, 0, 3, b, a0, a1, kb, 1, kb, c0 + 5 * kWuKeys, edge, false, false);
+                    stage2(c0 + 3 * kWuKeys, 1, 3, b, a1, a0, ka, 0, none, 0, edge, false, false);
+                }
+            }
+            __syncthreads();
+        };
+        int c0 = 0, b = 0;
+        bool pend = false;
+        for (; c0 + KC - 1 <= p0; c0 += KC, b ^= 1) {        // every key of the chunk is causal
+            chunk2(c0, b, false, pend);
+            pend = true;
         }
+        for (; c0 < nkeys; c0 += KC, b ^= 1) {               // the last chunks: masked, ragged
+            chunk2(c0, b, true, pend);
+            pend = true;
+        }
+        comb_math(b ^ 1, c0 - KC, y, dI, true);
+        comb_store(c0 - KC, dI, true);
+    }
+    // the rows' sum_s p log2 p of each group (WPG = 1): over the 16 key lanes, then per wave
+    if constexpr (WPG == 1) {
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) {
+            float v = kplp[qs];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+            if (col == 0) klp[wave][row_q(qs)] = v;
+        }
+        __syncthreads();
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        if (j >= nj) break;
-        float v = kacc[j];
+        float v = wave_sum(kacc[j]);
+        const int r = wave + NW * j;
+        if constexpr (WPG == 1) {
+            if (r < kWuRows) {
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-        const int r = wave + NW * (grp + 4 * j);
-        if (col == 0 && r < rows) kl[t0 + r] = v * kLn2;
+                for (int gg = 0; gg < GMAX; ++gg) v += gg < NW ? klp[min(gg, NW - 1)][r] : 0.f;  // group order
+            }
+        }
+        if (lane == 0 && r < rows) kl[t0 + r] = v * kLn2;
     }
 }
 
@@ -718,8 +908,9 @@ bool warmup_kl_supported(int Hq, int G)
     if (G < 1 || Hq % G) return false;
     const int hpg = Hq / G;
     if (hpg != 1 && hpg != 2 && hpg != 4 && hpg != 8 && hpg != 16) return false;
-    const int hpw = hpg < 4 ? hpg : 4;
-    return G * (hpg / hpw) <= 8;
+    // up to 8 waves of at most 4 heads, or up to 4 waves of 8 heads (their registers fill a SIMD)
+    const int hpw = hpg < 8 ? hpg : 8, nw = G * (hpg / hpw);
+    return hpw == 8 ? nw <= 4 : nw <= 8;
 }
 
 hipError_t launch_warmup_kl(const uint16_t* q, const uint16_t* k, int Tq, int Tk, int64_t q_pos0,
@@ -728,23 +919,30 @@ hipError_t launch_warmup_kl(const uint16_t* q, const uint16_t* k, int Tq, int Tk
 {
     if (Tq == 0) return hipSuccess;
     if (!warmup_kl_supported(Hq, G)) return hipErrorInvalidValue;
-    const int hpg = Hq / G, hpw = hpg < 4 ? hpg : 4, wpg = hpg / hpw, nw = G * wpg;
-    const int nj = nw >= 4 ? 1 : 4 / nw;
+    const int hpg = Hq / G, hpw = hpg < 8 ? hpg : 8, wpg = hpg / hpw, nw = G * wpg;
+    // rows per wave in the I part and the combine: wave + nw j for j < nj covers the 16 rows
+    int nj2 = 2;
+    while (nj2 * nw < kWuRows) nj2 *= 2;
     const dim3 grid((Tq + kWuRows - 1) / kWuRows), block(64 * nw);
-#define WU_KL(H, J, W) hipLaunchKernelGGL((warmup_kl_kernel<H, J, W>), grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl)
-    switch ((hpw * 8 + wpg) * 8 + nj) {
-    case (1 * 8 + 1) * 8 + 1: WU_KL(1, 1, 1); break;
-    case (1 * 8 + 1) * 8 + 2: WU_KL(1, 2, 1); break;
-    case (1 * 8 + 1) * 8 + 4: WU_KL(1, 4, 1); break;
-    case (2 * 8 + 1) * 8 + 1: WU_KL(2, 1, 1); break;
-    case (2 * 8 + 1) * 8 + 2: WU_KL(2, 2, 1); break;
-    case (2 * 8 + 1) * 8 + 4: WU_KL(2, 4, 1); break;
-    case (4 * 8 + 1) * 8 + 1: WU_KL(4, 1, 1); break;
-    case (4 * 8 + 1) * 8 + 2: WU_KL(4, 2, 1); break;
-    case (4 * 8 + 1) * 8 + 4: WU_KL(4, 4, 1); break;
-    case (4 * 8 + 2) * 8 + 1: WU_KL(4, 1, 2); break;
-    case (4 * 8 + 2) * 8 + 2: WU_KL(4, 2, 2); break;
-    case (4 * 8 + 4) * 8 + 1: WU_KL(4, 1, 4); break;
+#define WU_KL(H, W, J) hipLaunchKernelGGL((warmup_kl_kernel<H, W, J>), grid, block, 0, stream, q, k, Tq, Tk, q_pos0, Hq, G, hpg, sm_scale, lse, scores, ld, kl)
+    switch ((hpw * 8 + wpg) * 32 + nj2) {
+    case (1 * 8 + 1) * 32 + 16: WU_KL(1, 1, 16); break;
+    case (1 * 8 + 1) * 32 + 8: WU_KL(1, 1, 8); break;
+    case (1 * 8 + 1) * 32 + 4: WU_KL(1, 1, 4); break;
+    case (1 * 8 + 1) * 32 + 2: WU_KL(1, 1, 2); break;
+    case (2 * 8 + 1) * 32 + 16: WU_KL(2, 1, 16); break;
+    case (2 * 8 + 1) * 32 + 8: WU_KL(2, 1, 8); break;
+    case (2 * 8 + 1) * 32 + 4: WU_KL(2, 1, 4); break;
+    case (2 * 8 + 1) * 32 + 2: WU_KL(2, 1, 2); break;
+    case (4 * 8 + 1) * 32 + 16: WU_KL(4, 1, 16); break;
+    case (4 * 8 + 1) * 32 + 8: WU_KL(4, 1, 8); break;
+    case (4 * 8 + 1) * 32 + 4: WU_KL(4, 1, 4); break;
+    case (4 * 8 + 1) * 32 + 2: WU_KL(4, 1, 2); break;
+    case (8 * 8 + 1) * 32 + 16: WU_KL(8, 1, 16); break;
+    case (8 * 8 + 1) * 32 + 8: WU_KL(8, 1, 8); break;
+    case (8 * 8 + 1) * 32 + 4: WU_KL(8, 1, 4); break;
+    case (8 * 8 + 2) * 32 + 8: WU_KL(8, 2, 8); break;
+    case (8 * 8 + 2) * 32 + 4: WU_KL(8, 2, 4); break;
     default: return hipErrorInvalidValue;
     }
 #undef WU_KL

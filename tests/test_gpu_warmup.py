@@ -102,6 +102,49 @@ def test_warmup_kl_vs_oracle(L, q_pos0, Hq, G, with_lse):
     assert np.all(to_np(kl) >= -(G * np.abs(I32[causal]).max() * 2.0 ** -24 * 8 + 1e-6))
 
 
+@pytest.mark.parametrize("q_pos0,Hq,G", [(0, 32, 4), (90, 8, 2), (37, 16, 1)])
+def test_warmup_kl_scores_far_above_key0(q_pos0, Hq, G):
+    """Rows whose scores at a few keys exceed their score at key 0 by ~100 (natural units,
+    sm_scale q.K): the kernel's per-(row, head) sums referenced to key 0's score overflow
+    there and it takes its running-maximum walk instead; the loss and dI still match the
+    oracle.  Other rows (ordinary scores) share the workgroups."""
+    L = 260
+    _say("warm-up kl, large scores, q_pos0=%d Hq=%d G=%d" % (q_pos0, Hq, G))
+    cfg, x = _case(L, Hq, G, seed=77 + Hq)
+    Tq, sl, sm = L - q_pos0, slice(q_pos0, L), cfg.sm_scale
+    rng = np.random.default_rng(5 + G)
+    hpg = Hq // G
+    q = x["q"][sl].float().cpu().numpy()
+    k = x["k"].float().cpu().numpy()
+    hot_keys = [20, 131, 200]
+    for g in range(G):
+        u = rng.choice([-3.0, 3.0], size=128)
+        for s in hot_keys:
+            k[s, g] = u                                          # q.K = 9 * 128 per hot pair
+        for t in range(Tq):
+            if (q_pos0 + t) % 3 != 1 and q_pos0 + t >= hot_keys[0]:
+                q[t, g * hpg:(g + 1) * hpg] = u
+    q_d = torch.from_numpy(q).bfloat16().to(DEV)
+    k_d = torch.from_numpy(k).bfloat16().to(DEV)
+    I = oracle.index_scores(to_np(x["q_idx"][sl]), to_np(x["q_scale"][sl]), to_np(x["w"][sl]),
+                            to_np(x["k_idx"]), to_np(x["k_scale"]), oracle.FP8_E4M3, q_pos0=q_pos0)
+    I32 = I.astype(np.float32)
+    ld = L + 4
+    scores = np.full((Tq, ld), -np.inf, dtype=np.float32)
+    scores[:, :L] = I32
+    sc = torch.from_numpy(scores).to(DEV)
+    kl = dsa.indexer_warmup_kl(q_d, k_d, G, sm, sc, L, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    rkl, rdI = oracle.indexer_warmup_kl(to_np(q_d), to_np(k_d), oracle.BF16, G, sm,
+                                        I32.astype(np.float64), q_pos0=q_pos0)
+    causal = _causal_lists(Tq, L, q_pos0) >= 0
+    got = to_np(sc)
+    _check_kl(to_np(kl), np.where(causal, got[:, :L], 0.0), rkl, rdI, I32, G, "large scores")
+    # the hot rows put nearly all of p on the hot keys they see
+    t = Tq - 1 if (L - 1) % 3 != 1 else Tq - 2
+    assert rdI[t, hot_keys].sum() < -0.9 * G
+
+
 def _int_indexer(rng, T, Tk, HI):
     """FP8 codes of the integers -4..4 (every dot product exact in fp32, so both sides take
     the same ReLU decisions), positive scales, signed weights."""
