@@ -236,12 +236,14 @@ void warmup_kl_kernel(
                 }
         } else {
             float ref[4], sm[MT][4];
-            v8bf ka[4], kb[4];
+            v8bf k0[4], k1[4], k2[4], k3[4];                // keys of the chunk's steps 0..3
             v4f a0[MP], a1[MP];
-            load_keys(0, ka);
-            load_keys(kWuKeys, kb);
-            qk_part(ka, 0, a0);                              // slot 0: step 0, first tiles
-            if constexpr (H == 1) load_keys(2 * kWuKeys, ka);
+            load_keys(0, k0);
+            load_keys(kWuKeys, k1);
+            load_keys(2 * kWuKeys, k2);
+            load_keys(3 * kWuKeys, k3);
+            qk_part(k0, 0, a0);                              // slot 0: step 0, first tiles
+            if constexpr (H == 1) load_keys(4 * kWuKeys, k0);
 #pragma unroll
             for (int qs = 0; qs < 4; ++qs) ref[qs] = -INFINITY;
 #pragma unroll
@@ -277,29 +279,31 @@ void warmup_kl_kernel(
             auto chunk1 = [&](int c0, bool edge) {
                 float y[NJ];
                 load_I(c0, y);
+                // step u's keys are in k<u>, refilled with step u + 4's once its last slot's
+                // products are issued
                 if constexpr (H == 1) {
-                    stage1(c0, 0, a0, a1, kb, 0, kb, c0 + 3 * kWuKeys, edge, false, c0, y);
+                    stage1(c0, 0, a0, a1, k1, 0, k1, c0 + 5 * kWuKeys, edge, false, c0, y);
                     if (!edge || c0 + kWuKeys < nkeys)
-                        stage1(c0 + kWuKeys, 0, a1, a0, ka, 0, ka, c0 + 4 * kWuKeys, edge, false, c0, y);
+                        stage1(c0 + kWuKeys, 0, a1, a0, k2, 0, k2, c0 + 6 * kWuKeys, edge, false, c0, y);
                     if (!edge || c0 + 2 * kWuKeys < nkeys)
-                        stage1(c0 + 2 * kWuKeys, 0, a0, a1, kb, 0, kb, c0 + 5 * kWuKeys, edge, false, c0, y);
+                        stage1(c0 + 2 * kWuKeys, 0, a0, a1, k3, 0, k3, c0 + 7 * kWuKeys, edge, false, c0, y);
                     if (!edge || c0 + 3 * kWuKeys < nkeys)
-                        stage1(c0 + 3 * kWuKeys, 0, a1, a0, ka, 0, ka, c0 + 6 * kWuKeys, edge, !edge, c0, y);
+                        stage1(c0 + 3 * kWuKeys, 0, a1, a0, k0, 0, k0, c0 + 8 * kWuKeys, edge, !edge, c0, y);
                 } else {
                     v8bf* none = nullptr;
-                    stage1(c0, 0, a0, a1, ka, 1, ka, c0 + 2 * kWuKeys, edge, false, c0, y);
-                    stage1(c0, 1, a1, a0, kb, 0, none, 0, edge, false, c0, y);
+                    stage1(c0, 0, a0, a1, k0, 1, k0, c0 + 4 * kWuKeys, edge, false, c0, y);
+                    stage1(c0, 1, a1, a0, k1, 0, none, 0, edge, false, c0, y);
                     if (!edge || c0 + kWuKeys < nkeys) {
-                        stage1(c0 + kWuKeys, 0, a0, a1, kb, 1, kb, c0 + 3 * kWuKeys, edge, false, c0, y);
-                        stage1(c0 + kWuKeys, 1, a1, a0, ka, 0, none, 0, edge, false, c0, y);
+                        stage1(c0 + kWuKeys, 0, a0, a1, k1, 1, k1, c0 + 5 * kWuKeys, edge, false, c0, y);
+                        stage1(c0 + kWuKeys, 1, a1, a0, k2, 0, none, 0, edge, false, c0, y);
                     }
                     if (!edge || c0 + 2 * kWuKeys < nkeys) {
-                        stage1(c0 + 2 * kWuKeys, 0, a0, a1, ka, 1, ka, c0 + 4 * kWuKeys, edge, false, c0, y);
-                        stage1(c0 + 2 * kWuKeys, 1, a1, a0, kb, 0, none, 0, edge, false, c0, y);
+                        stage1(c0 + 2 * kWuKeys, 0, a0, a1, k2, 1, k2, c0 + 6 * kWuKeys, edge, false, c0, y);
+                        stage1(c0 + 2 * kWuKeys, 1, a1, a0, k3, 0, none, 0, edge, false, c0, y);
                     }
                     if (!edge || c0 + 3 * kWuKeys < nkeys) {
-                        stage1(c0 + 3 * kWuKeys, 0, a0, a1, kb, 1, kb, c0 + 5 * kWuKeys, edge, false, c0, y);
-                        stage1(c0 + 3 * kWuKeys, 1, a1, a0, ka, 0, none, 0, edge, !edge, c0, y);
+                        stage1(c0 + 3 * kWuKeys, 0, a0, a1, k3, 1, k3, c0 + 7 * kWuKeys, edge, false, c0, y);
+                        stage1(c0 + 3 * kWuKeys, 1, a1, a0, k0, 0, none, 0, edge, !edge, c0, y);
                     }
                 }
                 if (edge) lse_I(c0, y);                      // (inside the last stage otherwise)
@@ -328,12 +332,12 @@ void warmup_kl_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) { mx[mt][i] = -INFINITY; sm[mt][i] = 0.f; }
                 for (int s0 = 0; s0 < nkeys; s0 += kWuKeys) {
-                    load_keys(s0, ka);
+                    load_keys(s0, k0);
                     const int lim = s0 + col - p0;
 #pragma unroll
                     for (int part = 0; part < H; ++part) {
                         v4f acc[MP];
-                        qk_part(ka, part, acc);
+                        qk_part(k0, part, acc);
 #pragma unroll
                         for (int t = 0; t < MP; ++t)
 #pragma unroll
@@ -419,12 +423,14 @@ void warmup_kl_kernel(
             if (pend && I_valid(c0, j)) scores[(int64_t)(t0 + wave + NW * j) * ld + c0 + lane] = dI[j];
     };
     {
-        v8bf ka[4], kb[4];
+        v8bf k0[4], k1[4], k2[4], k3[4];
         v4f a0[MP], a1[MP];
-        load_keys(0, ka);
-        load_keys(kWuKeys, kb);
-        qk_part(ka, 0, a0);
-        if constexpr (H == 1) load_keys(2 * kWuKeys, ka);
+        load_keys(0, k0);
+        load_keys(kWuKeys, k1);
+        load_keys(2 * kWuKeys, k2);
+        load_keys(3 * kWuKeys, k3);
+        qk_part(k0, 0, a0);
+        if constexpr (H == 1) load_keys(4 * kWuKeys, k0);
         // y: the I values of the chunk whose pairs are pending; dI: their gradients
         float y[NJ], dI[NJ];
 #pragma unroll
@@ -468,31 +474,31 @@ void warmup_kl_kernel(
         auto chunk2 = [&](int c0, int b, bool edge, bool pend) {
             v8bf* none = nullptr;
             if constexpr (H == 1) {
-                stage2(c0, 0, 0, b, a0, a1, kb, 0, kb, c0 + 3 * kWuKeys, edge, true, pend);
+                stage2(c0, 0, 0, b, a0, a1, k1, 0, k1, c0 + 5 * kWuKeys, edge, true, pend);
                 comb_store(c0 - KC, dI, pend);
                 load_I(c0, y);
                 if (!edge || c0 + kWuKeys < nkeys)
-                    stage2(c0 + kWuKeys, 0, 1, b, a1, a0, ka, 0, ka, c0 + 4 * kWuKeys, edge, false, false);
+                    stage2(c0 + kWuKeys, 0, 1, b, a1, a0, k2, 0, k2, c0 + 6 * kWuKeys, edge, false, false);
                 if (!edge || c0 + 2 * kWuKeys < nkeys)
-                    stage2(c0 + 2 * kWuKeys, 0, 2, b, a0, a1, kb, 0, kb, c0 + 5 * kWuKeys, edge, false, false);
+                    stage2(c0 + 2 * kWuKeys, 0, 2, b, a0, a1, k3, 0, k3, c0 + 7 * kWuKeys, edge, false, false);
                 if (!edge || c0 + 3 * kWuKeys < nkeys)
-                    stage2(c0 + 3 * kWuKeys, 0, 3, b, a1, a0, ka, 0, ka, c0 + 6 * kWuKeys, edge, false, false);
+                    stage2(c0 + 3 * kWuKeys, 0, 3, b, a1, a0, k0, 0, k0, c0 + 8 * kWuKeys, edge, false, false);
             } else {
-                stage2(c0, 0, 0, b, a0, a1, ka, 1, ka, c0 + 2 * kWuKeys, edge, true, pend);
+                stage2(c0, 0, 0, b, a0, a1, k0, 1, k0, c0 + 4 * kWuKeys, edge, true, pend);
                 comb_store(c0 - KC, dI, pend);
                 load_I(c0, y);
-                stage2(c0, 1, 0, b, a1, a0, kb, 0, none, 0, edge, false, false);
+                stage2(c0, 1, 0, b, a1, a0, k1, 0, none, 0, edge, false, false);
                 if (!edge || c0 + kWuKeys < nkeys) {
-                    stage2(c0 + kWuKeys, 0, 1, b, a0, a1, kb, 1, kb, c0 + 3 * kWuKeys, edge, false, false);
-                    stage2(c0 + kWuKeys, 1, 1, b, a1, a0, ka, 0, none, 0, edge, false, false);
+                    stage2(c0 + kWuKeys, 0, 1, b, a0, a1, k1, 1, k1, c0 + 5 * kWuKeys, edge, false, false);
+                    stage2(c0 + kWuKeys, 1, 1, b, a1, a0, k2, 0, none, 0, edge, false, false);
                 }
                 if (!edge || c0 + 2 * kWuKeys < nkeys) {
-                    stage2(c0 + 2 * kWuKeys, 0, 2, b, a0, a1, ka, 1, ka, c0 + 4 * kWuKeys, edge, false, false);
-                    stage2(c0 + 2 * kWuKeys, 1, 2, b, a1, a0, kb, 0, none, 0, edge, false, false);
+                    stage2(c0 + 2 * kWuKeys, 0, 2, b, a0, a1, k2, 1, k2, c0 + 6 * kWuKeys, edge, false, false);
+                    stage2(c0 + 2 * kWuKeys, 1, 2, b, a1, a0, k3, 0, none, 0, edge, false, false);
                 }
                 if (!edge || c0 + 3 * kWuKeys < nkeys) {
-                    stage2(c0 + 3 * kWuKeys, 0, 3, b, a0, a1, kb, 1, kb, c0 + 5 * kWuKeys, edge, false, false);
-                    stage2(c0 + 3 * kWuKeys, 1, 3, b, a1, a0, ka, 0, none, 0, edge, false, false);
+                    stage2(c0 + 3 * kWuKeys, 0, 3, b, a0, a1, k3, 1, k3, c0 + 7 * kWuKeys, edge, false, false);
+                    stage2(c0 + 3 * kWuKeys, 1, 3, b, a1, a0, k0, 0, none, 0, edge, false, false);
                 }
             }
             __syncthreads();
