@@ -7,7 +7,8 @@
 //
 // One workgroup of 1024 threads owns a row; scores are compared through an
 // order-preserving 32-bit key (-0 and +0 map to the same key).
-//   1. A sample of the row (256 runs of 16 contiguous scores) gives, by two
+//   1. A sample of the row (n / 512 runs, 16 to 256, of 16 contiguous scores: about 1/32
+//      of the row) gives, by two
 //      radix digits of a select in LDS, a key that is a lower bound for the k-th
 //      largest with high probability (the sample rank is padded by about 3
 //      sigma, the bound is the low edge of that sample key's bin).
@@ -111,47 +112,91 @@ __device__ __forceinline__ void key_range(Get get, int64_t m, uint32_t* red, uin
 // ((key - kmin) & mask) > prefix and tied with it iff == prefix; `need` of the
 // tied elements complete the R.  Stopped after max_passes digits, kmin + prefix
 // is still a lower bound for the R-th largest key (the low edge of its bin).
+// A pass is one histogram of the digit over the elements still in the running, then wave 0
+// alone scans the bins from the top (32 per lane) and finds the bin holding the need-th
+// element: two barriers a pass.  With hist2 (a second kBins buffer) the next pass's bins are
+// cleared while this pass builds its own; without it, a third barrier separates the clearing.
 template <class Get>
 __device__ void radix_select(Get get, int64_t m, uint32_t R, uint32_t kmin, uint32_t kmax,
-                             uint32_t* hist, uint32_t* wsum, uint32_t* sh, uint32_t& prefix,
+                             uint32_t* hist, uint32_t* hist2, uint32_t* sh, uint32_t& prefix,
                              uint32_t& mask, uint32_t& need, int max_passes = 32) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const uint32_t range = kmax - kmin;
     int hi = range ? 32 - __clz(range) : 0;
     prefix = 0;
     mask = 0;
     need = R;
+    uint32_t* cur = hist;
+    uint32_t* nxt = hist2 ? hist2 : hist;
+    if (hi > 0) {
+        for (int i = tid; i < kBins; i += kTopkThreads) cur[i] = 0;
+        __syncthreads();
+    }
     while (hi > 0) {
         const int lo = hi > kDigitBits ? hi - kDigitBits : 0;
         const uint32_t dmask = (1u << (hi - lo)) - 1u;
-        for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
-        __syncthreads();
+        if (hist2)                                    // the buffer of the pass after this one
+            for (int i = tid; i < kBins; i += kTopkThreads) nxt[i] = 0;
         for (int64_t i = tid; i < m; i += kTopkThreads) {
             const uint32_t rel = get(i) - kmin;
-            if ((rel & mask) == prefix) atomicAdd(&hist[(rel >> lo) & dmask], 1u);
+            if ((rel & mask) == prefix) atomicAdd(&cur[(rel >> lo) & dmask], 1u);
         }
         __syncthreads();
-        // bins in descending order: thread t takes bins 2047-2t and 2046-2t
-        const uint32_t h0 = hist[kBins - 1 - 2 * tid], h1 = hist[kBins - 2 - 2 * tid];
-        uint32_t total;
-        const uint32_t above = block_excl_scan(h0 + h1, wsum, &total);
-        if (above < need && need <= above + h0) {
-            sh[0] = kBins - 1 - 2 * tid;
-            sh[1] = above;
-        } else if (above + h0 < need && need <= above + h0 + h1) {
-            sh[0] = kBins - 2 - 2 * tid;
-            sh[1] = above + h0;
+        if (tid < 64) {
+            // lane l holds bins kBins-1-32l .. kBins-32-32l, from the top down
+            constexpr int kPerLane = kBins / 64;
+            const int base = kBins - kPerLane * (lane + 1);   // the lane's bins: base .. base+31
+            const uint4* b4 = reinterpret_cast<const uint4*>(cur + base);
+            uint32_t sum = 0;
+#pragma unroll
+            for (int j = 0; j < kPerLane / 4; ++j) {
+                const uint4 v = b4[j];
+                sum += (v.x + v.y) + (v.z + v.w);
+            }
+            uint32_t incl = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += y;
+            }
+            // the lane whose bins hold the need-th element (exactly one), then its 32 bins
+            // from the top, one per lane of the wave's first half
+            const uint32_t above_l = incl - sum;
+            const int tl = __ffsll(__ballot(above_l < need && need <= incl)) - 1;
+            const uint32_t above_t = __shfl(above_l, tl, 64);
+            const int tbase = kBins - kPerLane * (tl + 1);
+            const uint32_t c = lane < kPerLane ? cur[tbase + kPerLane - 1 - lane] : 0u;
+            uint32_t ci = c;
+#pragma unroll
+            for (int o = 1; o < kPerLane; o <<= 1) {
+                const uint32_t y = __shfl_up(ci, o, 64);
+                if (lane >= o) ci += y;
+            }
+            const int f = __ffsll(__ballot(lane < kPerLane && need <= above_t + ci)) - 1;
+            if (lane == f) {
+                sh[0] = tbase + kPerLane - 1 - f;
+                sh[1] = above_t + ci - c;
+                sh[2] = c;
+            }
         }
         __syncthreads();
-        const uint32_t bin = sh[0];
+        const uint32_t bin = sh[0], in_bin = sh[2];
         need -= sh[1];
-        const uint32_t in_bin = hist[bin];
         prefix |= bin << lo;
         mask |= dmask << lo;
-        __syncthreads();                              // hist is rebuilt by the next pass
         hi = lo;
-        if (in_bin == need || --max_passes == 0) break;   // the whole bin is taken, or bound only
+        const bool done = in_bin == need || --max_passes == 0;   // the whole bin is taken, or bound only
+        if (!hist2) {
+            if (!done && hi > 0) {                    // wave 0 read the bins before the barrier
+                for (int i = tid; i < kBins; i += kTopkThreads) cur[i] = 0;
+                __syncthreads();
+            }
+        } else {
+            uint32_t* t = cur; cur = nxt; nxt = t;
+        }
+        if (done) break;
     }
+    __syncthreads();                                  // sh and the bins are free again
 }
 
 // Ordered compaction: element i (in position order) is selected when above the
@@ -196,8 +241,8 @@ __device__ void compact(Get get, Pos pos_of, int64_t m, uint32_t kmin, uint32_t 
     }
 }
 
-constexpr int kCap = 8192;                // LDS candidate capacity
-constexpr int kSampleRuns = 256;          // sample: 256 runs of 16 contiguous scores
+constexpr int kCap = 7936;                // LDS candidate capacity (two workgroups per CU fit)
+constexpr int kSampleRuns = 256;          // sample: up to 256 runs of 16 contiguous scores
 constexpr int kSample = kSampleRuns * 16;
 
 // Row length of workgroup row `row`: q_pos0 + row + 1, or row_len[row] when given
@@ -223,7 +268,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_kernel(   // 8 waves per
     if (run_if && *run_if == 0) return;              // gated launch with nothing to do
     __shared__ uint32_t ck[kCap];             // candidate keys, in position order
     __shared__ int32_t ci[kCap];              // their positions (the sample reuses this array)
-    __shared__ uint32_t hist[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins], hist2[kBins];
     __shared__ uint32_t wsum[2 * kTopkWaves];
     __shared__ uint32_t sh[4];
 
@@ -267,9 +312,12 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_kernel(   // 8 waves per
 
         // 1. sample -> lower bound for the k-th largest key (runs start on quads and
         //    end well inside the row)
+        // n / 512 runs (at least 16): the sample reads about 1/32 of the row at any length
         uint32_t* smp = reinterpret_cast<uint32_t*>(ci);
-        const int run = tid >> 2, part = tid & 3;
-        const float4 sv = quad((((int64_t)run * n / kSampleRuns) & ~(int64_t)3) + 4 * part);
+        const int runs = (int)min<int64_t>(kSampleRuns, max<int64_t>(16, n >> 9));
+        const int S = runs * 16;
+        const int run = min(tid >> 2, runs - 1), part = tid & 3;
+        const float4 sv = quad((((int64_t)run * n / runs) & ~(int64_t)3) + 4 * part);
 
         // the first two steps of the pass below stream in while the sample is ranked
         constexpr int kPer = 8;                       // consecutive scores per thread per step
@@ -283,21 +331,28 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_kernel(   // 8 waves per
         fetch(0, b0);
         fetch(kStepLen, b1);
 
-        smp[4 * tid + 0] = order_key(sv.x);
-        smp[4 * tid + 1] = order_key(sv.y);
-        smp[4 * tid + 2] = order_key(sv.z);
-        smp[4 * tid + 3] = order_key(sv.w);
+        if (4 * tid < S) {
+            smp[4 * tid + 0] = order_key(sv.x);
+            smp[4 * tid + 1] = order_key(sv.y);
+            smp[4 * tid + 2] = order_key(sv.z);
+            smp[4 * tid + 3] = order_key(sv.w);
+        }
         __syncthreads();
-        const double r = (double)k * kSample / (double)n;
-        uint32_t r_lo = (uint32_t)ceil(r + 3.0 * sqrt(r) + 8.0);
-        if (r_lo > (uint32_t)kSample) r_lo = kSample;
+        // sample rank of the bound: the expected rank of the k-th largest score, r = k S / n,
+        // padded by 6 sigma (+8) of independent draws: about k + 1800 candidates at any row
+        // length.  The 16 scores of a run are not independent when high scores come in
+        // clusters of positions; then a row can end with fewer than k candidates (the slow
+        // path below), about one in 4000 on clustered keys, against one in 40 at 3 sigma.
+        const double r = (double)k * S / (double)n;
+        uint32_t r_lo = (uint32_t)ceil(r + 6.0 * sqrt(r) + 8.0);
+        if (r_lo > (uint32_t)S) r_lo = S;
         auto get_s = [&](int64_t i) { return smp[i]; };
         uint32_t smin, smax, sp, sm, sn;
-        key_range(get_s, kSample, wsum, smin, smax);
+        key_range(get_s, S, wsum, smin, smax);
         // two digits are enough: the bin's low edge sits at most one bin width (2^-22
         // of the sample's key range) below the r_lo-th largest sample key.  (Keys are
         // not linear in the value, so one 2^-11 bin can span a large value range.)
-        radix_select(get_s, kSample, r_lo, smin, smax, hist, wsum, sh, sp, sm, sn, 2);
+        radix_select(get_s, S, r_lo, smin, smax, hist, hist2, sh, sp, sm, sn, 2);
         const uint32_t bound = smin + sp;             // <= the r_lo-th largest sample key
         __syncthreads();                              // the sample is dead from here on
 
@@ -365,14 +420,14 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_kernel(   // 8 waves per
         auto get_c = [&](int64_t i) { return ck[i]; };
         auto pos_c = [&](int64_t i) { return ci[i]; };
         key_range(get_c, m, wsum, kmin, kmax);
-        radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
+        radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, hist2, sh, prefix, mask, need);
         compact(get_c, pos_c, m, kmin, prefix, mask, need, wsum, out, out_key);
     } else {
         // 4. fallback: the same exact select and compaction over the row in memory
         auto get_g = [&](int64_t i) { return order_key(src[i]); };
         auto pos_g = [&](int64_t i) { return (int32_t)(begin + i); };
         key_range(get_g, n, wsum, kmin, kmax);
-        radix_select(get_g, n, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
+        radix_select(get_g, n, (uint32_t)k, kmin, kmax, hist, hist2, sh, prefix, mask, need);
         compact(get_g, pos_g, n, kmin, prefix, mask, need, wsum, out, out_key);
     }
 }
@@ -390,7 +445,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
 {
     __shared__ uint32_t ck[kMergeCap];
     __shared__ int32_t ci[kMergeCap];
-    __shared__ uint32_t hist[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
     __shared__ uint32_t wsum[2 * kTopkWaves];
     __shared__ uint32_t sh[4];
     const int row = blockIdx.x;
@@ -431,7 +486,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
     auto pos_c = [&](int64_t i) { return ci[i]; };
     uint32_t kmin, kmax, prefix, mask, need;
     key_range(get_c, m, wsum, kmin, kmax);
-    radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
+    radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, nullptr, sh, prefix, mask, need);
     compact(get_c, pos_c, m, kmin, prefix, mask, need, wsum, out);
 }
 
@@ -466,7 +521,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
     int first)
 {
     __shared__ uint32_t smp[kCandCap];
-    __shared__ uint32_t hist[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
     __shared__ uint32_t wsum[2 * kTopkWaves];
     __shared__ uint32_t sh[4];
     const int row = blockIdx.x, tid = threadIdx.x;
@@ -494,7 +549,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
     auto get_s = [&](int64_t i) { return smp[i]; };
     uint32_t smin, smax, sp, sm, sn;
     key_range(get_s, S, wsum, smin, smax);
-    radix_select(get_s, S, r_lo, smin, smax, hist, wsum, sh, sp, sm, sn, 2);
+    radix_select(get_s, S, r_lo, smin, smax, hist, nullptr, sh, sp, sm, sn, 2);
     // back to a float: a score is >= it exactly when its key is >= the bound key (the key
     // lies between two sample keys, so it is a finite value's key)
     if (tid == 0) {
@@ -513,7 +568,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_select_kernel(
 {
     __shared__ uint32_t ck[kCandCap];                 // keys, later the selected positions
     __shared__ uint32_t ci[kCandCap];                 // positions, later the tied positions
-    __shared__ uint32_t hist[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
     __shared__ uint32_t wsum[2 * kTopkWaves];
     __shared__ uint32_t sh[4];
     const int row = blockIdx.x, tid = threadIdx.x;
@@ -538,7 +593,7 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_select_kernel(
     auto get_c = [&](int64_t i) { return ck[i]; };
     uint32_t kmin, kmax, prefix, mask, need;
     key_range(get_c, m, wsum, kmin, kmax);
-    radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, wsum, sh, prefix, mask, need);
+    radix_select(get_c, m, (uint32_t)k, kmin, kmax, hist, nullptr, sh, prefix, mask, need);
     // split in place: positions above the threshold to ck[0..), tied positions to ci[0..)
     // (an element's new slot never exceeds its old index, and a step's elements are all
     // read before any is written)
