@@ -724,10 +724,6 @@ def main():
     if args.profile_kernel:
         run_profile_kernel(args, dsa, W, torch)
         return
-    if args.decode_only:
-        print(json.dumps([run_decode_bench(args, dsa, W, torch, n)
-                          for n in args.decode_workloads.split(",") if n]), flush=True)
-        return
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -736,6 +732,10 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.decode_only:
+        print(json.dumps([run_decode_bench(args, dsa, W, torch, n)
+                          for n in args.decode_workloads.split(",") if n]), flush=True)
+        return
     cfg, x, idx, out, ms_step, kern, fused_ms, same = run_prefill_bench(args, dsa, W, torch)
     dom = max(kern, key=lambda n: kern[n]["ms_per_step"])
     roofline = counter_roofline(kern, dom, cfg.name)

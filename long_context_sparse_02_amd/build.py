@@ -27,7 +27,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-fno-strict-alia
 # vector-ALU work of its inner loop.  Indexer inputs are finite FP8 values.
 # The warm-up loss kernel's matrix-core results are read by vector code right away: with
 # them in VGPRs (not AGPRs) no copy per score is needed.
-EXTRA = {"indexer.hip": ["-fno-honor-nans"],
+# The decode indexer reserves candidate slots with one atomic per group of pages and reads the
+# reply only after its page loop; the atomic optimizer would rewrite that atomic into a form
+# whose reply is read (and waited for, with every page in flight) right where it is issued.
+EXTRA = {"indexer.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
          "warmup.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "cache.hip", "train.hip", "warmup.hip",
            "dedup.hip", "noalloc.hip", "dsa_api.cpp"]

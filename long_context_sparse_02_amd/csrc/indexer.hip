@@ -802,11 +802,17 @@ struct PagedOut {
 };
 
 // Sampled keys cost two dependent round trips per page (block id, then key) and a sample
-// launch is small, so its waves take fewer pages each.
-template <int MODE> constexpr int paged_ppw() { return MODE == kModeSample ? 2 : kDecPagesPerWave; }
+// launch is small, so its waves take fewer pages each.  A candidate-mode wave takes two
+// groups of pages: the slot reservation (an atomic round trip) of the first group is issued
+// between the groups and its reply arrives while the second group streams, so only one
+// reservation per 2 kDecPagesPerWave pages is waited for.
+template <int MODE> constexpr int paged_groups() { return MODE == kModeCandidates ? 2 : 1; }
+template <int MODE> constexpr int paged_ppw() {
+    return MODE == kModeSample ? 2 : kDecPagesPerWave * paged_groups<MODE>();
+}
 
 template <int NHT, int MODE>                       // 16-head tiles of the query
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DSA_DEC_WAVES)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == kModeCandidates ? 3 : DSA_DEC_WAVES)))
 void index_fp8_paged_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ kcache,
@@ -880,6 +886,25 @@ void index_fp8_paged_kernel(
     };
     PageRegs ring[kDecDepth + 1];
     float res[PPW];                   // scores, stored after the page loop
+    constexpr int NG = paged_groups<MODE>(), GP = PPW / NG;
+    uint64_t kept[PPW];               // candidate mode: lanes of each page at or above the bound
+    uint32_t gbase[NG];               // candidate mode: first slot of each group (lane 0)
+    // candidate mode: group g's kept scores as (order key, position) from its reserved slot
+    auto write_group = [&](int g) {
+        uint2* __restrict__ dst = o.cand + (int64_t)b * o.cap;
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        // the reply is read here, not where the atomic was issued
+        uint32_t gb = gbase[g];
+        asm volatile("" : "+v"(gb));
+        uint32_t base = __shfl(gb, 0, 64);
+#pragma unroll
+        for (int j = g * GP; j < (g + 1) * GP; ++j) {
+            const uint32_t slot = base + __popcll(kept[j] & below);
+            if (((kept[j] >> lane) & 1ull) && slot < (uint32_t)o.cap)
+                dst[slot] = make_uint2(order_key(res[j]), (uint32_t)((page0 + j) * 64 + lane));
+            base += __popcll(kept[j]);
+        }
+    };
 #pragma unroll
     for (int i = 0; i < kDecDepth; ++i) fetch(min(i, last), ring[i]);
     // 3. stage the head tiles and weights while the first pages are in flight
@@ -900,7 +925,7 @@ void index_fp8_paged_kernel(
     // the back edge): ring slots are compile-time constants
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
-        if (i >= np) break;
+      if (i < np) {                   // uniform over the wave
         fetch(min(i + kDecDepth, last), ring[(i + kDecDepth) % (kDecDepth + 1)]);
         const PageRegs& cur = ring[i % (kDecDepth + 1)];
         // keep the compiler from hoisting the loop-invariant LDS tiles into registers
@@ -937,30 +962,28 @@ void index_fp8_paged_kernel(
             const bool valid = __shfl(blk_l, i, 64) >= 0;
             res[i] = valid ? mine * (qs * cur.scale) : -INFINITY;
         }
+      }
+        if (MODE == kModeCandidates && (i + 1) % GP == 0) {
+            // keep the group's keys at or above the sequence's bound (invalid and
+            // out-of-range keys hold -inf or are excluded); one atomic reserves the room,
+            // its reply is read after the page loop
+            const int g = i / GP;
+            uint32_t total = 0;
+#pragma unroll
+            for (int j = g * GP; j < (g + 1) * GP; ++j) {
+                const int64_t s = (int64_t)(page0 + j) * 64 + lane;
+                kept[j] = __ballot(j < np && s < len && res[j] >= tau_b);
+                total += __popcll(kept[j]);
+            }
+            gbase[g] = 0;
+            if (lane == 0 && total) gbase[g] = (uint32_t)atomicAdd(o.cnt + b, (int)total);
+        }
     }
     if (MODE == kModeCandidates) {
-        // keep the sequence's keys at or above its bound (invalid and out-of-range keys
-        // hold -inf or are excluded); one atomic per wave reserves the room
-        uint64_t kept[PPW];
-        uint32_t total = 0;
+        // after the page loop: a wait for one reply here would also wait for the pages
+        // in flight (the compiler does not count an atomic's reply in order with loads)
 #pragma unroll
-        for (int i = 0; i < PPW; ++i) {
-            const int64_t s = (int64_t)(page0 + i) * 64 + lane;
-            kept[i] = __ballot(i < np && s < len && res[i] >= tau_b);
-            total += __popcll(kept[i]);
-        }
-        uint32_t base = 0;
-        if (lane == 0 && total) base = (uint32_t)atomicAdd(o.cnt + b, (int)total);
-        base = __shfl(base, 0, 64);
-        uint2* __restrict__ dst = o.cand + (int64_t)b * o.cap;
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-        for (int i = 0; i < PPW; ++i) {
-            const uint32_t slot = base + __popcll(kept[i] & below);
-            if (((kept[i] >> lane) & 1ull) && slot < (uint32_t)o.cap)
-                dst[slot] = make_uint2(order_key(res[i]), (uint32_t)((page0 + i) * 64 + lane));
-            base += __popcll(kept[i]);
-        }
+        for (int g = 0; g < NG; ++g) write_group(g);
         return;
     }
     // score stores interleaved with the page stream slow it down: issue them last

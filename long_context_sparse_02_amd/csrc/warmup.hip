@@ -342,13 +342,14 @@ void warmup_kl_kernel(
                         for (int t = 0; t < MP; ++t)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
+                                // branch-free: a masked key enters as -inf and leaves
+                                // (mx, sm) as they were (mu = 0 while nothing is in yet)
                                 const int mt = part * MP + t;
-                                const float y = acc[t][i] * c2;
+                                const float y = row_of(mt, i) >= lim ? acc[t][i] * c2 : -INFINITY;
                                 const float nm = fmaxf(mx[mt][i], y);
-                                const float ns = fmaf(sm[mt][i], ex2(mx[mt][i] - nm), ex2(y - nm));
-                                const bool ok = row_of(mt, i) >= lim;
-                                sm[mt][i] = ok ? ns : sm[mt][i];
-                                mx[mt][i] = ok ? nm : mx[mt][i];
+                                const float mu = nm == -INFINITY ? 0.f : nm;
+                                sm[mt][i] = fmaf(sm[mt][i], ex2(mx[mt][i] - mu), ex2(y - mu));
+                                mx[mt][i] = nm;
                             }
                     }
                 }

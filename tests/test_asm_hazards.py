@@ -7,7 +7,8 @@ uniform branch placed between an MFMA and that read once left the taken path wit
 branch).  The kernels are written so that no branch sits there; this test compiles every HIP
 source to gfx950 assembly, follows each branch found within a few instructions after an MFMA,
 and counts the instructions (and s_nop cycles) before the first read of the MFMA's
-destination on the taken path.  Twelve cover the longest (16-pass) MFMA shapes in use.
+destination on the taken path (a walk ends at an unconditional branch; a register written on
+the path no longer holds the result).  Twelve cover the longest (16-pass) MFMA shapes in use.
 """
 import os
 import re
@@ -61,19 +62,23 @@ def short_paths(asm: str):
             bm = re.match(r"s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", u)
             if not (bm and bm.group(1) in labels):
                 continue
-            ws2 = ws
+            ws2, live = ws, set(dst)
             for u2 in _instrs(lines, labels[bm.group(1)] + 1):
-                if ws2 >= NEED:
+                if ws2 >= NEED or not live or u2.startswith(("s_endpgm", "s_branch")):
                     break
                 if u2.startswith("s_nop"):
                     ws2 += int(u2.split()[1]) + 1
                     continue
                 if u2.startswith("v_") and not u2.startswith("v_mfma"):
                     ops = re.findall(r"v\[\d+:\d+\]|v\d+", u2)
-                    if len(ops) > 1 and set().union(*[_regs(o) for o in ops[1:]]) & dst:
+                    if len(ops) > 1 and set().union(*[_regs(o) for o in ops[1:]]) & live:
                         found.append((func, i + 1, ws2, u2))
                         break
+                    if ops:                   # a register written here no longer holds the result
+                        live -= _regs(ops[0])
                 ws2 += 1
+            if u.startswith("s_branch"):      # the lines after it are not on this path
+                break
     return found
 
 
@@ -84,6 +89,14 @@ def test_scanner_flags_a_read_right_after_a_branch():
     assert len(short_paths(asm)) == 1
     padded = asm.replace("\ts_cbranch_scc1", "\ts_nop 7\n\ts_nop 7\n\ts_cbranch_scc1")
     assert short_paths(padded) == []
+    # a register written on the path before the read no longer holds the result, and the
+    # lines after an unconditional branch are not on the path
+    overwritten = asm.replace(".LBB0_2:", ".LBB0_2:\n\tv_mov_b32_e32 v34, 0")
+    assert short_paths(overwritten) == []
+    jumped = "\n".join(["_Zk:", "\tv_mfma_f32_16x16x32_bf16 v[34:37], v[26:29], v[30:33], v[46:49]",
+                        "\ts_branch .LBB0_3", ".LBB0_2:", "\tv_fma_f32 v34, v34, v79, -v89",
+                        ".LBB0_3:", "\ts_nop 7", "\ts_nop 7", "\tv_add_f32_e32 v1, v34, v2"])
+    assert short_paths(jumped) == []
 
 
 def test_compiled_kernels_have_no_short_mfma_paths():
