@@ -295,9 +295,19 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_kernel(   // 8 waves per
     bool in_lds = true;
 
     if (n <= kCap) {
-        for (int64_t i = tid; i < n; i += kTopkThreads) {
-            ck[i] = order_key(src[i]);
-            ci[i] = (int32_t)(begin + i);
+        // every load first (clamped into the row), then the keys: one round trip for the row
+        // instead of one per 1024 scores
+        constexpr int kIt = (kCap + kTopkThreads - 1) / kTopkThreads;
+        float v[kIt];
+#pragma unroll
+        for (int j = 0; j < kIt; ++j) v[j] = src[min<int64_t>(tid + (int64_t)j * kTopkThreads, n - 1)];
+#pragma unroll
+        for (int j = 0; j < kIt; ++j) {
+            const int64_t i = tid + (int64_t)j * kTopkThreads;
+            if (i < n) {
+                ck[i] = order_key(v[j]);
+                ci[i] = (int32_t)(begin + i);
+            }
         }
         m = n;
         __syncthreads();
@@ -514,6 +524,8 @@ __device__ void bitonic_sort_asc(uint32_t* a, int len) {
     }
 }
 
+static_assert(kCandCap % kTopkThreads == 0, "candidate lists and sample rows load in whole rounds");
+
 // Lower bound of row `row`'s k-th largest score from its S samples (see launch_topk_bound).
 __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
     const float* __restrict__ samples, int S, int64_t q_pos0, const int32_t* __restrict__ row_len,
@@ -537,8 +549,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_bound_kernel(
         if (tid == 0) tau[row] = -FLT_MAX;
         return;
     }
+    // every load first (clamped to the row's samples), then the keys: one round trip
     const float* __restrict__ src = samples + (int64_t)row * S;
-    for (int i = tid; i < S; i += kTopkThreads) smp[i] = order_key(src[i]);
+    constexpr int kIt = kCandCap / kTopkThreads;
+    float v[kIt];
+#pragma unroll
+    for (int j = 0; j < kIt; ++j) v[j] = src[min(tid + j * kTopkThreads, S - 1)];
+#pragma unroll
+    for (int j = 0; j < kIt; ++j)
+        if (tid + j * kTopkThreads < S) smp[tid + j * kTopkThreads] = order_key(v[j]);
     __syncthreads();
     // rank of the bound among the samples: the expected rank of the k-th largest score,
     // r = k S / n, padded by 5 sigma (+8): fewer than k scores at or above the bound needs
@@ -583,11 +602,19 @@ __global__ __launch_bounds__(kTopkThreads, 8) void topk_select_kernel(
         if (tid == 0) { fallback[0] = 1; atomicAdd(fallback + 2, 1); }
         return;
     }
+    // every load first (clamped to the list), then the LDS stores: one round trip for the list
     const uint2* __restrict__ src = cand + (int64_t)row * kCandCap;
-    for (int i = tid; i < m; i += kTopkThreads) {
-        const uint2 c = src[i];
-        ck[i] = c.x;
-        ci[i] = c.y;
+    constexpr int kIt = kCandCap / kTopkThreads;
+    uint2 cv[kIt];
+#pragma unroll
+    for (int j = 0; j < kIt; ++j) cv[j] = src[min(tid + j * kTopkThreads, m - 1)];
+#pragma unroll
+    for (int j = 0; j < kIt; ++j) {
+        const int i = tid + j * kTopkThreads;
+        if (i < m) {
+            ck[i] = cv[j].x;
+            ci[i] = cv[j].y;
+        }
     }
     __syncthreads();
     auto get_c = [&](int64_t i) { return ck[i]; };
