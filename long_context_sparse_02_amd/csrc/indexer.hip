@@ -770,8 +770,10 @@ __global__ __launch_bounds__(256) void index_f32_kernel(
 // lane groups.  The kernel is bound by the k^I stream (132 bytes per key), so
 // registers go to pages in flight: the workgroup's four waves share the query's
 // head tiles and weights through LDS, each wave owns kDecPagesPerWave
-// consecutive pages, reads their block ids once, and keeps the next
-// kDecDepth pages' codes and scales in flight while it computes the current one.
+// consecutive pages (twice that when keeping candidates), reads their block ids
+// once, and keeps the next kDecDepth pages' codes and scales in flight while it
+// computes the current one.  Candidate mode holds both groups' scores and masks
+// until its stores: it gets the registers of 3 waves per SIMD, not 4.
 #ifndef DSA_DEC_PAGES_PER_WAVE
 #define DSA_DEC_PAGES_PER_WAVE 8
 #endif
@@ -794,7 +796,7 @@ struct PageRegs {
 // Output modes, as in the prefill kernel: every score of the sequence into scores[b, s];
 // the scores of S sampled positions (per-key stratified, hashed offsets) into
 // samples[b, j] (a "page" is then 64 consecutive samples); or only the scores >= tau[b]
-// appended as (order key, position) to the sequence's list, one atomic per wave.
+// appended as (order key, position) to the sequence's list, one atomic per group of pages.
 struct PagedOut {
     float* scores; int64_t ld; const int* run_if;
     float* samples; int S;
