@@ -618,12 +618,24 @@ def test_decode_equals_prefill_last_row():
     _say("  decode vs prefill: sets differ by %d members (inside the band)" % len(a ^ b))
 
 
-def test_decode_candidate_path_equals_full_rows():
+# Sequence lengths for the candidate path: the second list puts a sequence's last wave (two
+# groups of 8 pages of 64 keys) at every kind of group boundary: second group empty (8 pages),
+# one page into it (9), one short of full (15), full (16), and a last page holding one key.
+_DECODE_BOUNDARY_LENS = [
+    [1, 2047, 2048, 2049, 8192, 8193, 9000, 12345, 20000, 33333, 40000, 40960],
+    [64 * (16 * 20 + 8), 64 * (16 * 20 + 8) - 1, 64 * (16 * 20 + 8) + 1, 64 * (16 * 30 + 9),
+     64 * (16 * 30 + 15), 64 * (16 * 37 + 15) - 30, 64 * 16 * 39 + 1, 64 * 7 + 3, 2049, 40960,
+     64 * (16 * 10 + 1) - 63, 64 * (16 * 25 + 12) - 17]]
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_decode_candidate_path_equals_full_rows(which):
     """The same sequences decoded with a block table of 640 columns (40K keys: full score
     rows and the top-k kernel) and padded to 1024 columns (64K: the sampled-bound candidate
     path) give bitwise the same index sets and outputs."""
-    cfg = W.scaled(W.DECODE_PAGED, B=12, Lmin=1, Lmax=40960, k=2048, seed=91)
-    lens = torch.tensor([1, 2047, 2048, 2049, 8192, 8193, 9000, 12345, 20000, 33333, 40000, 40960])
+    cfg = W.scaled(W.DECODE_PAGED, B=12, Lmin=1, Lmax=40960, k=2048, seed=91 + which)
+    lens = torch.tensor(_DECODE_BOUNDARY_LENS[which])
+    assert int(lens.max()) <= 40960 and len(lens) == cfg.B
     x = W.decode_inputs(cfg, DEV, lens=lens)
     assert x["max_blocks"] == 640
     args = (x["q"], x["q_idx"], x["q_scale"], x["w"], x["kidx_cache"], x["kidx_scale"],
